@@ -1,0 +1,283 @@
+/*
+ * sgqa_oracle.c -- TEST INFRASTRUCTURE ONLY.
+ *
+ * A plain, slow, fp64 CPU oracle for the Sparse GQA full-attention layer of
+ * StepFun's Step 5 Preview.  Only the tests, the smoke check and the
+ * benchmark's CPU-baseline leg may load it; the HIP library never does, and
+ * this file shares no source with it.
+ *
+ * What the layer computes, and where the pages say so:
+ *   - ai4snews "Step 5 Preview bets on depth over width", Interpretation,
+ *     second paragraph: the indexer entries of neighbouring history positions
+ *     are compressed into block representations with block size 8, which cuts
+ *     indexer and top-k selection cost 8x.
+ *   - ai.info "StepFun Details Step 5 Preview's 92-Block Agent Design",
+ *     section "Sparse GQA targets million-token context": Sparse GQA picks
+ *     relevant historical blocks instead of the whole history; tokens are
+ *     grouped into blocks of eight; top-k is 4096 tokens with those blocks.
+ *   - same page, section "Why StepFun chose 92 transformer blocks": the full
+ *     attention path is Gated Grouped-Query Attention.
+ *   - phantomic12 "Step 5 Preview" catalogue entry, config.json and
+ *     ATTENTION SPLIT parts: 64 query heads, 4 attention groups (4 KV heads),
+ *     head_dim 192; sparse_config topk 512, proxy_dim 256 on the
+ *     full-attention layers.
+ *
+ * Readings taken where the pages are silent (each is listed in the design doc):
+ *   block representation = mean of the block's proxy keys over the tokens
+ *   present; score = plain dot product of the query's proxy with a block
+ *   representation; candidates = complete past blocks j < floor(t/B); k counts
+ *   blocks including the query's own block, which is always kept; ties go to
+ *   the lower block index; output in ascending block order padded with -1;
+ *   head h uses KV head floor(h / (Hq/Hkv)); softmax scale 1/sqrt(d) (passed
+ *   in); a token attends to positions s <= t only; the gate is one logit per
+ *   (token, head) applied as a logistic sigmoid after normalisation.
+ *
+ * Every floating-point step runs in double.  bf16 inputs are widened exactly.
+ * Nothing here is blocked, fused or reordered beyond the definitions above.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* bf16 is the upper half of an IEEE binary32; widening is exact. */
+static double widen_bf16(uint16_t h)
+{
+    uint32_t bits = ((uint32_t)h) << 16;
+    float f;
+    memcpy(&f, &bits, sizeof f);
+    return (double)f;
+}
+
+/* Number of index blocks for a sequence of L tokens: ceil(L / B). */
+int64_t orc_num_blocks(int64_t L, int32_t B)
+{
+    return (L + B - 1) / B;
+}
+
+/* Number of candidate (complete, past) blocks of a query at position t. */
+int64_t orc_num_candidates(int64_t t, int32_t B)
+{
+    return t / B;
+}
+
+/*
+ * Block compression (ai4snews Interpretation, para. 2; ai.info "Sparse GQA
+ * targets million-token context"): kb[j] is the mean of kp over the tokens
+ * of block j that exist, i.e. positions jB .. min(jB+B, L) - 1.
+ *   kp : [L][P] bf16      kb : [ceil(L/B)][P] double
+ */
+void orc_index_build(const uint16_t *kp, int64_t L, int32_t P, int32_t B, double *kb)
+{
+    const int64_t nblk = orc_num_blocks(L, B);
+#pragma omp parallel for schedule(static)
+    for (int64_t j = 0; j < nblk; ++j) {
+        const int64_t first = j * B;
+        int64_t n = L - first;
+        if (n > B)
+            n = B;
+        for (int32_t p = 0; p < P; ++p) {
+            double sum = 0.0;
+            for (int64_t s = first; s < first + n; ++s)
+                sum += widen_bf16(kp[s * P + p]);
+            kb[j * P + p] = sum / (double)n;
+        }
+    }
+}
+
+/*
+ * Indexer scores (phantomic12 config.json / sparse_config: proxy_dim 256):
+ * for each query row r at position t[r], score[r][j] = sum_p qp[r][p]*kb[j][p]
+ * for every candidate block j < floor(t[r]/B).  Entries past the candidate
+ * count are left untouched.
+ *   qp : [nrows][P] bf16; kb : [nblk][P] double; out : [nrows][out_stride]
+ */
+void orc_scores(const uint16_t *qp, int64_t nrows, const int64_t *t, int32_t B, int32_t P,
+                const double *kb, double *out, int64_t out_stride)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t c = orc_num_candidates(t[r], B);
+        const uint16_t *q = qp + r * P;
+        for (int64_t j = 0; j < c; ++j) {
+            double acc = 0.0;
+            for (int32_t p = 0; p < P; ++p)
+                acc += widen_bf16(q[p]) * kb[j * P + p];
+            out[r * out_stride + j] = acc;
+        }
+    }
+}
+
+typedef struct {
+    double score;
+    int64_t block;
+} scored_block;
+
+/* Order: higher score first; equal scores -> lower block index first. */
+static int by_score_desc_then_index(const void *a, const void *b)
+{
+    const scored_block *x = (const scored_block *)a;
+    const scored_block *y = (const scored_block *)b;
+    if (x->score > y->score)
+        return -1;
+    if (x->score < y->score)
+        return 1;
+    if (x->block < y->block)
+        return -1;
+    if (x->block > y->block)
+        return 1;
+    return 0;
+}
+
+static int by_int32_asc(const void *a, const void *b)
+{
+    const int32_t x = *(const int32_t *)a, y = *(const int32_t *)b;
+    return (x > y) - (x < y);
+}
+
+/*
+ * Causal top-k by explicit sort (ai.info "Sparse GQA targets million-token
+ * context": relevant historical blocks are selected; phantomic12 sparse_config
+ * topk 512).  For the query at t with own block c = floor(t/B):
+ *   if c <= k-1 every block 0..c is kept;
+ *   else the candidates 0..c-1 are sorted by (score desc, index asc), the
+ *   first k-1 are kept, and c is added.
+ * The row is written in ascending block order, padded with -1 up to k.
+ *   scores : [nrows][stride] double (entries j < c used)   idx : [nrows][k]
+ */
+void orc_topk(const double *scores, int64_t nrows, int64_t stride, const int64_t *t,
+              int32_t B, int32_t k, int32_t *idx)
+{
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t c = orc_num_candidates(t[r], B);
+        int32_t *row = idx + r * (int64_t)k;
+        int32_t count = 0;
+        if (c <= (int64_t)k - 1) {
+            for (int64_t j = 0; j <= c; ++j)
+                row[count++] = (int32_t)j;
+        } else {
+            scored_block *cand = (scored_block *)malloc((size_t)c * sizeof(scored_block));
+            for (int64_t j = 0; j < c; ++j) {
+                cand[j].score = scores[r * stride + j];
+                cand[j].block = j;
+            }
+            qsort(cand, (size_t)c, sizeof(scored_block), by_score_desc_then_index);
+            for (int32_t i = 0; i < k - 1; ++i)
+                row[count++] = (int32_t)cand[i].block;
+            free(cand);
+            row[count++] = (int32_t)c;
+            qsort(row, (size_t)count, sizeof(int32_t), by_int32_asc);
+        }
+        for (int32_t i = count; i < k; ++i)
+            row[i] = -1;
+    }
+}
+
+/*
+ * Tokens a query at t attends to: every position of every selected block,
+ * restricted to positions <= t (the own block may extend past t).  -1 entries
+ * are padding.  Writes the positions in ascending order; returns the count.
+ */
+int64_t orc_token_set(const int32_t *sel, int32_t k, int32_t B, int64_t t, int64_t *tokens)
+{
+    int64_t n = 0;
+    for (int32_t i = 0; i < k; ++i) {
+        if (sel[i] < 0)
+            continue;
+        for (int32_t o = 0; o < B; ++o) {
+            const int64_t s = (int64_t)sel[i] * B + o;
+            if (s <= t)
+                tokens[n++] = s;
+        }
+    }
+    return n;
+}
+
+static double logistic(double x)
+{
+    return 1.0 / (1.0 + exp(-x));
+}
+
+/*
+ * Gated grouped-query attention of one query token over an explicit list of
+ * n key/value rows (ai.info "Why StepFun chose 92 transformer blocks": Gated
+ * Grouped-Query Attention; phantomic12 config.json: 64 heads, 4 groups,
+ * head_dim 192).  For head h with group g = floor(h / (Hq/Hkv)):
+ *   z_s  = scale * sum_i q[h][i] * K[s][g][i]
+ *   a    = sum_s softmax(z)_s * V[s][g][:]
+ *   out  = a * sigmoid(gate[h]);   lse = log sum_s exp(z_s)
+ *   q : [Hq][d]; krows, vrows : [n][Hkv][d]; gate : [Hq]; out : [Hq][d]
+ */
+void orc_attend(const uint16_t *q, const uint16_t *krows, const uint16_t *vrows, int64_t n,
+                const uint16_t *gate, int32_t Hq, int32_t Hkv, int32_t d, double scale,
+                double *out, double *lse)
+{
+    const int32_t heads_per_group = Hq / Hkv;
+    double *z = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    for (int32_t h = 0; h < Hq; ++h) {
+        const int32_t g = h / heads_per_group;
+        double m = -INFINITY;
+        for (int64_t s = 0; s < n; ++s) {
+            double dot = 0.0;
+            for (int32_t i = 0; i < d; ++i)
+                dot += widen_bf16(q[h * d + i]) * widen_bf16(krows[(s * Hkv + g) * d + i]);
+            z[s] = scale * dot;
+            if (z[s] > m)
+                m = z[s];
+        }
+        double Z = 0.0;
+        for (int64_t s = 0; s < n; ++s) {
+            z[s] = exp(z[s] - m);
+            Z += z[s];
+        }
+        const double gate_factor = logistic(widen_bf16(gate[h]));
+        for (int32_t i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int64_t s = 0; s < n; ++s)
+                acc += z[s] * widen_bf16(vrows[(s * Hkv + g) * d + i]);
+            out[h * d + i] = (acc / Z) * gate_factor;
+        }
+        if (lse)
+            lse[h] = m + log(Z);
+    }
+    free(z);
+}
+
+/*
+ * Sparse attention for a batch of query rows with the whole K/V cache on the
+ * host: for each row r, build its token set from idx[r] and attend.
+ *   q : [nrows][Hq][d]; t : [nrows]; K, V : [L][Hkv][d]; G : [nrows][Hq];
+ *   idx : [nrows][k]; out : [nrows][Hq][d]; lse : [nrows][Hq] (nullable)
+ * Returns 0, or -1 if a selected token lies outside [0, L).
+ */
+int orc_sparse_attention(const uint16_t *q, const int64_t *t, int64_t nrows,
+                         const uint16_t *K, const uint16_t *V, int64_t L,
+                         const uint16_t *G, const int32_t *idx, int32_t k, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t d, double scale,
+                         double *out, double *lse)
+{
+    int bad = 0;
+    const int64_t row = (int64_t)Hkv * d;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t r = 0; r < nrows; ++r) {
+        int64_t *tok = (int64_t *)malloc((size_t)k * B * sizeof(int64_t));
+        const int64_t n = orc_token_set(idx + r * (int64_t)k, k, B, t[r], tok);
+        uint16_t *kr = (uint16_t *)malloc((size_t)(n > 0 ? n : 1) * row * sizeof(uint16_t));
+        uint16_t *vr = (uint16_t *)malloc((size_t)(n > 0 ? n : 1) * row * sizeof(uint16_t));
+        for (int64_t i = 0; i < n; ++i) {
+            if (tok[i] < 0 || tok[i] >= L) {
+                bad = 1;
+                tok[i] = 0;
+            }
+            memcpy(kr + i * row, K + tok[i] * row, (size_t)row * sizeof(uint16_t));
+            memcpy(vr + i * row, V + tok[i] * row, (size_t)row * sizeof(uint16_t));
+        }
+        orc_attend(q + r * (int64_t)Hq * d, kr, vr, n, G + r * (int64_t)Hq, Hq, Hkv, d, scale,
+                   out + r * (int64_t)Hq * d, lse ? lse + r * (int64_t)Hq : NULL);
+        free(kr);
+        free(vr);
+        free(tok);
+    }
+    return bad ? -1 : 0;
+}

@@ -1,0 +1,336 @@
+"""Pins for the fp64 oracle: facts fixed by the pages or by mathematics.
+
+Each ``pin_*`` takes a loaded oracle library (the real one, or a copy with a
+planted mistake) and raises ``AssertionError`` when the oracle disagrees with
+something it does not itself define: a closed form, a textbook or library
+routine on a special case, an invariant, or a brute-force count.  None of them
+re-types the oracle's own formula.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+import oracle
+
+
+def bf16_bits(x) -> np.ndarray:
+    """float array -> raw bf16 bits (round to nearest even, via torch)."""
+    t = torch.as_tensor(np.asarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def widen(bits: np.ndarray) -> np.ndarray:
+    """raw bf16 bits -> float64 (exact)."""
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32).astype(
+        np.float64)
+
+
+def small_problem(L=96, Hq=8, Hkv=2, d=64, P=32, seed=0):
+    rng = np.random.default_rng(seed)
+    return dict(
+        Q=bf16_bits(rng.standard_normal((L, Hq, d))),
+        K=bf16_bits(rng.standard_normal((L, Hkv, d))),
+        V=bf16_bits(rng.standard_normal((L, Hkv, d))),
+        G=bf16_bits(rng.standard_normal((L, Hq))),
+        kp=bf16_bits(rng.standard_normal((L, P))),
+        qp=bf16_bits(rng.standard_normal((L, P))),
+    )
+
+
+def lexsort_selection(scores_row: np.ndarray, c: int, k: int) -> np.ndarray:
+    """Textbook selection: numpy lexsort by (score desc, index asc), own block added."""
+    if c <= k - 1:
+        sel = np.arange(c + 1)
+    else:
+        s = scores_row[:c]
+        order = np.lexsort((np.arange(c), -s))
+        sel = np.sort(np.concatenate([order[: k - 1], [c]]))
+    out = np.full(k, -1, dtype=np.int32)
+    out[: len(sel)] = sel
+    return out
+
+
+def sdpa_reference(p, mask: np.ndarray, scale: float):
+    """Library attention: torch SDPA in fp64 with KV heads repeated, times sigmoid(gate)."""
+    Q = torch.from_numpy(widen(p["Q"]))  # [T, Hq, d]
+    K = torch.from_numpy(widen(p["K"]))
+    V = torch.from_numpy(widen(p["V"]))
+    G = torch.from_numpy(widen(p["G"]))
+    Hq, Hkv = Q.shape[1], K.shape[1]
+    rep = Hq // Hkv
+    q = Q.permute(1, 0, 2)
+    k = K.permute(1, 0, 2).repeat_interleave(rep, dim=0)
+    v = V.permute(1, 0, 2).repeat_interleave(rep, dim=0)
+    m = torch.from_numpy(mask)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=m, scale=scale)
+    o = o.permute(1, 0, 2) * torch.sigmoid(G)[:, :, None]
+    return o.numpy()
+
+
+def oracle_full_layer(lib, p, B, k, scale):
+    """Oracle steps 1-4 for every row of a small single-sequence prefill."""
+    L = p["K"].shape[0]
+    t = np.arange(L, dtype=np.int64)
+    kb = oracle.index_build(p["kp"], B, lib=lib)
+    width = max(1, (L - 1) // B)
+    sc = oracle.scores(p["qp"], t, B, kb, width=width, lib=lib)
+    idx = oracle.topk(sc, t, B, k, lib=lib)
+    out, lse = oracle.sparse_attention(p["Q"], t, p["K"], p["V"], p["G"], idx, B, scale, lib=lib)
+    return kb, sc, idx, out, lse
+
+
+# --------------------------------------------------------------------------- index
+def pin_index_b1_identity(lib):
+    """B = 1: every block is one token, so its mean is the token's proxy key, bit for bit."""
+    p = small_problem()
+    kb = oracle.index_build(p["kp"], 1, lib=lib)
+    assert np.array_equal(kb, widen(p["kp"]))
+
+
+def pin_index_closed_form(lib):
+    """kp[s][p] = s + p (exact in bf16 for s+p < 256): block j's mean is first + (n-1)/2 + p,
+    with n = 8 for full blocks and n = 3 for the trailing block of L = 43."""
+    L, P, B = 43, 16, 8
+    vals = np.arange(L)[:, None] + np.arange(P)[None, :]
+    kb = oracle.index_build(bf16_bits(vals), B, lib=lib)
+    assert kb.shape == (6, P)
+    for j in range(6):
+        n = min(B, L - j * B)
+        want = j * B + (n - 1) / 2.0 + np.arange(P)
+        assert np.array_equal(kb[j], want), (j, kb[j], want)
+
+
+# --------------------------------------------------------------------------- scores
+def pin_scores_basis(lib):
+    """qp = unit vector e_p picks column p of kb; only blocks j < floor(t/B) are scored."""
+    P, B = 32, 8
+    rng = np.random.default_rng(3)
+    kb = rng.standard_normal((40, P))
+    t = np.array([0, 7, 8, 15, 16, 100, 319], dtype=np.int64)
+    cols = np.array([0, 5, 31, 2, 17, 9, 30])
+    qp = np.zeros((len(t), P))
+    qp[np.arange(len(t)), cols] = 1.0
+    sc = oracle.scores(bf16_bits(qp), t, B, kb, width=40, lib=lib)
+    for r, (tt, cc) in enumerate(zip(t, cols)):
+        c = tt // B
+        assert np.array_equal(sc[r, :c], kb[:c, cc]), (tt, cc)
+        assert np.all(np.isnan(sc[r, c:])), (tt, "scored a block that is not a complete past block")
+
+
+def pin_scores_bilinear(lib):
+    """score(a*qp1 + b*qp2) = a*score(qp1) + b*score(qp2) with exactly representable weights,
+    and swapping the roles of P coordinates permutes nothing (sum is symmetric)."""
+    P, B = 32, 8
+    rng = np.random.default_rng(5)
+    kb = rng.standard_normal((20, P))
+    q1 = bf16_bits(rng.integers(-4, 5, size=(1, P)).astype(np.float64))
+    q2 = bf16_bits(rng.integers(-4, 5, size=(1, P)).astype(np.float64))
+    q3 = bf16_bits(2.0 * widen(q1) - widen(q2))
+    t = np.array([160], dtype=np.int64)
+    s1 = oracle.scores(q1, t, B, kb, width=20, lib=lib)
+    s2 = oracle.scores(q2, t, B, kb, width=20, lib=lib)
+    s3 = oracle.scores(q3, t, B, kb, width=20, lib=lib)
+    np.testing.assert_allclose(s3, 2 * s1 - s2, rtol=0, atol=1e-12)
+    perm = rng.permutation(P)
+    s4 = oracle.scores(np.ascontiguousarray(q1[:, perm]), t, B, np.ascontiguousarray(kb[:, perm]),
+                       width=20, lib=lib)
+    np.testing.assert_allclose(s4, s1, rtol=0, atol=1e-12)
+    # a non-symmetric kb probe: reversing P on the query alone must change the scores
+    s5 = oracle.scores(np.ascontiguousarray(q1[:, ::-1]), t, B, kb, width=20, lib=lib)
+    dense = widen(q1)[0][::-1] @ kb.T
+    np.testing.assert_allclose(s5[0], dense, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------- top-k
+def pin_topk_lexsort(lib):
+    """Against numpy.lexsort on rows full of exact ties (scores drawn from 5 values)."""
+    B, k = 8, 6
+    rng = np.random.default_rng(7)
+    t = np.arange(0, 400, 3, dtype=np.int64)
+    width = 400 // B
+    sc = rng.integers(0, 5, size=(len(t), width)).astype(np.float64)
+    idx = oracle.topk(sc, t, B, k, lib=lib)
+    for r, tt in enumerate(t):
+        want = lexsort_selection(sc[r], int(tt // B), k)
+        assert np.array_equal(idx[r], want), (tt, idx[r], want)
+
+
+def pin_topk_invariants(lib):
+    """Causal, own block kept, |S| = min(k, c+1), ascending, unique, -1 padding at the end."""
+    rng = np.random.default_rng(11)
+    for B, k in ((8, 4), (8, 16), (1, 8), (1, 1), (8, 1)):
+        t = rng.integers(0, 2000, size=60).astype(np.int64)
+        width = int(t.max()) // B + 1
+        sc = rng.standard_normal((len(t), width))
+        idx = oracle.topk(sc, t, B, k, lib=lib)
+        for r, tt in enumerate(t):
+            c = int(tt // B)
+            row = idx[r]
+            valid = row[row >= 0]
+            assert len(valid) == min(k, c + 1)
+            assert np.all(row[len(valid):] == -1)
+            assert np.all(np.diff(valid) > 0)
+            assert valid[-1] == c
+            assert valid.max() <= c
+
+
+def pin_topk_planted(lib):
+    """End to end through index, scores and top-k: blocks whose proxy keys all equal +u
+    (u = the query's proxy) must be exactly the selection; the rest have kp = -u."""
+    B, k, P = 8, 5, 32
+    nblk = 30
+    L = nblk * B
+    rng = np.random.default_rng(13)
+    u = np.sign(rng.standard_normal(P))
+    planted = np.sort(rng.choice(nblk - 1, size=k - 1, replace=False))
+    kp = np.tile(-u, (L, 1))
+    for j in planted:
+        kp[j * B:(j + 1) * B] = u
+    kbits = bf16_bits(kp)
+    t = np.array([L - 1], dtype=np.int64)
+    kb = oracle.index_build(kbits, B, lib=lib)
+    sc = oracle.scores(bf16_bits(u[None, :]), t, B, kb, width=nblk, lib=lib)
+    idx = oracle.topk(sc, t, B, k, lib=lib)
+    want = np.sort(np.concatenate([planted, [nblk - 1]]))
+    assert np.array_equal(idx[0], want), (idx[0], want)
+
+
+# --------------------------------------------------------------------------- attention
+def _mask_from_selection(idx: np.ndarray, B: int, L: int) -> np.ndarray:
+    """Boolean [T, L] mask built directly from selected block ids (not from the oracle)."""
+    T = idx.shape[0]
+    blk = np.arange(L) // B
+    m = np.zeros((T, L), dtype=bool)
+    for t in range(T):
+        sel = idx[t][idx[t] >= 0]
+        m[t] = np.isin(blk, sel) & (np.arange(L) <= t)
+    return m
+
+
+def pin_attention_dense_sdpa(lib):
+    """k covers every block: sparse attention is dense causal GQA (torch SDPA, fp64)."""
+    p = small_problem()
+    L = p["K"].shape[0]
+    d = p["Q"].shape[2]
+    scale = 1.0 / math.sqrt(d)
+    for B in (8, 1):
+        k = L // B + 1
+        _, _, idx, out, _ = oracle_full_layer(lib, p, B, k, scale)
+        ref = sdpa_reference(p, np.tril(np.ones((L, L), dtype=bool)), scale)
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def pin_attention_sparse_sdpa(lib):
+    """Any selection: equal to SDPA under the block mask built from the selected ids."""
+    p = small_problem(seed=1)
+    L = p["K"].shape[0]
+    d = p["Q"].shape[2]
+    scale = 1.0 / math.sqrt(d)
+    for B, k in ((8, 4), (8, 1), (1, 5), (8, 2)):
+        _, sc, idx, out, _ = oracle_full_layer(lib, p, B, k, scale)
+        ref = sdpa_reference(p, _mask_from_selection(idx, B, L), scale)
+        np.testing.assert_allclose(out, ref, rtol=0, atol=1e-12)
+
+
+def pin_attention_t0_closed_form(lib):
+    """At t = 0 the only token is itself: out[0, h] = sigmoid(G[0, h]) * V[0, g(h)]."""
+    p = small_problem(seed=2)
+    d = p["Q"].shape[2]
+    _, _, _, out, lse = oracle_full_layer(lib, p, 8, 4, 1.0 / math.sqrt(d))
+    V0 = widen(p["V"])[0]
+    G0 = widen(p["G"])[0]
+    Hq, Hkv = p["Q"].shape[1], p["K"].shape[1]
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        np.testing.assert_allclose(out[0, h], V0[g] / (1.0 + np.exp(-G0[h])), rtol=0, atol=1e-15)
+        # one token: lse is its logit
+        z = (widen(p["Q"])[0, h] @ widen(p["K"])[0, g]) / math.sqrt(d)
+        np.testing.assert_allclose(lse[0, h], z, rtol=0, atol=1e-12)
+
+
+def pin_attention_constant_keys(lib):
+    """All keys equal: every logit is the same z0, so lse = z0 + ln|U_t| and the output is
+    sigmoid(G) times the plain mean of V over the attended tokens."""
+    p = small_problem(seed=4)
+    L, Hkv, d = p["K"].shape
+    Hq = p["Q"].shape[1]
+    K = np.broadcast_to(p["K"][:1], p["K"].shape).copy()
+    p = dict(p, K=K)
+    B, k = 8, 3
+    scale = 1.0 / math.sqrt(d)
+    _, _, idx, out, lse = oracle_full_layer(lib, p, B, k, scale)
+    Vw, Qw, Kw, Gw = widen(p["V"]), widen(p["Q"]), widen(K), widen(p["G"])
+    blk = np.arange(L) // B
+    for t in (0, 5, 8, 23, 40, 95):
+        sel = idx[t][idx[t] >= 0]
+        toks = np.nonzero(np.isin(blk, sel) & (np.arange(L) <= t))[0]
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            z0 = scale * (Qw[t, h] @ Kw[0, g])
+            np.testing.assert_allclose(lse[t, h], z0 + math.log(len(toks)), rtol=0, atol=1e-12)
+            want = Vw[toks, g].mean(axis=0) / (1.0 + math.exp(-Gw[t, h]))
+            np.testing.assert_allclose(out[t, h], want, rtol=0, atol=1e-12)
+
+
+def pin_attention_bounds(lib):
+    """Convexity: sigmoid(G)*min_U V <= out <= sigmoid(G)*max_U V, per dimension."""
+    p = small_problem(seed=6)
+    L, Hkv, d = p["K"].shape
+    Hq = p["Q"].shape[1]
+    B, k = 8, 3
+    _, _, idx, out, _ = oracle_full_layer(lib, p, B, k, 1.0 / math.sqrt(d))
+    Vw, Gw = widen(p["V"]), widen(p["G"])
+    blk = np.arange(L) // B
+    for t in range(L):
+        sel = idx[t][idx[t] >= 0]
+        toks = np.nonzero(np.isin(blk, sel) & (np.arange(L) <= t))[0]
+        for h in range(Hq):
+            g = h // (Hq // Hkv)
+            sg = 1.0 / (1.0 + math.exp(-Gw[t, h]))
+            lo = sg * Vw[toks, g].min(axis=0) - 1e-12
+            hi = sg * Vw[toks, g].max(axis=0) + 1e-12
+            assert np.all(out[t, h] >= lo) and np.all(out[t, h] <= hi), (t, h)
+
+
+def pin_coverage_identity(lib):
+    """exp(lse_sparse - lse_dense) is the dense softmax mass on the selected tokens
+    (library softmax over the masked fp64 logits)."""
+    p = small_problem(seed=8)
+    L, Hkv, d = p["K"].shape
+    Hq = p["Q"].shape[1]
+    scale = 1.0 / math.sqrt(d)
+    B = 8
+    _, _, idx_s, _, lse_s = oracle_full_layer(lib, p, B, 3, scale)
+    _, _, _, _, lse_d = oracle_full_layer(lib, p, B, L // B + 1, scale)
+    Q = torch.from_numpy(widen(p["Q"]))
+    K = torch.from_numpy(widen(p["K"]))
+    logits = torch.einsum("thd,sgd->thgs", Q, K)  # all (head, group) pairs
+    mask = _mask_from_selection(idx_s, B, L)
+    causal = np.tril(np.ones((L, L), dtype=bool))
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        z = logits[:, h, g, :] * scale
+        z = z.masked_fill(~torch.from_numpy(causal), float("-inf"))
+        w = torch.softmax(z, dim=-1).numpy()
+        mass = (w * mask).sum(axis=1)
+        np.testing.assert_allclose(np.exp(lse_s[:, h] - lse_d[:, h]), mass, rtol=1e-12, atol=1e-14)
+
+
+ALL_PINS = [
+    pin_index_b1_identity,
+    pin_index_closed_form,
+    pin_scores_basis,
+    pin_scores_bilinear,
+    pin_topk_lexsort,
+    pin_topk_invariants,
+    pin_topk_planted,
+    pin_attention_dense_sdpa,
+    pin_attention_sparse_sdpa,
+    pin_attention_t0_closed_form,
+    pin_attention_constant_keys,
+    pin_attention_bounds,
+    pin_coverage_identity,
+]

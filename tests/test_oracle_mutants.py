@@ -1,0 +1,56 @@
+"""Plant one plausible mistake at a time in a copy of the oracle (on the CPU) and check that
+at least one pin catches it.  This is how the pins are shown to be sensitive: a dropped
+term, a wrong sign or index, or a transposed operand anywhere in the oracle fails one."""
+import os
+import subprocess
+
+import pytest
+
+import oracle
+from pins import ALL_PINS
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "sgqa_oracle.c")
+
+# (name, original text, planted mistake)
+MUTANTS = [
+    ("mean-divides-by-B", "kb[j * P + p] = sum / (double)n;", "kb[j * P + p] = sum / (double)B;"),
+    ("mean-drops-last-token", "for (int64_t s = first; s < first + n; ++s)",
+     "for (int64_t s = first; s < first + n - 1; ++s)"),
+    ("own-block-scored", "return t / B;\n}\n\n/*\n * Block", "return t / B + 1;\n}\n\n/*\n * Block"),
+    ("score-transposed-operand", "acc += widen_bf16(q[p]) * kb[j * P + p];",
+     "acc += widen_bf16(q[p]) * kb[j * P + (P - 1 - p)];"),
+    ("sort-ascending", "if (x->score > y->score)\n        return -1;",
+     "if (x->score > y->score)\n        return 1;"),
+    ("tie-prefers-high-index", "if (x->block < y->block)\n        return -1;",
+     "if (x->block < y->block)\n        return 1;"),
+    ("own-block-not-forced", "            row[count++] = (int32_t)c;\n            qsort",
+     "            qsort"),
+    ("small-case-drops-own", "for (int64_t j = 0; j <= c; ++j)", "for (int64_t j = 0; j < c; ++j)"),
+    ("causal-excludes-self", "if (s <= t)", "if (s < t)"),
+    ("scale-dropped", "z[s] = scale * dot;", "z[s] = dot;"),
+    ("group-map-interleaved", "const int32_t g = h / heads_per_group;",
+     "const int32_t g = h % Hkv;"),
+    ("key-is-value", "widen_bf16(krows[(s * Hkv + g) * d + i])", "widen_bf16(vrows[(s * Hkv + g) * d + i])"),
+    ("gate-sign", "return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(x));"),
+    ("no-normalisation", "out[h * d + i] = (acc / Z) * gate_factor;", "out[h * d + i] = acc * gate_factor;"),
+    ("lse-drops-max", "lse[h] = m + log(Z);", "lse[h] = log(Z);"),
+    ("softmax-no-max-shift", "z[s] = exp(z[s] - m);", "z[s] = exp(z[s]);"),
+]
+
+
+@pytest.mark.parametrize("name,orig,bad", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_pins_catch_planted_mistake(name, orig, bad, tmp_path):
+    src = open(SRC).read()
+    assert src.count(orig) == 1, f"mutation anchor for {name} not unique/present"
+    mut_src = tmp_path / "mutant.c"
+    mut_src.write_text(src.replace(orig, bad))
+    lib_path = str(tmp_path / "libmutant.so")
+    oracle.build(force=True, src=str(mut_src), out=lib_path)
+    lib = oracle.load(lib_path)
+    caught = []
+    for pin in ALL_PINS:
+        try:
+            pin(lib)
+        except (AssertionError, ValueError, FloatingPointError):
+            caught.append(pin.__name__)
+    assert caught, f"no pin caught mutant {name}"
