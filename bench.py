@@ -1,0 +1,285 @@
+"""Benchmark of the Sparse GQA full-attention layer on one MI355X.
+
+A step is one pass of the whole layer over the 131 072-token prefill workload
+(64 query heads, 4 KV heads, d 192, proxy 256, blocks of 8, top-512 blocks):
+sgqa_index_build over every block, sgqa_indexer_topk for every query, and
+sgqa_sparse_attn_prefill.  Inputs are synthetic and already resident in HBM.
+The decode workload (16 sequences x 1 048 576 cached tokens, one query each:
+sgqa_indexer_topk + sgqa_sparse_attn_decode on a prebuilt index) is timed on the
+same line under "decode".  Kernel durations come from HIP events recorded on
+the stream the kernels run on.  The CPU baseline is the fp64 oracle on a sample
+of query rows, timed on this host.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-decode] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "Sparse-GQA prefill tokens/s/layer @128K; decode µs/layer @1M; % roofline"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
+
+
+def log(msg):
+    print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
+
+
+def attended_pairs(q_start: int, T: int, B: int, k: int) -> int:
+    """Sum over queries of |U_t| (tokens attended), from the selection rule."""
+    total = 0
+    for t in range(q_start, q_start + T):
+        c = t // B
+        total += t + 1 if c <= k - 1 else (k - 1) * B + (t % B) + 1
+    return total
+
+
+def scored_pairs(q_start: int, T: int, B: int) -> int:
+    return sum(t // B for t in range(q_start, q_start + T))
+
+
+def bench_prefill(steps: int, warmup: int):
+    import torch
+    from long_context_sparse_18_amd import WORKLOADS, inputs, sgqa
+
+    wl = WORKLOADS[2]
+    s = wl.shape
+    dev = torch.device("cuda:0")
+    log(f"prefill: generating {wl.name}")
+    d = inputs.make_prefill(wl, 2, dev)
+    kb = torch.empty((wl.nblk, s.proxy_dim), dtype=torch.bfloat16, device=dev)
+    idx = torch.empty((wl.T, s.topk_blocks), dtype=torch.int32, device=dev)
+    out = torch.empty_like(d["Q"])
+    lse = torch.empty((wl.T, s.num_q_heads), dtype=torch.float32, device=dev)
+    ws = torch.empty(sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, s, 1, wl.T, wl.L),
+                     dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(s.head_dim)
+    stream = torch.cuda.current_stream(dev)
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def step(marks):
+        marks.append(ev())
+        sgqa.index_build(s, d["kp"], kb, [wl.L], stream=stream)
+        marks.append(ev())
+        sgqa.indexer_topk(s, d["qp"], kb, [wl.q_start], idx, workspace=ws, stream=stream)
+        marks.append(ev())
+        sgqa.sparse_attn_prefill(s, d["Q"], d["K"], d["V"], d["G"], idx, wl.q_start, wl.L, scale,
+                                 out, lse, stream=stream)
+        marks.append(ev())
+
+    for _ in range(warmup):
+        step([])
+    torch.cuda.synchronize()
+    log(f"prefill: timing {steps} steps")
+    marks = []
+    t0 = ev()
+    for _ in range(steps):
+        step(marks)
+    t1 = ev()
+    torch.cuda.synchronize()
+    total_ms = t0.elapsed_time(t1)
+    per = [[marks[4 * i + j].elapsed_time(marks[4 * i + j + 1]) for j in range(3)]
+           for i in range(steps)]
+    build_ms = sum(p[0] for p in per) / steps
+    topk_ms = sum(p[1] for p in per) / steps
+    attn_ms = sum(p[2] for p in per) / steps
+    pairs = attended_pairs(wl.q_start, wl.T, s.block_size, s.topk_blocks)
+    flops = 4 * s.head_dim * s.num_q_heads * pairs
+    gather_bytes = pairs * s.num_kv_heads * s.head_dim * 2 * 2
+    res = dict(wl=wl, total_ms=total_ms, ms_per_step=total_ms / steps, build_ms=build_ms,
+               topk_ms=topk_ms, attn_ms=attn_ms, pairs=pairs, attn_flops=flops,
+               gather_bytes=gather_bytes, data=d, kb=kb, idx=idx)
+    return res
+
+
+def bench_decode(steps: int, warmup: int):
+    import torch
+    from long_context_sparse_18_amd import WORKLOADS, inputs, sgqa
+
+    wl = WORKLOADS[3]
+    s = wl.shape
+    n = wl.nseq
+    dev = torch.device("cuda:0")
+    log("decode: generating 16 x 1M-token caches")
+    d = inputs.make_decode(wl, 3, dev)
+    kb = torch.empty((n, wl.nblk, s.proxy_dim), dtype=torch.bfloat16, device=dev)
+    sgqa.index_build(s, d["kp"], kb, [wl.L] * n)
+    del d["kp"]
+    idx = torch.empty((n, 1, s.topk_blocks), dtype=torch.int32, device=dev)
+    out = torch.empty_like(d["Q"])
+    ws_topk = torch.empty(sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, s, n, 1, wl.L),
+                          dtype=torch.uint8, device=dev)
+    ws_attn = torch.empty(sgqa.workspace_bytes(sgqa.OP_ATTN_DECODE, s, n, 1, wl.L),
+                          dtype=torch.uint8, device=dev)
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(s.head_dim)
+    stream = torch.cuda.current_stream(dev)
+    qp = d["qp"].unsqueeze(1)
+
+    def step():
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        m = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        sgqa.indexer_topk(s, qp, kb, [wl.L - 1] * n, idx, workspace=ws_topk, stream=stream)
+        m.record(stream)
+        sgqa.sparse_attn_decode(s, d["Q"], d["K"], d["V"], d["G"], idx.view(n, -1), [wl.L] * n,
+                                scale, out, workspace=ws_attn, stream=stream)
+        b.record(stream)
+        return a, m, b
+
+    for _ in range(warmup):
+        flush.fill_(1)
+        step()
+    torch.cuda.synchronize()
+    times, t_topk, t_attn = [], [], []
+    for _ in range(steps):
+        flush.fill_(1)   # no step starts with the caches warm
+        a, m, b = step()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+        t_topk.append(a.elapsed_time(m) * 1e3)
+        t_attn.append(m.elapsed_time(b) * 1e3)
+    times.sort()
+    med = times[len(times) // 2]
+    # algorithmic bytes: the whole index scan, the gathered K/V rows, and the small tensors
+    per_seq = ((wl.L - 1) // s.block_size) * s.proxy_dim * 2 \
+        + s.topk_blocks * s.block_size * s.num_kv_heads * s.head_dim * 2 * 2 \
+        + (2 * s.num_q_heads * s.head_dim * 2 + s.proxy_dim * 2 + s.num_q_heads * 2
+           + s.topk_blocks * 4)
+    bytes_total = per_seq * n
+    return dict(us_median=med, us_topk=sorted(t_topk)[len(t_topk) // 2],
+                us_attn=sorted(t_attn)[len(t_attn) // 2], bytes=bytes_total,
+                gbs=bytes_total / (med * 1e-6) / 1e9)
+
+
+def cpu_baseline(pre, rows: int, seed: int = 0):
+    """The fp64 oracle on a sample of query rows of the same prefill workload."""
+    import numpy as np
+    import oracle
+    from long_context_sparse_18_amd.inputs import bits
+
+    wl = pre["wl"]
+    s = wl.shape
+    d = pre["data"]
+    rng = np.random.default_rng(seed)
+    sel_rows = np.sort(rng.choice(wl.T, size=rows, replace=False)).astype(np.int64)
+    import torch
+    rt = torch.from_numpy(sel_rows).to(d["Q"].device)
+    kp = bits(d["kp"])
+    qp = bits(d["qp"].index_select(0, rt))
+    q = bits(d["Q"].index_select(0, rt))
+    g = bits(d["G"].index_select(0, rt))
+    K, V = bits(d["K"]), bits(d["V"])
+    t = sel_rows + wl.q_start
+    lib = oracle.load()
+    t0 = time.perf_counter()
+    kb = oracle.index_build(kp, s.block_size, lib=lib)
+    t1 = time.perf_counter()
+    sc = oracle.scores(qp, t, s.block_size, kb, width=max(1, int(t.max()) // s.block_size), lib=lib)
+    idx = oracle.topk(sc, t, s.block_size, s.topk_blocks, lib=lib)
+    t2 = time.perf_counter()
+    oracle.sparse_attention(q, t, K, V, g, idx, s.block_size, 1.0 / math.sqrt(s.head_dim), lib=lib)
+    t3 = time.perf_counter()
+    per_row = (t3 - t1) / rows
+    full_s = (t1 - t0) + per_row * wl.T
+    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+    return {"value": wl.T / full_s, "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
+            "sample": (f"full index build ({t1 - t0:.2f} s) + {rows} random query rows of the "
+                       f"131072-token prefill (scores+sort {t2 - t1:.2f} s, attention "
+                       f"{t3 - t2:.2f} s), extrapolated to all rows")}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--cpu-rows", type=int, default=192)
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
+        print("bench.py measures one GPU: this layer is not sharded across GPUs here "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from long_context_sparse_18_amd import sgqa
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    if not os.path.exists(sgqa.lib_path()):
+        from long_context_sparse_18_amd import build as _b
+        _b.build()
+    sgqa.load()
+
+    pre = bench_prefill(args.steps, args.warmup)
+    wl = pre["wl"]
+    s = wl.shape
+    tokens_per_s = wl.T / (pre["ms_per_step"] / 1e3)
+    attn_tflops = pre["attn_flops"] / (pre["attn_ms"] / 1e3) / 1e12
+    log(f"prefill: {pre['ms_per_step']:.2f} ms/step (build {pre['build_ms']:.3f}, topk "
+        f"{pre['topk_ms']:.3f}, attn {pre['attn_ms']:.3f}) -> {tokens_per_s:,.0f} tokens/s, "
+        f"attention {attn_tflops:.1f} TFLOP/s")
+    cpu = None
+    if not args.no_cpu:
+        log(f"cpu baseline: oracle on {args.cpu_rows} rows")
+        cpu = cpu_baseline(pre, args.cpu_rows)
+    for key in ("data", "kb", "idx"):
+        pre.pop(key, None)
+    torch.cuda.empty_cache()
+    dec = None
+    if not args.no_decode:
+        dec = bench_decode(max(args.steps, 5), args.warmup)
+        log(f"decode: {dec['us_median']:.1f} us/step (topk {dec['us_topk']:.1f}, attn "
+            f"{dec['us_attn']:.1f}), {dec['gbs']:.0f} GB/s")
+
+    line = {
+        "metric": METRIC,
+        "value": tokens_per_s,
+        "unit": "tokens/s/layer",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "T": wl.T, "L": wl.L, "q_heads": s.num_q_heads,
+                   "kv_heads": s.num_kv_heads, "head_dim": s.head_dim, "proxy_dim": s.proxy_dim,
+                   "block_size": s.block_size, "topk_blocks": s.topk_blocks},
+        "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": None,
+                     "kernel": "k_attn_prefill<192>",
+                     "gather_GBps": pre["gather_bytes"] / (pre["attn_ms"] / 1e3) / 1e9},
+        "cpu_baseline": cpu,
+        "stages_ms": {"index_build": pre["build_ms"], "indexer_topk": pre["topk_ms"],
+                      "sparse_attn_prefill": pre["attn_ms"]},
+        "indexer_share": (pre["build_ms"] + pre["topk_ms"]) / pre["ms_per_step"],
+    }
+    if dec is not None:
+        line["decode"] = {"workload": "decode-1m-x16", "us_per_layer": dec["us_median"],
+                          "us_indexer_topk": dec["us_topk"], "us_attention": dec["us_attn"],
+                          "GBps": dec["gbs"], "hbm_frac": dec["gbs"] / PEAK_HBM_GBS,
+                          "algorithmic_bytes": dec["bytes"]}
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

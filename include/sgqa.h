@@ -1,0 +1,181 @@
+/*
+ * sgqa.h -- C ABI of libsgqa.so, the MI355X (gfx950) Sparse GQA full-attention layer.
+ *
+ * The layer is the full-attention path of StepFun's Step 5 Preview:
+ *   - ai.info "StepFun Details Step 5 Preview's 92-Block Agent Design", section
+ *     "Sparse GQA targets million-token context": relevant historical blocks are
+ *     selected instead of the whole history; tokens are grouped in blocks of 8;
+ *     top-k 4096 tokens.
+ *   - ai4snews "Step 5 Preview bets on depth over width", Interpretation para. 2:
+ *     indexer entries of adjacent history positions are compressed into block
+ *     representations of size 8, cutting indexer and top-k cost 8x.
+ *   - same ai.info page, section "Why StepFun chose 92 transformer blocks": the
+ *     full-attention layers are Gated Grouped-Query Attention.
+ *   - phantomic12 "Step 5 Preview" catalogue entry, config.json and ATTENTION
+ *     SPLIT parts: 64 query heads, 4 KV heads, head_dim 192, max positions
+ *     1048576; sparse_config topk 512 (blocks), proxy_dim 256.
+ *
+ * Conventions shared by every entry point
+ *   - Tensors are dense, row-major, last dimension contiguous.  bf16 values are
+ *     passed as raw 16-bit patterns (sgqa_bf16).  Element strides are in
+ *     elements, not bytes.
+ *   - Device pointers (marked [dev]) must be device memory of the current HIP
+ *     device; host pointers (marked [host]) are read during the call only.
+ *   - Ownership: the caller owns every buffer, including the workspace.  The
+ *     library never allocates, frees or synchronises; all work is enqueued on
+ *     `stream` (a hipStream_t; NULL = the default stream).
+ *   - Errors: every call validates its arguments in plain host code before any
+ *     HIP call and returns a status; SGQA_ERR_HIP reports a failed launch.
+ *     Faults inside kernels surface at the caller's next synchronisation.
+ *     sgqa_last_error() returns a per-thread description of the last failure.
+ *   - Determinism: the same inputs on the same device give bit-identical
+ *     outputs (no floating-point atomics).
+ *   - Positions are int64.  The query at position t has own block c = t / B.
+ *
+ * Supported shapes: heads_per_group = Hq / Hkv in 1..16, Hkv in 1..8,
+ * head_dim in {64, 128, 192}, proxy_dim a multiple of 32 up to 512,
+ * block_size in {1, 2, 4, 8, 16, 32}, 1 <= topk_blocks <= 4096 with
+ * topk_blocks * block_size <= 32768, nseq <= 64.
+ */
+#ifndef SGQA_H
+#define SGQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef uint16_t sgqa_bf16; /* raw bf16 bits */
+
+typedef enum {
+    SGQA_OK = 0,
+    SGQA_ERR_NULL = 1,        /* a required pointer is NULL */
+    SGQA_ERR_SHAPE = 2,       /* sizes, strides or positions are inconsistent */
+    SGQA_ERR_UNSUPPORTED = 3, /* a valid shape this build does not implement */
+    SGQA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
+    SGQA_ERR_HIP = 5          /* a HIP launch failed */
+} sgqa_status;
+
+/* Layer widths.  num_q_heads = Hq, num_kv_heads = Hkv (the pages' attention
+ * groups), head_dim = d, proxy_dim = P, block_size = B, topk_blocks = k
+ * (blocks kept per query, the query's own block included). */
+typedef struct {
+    int32_t num_q_heads;
+    int32_t num_kv_heads;
+    int32_t head_dim;
+    int32_t proxy_dim;
+    int32_t block_size;
+    int32_t topk_blocks;
+} sgqa_dims;
+
+/* Operation ids for sgqa_workspace_bytes. */
+enum { SGQA_OP_INDEXER_TOPK = 1, SGQA_OP_ATTN_DECODE = 2 };
+
+/*
+ * Block compression (ai4snews Interpretation para. 2; ai.info "Sparse GQA
+ * targets million-token context"): for each sequence s and block j in
+ * [blk_begin, min(blk_end, ceil(L_s/B))),
+ *     kb[s][j][:] = mean of kp[s][jB .. min(jB+B, L_s)-1][:]
+ * summed in fp32 and rounded to bf16 (round to nearest even).  A trailing
+ * partial block is the mean of the tokens present.  blk_end < 0 means "to the
+ * last block".  Blocks outside the range are not written, so a decode or
+ * chunked-prefill loop can refresh only the blocks it touched.
+ *   kp        [dev]  [nseq][*][P] bf16, sequence stride kp_seq_stride elements
+ *   kb        [dev]  [nseq][*][P] bf16, sequence stride kb_seq_stride elements
+ *   seq_lens  [host] [nseq] tokens per sequence (L_s >= 0)
+ */
+sgqa_status sgqa_index_build(const sgqa_dims *dims, const sgqa_bf16 *kp, int64_t kp_seq_stride,
+                             sgqa_bf16 *kb, int64_t kb_seq_stride, const int64_t *seq_lens,
+                             int32_t nseq, int64_t blk_begin, int64_t blk_end, void *stream);
+
+/*
+ * Indexer scores and causal top-k (phantomic12 sparse_config: topk 512,
+ * proxy_dim 256; ai.info "Sparse GQA targets million-token context").  For
+ * query i of sequence s at position t = q_start[s] + i, with c = t / B:
+ *     score[j] = sum_p qp[s][i][p] * kb[s][j][p]  for every complete past
+ *                block j < c (bf16 inputs, fp32 accumulation);
+ *     if c <= k-1 the selection is {0..c}; otherwise it is the k-1 highest
+ *     scores (ties to the lower block index) plus the own block c.
+ * idx[s][i][:] lists the selection in ascending block order, padded with -1
+ * to k entries.  sel_scores (optional) holds the fp32 score of each selected
+ * block, +inf for the own block and -inf for padding.
+ *   qp         [dev]  [nseq][T][P] bf16, sequence stride qp_seq_stride elements
+ *   kb         [dev]  [nseq][*][P] bf16 holding at least blocks 0..c-1 of
+ *                      every query, sequence stride kb_seq_stride elements
+ *   q_start    [host] [nseq] position of each sequence's first query (>= 0)
+ *   idx        [dev]  [nseq][T][k] int32
+ *   sel_scores [dev]  [nseq][T][k] fp32, may be NULL
+ *   workspace  [dev]  scratch of workspace_bytes bytes (at least
+ *                      sgqa_workspace_bytes(SGQA_OP_INDEXER_TOPK, ...) with
+ *                      T = 1 rounded up; more lets one launch cover more rows)
+ */
+sgqa_status sgqa_indexer_topk(const sgqa_dims *dims, const sgqa_bf16 *qp, int64_t qp_seq_stride,
+                              const sgqa_bf16 *kb, int64_t kb_seq_stride, const int64_t *q_start,
+                              int32_t nseq, int32_t T, int32_t *idx, float *sel_scores,
+                              void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Gated sparse GQA attention, prefill (ai.info "Why StepFun chose 92
+ * transformer blocks": Gated Grouped-Query Attention; ai4snews Interpretation
+ * para. 2: a sparse attention operator over the selected blocks).  For query
+ * row i at t = q_start + i and head h, with group g = h / (Hq/Hkv), over the
+ * tokens U = { s : s/B in idx[i], s <= t }:
+ *     z_s = softmax_scale * q[i][h] . K[s][g];   a = sum_s softmax(z)_s V[s][g]
+ *     out[i][h] = a * sigmoid(gate[i][h]);      lse[i][h] = log sum_s exp(z_s)
+ * QK^T and PV run on bf16 MFMA with fp32 accumulation; the softmax is fp32
+ * online; probabilities are rounded to bf16 for PV; out is rounded to bf16.
+ * Only the first min(k, c+1) entries of each idx row are read; entries that
+ * are -1 or outside [0, c] are skipped.
+ *   q     [dev] [T][Hq][d] bf16        k_cache, v_cache [dev] [L][Hkv][d] bf16
+ *   gate  [dev] [T][Hq] bf16 logits    idx [dev] [T][k] int32 (as produced above)
+ *   out   [dev] [T][Hq][d] bf16        lse [dev] [T][Hq] fp32, may be NULL
+ * Requires q_start + T <= L.
+ */
+sgqa_status sgqa_sparse_attn_prefill(const sgqa_dims *dims, const sgqa_bf16 *q,
+                                     const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
+                                     const sgqa_bf16 *gate, const int32_t *idx, int64_t q_start,
+                                     int32_t T, int64_t L, float softmax_scale, sgqa_bf16 *out,
+                                     float *lse, void *stream);
+
+/*
+ * Gated sparse GQA attention, decode: one new query per sequence at position
+ * t = cache_lens[s] - 1 (its K/V already appended), same arithmetic as the
+ * prefill call.  The selected tokens are split across workgroups and the
+ * partial softmax states are merged exactly (log-sum-exp) before the gate.
+ *   q      [dev]  [nseq][Hq][d] bf16
+ *   k_cache, v_cache [dev] [nseq][*][Hkv][d] bf16, sequence stride
+ *                  cache_seq_stride elements
+ *   gate   [dev]  [nseq][Hq] bf16       idx [dev] [nseq][k] int32
+ *   cache_lens [host] [nseq], each >= 1
+ *   out    [dev]  [nseq][Hq][d] bf16    lse [dev] [nseq][Hq] fp32, may be NULL
+ *   workspace [dev] at least sgqa_workspace_bytes(SGQA_OP_ATTN_DECODE, ...)
+ */
+sgqa_status sgqa_sparse_attn_decode(const sgqa_dims *dims, const sgqa_bf16 *q,
+                                    const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
+                                    int64_t cache_seq_stride, const sgqa_bf16 *gate,
+                                    const int32_t *idx, const int64_t *cache_lens, int32_t nseq,
+                                    float softmax_scale, sgqa_bf16 *out, float *lse,
+                                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Workspace size in bytes for `op` (SGQA_OP_INDEXER_TOPK or
+ * SGQA_OP_ATTN_DECODE) given nseq sequences of T queries and caches of at
+ * most Lmax tokens.  For the indexer this is the size that lets one pass cover
+ * all rows, capped at 2 GiB; smaller buffers (down to one 64-row pass) also
+ * work.  Returns 0 for invalid arguments.
+ */
+size_t sgqa_workspace_bytes(int op, const sgqa_dims *dims, int32_t nseq, int32_t T, int64_t Lmax);
+
+/* Static description of a status code. */
+const char *sgqa_status_string(sgqa_status status);
+
+/* Per-thread description of the most recent failure ("" if none). */
+const char *sgqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SGQA_H */

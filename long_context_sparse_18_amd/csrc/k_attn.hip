@@ -1,0 +1,382 @@
+// k_attn.hip -- gathered gated GQA attention over the selected blocks (gfx950).
+//
+// ai.info "StepFun Details Step 5 Preview's 92-Block Agent Design", section
+// "Why StepFun chose 92 transformer blocks": the full-attention layers are
+// Gated Grouped-Query Attention; section "Sparse GQA targets million-token
+// context": they attend only to the selected historical blocks.  ai4snews
+// Interpretation para. 2 names a sparse flash-attention operator for this.
+//
+// One wave owns one (query token, KV group): the 16 query heads of the group
+// are the M dimension of v_mfma_f32_16x16x32_bf16, so every gathered K/V row
+// feeds 16 heads.  Per step of 32 token slots (4 blocks of 8):
+//   S^T[slot][head] = K_rows . Q^T   (K rows loaded straight into the A operand)
+//   online softmax in fp32, base-2 domain, per head (= lane % 16)
+//   O^T[d][head]   += V^T . P^T      (V rows staged in LDS, read transposed)
+// The P^T operand is exactly the layout S^T leaves in the registers once the
+// contraction slots are ordered {4q..4q+3, 16+4q..16+4q+3} for lane row q,
+// so no register shuffle is needed between the two products.
+// Prefill: one workgroup per query token, one wave per KV group (the rows of
+// all groups of a token are adjacent in memory).  Decode: the selected blocks
+// of each (sequence, group) are split across workgroups and the partial
+// softmax states are merged exactly afterwards.
+#include <hip/hip_runtime.h>
+
+#include "sgqa_device.hpp"
+#include "sgqa_launch.hpp"
+
+namespace sgqa {
+
+constexpr int kSlots = 32;  // token slots per step
+
+template <int D>
+struct WaveState {
+    f32x4 acc[D / 16];  // acc[mt][i] = O^T[d = 16*mt + 4*q + i][head = lane % 16]
+    float m;            // running max of the base-2 logits of this lane's head
+    float l;            // this lane's share of the denominator, summing the bf16 weights PV uses
+    float l32;          // the same share summing the fp32 weights (for the log-sum-exp)
+};
+
+// Attend one wave's (token, group) over selected entries [e_begin, e_end).
+// Kg/Vg point at element (token 0, group g, dim 0) of the cache; rows are
+// Hkv*D elements apart.  `vs` is this wave's LDS buffer [kSlots][D + 4].
+template <int D>
+__device__ __forceinline__ void attend_range(const uint16_t *__restrict__ Kg,
+                                             const uint16_t *__restrict__ Vg, int Hkv,
+                                             const int32_t *__restrict__ sel, int e_begin,
+                                             int e_end, int64_t t, int64_t c, int B,
+                                             const bf16x8 (&qf)[D / 32], float scale_log2,
+                                             uint16_t *vs, WaveState<D> &st)
+{
+    constexpr int kLd = D + 4;         // LDS row stride in elements (bytes = 8 mod 32)
+    constexpr int kPieces = D / 8;     // 16-byte pieces per row
+    constexpr int kVChunks = D / 16;   // V pieces per lane per step (32 * kPieces / 64)
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    const int64_t row_elems = (int64_t)Hkv * D;
+    const int eps = kSlots / B;  // entries per step
+    const float neg_inf = -__builtin_inff();
+
+    for (int e_base = e_begin; e_base < e_end; e_base += eps) {
+        // Token of slot (lane & 31): clamped load position + validity.
+        int64_t s_ld;
+        bool valid;
+        {
+            const int slot = lane & 31;
+            const int e = e_base + slot / B;
+            const int32_t blk = (e < e_end) ? sel[e] : -1;
+            const int64_t s = (int64_t)blk * B + (slot % B);
+            valid = blk >= 0 && (int64_t)blk <= c && s <= t;
+            s_ld = valid ? s : t;
+        }
+        const uint64_t vmask = __ballot(valid);
+        const int s_lo = (int)(s_ld & 0xffffffff), s_hi = (int)(s_ld >> 32);
+
+        // K rows for the two 16-slot A tiles.
+        u32x4 kv[2][D / 32];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int src = h * 16 + col;
+            const int64_t sk = ((int64_t)(uint32_t)__shfl(s_lo, src)) |
+                               ((int64_t)__shfl(s_hi, src) << 32);
+            const uint16_t *kr = Kg + sk * row_elems + q4 * 8;
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk)
+                kv[h][kk] = load16(kr + kk * 32);
+        }
+        // V pieces: flat piece f = lane + 64*ci covers slot f / kPieces, piece f % kPieces.
+        u32x4 vv[kVChunks];
+#pragma unroll
+        for (int ci = 0; ci < kVChunks; ++ci) {
+            const int f = lane + 64 * ci;
+            const int slot = f / kPieces, piece = f - slot * kPieces;
+            const int64_t sv = ((int64_t)(uint32_t)__shfl(s_lo, slot)) |
+                               ((int64_t)__shfl(s_hi, slot) << 32);
+            vv[ci] = load16(Vg + sv * row_elems + piece * 8);
+        }
+
+        // S^T = K Q^T for slots 0-15 and 16-31.
+        f32x4 sc[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk)
+                sc[h] = mfma_16x16x32(as_bf16x8(kv[h][kk]), qf[kk], sc[h]);
+        }
+
+        // Online softmax (base 2).  Lane holds slots 16h + 4*q4 + r of head col.
+        float x[2][4];
+        float mloc = neg_inf;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int slot = h * 16 + q4 * 4 + r;
+                const bool ok = (vmask >> slot) & 1ull;
+                x[h][r] = ok ? sc[h][r] * scale_log2 : neg_inf;
+                mloc = fmaxf(mloc, x[h][r]);
+            }
+        const float m_new = fmaxf(st.m, max_across_rows(mloc));
+        const bool any = m_new != neg_inf;
+        const float alpha = any ? fast_exp2(st.m - m_new) : 1.0f;
+        float p[2][4];
+        float psum = 0.f, psum32 = 0.f;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const float pe = any ? fast_exp2(x[h][r] - m_new) : 0.f;
+                // normalise by the bf16 weights PV uses, so the output is a convex combination
+                p[h][r] = bf16_bits_to_f32(f32_to_bf16_bits(pe));
+                psum += p[h][r];
+                psum32 += pe;
+            }
+        st.l = st.l * alpha + psum;
+        st.l32 = st.l32 * alpha + psum32;
+        st.m = m_new;
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                st.acc[mt][r] *= alpha;
+        u32x4 pw;
+        pw[0] = pack_bf16x2(p[0][0], p[0][1]);
+        pw[1] = pack_bf16x2(p[0][2], p[0][3]);
+        pw[2] = pack_bf16x2(p[1][0], p[1][1]);
+        pw[3] = pack_bf16x2(p[1][2], p[1][3]);
+        const bf16x8 pf = as_bf16x8(pw);
+
+        // Stage V rows in LDS (row stride kLd elements, 8-byte aligned).
+        __syncthreads();
+#pragma unroll
+        for (int ci = 0; ci < kVChunks; ++ci) {
+            const int f = lane + 64 * ci;
+            const int slot = f / kPieces, piece = f - slot * kPieces;
+            uint2 *dst = reinterpret_cast<uint2 *>(vs + slot * kLd + piece * 8);
+            dst[0] = uint2{vv[ci][0], vv[ci][1]};
+            dst[1] = uint2{vv[ci][2], vv[ci][3]};
+        }
+        __syncthreads();
+
+        // O^T += V^T P^T: A[m = d][k = slot perm(8*q4 + j)], slots 4q4+j (j<4), 16+4q4+j-4.
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) {
+            const uint16_t *vc = vs + mt * 16 + col;
+            u32x4 aw;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int j0 = 2 * jj, j1 = 2 * jj + 1;
+                const int sl0 = j0 < 4 ? q4 * 4 + j0 : 16 + q4 * 4 + (j0 - 4);
+                const int sl1 = j1 < 4 ? q4 * 4 + j1 : 16 + q4 * 4 + (j1 - 4);
+                aw[jj] = (uint32_t)vc[sl0 * kLd] | ((uint32_t)vc[sl1 * kLd] << 16);
+            }
+            st.acc[mt] = mfma_16x16x32(as_bf16x8(aw), pf, st.acc[mt]);
+        }
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void load_q(const uint16_t *__restrict__ qh, int hpg, bf16x8 (&qf)[D / 32])
+{
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (col < hpg)
+            v = load16(qh + (int64_t)col * D + kk * 32 + q4 * 8);
+        qf[kk] = as_bf16x8(v);
+    }
+}
+
+template <int D>
+__device__ __forceinline__ void init_state(WaveState<D> &st)
+{
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt)
+        st.acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m = -__builtin_inff();
+    st.l = 0.f;
+    st.l32 = 0.f;
+}
+
+__device__ __forceinline__ float sigmoid_f32(float x)
+{
+    return 1.0f / (1.0f + fast_exp2(-x * 1.4426950408889634f));
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
+{
+    extern __shared__ __align__(16) uint16_t lds[];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    const int64_t r = (int64_t)a.rows - 1 - blockIdx.x;  // longest rows first
+    const int64_t t = a.q_start + r;
+    const int64_t c = t / a.B;
+    const int nvalid = (int)((c + 1 < a.k) ? c + 1 : a.k);
+    const int g = wave;
+    const int hpg = a.Hq / a.Hkv;
+
+    bf16x8 qf[D / 32];
+    load_q<D>(a.q + (r * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
+    WaveState<D> st;
+    init_state<D>(st);
+    attend_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D, a.Hkv, a.idx + r * a.k, 0, nvalid,
+                    t, c, a.B, qf, a.scale_log2, lds + wave * kSlots * (D + 4), st);
+
+    const float l = sum_across_rows(st.l);
+    const float l32 = sum_across_rows(st.l32);
+    if (col < hpg) {
+        const int h = g * hpg + col;
+        const float inv = 1.0f / l;
+        const float gsig = sigmoid_f32(bf16_bits_to_f32(a.gate[r * a.Hq + h]));
+        uint16_t *o = a.out + (r * a.Hq + h) * D + q4 * 4;
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) {
+            const float f = inv * gsig;
+            uint2 w;
+            w.x = pack_bf16x2(st.acc[mt][0] * f, st.acc[mt][1] * f);
+            w.y = pack_bf16x2(st.acc[mt][2] * f, st.acc[mt][3] * f);
+            *reinterpret_cast<uint2 *>(o + mt * 16) = w;
+        }
+        if (a.lse && q4 == 0)
+            a.lse[r * a.Hq + h] = (st.m + fast_log2(l32)) * 0.6931471805599453f;
+    }
+}
+
+template <int D>
+__global__ __launch_bounds__(512) void k_attn_decode_part(AttnArgs a)
+{
+    extern __shared__ __align__(16) uint16_t lds[];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    const int s = blockIdx.y;
+    const int split = blockIdx.x;
+    const int64_t t = a.qpos.v[s];
+    const int64_t c = t / a.B;
+    const int nvalid = (int)((c + 1 < a.k) ? c + 1 : a.k);
+    const int e0 = split * a.entries_per_split;
+    const int e1 = min(e0 + a.entries_per_split, nvalid);
+    const int g = wave;
+    const int hpg = a.Hq / a.Hkv;
+
+    bf16x8 qf[D / 32];
+    load_q<D>(a.q + ((int64_t)s * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
+    WaveState<D> st;
+    init_state<D>(st);
+    const int64_t base = (int64_t)s * a.cache_seq_stride + (int64_t)g * D;
+    if (e0 < e1)
+        attend_range<D>(a.kc + base, a.vc + base, a.Hkv, a.idx + (int64_t)s * a.k, e0, e1, t, c,
+                        a.B, qf, a.scale_log2, lds + wave * kSlots * (D + 4), st);
+
+    const float l = sum_across_rows(st.l);
+    const float l32 = sum_across_rows(st.l32);
+    if (col < hpg) {
+        const int h = g * hpg + col;
+        const int64_t slot = ((int64_t)s * a.nsplit + split) * a.Hq + h;
+        float *po = a.part_o + slot * D + q4 * 4;
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt)
+            *reinterpret_cast<f32x4 *>(po + mt * 16) = st.acc[mt];
+        if (q4 == 0) {
+            a.part_ml[slot * 3 + 0] = st.m;
+            a.part_ml[slot * 3 + 1] = l;
+            a.part_ml[slot * 3 + 2] = l32;
+        }
+    }
+}
+
+// Exact merge of the split partial states of one (sequence, head), then the gate.
+__global__ __launch_bounds__(64) void k_attn_decode_merge(AttnArgs a)
+{
+    const int s = blockIdx.y, h = blockIdx.x;
+    const int D = a.d;
+    const float neg_inf = -__builtin_inff();
+    const float *ml = a.part_ml + ((int64_t)s * a.nsplit * a.Hq + h) * 3;
+    const int64_t ml_step = (int64_t)a.Hq * 3;
+    float M = neg_inf;
+    for (int i = 0; i < a.nsplit; ++i)
+        M = fmaxf(M, ml[i * ml_step]);
+    float Lsum = 0.f, L32 = 0.f;
+    for (int i = 0; i < a.nsplit; ++i) {
+        const float mi = ml[i * ml_step];
+        if (mi != neg_inf) {
+            const float w = fast_exp2(mi - M);
+            Lsum += ml[i * ml_step + 1] * w;
+            L32 += ml[i * ml_step + 2] * w;
+        }
+    }
+    const float gsig = sigmoid_f32(bf16_bits_to_f32(a.gate[(int64_t)s * a.Hq + h]));
+    const float f = gsig / Lsum;
+    const float *po = a.part_o + ((int64_t)s * a.nsplit * a.Hq + h) * D;
+    const int64_t po_step = (int64_t)a.Hq * D;
+    for (int dd = threadIdx.x; dd < D; dd += 64) {
+        float o = 0.f;
+        for (int i = 0; i < a.nsplit; ++i) {
+            const float mi = ml[i * ml_step];
+            if (mi != neg_inf)
+                o += po[i * po_step + dd] * fast_exp2(mi - M);
+        }
+        a.out[((int64_t)s * a.Hq + h) * D + dd] = (uint16_t)f32_to_bf16_bits(o * f);
+    }
+    if (a.lse && threadIdx.x == 0)
+        a.lse[(int64_t)s * a.Hq + h] = (M + fast_log2(L32)) * 0.6931471805599453f;
+}
+
+void decode_split_plan(int k, int B, int &nsplit, int &entries_per_split)
+{
+    const int eps = kSlots / B;  // entries per 32-slot step
+    int per = (k + 15) / 16;     // aim for 16 splits
+    per = ((per + eps - 1) / eps) * eps;
+    entries_per_split = per;
+    nsplit = (k + per - 1) / per;
+}
+
+template <int D>
+static hipError_t launch_prefill_d(const AttnArgs &a, hipStream_t stream)
+{
+    const size_t lds = (size_t)a.Hkv * kSlots * (D + 4) * sizeof(uint16_t);
+    hipLaunchKernelGGL(k_attn_prefill<D>, dim3((unsigned)a.rows), dim3(64 * a.Hkv), lds, stream, a);
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_decode_d(const AttnArgs &a, hipStream_t stream)
+{
+    const size_t lds = (size_t)a.Hkv * kSlots * (D + 4) * sizeof(uint16_t);
+    hipLaunchKernelGGL(k_attn_decode_part<D>, dim3((unsigned)a.nsplit, (unsigned)a.rows),
+                       dim3(64 * a.Hkv), lds, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_attn_decode_merge, dim3((unsigned)a.Hq, (unsigned)a.rows), dim3(64), 0,
+                       stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream)
+{
+    if (a.rows <= 0)
+        return hipSuccess;
+    switch (a.d) {
+    case 64: return launch_prefill_d<64>(a, stream);
+    case 128: return launch_prefill_d<128>(a, stream);
+    case 192: return launch_prefill_d<192>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream)
+{
+    if (a.rows <= 0)
+        return hipSuccess;
+    switch (a.d) {
+    case 64: return launch_decode_d<64>(a, stream);
+    case 128: return launch_decode_d<128>(a, stream);
+    case 192: return launch_decode_d<192>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+} // namespace sgqa

@@ -1,0 +1,404 @@
+// sgqa_api.cpp -- the C ABI of libsgqa.so: argument validation and dispatch.
+//
+// Every check below is plain host C++ and runs before the first HIP call, so
+// each error path can be exercised on a machine without a GPU.  The entry
+// points and their arithmetic are specified in include/sgqa.h.
+#include "sgqa.h"
+
+#include <stdarg.h>
+#include <stdio.h>
+
+#include <cmath>
+#include <string>
+
+#include "sgqa_launch.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+sgqa_status fail(sgqa_status st, const char *fmt, ...)
+{
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return st;
+}
+
+sgqa_status ok()
+{
+    g_last_error.clear();
+    return SGQA_OK;
+}
+
+bool aligned(const void *p, uintptr_t a)
+{
+    return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+int64_t ceil_div(int64_t a, int64_t b)
+{
+    return (a + b - 1) / b;
+}
+
+int64_t round_up(int64_t a, int64_t b)
+{
+    return ceil_div(a, b) * b;
+}
+
+sgqa_status check_dims(const sgqa_dims *d, bool need_attn, bool need_proxy)
+{
+    if (!d)
+        return fail(SGQA_ERR_NULL, "dims is NULL");
+    if (d->block_size <= 0 || d->topk_blocks <= 0)
+        return fail(SGQA_ERR_SHAPE, "block_size (%d) and topk_blocks (%d) must be positive",
+                    d->block_size, d->topk_blocks);
+    const int B = d->block_size;
+    if (B != 1 && B != 2 && B != 4 && B != 8 && B != 16 && B != 32)
+        return fail(SGQA_ERR_UNSUPPORTED, "block_size %d not in {1,2,4,8,16,32}", B);
+    if (d->topk_blocks > 4096 || (int64_t)d->topk_blocks * B > 32768)
+        return fail(SGQA_ERR_UNSUPPORTED, "topk_blocks %d x block_size %d exceeds 4096 blocks / 32768 tokens",
+                    d->topk_blocks, B);
+    if (need_proxy) {
+        if (d->proxy_dim <= 0)
+            return fail(SGQA_ERR_SHAPE, "proxy_dim %d must be positive", d->proxy_dim);
+        if (d->proxy_dim % 32 != 0 || d->proxy_dim > 512)
+            return fail(SGQA_ERR_UNSUPPORTED, "proxy_dim %d must be a multiple of 32 up to 512",
+                        d->proxy_dim);
+    }
+    if (need_attn) {
+        if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0)
+            return fail(SGQA_ERR_SHAPE, "head counts and head_dim must be positive");
+        if (d->num_q_heads % d->num_kv_heads != 0)
+            return fail(SGQA_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                        d->num_q_heads, d->num_kv_heads);
+        if (d->num_q_heads / d->num_kv_heads > 16 || d->num_kv_heads > 8)
+            return fail(SGQA_ERR_UNSUPPORTED, "need heads per group <= 16 and num_kv_heads <= 8");
+        if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 192)
+            return fail(SGQA_ERR_UNSUPPORTED, "head_dim %d not in {64,128,192}", d->head_dim);
+    }
+    return SGQA_OK;
+}
+
+sgqa_status hip_status(hipError_t e, const char *what)
+{
+    if (e != hipSuccess)
+        return fail(SGQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+    return ok();
+}
+
+struct TopkPlan {
+    int64_t max_cand;  // largest candidate count over all rows
+    int64_t ld;        // score row stride (floats)
+    int32_t nq;        // queries per sequence per pass
+};
+
+TopkPlan topk_plan(const sgqa_dims *d, const int64_t *q_start, int32_t nseq, int32_t T, size_t ws)
+{
+    TopkPlan p{0, 64, 0};
+    int64_t max_pos = 0;
+    for (int s = 0; s < nseq; ++s)
+        max_pos = q_start[s] + T - 1 > max_pos ? q_start[s] + T - 1 : max_pos;
+    p.max_cand = max_pos / d->block_size;
+    p.ld = round_up(p.max_cand > 0 ? p.max_cand : 1, 64);
+    const int64_t row_bytes = p.ld * (int64_t)sizeof(float) * nseq;
+    int64_t nq = (int64_t)(ws / (size_t)row_bytes);
+    if (nq >= T)
+        nq = T;
+    else
+        nq = (nq / 64) * 64;
+    p.nq = (int32_t)nq;
+    return p;
+}
+
+constexpr size_t kIndexerWorkspaceCap = size_t(2) << 30;
+
+} // namespace
+
+extern "C" {
+
+const char *sgqa_status_string(sgqa_status st)
+{
+    switch (st) {
+    case SGQA_OK: return "ok";
+    case SGQA_ERR_NULL: return "null pointer";
+    case SGQA_ERR_SHAPE: return "inconsistent shape";
+    case SGQA_ERR_UNSUPPORTED: return "unsupported shape";
+    case SGQA_ERR_WORKSPACE: return "workspace too small";
+    case SGQA_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+const char *sgqa_last_error(void)
+{
+    return g_last_error.c_str();
+}
+
+size_t sgqa_workspace_bytes(int op, const sgqa_dims *dims, int32_t nseq, int32_t T, int64_t Lmax)
+{
+    if (!dims || nseq <= 0 || nseq > sgqa::kMaxSeq || T < 0 || Lmax < 0)
+        return 0;
+    if (op == SGQA_OP_INDEXER_TOPK) {
+        if (check_dims(dims, false, true) != SGQA_OK)
+            return 0;
+        const int64_t max_cand = Lmax > 0 ? (Lmax - 1) / dims->block_size : 0;
+        const int64_t ld = round_up(max_cand > 0 ? max_cand : 1, 64);
+        const int64_t per_q = ld * (int64_t)sizeof(float) * nseq;
+        const int64_t min_rows = T < 64 ? (T > 0 ? T : 1) : 64;
+        int64_t bytes = per_q * (T > 0 ? T : 1);
+        if ((size_t)bytes > kIndexerWorkspaceCap)
+            bytes = ((int64_t)kIndexerWorkspaceCap / (per_q * 64)) * (per_q * 64);
+        if (bytes < per_q * min_rows)
+            bytes = per_q * min_rows;
+        return (size_t)bytes;
+    }
+    if (op == SGQA_OP_ATTN_DECODE) {
+        if (check_dims(dims, true, false) != SGQA_OK)
+            return 0;
+        int nsplit, eps;
+        sgqa::decode_split_plan(dims->topk_blocks, dims->block_size, nsplit, eps);
+        const size_t slots = (size_t)nseq * nsplit * dims->num_q_heads;
+        return slots * dims->head_dim * sizeof(float) + slots * 3 * sizeof(float);
+    }
+    return 0;
+}
+
+sgqa_status sgqa_index_build(const sgqa_dims *dims, const sgqa_bf16 *kp, int64_t kp_seq_stride,
+                             sgqa_bf16 *kb, int64_t kb_seq_stride, const int64_t *seq_lens,
+                             int32_t nseq, int64_t blk_begin, int64_t blk_end, void *stream)
+{
+    sgqa_status st = check_dims(dims, false, true);
+    if (st != SGQA_OK)
+        return st;
+    if (nseq < 0 || nseq > sgqa::kMaxSeq)
+        return fail(nseq < 0 ? SGQA_ERR_SHAPE : SGQA_ERR_UNSUPPORTED, "nseq %d not in [0, %d]", nseq,
+                    sgqa::kMaxSeq);
+    if (nseq == 0)
+        return ok();
+    if (!kp || !kb || !seq_lens)
+        return fail(SGQA_ERR_NULL, "kp, kb and seq_lens must be non-NULL");
+    if (!aligned(kp, 16) || !aligned(kb, 16))
+        return fail(SGQA_ERR_SHAPE, "kp and kb must be 16-byte aligned");
+    if (blk_begin < 0)
+        return fail(SGQA_ERR_SHAPE, "blk_begin %lld is negative", (long long)blk_begin);
+    const int P = dims->proxy_dim, B = dims->block_size;
+    int64_t max_len = 0;
+    for (int s = 0; s < nseq; ++s) {
+        if (seq_lens[s] < 0)
+            return fail(SGQA_ERR_SHAPE, "seq_lens[%d] = %lld is negative", s, (long long)seq_lens[s]);
+        max_len = seq_lens[s] > max_len ? seq_lens[s] : max_len;
+    }
+    if (nseq > 1) {
+        if (kp_seq_stride < max_len * P || kp_seq_stride % 8 != 0)
+            return fail(SGQA_ERR_SHAPE, "kp_seq_stride %lld must be >= %lld and a multiple of 8",
+                        (long long)kp_seq_stride, (long long)(max_len * P));
+        if (kb_seq_stride < ceil_div(max_len, B) * P || kb_seq_stride % 8 != 0)
+            return fail(SGQA_ERR_SHAPE, "kb_seq_stride %lld must be >= %lld and a multiple of 8",
+                        (long long)kb_seq_stride, (long long)(ceil_div(max_len, B) * P));
+    }
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    for (int s = 0; s < nseq; ++s) {
+        const int64_t nblk = ceil_div(seq_lens[s], B);
+        const int64_t j0 = blk_begin < nblk ? blk_begin : nblk;
+        const int64_t j1 = (blk_end < 0 || blk_end > nblk) ? nblk : blk_end;
+        if (j1 <= j0)
+            continue;
+        hipError_t e = sgqa::launch_index_build(kp + (int64_t)s * kp_seq_stride,
+                                                kb + (int64_t)s * kb_seq_stride, seq_lens[s], P, B,
+                                                j0, j1, hs);
+        if (e != hipSuccess)
+            return hip_status(e, "index_build launch");
+    }
+    return ok();
+}
+
+sgqa_status sgqa_indexer_topk(const sgqa_dims *dims, const sgqa_bf16 *qp, int64_t qp_seq_stride,
+                              const sgqa_bf16 *kb, int64_t kb_seq_stride, const int64_t *q_start,
+                              int32_t nseq, int32_t T, int32_t *idx, float *sel_scores,
+                              void *workspace, size_t workspace_bytes, void *stream)
+{
+    sgqa_status st = check_dims(dims, false, true);
+    if (st != SGQA_OK)
+        return st;
+    if (nseq < 0 || T < 0)
+        return fail(SGQA_ERR_SHAPE, "nseq %d and T %d must be non-negative", nseq, T);
+    if (nseq > sgqa::kMaxSeq)
+        return fail(SGQA_ERR_UNSUPPORTED, "nseq %d exceeds %d", nseq, sgqa::kMaxSeq);
+    if (nseq == 0 || T == 0)
+        return ok();
+    if (!qp || !kb || !q_start || !idx)
+        return fail(SGQA_ERR_NULL, "qp, kb, q_start and idx must be non-NULL");
+    if (!aligned(qp, 16) || !aligned(kb, 16) || !aligned(idx, 4) || !aligned(sel_scores, 4))
+        return fail(SGQA_ERR_SHAPE, "qp and kb must be 16-byte aligned");
+    const int P = dims->proxy_dim;
+    for (int s = 0; s < nseq; ++s)
+        if (q_start[s] < 0)
+            return fail(SGQA_ERR_SHAPE, "q_start[%d] = %lld is negative", s, (long long)q_start[s]);
+    if (nseq > 1 && (qp_seq_stride < (int64_t)T * P || qp_seq_stride % 8 != 0))
+        return fail(SGQA_ERR_SHAPE, "qp_seq_stride %lld must be >= T*P and a multiple of 8",
+                    (long long)qp_seq_stride);
+    if (nseq > 1 && kb_seq_stride % 8 != 0)
+        return fail(SGQA_ERR_SHAPE, "kb_seq_stride must be a multiple of 8");
+    const TopkPlan plan = topk_plan(dims, q_start, nseq, T, workspace ? workspace_bytes : 0);
+    if (!workspace || plan.nq <= 0)
+        return fail(SGQA_ERR_WORKSPACE,
+                    "workspace of %zu bytes cannot hold one pass (need >= %lld bytes)",
+                    workspace ? workspace_bytes : (size_t)0,
+                    (long long)(plan.ld * 4 * nseq * (T < 64 ? T : 64)));
+    if (!aligned(workspace, 16))
+        return fail(SGQA_ERR_SHAPE, "workspace must be 16-byte aligned");
+
+    hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+    sgqa::ScoreArgs sa{};
+    sa.qp = qp;
+    sa.qp_seq_stride = qp_seq_stride;
+    sa.kb = kb;
+    sa.kb_seq_stride = kb_seq_stride;
+    sa.nseq = nseq;
+    sa.P = P;
+    sa.B = dims->block_size;
+    sa.ws = static_cast<float *>(workspace);
+    sa.ld = plan.ld;
+    sgqa::SelectArgs se{};
+    se.ws = sa.ws;
+    se.ld = plan.ld;
+    se.nseq = nseq;
+    se.T = T;
+    se.B = dims->block_size;
+    se.k = dims->topk_blocks;
+    se.idx = idx;
+    se.sel_scores = sel_scores;
+    for (int s = 0; s < nseq; ++s)
+        sa.q_start.v[s] = se.q_start.v[s] = q_start[s];
+    for (int32_t t0 = 0; t0 < T; t0 += plan.nq) {
+        const int32_t nq = (T - t0) < plan.nq ? (T - t0) : plan.nq;
+        int64_t max_pos = 0;
+        for (int s = 0; s < nseq; ++s)
+            max_pos = q_start[s] + t0 + nq - 1 > max_pos ? q_start[s] + t0 + nq - 1 : max_pos;
+        sa.t0 = se.t0 = t0;
+        sa.nq = se.nq = nq;
+        sa.max_cand = se.max_cand = max_pos / dims->block_size;
+        hipError_t e = sgqa::launch_scores(sa, hs);
+        if (e != hipSuccess)
+            return hip_status(e, "indexer scores launch");
+        e = sgqa::launch_select(se, hs);
+        if (e != hipSuccess)
+            return hip_status(e, "top-k select launch");
+    }
+    return ok();
+}
+
+sgqa_status sgqa_sparse_attn_prefill(const sgqa_dims *dims, const sgqa_bf16 *q,
+                                     const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
+                                     const sgqa_bf16 *gate, const int32_t *idx, int64_t q_start,
+                                     int32_t T, int64_t L, float softmax_scale, sgqa_bf16 *out,
+                                     float *lse, void *stream)
+{
+    sgqa_status st = check_dims(dims, true, false);
+    if (st != SGQA_OK)
+        return st;
+    if (T < 0 || q_start < 0 || L < 0)
+        return fail(SGQA_ERR_SHAPE, "T, q_start and L must be non-negative");
+    if (q_start + T > L)
+        return fail(SGQA_ERR_SHAPE, "q_start + T = %lld exceeds L = %lld", (long long)(q_start + T),
+                    (long long)L);
+    if (!std::isfinite(softmax_scale))
+        return fail(SGQA_ERR_SHAPE, "softmax_scale must be finite");
+    if (T == 0)
+        return ok();
+    if (!q || !k_cache || !v_cache || !gate || !idx || !out)
+        return fail(SGQA_ERR_NULL, "q, k_cache, v_cache, gate, idx and out must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 8) ||
+        !aligned(idx, 4) || !aligned(lse, 4) || !aligned(gate, 2))
+        return fail(SGQA_ERR_SHAPE, "q, k_cache, v_cache must be 16-byte and out 8-byte aligned");
+    sgqa::AttnArgs a{};
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.gate = gate;
+    a.idx = idx;
+    a.q_start = q_start;
+    a.rows = T;
+    a.Hq = dims->num_q_heads;
+    a.Hkv = dims->num_kv_heads;
+    a.d = dims->head_dim;
+    a.B = dims->block_size;
+    a.k = dims->topk_blocks;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.out = out;
+    a.lse = lse;
+    return hip_status(sgqa::launch_attn_prefill(a, reinterpret_cast<hipStream_t>(stream)),
+                      "sparse_attn_prefill launch");
+}
+
+sgqa_status sgqa_sparse_attn_decode(const sgqa_dims *dims, const sgqa_bf16 *q,
+                                    const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
+                                    int64_t cache_seq_stride, const sgqa_bf16 *gate,
+                                    const int32_t *idx, const int64_t *cache_lens, int32_t nseq,
+                                    float softmax_scale, sgqa_bf16 *out, float *lse,
+                                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    sgqa_status st = check_dims(dims, true, false);
+    if (st != SGQA_OK)
+        return st;
+    if (nseq < 0)
+        return fail(SGQA_ERR_SHAPE, "nseq %d is negative", nseq);
+    if (nseq > sgqa::kMaxSeq)
+        return fail(SGQA_ERR_UNSUPPORTED, "nseq %d exceeds %d", nseq, sgqa::kMaxSeq);
+    if (!std::isfinite(softmax_scale))
+        return fail(SGQA_ERR_SHAPE, "softmax_scale must be finite");
+    if (nseq == 0)
+        return ok();
+    if (!q || !k_cache || !v_cache || !gate || !idx || !out || !cache_lens)
+        return fail(SGQA_ERR_NULL, "q, caches, gate, idx, cache_lens and out must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 2) ||
+        !aligned(idx, 4) || !aligned(lse, 4) || !aligned(gate, 2))
+        return fail(SGQA_ERR_SHAPE, "q and caches must be 16-byte aligned");
+    const int64_t row = (int64_t)dims->num_kv_heads * dims->head_dim;
+    int64_t max_len = 0;
+    for (int s = 0; s < nseq; ++s) {
+        if (cache_lens[s] < 1)
+            return fail(SGQA_ERR_SHAPE, "cache_lens[%d] = %lld must be >= 1", s,
+                        (long long)cache_lens[s]);
+        max_len = cache_lens[s] > max_len ? cache_lens[s] : max_len;
+    }
+    if (nseq > 1 && (cache_seq_stride < max_len * row || cache_seq_stride % 8 != 0))
+        return fail(SGQA_ERR_SHAPE, "cache_seq_stride %lld must be >= %lld and a multiple of 8",
+                    (long long)cache_seq_stride, (long long)(max_len * row));
+    const size_t need = sgqa_workspace_bytes(SGQA_OP_ATTN_DECODE, dims, nseq, 1, max_len);
+    if (!workspace || workspace_bytes < need)
+        return fail(SGQA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16))
+        return fail(SGQA_ERR_SHAPE, "workspace must be 16-byte aligned");
+    sgqa::AttnArgs a{};
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.cache_seq_stride = cache_seq_stride;
+    a.gate = gate;
+    a.idx = idx;
+    for (int s = 0; s < nseq; ++s)
+        a.qpos.v[s] = cache_lens[s] - 1;
+    a.rows = nseq;
+    a.Hq = dims->num_q_heads;
+    a.Hkv = dims->num_kv_heads;
+    a.d = dims->head_dim;
+    a.B = dims->block_size;
+    a.k = dims->topk_blocks;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.out = out;
+    a.lse = lse;
+    sgqa::decode_split_plan(a.k, a.B, a.nsplit, a.entries_per_split);
+    const size_t slots = (size_t)nseq * a.nsplit * a.Hq;
+    a.part_o = static_cast<float *>(workspace);
+    a.part_ml = a.part_o + slots * a.d;
+    return hip_status(sgqa::launch_attn_decode(a, reinterpret_cast<hipStream_t>(stream)),
+                      "sparse_attn_decode launch");
+}
+
+} // extern "C"

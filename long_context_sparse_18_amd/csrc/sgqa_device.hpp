@@ -1,0 +1,128 @@
+// sgqa_device.hpp -- device helpers shared by the gfx950 kernels of libsgqa.
+//
+// Wave64 primitives, bf16 packing with round-to-nearest-even, the CDNA4 bf16
+// MFMA operand types, and the order-preserving float key used by the top-k.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgqa {
+
+constexpr int kWave = 64;
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;  // MFMA A/B operand (8 x bf16)
+typedef __attribute__((ext_vector_type(4))) float f32x4;    // 16x16 MFMA accumulator slice
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4;
+
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t h)
+{
+    return __uint_as_float(h << 16);
+}
+
+// Round a finite fp32 to bf16 (nearest, ties to even).  NaN stays NaN.
+__device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return (u >> 16) | 0x40u;
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
+{
+    return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v)
+{
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+__device__ __forceinline__ u32x4 load16(const void *p)
+{
+    return *reinterpret_cast<const u32x4 *>(p);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float fast_exp2(float x)
+{
+    return __builtin_amdgcn_exp2f(x);
+}
+
+__device__ __forceinline__ float fast_log2(float x)
+{
+    return __builtin_amdgcn_logf(x);
+}
+
+// Order-preserving map fp32 -> u32: a > b as floats <=> key(a) > key(b).
+// -0.0 is folded onto +0.0 so equal scores get equal keys.
+__device__ __forceinline__ uint32_t score_key(float f)
+{
+    uint32_t u = __float_as_uint(f == 0.0f ? 0.0f : f);
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k)
+{
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7fffffffu) : ~k;
+    return __uint_as_float(u);
+}
+
+// Butterfly reductions across the four 16-lane rows of a wave (lanes l, l^16, l^32, l^48).
+__device__ __forceinline__ float max_across_rows(float v)
+{
+    v = fmaxf(v, __shfl_xor(v, 16));
+    v = fmaxf(v, __shfl_xor(v, 32));
+    return v;
+}
+
+__device__ __forceinline__ float sum_across_rows(float v)
+{
+    v += __shfl_xor(v, 16);
+    v += __shfl_xor(v, 32);
+    return v;
+}
+
+// Inclusive prefix sum of an int across a 64-lane wave.
+__device__ __forceinline__ int wave_inclusive_scan(int v)
+{
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        int n = __shfl_up(v, o);
+        if (lane >= o)
+            v += n;
+    }
+    return v;
+}
+
+// Exclusive prefix sum over a workgroup of NT threads; returns the prefix of
+// this thread and writes the workgroup total.  `scratch` holds NT/64 ints.
+template <int NT>
+__device__ __forceinline__ int block_exclusive_scan(int v, int *scratch, int &total)
+{
+    constexpr int NW = NT / 64;
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int inc = wave_inclusive_scan(v);
+    if (lane == 63)
+        scratch[w] = inc;
+    __syncthreads();
+    int before = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < NW; ++i) {
+        int s = scratch[i];
+        before += (i < w) ? s : 0;
+        tot += s;
+    }
+    __syncthreads();
+    total = tot;
+    return before + inc - v;
+}
+
+} // namespace sgqa

@@ -1,0 +1,82 @@
+// sgqa_launch.hpp -- internal launchers behind the C ABI (arguments already validated).
+#pragma once
+
+#include <hip/hip_runtime_api.h>
+#include <stdint.h>
+
+namespace sgqa {
+
+constexpr int kMaxSeq = 64;
+
+// Per-sequence positions passed by value in the kernel arguments.
+struct SeqPositions {
+    int64_t v[kMaxSeq];
+};
+
+// Block compression of one sequence: kb[j] = mean(kp[jB .. min(jB+B, L)-1]) for j in [j0, j1).
+hipError_t launch_index_build(const uint16_t *kp, uint16_t *kb, int64_t L, int P, int B,
+                              int64_t j0, int64_t j1, hipStream_t stream);
+
+// Indexer scores for queries [t0, t0+nq) of every sequence into ws rows
+// (row = s*nq + i, row stride ld floats); only blocks j < (q_start[s]+i)/B are written.
+struct ScoreArgs {
+    const uint16_t *qp;
+    int64_t qp_seq_stride;
+    const uint16_t *kb;
+    int64_t kb_seq_stride;
+    SeqPositions q_start;
+    int32_t nseq;
+    int32_t t0;
+    int32_t nq;
+    int32_t P;
+    int32_t B;
+    int64_t max_cand;  // largest candidate count over the rows of this pass
+    float *ws;
+    int64_t ld;
+};
+hipError_t launch_scores(const ScoreArgs &a, hipStream_t stream);
+
+// Causal top-k of every row of a score pass (see sgqa_indexer_topk).
+struct SelectArgs {
+    const float *ws;
+    int64_t ld;
+    SeqPositions q_start;
+    int32_t nseq;
+    int32_t t0;
+    int32_t nq;
+    int32_t T;
+    int32_t B;
+    int32_t k;
+    int64_t max_cand;
+    int32_t *idx;
+    float *sel_scores;
+};
+hipError_t launch_select(const SelectArgs &a, hipStream_t stream);
+
+struct AttnArgs {
+    const uint16_t *q;       // [rows][Hq][d]
+    const uint16_t *kc;      // K cache base of sequence 0
+    const uint16_t *vc;      // V cache base of sequence 0
+    int64_t cache_seq_stride;  // elements, decode only
+    const uint16_t *gate;    // [rows][Hq]
+    const int32_t *idx;      // [rows][k]
+    int64_t q_start;         // prefill: position of row 0
+    SeqPositions qpos;       // decode: query position per sequence
+    int32_t rows;            // prefill: T; decode: nseq
+    int32_t Hq, Hkv, d, B, k;
+    float scale_log2;        // softmax_scale * log2(e)
+    uint16_t *out;
+    float *lse;
+    // decode split-K partials
+    float *part_o;           // [nseq][nsplit][Hq][d]
+    float *part_ml;          // [nseq][nsplit][Hq][3]: max, bf16-weight sum, fp32-weight sum
+    int32_t nsplit;
+    int32_t entries_per_split;
+};
+hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream);
+
+// Decode split-K geometry for k selected entries of B tokens.
+void decode_split_plan(int k, int B, int &nsplit, int &entries_per_split);
+
+} // namespace sgqa

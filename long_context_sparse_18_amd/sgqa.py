@@ -1,0 +1,172 @@
+"""Thin ctypes binding of libsgqa.so (argument marshalling only).
+
+Each function has the name of the C entry point without the ``sgqa_`` prefix
+and takes torch device tensors; every step of the layer runs in the library's
+HIP kernels.  PyTorch supplies device memory and the current stream.  If the
+library is not built the first call raises: there is no CPU fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+from .configs import LayerShape
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsgqa.so")
+_lib = None
+
+OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
+OP_INDEXER_TOPK = 1
+OP_ATTN_DECODE = 2
+
+EXPORTS = ("sgqa_index_build", "sgqa_indexer_topk", "sgqa_sparse_attn_prefill",
+           "sgqa_sparse_attn_decode", "sgqa_workspace_bytes", "sgqa_status_string",
+           "sgqa_last_error")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("num_q_heads", ctypes.c_int32), ("num_kv_heads", ctypes.c_int32),
+                ("head_dim", ctypes.c_int32), ("proxy_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("topk_blocks", ctypes.c_int32)]
+
+    @classmethod
+    def of(cls, s: LayerShape) -> "Dims":
+        return cls(s.num_q_heads, s.num_kv_heads, s.head_dim, s.proxy_dim, s.block_size,
+                   s.topk_blocks)
+
+
+class SgqaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(msg)
+        self.status = status
+
+
+def lib_path() -> str:
+    return _LIB_PATH
+
+
+def load():
+    """Load libsgqa.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is missing: build it with __graft_entry__.build()")
+    lib = ctypes.CDLL(_LIB_PATH)
+    p, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    dp = ctypes.POINTER(Dims)
+    st = ctypes.c_int
+    lib.sgqa_index_build.restype = st
+    lib.sgqa_index_build.argtypes = [dp, p, i64, p, i64, p, i32, i64, i64, p]
+    lib.sgqa_indexer_topk.restype = st
+    lib.sgqa_indexer_topk.argtypes = [dp, p, i64, p, i64, p, i32, i32, p, p, p, sz, p]
+    lib.sgqa_sparse_attn_prefill.restype = st
+    lib.sgqa_sparse_attn_prefill.argtypes = [dp, p, p, p, p, p, i64, i32, i64, ctypes.c_float, p,
+                                             p, p]
+    lib.sgqa_sparse_attn_decode.restype = st
+    lib.sgqa_sparse_attn_decode.argtypes = [dp, p, p, p, i64, p, p, p, i32, ctypes.c_float, p, p,
+                                            p, sz, p]
+    lib.sgqa_workspace_bytes.restype = sz
+    lib.sgqa_workspace_bytes.argtypes = [ctypes.c_int, dp, i32, i32, i64]
+    lib.sgqa_status_string.restype = ctypes.c_char_p
+    lib.sgqa_status_string.argtypes = [ctypes.c_int]
+    lib.sgqa_last_error.restype = ctypes.c_char_p
+    lib.sgqa_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def check(status: int):
+    if status != OK:
+        lib = load()
+        raise SgqaError(status, f"{lib.sgqa_status_string(status).decode()}: "
+                                f"{lib.sgqa_last_error().decode()}")
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, ref: torch.Tensor):
+    if stream is None:
+        stream = torch.cuda.current_stream(ref.device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _i64_array(vals):
+    vals = [int(v) for v in vals]
+    return (ctypes.c_int64 * max(1, len(vals)))(*vals)
+
+
+def _need_cuda(*ts):
+    for t in ts:
+        if t is not None and not t.is_cuda:
+            raise ValueError("libsgqa takes device tensors")
+
+
+def workspace_bytes(op: int, shape: LayerShape, nseq: int, T: int, Lmax: int) -> int:
+    d = Dims.of(shape)
+    return int(load().sgqa_workspace_bytes(op, ctypes.byref(d), nseq, T, Lmax))
+
+
+def index_build(shape: LayerShape, kp: torch.Tensor, kb: torch.Tensor, seq_lens,
+                blk_begin: int = 0, blk_end: int = -1, stream=None):
+    """kp [nseq, Lmax, P] (or [L, P]) -> kb [nseq, nblk, P] (or [nblk, P]), bf16."""
+    _need_cuda(kp, kb)
+    kp3 = kp if kp.dim() == 3 else kp.unsqueeze(0)
+    kb3 = kb if kb.dim() == 3 else kb.unsqueeze(0)
+    d = Dims.of(shape)
+    seq_lens = list(seq_lens)
+    check(load().sgqa_index_build(ctypes.byref(d), _ptr(kp3), kp3.stride(0), _ptr(kb3),
+                                  kb3.stride(0), _i64_array(seq_lens), len(seq_lens), blk_begin,
+                                  blk_end, _stream(stream, kp)))
+
+
+def indexer_topk(shape: LayerShape, qp: torch.Tensor, kb: torch.Tensor, q_start, idx: torch.Tensor,
+                 sel_scores: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                 stream=None):
+    """qp [nseq, T, P] (or [T, P]), kb [nseq, nblk, P] -> idx [nseq, T, k] int32."""
+    _need_cuda(qp, kb, idx, sel_scores, workspace)
+    qp3 = qp if qp.dim() == 3 else qp.unsqueeze(0)
+    kb3 = kb if kb.dim() == 3 else kb.unsqueeze(0)
+    q_start = list(q_start)
+    nseq, T = qp3.shape[0], qp3.shape[1]
+    if workspace is None:
+        lmax = max(q_start) + T
+        workspace = torch.empty(workspace_bytes(OP_INDEXER_TOPK, shape, nseq, T, lmax),
+                                dtype=torch.uint8, device=qp.device)
+    d = Dims.of(shape)
+    check(load().sgqa_indexer_topk(ctypes.byref(d), _ptr(qp3), qp3.stride(0), _ptr(kb3),
+                                   kb3.stride(0), _i64_array(q_start), nseq, T, _ptr(idx),
+                                   _ptr(sel_scores), _ptr(workspace), workspace.numel(),
+                                   _stream(stream, qp)))
+
+
+def sparse_attn_prefill(shape: LayerShape, q, k_cache, v_cache, gate, idx, q_start: int, L: int,
+                        softmax_scale: float, out, lse=None, stream=None):
+    _need_cuda(q, k_cache, v_cache, gate, idx, out, lse)
+    d = Dims.of(shape)
+    check(load().sgqa_sparse_attn_prefill(ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                          _ptr(gate), _ptr(idx), q_start, q.shape[0], L,
+                                          softmax_scale, _ptr(out), _ptr(lse), _stream(stream, q)))
+
+
+def sparse_attn_decode(shape: LayerShape, q, k_cache, v_cache, gate, idx, cache_lens,
+                       softmax_scale: float, out, lse=None, workspace=None, stream=None):
+    """q [nseq, Hq, d]; caches [nseq, Lmax, Hkv, d]; idx [nseq, k]; one query per sequence."""
+    _need_cuda(q, k_cache, v_cache, gate, idx, out, lse, workspace)
+    cache_lens = list(cache_lens)
+    nseq = len(cache_lens)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(OP_ATTN_DECODE, shape, nseq, 1, max(cache_lens)),
+                                dtype=torch.uint8, device=q.device)
+    d = Dims.of(shape)
+    check(load().sgqa_sparse_attn_decode(ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                         k_cache.stride(0), _ptr(gate), _ptr(idx),
+                                         _i64_array(cache_lens), nseq, softmax_scale, _ptr(out),
+                                         _ptr(lse), _ptr(workspace), workspace.numel(),
+                                         _stream(stream, q)))

@@ -1,0 +1,162 @@
+"""The C-ABI library loads, exports every symbol the header declares, and rejects bad
+arguments in host code before any HIP call (runs without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_sparse_18_amd import REAL, TINY, sgqa
+from long_context_sparse_18_amd.configs import with_selection
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgqa.h")
+
+FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sgqa_[a-z_]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = sgqa.load()
+    names = declared_functions()
+    assert set(names) == set(sgqa.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    lib = sgqa.load()
+    for st in range(6):
+        assert lib.sgqa_status_string(st)
+    assert lib.sgqa_status_string(99) == b"unknown status"
+
+
+def dims(**kw):
+    s = sgqa.Dims.of(REAL)
+    for k, v in kw.items():
+        setattr(s, k, v)
+    return s
+
+
+def call_prefill(d, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, g=FAKE, idx=FAKE, q_start=0, T=16, L=16, scale=0.07, out=FAKE,
+             lse=None)
+    a.update(kw)
+    return sgqa.load().sgqa_sparse_attn_prefill(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"],
+                                                a["idx"], a["q_start"], a["T"], a["L"], a["scale"],
+                                                a["out"], a["lse"], None)
+
+
+@pytest.mark.parametrize("kw,want", [
+    (dict(num_kv_heads=3), sgqa.ERR_SHAPE),           # 64 % 3 != 0
+    (dict(num_kv_heads=2), sgqa.ERR_UNSUPPORTED),     # 32 heads per group
+    (dict(head_dim=96), sgqa.ERR_UNSUPPORTED),
+    (dict(head_dim=0), sgqa.ERR_SHAPE),
+    (dict(block_size=3), sgqa.ERR_UNSUPPORTED),
+    (dict(block_size=0), sgqa.ERR_SHAPE),
+    (dict(topk_blocks=0), sgqa.ERR_SHAPE),
+    (dict(topk_blocks=4097), sgqa.ERR_UNSUPPORTED),
+    (dict(topk_blocks=2048, block_size=32), sgqa.ERR_UNSUPPORTED),  # 65536 tokens
+])
+def test_prefill_rejects_bad_dims(kw, want):
+    assert call_prefill(dims(**kw)) == want
+
+
+def test_prefill_rejects_bad_sizes_and_pointers():
+    d = dims()
+    assert call_prefill(d, q_start=10, T=16, L=20) == sgqa.ERR_SHAPE
+    assert call_prefill(d, T=-1) == sgqa.ERR_SHAPE
+    assert call_prefill(d, q=None) == sgqa.ERR_NULL
+    assert call_prefill(d, out=None) == sgqa.ERR_NULL
+    assert call_prefill(d, q=ctypes.c_void_p((1 << 20) + 2)) == sgqa.ERR_SHAPE  # misaligned
+    assert call_prefill(d, scale=float("inf")) == sgqa.ERR_SHAPE
+    assert call_prefill(d, T=0) == sgqa.OK  # nothing to do, no HIP call
+    assert sgqa.load().sgqa_last_error() == b""
+    assert call_prefill(d, q_start=10, T=16, L=20) == sgqa.ERR_SHAPE
+    assert b"exceeds L" in sgqa.load().sgqa_last_error()
+
+
+def test_null_dims():
+    lib = sgqa.load()
+    assert lib.sgqa_sparse_attn_prefill(None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 0.1, FAKE,
+                                        None, None) == sgqa.ERR_NULL
+
+
+def test_indexer_validation():
+    lib = sgqa.load()
+    d = dims()
+    qs = (ctypes.c_int64 * 2)(0, 0)
+
+    def call(qp=FAKE, kb=FAKE, q_start=qs, nseq=1, T=64, idx=FAKE, ws=FAKE, wsb=1 << 30,
+             qp_stride=64 * 256, d=d):
+        return lib.sgqa_indexer_topk(ctypes.byref(d), qp, qp_stride, kb, 1 << 20, q_start, nseq, T,
+                                     idx, None, ws, wsb, None)
+
+    assert call(qp=None) == sgqa.ERR_NULL
+    assert call(idx=None) == sgqa.ERR_NULL
+    assert call(q_start=None) == sgqa.ERR_NULL
+    assert call(T=-1) == sgqa.ERR_SHAPE
+    assert call(nseq=65) == sgqa.ERR_UNSUPPORTED
+    assert call(ws=None) == sgqa.ERR_WORKSPACE
+    assert call(wsb=16) == sgqa.ERR_WORKSPACE
+    assert call(nseq=2, qp_stride=100) == sgqa.ERR_SHAPE
+    neg = (ctypes.c_int64 * 1)(-5)
+    assert call(q_start=neg) == sgqa.ERR_SHAPE
+    bad = dims(proxy_dim=48)
+    assert call(d=bad) == sgqa.ERR_UNSUPPORTED
+    assert call(T=0) == sgqa.OK
+
+
+def test_index_build_validation():
+    lib = sgqa.load()
+    d = dims()
+    lens = (ctypes.c_int64 * 2)(1024, 1024)
+    assert lib.sgqa_index_build(ctypes.byref(d), None, 0, FAKE, 0, lens, 1, 0, -1, None) == sgqa.ERR_NULL
+    assert lib.sgqa_index_build(ctypes.byref(d), FAKE, 0, FAKE, 0, None, 1, 0, -1, None) == sgqa.ERR_NULL
+    assert lib.sgqa_index_build(ctypes.byref(d), FAKE, 0, FAKE, 0, lens, 1, -1, -1, None) == sgqa.ERR_SHAPE
+    # two sequences need strides that separate them
+    assert lib.sgqa_index_build(ctypes.byref(d), FAKE, 10, FAKE, 1 << 20, lens, 2, 0, -1, None) == sgqa.ERR_SHAPE
+    assert lib.sgqa_index_build(ctypes.byref(d), FAKE, 1 << 20, FAKE, 8, lens, 2, 0, -1, None) == sgqa.ERR_SHAPE
+    neg = (ctypes.c_int64 * 1)(-1)
+    assert lib.sgqa_index_build(ctypes.byref(d), FAKE, 0, FAKE, 0, neg, 1, 0, -1, None) == sgqa.ERR_SHAPE
+    assert lib.sgqa_index_build(ctypes.byref(d), FAKE, 0, FAKE, 0, lens, 0, 0, -1, None) == sgqa.OK
+
+
+def test_decode_validation():
+    lib = sgqa.load()
+    d = dims()
+    lens = (ctypes.c_int64 * 2)(1 << 20, 1 << 20)
+    need = lib.sgqa_workspace_bytes(sgqa.OP_ATTN_DECODE, ctypes.byref(d), 2, 1, 1 << 20)
+    assert need > 0
+
+    def call(lens=lens, nseq=2, stride=(1 << 20) * 4 * 192, ws=FAKE, wsb=need, q=FAKE):
+        return lib.sgqa_sparse_attn_decode(ctypes.byref(d), q, FAKE, FAKE, stride, FAKE, FAKE, lens,
+                                           nseq, 0.07, FAKE, None, ws, wsb, None)
+
+    assert call(q=None) == sgqa.ERR_NULL
+    assert call(lens=None) == sgqa.ERR_NULL
+    assert call(stride=100) == sgqa.ERR_SHAPE
+    assert call(wsb=need - 1) == sgqa.ERR_WORKSPACE
+    assert call(ws=None) == sgqa.ERR_WORKSPACE
+    zero = (ctypes.c_int64 * 1)(0)
+    assert call(lens=zero, nseq=1) == sgqa.ERR_SHAPE
+    assert call(nseq=65) == sgqa.ERR_UNSUPPORTED
+    assert call(nseq=0) == sgqa.OK
+
+
+def test_workspace_sizes():
+    # full pass for a 32K prefill: 32768 rows x 4096 candidates (ld 4096) x 4 B = 512 MiB
+    assert sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, REAL, 1, 32768, 32768) == 32768 * 4096 * 4
+    # capped at 2 GiB, in whole 64-row passes, for the 128K prefill
+    big = sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, REAL, 1, 131072, 131072)
+    assert big <= 2 << 30 and big % (16384 * 4 * 64) == 0
+    # decode: 16 splits of 32 blocks; partial o + (m, l) per (seq, split, head)
+    ws = sgqa.workspace_bytes(sgqa.OP_ATTN_DECODE, REAL, 16, 1, 1 << 20)
+    assert ws == 16 * 16 * 64 * (192 + 3) * 4
+    assert sgqa.workspace_bytes(sgqa.OP_ATTN_DECODE, with_selection(TINY, 8, 16), 1, 1, 1024) > 0
+    assert sgqa.workspace_bytes(7, REAL, 1, 1, 1) == 0
