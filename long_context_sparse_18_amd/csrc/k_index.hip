@@ -6,8 +6,8 @@
 // of 8 tokens.  Here the representation is the mean over the tokens present.
 //
 // Pure HBM streaming: each thread owns 8 consecutive proxy features (16 B) of
-// one block, issues all B row loads at once, sums in fp32 and writes one 16 B
-// bf16 chunk.  A wave covers 64 x 16 B = 1 KiB of contiguous output, and its
+// one block, issues all B row loads at once, sums exactly in fp64 and writes
+// one 16 B chunk of correctly rounded bf16 means.  A wave covers 64 x 16 B = 1 KiB of contiguous output, and its
 // loads for row r of the blocks it covers are contiguous 512 B runs.
 #include <hip/hip_runtime.h>
 
@@ -32,10 +32,13 @@ __global__ __launch_bounds__(256) void k_index_build(const uint16_t *__restrict_
     const int64_t n = (L - first < B) ? (L - first) : B;
     const uint16_t *src = kp + first * P + c * 8;
 
-    float acc[8];
+    // fp64 sums of bf16 inputs are exact (8-bit significands, 53-bit accumulator), so the
+    // mean below is the correctly rounded fp64 quotient; it is then rounded once more to
+    // bf16, through a round-to-odd fp32 step that keeps the final rounding exact.
+    double acc[8];
 #pragma unroll
     for (int e = 0; e < 8; ++e)
-        acc[e] = 0.0f;
+        acc[e] = 0.0;
 
     if (n == B) {
         u32x4 v[B];
@@ -46,31 +49,28 @@ __global__ __launch_bounds__(256) void k_index_build(const uint16_t *__restrict_
         for (int r = 0; r < B; ++r) {
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                acc[2 * w] += bf16_bits_to_f32(v[r][w] & 0xffffu);
-                acc[2 * w + 1] += bf16_bits_to_f32(v[r][w] >> 16);
+                acc[2 * w] += (double)bf16_bits_to_f32(v[r][w] & 0xffffu);
+                acc[2 * w + 1] += (double)bf16_bits_to_f32(v[r][w] >> 16);
             }
         }
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            acc[e] *= (1.0f / B);  // B is a power of two: exact
     } else {
         for (int64_t r = 0; r < n; ++r) {
             u32x4 v = load16(src + r * P);
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
-                acc[2 * w] += bf16_bits_to_f32(v[w] & 0xffffu);
-                acc[2 * w + 1] += bf16_bits_to_f32(v[w] >> 16);
+                acc[2 * w] += (double)bf16_bits_to_f32(v[w] & 0xffffu);
+                acc[2 * w + 1] += (double)bf16_bits_to_f32(v[w] >> 16);
             }
         }
-        const float fn = (float)n;
-#pragma unroll
-        for (int e = 0; e < 8; ++e)
-            acc[e] = acc[e] / fn;
     }
+    const double dn = (double)n;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+        acc[e] = acc[e] / dn;
     u32x4 o;
 #pragma unroll
     for (int w = 0; w < 4; ++w)
-        o[w] = pack_bf16x2(acc[2 * w], acc[2 * w + 1]);
+        o[w] = f64_to_bf16_bits(acc[2 * w]) | (f64_to_bf16_bits(acc[2 * w + 1]) << 16);
     *reinterpret_cast<u32x4 *>(kb + j * P + c * 8) = o;
 }
 

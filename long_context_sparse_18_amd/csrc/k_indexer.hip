@@ -138,6 +138,16 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a)
         return;
     }
 
+    if (k == 1) {
+        // Only the own block is kept.
+        if (tid == 0) {
+            out[0] = (int32_t)c;
+            if (osc)
+                osc[0] = __builtin_inff();
+        }
+        return;
+    }
+
     // ---- radix select of the (k-1)-th largest key
     int need = k - 1;
     uint32_t prefix = 0, pmask = 0;
@@ -219,7 +229,7 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a)
         int pos = block_exclusive_scan<NT>(n_take, scan_buf, sel_total) + run_sel;
 #pragma unroll
         for (int e = 0; e < kItems; ++e) {
-            if (take[e]) {
+            if (take[e] && pos < k - 1) {
                 const int j = base + tid * kItems + e;
                 out[pos] = j;
                 if (osc)

@@ -30,6 +30,18 @@ __device__ __forceinline__ uint32_t f32_to_bf16_bits(float f)
     return u >> 16;
 }
 
+// Round an fp64 value to bf16 (nearest, ties to even) without double rounding:
+// first to fp32 rounding to odd (truncate, then set the last bit if inexact),
+// which keeps enough bits for the final round-to-nearest-even to be exact.
+__device__ __forceinline__ uint32_t f64_to_bf16_bits(double x)
+{
+    float f = __double2float_rz(x);
+    uint32_t u = __float_as_uint(f);
+    if ((double)f != x && (u & 0x7f800000u) != 0x7f800000u)
+        u |= 1u;
+    return f32_to_bf16_bits(__uint_as_float(u));
+}
+
 __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi)
 {
     return f32_to_bf16_bits(lo) | (f32_to_bf16_bits(hi) << 16);
