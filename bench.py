@@ -30,6 +30,22 @@ PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0       # MI355X HBM3E
 
 
+def measured_traffic(name: str):
+    """HBM bytes per launch from a committed rocprofv3 summary, or None when the kernel's
+    sources changed since the counters were taken (their hash no longer matches)."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", name + ".json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for src in rec["sources"]:
+        h.update(open(os.path.join(ROOT, src), "rb").read())
+    if h.hexdigest()[:16] != rec["source_sha"]:
+        return None
+    return rec["fetch_bytes"] + rec["write_bytes"]
+
+
 def log(msg):
     print(f"[bench {time.strftime('%H:%M:%S')}] {msg}", file=sys.stderr, flush=True)
 
@@ -98,10 +114,15 @@ def bench_prefill(steps: int, warmup: int):
     attn_ms = sum(p[2] for p in per) / steps
     pairs = attended_pairs(wl.q_start, wl.T, s.block_size, s.topk_blocks)
     flops = 4 * s.head_dim * s.num_q_heads * pairs
+    # algorithmic bytes of the attention launch: every attended (query, token) pair reads that
+    # token's K and V rows of all KV heads; plus q, gate, idx in and out, lse out
     gather_bytes = pairs * s.num_kv_heads * s.head_dim * 2 * 2
+    io_bytes = wl.T * (2 * s.num_q_heads * s.head_dim * 2 + s.num_q_heads * (2 + 4)
+                       + s.topk_blocks * 4)
     res = dict(wl=wl, total_ms=total_ms, ms_per_step=total_ms / steps, build_ms=build_ms,
                topk_ms=topk_ms, attn_ms=attn_ms, pairs=pairs, attn_flops=flops,
-               gather_bytes=gather_bytes, data=d, kb=kb, idx=idx)
+               gather_bytes=gather_bytes, attn_bytes=gather_bytes + io_bytes, data=d, kb=kb,
+               idx=idx)
     return res
 
 
@@ -211,6 +232,10 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3072)
+    ap.add_argument("--no-prefill", action="store_true",
+                    help="time only the decode workload (for profiling runs)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="run only a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this layer is not sharded across GPUs here "
@@ -227,11 +252,26 @@ def main():
         _b.build()
     sgqa.load()
 
+    if args.copy_probe:
+        src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: 3 copies of 1 GiB")
+        return
+    if args.no_prefill:
+        dec = bench_decode(max(args.steps, 5), args.warmup)
+        log(f"decode: {dec['us_median']:.1f} us/step (topk {dec['us_topk']:.1f}, attn "
+            f"{dec['us_attn']:.1f}), {dec['gbs']:.0f} GB/s")
+        return
+
     pre = bench_prefill(args.steps, args.warmup)
     wl = pre["wl"]
     s = wl.shape
     tokens_per_s = wl.T / (pre["ms_per_step"] / 1e3)
     attn_tflops = pre["attn_flops"] / (pre["attn_ms"] / 1e3) / 1e12
+    attn_gbs = pre["attn_bytes"] / (pre["attn_ms"] / 1e3) / 1e9
     log(f"prefill: {pre['ms_per_step']:.2f} ms/step (build {pre['build_ms']:.3f}, topk "
         f"{pre['topk_ms']:.3f}, attn {pre['attn_ms']:.3f}) -> {tokens_per_s:,.0f} tokens/s, "
         f"attention {attn_tflops:.1f} TFLOP/s")
@@ -264,10 +304,11 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "L": wl.L, "q_heads": s.num_q_heads,
                    "kv_heads": s.num_kv_heads, "head_dim": s.head_dim, "proxy_dim": s.proxy_dim,
                    "block_size": s.block_size, "topk_blocks": s.topk_blocks},
-        "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
-                     "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS, "traffic": None,
-                     "kernel": "k_attn_prefill<192>",
-                     "gather_GBps": pre["gather_bytes"] / (pre["attn_ms"] / 1e3) / 1e9},
+        "roofline": {"bound": "hbm", "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": attn_gbs / PEAK_HBM_GBS,
+                     "traffic": measured_traffic("attn_prefill_128k"),
+                     "kernel": "k_attn_prefill<192>", "algorithmic_bytes": pre["attn_bytes"],
+                     "mfma_tflops": attn_tflops, "mfma_frac": attn_tflops / PEAK_BF16_TFLOPS},
         "cpu_baseline": cpu,
         "stages_ms": {"index_build": pre["build_ms"], "indexer_topk": pre["topk_ms"],
                       "sparse_attn_prefill": pre["attn_ms"]},
