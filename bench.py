@@ -145,7 +145,9 @@ def bench_decode(steps: int, warmup: int):
                           dtype=torch.uint8, device=dev)
     ws_attn = torch.empty(sgqa.workspace_bytes(sgqa.OP_ATTN_DECODE, s, n, 1, wl.L),
                           dtype=torch.uint8, device=dev)
-    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    # cold-cache protocol: read (not write) 512 MiB between steps, so no dirty lines are
+    # left to be written back while the timed kernels run
+    flush = torch.ones(128 << 20, dtype=torch.float32, device=dev)
     scale = 1.0 / math.sqrt(s.head_dim)
     stream = torch.cuda.current_stream(dev)
     qp = d["qp"].unsqueeze(1)
@@ -163,12 +165,12 @@ def bench_decode(steps: int, warmup: int):
         return a, m, b
 
     for _ in range(warmup):
-        flush.fill_(1)
+        flush.sum()
         step()
     torch.cuda.synchronize()
     times, t_topk, t_attn = [], [], []
     for _ in range(steps):
-        flush.fill_(1)   # no step starts with the caches warm
+        flush.sum()   # no step starts with the caches warm
         a, m, b = step()
         torch.cuda.synchronize()
         times.append(a.elapsed_time(b) * 1e3)

@@ -288,46 +288,56 @@ __global__ __launch_bounds__(512) void k_attn_decode_part(AttnArgs a)
 }
 
 // Exact merge of the split partial states of one (sequence, head), then the gate.
-__global__ __launch_bounds__(64) void k_attn_decode_merge(AttnArgs a)
+// One thread per output dimension; the per-split (max, sums) go through LDS once.
+constexpr int kMaxSplits = 64;
+
+__global__ __launch_bounds__(256) void k_attn_decode_merge(AttnArgs a)
 {
+    __shared__ float w_sh[kMaxSplits];
+    __shared__ float l_sh[kMaxSplits];
+    __shared__ float l32_sh[kMaxSplits];
     const int s = blockIdx.y, h = blockIdx.x;
-    const int D = a.d;
+    const int D = a.d, ns = a.nsplit, tid = threadIdx.x;
     const float neg_inf = -__builtin_inff();
-    const float *ml = a.part_ml + ((int64_t)s * a.nsplit * a.Hq + h) * 3;
-    const int64_t ml_step = (int64_t)a.Hq * 3;
+    const int64_t base = (int64_t)s * ns * a.Hq + h;  // slot of split 0
+    if (tid < ns) {
+        const float *ml = a.part_ml + (base + (int64_t)tid * a.Hq) * 3;
+        w_sh[tid] = ml[0];
+        l_sh[tid] = ml[1];
+        l32_sh[tid] = ml[2];
+    }
+    __syncthreads();
     float M = neg_inf;
-    for (int i = 0; i < a.nsplit; ++i)
-        M = fmaxf(M, ml[i * ml_step]);
+    for (int i = 0; i < ns; ++i)
+        M = fmaxf(M, w_sh[i]);
     float Lsum = 0.f, L32 = 0.f;
-    for (int i = 0; i < a.nsplit; ++i) {
-        const float mi = ml[i * ml_step];
-        if (mi != neg_inf) {
-            const float w = fast_exp2(mi - M);
-            Lsum += ml[i * ml_step + 1] * w;
-            L32 += ml[i * ml_step + 2] * w;
-        }
+    for (int i = 0; i < ns; ++i) {
+        const float w = w_sh[i] == neg_inf ? 0.f : fast_exp2(w_sh[i] - M);
+        Lsum += l_sh[i] * w;
+        L32 += l32_sh[i] * w;
     }
-    const float gsig = sigmoid_f32(bf16_bits_to_f32(a.gate[(int64_t)s * a.Hq + h]));
-    const float f = gsig / Lsum;
-    const float *po = a.part_o + ((int64_t)s * a.nsplit * a.Hq + h) * D;
-    const int64_t po_step = (int64_t)a.Hq * D;
-    for (int dd = threadIdx.x; dd < D; dd += 64) {
+    __syncthreads();
+    if (tid < ns)
+        w_sh[tid] = w_sh[tid] == neg_inf ? 0.f : fast_exp2(w_sh[tid] - M);
+    __syncthreads();
+    if (tid < D) {
+        const float *po = a.part_o + base * D + tid;
+        const int64_t step = (int64_t)a.Hq * D;
         float o = 0.f;
-        for (int i = 0; i < a.nsplit; ++i) {
-            const float mi = ml[i * ml_step];
-            if (mi != neg_inf)
-                o += po[i * po_step + dd] * fast_exp2(mi - M);
-        }
-        a.out[((int64_t)s * a.Hq + h) * D + dd] = (uint16_t)f32_to_bf16_bits(o * f);
+#pragma unroll 8
+        for (int i = 0; i < ns; ++i)
+            o += po[i * step] * w_sh[i];
+        const float gsig = sigmoid_f32(bf16_bits_to_f32(a.gate[(int64_t)s * a.Hq + h]));
+        a.out[((int64_t)s * a.Hq + h) * D + tid] = (uint16_t)f32_to_bf16_bits(o * (gsig / Lsum));
     }
-    if (a.lse && threadIdx.x == 0)
+    if (a.lse && tid == 0)
         a.lse[(int64_t)s * a.Hq + h] = (M + fast_log2(L32)) * 0.6931471805599453f;
 }
 
 void decode_split_plan(int k, int B, int &nsplit, int &entries_per_split)
 {
     const int eps = kSlots / B;  // entries per 32-slot step
-    int per = (k + 15) / 16;     // aim for 16 splits
+    int per = (k + 31) / 32;     // aim for 32 splits
     per = ((per + eps - 1) / eps) * eps;
     entries_per_split = per;
     nsplit = (k + per - 1) / per;
@@ -350,7 +360,8 @@ static hipError_t launch_decode_d(const AttnArgs &a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(k_attn_decode_merge, dim3((unsigned)a.Hq, (unsigned)a.rows), dim3(64), 0,
+    const unsigned nt = (unsigned)((a.d + 63) / 64 * 64);
+    hipLaunchKernelGGL(k_attn_decode_merge, dim3((unsigned)a.Hq, (unsigned)a.rows), dim3(nt), 0,
                        stream, a);
     return hipGetLastError();
 }

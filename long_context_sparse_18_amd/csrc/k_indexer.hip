@@ -107,15 +107,136 @@ hipError_t launch_scores(const ScoreArgs &a, hipStream_t stream)
 }
 
 // --------------------------------------------------------------------------------------------
+// Exact radix select, shared by every selection kernel.  `key_at(j)` yields the
+// order-preserving key of element j in [0, n).  Returns the key of the need-th
+// largest element and how many elements equal to it are kept (the lowest positions).
+struct KthKey {
+    uint32_t key;
+    int take_eq;
+};
+
+struct SelectShared {
+    uint32_t hist[4096];
+    int scan[16];
+    uint32_t digit;
+    int need;
+};
+
+// Radix select over the bits top..0 of keys that all share `prefix` on the bits in `pmask`.
+template <int NT, typename KeyAt>
+__device__ KthKey radix_select_bits(KeyAt key_at, int n, int need, SelectShared &sh, int top,
+                                    uint32_t prefix, uint32_t pmask)
+{
+    const int tid = threadIdx.x;
+#pragma unroll 1
+    while (top >= 0) {
+        const int width = top + 1 < 12 ? top + 1 : 12;
+        const int shift = top + 1 - width;
+        const int nb = 1 << width;
+        for (int b = tid; b < nb; b += NT)
+            sh.hist[b] = 0;
+        __syncthreads();
+        for (int j = tid; j < n; j += NT) {
+            const uint32_t key = key_at(j);
+            if ((key & pmask) == prefix)
+                atomicAdd(&sh.hist[(key >> shift) & (nb - 1)], 1u);
+        }
+        __syncthreads();
+        const int per = nb >= NT ? nb / NT : 1;
+        const int lo = tid * per;
+        int local = 0;
+        if (lo < nb)
+            for (int b = lo; b < lo + per; ++b)
+                local += (int)sh.hist[b];
+        int total;
+        const int below = block_exclusive_scan<NT>(local, sh.scan, total);
+        const int above = total - below - local;
+        if (lo < nb && above < need && need <= above + local) {
+            int acc = above;
+            for (int b = lo + per - 1; b >= lo; --b) {
+                const int h = (int)sh.hist[b];
+                if (acc + h >= need) {
+                    sh.digit = (uint32_t)b;
+                    sh.need = need - acc;
+                    break;
+                }
+                acc += h;
+            }
+        }
+        __syncthreads();
+        need = sh.need;
+        prefix |= sh.digit << shift;
+        pmask |= (uint32_t)(nb - 1) << shift;
+        top = shift - 1;
+        __syncthreads();
+    }
+    return KthKey{prefix, need};
+}
+
+template <int NT, typename KeyAt>
+__device__ KthKey radix_select(KeyAt key_at, int n, int need, SelectShared &sh)
+{
+    return radix_select_bits<NT>(key_at, n, need, sh, 31, 0u, 0u);
+}
+
+// Ordered compaction of the selected elements: emit(pos, j, key) for every element
+// with key > kth, and for the first th.take_eq elements equal to kth, in increasing j;
+// positions count from 0 and stop at `limit`.
+template <int NT, typename KeyAt, typename Emit>
+__device__ void emit_selected(KeyAt key_at, int n, KthKey th, int limit, SelectShared &sh,
+                              Emit emit)
+{
+    constexpr int kItems = 4;
+    const int tid = threadIdx.x;
+    int run_sel = 0, run_eq = 0;
+#pragma unroll 1
+    for (int base = 0; base < n; base += NT * kItems) {
+        uint32_t keys[kItems];
+        int n_eq = 0;
+#pragma unroll
+        for (int e = 0; e < kItems; ++e) {
+            const int j = base + tid * kItems + e;
+            keys[e] = j < n ? key_at(j) : 0u;
+            n_eq += (j < n && keys[e] == th.key) ? 1 : 0;
+        }
+        int eq_total;
+        int eq_before = block_exclusive_scan<NT>(n_eq, sh.scan, eq_total) + run_eq;
+        bool take[kItems];
+        int n_take = 0;
+#pragma unroll
+        for (int e = 0; e < kItems; ++e) {
+            const int j = base + tid * kItems + e;
+            bool tk = false;
+            if (j < n) {
+                if (keys[e] > th.key)
+                    tk = true;
+                else if (keys[e] == th.key) {
+                    tk = eq_before < th.take_eq;
+                    ++eq_before;
+                }
+            }
+            take[e] = tk;
+            n_take += tk ? 1 : 0;
+        }
+        int sel_total;
+        int pos = block_exclusive_scan<NT>(n_take, sh.scan, sel_total) + run_sel;
+#pragma unroll
+        for (int e = 0; e < kItems; ++e) {
+            if (take[e] && pos < limit) {
+                emit(pos, base + tid * kItems + e, keys[e]);
+                ++pos;
+            }
+        }
+        run_eq += eq_total;
+        run_sel += sel_total;
+    }
+}
+
+// One workgroup per query row of a score pass (rows of any length).
 template <int NT>
 __global__ __launch_bounds__(NT) void k_select(SelectArgs a)
 {
-    constexpr int kItems = 4;
-    __shared__ uint32_t hist[4096];
-    __shared__ int scan_buf[NT / 64];
-    __shared__ uint32_t sh_digit;
-    __shared__ int sh_need;
-
+    __shared__ SelectShared sh;
     const int tid = threadIdx.x;
     const int row = blockIdx.x;
     const int s = row / a.nq;
@@ -130,121 +251,268 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a)
     if (c <= (int64_t)k - 1) {
         // Every past block and the own block are kept.
         for (int e = tid; e < k; e += NT) {
-            const bool live = e <= c;
-            out[e] = live ? e : -1;
+            out[e] = e <= c ? e : -1;
             if (osc)
                 osc[e] = (e < c) ? srow[e] : (e == c ? __builtin_inff() : -__builtin_inff());
         }
         return;
     }
-
-    if (k == 1) {
-        // Only the own block is kept.
-        if (tid == 0) {
-            out[0] = (int32_t)c;
+    if (k > 1) {
+        auto key_at = [&](int j) { return score_key(srow[j]); };
+        const KthKey th = radix_select<NT>(key_at, (int)c, k - 1, sh);
+        emit_selected<NT>(key_at, (int)c, th, k - 1, sh, [&](int pos, int j, uint32_t key) {
+            out[pos] = j;
             if (osc)
-                osc[0] = __builtin_inff();
-        }
-        return;
-    }
-
-    // ---- radix select of the (k-1)-th largest key
-    int need = k - 1;
-    uint32_t prefix = 0, pmask = 0;
-    const int cn = (int)c;
-#pragma unroll 1
-    for (int pass = 0; pass < 3; ++pass) {
-        const int shift = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
-        const int nb = pass == 2 ? 256 : 4096;
-        for (int b = tid; b < nb; b += NT)
-            hist[b] = 0;
-        __syncthreads();
-        for (int j = tid; j < cn; j += NT) {
-            const uint32_t key = score_key(srow[j]);
-            if ((key & pmask) == prefix)
-                atomicAdd(&hist[(key >> shift) & (nb - 1)], 1u);
-        }
-        __syncthreads();
-        const int per = nb >= NT ? nb / NT : 1;
-        const int lo = tid * per;
-        int local = 0;
-        if (lo < nb)
-            for (int b = lo; b < lo + per; ++b)
-                local += (int)hist[b];
-        int total;
-        const int below = block_exclusive_scan<NT>(local, scan_buf, total);
-        const int above = total - below - local;
-        if (lo < nb && above < need && need <= above + local) {
-            int acc = above;
-            for (int b = lo + per - 1; b >= lo; --b) {
-                const int h = (int)hist[b];
-                if (acc + h >= need) {
-                    sh_digit = (uint32_t)b;
-                    sh_need = need - acc;
-                    break;
-                }
-                acc += h;
-            }
-        }
-        __syncthreads();
-        need = sh_need;
-        prefix |= sh_digit << shift;
-        pmask |= (uint32_t)(nb - 1) << shift;
-        __syncthreads();
-    }
-    const uint32_t kth = prefix;  // exact key of the (k-1)-th largest score
-
-    // ---- emit in ascending block order
-    int run_sel = 0, run_eq = 0;
-#pragma unroll 1
-    for (int base = 0; base < cn; base += NT * kItems) {
-        uint32_t keys[kItems];
-        int n_eq = 0;
-#pragma unroll
-        for (int e = 0; e < kItems; ++e) {
-            const int j = base + tid * kItems + e;
-            keys[e] = j < cn ? score_key(srow[j]) : 0u;
-            n_eq += (j < cn && keys[e] == kth) ? 1 : 0;
-        }
-        int eq_total;
-        int eq_before = block_exclusive_scan<NT>(n_eq, scan_buf, eq_total) + run_eq;
-        bool take[kItems];
-        int n_take = 0;
-#pragma unroll
-        for (int e = 0; e < kItems; ++e) {
-            const int j = base + tid * kItems + e;
-            bool tk = false;
-            if (j < cn) {
-                if (keys[e] > kth)
-                    tk = true;
-                else if (keys[e] == kth) {
-                    tk = eq_before < need;
-                    ++eq_before;
-                }
-            }
-            take[e] = tk;
-            n_take += tk ? 1 : 0;
-        }
-        int sel_total;
-        int pos = block_exclusive_scan<NT>(n_take, scan_buf, sel_total) + run_sel;
-#pragma unroll
-        for (int e = 0; e < kItems; ++e) {
-            if (take[e] && pos < k - 1) {
-                const int j = base + tid * kItems + e;
-                out[pos] = j;
-                if (osc)
-                    osc[pos] = key_score(keys[e]);
-                ++pos;
-            }
-        }
-        run_eq += eq_total;
-        run_sel += sel_total;
+                osc[pos] = key_score(key);
+        });
     }
     if (tid == 0) {
         out[k - 1] = (int32_t)c;
         if (osc)
             osc[k - 1] = __builtin_inff();
     }
+}
+
+// --------------------------------------------------------------------------------------------
+// Decode: one query per sequence against the whole index, in three launches.
+//  1. k_decode_keys streams kb at HBM rate (2048+ workgroups): the MFMA A operand is
+//     the query proxy broadcast to all 16 rows, so row 0 of each 16x16 result holds
+//     16 block scores; they are stored as order-preserving keys.
+//  2. k_decode_chunk_select loads one chunk of keys into LDS and writes the chunk's
+//     exact top-(k-1) in ascending block order.
+//  3. k_decode_final selects the top-(k-1) of the concatenated chunk candidates.
+// The union of chunk-local top-(k-1) sets contains the global top-(k-1) under the
+// same total order (score desc, block asc), so the result is exact.
+constexpr int kKeysPerWG = 1024;
+
+template <int P>
+__global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
+{
+    constexpr int U = 4;  // 16-block groups in flight per wave
+    const int s = blockIdx.y;
+    const int64_t t = a.pos.v[s];
+    const int64_t c = t / a.B;
+    const int64_t j0 = (int64_t)blockIdx.x * kKeysPerWG;
+    if (j0 >= c)
+        return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    const uint16_t *kb = a.kb + (int64_t)s * a.kb_seq_stride;
+    const uint16_t *qp = a.qp + (int64_t)s * a.qp_seq_stride;
+    uint32_t *keys = a.keys + (int64_t)s * a.keys_ld;
+
+    bf16x8 af[P / 32];
+#pragma unroll
+    for (int kk = 0; kk < P / 32; ++kk)
+        af[kk] = as_bf16x8(load16(qp + kk * 32 + q4 * 8));
+
+    // waves interleave over the workgroup's 64 groups (adjacent waves read adjacent rows)
+    constexpr int NG = kKeysPerWG / 16;
+#pragma unroll 1
+    for (int g0 = wave; g0 < NG; g0 += 4 * U) {
+        u32x4 bv[U][P / 32];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int64_t jb = j0 + (int64_t)(g0 + 4 * u) * 16 + col;
+            if (g0 + 4 * u >= NG || jb >= c)
+                jb = j0;  // a valid row; its score is discarded
+#pragma unroll
+            for (int kk = 0; kk < P / 32; ++kk)
+                bv[u][kk] = load16(kb + jb * P + kk * 32 + q4 * 8);
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < P / 32; ++kk)
+                acc = mfma_16x16x32(af[kk], as_bf16x8(bv[u][kk]), acc);
+            const int64_t j = j0 + (int64_t)(g0 + 4 * u) * 16 + col;
+            if (q4 == 0 && g0 + 4 * u < NG && j < c)
+                keys[j] = score_key(acc[0]);
+        }
+    }
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void k_decode_chunk_select(DecodeTopkArgs a)
+{
+    extern __shared__ __align__(16) uint32_t ck_lds[];  // [a.chunk]
+    __shared__ SelectShared sh;
+    const int s = blockIdx.y, ch = blockIdx.x;
+    const int64_t t = a.pos.v[s];
+    const int64_t c = t / a.B;
+    const int64_t j0 = (int64_t)ch * a.chunk;
+    if (j0 >= c)
+        return;
+    const int n = (int)((c - j0) < a.chunk ? (c - j0) : a.chunk);
+    const int tid = threadIdx.x;
+    const uint32_t *src = a.keys + (int64_t)s * a.keys_ld + j0;
+    const int keep = a.k - 1;
+    uint32_t *ck = a.cand_key + ((int64_t)s * a.nchunks + ch) * keep;
+    int32_t *ci = a.cand_idx + ((int64_t)s * a.nchunks + ch) * keep;
+    if (n <= keep) {
+        for (int j = tid; j < n; j += NT) {
+            ck[j] = src[j];
+            ci[j] = (int32_t)(j0 + j);
+        }
+        return;
+    }
+    // all of this thread's loads are issued before any LDS store
+    constexpr int kBatch = 8;
+    for (int j0b = 0; j0b < n; j0b += NT * kBatch) {
+        uint32_t v[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int j = j0b + b * NT + tid;
+            v[b] = j < n ? src[j] : 0u;
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+            const int j = j0b + b * NT + tid;
+            if (j < n)
+                ck_lds[j] = v[b];
+        }
+    }
+    __syncthreads();
+    auto key_at = [&](int j) { return ck_lds[j]; };
+    const KthKey th = radix_select<NT>(key_at, n, keep, sh);
+    emit_selected<NT>(key_at, n, th, keep, sh, [&](int pos, int j, uint32_t key) {
+        ck[pos] = key;
+        ci[pos] = (int32_t)(j0 + j);
+    });
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void k_decode_final(DecodeTopkArgs a)
+{
+    extern __shared__ __align__(16) uint32_t keys[];  // [nchunks * (k-1)]
+    __shared__ SelectShared sh;
+    __shared__ int offs[kMaxDecodeChunks + 1];
+    const int s = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int64_t t = a.pos.v[s];
+    const int64_t c = t / a.B;
+    const int k = a.k, keep = k - 1;
+    int32_t *out = a.idx + (int64_t)s * k;
+    float *osc = a.sel_scores ? a.sel_scores + (int64_t)s * k : nullptr;
+
+    // candidate counts per chunk, concatenated in chunk (= ascending block) order
+    if (tid == 0) {
+        int o = 0;
+        for (int ch = 0; ch < a.nchunks; ++ch) {
+            offs[ch] = o;
+            const int64_t j0 = (int64_t)ch * a.chunk;
+            if (j0 < c) {
+                const int64_t n = (c - j0) < a.chunk ? (c - j0) : a.chunk;
+                o += (int)(n < keep ? n : keep);
+            }
+        }
+        offs[a.nchunks] = o;
+    }
+    __syncthreads();
+    const int total = offs[a.nchunks];
+    // position of concatenated candidate e in the per-chunk arrays
+    auto cand_slot = [&](int e) {
+        int ch = 0;
+        while (offs[ch + 1] <= e)
+            ++ch;
+        return ((int64_t)s * a.nchunks + ch) * keep + (e - offs[ch]);
+    };
+    {
+        constexpr int kBatch = 8;
+        for (int e0 = 0; e0 < total; e0 += NT * kBatch) {
+            uint32_t v[kBatch];
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int e = e0 + b * NT + tid;
+                v[b] = e < total ? a.cand_key[cand_slot(e)] : 0u;
+            }
+#pragma unroll
+            for (int b = 0; b < kBatch; ++b) {
+                const int e = e0 + b * NT + tid;
+                if (e < total)
+                    keys[e] = v[b];
+            }
+        }
+    }
+    __syncthreads();
+    auto cand_index = [&](int e) { return a.cand_idx[cand_slot(e)]; };
+
+    if (c <= (int64_t)keep) {
+        // every past block is a candidate and is kept (total == c)
+        for (int e = tid; e < k; e += NT) {
+            out[e] = e <= c ? (e < c ? cand_index(e) : (int32_t)c) : -1;
+            if (osc)
+                osc[e] = e < c ? key_score(keys[e]) : (e == c ? __builtin_inff() : -__builtin_inff());
+        }
+        return;
+    }
+    if (keep > 0) {
+        auto key_at = [&](int e) { return keys[e]; };
+        const KthKey th = radix_select<NT>(key_at, total, keep, sh);
+        emit_selected<NT>(key_at, total, th, keep, sh, [&](int pos, int e, uint32_t key) {
+            out[pos] = cand_index(e);
+            if (osc)
+                osc[pos] = key_score(key);
+        });
+    }
+    if (tid == 0) {
+        out[k - 1] = (int32_t)c;
+        if (osc)
+            osc[k - 1] = __builtin_inff();
+    }
+}
+
+bool decode_topk_plan(int64_t max_cand, int k, int &nchunks, int &chunk)
+{
+    if (k < 2 || max_cand <= 0)
+        return false;
+    int64_t nc = (max_cand + 8191) / 8192;
+    if (nc < 1)
+        nc = 1;
+    if (nc > kMaxDecodeChunks)
+        nc = kMaxDecodeChunks;
+    int64_t ch = (max_cand + nc - 1) / nc;
+    ch = ((ch + 15) / 16) * 16;
+    if (ch * 4 > kDecodeLdsBytes || nc * (int64_t)(k - 1) * 4 > kDecodeLdsBytes)
+        return false;
+    nchunks = (int)nc;
+    chunk = (int)ch;
+    return true;
+}
+
+int64_t decode_keys_ld(int64_t max_cand)
+{
+    return ((max_cand + kKeysPerWG - 1) / kKeysPerWG) * kKeysPerWG;
+}
+
+template <int P>
+static void launch_decode_keys_p(const DecodeTopkArgs &a, hipStream_t stream)
+{
+    const unsigned nwg = (unsigned)(a.keys_ld / kKeysPerWG);
+    hipLaunchKernelGGL(k_decode_keys<P>, dim3(nwg, (unsigned)a.nseq), dim3(256), 0, stream, a);
+}
+
+hipError_t launch_decode_topk(const DecodeTopkArgs &a, hipStream_t stream)
+{
+    switch (a.P) {
+    case 32: launch_decode_keys_p<32>(a, stream); break;
+    case 64: launch_decode_keys_p<64>(a, stream); break;
+    case 128: launch_decode_keys_p<128>(a, stream); break;
+    case 256: launch_decode_keys_p<256>(a, stream); break;
+    default: return hipErrorInvalidValue;
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_decode_chunk_select<512>, dim3((unsigned)a.nchunks, (unsigned)a.nseq),
+                       dim3(512), (size_t)a.chunk * 4, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_decode_final<1024>, dim3((unsigned)a.nseq), dim3(1024),
+                       (size_t)a.nchunks * (a.k - 1) * 4, stream, a);
+    return hipGetLastError();
 }
 
 hipError_t launch_select(const SelectArgs &a, hipStream_t stream)

@@ -155,8 +155,8 @@ def test_workspace_sizes():
     # capped at 2 GiB, in whole 64-row passes, for the 128K prefill
     big = sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, REAL, 1, 131072, 131072)
     assert big <= 2 << 30 and big % (16384 * 4 * 64) == 0
-    # decode: 16 splits of 32 blocks; partial o + (m, l) per (seq, split, head)
+    # decode: 32 splits of 16 blocks; partial o + (max, two sums) per (seq, split, head)
     ws = sgqa.workspace_bytes(sgqa.OP_ATTN_DECODE, REAL, 16, 1, 1 << 20)
-    assert ws == 16 * 16 * 64 * (192 + 3) * 4
+    assert ws == 16 * 32 * 64 * (192 + 3) * 4
     assert sgqa.workspace_bytes(sgqa.OP_ATTN_DECODE, with_selection(TINY, 8, 16), 1, 1, 1024) > 0
     assert sgqa.workspace_bytes(7, REAL, 1, 1, 1) == 0

@@ -171,3 +171,36 @@ def test_tiny_empty_calls_are_noops(tiny):
     sgqa.indexer_topk(shape, tiny["qp"][:0], tiny["kp"][:16], [0], idx)
     torch.cuda.synchronize()
     assert torch.all(out == 7.0) and torch.all(idx == 5)
+
+
+@pytest.mark.parametrize("k", [16, 300])
+def test_decode_topk_many_chunks(k):
+    """One query per sequence against long indexes (up to 25 000 blocks), so the decode
+    top-k splits the candidates over several chunks; checked against the oracle."""
+    lens = [70001, 131072, 200003, 9]
+    Lmax = max(lens)
+    shape = with_selection(WL.shape, 8, k)
+    wl = Workload("tiny-long", shape, nseq=len(lens), T=1, L=Lmax, q_start=Lmax - 1)
+    n = len(lens)
+    kp = torch.empty((n, Lmax, shape.proxy_dim), dtype=torch.bfloat16, device=DEV)
+    qp = torch.empty((n, 1, shape.proxy_dim), dtype=torch.bfloat16, device=DEV)
+    for b in range(n):
+        _, _, kpb = inputs.make_cache(wl, 7, DEV, seq=b)
+        kp[b].copy_(kpb)
+        qp[b, 0].copy_(inputs.make_queries(wl, 7, DEV, seq=b, T=1)[2][0])
+    nblk = -(-Lmax // 8)
+    kb = torch.empty((n, nblk, shape.proxy_dim), dtype=torch.bfloat16, device=DEV)
+    sgqa.index_build(shape, kp, kb, lens)
+    idx = torch.empty((n, 1, k), dtype=torch.int32, device=DEV)
+    sel = torch.empty((n, 1, k), dtype=torch.float32, device=DEV)
+    sgqa.indexer_topk(shape, qp, kb, [L_ - 1 for L_ in lens], idx, sel)
+    torch.cuda.synchronize()
+    for b, L_ in enumerate(lens):
+        t = np.array([L_ - 1])
+        c = int(t[0] // 8)
+        kbw = parity.widen(bits(kb[b, : -(-L_ // 8)]))
+        sc = oracle.scores(bits(qp[b]), t, 8, kbw, width=max(1, c))
+        ref = oracle.topk(sc, t, 8, k)
+        got = idx[b, 0].cpu().numpy()
+        assert parity.check_selection(got, sc[0], c, k, ref[0]) or c > 1000
+        parity.check_sel_scores(sel[b, 0].cpu().numpy(), got, sc[0], c, k)
