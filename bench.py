@@ -189,6 +189,63 @@ def bench_decode(steps: int, warmup: int):
                 gbs=bytes_total / (med * 1e-6) / 1e9)
 
 
+def bench_coverage():
+    """Token coverage on the 32 768-token prefill: the share of the exact (dense) softmax
+    mass that lands on the selected tokens, exp(lse_sparse - lse_dense), averaged over all
+    (query, head); at B=8 with 512 blocks and at B=1 with 2048 tokens.  Also times index
+    build + indexer top-k at both settings (the pages' 8x cost cut)."""
+    import torch
+    from long_context_sparse_18_amd import WORKLOADS, inputs, sgqa, with_selection
+
+    wl = WORKLOADS[1]
+    dev = torch.device("cuda:0")
+    d = inputs.make_prefill(wl, 1, dev)
+    scale = 1.0 / math.sqrt(wl.shape.head_dim)
+    stream = torch.cuda.current_stream(dev)
+    lses, times = {}, {}
+    for tag, B, k in (("b8_k512", 8, 512), ("b1_k2048", 1, 2048), ("dense", 8, wl.L // 8)):
+        s = with_selection(wl.shape, B, k)
+        kb = torch.empty((-(-wl.L // B), s.proxy_dim), dtype=torch.bfloat16, device=dev)
+        idx = torch.empty((wl.T, k), dtype=torch.int32, device=dev)
+        ws = torch.empty(sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, s, 1, wl.T, wl.L),
+                         dtype=torch.uint8, device=dev)
+        out = torch.empty_like(d["Q"])
+        lse = torch.empty((wl.T, s.num_q_heads), dtype=torch.float32, device=dev)
+        best = None
+        for rep in range(3):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            sgqa.index_build(s, d["kp"], kb, [wl.L], stream=stream)
+            sgqa.indexer_topk(s, d["qp"], kb, [0], idx, workspace=ws, stream=stream)
+            b.record(stream)
+            torch.cuda.synchronize()
+            ms = a.elapsed_time(b)
+            best = ms if best is None else min(best, ms)
+        sgqa.sparse_attn_prefill(s, d["Q"], d["K"], d["V"], d["G"], idx, 0, wl.L, scale, out, lse,
+                                 stream=stream)
+        torch.cuda.synchronize()
+        lses[tag] = lse
+        times[tag] = best
+        del kb, idx, ws, out
+    res = {"workload": wl.name,
+           "indexer_ms": {k_: round(v, 4) for k_, v in times.items() if k_ != "dense"},
+           "indexer_cost_ratio_b1_over_b8": times["b1_k2048"] / times["b8_k512"],
+           "pages_coverage_b8_k4096": 0.7806, "pages_coverage_b1_k2048": 0.7909}
+    t = torch.arange(wl.T, device=dev)
+    for tag, B, k in (("b8_k512", 8, 512), ("b1_k2048", 1, 2048)):
+        cov = torch.exp((lses[tag] - lses["dense"]).double())
+        res[f"coverage_{tag}"] = cov.mean().item()
+        far = t >= k * B
+        res[f"coverage_{tag}_t_ge_kB"] = cov[far].mean().item()
+        # if the proxy scores carried no information about the logits, each attended token
+        # would hold an equal share of the mass on average: E[cov_t] = |U_t| / (t + 1)
+        c = t // B
+        n_att = torch.where(c <= k - 1, t + 1, (k - 1) * B + t % B + 1)
+        res[f"coverage_{tag}_if_uninformative"] = (n_att.double() / (t + 1)).mean().item()
+    return res
+
+
 def cpu_baseline(pre, rows: int, seed: int = 0):
     """The fp64 oracle on a sample of query rows of the same prefill workload."""
     import numpy as np
@@ -234,6 +291,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3072)
+    ap.add_argument("--no-coverage", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="time only the decode workload (for profiling runs)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -284,6 +342,12 @@ def main():
     for key in ("data", "kb", "idx"):
         pre.pop(key, None)
     torch.cuda.empty_cache()
+    cov = None
+    if not args.no_coverage:
+        log("coverage: 32K prefill at B=8/k=512, B=1/k=2048 and dense")
+        cov = bench_coverage()
+        log(f"coverage: {cov}")
+        torch.cuda.empty_cache()
     dec = None
     if not args.no_decode:
         dec = bench_decode(max(args.steps, 5), args.warmup)
@@ -316,6 +380,8 @@ def main():
                       "sparse_attn_prefill": pre["attn_ms"]},
         "indexer_share": (pre["build_ms"] + pre["topk_ms"]) / pre["ms_per_step"],
     }
+    if cov is not None:
+        line["coverage"] = cov
     if dec is not None:
         line["decode"] = {"workload": "decode-1m-x16", "us_per_layer": dec["us_median"],
                           "us_indexer_topk": dec["us_topk"], "us_attention": dec["us_attn"],
