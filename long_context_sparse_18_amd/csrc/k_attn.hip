@@ -28,6 +28,16 @@ namespace sgqa {
 
 constexpr int kSlots = 32;  // token slots per step
 
+// Each wave stages V in its own LDS region, so only the wave's own LDS operations need
+// ordering: they execute in issue order, and these fences keep the compiler from moving
+// LDS accesses across the hand-off.  Waves of one workgroup never wait for each other.
+__device__ __forceinline__ void wave_lds_handoff()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 template <int D>
 struct WaveState {
     f32x4 acc[D / 16];  // acc[mt][i] = O^T[d = 16*mt + 4*q + i][head = lane % 16]
@@ -147,7 +157,7 @@ __device__ __forceinline__ void attend_range(const uint16_t *__restrict__ Kg,
         const bf16x8 pf = as_bf16x8(pw);
 
         // Stage V rows in LDS (row stride kLd elements, 8-byte aligned).
-        __syncthreads();
+        wave_lds_handoff();
 #pragma unroll
         for (int ci = 0; ci < kVChunks; ++ci) {
             const int f = lane + 64 * ci;
@@ -156,7 +166,7 @@ __device__ __forceinline__ void attend_range(const uint16_t *__restrict__ Kg,
             dst[0] = uint2{vv[ci][0], vv[ci][1]};
             dst[1] = uint2{vv[ci][2], vv[ci][3]};
         }
-        __syncthreads();
+        wave_lds_handoff();
 
         // O^T += V^T P^T: A[m = d][k = slot perm(8*q4 + j)], slots 4q4+j (j<4), 16+4q4+j-4.
 #pragma unroll
@@ -205,18 +215,35 @@ __device__ __forceinline__ float sigmoid_f32(float x)
     return 1.0f / (1.0f + fast_exp2(-x * 1.4426950408889634f));
 }
 
-template <int D>
+// kGroupPerXcd: workgroups are dispatched round-robin over the 8 XCDs; XCD x serves KV
+// group x / (8 / Hkv) only, so each XCD's L2 holds one group's K/V rows, and the 4 waves
+// of a workgroup take 4 consecutive tokens of that group.  Otherwise one workgroup takes
+// one token and its waves take the groups (adjacent rows of one token).
+template <int D, bool kGroupPerXcd>
 __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
 {
     extern __shared__ __align__(16) uint16_t lds[];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int col = lane & 15, q4 = lane >> 4;
-    const int64_t r = (int64_t)a.rows - 1 - blockIdx.x;  // longest rows first
+    const int hpg = a.Hq / a.Hkv;
+    int64_t r;
+    int g;
+    if constexpr (kGroupPerXcd) {
+        const int R = 8 / a.Hkv;
+        const int x = blockIdx.x & 7;
+        g = x / R;
+        const int64_t tile = (int64_t)(blockIdx.x >> 3) * R + (x % R);
+        const int64_t row = tile * 4 + wave;
+        if (row >= a.rows)
+            return;  // waves never synchronise with each other
+        r = (int64_t)a.rows - 1 - row;  // longest rows first
+    } else {
+        r = (int64_t)a.rows - 1 - blockIdx.x;
+        g = wave;
+    }
     const int64_t t = a.q_start + r;
     const int64_t c = t / a.B;
     const int nvalid = (int)((c + 1 < a.k) ? c + 1 : a.k);
-    const int g = wave;
-    const int hpg = a.Hq / a.Hkv;
 
     bf16x8 qf[D / 32];
     load_q<D>(a.q + (r * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
@@ -346,8 +373,19 @@ void decode_split_plan(int k, int B, int &nsplit, int &entries_per_split)
 template <int D>
 static hipError_t launch_prefill_d(const AttnArgs &a, hipStream_t stream)
 {
-    const size_t lds = (size_t)a.Hkv * kSlots * (D + 4) * sizeof(uint16_t);
-    hipLaunchKernelGGL(k_attn_prefill<D>, dim3((unsigned)a.rows), dim3(64 * a.Hkv), lds, stream, a);
+    // Group-per-XCD mapping whenever the groups divide the 8 XCDs (measured 17 % faster
+    // than one-token-per-workgroup on the 128K prefill); the other mapping otherwise.
+    if (8 % a.Hkv == 0) {
+        const int R = 8 / a.Hkv;
+        const int64_t ntiles = ((int64_t)a.rows + 3) / 4;
+        const int64_t nwg = (ntiles + R - 1) / R * 8;
+        const size_t lds = (size_t)4 * kSlots * (D + 4) * sizeof(uint16_t);
+        hipLaunchKernelGGL((k_attn_prefill<D, true>), dim3((unsigned)nwg), dim3(256), lds, stream, a);
+    } else {
+        const size_t lds = (size_t)a.Hkv * kSlots * (D + 4) * sizeof(uint16_t);
+        hipLaunchKernelGGL((k_attn_prefill<D, false>), dim3((unsigned)a.rows), dim3(64 * a.Hkv), lds,
+                           stream, a);
+    }
     return hipGetLastError();
 }
 
