@@ -274,16 +274,19 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a)
 }
 
 // --------------------------------------------------------------------------------------------
-// Decode: one query per sequence against the whole index, in three launches.
-//  1. k_decode_keys streams kb at HBM rate (2048+ workgroups): the MFMA A operand is
-//     the query proxy broadcast to all 16 rows, so row 0 of each 16x16 result holds
-//     16 block scores; they are stored as order-preserving keys.
-//  2. k_decode_chunk_select loads one chunk of keys into LDS and writes the chunk's
-//     exact top-(k-1) in ascending block order.
-//  3. k_decode_final selects the top-(k-1) of the concatenated chunk candidates.
-// The union of chunk-local top-(k-1) sets contains the global top-(k-1) under the
-// same total order (score desc, block asc), so the result is exact.
+// Decode: one query per sequence against the whole index.
+//  1. k_decode_keys streams kb at HBM rate (one workgroup per 1024 blocks): the MFMA A
+//     operand is the query proxy broadcast to all 16 rows, so row 0 of each 16x16 result
+//     holds 16 block scores; they are stored as order-preserving keys.
+//  2. k_decode_select (one workgroup per sequence) takes a strided sample of 2048 keys and
+//     uses a sample order statistic as a conservative threshold (about twice k-1 keys are
+//     expected above it), compacts the keys at or above it in ascending block order, and
+//     selects exactly among those candidates (ties to the lowest block).  If fewer than k-1
+//     keys clear the threshold, or too many, it selects exactly over all keys instead, so
+//     the result never depends on the sample.
 constexpr int kKeysPerWG = 1024;
+constexpr int kSample = 2048;
+constexpr int kCandCap = 4096;
 
 template <int P>
 __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
@@ -334,156 +337,150 @@ __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
 }
 
 template <int NT>
-__global__ __launch_bounds__(NT) void k_decode_chunk_select(DecodeTopkArgs a)
+__global__ __launch_bounds__(NT) void k_decode_select(DecodeTopkArgs a)
 {
-    extern __shared__ __align__(16) uint32_t ck_lds[];  // [a.chunk]
     __shared__ SelectShared sh;
-    const int s = blockIdx.y, ch = blockIdx.x;
-    const int64_t t = a.pos.v[s];
-    const int64_t c = t / a.B;
-    const int64_t j0 = (int64_t)ch * a.chunk;
-    if (j0 >= c)
-        return;
-    const int n = (int)((c - j0) < a.chunk ? (c - j0) : a.chunk);
-    const int tid = threadIdx.x;
-    const uint32_t *src = a.keys + (int64_t)s * a.keys_ld + j0;
-    const int keep = a.k - 1;
-    uint32_t *ck = a.cand_key + ((int64_t)s * a.nchunks + ch) * keep;
-    int32_t *ci = a.cand_idx + ((int64_t)s * a.nchunks + ch) * keep;
-    if (n <= keep) {
-        for (int j = tid; j < n; j += NT) {
-            ck[j] = src[j];
-            ci[j] = (int32_t)(j0 + j);
-        }
-        return;
-    }
-    // all of this thread's loads are issued before any LDS store
-    constexpr int kBatch = 8;
-    for (int j0b = 0; j0b < n; j0b += NT * kBatch) {
-        uint32_t v[kBatch];
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int j = j0b + b * NT + tid;
-            v[b] = j < n ? src[j] : 0u;
-        }
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-            const int j = j0b + b * NT + tid;
-            if (j < n)
-                ck_lds[j] = v[b];
-        }
-    }
-    __syncthreads();
-    auto key_at = [&](int j) { return ck_lds[j]; };
-    const KthKey th = radix_select<NT>(key_at, n, keep, sh);
-    emit_selected<NT>(key_at, n, th, keep, sh, [&](int pos, int j, uint32_t key) {
-        ck[pos] = key;
-        ci[pos] = (int32_t)(j0 + j);
-    });
-}
-
-template <int NT>
-__global__ __launch_bounds__(NT) void k_decode_final(DecodeTopkArgs a)
-{
-    extern __shared__ __align__(16) uint32_t keys[];  // [nchunks * (k-1)]
-    __shared__ SelectShared sh;
-    __shared__ int offs[kMaxDecodeChunks + 1];
-    const int s = blockIdx.x;
-    const int tid = threadIdx.x;
+    __shared__ uint32_t sample[kSample];
+    __shared__ uint32_t cand_key[kCandCap];
+    __shared__ int32_t cand_idx[kCandCap];
+    const int s = blockIdx.x, tid = threadIdx.x;
     const int64_t t = a.pos.v[s];
     const int64_t c = t / a.B;
     const int k = a.k, keep = k - 1;
+    const uint32_t *keys = a.keys + (int64_t)s * a.keys_ld;
     int32_t *out = a.idx + (int64_t)s * k;
     float *osc = a.sel_scores ? a.sel_scores + (int64_t)s * k : nullptr;
 
-    // candidate counts per chunk, concatenated in chunk (= ascending block) order
-    if (tid == 0) {
-        int o = 0;
-        for (int ch = 0; ch < a.nchunks; ++ch) {
-            offs[ch] = o;
-            const int64_t j0 = (int64_t)ch * a.chunk;
-            if (j0 < c) {
-                const int64_t n = (c - j0) < a.chunk ? (c - j0) : a.chunk;
-                o += (int)(n < keep ? n : keep);
-            }
-        }
-        offs[a.nchunks] = o;
-    }
-    __syncthreads();
-    const int total = offs[a.nchunks];
-    // position of concatenated candidate e in the per-chunk arrays
-    auto cand_slot = [&](int e) {
-        int ch = 0;
-        while (offs[ch + 1] <= e)
-            ++ch;
-        return ((int64_t)s * a.nchunks + ch) * keep + (e - offs[ch]);
-    };
-    {
-        constexpr int kBatch = 8;
-        for (int e0 = 0; e0 < total; e0 += NT * kBatch) {
-            uint32_t v[kBatch];
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                const int e = e0 + b * NT + tid;
-                v[b] = e < total ? a.cand_key[cand_slot(e)] : 0u;
-            }
-#pragma unroll
-            for (int b = 0; b < kBatch; ++b) {
-                const int e = e0 + b * NT + tid;
-                if (e < total)
-                    keys[e] = v[b];
-            }
-        }
-    }
-    __syncthreads();
-    auto cand_index = [&](int e) { return a.cand_idx[cand_slot(e)]; };
-
     if (c <= (int64_t)keep) {
-        // every past block is a candidate and is kept (total == c)
         for (int e = tid; e < k; e += NT) {
-            out[e] = e <= c ? (e < c ? cand_index(e) : (int32_t)c) : -1;
+            out[e] = e <= c ? e : -1;
             if (osc)
                 osc[e] = e < c ? key_score(keys[e]) : (e == c ? __builtin_inff() : -__builtin_inff());
         }
         return;
     }
-    if (keep > 0) {
-        auto key_at = [&](int e) { return keys[e]; };
-        const KthKey th = radix_select<NT>(key_at, total, keep, sh);
-        emit_selected<NT>(key_at, total, th, keep, sh, [&](int pos, int e, uint32_t key) {
-            out[pos] = cand_index(e);
-            if (osc)
-                osc[pos] = key_score(key);
-        });
-    }
     if (tid == 0) {
-        out[k - 1] = (int32_t)c;
+        out[keep] = (int32_t)c;
         if (osc)
-            osc[k - 1] = __builtin_inff();
+            osc[keep] = __builtin_inff();
+    }
+    if (keep == 0)
+        return;
+    const int cn = (int)c;
+    auto emit = [&](int pos, int j, uint32_t key) {
+        out[pos] = j;
+        if (osc)
+            osc[pos] = key_score(key);
+    };
+
+    // 1) threshold from a strided sample
+    const int ns = cn < kSample ? cn : kSample;
+    const int stride = cn / ns;
+    for (int i = tid; i < ns; i += NT)
+        sample[i] = keys[(int64_t)i * stride];
+    __syncthreads();
+    int r = (2 * keep + stride - 1) / stride + 8;
+    if (r > ns)
+        r = ns;
+    auto sample_at = [&](int i) { return sample[i]; };
+    const uint32_t thresh = radix_select<NT>(sample_at, ns, r, sh).key;
+
+    // 2) count the keys >= thresh: each wave owns a contiguous range of 16-byte vectors and
+    //    walks it 64 vectors (1 KiB) per load; one workgroup scan gives each wave its base
+    constexpr int NW = NT / 64;
+    constexpr int kUnroll = 16;  // 256 KiB of loads in flight per workgroup
+    const int lane = tid & 63, wave = tid >> 6;
+    const u32x4 *kv = reinterpret_cast<const u32x4 *>(keys);
+    const int nvec = (cn + 3) >> 2;
+    const int wper = ((nvec + NW - 1) / NW + 63) & ~63;  // whole 64-vector steps per wave
+    const int w0 = wave * wper;
+    const int w1 = w0 + wper < nvec ? w0 + wper : nvec;
+    auto count_ge = [&](const u32x4 &v, int q) {
+        int n = 0;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            n += (4 * q + e < cn && v[e] >= thresh) ? 1 : 0;
+        return n;
+    };
+    int local = 0;
+    for (int q0 = w0; q0 < w1; q0 += 64 * kUnroll) {
+        u32x4 v[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int q = q0 + u * 64 + lane;
+            v[u] = q < w1 ? kv[q] : u32x4{0u, 0u, 0u, 0u};
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+            const int q = q0 + u * 64 + lane;
+            if (q < w1)
+                local += count_ge(v[u], q);
+        }
+    }
+    // wave total on every lane, then the waves' exclusive prefix
+    int wtot = local;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        wtot += __shfl_xor(wtot, o);
+    int total;
+    const int wbase = block_exclusive_scan<NT>(lane == 0 ? wtot : 0, sh.scan, total);
+    const int base0 = __shfl(wbase, 0);
+
+    if (total >= keep && total <= kCandCap) {
+        // 3) candidates in ascending block order (per-step wave scans), then an exact
+        //    selection among them
+        int run = base0;
+        for (int q0 = w0; q0 < w1; q0 += 64 * kUnroll) {
+            u32x4 v[kUnroll];
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int q = q0 + u * 64 + lane;
+                v[u] = q < w1 ? kv[q] : u32x4{0u, 0u, 0u, 0u};
+            }
+#pragma unroll
+            for (int u = 0; u < kUnroll; ++u) {
+                const int q = q0 + u * 64 + lane;
+                const int n = q < w1 ? count_ge(v[u], q) : 0;
+                const int incl = wave_inclusive_scan(n);
+                int p = run + incl - n;
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const int j = 4 * q + e;
+                    if (q < w1 && j < cn && v[u][e] >= thresh) {
+                        cand_key[p] = v[u][e];
+                        cand_idx[p] = j;
+                        ++p;
+                    }
+                }
+                run += __shfl(incl, 63);
+            }
+        }
+        __syncthreads();
+        auto cand_at = [&](int e) { return cand_key[e]; };
+        const KthKey th = radix_select<NT>(cand_at, total, keep, sh);
+        emit_selected<NT>(cand_at, total, th, keep, sh,
+                          [&](int p, int e, uint32_t key) { emit(p, cand_idx[e], key); });
+    } else {
+        // the sample missed (rare): exact selection over every key
+        auto key_at = [&](int j) { return keys[j]; };
+        const KthKey th = radix_select<NT>(key_at, cn, keep, sh);
+        emit_selected<NT>(key_at, cn, th, keep, sh, emit);
     }
 }
 
-bool decode_topk_plan(int64_t max_cand, int k, int &nchunks, int &chunk)
+bool decode_topk_supported(int64_t max_cand, int k)
 {
-    if (k < 2 || max_cand <= 0)
-        return false;
-    int64_t nc = (max_cand + 8191) / 8192;
-    if (nc < 1)
-        nc = 1;
-    if (nc > kMaxDecodeChunks)
-        nc = kMaxDecodeChunks;
-    int64_t ch = (max_cand + nc - 1) / nc;
-    ch = ((ch + 15) / 16) * 16;
-    if (ch * 4 > kDecodeLdsBytes || nc * (int64_t)(k - 1) * 4 > kDecodeLdsBytes)
-        return false;
-    nchunks = (int)nc;
-    chunk = (int)ch;
-    return true;
+    return k >= 2 && max_cand > 0 && max_cand <= kDecodeMaxCand;
 }
 
 int64_t decode_keys_ld(int64_t max_cand)
 {
     return ((max_cand + kKeysPerWG - 1) / kKeysPerWG) * kKeysPerWG;
+}
+
+size_t decode_topk_workspace(int nseq, int64_t max_cand)
+{
+    return (size_t)nseq * decode_keys_ld(max_cand) * 4;
 }
 
 template <int P>
@@ -505,13 +502,7 @@ hipError_t launch_decode_topk(const DecodeTopkArgs &a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    hipLaunchKernelGGL(k_decode_chunk_select<512>, dim3((unsigned)a.nchunks, (unsigned)a.nseq),
-                       dim3(512), (size_t)a.chunk * 4, stream, a);
-    e = hipGetLastError();
-    if (e != hipSuccess)
-        return e;
-    hipLaunchKernelGGL(k_decode_final<1024>, dim3((unsigned)a.nseq), dim3(1024),
-                       (size_t)a.nchunks * (a.k - 1) * 4, stream, a);
+    hipLaunchKernelGGL(k_decode_select<1024>, dim3((unsigned)a.nseq), dim3(1024), 0, stream, a);
     return hipGetLastError();
 }
 

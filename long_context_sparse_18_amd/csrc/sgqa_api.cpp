@@ -154,10 +154,8 @@ size_t sgqa_workspace_bytes(int op, const sgqa_dims *dims, int32_t nseq, int32_t
             bytes = ((int64_t)kIndexerWorkspaceCap / (per_q * 64)) * (per_q * 64);
         if (bytes < per_q * min_rows)
             bytes = per_q * min_rows;
-        int nchunks, chunk;
-        if (T == 1 && sgqa::decode_topk_plan(max_cand, dims->topk_blocks, nchunks, chunk)) {
-            const int64_t dec = (int64_t)nseq * nchunks * (dims->topk_blocks - 1) * 8 +
-                                (int64_t)nseq * sgqa::decode_keys_ld(max_cand) * 4;
+        if (T == 1 && sgqa::decode_topk_supported(max_cand, dims->topk_blocks)) {
+            const int64_t dec = (int64_t)sgqa::decode_topk_workspace(nseq, max_cand);
             bytes = dec > bytes ? dec : bytes;
         }
         return (size_t)bytes;
@@ -260,34 +258,26 @@ sgqa_status sgqa_indexer_topk(const sgqa_dims *dims, const sgqa_bf16 *qp, int64_
 
     hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
 
-    // One query per sequence: chunked scan with chunk-local selection, then an exact merge.
-    int nchunks = 0, chunk = 0;
+    // One query per sequence: score keys with a top-bit histogram, then one select per sequence.
     const bool p_ok = P == 32 || P == 64 || P == 128 || P == 256;
-    if (T == 1 && p_ok && sgqa::decode_topk_plan(plan.max_cand, dims->topk_blocks, nchunks, chunk)) {
-        const size_t cand = (size_t)nseq * nchunks * (dims->topk_blocks - 1);
-        const int64_t keys_ld = sgqa::decode_keys_ld(plan.max_cand);
-        if (workspace_bytes >= cand * 8 + (size_t)nseq * keys_ld * 4) {
-            sgqa::DecodeTopkArgs da{};
-            da.qp = qp;
-            da.qp_seq_stride = qp_seq_stride;
-            da.kb = kb;
-            da.kb_seq_stride = kb_seq_stride;
-            for (int s = 0; s < nseq; ++s)
-                da.pos.v[s] = q_start[s];
-            da.nseq = nseq;
-            da.P = P;
-            da.B = dims->block_size;
-            da.k = dims->topk_blocks;
-            da.nchunks = nchunks;
-            da.chunk = chunk;
-            da.keys = static_cast<uint32_t *>(workspace);
-            da.keys_ld = keys_ld;
-            da.cand_key = da.keys + (size_t)nseq * keys_ld;
-            da.cand_idx = reinterpret_cast<int32_t *>(da.cand_key + cand);
-            da.idx = idx;
-            da.sel_scores = sel_scores;
-            return hip_status(sgqa::launch_decode_topk(da, hs), "decode top-k launch");
-        }
+    if (T == 1 && p_ok && sgqa::decode_topk_supported(plan.max_cand, dims->topk_blocks) &&
+        workspace_bytes >= sgqa::decode_topk_workspace(nseq, plan.max_cand)) {
+        sgqa::DecodeTopkArgs da{};
+        da.qp = qp;
+        da.qp_seq_stride = qp_seq_stride;
+        da.kb = kb;
+        da.kb_seq_stride = kb_seq_stride;
+        for (int s = 0; s < nseq; ++s)
+            da.pos.v[s] = q_start[s];
+        da.nseq = nseq;
+        da.P = P;
+        da.B = dims->block_size;
+        da.k = dims->topk_blocks;
+        da.keys = static_cast<uint32_t *>(workspace);
+        da.keys_ld = sgqa::decode_keys_ld(plan.max_cand);
+        da.idx = idx;
+        da.sel_scores = sel_scores;
+        return hip_status(sgqa::launch_decode_topk(da, hs), "decode top-k launch");
     }
 
     sgqa::ScoreArgs sa{};

@@ -53,11 +53,9 @@ struct SelectArgs {
 };
 hipError_t launch_select(const SelectArgs &a, hipStream_t stream);
 
-// Decode-shaped top-k (one query per sequence): score keys for every block, chunk-local
-// selection, then an exact merge.  keys holds nseq * keys_ld entries and cand_* hold
-// nseq * nchunks * (k-1) entries each.
-constexpr int kMaxDecodeChunks = 16;
-constexpr int kDecodeLdsBytes = 40 * 1024;  // + ~16.5 KB static LDS stays under 64 KB
+// Decode-shaped top-k (one query per sequence): score keys for every block, then one
+// selection workgroup per sequence.  The workspace holds keys [nseq][keys_ld] (u32).
+constexpr int64_t kDecodeMaxCand = int64_t(1) << 30;
 struct DecodeTopkArgs {
     const uint16_t *qp;  // query proxy of sequence s at qp + s * qp_seq_stride
     int64_t qp_seq_stride;
@@ -68,18 +66,15 @@ struct DecodeTopkArgs {
     int32_t P;
     int32_t B;
     int32_t k;
-    int32_t nchunks;
-    int32_t chunk;       // candidate blocks per chunk
     uint32_t *keys;      // [nseq][keys_ld] order-preserving score keys
     int64_t keys_ld;
-    uint32_t *cand_key;
-    int32_t *cand_idx;
     int32_t *idx;        // [nseq][k]
     float *sel_scores;   // [nseq][k] or null
 };
 // False when the shape is outside the decode path (then the general path is used).
-bool decode_topk_plan(int64_t max_cand, int k, int &nchunks, int &chunk);
+bool decode_topk_supported(int64_t max_cand, int k);
 int64_t decode_keys_ld(int64_t max_cand);
+size_t decode_topk_workspace(int nseq, int64_t max_cand);
 hipError_t launch_decode_topk(const DecodeTopkArgs &a, hipStream_t stream);
 
 struct AttnArgs {
