@@ -119,7 +119,22 @@ def bench_prefill(steps: int, warmup: int):
     gather_bytes = pairs * s.num_kv_heads * s.head_dim * 2 * 2
     io_bytes = wl.T * (2 * s.num_q_heads * s.head_dim * 2 + s.num_q_heads * (2 + 4)
                        + s.topk_blocks * 4)
-    res = dict(wl=wl, total_ms=total_ms, ms_per_step=total_ms / steps, build_ms=build_ms,
+    # the sibling layer type on the same inputs: gated sliding-window attention, window 512
+    W = 512
+    sgqa.swa_prefill(s, d["Q"], d["K"], d["V"], d["G"], wl.q_start, wl.L, W, scale, out,
+                     stream=stream)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    for _ in range(steps):
+        sgqa.swa_prefill(s, d["Q"], d["K"], d["V"], d["G"], wl.q_start, wl.L, W, scale, out,
+                         stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    swa_ms = a.elapsed_time(b) / steps
+    swa_pairs = sum(min(W, t + 1) for t in range(wl.q_start, wl.q_start + wl.T))
+    swa = {"window": W, "ms": swa_ms, "tokens_per_s": wl.T / (swa_ms / 1e3),
+           "tflops": 4 * s.head_dim * s.num_q_heads * swa_pairs / (swa_ms / 1e3) / 1e12}
+    res = dict(wl=wl, total_ms=total_ms, ms_per_step=total_ms / steps, build_ms=build_ms, swa=swa,
                topk_ms=topk_ms, attn_ms=attn_ms, pairs=pairs, attn_flops=flops,
                gather_bytes=gather_bytes, attn_bytes=gather_bytes + io_bytes, data=d, kb=kb,
                idx=idx)
@@ -380,6 +395,7 @@ def main():
                       "sparse_attn_prefill": pre["attn_ms"]},
         "indexer_share": (pre["build_ms"] + pre["topk_ms"]) / pre["ms_per_step"],
     }
+    line["sliding_window_attention"] = pre["swa"]
     if cov is not None:
         line["coverage"] = cov
     if dec is not None:

@@ -78,7 +78,7 @@ enum { SGQA_OP_INDEXER_TOPK = 1, SGQA_OP_ATTN_DECODE = 2 };
  * targets million-token context"): for each sequence s and block j in
  * [blk_begin, min(blk_end, ceil(L_s/B))),
  *     kb[s][j][:] = mean of kp[s][jB .. min(jB+B, L_s)-1][:]
- * summed in fp32 and rounded to bf16 (round to nearest even).  A trailing
+ * summed exactly and rounded once to bf16 (nearest, ties to even).  A trailing
  * partial block is the mean of the tokens present.  blk_end < 0 means "to the
  * last block".  Blocks outside the range are not written, so a decode or
  * chunked-prefill loop can refresh only the blocks it touched.
@@ -158,6 +158,24 @@ sgqa_status sgqa_sparse_attn_decode(const sgqa_dims *dims, const sgqa_bf16 *q,
                                     const int32_t *idx, const int64_t *cache_lens, int32_t nseq,
                                     float softmax_scale, sgqa_bf16 *out, float *lse,
                                     void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Gated sliding-window attention, the sibling layer type (ai.info "Why StepFun
+ * chose 92 transformer blocks": the efficient layers use Gated Sliding Window
+ * Attention; phantomic12 config.json: sliding_window 512).  For query row i at
+ * t = q_start + i and head h with group g = h / (Hq/Hkv), over the window
+ * U = { s : max(0, t - window + 1) <= s <= t } (the `window` most recent
+ * positions, the query's own included), with the same arithmetic as
+ * sgqa_sparse_attn_prefill:
+ *     out[i][h] = sigmoid(gate[i][h]) * sum_s softmax(z)_s V[s][g],
+ *     z_s = softmax_scale * q[i][h] . K[s][g];   lse[i][h] = log sum_s exp(z_s)
+ * Only num_q_heads, num_kv_heads and head_dim of dims are read.  Layouts as in
+ * sgqa_sparse_attn_prefill (no idx).  Requires window >= 1 and q_start + T <= L.
+ */
+sgqa_status sgqa_swa_prefill(const sgqa_dims *dims, const sgqa_bf16 *q, const sgqa_bf16 *k_cache,
+                             const sgqa_bf16 *v_cache, const sgqa_bf16 *gate, int64_t q_start,
+                             int32_t T, int64_t L, int64_t window, float softmax_scale,
+                             sgqa_bf16 *out, float *lse, void *stream);
 
 /*
  * Workspace size in bytes for `op` (SGQA_OP_INDEXER_TOPK or

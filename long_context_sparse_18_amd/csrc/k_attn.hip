@@ -46,16 +46,49 @@ struct WaveState {
     float l32;          // the same share summing the fp32 weights (for the log-sum-exp)
 };
 
-// Attend one wave's (token, group) over selected entries [e_begin, e_end).
+// Where the tokens of one query come from, 32 slots per step.
+// SparseTokens: the selected blocks idx[e_begin, e_end) of a query at t (own block c);
+// slots beyond t, -1 entries and ids outside [0, c] are invalid.
+struct SparseTokens {
+    const int32_t *sel;
+    int e_begin, e_end;
+    int64_t t, c;
+    int B;
+    __device__ int steps() const
+    {
+        const int eps = kSlots / B;
+        return (e_end - e_begin + eps - 1) / eps;
+    }
+    __device__ void slot(int step, int sl, int64_t &s_ld, bool &valid) const
+    {
+        const int e = e_begin + step * (kSlots / B) + sl / B;
+        const int32_t blk = (e < e_end) ? sel[e] : -1;
+        const int64_t s = (int64_t)blk * B + (sl % B);
+        valid = blk >= 0 && (int64_t)blk <= c && s <= t;
+        s_ld = valid ? s : t;
+    }
+};
+
+// WindowTokens: the contiguous positions [s0, t].
+struct WindowTokens {
+    int64_t s0, t;
+    __device__ int steps() const { return (int)((t - s0 + kSlots) / kSlots); }
+    __device__ void slot(int step, int sl, int64_t &s_ld, bool &valid) const
+    {
+        const int64_t s = s0 + (int64_t)step * kSlots + sl;
+        valid = s <= t;
+        s_ld = valid ? s : t;
+    }
+};
+
+// Attend one wave's (token, group) over the tokens of `src`.
 // Kg/Vg point at element (token 0, group g, dim 0) of the cache; rows are
 // Hkv*D elements apart.  `vs` is this wave's LDS buffer [kSlots][D + 4].
-template <int D>
+template <int D, typename Src>
 __device__ __forceinline__ void attend_range(const uint16_t *__restrict__ Kg,
                                              const uint16_t *__restrict__ Vg, int Hkv,
-                                             const int32_t *__restrict__ sel, int e_begin,
-                                             int e_end, int64_t t, int64_t c, int B,
-                                             const bf16x8 (&qf)[D / 32], float scale_log2,
-                                             uint16_t *vs, WaveState<D> &st)
+                                             const Src &src, const bf16x8 (&qf)[D / 32],
+                                             float scale_log2, uint16_t *vs, WaveState<D> &st)
 {
     constexpr int kLd = D + 4;         // LDS row stride in elements (bytes = 8 mod 32)
     constexpr int kPieces = D / 8;     // 16-byte pieces per row
@@ -63,21 +96,14 @@ __device__ __forceinline__ void attend_range(const uint16_t *__restrict__ Kg,
     const int lane = threadIdx.x & 63;
     const int col = lane & 15, q4 = lane >> 4;
     const int64_t row_elems = (int64_t)Hkv * D;
-    const int eps = kSlots / B;  // entries per step
     const float neg_inf = -__builtin_inff();
+    const int nsteps = src.steps();
 
-    for (int e_base = e_begin; e_base < e_end; e_base += eps) {
+    for (int step = 0; step < nsteps; ++step) {
         // Token of slot (lane & 31): clamped load position + validity.
         int64_t s_ld;
         bool valid;
-        {
-            const int slot = lane & 31;
-            const int e = e_base + slot / B;
-            const int32_t blk = (e < e_end) ? sel[e] : -1;
-            const int64_t s = (int64_t)blk * B + (slot % B);
-            valid = blk >= 0 && (int64_t)blk <= c && s <= t;
-            s_ld = valid ? s : t;
-        }
+        src.slot(step, lane & 31, s_ld, valid);
         const uint64_t vmask = __ballot(valid);
         const int s_lo = (int)(s_ld & 0xffffffff), s_hi = (int)(s_ld >> 32);
 
@@ -215,53 +241,22 @@ __device__ __forceinline__ float sigmoid_f32(float x)
     return 1.0f / (1.0f + fast_exp2(-x * 1.4426950408889634f));
 }
 
-// kGroupPerXcd: workgroups are dispatched round-robin over the 8 XCDs; XCD x serves KV
-// group x / (8 / Hkv) only, so each XCD's L2 holds one group's K/V rows, and the 4 waves
-// of a workgroup take 4 consecutive tokens of that group.  Otherwise one workgroup takes
-// one token and its waves take the groups (adjacent rows of one token).
-template <int D, bool kGroupPerXcd>
-__global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
+// Normalise, gate and store one (row, group): out[r][g*hpg + head][:] and lse.
+template <int D>
+__device__ __forceinline__ void store_row(const WaveState<D> &st, const AttnArgs &a, int64_t r,
+                                          int g, int hpg)
 {
-    extern __shared__ __align__(16) uint16_t lds[];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int lane = threadIdx.x & 63;
     const int col = lane & 15, q4 = lane >> 4;
-    const int hpg = a.Hq / a.Hkv;
-    int64_t r;
-    int g;
-    if constexpr (kGroupPerXcd) {
-        const int R = 8 / a.Hkv;
-        const int x = blockIdx.x & 7;
-        g = x / R;
-        const int64_t tile = (int64_t)(blockIdx.x >> 3) * R + (x % R);
-        const int64_t row = tile * 4 + wave;
-        if (row >= a.rows)
-            return;  // waves never synchronise with each other
-        r = (int64_t)a.rows - 1 - row;  // longest rows first
-    } else {
-        r = (int64_t)a.rows - 1 - blockIdx.x;
-        g = wave;
-    }
-    const int64_t t = a.q_start + r;
-    const int64_t c = t / a.B;
-    const int nvalid = (int)((c + 1 < a.k) ? c + 1 : a.k);
-
-    bf16x8 qf[D / 32];
-    load_q<D>(a.q + (r * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
-    WaveState<D> st;
-    init_state<D>(st);
-    attend_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D, a.Hkv, a.idx + r * a.k, 0, nvalid,
-                    t, c, a.B, qf, a.scale_log2, lds + wave * kSlots * (D + 4), st);
-
     const float l = sum_across_rows(st.l);
     const float l32 = sum_across_rows(st.l32);
     if (col < hpg) {
         const int h = g * hpg + col;
-        const float inv = 1.0f / l;
         const float gsig = sigmoid_f32(bf16_bits_to_f32(a.gate[r * a.Hq + h]));
+        const float f = gsig / l;
         uint16_t *o = a.out + (r * a.Hq + h) * D + q4 * 4;
 #pragma unroll
         for (int mt = 0; mt < D / 16; ++mt) {
-            const float f = inv * gsig;
             uint2 w;
             w.x = pack_bf16x2(st.acc[mt][0] * f, st.acc[mt][1] * f);
             w.y = pack_bf16x2(st.acc[mt][2] * f, st.acc[mt][3] * f);
@@ -270,6 +265,82 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
         if (a.lse && q4 == 0)
             a.lse[r * a.Hq + h] = (st.m + fast_log2(l32)) * 0.6931471805599453f;
     }
+}
+
+// Row and group of this wave under the two workgroup mappings (see k_attn_prefill).
+// Returns false for waves past the last row.
+template <bool kGroupPerXcd>
+__device__ __forceinline__ bool wave_row_group(const AttnArgs &a, int64_t &r, int &g)
+{
+    const int wave = threadIdx.x >> 6;
+    if constexpr (kGroupPerXcd) {
+        const int R = 8 / a.Hkv;
+        const int x = blockIdx.x & 7;
+        g = x / R;
+        const int64_t tile = (int64_t)(blockIdx.x >> 3) * R + (x % R);
+        const int64_t row = tile * 4 + wave;
+        if (row >= a.rows)
+            return false;
+        r = (int64_t)a.rows - 1 - row;  // longest rows first
+    } else {
+        r = (int64_t)a.rows - 1 - blockIdx.x;
+        g = wave;
+    }
+    return true;
+}
+
+// kGroupPerXcd: workgroups are dispatched round-robin over the 8 XCDs; XCD x serves KV
+// group x / (8 / Hkv) only, so each XCD's L2 holds one group's K/V rows, and the 4 waves
+// of a workgroup take 4 consecutive tokens of that group.  Otherwise one workgroup takes
+// one token and its waves take the groups (adjacent rows of one token).
+template <int D, bool kGroupPerXcd>
+__global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
+{
+    extern __shared__ __align__(16) uint16_t lds[];
+    const int wave = threadIdx.x >> 6;
+    const int hpg = a.Hq / a.Hkv;
+    int64_t r;
+    int g;
+    if (!wave_row_group<kGroupPerXcd>(a, r, g))
+        return;  // waves never synchronise with each other
+    const int64_t t = a.q_start + r;
+    const int64_t c = t / a.B;
+    const int nvalid = (int)((c + 1 < a.k) ? c + 1 : a.k);
+
+    bf16x8 qf[D / 32];
+    load_q<D>(a.q + (r * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
+    WaveState<D> st;
+    init_state<D>(st);
+    const SparseTokens src{a.idx + r * a.k, 0, nvalid, t, c, a.B};
+    attend_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D, a.Hkv, src, qf, a.scale_log2,
+                    lds + wave * kSlots * (D + 4), st);
+
+    store_row<D>(st, a, r, g, hpg);
+}
+
+// Gated sliding-window attention: the same per-(token, group) wave over the contiguous
+// positions [max(0, t - window + 1), t].
+template <int D, bool kGroupPerXcd>
+__global__ __launch_bounds__(512) void k_swa(AttnArgs a)
+{
+    extern __shared__ __align__(16) uint16_t lds[];
+    const int wave = threadIdx.x >> 6;
+    const int hpg = a.Hq / a.Hkv;
+    int64_t r;
+    int g;
+    if (!wave_row_group<kGroupPerXcd>(a, r, g))
+        return;
+    const int64_t t = a.q_start + r;
+    const int64_t s0 = t - a.window + 1 > 0 ? t - a.window + 1 : 0;
+
+    bf16x8 qf[D / 32];
+    load_q<D>(a.q + (r * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
+    WaveState<D> st;
+    init_state<D>(st);
+    const WindowTokens src{s0, t};
+    attend_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D, a.Hkv, src, qf, a.scale_log2,
+                    lds + wave * kSlots * (D + 4), st);
+    store_row<D>(st, a, r, g, hpg);
 }
 
 template <int D>
@@ -293,9 +364,11 @@ __global__ __launch_bounds__(512) void k_attn_decode_part(AttnArgs a)
     WaveState<D> st;
     init_state<D>(st);
     const int64_t base = (int64_t)s * a.cache_seq_stride + (int64_t)g * D;
-    if (e0 < e1)
-        attend_range<D>(a.kc + base, a.vc + base, a.Hkv, a.idx + (int64_t)s * a.k, e0, e1, t, c,
-                        a.B, qf, a.scale_log2, lds + wave * kSlots * (D + 4), st);
+    if (e0 < e1) {
+        const SparseTokens src{a.idx + (int64_t)s * a.k, e0, e1, t, c, a.B};
+        attend_range<D>(a.kc + base, a.vc + base, a.Hkv, src, qf, a.scale_log2,
+                        lds + wave * kSlots * (D + 4), st);
+    }
 
     const float l = sum_across_rows(st.l);
     const float l32 = sum_across_rows(st.l32);
@@ -370,7 +443,7 @@ void decode_split_plan(int k, int B, int &nsplit, int &entries_per_split)
     nsplit = (k + per - 1) / per;
 }
 
-template <int D>
+template <int D, bool kWindow>
 static hipError_t launch_prefill_d(const AttnArgs &a, hipStream_t stream)
 {
     // Group-per-XCD mapping whenever the groups divide the 8 XCDs (measured 17 % faster
@@ -380,11 +453,19 @@ static hipError_t launch_prefill_d(const AttnArgs &a, hipStream_t stream)
         const int64_t ntiles = ((int64_t)a.rows + 3) / 4;
         const int64_t nwg = (ntiles + R - 1) / R * 8;
         const size_t lds = (size_t)4 * kSlots * (D + 4) * sizeof(uint16_t);
-        hipLaunchKernelGGL((k_attn_prefill<D, true>), dim3((unsigned)nwg), dim3(256), lds, stream, a);
+        if (kWindow)
+            hipLaunchKernelGGL((k_swa<D, true>), dim3((unsigned)nwg), dim3(256), lds, stream, a);
+        else
+            hipLaunchKernelGGL((k_attn_prefill<D, true>), dim3((unsigned)nwg), dim3(256), lds,
+                               stream, a);
     } else {
         const size_t lds = (size_t)a.Hkv * kSlots * (D + 4) * sizeof(uint16_t);
-        hipLaunchKernelGGL((k_attn_prefill<D, false>), dim3((unsigned)a.rows), dim3(64 * a.Hkv), lds,
-                           stream, a);
+        if (kWindow)
+            hipLaunchKernelGGL((k_swa<D, false>), dim3((unsigned)a.rows), dim3(64 * a.Hkv), lds,
+                               stream, a);
+        else
+            hipLaunchKernelGGL((k_attn_prefill<D, false>), dim3((unsigned)a.rows),
+                               dim3(64 * a.Hkv), lds, stream, a);
     }
     return hipGetLastError();
 }
@@ -409,9 +490,21 @@ hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream)
     if (a.rows <= 0)
         return hipSuccess;
     switch (a.d) {
-    case 64: return launch_prefill_d<64>(a, stream);
-    case 128: return launch_prefill_d<128>(a, stream);
-    case 192: return launch_prefill_d<192>(a, stream);
+    case 64: return launch_prefill_d<64, false>(a, stream);
+    case 128: return launch_prefill_d<128, false>(a, stream);
+    case 192: return launch_prefill_d<192, false>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+hipError_t launch_swa(const AttnArgs &a, hipStream_t stream)
+{
+    if (a.rows <= 0)
+        return hipSuccess;
+    switch (a.d) {
+    case 64: return launch_prefill_d<64, true>(a, stream);
+    case 128: return launch_prefill_d<128, true>(a, stream);
+    case 192: return launch_prefill_d<192, true>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

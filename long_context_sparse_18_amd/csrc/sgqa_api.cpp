@@ -83,6 +83,22 @@ sgqa_status check_dims(const sgqa_dims *d, bool need_attn, bool need_proxy)
     return SGQA_OK;
 }
 
+sgqa_status check_heads(const sgqa_dims *d)
+{
+    if (!d)
+        return fail(SGQA_ERR_NULL, "dims is NULL");
+    if (d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0)
+        return fail(SGQA_ERR_SHAPE, "head counts and head_dim must be positive");
+    if (d->num_q_heads % d->num_kv_heads != 0)
+        return fail(SGQA_ERR_SHAPE, "num_q_heads %d is not a multiple of num_kv_heads %d",
+                    d->num_q_heads, d->num_kv_heads);
+    if (d->num_q_heads / d->num_kv_heads > 16 || d->num_kv_heads > 8)
+        return fail(SGQA_ERR_UNSUPPORTED, "need heads per group <= 16 and num_kv_heads <= 8");
+    if (d->head_dim != 64 && d->head_dim != 128 && d->head_dim != 192)
+        return fail(SGQA_ERR_UNSUPPORTED, "head_dim %d not in {64,128,192}", d->head_dim);
+    return SGQA_OK;
+}
+
 sgqa_status hip_status(hipError_t e, const char *what)
 {
     if (e != hipSuccess)
@@ -360,6 +376,48 @@ sgqa_status sgqa_sparse_attn_prefill(const sgqa_dims *dims, const sgqa_bf16 *q,
     a.lse = lse;
     return hip_status(sgqa::launch_attn_prefill(a, reinterpret_cast<hipStream_t>(stream)),
                       "sparse_attn_prefill launch");
+}
+
+sgqa_status sgqa_swa_prefill(const sgqa_dims *dims, const sgqa_bf16 *q, const sgqa_bf16 *k_cache,
+                             const sgqa_bf16 *v_cache, const sgqa_bf16 *gate, int64_t q_start,
+                             int32_t T, int64_t L, int64_t window, float softmax_scale,
+                             sgqa_bf16 *out, float *lse, void *stream)
+{
+    sgqa_status st = check_heads(dims);
+    if (st != SGQA_OK)
+        return st;
+    if (T < 0 || q_start < 0 || L < 0)
+        return fail(SGQA_ERR_SHAPE, "T, q_start and L must be non-negative");
+    if (q_start + T > L)
+        return fail(SGQA_ERR_SHAPE, "q_start + T = %lld exceeds L = %lld", (long long)(q_start + T),
+                    (long long)L);
+    if (window < 1)
+        return fail(SGQA_ERR_SHAPE, "window %lld must be >= 1", (long long)window);
+    if (!std::isfinite(softmax_scale))
+        return fail(SGQA_ERR_SHAPE, "softmax_scale must be finite");
+    if (T == 0)
+        return ok();
+    if (!q || !k_cache || !v_cache || !gate || !out)
+        return fail(SGQA_ERR_NULL, "q, k_cache, v_cache, gate and out must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 8) ||
+        !aligned(lse, 4) || !aligned(gate, 2))
+        return fail(SGQA_ERR_SHAPE, "q, k_cache, v_cache must be 16-byte and out 8-byte aligned");
+    sgqa::AttnArgs a{};
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.gate = gate;
+    a.q_start = q_start;
+    a.rows = T;
+    a.Hq = dims->num_q_heads;
+    a.Hkv = dims->num_kv_heads;
+    a.d = dims->head_dim;
+    a.window = window;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.out = out;
+    a.lse = lse;
+    return hip_status(sgqa::launch_swa(a, reinterpret_cast<hipStream_t>(stream)),
+                      "swa_prefill launch");
 }
 
 sgqa_status sgqa_sparse_attn_decode(const sgqa_dims *dims, const sgqa_bf16 *q,

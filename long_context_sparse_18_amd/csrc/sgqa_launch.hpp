@@ -96,9 +96,11 @@ struct AttnArgs {
     float *part_ml;          // [nseq][nsplit][Hq][3]: max, bf16-weight sum, fp32-weight sum
     int32_t nsplit;
     int32_t entries_per_split;
+    int64_t window;          // sliding-window attention: tokens per window
 };
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream);
+hipError_t launch_swa(const AttnArgs &a, hipStream_t stream);
 
 // Decode split-K geometry for k selected entries of B tokens.
 void decode_split_plan(int k, int B, int &nsplit, int &entries_per_split);

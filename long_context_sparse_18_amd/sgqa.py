@@ -22,8 +22,8 @@ OP_INDEXER_TOPK = 1
 OP_ATTN_DECODE = 2
 
 EXPORTS = ("sgqa_index_build", "sgqa_indexer_topk", "sgqa_sparse_attn_prefill",
-           "sgqa_sparse_attn_decode", "sgqa_workspace_bytes", "sgqa_status_string",
-           "sgqa_last_error")
+           "sgqa_sparse_attn_decode", "sgqa_swa_prefill", "sgqa_workspace_bytes",
+           "sgqa_status_string", "sgqa_last_error")
 
 
 class Dims(ctypes.Structure):
@@ -68,6 +68,8 @@ def load():
     lib.sgqa_sparse_attn_decode.restype = st
     lib.sgqa_sparse_attn_decode.argtypes = [dp, p, p, p, i64, p, p, p, i32, ctypes.c_float, p, p,
                                             p, sz, p]
+    lib.sgqa_swa_prefill.restype = st
+    lib.sgqa_swa_prefill.argtypes = [dp, p, p, p, p, i64, i32, i64, i64, ctypes.c_float, p, p, p]
     lib.sgqa_workspace_bytes.restype = sz
     lib.sgqa_workspace_bytes.argtypes = [ctypes.c_int, dp, i32, i32, i64]
     lib.sgqa_status_string.restype = ctypes.c_char_p
@@ -170,3 +172,13 @@ def sparse_attn_decode(shape: LayerShape, q, k_cache, v_cache, gate, idx, cache_
                                          _i64_array(cache_lens), nseq, softmax_scale, _ptr(out),
                                          _ptr(lse), _ptr(workspace), workspace.numel(),
                                          _stream(stream, q)))
+
+
+def swa_prefill(shape: LayerShape, q, k_cache, v_cache, gate, q_start: int, L: int, window: int,
+                softmax_scale: float, out, lse=None, stream=None):
+    """Gated sliding-window attention of q [T, Hq, d] over the last `window` positions."""
+    _need_cuda(q, k_cache, v_cache, gate, out, lse)
+    d = Dims.of(shape)
+    check(load().sgqa_swa_prefill(ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                  _ptr(gate), q_start, q.shape[0], L, window, softmax_scale,
+                                  _ptr(out), _ptr(lse), _stream(stream, q)))

@@ -53,6 +53,10 @@ def _bind(lib):
     lib.orc_token_set.argtypes = [p, i32, i32, i64, p]
     lib.orc_attend.restype = None
     lib.orc_attend.argtypes = [p, p, p, i64, p, i32, i32, i32, dbl, p, p]
+    lib.orc_window_token_set.restype = i64
+    lib.orc_window_token_set.argtypes = [i64, i64, p]
+    lib.orc_window_attention.restype = ctypes.c_int
+    lib.orc_window_attention.argtypes = [p, p, i64, p, p, i64, p, i64, i32, i32, i32, dbl, p, p]
     lib.orc_sparse_attention.restype = ctypes.c_int
     lib.orc_sparse_attention.argtypes = [p, p, i64, p, p, i64, p, p, i32, i32, i32, i32, i32,
                                          dbl, p, p]
@@ -193,4 +197,26 @@ def sparse_attention(q_bits, t, K_bits, V_bits, G_bits, idx, B: int, scale: floa
                                   B, Hq, Hkv, d, float(scale), _ptr(out), _ptr(lse))
     if rc != 0:
         raise ValueError("a selected token lies outside the cache")
+    return out, lse
+
+
+def window_attention(q_bits, t, K_bits, V_bits, G_bits, window: int, scale: float, lib=None):
+    """Gated sliding-window attention (the ``window`` most recent positions, own included)
+    for query rows at positions ``t``; shapes as :func:`sparse_attention` without idx."""
+    lib = lib or load()
+    q = _u16(q_bits)
+    K = _u16(K_bits)
+    V = _u16(V_bits)
+    G = _u16(G_bits)
+    t = np.ascontiguousarray(t, dtype=np.int64)
+    n, Hq, d = q.shape
+    L, Hkv, d2 = K.shape
+    if d2 != d or V.shape != K.shape or G.shape != (n, Hq) or t.shape != (n,):
+        raise ValueError("shape mismatch in window_attention")
+    out = np.empty((n, Hq, d), dtype=np.float64)
+    lse = np.empty((n, Hq), dtype=np.float64)
+    rc = lib.orc_window_attention(_ptr(q), _ptr(t), n, _ptr(K), _ptr(V), L, _ptr(G), int(window),
+                                  Hq, Hkv, d, float(scale), _ptr(out), _ptr(lse))
+    if rc != 0:
+        raise ValueError("a window position lies outside the cache")
     return out, lse

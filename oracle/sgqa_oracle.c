@@ -281,3 +281,55 @@ int orc_sparse_attention(const uint16_t *q, const int64_t *t, int64_t nrows,
     }
     return bad ? -1 : 0;
 }
+
+/*
+ * Gated sliding-window attention, the sibling layer type (ai.info "Why StepFun
+ * chose 92 transformer blocks": the efficient layers use Gated Sliding Window
+ * Attention; phantomic12 config.json: sliding_window 512).  Reading: the window
+ * is the W most recent positions, the query's own included, so a query at t
+ * attends to max(0, t-W+1) .. t.  Writes the positions and returns the count.
+ */
+int64_t orc_window_token_set(int64_t t, int64_t W, int64_t *tokens)
+{
+    int64_t first = t - W + 1;
+    if (first < 0)
+        first = 0;
+    int64_t n = 0;
+    for (int64_t s = first; s <= t; ++s)
+        tokens[n++] = s;
+    return n;
+}
+
+/*
+ * Window attention for a batch of query rows with the cache on the host; same
+ * arithmetic as orc_attend.  Shapes as orc_sparse_attention, no selection.
+ */
+int orc_window_attention(const uint16_t *q, const int64_t *t, int64_t nrows, const uint16_t *K,
+                         const uint16_t *V, int64_t L, const uint16_t *G, int64_t W, int32_t Hq,
+                         int32_t Hkv, int32_t d, double scale, double *out, double *lse)
+{
+    int bad = 0;
+    const int64_t row = (int64_t)Hkv * d;
+#pragma omp parallel for schedule(dynamic, 1) reduction(| : bad)
+    for (int64_t r = 0; r < nrows; ++r) {
+        const int64_t cap = W < t[r] + 1 ? W : t[r] + 1;
+        int64_t *tok = (int64_t *)malloc((size_t)(cap > 0 ? cap : 1) * sizeof(int64_t));
+        const int64_t n = orc_window_token_set(t[r], W, tok);
+        uint16_t *kr = (uint16_t *)malloc((size_t)(n > 0 ? n : 1) * row * sizeof(uint16_t));
+        uint16_t *vr = (uint16_t *)malloc((size_t)(n > 0 ? n : 1) * row * sizeof(uint16_t));
+        for (int64_t i = 0; i < n; ++i) {
+            if (tok[i] < 0 || tok[i] >= L) {
+                bad = 1;
+                tok[i] = 0;
+            }
+            memcpy(kr + i * row, K + tok[i] * row, (size_t)row * sizeof(uint16_t));
+            memcpy(vr + i * row, V + tok[i] * row, (size_t)row * sizeof(uint16_t));
+        }
+        orc_attend(q + r * (int64_t)Hq * d, kr, vr, n, G + r * (int64_t)Hq, Hq, Hkv, d, scale,
+                   out + r * (int64_t)Hq * d, lse ? lse + r * (int64_t)Hq : NULL);
+        free(kr);
+        free(vr);
+        free(tok);
+    }
+    return bad ? -1 : 0;
+}

@@ -319,6 +319,47 @@ def pin_coverage_identity(lib):
         np.testing.assert_allclose(np.exp(lse_s[:, h] - lse_d[:, h]), mass, rtol=1e-12, atol=1e-14)
 
 
+# --------------------------------------------------------------------------- sliding window
+def pin_window_dense_and_band(lib):
+    """Window covering the whole prefix is dense causal attention; any window equals SDPA
+    under the band mask t-W < s <= t (torch, fp64)."""
+    p = small_problem(seed=9)
+    L, Hkv, d = p["K"].shape
+    scale = 1.0 / math.sqrt(d)
+    t = np.arange(L, dtype=np.int64)
+    for W in (L, 1000, 17, 8, 2):
+        out, _ = oracle.window_attention(p["Q"], t, p["K"], p["V"], p["G"], W, scale, lib=lib)
+        s_ = np.arange(L)
+        band = (s_[None, :] <= t[:, None]) & (s_[None, :] > t[:, None] - W)
+        np.testing.assert_allclose(out, sdpa_reference(p, band, scale), rtol=0, atol=1e-12)
+
+
+def pin_window_one_closed_form(lib):
+    """W = 1: each query sees only itself, out = sigmoid(G) V[t] and lse = its own logit."""
+    p = small_problem(seed=10)
+    L, Hkv, d = p["K"].shape
+    Hq = p["Q"].shape[1]
+    t = np.arange(L, dtype=np.int64)
+    out, lse = oracle.window_attention(p["Q"], t, p["K"], p["V"], p["G"], 1, 1.0 / math.sqrt(d),
+                                       lib=lib)
+    Qw, Kw, Vw, Gw = widen(p["Q"]), widen(p["K"]), widen(p["V"]), widen(p["G"])
+    for h in range(Hq):
+        g = h // (Hq // Hkv)
+        np.testing.assert_allclose(out[:, h], Vw[:, g] / (1 + np.exp(-Gw[:, h]))[:, None],
+                                   rtol=0, atol=1e-15)
+        z = np.einsum("td,td->t", Qw[:, h], Kw[:, g]) / math.sqrt(d)
+        np.testing.assert_allclose(lse[:, h], z, rtol=0, atol=1e-12)
+
+
+def pin_window_token_count(lib):
+    """The window holds min(W, t+1) positions ending at t."""
+    for t_, W in ((0, 512), (5, 512), (511, 512), (512, 512), (100000, 512), (7, 1)):
+        toks = np.empty(max(1, W), dtype=np.int64)
+        n = lib.orc_window_token_set(t_, W, oracle._ptr(toks))
+        assert n == min(W, t_ + 1)
+        assert toks[n - 1] == t_ and toks[0] == t_ - n + 1
+
+
 ALL_PINS = [
     pin_index_b1_identity,
     pin_index_closed_form,
@@ -333,4 +374,7 @@ ALL_PINS = [
     pin_attention_constant_keys,
     pin_attention_bounds,
     pin_coverage_identity,
+    pin_window_dense_and_band,
+    pin_window_one_closed_form,
+    pin_window_token_count,
 ]

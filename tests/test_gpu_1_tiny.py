@@ -204,3 +204,34 @@ def test_decode_topk_many_chunks(k):
         got = idx[b, 0].cpu().numpy()
         assert parity.check_selection(got, sc[0], c, k, ref[0]) or c > 1000
         parity.check_sel_scores(sel[b, 0].cpu().numpy(), got, sc[0], c, k)
+
+
+@pytest.mark.parametrize("window", [1, 8, 17, 512, 5000])
+def test_tiny_sliding_window_every_row(tiny, tiny_host, window):
+    """Gated sliding-window attention on every row of the tiny layer, against the oracle."""
+    shape = WL.shape
+    out = torch.empty_like(tiny["Q"])
+    lse = torch.empty((WL.T, shape.num_q_heads), dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(shape.head_dim)
+    sgqa.swa_prefill(shape, tiny["Q"], tiny["K"], tiny["V"], tiny["G"], 0, WL.L, window, scale,
+                     out, lse)
+    torch.cuda.synchronize()
+    t = np.arange(WL.T)
+    o_ref, l_ref = oracle.window_attention(bits(tiny["Q"]), t, tiny_host[0], tiny_host[1],
+                                           bits(tiny["G"]), window, scale)
+    parity.check_attention(bits(out), o_ref, lse.cpu().numpy(), l_ref)
+
+
+def test_tiny_sliding_window_chunk_mid_sequence(tiny, tiny_host):
+    """Queries [300, 700) of a 700-token cache with a window of 64."""
+    shape = WL.shape
+    q0, L, W = 300, 700, 64
+    out = torch.empty_like(tiny["Q"][q0:L])
+    scale = 1.0 / math.sqrt(shape.head_dim)
+    sgqa.swa_prefill(shape, tiny["Q"][q0:L], tiny["K"][:L], tiny["V"][:L], tiny["G"][q0:L], q0, L,
+                     W, scale, out)
+    torch.cuda.synchronize()
+    t = np.arange(q0, L)
+    o_ref, _ = oracle.window_attention(bits(tiny["Q"][q0:L]), t, tiny_host[0][:L],
+                                       tiny_host[1][:L], bits(tiny["G"][q0:L]), W, scale)
+    parity.check_attention(bits(out), o_ref)

@@ -3,6 +3,7 @@ at least one pin catches it.  This is how the pins are shown to be sensitive: a 
 term, a wrong sign or index, or a transposed operand anywhere in the oracle fails one."""
 import os
 import subprocess
+import sys
 
 import pytest
 
@@ -35,7 +36,26 @@ MUTANTS = [
     ("no-normalisation", "out[h * d + i] = (acc / Z) * gate_factor;", "out[h * d + i] = acc * gate_factor;"),
     ("lse-drops-max", "lse[h] = m + log(Z);", "lse[h] = log(Z);"),
     ("softmax-no-max-shift", "z[s] = exp(z[s] - m);", "z[s] = exp(z[s]);"),
+    ("window-one-too-wide", "int64_t first = t - W + 1;", "int64_t first = t - W;"),
+    ("window-excludes-self", "for (int64_t s = first; s <= t; ++s)", "for (int64_t s = first; s < t; ++s)"),
 ]
+
+
+RUNNER = """
+import sys
+sys.path.insert(0, {tests!r})
+sys.path.insert(0, {root!r})
+import oracle
+from pins import ALL_PINS
+lib = oracle.load({lib!r})
+caught = []
+for pin in ALL_PINS:
+    try:
+        pin(lib)
+    except (AssertionError, ValueError, FloatingPointError):
+        caught.append(pin.__name__)
+print("CAUGHT", ",".join(caught))
+"""
 
 
 @pytest.mark.parametrize("name,orig,bad", MUTANTS, ids=[m[0] for m in MUTANTS])
@@ -46,11 +66,13 @@ def test_pins_catch_planted_mistake(name, orig, bad, tmp_path):
     mut_src.write_text(src.replace(orig, bad))
     lib_path = str(tmp_path / "libmutant.so")
     oracle.build(force=True, src=str(mut_src), out=lib_path)
-    lib = oracle.load(lib_path)
-    caught = []
-    for pin in ALL_PINS:
-        try:
-            pin(lib)
-        except (AssertionError, ValueError, FloatingPointError):
-            caught.append(pin.__name__)
+    # each mutant runs in its own process: a planted mistake may also crash (e.g. write past
+    # a buffer sized for the correct token count), which counts as caught
+    tests_dir = os.path.dirname(os.path.abspath(__file__))
+    code = RUNNER.format(tests=tests_dir, root=os.path.dirname(tests_dir), lib=lib_path)
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300)
+    if r.returncode != 0:
+        return  # the mutant crashed under the pins
+    line = [l for l in r.stdout.splitlines() if l.startswith("CAUGHT")][-1]
+    caught = [c for c in line[len("CAUGHT"):].strip().split(",") if c]
     assert caught, f"no pin caught mutant {name}"
