@@ -277,16 +277,21 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a)
 // Decode: one query per sequence against the whole index.
 //  1. k_decode_keys streams kb at HBM rate (one workgroup per 1024 blocks): the MFMA A
 //     operand is the query proxy broadcast to all 16 rows, so row 0 of each 16x16 result
-//     holds 16 block scores; they are stored as order-preserving keys.
-//  2. k_decode_select (one workgroup per sequence) takes a strided sample of 2048 keys and
-//     uses a sample order statistic as a conservative threshold (about twice k-1 keys are
-//     expected above it), compacts the keys at or above it in ascending block order, and
-//     selects exactly among those candidates (ties to the lowest block).  If fewer than k-1
-//     keys clear the threshold, or too many, it selects exactly over all keys instead, so
-//     the result never depends on the sample.
+//     holds 16 block scores; they are stored as order-preserving keys, and the largest
+//     key of every "unit" of 64 consecutive blocks is stored too.
+//  2. k_decode_select (one workgroup per sequence): K* = the (k-1)-th largest unit maximum
+//     is an exact lower bound for the selection (the k-1 best unit maxima are themselves
+//     blocks at or above K*, so the (k-1)-th best block is too), and every selected block
+//     lies in a unit whose maximum is >= K*.  Only those units' keys are read; the blocks
+//     at or above K* among them are selected exactly (ties to the lowest block) and written
+//     in ascending order through an LDS bitmap.  If too many units qualify (heavy ties) it
+//     selects exactly over all keys instead.
 constexpr int kKeysPerWG = 1024;
-constexpr int kSample = 2048;
-constexpr int kCandCap = 4096;
+constexpr int kUnitBlocks = 64;        // consecutive blocks per unit
+constexpr int kUnitsPerWG = kKeysPerWG / kUnitBlocks;
+constexpr int kMaxUnits = 8192;        // LDS words of the select (unit maxima, then bitmap)
+constexpr int kUnitListCap = 4096;
+constexpr int kCandCap = 2048;
 
 template <int P>
 __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
@@ -310,6 +315,7 @@ __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
         af[kk] = as_bf16x8(load16(qp + kk * 32 + q4 * 8));
 
     // waves interleave over the workgroup's 64 groups (adjacent waves read adjacent rows)
+    __shared__ uint32_t kl[kKeysPerWG];
     constexpr int NG = kKeysPerWG / 16;
 #pragma unroll 1
     for (int g0 = wave; g0 < NG; g0 += 4 * U) {
@@ -317,7 +323,7 @@ __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
 #pragma unroll
         for (int u = 0; u < U; ++u) {
             int64_t jb = j0 + (int64_t)(g0 + 4 * u) * 16 + col;
-            if (g0 + 4 * u >= NG || jb >= c)
+            if (jb >= c)
                 jb = j0;  // a valid row; its score is discarded
 #pragma unroll
             for (int kk = 0; kk < P / 32; ++kk)
@@ -329,20 +335,42 @@ __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
 #pragma unroll
             for (int kk = 0; kk < P / 32; ++kk)
                 acc = mfma_16x16x32(af[kk], as_bf16x8(bv[u][kk]), acc);
-            const int64_t j = j0 + (int64_t)(g0 + 4 * u) * 16 + col;
-            if (q4 == 0 && g0 + 4 * u < NG && j < c)
-                keys[j] = score_key(acc[0]);
+            const int jl = (g0 + 4 * u) * 16 + col;
+            if (q4 == 0) {
+                const uint32_t key = j0 + jl < c ? score_key(acc[0]) : 0u;
+                kl[jl] = key;
+                if (j0 + jl < c)
+                    keys[j0 + jl] = key;
+            }
         }
     }
+    __syncthreads();
+    // unit maxima: 16 threads per unit, 4 consecutive keys each, then a 16-lane max
+    uint32_t m4 = 0u;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t v = kl[tid * 4 + e];
+        m4 = v > m4 ? v : m4;
+    }
+#pragma unroll
+    for (int o = 8; o > 0; o >>= 1) {
+        const uint32_t v = (uint32_t)__shfl_xor((int)m4, o);
+        m4 = v > m4 ? v : m4;
+    }
+    if ((tid & 15) == 0)
+        a.umax[(int64_t)s * a.units_ld + (int64_t)blockIdx.x * kUnitsPerWG + (tid >> 4)] = m4;
 }
 
 template <int NT>
 __global__ __launch_bounds__(NT) void k_decode_select(DecodeTopkArgs a)
 {
     __shared__ SelectShared sh;
-    __shared__ uint32_t sample[kSample];
-    __shared__ uint32_t cand_key[kCandCap];
-    __shared__ int32_t cand_idx[kCandCap];
+    __shared__ uint32_t big[kMaxUnits];          // unit maxima, then candidate keys + blocks
+    __shared__ uint16_t units[kUnitListCap];
+    __shared__ int n_cand;
+    uint32_t *cand_key = big;
+    int32_t *cand_idx = reinterpret_cast<int32_t *>(big + kCandCap);
+    uint32_t *bitmap = big + 2 * kCandCap;       // one bit per block, after the candidates
     const int s = blockIdx.x, tid = threadIdx.x;
     const int64_t t = a.pos.v[s];
     const int64_t c = t / a.B;
@@ -373,104 +401,127 @@ __global__ __launch_bounds__(NT) void k_decode_select(DecodeTopkArgs a)
             osc[pos] = key_score(key);
     };
 
-    // 1) threshold from a strided sample
-    const int ns = cn < kSample ? cn : kSample;
-    const int stride = cn / ns;
-    for (int i = tid; i < ns; i += NT)
-        sample[i] = keys[(int64_t)i * stride];
+    // 1) K* = the keep-th largest unit maximum
+    const int nunits = (int)((c + kUnitBlocks - 1) / kUnitBlocks);
+    const uint32_t *um = a.umax + (int64_t)s * a.units_ld;
+    for (int u = tid; u < nunits; u += NT)
+        big[u] = um[u];
     __syncthreads();
-    int r = (2 * keep + stride - 1) / stride + 8;
-    if (r > ns)
-        r = ns;
-    auto sample_at = [&](int i) { return sample[i]; };
-    const uint32_t thresh = radix_select<NT>(sample_at, ns, r, sh).key;
+    auto umax_at = [&](int u) { return big[u]; };
+    // with no more units than blocks to keep, every unit qualifies
+    const uint32_t kstar = nunits <= keep ? 0u : radix_select<NT>(umax_at, nunits, keep, sh).key;
 
-    // 2) count the keys >= thresh: each wave owns a contiguous range of 16-byte vectors and
-    //    walks it 64 vectors (1 KiB) per load; one workgroup scan gives each wave its base
-    constexpr int NW = NT / 64;
-    constexpr int kUnroll = 16;  // 256 KiB of loads in flight per workgroup
-    const int lane = tid & 63, wave = tid >> 6;
-    const u32x4 *kv = reinterpret_cast<const u32x4 *>(keys);
-    const int nvec = (cn + 3) >> 2;
-    const int wper = ((nvec + NW - 1) / NW + 63) & ~63;  // whole 64-vector steps per wave
-    const int w0 = wave * wper;
-    const int w1 = w0 + wper < nvec ? w0 + wper : nvec;
-    auto count_ge = [&](const u32x4 &v, int q) {
-        int n = 0;
-#pragma unroll
-        for (int e = 0; e < 4; ++e)
-            n += (4 * q + e < cn && v[e] >= thresh) ? 1 : 0;
-        return n;
-    };
-    int local = 0;
-    for (int q0 = w0; q0 < w1; q0 += 64 * kUnroll) {
-        u32x4 v[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int q = q0 + u * 64 + lane;
-            v[u] = q < w1 ? kv[q] : u32x4{0u, 0u, 0u, 0u};
-        }
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-            const int q = q0 + u * 64 + lane;
-            if (q < w1)
-                local += count_ge(v[u], q);
-        }
+    // 2) units whose maximum reaches K*, in order
+    int flag = 0;
+    const int per = (nunits + NT - 1) / NT;
+    for (int u = tid * per; u < tid * per + per && u < nunits; ++u)
+        flag += big[u] >= kstar ? 1 : 0;
+    int nu;
+    int pos = block_exclusive_scan<NT>(flag, sh.scan, nu);
+    if (nu <= kUnitListCap) {
+        for (int u = tid * per; u < tid * per + per && u < nunits; ++u)
+            if (big[u] >= kstar)
+                units[pos++] = (uint16_t)u;
     }
-    // wave total on every lane, then the waves' exclusive prefix
-    int wtot = local;
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1)
-        wtot += __shfl_xor(wtot, o);
-    int total;
-    const int wbase = block_exclusive_scan<NT>(lane == 0 ? wtot : 0, sh.scan, total);
-    const int base0 = __shfl(wbase, 0);
+    if (tid == 0)
+        n_cand = 0;
+    __syncthreads();
 
-    if (total >= keep && total <= kCandCap) {
-        // 3) candidates in ascending block order (per-step wave scans), then an exact
-        //    selection among them
-        int run = base0;
-        for (int q0 = w0; q0 < w1; q0 += 64 * kUnroll) {
-            u32x4 v[kUnroll];
+    if (nu <= kUnitListCap) {
+        // 3) the blocks of those units that reach K* (16 independent loads per unit)
+        const int nwords = (cn + 31) >> 5;
+        for (int w = tid; w < nwords; w += NT)
+            bitmap[w] = 0u;
+        bool overflow = false;
+        constexpr int kG = 8;  // loads in flight per thread; a unit is 256 contiguous bytes
+        for (int e0 = 0; e0 < nu * kUnitBlocks; e0 += NT * kG) {
+            uint32_t kv[kG];
+            int64_t jv[kG];
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int q = q0 + u * 64 + lane;
-                v[u] = q < w1 ? kv[q] : u32x4{0u, 0u, 0u, 0u};
+            for (int b = 0; b < kG; ++b) {
+                const int e = e0 + b * NT + tid;
+                jv[b] = e < nu * kUnitBlocks
+                            ? (int64_t)units[e / kUnitBlocks] * kUnitBlocks + (e % kUnitBlocks)
+                            : (int64_t)cn;
             }
 #pragma unroll
-            for (int u = 0; u < kUnroll; ++u) {
-                const int q = q0 + u * 64 + lane;
-                const int n = q < w1 ? count_ge(v[u], q) : 0;
-                const int incl = wave_inclusive_scan(n);
-                int p = run + incl - n;
+            for (int b = 0; b < kG; ++b)
+                kv[b] = jv[b] < cn ? keys[jv[b]] : 0u;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int j = 4 * q + e;
-                    if (q < w1 && j < cn && v[u][e] >= thresh) {
-                        cand_key[p] = v[u][e];
-                        cand_idx[p] = j;
-                        ++p;
+            for (int b = 0; b < kG; ++b) {
+                if (jv[b] < cn && kv[b] >= kstar) {
+                    const int slot = atomicAdd(&n_cand, 1);
+                    if (slot < kCandCap) {
+                        cand_key[slot] = kv[b];
+                        cand_idx[slot] = (int32_t)jv[b];
                     }
                 }
-                run += __shfl(incl, 63);
             }
         }
         __syncthreads();
-        auto cand_at = [&](int e) { return cand_key[e]; };
-        const KthKey th = radix_select<NT>(cand_at, total, keep, sh);
-        emit_selected<NT>(cand_at, total, th, keep, sh,
-                          [&](int p, int e, uint32_t key) { emit(p, cand_idx[e], key); });
-    } else {
-        // the sample missed (rare): exact selection over every key
-        auto key_at = [&](int j) { return keys[j]; };
-        const KthKey th = radix_select<NT>(key_at, cn, keep, sh);
-        emit_selected<NT>(key_at, cn, th, keep, sh, emit);
+        const int m = n_cand;
+        overflow = m > kCandCap;
+        if (!overflow) {
+            // 4) exact selection among the candidates, ties to the lowest block
+            auto cand_at = [&](int e) { return cand_key[e]; };
+            const KthKey th = radix_select<NT>(cand_at, m, keep, sh);
+            // keys equal to the threshold: all of them are kept unless there are more than
+            // needed (exact float ties), then the lowest blocks win
+            int n_eq_local = 0;
+            for (int e = tid; e < m; e += NT)
+                n_eq_local += cand_key[e] == th.key ? 1 : 0;
+            int n_eq;
+            block_exclusive_scan<NT>(n_eq_local, sh.scan, n_eq);
+            for (int e = tid; e < m; e += NT) {
+                const uint32_t key = cand_key[e];
+                const int32_t j = cand_idx[e];
+                bool take = key > th.key;
+                if (key == th.key) {
+                    if (n_eq == th.take_eq) {
+                        take = true;
+                    } else {
+                        int rank = 0;  // equal keys with a lower block index
+                        for (int f = 0; f < m; ++f)
+                            rank += (cand_key[f] == key && cand_idx[f] < j) ? 1 : 0;
+                        take = rank < th.take_eq;
+                    }
+                }
+                if (take)
+                    atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+            }
+            __syncthreads();
+            // 5) ascending compaction of the bitmap
+            const int per_w = (nwords + NT - 1) / NT;
+            const int w0 = tid * per_w;
+            int local = 0;
+            for (int w = w0; w < w0 + per_w && w < nwords; ++w)
+                local += __popc(bitmap[w]);
+            int total;
+            int p = block_exclusive_scan<NT>(local, sh.scan, total);
+            for (int w = w0; w < w0 + per_w && w < nwords; ++w) {
+                uint32_t bits = bitmap[w];
+                while (bits && p < keep) {
+                    const int j = (w << 5) + __builtin_ctz(bits);
+                    bits &= bits - 1;
+                    emit(p, j, keys[j]);
+                    ++p;
+                }
+            }
+            return;
+        }
     }
+    // heavy ties: exact selection over every key
+    auto key_at = [&](int j) { return keys[j]; };
+    const KthKey th = radix_select<NT>(key_at, cn, keep, sh);
+    emit_selected<NT>(key_at, cn, th, keep, sh, emit);
 }
 
 bool decode_topk_supported(int64_t max_cand, int k)
 {
-    return k >= 2 && max_cand > 0 && max_cand <= kDecodeMaxCand;
+    // the unit maxima of one sequence and the bitmap of its blocks fit in the select's LDS
+    return k >= 2 && max_cand > 0 && max_cand <= kDecodeMaxCand &&
+           (max_cand + kUnitBlocks - 1) / kUnitBlocks <= kMaxUnits &&
+           (max_cand + 31) / 32 <= kMaxUnits - 2 * kCandCap;
 }
 
 int64_t decode_keys_ld(int64_t max_cand)
@@ -478,9 +529,14 @@ int64_t decode_keys_ld(int64_t max_cand)
     return ((max_cand + kKeysPerWG - 1) / kKeysPerWG) * kKeysPerWG;
 }
 
+int64_t decode_units_ld(int64_t max_cand)
+{
+    return decode_keys_ld(max_cand) / kKeysPerWG * kUnitsPerWG;
+}
+
 size_t decode_topk_workspace(int nseq, int64_t max_cand)
 {
-    return (size_t)nseq * decode_keys_ld(max_cand) * 4;
+    return (size_t)nseq * (decode_keys_ld(max_cand) + decode_units_ld(max_cand)) * 4;
 }
 
 template <int P>

@@ -291,6 +291,8 @@ sgqa_status sgqa_indexer_topk(const sgqa_dims *dims, const sgqa_bf16 *qp, int64_
         da.k = dims->topk_blocks;
         da.keys = static_cast<uint32_t *>(workspace);
         da.keys_ld = sgqa::decode_keys_ld(plan.max_cand);
+        da.umax = da.keys + (size_t)nseq * da.keys_ld;
+        da.units_ld = sgqa::decode_units_ld(plan.max_cand);
         da.idx = idx;
         da.sel_scores = sel_scores;
         return hip_status(sgqa::launch_decode_topk(da, hs), "decode top-k launch");

@@ -54,8 +54,9 @@ struct SelectArgs {
 hipError_t launch_select(const SelectArgs &a, hipStream_t stream);
 
 // Decode-shaped top-k (one query per sequence): score keys for every block, then one
-// selection workgroup per sequence.  The workspace holds keys [nseq][keys_ld] (u32).
-constexpr int64_t kDecodeMaxCand = int64_t(1) << 30;
+// selection workgroup per sequence.  The workspace holds keys [nseq][keys_ld] and unit
+// maxima [nseq][units_ld] (u32).
+constexpr int64_t kDecodeMaxCand = 131072;
 struct DecodeTopkArgs {
     const uint16_t *qp;  // query proxy of sequence s at qp + s * qp_seq_stride
     int64_t qp_seq_stride;
@@ -68,12 +69,15 @@ struct DecodeTopkArgs {
     int32_t k;
     uint32_t *keys;      // [nseq][keys_ld] order-preserving score keys
     int64_t keys_ld;
+    uint32_t *umax;      // [nseq][units_ld] largest key of each 16-block unit
+    int64_t units_ld;
     int32_t *idx;        // [nseq][k]
     float *sel_scores;   // [nseq][k] or null
 };
 // False when the shape is outside the decode path (then the general path is used).
 bool decode_topk_supported(int64_t max_cand, int k);
 int64_t decode_keys_ld(int64_t max_cand);
+int64_t decode_units_ld(int64_t max_cand);
 size_t decode_topk_workspace(int nseq, int64_t max_cand);
 hipError_t launch_decode_topk(const DecodeTopkArgs &a, hipStream_t stream);
 
