@@ -78,6 +78,8 @@ def bench_prefill(steps: int, warmup: int):
     lse = torch.empty((wl.T, s.num_q_heads), dtype=torch.float32, device=dev)
     ws = torch.empty(sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, s, 1, wl.T, wl.L),
                      dtype=torch.uint8, device=dev)
+    ws_attn = torch.empty(sgqa.workspace_bytes(sgqa.OP_ATTN_PREFILL, s, 1, wl.T, wl.L),
+                          dtype=torch.uint8, device=dev)
     scale = 1.0 / math.sqrt(s.head_dim)
     stream = torch.cuda.current_stream(dev)
 
@@ -93,7 +95,7 @@ def bench_prefill(steps: int, warmup: int):
         sgqa.indexer_topk(s, d["qp"], kb, [wl.q_start], idx, workspace=ws, stream=stream)
         marks.append(ev())
         sgqa.sparse_attn_prefill(s, d["Q"], d["K"], d["V"], d["G"], idx, wl.q_start, wl.L, scale,
-                                 out, lse, stream=stream)
+                                 out, lse, workspace=ws_attn, stream=stream)
         marks.append(ev())
 
     for _ in range(warmup):

@@ -71,7 +71,7 @@ typedef struct {
 } sgqa_dims;
 
 /* Operation ids for sgqa_workspace_bytes. */
-enum { SGQA_OP_INDEXER_TOPK = 1, SGQA_OP_ATTN_DECODE = 2 };
+enum { SGQA_OP_INDEXER_TOPK = 1, SGQA_OP_ATTN_DECODE = 2, SGQA_OP_ATTN_PREFILL = 3 };
 
 /*
  * Block compression (ai4snews Interpretation para. 2; ai.info "Sparse GQA
@@ -128,16 +128,25 @@ sgqa_status sgqa_indexer_topk(const sgqa_dims *dims, const sgqa_bf16 *qp, int64_
  * online; probabilities are rounded to bf16 for PV; out is rounded to bf16.
  * Only the first min(k, c+1) entries of each idx row are read; entries that
  * are -1 or outside [0, c] are skipped.
+ * With a workspace (optional) the selected blocks of each query are visited in
+ * several launches, each over one slice of the history, so that each XCD's L2
+ * holds a smaller working set; the softmax state is carried exactly between
+ * launches, so the result does not depend on the workspace size beyond the
+ * order of fp32 additions.  Rows are processed in chunks that fit it.
  *   q     [dev] [T][Hq][d] bf16        k_cache, v_cache [dev] [L][Hkv][d] bf16
  *   gate  [dev] [T][Hq] bf16 logits    idx [dev] [T][k] int32 (as produced above)
  *   out   [dev] [T][Hq][d] bf16        lse [dev] [T][Hq] fp32, may be NULL
+ *   workspace [dev] NULL, or >= sgqa_workspace_bytes(SGQA_OP_ATTN_PREFILL, dims,
+ *                   1, 1, L) bytes (one row); sgqa_workspace_bytes with T rows
+ *                   gives the size for a single chunk
  * Requires q_start + T <= L.
  */
 sgqa_status sgqa_sparse_attn_prefill(const sgqa_dims *dims, const sgqa_bf16 *q,
                                      const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
                                      const sgqa_bf16 *gate, const int32_t *idx, int64_t q_start,
                                      int32_t T, int64_t L, float softmax_scale, sgqa_bf16 *out,
-                                     float *lse, void *stream);
+                                     float *lse, void *workspace, size_t workspace_bytes,
+                                     void *stream);
 
 /*
  * Gated sparse GQA attention, decode: one new query per sequence at position
@@ -178,11 +187,12 @@ sgqa_status sgqa_swa_prefill(const sgqa_dims *dims, const sgqa_bf16 *q, const sg
                              sgqa_bf16 *out, float *lse, void *stream);
 
 /*
- * Workspace size in bytes for `op` (SGQA_OP_INDEXER_TOPK or
- * SGQA_OP_ATTN_DECODE) given nseq sequences of T queries and caches of at
+ * Workspace size in bytes for `op` (SGQA_OP_INDEXER_TOPK, SGQA_OP_ATTN_DECODE or
+ * SGQA_OP_ATTN_PREFILL) given nseq sequences of T queries and caches of at
  * most Lmax tokens.  For the indexer this is the size that lets one pass cover
  * all rows, capped at 2 GiB; smaller buffers (down to one 64-row pass) also
- * work.  Returns 0 for invalid arguments.
+ * work.  For the prefill attention it is the state of min(T, 32768) rows.
+ * Returns 0 for invalid arguments.
  */
 size_t sgqa_workspace_bytes(int op, const sgqa_dims *dims, int32_t nseq, int32_t T, int64_t Lmax);
 

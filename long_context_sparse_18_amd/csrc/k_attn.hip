@@ -267,6 +267,41 @@ __device__ __forceinline__ void store_row(const WaveState<D> &st, const AttnArgs
     }
 }
 
+// Between the launches of a sliced prefill each wave parks its raw register state (the
+// 4*(D/16) accumulator values, max and the two partial sums of every lane) in the
+// workspace, in lane order, so the next launch resumes exactly where this one stopped.
+template <int D>
+constexpr int state_floats()
+{
+    return 4 * (D / 16) + 4;  // + m, l, l32, pad
+}
+
+__device__ __forceinline__ int64_t state_offset(const AttnArgs &a, int64_t r, int g)
+{
+    return ((r * a.Hkv + g) * 64) * (int64_t)a.state_stride + (threadIdx.x & 63) * a.state_stride;
+}
+
+template <int D>
+__device__ __forceinline__ void save_state(const WaveState<D> &st, float *p)
+{
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt)
+        *reinterpret_cast<f32x4 *>(p + 4 * mt) = st.acc[mt];
+    *reinterpret_cast<f32x4 *>(p + 4 * (D / 16)) = f32x4{st.m, st.l, st.l32, 0.f};
+}
+
+template <int D>
+__device__ __forceinline__ void load_state(WaveState<D> &st, const float *p)
+{
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt)
+        st.acc[mt] = *reinterpret_cast<const f32x4 *>(p + 4 * mt);
+    const f32x4 v = *reinterpret_cast<const f32x4 *>(p + 4 * (D / 16));
+    st.m = v[0];
+    st.l = v[1];
+    st.l32 = v[2];
+}
+
 // Row and group of this wave under the two workgroup mappings (see k_attn_prefill).
 // Returns false for waves past the last row.
 template <bool kGroupPerXcd>
@@ -310,12 +345,40 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
     bf16x8 qf[D / 32];
     load_q<D>(a.q + (r * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
     WaveState<D> st;
-    init_state<D>(st);
-    const SparseTokens src{a.idx + r * a.k, 0, nvalid, t, c, a.B};
+    int e_lo = 0, e_hi = nvalid;
+    if (a.nslices > 1) {
+        // this launch covers the blocks in [c*s/S, c*(s+1)/S) (the last slice also holds the
+        // own block c); the idx row is ascending, so that is a contiguous run of entries
+        const int64_t lo = c * a.slice / a.nslices;
+        const int64_t hi = a.slice + 1 == a.nslices ? c + 1 : c * (a.slice + 1) / a.nslices;
+        const int32_t *row = a.idx + r * a.k;
+        const int lane = threadIdx.x & 63;
+        int below_lo = 0, below_hi = 0;
+        for (int e = lane; e < nvalid; e += 64) {
+            const int32_t b = row[e];
+            below_lo += (b >= 0 && b < lo) ? 1 : 0;
+            below_hi += (b >= 0 && b < hi) ? 1 : 0;
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            below_lo += __shfl_xor(below_lo, o);
+            below_hi += __shfl_xor(below_hi, o);
+        }
+        e_lo = below_lo;
+        e_hi = a.slice + 1 == a.nslices ? nvalid : below_hi;
+    }
+    if (a.slice == 0)
+        init_state<D>(st);
+    else
+        load_state<D>(st, a.state + state_offset(a, r, g));
+    const SparseTokens src{a.idx + r * a.k, e_lo, e_hi, t, c, a.B};
     attend_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D, a.Hkv, src, qf, a.scale_log2,
                     lds + wave * kSlots * (D + 4), st);
 
-    store_row<D>(st, a, r, g, hpg);
+    if (a.slice + 1 >= a.nslices)
+        store_row<D>(st, a, r, g, hpg);
+    else
+        save_state<D>(st, a.state + state_offset(a, r, g));
 }
 
 // Gated sliding-window attention: the same per-(token, group) wave over the contiguous
@@ -470,6 +533,34 @@ static hipError_t launch_prefill_d(const AttnArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
+// Sliced prefill: rows in chunks that fit the workspace, each chunk in `nslices` launches.
+template <int D>
+static hipError_t launch_prefill_sliced(const AttnArgs &a0, hipStream_t stream)
+{
+    const int64_t per_row = (int64_t)a0.Hkv * 64 * a0.state_stride * sizeof(float);
+    int64_t chunk = a0.state_bytes / per_row;
+    if (chunk > a0.rows)
+        chunk = a0.rows;
+    for (int64_t r0 = 0; r0 < a0.rows; r0 += chunk) {
+        AttnArgs a = a0;
+        const int64_t n = a0.rows - r0 < chunk ? a0.rows - r0 : chunk;
+        a.rows = (int32_t)n;
+        a.q_start = a0.q_start + r0;
+        a.q = a0.q + r0 * a0.Hq * D;
+        a.gate = a0.gate + r0 * a0.Hq;
+        a.idx = a0.idx + r0 * a0.k;
+        a.out = a0.out + r0 * a0.Hq * D;
+        a.lse = a0.lse ? a0.lse + r0 * a0.Hq : nullptr;
+        for (int sl = 0; sl < a0.nslices; ++sl) {
+            a.slice = sl;
+            hipError_t e = launch_prefill_d<D, false>(a, stream);
+            if (e != hipSuccess)
+                return e;
+        }
+    }
+    return hipSuccess;
+}
+
 template <int D>
 static hipError_t launch_decode_d(const AttnArgs &a, hipStream_t stream)
 {
@@ -489,12 +580,25 @@ hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream)
 {
     if (a.rows <= 0)
         return hipSuccess;
+    if (a.nslices > 1) {
+        switch (a.d) {
+        case 64: return launch_prefill_sliced<64>(a, stream);
+        case 128: return launch_prefill_sliced<128>(a, stream);
+        case 192: return launch_prefill_sliced<192>(a, stream);
+        default: return hipErrorInvalidValue;
+        }
+    }
     switch (a.d) {
     case 64: return launch_prefill_d<64, false>(a, stream);
     case 128: return launch_prefill_d<128, false>(a, stream);
     case 192: return launch_prefill_d<192, false>(a, stream);
     default: return hipErrorInvalidValue;
     }
+}
+
+int prefill_state_stride(int d)
+{
+    return 4 * (d / 16) + 4;
 }
 
 hipError_t launch_swa(const AttnArgs &a, hipStream_t stream)

@@ -101,10 +101,18 @@ struct AttnArgs {
     int32_t nsplit;
     int32_t entries_per_split;
     int64_t window;          // sliding-window attention: tokens per window
+    // sliced prefill: launch `slice` of `nslices` over each query's blocks, parking the
+    // per-lane softmax state (state_stride floats per lane) in `state`
+    int32_t nslices;
+    int32_t slice;
+    float *state;
+    int64_t state_bytes;
+    int32_t state_stride;
 };
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_swa(const AttnArgs &a, hipStream_t stream);
+int prefill_state_stride(int d);
 
 // Decode split-K geometry for k selected entries of B tokens.
 void decode_split_plan(int k, int B, int &nsplit, int &entries_per_split);

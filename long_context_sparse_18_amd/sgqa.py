@@ -20,6 +20,7 @@ _lib = None
 OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
 OP_INDEXER_TOPK = 1
 OP_ATTN_DECODE = 2
+OP_ATTN_PREFILL = 3
 
 EXPORTS = ("sgqa_index_build", "sgqa_indexer_topk", "sgqa_sparse_attn_prefill",
            "sgqa_sparse_attn_decode", "sgqa_swa_prefill", "sgqa_workspace_bytes",
@@ -64,7 +65,7 @@ def load():
     lib.sgqa_indexer_topk.argtypes = [dp, p, i64, p, i64, p, i32, i32, p, p, p, sz, p]
     lib.sgqa_sparse_attn_prefill.restype = st
     lib.sgqa_sparse_attn_prefill.argtypes = [dp, p, p, p, p, p, i64, i32, i64, ctypes.c_float, p,
-                                             p, p]
+                                             p, p, sz, p]
     lib.sgqa_sparse_attn_decode.restype = st
     lib.sgqa_sparse_attn_decode.argtypes = [dp, p, p, p, i64, p, p, p, i32, ctypes.c_float, p, p,
                                             p, sz, p]
@@ -149,12 +150,16 @@ def indexer_topk(shape: LayerShape, qp: torch.Tensor, kb: torch.Tensor, q_start,
 
 
 def sparse_attn_prefill(shape: LayerShape, q, k_cache, v_cache, gate, idx, q_start: int, L: int,
-                        softmax_scale: float, out, lse=None, stream=None):
-    _need_cuda(q, k_cache, v_cache, gate, idx, out, lse)
+                        softmax_scale: float, out, lse=None, workspace=None, stream=None):
+    """Sparse attention for q [T, Hq, d]; ``workspace`` (optional, uint8 device tensor) enables
+    the history-sliced launches."""
+    _need_cuda(q, k_cache, v_cache, gate, idx, out, lse, workspace)
     d = Dims.of(shape)
+    ws_bytes = workspace.numel() if workspace is not None else 0
     check(load().sgqa_sparse_attn_prefill(ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                           _ptr(gate), _ptr(idx), q_start, q.shape[0], L,
-                                          softmax_scale, _ptr(out), _ptr(lse), _stream(stream, q)))
+                                          softmax_scale, _ptr(out), _ptr(lse), _ptr(workspace),
+                                          ws_bytes, _stream(stream, q)))
 
 
 def sparse_attn_decode(shape: LayerShape, q, k_cache, v_cache, gate, idx, cache_lens,

@@ -19,7 +19,8 @@ def say(msg: str):
     sys.stdout.flush()
 
 
-def run_prefill(shape, d, q_start: int, L: int, workspace=None, kb=None, build_index=True):
+def run_prefill(shape, d, q_start: int, L: int, workspace=None, kb=None, build_index=True,
+                attn_workspace=None):
     """index_build -> indexer_topk -> sparse_attn_prefill for one sequence."""
     dev = d["Q"].device
     T = d["Q"].shape[0]
@@ -35,7 +36,7 @@ def run_prefill(shape, d, q_start: int, L: int, workspace=None, kb=None, build_i
     out = torch.empty_like(d["Q"])
     lse = torch.empty((T, shape.num_q_heads), dtype=torch.float32, device=dev)
     sgqa.sparse_attn_prefill(shape, d["Q"], d["K"], d["V"], d["G"], idx, q_start, L,
-                             1.0 / math.sqrt(shape.head_dim), out, lse)
+                             1.0 / math.sqrt(shape.head_dim), out, lse, workspace=attn_workspace)
     torch.cuda.synchronize()
     return dict(kb=kb, idx=idx, sel=sel, out=out, lse=lse)
 

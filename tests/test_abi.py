@@ -49,7 +49,8 @@ def call_prefill(d, **kw):
     a.update(kw)
     return sgqa.load().sgqa_sparse_attn_prefill(ctypes.byref(d), a["q"], a["k"], a["v"], a["g"],
                                                 a["idx"], a["q_start"], a["T"], a["L"], a["scale"],
-                                                a["out"], a["lse"], None)
+                                                a["out"], a["lse"], a.get("ws"), a.get("wsb", 0),
+                                                None)
 
 
 @pytest.mark.parametrize("kw,want", [
@@ -75,6 +76,8 @@ def test_prefill_rejects_bad_sizes_and_pointers():
     assert call_prefill(d, out=None) == sgqa.ERR_NULL
     assert call_prefill(d, q=ctypes.c_void_p((1 << 20) + 2)) == sgqa.ERR_SHAPE  # misaligned
     assert call_prefill(d, scale=float("inf")) == sgqa.ERR_SHAPE
+    assert call_prefill(d, ws=FAKE, wsb=100) == sgqa.ERR_WORKSPACE
+    assert call_prefill(d, ws=ctypes.c_void_p((1 << 20) + 8), wsb=1 << 30) == sgqa.ERR_SHAPE
     assert call_prefill(d, T=0) == sgqa.OK  # nothing to do, no HIP call
     assert sgqa.load().sgqa_last_error() == b""
     assert call_prefill(d, q_start=10, T=16, L=20) == sgqa.ERR_SHAPE
@@ -84,7 +87,7 @@ def test_prefill_rejects_bad_sizes_and_pointers():
 def test_null_dims():
     lib = sgqa.load()
     assert lib.sgqa_sparse_attn_prefill(None, FAKE, FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 0.1, FAKE,
-                                        None, None) == sgqa.ERR_NULL
+                                        None, None, 0, None) == sgqa.ERR_NULL
 
 
 def test_indexer_validation():

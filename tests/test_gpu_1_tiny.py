@@ -66,6 +66,23 @@ def test_tiny_dense_selection_matches_sdpa(tiny):
     assert ((got - o).norm() / o.norm()).item() < 5e-3
 
 
+@pytest.mark.parametrize("rows_per_chunk", [1000, 300, 1])
+def test_tiny_sliced_prefill_matches(tiny, tiny_host, rows_per_chunk):
+    """With a workspace the selected blocks are visited in history slices, with the softmax
+    state carried between launches, in row chunks that fit the workspace: same result as the
+    single pass up to fp32 summation order, and oracle parity on every row."""
+    shape = WL.shape
+    per_row = sgqa.workspace_bytes(sgqa.OP_ATTN_PREFILL, shape, 1, 1, WL.L)
+    ws = torch.empty(per_row * rows_per_chunk, dtype=torch.uint8, device=DEV)
+    one = run_prefill(shape, tiny, 0, WL.L)
+    sliced = run_prefill(shape, tiny, 0, WL.L, attn_workspace=ws)
+    assert torch.equal(one["idx"], sliced["idx"])
+    diff = (one["out"].float() - sliced["out"].float()).abs().max().item()
+    assert diff <= 2 ** -6, diff
+    st = check_prefill_rows(shape, tiny, sliced, 0, np.arange(WL.T), host_cache=tiny_host)
+    say(f"tiny sliced ({rows_per_chunk} rows/chunk): {st}")
+
+
 def test_tiny_deterministic(tiny):
     a = run_prefill(WL.shape, tiny, 0, WL.L)
     b = run_prefill(WL.shape, tiny, 0, WL.L)
