@@ -277,19 +277,22 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a)
 // Decode: one query per sequence against the whole index.
 //  1. k_decode_keys streams kb at HBM rate (one workgroup per 1024 blocks): the MFMA A
 //     operand is the query proxy broadcast to all 16 rows, so row 0 of each 16x16 result
-//     holds 16 block scores; they are stored as order-preserving keys, and the largest
-//     key of every "unit" of 64 consecutive blocks is stored too.
+//     holds the scores of 16 consecutive blocks; they are stored as order-preserving keys,
+//     and their largest key (the maximum of that "unit" of 16 blocks) is stored too.
 //  2. k_decode_select (one workgroup per sequence): K* = the (k-1)-th largest unit maximum
-//     is an exact lower bound for the selection (the k-1 best unit maxima are themselves
-//     blocks at or above K*, so the (k-1)-th best block is too), and every selected block
-//     lies in a unit whose maximum is >= K*.  Only those units' keys are read; the blocks
-//     at or above K* among them are selected exactly (ties to the lowest block) and written
-//     in ascending order through an LDS bitmap.  If too many units qualify (heavy ties) it
-//     selects exactly over all keys instead.
+//     is a lower bound for the selection (the k-1 best unit maxima are themselves blocks
+//     at or above K*, so the (k-1)-th best block is too), and so is any K' <= K*; every
+//     selected block lies in a unit whose maximum is >= K'.  K' is the lower edge of the
+//     histogram bin that holds K* (one pass, the digit taken just below the bits all maxima
+//     share).  Only the qualifying units' keys are read; the blocks at or above K' among
+//     them are selected exactly (ties to the lowest block) and written in ascending order
+//     from per-word prefix counts of an LDS bitmap.  If too many units or candidates
+//     qualify (heavy ties) it selects exactly over all keys instead.
 constexpr int kKeysPerWG = 1024;
-constexpr int kUnitBlocks = 64;        // consecutive blocks per unit
+constexpr int kUnitBlocks = 16;        // consecutive blocks per unit (one MFMA result row)
 constexpr int kUnitsPerWG = kKeysPerWG / kUnitBlocks;
-constexpr int kMaxUnits = 8192;        // LDS words of the select (unit maxima, then bitmap)
+constexpr int kMaxUnits = 8192;        // unit maxima one select workgroup holds
+constexpr int kBitmapWords = 4096;     // one bit per candidate block
 constexpr int kUnitListCap = 4096;
 constexpr int kCandCap = 2048;
 
@@ -314,15 +317,15 @@ __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
     for (int kk = 0; kk < P / 32; ++kk)
         af[kk] = as_bf16x8(load16(qp + kk * 32 + q4 * 8));
 
-    // waves interleave over the workgroup's 64 groups (adjacent waves read adjacent rows)
-    __shared__ uint32_t kl[kKeysPerWG];
-    constexpr int NG = kKeysPerWG / 16;
+    // waves interleave over the workgroup's 64 units (adjacent waves read adjacent rows)
+    uint32_t *umax = a.umax + (int64_t)s * a.units_ld + (int64_t)blockIdx.x * kUnitsPerWG;
+    constexpr int NG = kKeysPerWG / kUnitBlocks;
 #pragma unroll 1
     for (int g0 = wave; g0 < NG; g0 += 4 * U) {
         u32x4 bv[U][P / 32];
 #pragma unroll
         for (int u = 0; u < U; ++u) {
-            int64_t jb = j0 + (int64_t)(g0 + 4 * u) * 16 + col;
+            int64_t jb = j0 + (int64_t)(g0 + 4 * u) * kUnitBlocks + col;
             if (jb >= c)
                 jb = j0;  // a valid row; its score is discarded
 #pragma unroll
@@ -335,42 +338,115 @@ __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
 #pragma unroll
             for (int kk = 0; kk < P / 32; ++kk)
                 acc = mfma_16x16x32(af[kk], as_bf16x8(bv[u][kk]), acc);
-            const int jl = (g0 + 4 * u) * 16 + col;
+            const int64_t j = j0 + (int64_t)(g0 + 4 * u) * kUnitBlocks + col;
+            const uint32_t key = j < c ? score_key(acc[0]) : 0u;
+            // unit maximum over the 16 lanes of this lane's row group (xor stays inside it)
+            uint32_t m = key;
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) {
+                const uint32_t v = (uint32_t)__shfl_xor((int)m, o);
+                m = v > m ? v : m;
+            }
             if (q4 == 0) {
-                const uint32_t key = j0 + jl < c ? score_key(acc[0]) : 0u;
-                kl[jl] = key;
-                if (j0 + jl < c)
-                    keys[j0 + jl] = key;
+                if (j < c)
+                    keys[j] = key;
+                if (col == 0)
+                    umax[g0 + 4 * u] = m;
             }
         }
     }
+}
+
+// Bitwise OR and AND over the workgroup (every thread calls; `red` holds 2 * NT/64 words).
+template <int NT>
+__device__ __forceinline__ void block_or_and(uint32_t &vor, uint32_t &vand, uint32_t *red)
+{
+    constexpr int NW = NT / 64;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+        vor |= (uint32_t)__shfl_xor((int)vor, o);
+        vand &= (uint32_t)__shfl_xor((int)vand, o);
+    }
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    if (lane == 0) {
+        red[w] = vor;
+        red[NW + w] = vand;
+    }
     __syncthreads();
-    // unit maxima: 16 threads per unit, 4 consecutive keys each, then a 16-lane max
-    uint32_t m4 = 0u;
+    vor = 0u;
+    vand = ~0u;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        const uint32_t v = kl[tid * 4 + e];
-        m4 = v > m4 ? v : m4;
+    for (int i = 0; i < NW; ++i) {
+        vor |= red[i];
+        vand &= red[NW + i];
     }
+}
+
+// Reserve `cnt` consecutive slots per lane behind the counter; returns this lane's first.
+__device__ __forceinline__ int wave_append(int cnt, int *counter)
+{
+    const int inc = wave_inclusive_scan(cnt);
+    const int tot = __shfl(inc, 63);
+    int base = 0;
+    if ((threadIdx.x & 63) == 63 && tot > 0)
+        base = atomicAdd(counter, tot);
+    return __shfl(base, 63) + inc - cnt;
+}
+
+// The bin of a 4096-bin histogram that holds the need-th largest counted element:
+// thread t owns bins [4t, 4t + 4).  Results are valid for every thread on return.
+struct BinFind {
+    uint32_t digit;
+    int need;  // rank of the element inside its bin (1 = the bin's largest)
+    int cnt;   // elements in the bin
+    int ge;    // elements in this bin and above
+};
+
+template <int NT>
+__device__ __forceinline__ BinFind find_bin(const uint32_t *hist, int need, int *scan,
+                                            BinFind &res)
+{
+    static_assert(NT * 4 == 4096, "four bins per thread");
+    const int tid = threadIdx.x;
+    const u32x4 h = *reinterpret_cast<const u32x4 *>(hist + 4 * tid);
+    const int local = (int)(h[0] + h[1] + h[2] + h[3]);
+    int total;
+    const int below = block_exclusive_scan<NT>(local, scan, total);
+    const int above = total - below - local;
+    if (above < need && need <= above + local) {
+        int acc = above;
 #pragma unroll
-    for (int o = 8; o > 0; o >>= 1) {
-        const uint32_t v = (uint32_t)__shfl_xor((int)m4, o);
-        m4 = v > m4 ? v : m4;
+        for (int b = 3; b >= 0; --b) {
+            const int hb = (int)h[b];
+            if (acc < need && need <= acc + hb) {
+                res.digit = (uint32_t)(4 * tid + b);
+                res.need = need - acc;
+                res.cnt = hb;
+                res.ge = acc + hb;
+            }
+            acc += hb;
+        }
     }
-    if ((tid & 15) == 0)
-        a.umax[(int64_t)s * a.units_ld + (int64_t)blockIdx.x * kUnitsPerWG + (tid >> 4)] = m4;
+    __syncthreads();
+    return res;
 }
 
 template <int NT>
 __global__ __launch_bounds__(NT) void k_decode_select(DecodeTopkArgs a)
 {
-    __shared__ SelectShared sh;
-    __shared__ uint32_t big[kMaxUnits];          // unit maxima, then candidate keys + blocks
+    constexpr int kPer = kMaxUnits / NT;       // unit maxima per thread
+    constexpr int kCandPer = kCandCap / NT;    // candidates per thread
+    static_assert(kPer * NT == kMaxUnits && kCandPer * NT == kCandCap, "");
+    __shared__ __align__(16) SelectShared sh;  // histogram A (+ scan scratch)
+    __shared__ __align__(16) uint32_t hist_b[4096];
+    __shared__ __align__(16) uint32_t bitmap[kBitmapWords];
+    __shared__ uint32_t cand_key[kCandCap];
+    __shared__ int32_t cand_idx[kCandCap];
     __shared__ uint16_t units[kUnitListCap];
-    __shared__ int n_cand;
-    uint32_t *cand_key = big;
-    int32_t *cand_idx = reinterpret_cast<int32_t *>(big + kCandCap);
-    uint32_t *bitmap = big + 2 * kCandCap;       // one bit per block, after the candidates
+    __shared__ uint32_t red[4 * (NT / 64)];  // two OR/AND reductions
+    __shared__ int n_units, n_cand;
+    __shared__ BinFind bf;
+    uint32_t *hist_a = sh.hist;
     const int s = blockIdx.x, tid = threadIdx.x;
     const int64_t t = a.pos.v[s];
     const int64_t c = t / a.B;
@@ -395,122 +471,220 @@ __global__ __launch_bounds__(NT) void k_decode_select(DecodeTopkArgs a)
     if (keep == 0)
         return;
     const int cn = (int)c;
-    auto emit = [&](int pos, int j, uint32_t key) {
-        out[pos] = j;
-        if (osc)
-            osc[pos] = key_score(key);
-    };
+    const int nunits = (cn + kUnitBlocks - 1) / kUnitBlocks;
 
-    // 1) K* = the keep-th largest unit maximum
-    const int nunits = (int)((c + kUnitBlocks - 1) / kUnitBlocks);
-    const uint32_t *um = a.umax + (int64_t)s * a.units_ld;
-    for (int u = tid; u < nunits; u += NT)
-        big[u] = um[u];
-    __syncthreads();
-    auto umax_at = [&](int u) { return big[u]; };
-    // with no more units than blocks to keep, every unit qualifies
-    const uint32_t kstar = nunits <= keep ? 0u : radix_select<NT>(umax_at, nunits, keep, sh).key;
-
-    // 2) units whose maximum reaches K*, in order
-    int flag = 0;
-    const int per = (nunits + NT - 1) / NT;
-    for (int u = tid * per; u < tid * per + per && u < nunits; ++u)
-        flag += big[u] >= kstar ? 1 : 0;
-    int nu;
-    int pos = block_exclusive_scan<NT>(flag, sh.scan, nu);
-    if (nu <= kUnitListCap) {
-        for (int u = tid * per; u < tid * per + per && u < nunits; ++u)
-            if (big[u] >= kstar)
-                units[pos++] = (uint16_t)u;
+#pragma unroll
+    for (int i = 0; i < 4096 / NT; ++i) {
+        hist_a[i * NT + tid] = 0u;
+        hist_b[i * NT + tid] = 0u;
     }
-    if (tid == 0)
+    for (int w = tid; w < kBitmapWords; w += NT)
+        bitmap[w] = 0u;
+    if (tid == 0) {
+        n_units = 0;
         n_cand = 0;
-    __syncthreads();
+    }
 
+    // 1) K' <= K*: the unit maxima (thread tid holds units b * NT + tid), their common
+    //    leading bits, and one 12-bit histogram below them
+    const uint32_t *um = a.umax + (int64_t)s * a.units_ld;
+    uint32_t mx[kPer];
+    uint32_t vor = 0u, vand = ~0u;
+#pragma unroll
+    for (int b = 0; b < kPer; ++b) {
+        const int u = b * NT + tid;
+        mx[b] = u < nunits ? um[u] : 0u;
+    }
+#pragma unroll
+    for (int b = 0; b < kPer; ++b)
+        if (b * NT + tid < nunits) {
+            vor |= mx[b];
+            vand &= mx[b];
+        }
+    block_or_and<NT>(vor, vand, red);
+    uint32_t kp = 0u;  // with no more units than blocks to keep, every unit qualifies
+    int nu = nunits;
+    if (nunits > keep) {
+        const uint32_t diff = vor ^ vand;
+        if (diff == 0u) {
+            kp = vand;  // all maxima equal
+        } else {
+            const int top = 31 - __builtin_clz(diff);
+            const int width = top + 1 < 12 ? top + 1 : 12;
+            const int shift = top + 1 - width;
+            const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+            for (int b = 0; b < kPer; ++b)
+                if (b * NT + tid < nunits)
+                    atomicAdd(&hist_a[(mx[b] >> shift) & dmask], 1u);
+            __syncthreads();
+            const BinFind r = find_bin<NT>(hist_a, keep, sh.scan, bf);
+            kp = (vand & ~((2u << top) - 1u)) | (r.digit << shift);
+            nu = r.ge;
+#pragma unroll
+            for (int i = 0; i < 4096 / NT; ++i)
+                hist_a[i * NT + tid] = 0u;  // for the third candidate pass
+        }
+    }
+
+    bool exact_done = false;
     if (nu <= kUnitListCap) {
-        // 3) the blocks of those units that reach K* (16 independent loads per unit)
-        const int nwords = (cn + 31) >> 5;
-        for (int w = tid; w < nwords; w += NT)
-            bitmap[w] = 0u;
-        bool overflow = false;
-        constexpr int kG = 8;  // loads in flight per thread; a unit is 256 contiguous bytes
-        for (int e0 = 0; e0 < nu * kUnitBlocks; e0 += NT * kG) {
-            uint32_t kv[kG];
-            int64_t jv[kG];
+        // 2) the qualifying units, in any order
+        int q = 0;
 #pragma unroll
-            for (int b = 0; b < kG; ++b) {
-                const int e = e0 + b * NT + tid;
-                jv[b] = e < nu * kUnitBlocks
-                            ? (int64_t)units[e / kUnitBlocks] * kUnitBlocks + (e % kUnitBlocks)
-                            : (int64_t)cn;
+        for (int b = 0; b < kPer; ++b)
+            q += (b * NT + tid < nunits && mx[b] >= kp) ? 1 : 0;
+        int pos = wave_append(q, &n_units);
+#pragma unroll
+        for (int b = 0; b < kPer; ++b)
+            if (b * NT + tid < nunits && mx[b] >= kp)
+                units[pos++] = (uint16_t)(b * NT + tid);
+        __syncthreads();
+        nu = n_units;
+
+        // 3) their keys at or above K' (16 bytes = 4 blocks per load)
+        const int nchunks = nu * (kUnitBlocks / 4);
+        for (int e0 = 0; e0 < nchunks; e0 += 4 * NT) {
+            u32x4 kv[4];
+            int jc[4];
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int e = e0 + r * NT + tid;
+                jc[r] = e < nchunks ? (int)units[e / (kUnitBlocks / 4)] * kUnitBlocks +
+                                          (e % (kUnitBlocks / 4)) * 4
+                                    : -1;
             }
 #pragma unroll
-            for (int b = 0; b < kG; ++b)
-                kv[b] = jv[b] < cn ? keys[jv[b]] : 0u;
+            for (int r = 0; r < 4; ++r)
+                kv[r] = jc[r] >= 0 ? *reinterpret_cast<const u32x4 *>(keys + jc[r])
+                                   : u32x4{0u, 0u, 0u, 0u};
+            int cnt = 0;
 #pragma unroll
-            for (int b = 0; b < kG; ++b) {
-                if (jv[b] < cn && kv[b] >= kstar) {
-                    const int slot = atomicAdd(&n_cand, 1);
-                    if (slot < kCandCap) {
-                        cand_key[slot] = kv[b];
-                        cand_idx[slot] = (int32_t)jv[b];
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    cnt += (jc[r] >= 0 && jc[r] + i < cn && kv[r][i] >= kp) ? 1 : 0;
+            int slot = wave_append(cnt, &n_cand);
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+#pragma unroll
+                for (int i = 0; i < 4; ++i)
+                    if (jc[r] >= 0 && jc[r] + i < cn && kv[r][i] >= kp) {
+                        if (slot < kCandCap) {
+                            cand_key[slot] = kv[r][i];
+                            cand_idx[slot] = jc[r] + i;
+                        }
+                        ++slot;
                     }
-                }
-            }
         }
         __syncthreads();
         const int m = n_cand;
-        overflow = m > kCandCap;
-        if (!overflow) {
-            // 4) exact selection among the candidates, ties to the lowest block
-            auto cand_at = [&](int e) { return cand_key[e]; };
-            const KthKey th = radix_select<NT>(cand_at, m, keep, sh);
-            // keys equal to the threshold: all of them are kept unless there are more than
-            // needed (exact float ties), then the lowest blocks win
-            int n_eq_local = 0;
-            for (int e = tid; e < m; e += NT)
-                n_eq_local += cand_key[e] == th.key ? 1 : 0;
-            int n_eq;
-            block_exclusive_scan<NT>(n_eq_local, sh.scan, n_eq);
-            for (int e = tid; e < m; e += NT) {
-                const uint32_t key = cand_key[e];
-                const int32_t j = cand_idx[e];
-                bool take = key > th.key;
-                if (key == th.key) {
-                    if (n_eq == th.take_eq) {
-                        take = true;
-                    } else {
-                        int rank = 0;  // equal keys with a lower block index
-                        for (int f = 0; f < m; ++f)
-                            rank += (cand_key[f] == key && cand_idx[f] < j) ? 1 : 0;
-                        take = rank < th.take_eq;
-                    }
+        if (m <= kCandCap) {
+            // 4) exact selection of `keep` candidates: radix passes below their common bits,
+            //    stopping once the threshold bin is taken whole
+            uint32_t ck[kCandPer];
+            int32_t cj[kCandPer];
+            vor = 0u;
+            vand = ~0u;
+#pragma unroll
+            for (int r = 0; r < kCandPer; ++r) {
+                const int e = r * NT + tid;
+                ck[r] = e < m ? cand_key[e] : 0u;
+                cj[r] = e < m ? cand_idx[e] : -1;
+                if (e < m) {
+                    vor |= ck[r];
+                    vand &= ck[r];
                 }
-                if (take)
-                    atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+            }
+            block_or_and<NT>(vor, vand, red + NT / 32);
+            uint32_t P = vand, pmask = ~0u;
+            int need = keep, cnt = m;
+            const uint32_t diff = vor ^ vand;
+            if (diff != 0u) {
+                int top = 31 - __builtin_clz(diff);
+                pmask = ~((2u << top) - 1u);
+                P = vand & pmask;
+#pragma unroll 1
+                for (int pass = 0;; ++pass) {
+                    const int width = top + 1 < 12 ? top + 1 : 12;
+                    const int shift = top + 1 - width;
+                    const uint32_t dmask = (1u << width) - 1u;
+                    uint32_t *H = (pass & 1) ? hist_a : hist_b;
+#pragma unroll
+                    for (int r = 0; r < kCandPer; ++r)
+                        if (cj[r] >= 0 && (ck[r] & pmask) == P)
+                            atomicAdd(&H[(ck[r] >> shift) & dmask], 1u);
+                    __syncthreads();
+                    const BinFind rb = find_bin<NT>(H, need, sh.scan, bf);
+#pragma unroll
+                    for (int i = 0; i < 4096 / NT; ++i)
+                        H[i * NT + tid] = 0u;  // for the pass after next
+                    P |= rb.digit << shift;
+                    pmask |= dmask << shift;
+                    need = rb.need;
+                    cnt = rb.cnt;
+                    if (need == cnt || shift == 0)
+                        break;
+                    top = shift - 1;
+                }
+            }
+            // take: every key above the prefix P; at P, all of them when the count matches,
+            // else (exact ties of the full key) the `need` lowest blocks
+            bool take[kCandPer];
+#pragma unroll
+            for (int r = 0; r < kCandPer; ++r) {
+                take[r] = false;
+                if (cj[r] < 0)
+                    continue;
+                const uint32_t km = ck[r] & pmask;
+                if (km != P) {
+                    take[r] = km > P;
+                } else if (need == cnt) {
+                    take[r] = true;
+                } else {
+                    int rank = 0;
+                    for (int f = 0; f < m; ++f)
+                        rank += (cand_key[f] == ck[r] && cand_idx[f] < cj[r]) ? 1 : 0;
+                    take[r] = rank < need;
+                }
+                if (take[r])
+                    atomicOr(&bitmap[cj[r] >> 5], 1u << (cj[r] & 31));
             }
             __syncthreads();
-            // 5) ascending compaction of the bitmap
-            const int per_w = (nwords + NT - 1) / NT;
-            const int w0 = tid * per_w;
-            int local = 0;
-            for (int w = w0; w < w0 + per_w && w < nwords; ++w)
-                local += __popc(bitmap[w]);
+            // 5) output positions: exclusive prefix of the bitmap popcounts per word
+            uint32_t *wpre = hist_a;
+            static_assert(kBitmapWords == 4 * NT, "four bitmap words per thread");
+            const u32x4 bw = *reinterpret_cast<const u32x4 *>(bitmap + 4 * tid);
+            const int p0 = __popc(bw[0]), p1 = __popc(bw[1]), p2 = __popc(bw[2]);
             int total;
-            int p = block_exclusive_scan<NT>(local, sh.scan, total);
-            for (int w = w0; w < w0 + per_w && w < nwords; ++w) {
-                uint32_t bits = bitmap[w];
-                while (bits && p < keep) {
-                    const int j = (w << 5) + __builtin_ctz(bits);
-                    bits &= bits - 1;
-                    emit(p, j, keys[j]);
-                    ++p;
+            const int before = block_exclusive_scan<NT>(p0 + p1 + p2 + __popc(bw[3]), sh.scan,
+                                                        total);
+            *reinterpret_cast<u32x4 *>(wpre + 4 * tid) =
+                u32x4{(uint32_t)before, (uint32_t)(before + p0), (uint32_t)(before + p0 + p1),
+                      (uint32_t)(before + p0 + p1 + p2)};
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < kCandPer; ++r)
+                if (take[r]) {
+                    const int j = cj[r], w = j >> 5;
+                    const int p = (int)wpre[w] + __popc(bitmap[w] & ((1u << (j & 31)) - 1u));
+                    if (p < keep) {  // exactly `keep` bits are set
+                        out[p] = j;
+                        if (osc)
+                            osc[p] = key_score(ck[r]);
+                    }
                 }
-            }
-            return;
+            exact_done = true;
         }
     }
+    if (exact_done)
+        return;
     // heavy ties: exact selection over every key
+    auto emit = [&](int p, int j, uint32_t key) {
+        out[p] = j;
+        if (osc)
+            osc[p] = key_score(key);
+    };
     auto key_at = [&](int j) { return keys[j]; };
     const KthKey th = radix_select<NT>(key_at, cn, keep, sh);
     emit_selected<NT>(key_at, cn, th, keep, sh, emit);
@@ -521,7 +695,7 @@ bool decode_topk_supported(int64_t max_cand, int k)
     // the unit maxima of one sequence and the bitmap of its blocks fit in the select's LDS
     return k >= 2 && max_cand > 0 && max_cand <= kDecodeMaxCand &&
            (max_cand + kUnitBlocks - 1) / kUnitBlocks <= kMaxUnits &&
-           (max_cand + 31) / 32 <= kMaxUnits - 2 * kCandCap;
+           (max_cand + 31) / 32 <= kBitmapWords;
 }
 
 int64_t decode_keys_ld(int64_t max_cand)

@@ -252,3 +252,61 @@ def test_tiny_sliding_window_chunk_mid_sequence(tiny, tiny_host):
     o_ref, _ = oracle.window_attention(bits(tiny["Q"][q0:L]), t, tiny_host[0][:L],
                                        tiny_host[1][:L], bits(tiny["G"][q0:L]), W, scale)
     parity.check_attention(bits(out), o_ref)
+
+
+def _integer_index(shape, n, nblk, seed):
+    """kb and qp with small integer entries: every score is an exact integer in fp32 and
+    fp64 alike, so heavy exact ties are common and the selection is fully determined by
+    the lowest-index rule."""
+    g = torch.Generator().manual_seed(seed)
+    kb = torch.randint(-2, 3, (n, nblk, shape.proxy_dim), generator=g).to(torch.bfloat16)
+    return kb
+
+
+@pytest.mark.parametrize("k", [16, 512, 3000])
+def test_decode_topk_exact_ties(k):
+    """Decode top-k on integer-valued scores (many exact ties, one all-zero query so that
+    every score ties): the selection and its scores must equal the oracle's exactly."""
+    lens = [1048576, 400003, 9, 5000]
+    n, Lmax = len(lens), max(lens)
+    shape = with_selection(WL.shape, 8, k)
+    nblk = -(-Lmax // 8)
+    kb = _integer_index(shape, n, nblk, 11 + k).to(DEV)
+    g = torch.Generator().manual_seed(5)
+    qp = torch.randint(-2, 3, (n, 1, shape.proxy_dim), generator=g).to(torch.bfloat16)
+    qp[3].zero_()
+    qp = qp.to(DEV)
+    idx = torch.empty((n, 1, k), dtype=torch.int32, device=DEV)
+    sel = torch.empty((n, 1, k), dtype=torch.float32, device=DEV)
+    say(f"decode ties k={k}")
+    sgqa.indexer_topk(shape, qp, kb, [L_ - 1 for L_ in lens], idx, sel)
+    torch.cuda.synchronize()
+    for b, L_ in enumerate(lens):
+        t = np.array([L_ - 1])
+        c = int(t[0] // 8)
+        kbw = parity.widen(bits(kb[b, : -(-L_ // 8)]))
+        sc = oracle.scores(bits(qp[b]), t, 8, kbw, width=max(1, c))
+        ref = oracle.topk(sc, t, 8, k)[0]
+        got = idx[b, 0].cpu().numpy()
+        assert np.array_equal(got, ref), f"seq {b}: selection differs"
+        want = np.where(ref < 0, -np.inf, np.where(ref == c, np.inf, sc[0][np.clip(ref, 0, max(0, c - 1))]))
+        assert np.array_equal(sel[b, 0].cpu().numpy().astype(np.float64), want)
+
+
+def test_prefill_topk_exact_ties():
+    """Prefill top-k (one workgroup per query row) on integer-valued scores: exact."""
+    k, T, q0 = 512, 96, 30000
+    shape = with_selection(WL.shape, 8, k)
+    nblk = -(-(q0 + T) // 8)
+    kb = _integer_index(shape, 1, nblk, 3)[0].to(DEV)
+    g = torch.Generator().manual_seed(9)
+    qp = torch.randint(-2, 3, (T, shape.proxy_dim), generator=g).to(torch.bfloat16)
+    qp[7].zero_()
+    qp = qp.to(DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    sgqa.indexer_topk(shape, qp, kb, [q0], idx)
+    torch.cuda.synchronize()
+    t = np.arange(q0, q0 + T)
+    sc = oracle.scores(bits(qp), t, 8, parity.widen(bits(kb)), width=int(t.max()) // 8)
+    ref = oracle.topk(sc, t, 8, k)
+    assert np.array_equal(idx.cpu().numpy(), ref)
