@@ -45,6 +45,8 @@ def _bind(lib):
     lib.orc_num_candidates.argtypes = [i64, i32]
     lib.orc_index_build.restype = None
     lib.orc_index_build.argtypes = [p, i64, i32, i32, p]
+    lib.orc_index_build_from_keys.restype = None
+    lib.orc_index_build_from_keys.argtypes = [p, i64, i32, p, i32, i32, p]
     lib.orc_scores.restype = None
     lib.orc_scores.argtypes = [p, i64, p, i32, i32, p, p, i64]
     lib.orc_topk.restype = None
@@ -104,6 +106,25 @@ def index_build(kp_bits: np.ndarray, B: int, lib=None) -> np.ndarray:
     L, P = kp.shape
     kb = np.empty((num_blocks(L, B, lib), P), dtype=np.float64)
     lib.orc_index_build(_ptr(kp), L, P, B, _ptr(kb))
+    return kb
+
+
+def index_build_from_keys(k_bits: np.ndarray, wt_bits: np.ndarray, B: int, lib=None) -> np.ndarray:
+    """Block representations from the keys: the projection (``wt`` = W transposed, [P, width])
+    of each block's mean concatenated key, which equals the block mean of the projected keys
+    (the proxy width is fixed by phantomic12 config.json / sparse_config; blocks of 8 by
+    ai4snews Interpretation para. 2).  ``k_bits``: [L, Hkv, d] or [L, width] uint16 ->
+    [ceil(L/B), P] float64."""
+    lib = lib or load()
+    K = _u16(k_bits)
+    L = K.shape[0]
+    K = K.reshape(L, -1)
+    wt = _u16(wt_bits)
+    P, width = wt.shape
+    if K.shape[1] != width:
+        raise ValueError("key width does not match the projection")
+    kb = np.empty((num_blocks(L, B, lib), P), dtype=np.float64)
+    lib.orc_index_build_from_keys(_ptr(K), L, width, _ptr(wt), P, B, _ptr(kb))
     return kb
 
 

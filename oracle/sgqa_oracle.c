@@ -86,6 +86,49 @@ void orc_index_build(const uint16_t *kp, int64_t L, int32_t P, int32_t B, double
 }
 
 /*
+ * Index maintenance straight from the keys.  The pages fix only the proxy
+ * width (phantomic12 config.json, sparse_config: proxy_dim 256) and that the
+ * indexer works on block representations of size 8 (ai4snews Interpretation,
+ * para. 2).  Reading: a token's proxy key is a linear projection of its
+ * concatenated KV-head keys, kp[s] = K[s] . W.  The projection is linear, so
+ * the block mean of the proxy keys is the projection of the block's mean key:
+ *   kb[j][p] = sum_i wt[p][i] * m_j[i],  m_j[i] = (1/n_j) sum_{s in block j} K[s][i]
+ * with n_j = min(B, L - jB) (only the tokens present) and i over the
+ * width = Hkv*d coordinates of the concatenated key.
+ *   K : [L][width] bf16 (a [L][Hkv][d] cache)   wt : [P][width] bf16 (W transposed)
+ *   kb : [ceil(L/B)][P] double
+ */
+void orc_index_build_from_keys(const uint16_t *K, int64_t L, int32_t width, const uint16_t *wt,
+                               int32_t P, int32_t B, double *kb)
+{
+    const int64_t nblk = orc_num_blocks(L, B);
+#pragma omp parallel
+    {
+        double *m = (double *)malloc(sizeof(double) * (size_t)width);
+#pragma omp for schedule(static)
+        for (int64_t j = 0; j < nblk; ++j) {
+            const int64_t first = j * B;
+            int64_t n = L - first;
+            if (n > B)
+                n = B;
+            for (int32_t i = 0; i < width; ++i) {
+                double sum = 0.0;
+                for (int64_t s = first; s < first + n; ++s)
+                    sum += widen_bf16(K[s * width + i]);
+                m[i] = sum / (double)n;
+            }
+            for (int32_t p = 0; p < P; ++p) {
+                double acc = 0.0;
+                for (int32_t i = 0; i < width; ++i)
+                    acc += widen_bf16(wt[(int64_t)p * width + i]) * m[i];
+                kb[j * P + p] = acc;
+            }
+        }
+        free(m);
+    }
+}
+
+/*
  * Indexer scores (phantomic12 config.json / sparse_config: proxy_dim 256):
  * for each query row r at position t[r], score[r][j] = sum_p qp[r][p]*kb[j][p]
  * for every candidate block j < floor(t[r]/B).  Entries past the candidate

@@ -103,6 +103,38 @@ def pin_index_closed_form(lib):
         assert np.array_equal(kb[j], want), (j, kb[j], want)
 
 
+def pin_index_from_keys_project_then_average(lib):
+    """Linearity: projecting each block's mean key equals averaging the projected keys,
+    computed the other way round with a numpy fp64 matmul, trailing partial block included
+    (L = 43, B = 8: five full blocks and one of 3 tokens)."""
+    rng = np.random.default_rng(21)
+    L, Hkv, d, P, B = 43, 2, 24, 16, 8
+    K = bf16_bits(rng.standard_normal((L, Hkv, d)))
+    wt = bf16_bits(rng.standard_normal((P, Hkv * d)) / math.sqrt(Hkv * d))
+    kb = oracle.index_build_from_keys(K, wt, B, lib=lib)
+    kp = widen(K).reshape(L, -1) @ widen(wt).T  # [L, P]
+    want = np.stack([kp[j * B: min(L, (j + 1) * B)].mean(axis=0) for j in range(-(-L // B))])
+    assert kb.shape == want.shape
+    assert np.allclose(kb, want, rtol=1e-12, atol=1e-12), np.abs(kb - want).max()
+    kb1 = oracle.index_build_from_keys(K, wt, 1, lib=lib)
+    assert np.allclose(kb1, kp, rtol=1e-12, atol=1e-12)
+
+
+def pin_index_from_keys_selection_matrix(lib):
+    """W = a coordinate selection (rows of the identity, permuted): the fused build must equal
+    the proxy-key block compression of the selected key coordinates, bit for bit."""
+    rng = np.random.default_rng(22)
+    L, Hkv, d, B = 61, 2, 16, 8
+    width = Hkv * d
+    K = bf16_bits(rng.standard_normal((L, Hkv, d)))
+    pick = rng.permutation(width)[:12]
+    wt = np.zeros((len(pick), width))
+    wt[np.arange(len(pick)), pick] = 1.0
+    kb = oracle.index_build_from_keys(K, bf16_bits(wt), B, lib=lib)
+    kp = K.reshape(L, width)[:, pick]
+    assert np.array_equal(kb, oracle.index_build(np.ascontiguousarray(kp), B, lib=lib))
+
+
 # --------------------------------------------------------------------------- scores
 def pin_scores_basis(lib):
     """qp = unit vector e_p picks column p of kb; only blocks j < floor(t/B) are scored."""
@@ -363,6 +395,8 @@ def pin_window_token_count(lib):
 ALL_PINS = [
     pin_index_b1_identity,
     pin_index_closed_form,
+    pin_index_from_keys_project_then_average,
+    pin_index_from_keys_selection_matrix,
     pin_scores_basis,
     pin_scores_bilinear,
     pin_topk_lexsort,

@@ -15,8 +15,13 @@ SRC = os.path.join(os.path.dirname(oracle.__file__), "sgqa_oracle.c")
 # (name, original text, planted mistake)
 MUTANTS = [
     ("mean-divides-by-B", "kb[j * P + p] = sum / (double)n;", "kb[j * P + p] = sum / (double)B;"),
-    ("mean-drops-last-token", "for (int64_t s = first; s < first + n; ++s)",
-     "for (int64_t s = first; s < first + n - 1; ++s)"),
+    ("mean-drops-last-token", "for (int64_t s = first; s < first + n; ++s)\n                sum += widen_bf16(kp",
+     "for (int64_t s = first; s < first + n - 1; ++s)\n                sum += widen_bf16(kp"),
+    ("fused-mean-divides-by-B", "m[i] = sum / (double)n;", "m[i] = sum / (double)B;"),
+    ("fused-weight-transposed", "acc += widen_bf16(wt[(int64_t)p * width + i]) * m[i];",
+     "acc += widen_bf16(wt[(int64_t)i * P + p]) * m[i];"),
+    ("fused-skips-first-token", "for (int64_t s = first; s < first + n; ++s)\n                    sum += widen_bf16(K",
+     "for (int64_t s = first + 1; s < first + n; ++s)\n                    sum += widen_bf16(K"),
     ("own-block-scored", "return t / B;\n}\n\n/*\n * Block", "return t / B + 1;\n}\n\n/*\n * Block"),
     ("score-transposed-operand", "acc += widen_bf16(q[p]) * kb[j * P + p];",
      "acc += widen_bf16(q[p]) * kb[j * P + (P - 1 - p)];"),
