@@ -136,7 +136,26 @@ def bench_prefill(steps: int, warmup: int):
     swa_pairs = sum(min(W, t + 1) for t in range(wl.q_start, wl.q_start + wl.T))
     swa = {"window": W, "ms": swa_ms, "tokens_per_s": wl.T / (swa_ms / 1e3),
            "tflops": 4 * s.head_dim * s.num_q_heads * swa_pairs / (swa_ms / 1e3) / 1e12}
+    # index maintenance straight from the keys (no proxy-key tensor): every block of the
+    # 128K cache, mean key projected by W^T [P, Hkv*d]
+    wkt = inputs.proxy_weights(wl, 2, dev)[1].t().contiguous().to(torch.bfloat16)
+    kb_f = torch.empty_like(kb)
+    sgqa.index_build_from_keys(s, d["K"], wkt, kb_f, [wl.L], stream=stream)
+    a.record(stream)
+    for _ in range(steps):
+        sgqa.index_build_from_keys(s, d["K"], wkt, kb_f, [wl.L], stream=stream)
+    b.record(stream)
+    torch.cuda.synchronize()
+    fk_ms = a.elapsed_time(b) / steps
+    width = s.num_kv_heads * s.head_dim
+    fk_bytes = wl.L * width * 2 + wl.nblk * s.proxy_dim * 2 + s.proxy_dim * width * 2
+    fused_index = {"ms": fk_ms, "GBps": fk_bytes / (fk_ms / 1e3) / 1e9,
+                   "hbm_frac": fk_bytes / (fk_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                   "algorithmic_bytes": fk_bytes,
+                   "mfma_tflops": 2 * 2 * wl.nblk * width * s.proxy_dim / (fk_ms / 1e3) / 1e12}
+    del kb_f
     res = dict(wl=wl, total_ms=total_ms, ms_per_step=total_ms / steps, build_ms=build_ms, swa=swa,
+               fused_index=fused_index,
                topk_ms=topk_ms, attn_ms=attn_ms, pairs=pairs, attn_flops=flops,
                gather_bytes=gather_bytes, attn_bytes=gather_bytes + io_bytes, data=d, kb=kb,
                idx=idx)
@@ -352,6 +371,8 @@ def main():
     log(f"prefill: {pre['ms_per_step']:.2f} ms/step (build {pre['build_ms']:.3f}, topk "
         f"{pre['topk_ms']:.3f}, attn {pre['attn_ms']:.3f}) -> {tokens_per_s:,.0f} tokens/s, "
         f"attention {attn_tflops:.1f} TFLOP/s")
+    log(f"sliding window: {pre['swa']['ms']:.3f} ms; index from keys: "
+        f"{pre['fused_index']['ms']:.3f} ms ({pre['fused_index']['GBps']:.0f} GB/s)")
     cpu = None
     if not args.no_cpu:
         log(f"cpu baseline: oracle on {args.cpu_rows} rows")
@@ -398,6 +419,7 @@ def main():
         "indexer_share": (pre["build_ms"] + pre["topk_ms"]) / pre["ms_per_step"],
     }
     line["sliding_window_attention"] = pre["swa"]
+    line["index_build_from_keys"] = pre["fused_index"]
     if cov is not None:
         line["coverage"] = cov
     if dec is not None:

@@ -91,6 +91,32 @@ sgqa_status sgqa_index_build(const sgqa_dims *dims, const sgqa_bf16 *kp, int64_t
                              int32_t nseq, int64_t blk_begin, int64_t blk_end, void *stream);
 
 /*
+ * Index maintenance from the keys (block compression as above, with the proxy
+ * key of a token read as the linear projection of its concatenated KV-head
+ * keys; phantomic12 config.json, sparse_config, fixes the proxy width).  The
+ * projection is linear, so for each sequence s and block j in
+ * [blk_begin, min(blk_end, ceil(L_s/B))),
+ *     kb[s][j][p] = sum_i w_kt[p][i] * m[i],
+ *     m[i] = mean of k_cache[s][jB .. min(jB+B, L_s)-1][i],  i < Hkv*d
+ * (i indexes the concatenated key, head g at i = g*d .. g*d+d-1): one
+ * projection per block, and no proxy-key tensor.  The mean is formed in fp32
+ * and kept to ~2^-17 relative through the bf16 matrix cores (hi + lo split);
+ * the result is rounded once to bf16 (nearest, ties to even).  Blocks outside
+ * the range are not written, so a decode loop refreshes its trailing block by
+ * passing that one block.  Needs proxy_dim in {32, 64, 128, 256, 512}.
+ *   k_cache   [dev]  [nseq][*][Hkv][d] bf16, sequence stride cache_seq_stride elements
+ *   w_kt      [dev]  [P][Hkv*d] bf16: row p is the projection vector of proxy
+ *                    feature p (the projection matrix transposed)
+ *   kb        [dev]  [nseq][*][P] bf16, sequence stride kb_seq_stride elements
+ *   seq_lens  [host] [nseq] tokens per sequence (L_s >= 0), nseq <= 64
+ */
+sgqa_status sgqa_index_build_from_keys(const sgqa_dims *dims, const sgqa_bf16 *k_cache,
+                                       int64_t cache_seq_stride, const sgqa_bf16 *w_kt,
+                                       sgqa_bf16 *kb, int64_t kb_seq_stride,
+                                       const int64_t *seq_lens, int32_t nseq, int64_t blk_begin,
+                                       int64_t blk_end, void *stream);
+
+/*
  * Indexer scores and causal top-k (phantomic12 sparse_config: topk 512,
  * proxy_dim 256; ai.info "Sparse GQA targets million-token context").  For
  * query i of sequence s at position t = q_start[s] + i, with c = t / B:

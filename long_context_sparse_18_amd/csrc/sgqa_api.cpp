@@ -243,6 +243,71 @@ sgqa_status sgqa_index_build(const sgqa_dims *dims, const sgqa_bf16 *kp, int64_t
     return ok();
 }
 
+sgqa_status sgqa_index_build_from_keys(const sgqa_dims *dims, const sgqa_bf16 *k_cache,
+                                       int64_t cache_seq_stride, const sgqa_bf16 *w_kt,
+                                       sgqa_bf16 *kb, int64_t kb_seq_stride,
+                                       const int64_t *seq_lens, int32_t nseq, int64_t blk_begin,
+                                       int64_t blk_end, void *stream)
+{
+    sgqa_status st = check_dims(dims, false, true);
+    if (st != SGQA_OK)
+        return st;
+    st = check_heads(dims);
+    if (st != SGQA_OK)
+        return st;
+    const int P = dims->proxy_dim, B = dims->block_size;
+    if (P != 32 && P != 64 && P != 128 && P != 256 && P != 512)
+        return fail(SGQA_ERR_UNSUPPORTED, "proxy_dim %d not in {32,64,128,256,512}", P);
+    if (nseq < 0 || nseq > sgqa::kMaxSeq)
+        return fail(nseq < 0 ? SGQA_ERR_SHAPE : SGQA_ERR_UNSUPPORTED, "nseq %d not in [0, %d]", nseq,
+                    sgqa::kMaxSeq);
+    if (nseq == 0)
+        return ok();
+    if (!k_cache || !w_kt || !kb || !seq_lens)
+        return fail(SGQA_ERR_NULL, "k_cache, w_kt, kb and seq_lens must be non-NULL");
+    if (!aligned(k_cache, 16) || !aligned(w_kt, 16) || !aligned(kb, 2))
+        return fail(SGQA_ERR_SHAPE, "k_cache and w_kt must be 16-byte aligned");
+    if (blk_begin < 0)
+        return fail(SGQA_ERR_SHAPE, "blk_begin %lld is negative", (long long)blk_begin);
+    const int64_t width = (int64_t)dims->num_kv_heads * dims->head_dim;
+    int64_t max_len = 0;
+    for (int s = 0; s < nseq; ++s) {
+        if (seq_lens[s] < 0)
+            return fail(SGQA_ERR_SHAPE, "seq_lens[%d] = %lld is negative", s, (long long)seq_lens[s]);
+        max_len = seq_lens[s] > max_len ? seq_lens[s] : max_len;
+    }
+    if (nseq > 1) {
+        if (cache_seq_stride < max_len * width || cache_seq_stride % 8 != 0)
+            return fail(SGQA_ERR_SHAPE, "cache_seq_stride %lld must be >= %lld and a multiple of 8",
+                        (long long)cache_seq_stride, (long long)(max_len * width));
+        if (kb_seq_stride < ceil_div(max_len, B) * P)
+            return fail(SGQA_ERR_SHAPE, "kb_seq_stride %lld must be >= %lld",
+                        (long long)kb_seq_stride, (long long)(ceil_div(max_len, B) * P));
+    }
+    sgqa::IndexKeysArgs a{};
+    a.k = k_cache;
+    a.cache_seq_stride = cache_seq_stride;
+    a.wt = w_kt;
+    a.kb = kb;
+    a.kb_seq_stride = kb_seq_stride;
+    a.width = (int)width;
+    a.P = P;
+    a.B = B;
+    a.nseq = nseq;
+    int64_t max_blocks = 0;
+    for (int s = 0; s < nseq; ++s) {
+        const int64_t nblk = ceil_div(seq_lens[s], B);
+        const int64_t j0 = blk_begin < nblk ? blk_begin : nblk;
+        const int64_t j1 = (blk_end < 0 || blk_end > nblk) ? nblk : (blk_end > j0 ? blk_end : j0);
+        a.len.v[s] = seq_lens[s];
+        a.j0.v[s] = j0;
+        a.j1.v[s] = j1;
+        max_blocks = j1 - j0 > max_blocks ? j1 - j0 : max_blocks;
+    }
+    return hip_status(sgqa::launch_index_from_keys(a, max_blocks, reinterpret_cast<hipStream_t>(stream)),
+                      "index_build_from_keys launch");
+}
+
 sgqa_status sgqa_indexer_topk(const sgqa_dims *dims, const sgqa_bf16 *qp, int64_t qp_seq_stride,
                               const sgqa_bf16 *kb, int64_t kb_seq_stride, const int64_t *q_start,
                               int32_t nseq, int32_t T, int32_t *idx, float *sel_scores,

@@ -17,6 +17,20 @@ struct SeqPositions {
 hipError_t launch_index_build(const uint16_t *kp, uint16_t *kb, int64_t L, int P, int B,
                               int64_t j0, int64_t j1, hipStream_t stream);
 
+// Index maintenance from the keys, all sequences in one launch: for sequence s and block
+// j in [j0[s], j1[s]), kb[j] = (mean of the concatenated keys of its tokens) . W, with
+// wt = W transposed ([P][width]), width = Hkv * d.
+struct IndexKeysArgs {
+    const uint16_t *k;       // [nseq][cache_seq_stride] of [L][width]
+    int64_t cache_seq_stride;
+    const uint16_t *wt;      // [P][width]
+    uint16_t *kb;            // [nseq][kb_seq_stride] of [nblk][P]
+    int64_t kb_seq_stride;
+    int width, P, B, nseq;
+    SeqPositions len, j0, j1;
+};
+hipError_t launch_index_from_keys(const IndexKeysArgs &a, int64_t max_blocks, hipStream_t stream);
+
 // Indexer scores for queries [t0, t0+nq) of every sequence into ws rows
 // (row = s*nq + i, row stride ld floats); only blocks j < (q_start[s]+i)/B are written.
 struct ScoreArgs {

@@ -22,7 +22,7 @@ OP_INDEXER_TOPK = 1
 OP_ATTN_DECODE = 2
 OP_ATTN_PREFILL = 3
 
-EXPORTS = ("sgqa_index_build", "sgqa_indexer_topk", "sgqa_sparse_attn_prefill",
+EXPORTS = ("sgqa_index_build", "sgqa_index_build_from_keys", "sgqa_indexer_topk", "sgqa_sparse_attn_prefill",
            "sgqa_sparse_attn_decode", "sgqa_swa_prefill", "sgqa_workspace_bytes",
            "sgqa_status_string", "sgqa_last_error")
 
@@ -61,6 +61,8 @@ def load():
     st = ctypes.c_int
     lib.sgqa_index_build.restype = st
     lib.sgqa_index_build.argtypes = [dp, p, i64, p, i64, p, i32, i64, i64, p]
+    lib.sgqa_index_build_from_keys.restype = st
+    lib.sgqa_index_build_from_keys.argtypes = [dp, p, i64, p, p, i64, p, i32, i64, i64, p]
     lib.sgqa_indexer_topk.restype = st
     lib.sgqa_indexer_topk.argtypes = [dp, p, i64, p, i64, p, i32, i32, p, p, p, sz, p]
     lib.sgqa_sparse_attn_prefill.restype = st
@@ -127,6 +129,22 @@ def index_build(shape: LayerShape, kp: torch.Tensor, kb: torch.Tensor, seq_lens,
     check(load().sgqa_index_build(ctypes.byref(d), _ptr(kp3), kp3.stride(0), _ptr(kb3),
                                   kb3.stride(0), _i64_array(seq_lens), len(seq_lens), blk_begin,
                                   blk_end, _stream(stream, kp)))
+
+
+def index_build_from_keys(shape: LayerShape, k_cache: torch.Tensor, w_kt: torch.Tensor,
+                          kb: torch.Tensor, seq_lens, blk_begin: int = 0, blk_end: int = -1,
+                          stream=None):
+    """k_cache [nseq, Lmax, Hkv, d] (or [L, Hkv, d]), w_kt [P, Hkv*d] -> kb [nseq, nblk, P]
+    (or [nblk, P]), bf16: each block's mean concatenated key, projected."""
+    _need_cuda(k_cache, w_kt, kb)
+    k4 = k_cache if k_cache.dim() == 4 else k_cache.unsqueeze(0)
+    kb3 = kb if kb.dim() == 3 else kb.unsqueeze(0)
+    d = Dims.of(shape)
+    seq_lens = list(seq_lens)
+    check(load().sgqa_index_build_from_keys(ctypes.byref(d), _ptr(k4), k4.stride(0), _ptr(w_kt),
+                                            _ptr(kb3), kb3.stride(0), _i64_array(seq_lens),
+                                            len(seq_lens), blk_begin, blk_end,
+                                            _stream(stream, k_cache)))
 
 
 def indexer_topk(shape: LayerShape, qp: torch.Tensor, kb: torch.Tensor, q_start, idx: torch.Tensor,

@@ -57,6 +57,22 @@ def check_kb(kb_gpu_bits: np.ndarray, kb_ref: np.ndarray) -> dict:
     return {"kb_bit_equal_to_rne": exact, "kb_max_abs_err": float(err.max())}
 
 
+def check_kb_projected(kb_gpu_bits: np.ndarray, kb_ref: np.ndarray) -> dict:
+    """Block representations formed by a projection (a dot product over Hkv*d terms): the
+    error of each element is measured against its row's largest magnitude, as for the
+    indexer scores, plus half a bf16 ulp of the element for the final rounding."""
+    g = widen(kb_gpu_bits)
+    err = np.abs(g - kb_ref)
+    scale = np.abs(kb_ref).max(axis=-1, keepdims=True)
+    tol = KB_RTOL * scale + 0.5 * ulp_bf16(kb_ref)
+    bad = err > tol
+    assert not bad.any(), (f"{bad.sum()} kb elements out of tolerance; worst "
+                           f"{(err - tol).max():.3g} over")
+    exact = float(np.mean(g == rne_bf16(kb_ref)))
+    return {"kb_bit_equal_to_rne": exact, "kb_max_abs_err": float(err.max()),
+            "kb_max_rel_to_row": float((err / scale).max())}
+
+
 def score_tau(ref_row: np.ndarray) -> float:
     return SCORE_RTOL * float(np.max(np.abs(ref_row))) if ref_row.size else 0.0
 

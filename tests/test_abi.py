@@ -130,6 +130,30 @@ def test_index_build_validation():
     assert lib.sgqa_index_build(ctypes.byref(d), FAKE, 0, FAKE, 0, lens, 0, 0, -1, None) == sgqa.OK
 
 
+def test_index_build_from_keys_validation():
+    lib = sgqa.load()
+    lens = (ctypes.c_int64 * 2)(1024, 1024)
+    width = REAL.num_kv_heads * REAL.head_dim
+
+    def call(d=None, k=FAKE, wt=FAKE, kb=FAKE, kstride=1024 * width, kbstride=128 * 256,
+             lens=lens, nseq=2, b0=0):
+        d = d or dims()
+        return lib.sgqa_index_build_from_keys(ctypes.byref(d), k, kstride, wt, kb, kbstride, lens,
+                                              nseq, b0, -1, None)
+
+    assert call(k=None) == sgqa.ERR_NULL
+    assert call(wt=None) == sgqa.ERR_NULL
+    assert call(lens=None) == sgqa.ERR_NULL
+    assert call(b0=-1) == sgqa.ERR_SHAPE
+    assert call(kstride=10) == sgqa.ERR_SHAPE
+    assert call(kbstride=8) == sgqa.ERR_SHAPE
+    assert call(wt=ctypes.c_void_p((1 << 20) + 2)) == sgqa.ERR_SHAPE
+    assert call(d=dims(proxy_dim=96)) == sgqa.ERR_UNSUPPORTED
+    assert call(d=dims(head_dim=96)) == sgqa.ERR_UNSUPPORTED
+    assert call(nseq=65) == sgqa.ERR_UNSUPPORTED
+    assert call(nseq=0) == sgqa.OK
+
+
 def test_decode_validation():
     lib = sgqa.load()
     d = dims()

@@ -310,3 +310,44 @@ def test_prefill_topk_exact_ties():
     sc = oracle.scores(bits(qp), t, 8, parity.widen(bits(kb)), width=int(t.max()) // 8)
     ref = oracle.topk(sc, t, 8, k)
     assert np.array_equal(idx.cpu().numpy(), ref)
+
+
+def _w_kt(wl, seed):
+    """The key projection of the synthetic recipe as bf16 W^T [P, Hkv*d]."""
+    return inputs.proxy_weights(wl, seed, DEV)[1].t().contiguous().to(torch.bfloat16)
+
+
+@pytest.mark.parametrize("B", [8, 1, 32])
+def test_tiny_index_from_keys(tiny, B):
+    """Fused index maintenance on three sequences of different lengths (full and partial
+    trailing blocks) against the oracle; then a one-block refresh leaves the rest untouched."""
+    shape = with_selection(WL.shape, B, 16)
+    lens = [1024, 1000, 37]
+    n, Lmax = len(lens), max(lens)
+    K = torch.zeros((n, Lmax) + tuple(tiny["K"].shape[1:]), dtype=torch.bfloat16, device=DEV)
+    for b, L_ in enumerate(lens):
+        K[b, :L_] = tiny["K"][:L_].roll(shifts=97 * b, dims=0)
+    wkt = _w_kt(WL, 3)
+    nblk = -(-Lmax // B)
+    kb = torch.full((n, nblk, shape.proxy_dim), 7.0, dtype=torch.bfloat16, device=DEV)
+    sgqa.index_build_from_keys(shape, K, wkt, kb, lens)
+    torch.cuda.synchronize()
+    for b, L_ in enumerate(lens):
+        ref = oracle.index_build_from_keys(bits(K[b, :L_]), bits(wkt), B)
+        st = parity.check_kb_projected(bits(kb[b, : ref.shape[0]]), ref)
+        assert st["kb_bit_equal_to_rne"] >= 0.99, st
+        assert torch.all(kb[b, ref.shape[0]:] == 7.0)
+    # refresh only the trailing block of each sequence after zeroing it
+    last = [-(-L_ // B) - 1 for L_ in lens]
+    for b in range(n):
+        kb[b, last[b]] = 0
+    before = kb.clone()
+    for b, L_ in enumerate(lens):
+        sgqa.index_build_from_keys(shape, K[b], wkt, kb[b], [L_], last[b], last[b] + 1)
+    torch.cuda.synchronize()
+    for b, L_ in enumerate(lens):
+        ref = oracle.index_build_from_keys(bits(K[b, last[b] * B: L_]), bits(wkt), B)
+        parity.check_kb_projected(bits(kb[b, last[b]:last[b] + 1]), ref)
+        mask = torch.ones(nblk, dtype=torch.bool, device=DEV)
+        mask[last[b]] = False
+        assert torch.equal(kb[b][mask], before[b][mask])

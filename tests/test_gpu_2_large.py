@@ -119,6 +119,50 @@ def test_decode_1m_batch16():
     assert exact >= n - 1
 
 
+def test_index_from_keys_128k():
+    """Fused index maintenance at the real shape (width 4 x 192, proxy 256) over the whole
+    128K prefill: every block against the oracle."""
+    wl = WORKLOADS[2]
+    shape = wl.shape
+    say("fused index 128K: generating")
+    K, _, _ = inputs.make_cache(wl, 2, DEV)
+    wkt = inputs.proxy_weights(wl, 2, DEV)[1].t().contiguous().to(torch.bfloat16)
+    kb = torch.empty((wl.nblk, shape.proxy_dim), dtype=torch.bfloat16, device=DEV)
+    sgqa.index_build_from_keys(shape, K, wkt, kb, [wl.L])
+    torch.cuda.synchronize()
+    say("fused index 128K: oracle")
+    ref = oracle.index_build_from_keys(bits(K), bits(wkt), shape.block_size)
+    st = parity.check_kb_projected(bits(kb), ref)
+    say(f"fused index 128K: {st}")
+    assert st["kb_bit_equal_to_rne"] >= 0.99
+
+
+def test_index_from_keys_decode_1m():
+    """Fused index maintenance for 16 sequences of ~1M tokens with different lengths (partial
+    trailing blocks) in one launch; sampled blocks of every sequence against the oracle."""
+    wl = WORKLOADS[3]
+    shape = wl.shape
+    n, B = wl.nseq, shape.block_size
+    lens = [wl.L - 3 * s for s in range(n)]
+    say("fused index 1M x 16: generating keys")
+    K = torch.empty((n, wl.L, shape.num_kv_heads, shape.head_dim), dtype=torch.bfloat16,
+                    device=DEV)
+    for s in range(n):
+        inputs.make_cache(wl, 3, DEV, seq=s, K_out=K[s])
+    wkt = inputs.proxy_weights(wl, 3, DEV)[1].t().contiguous().to(torch.bfloat16)
+    kb = torch.empty((n, wl.nblk, shape.proxy_dim), dtype=torch.bfloat16, device=DEV)
+    sgqa.index_build_from_keys(shape, K, wkt, kb, lens)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    for s, L_ in enumerate(lens):
+        nb = -(-L_ // B)
+        blocks = sorted(set([0, 1, nb - 2, nb - 1] + list(rng.integers(0, nb, 28))))
+        for j in blocks:
+            ref = oracle.index_build_from_keys(bits(K[s, j * B: min(L_, (j + 1) * B)]), bits(wkt), B)
+            parity.check_kb_projected(bits(kb[s, j:j + 1]), ref)
+    say("fused index 1M x 16: ok")
+
+
 def test_sliding_window_32k_real_shape():
     """Gated sliding-window attention (window 512) at the real layer shape on the 32K
     prefill, sampled rows against the oracle."""
