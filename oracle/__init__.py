@@ -55,6 +55,16 @@ def _bind(lib):
     lib.orc_token_set.argtypes = [p, i32, i32, i64, p]
     lib.orc_attend.restype = None
     lib.orc_attend.argtypes = [p, p, p, i64, p, i32, i32, i32, dbl, p, p]
+    lib.orc_attend_f64.restype = None
+    lib.orc_attend_f64.argtypes = [p, p, p, i64, p, i32, i32, i32, dbl, p, p]
+    lib.orc_e4m3_decode.restype = dbl
+    lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
+    lib.orc_e4m3_encode.restype = ctypes.c_uint8
+    lib.orc_e4m3_encode.argtypes = [ctypes.c_float]
+    lib.orc_quantize_rows.restype = None
+    lib.orc_quantize_rows.argtypes = [p, i64, i32, p, p]
+    lib.orc_dequant_rows.restype = None
+    lib.orc_dequant_rows.argtypes = [p, p, i64, i32, p]
     lib.orc_window_token_set.restype = i64
     lib.orc_window_token_set.argtypes = [i64, i64, p]
     lib.orc_window_attention.restype = ctypes.c_int
@@ -192,6 +202,68 @@ def attend(q_bits, k_rows, v_rows, gate_bits, scale: float, lib=None):
     lib.orc_attend(_ptr(q), _ptr(kr), _ptr(vr), n, _ptr(g), Hq, Hkv, d, float(scale), _ptr(out),
                    _ptr(lse))
     return out, lse
+
+
+def attend_f64(q_bits, k_rows, v_rows, gate_bits, scale: float, lib=None):
+    """Gated GQA of one query over explicit K/V rows given as float64 [n, Hkv, d] (for
+    dequantised FP8 rows) -> (out [Hq, d], lse [Hq])."""
+    lib = lib or load()
+    q = _u16(q_bits)
+    kr = np.ascontiguousarray(k_rows, dtype=np.float64)
+    vr = np.ascontiguousarray(v_rows, dtype=np.float64)
+    g = _u16(gate_bits)
+    Hq, d = q.shape
+    n, Hkv, d2 = kr.shape
+    if d2 != d or vr.shape != kr.shape or g.shape != (Hq,) or Hq % Hkv:
+        raise ValueError("shape mismatch in attend_f64")
+    out = np.empty((Hq, d), dtype=np.float64)
+    lse = np.empty((Hq,), dtype=np.float64)
+    lib.orc_attend_f64(_ptr(q), _ptr(kr), _ptr(vr), n, _ptr(g), Hq, Hkv, d, float(scale),
+                       _ptr(out), _ptr(lse))
+    return out, lse
+
+
+def e4m3_decode(codes, lib=None) -> np.ndarray:
+    """OCP E4M3 codes -> float64 values (NaN for the NaN codes)."""
+    lib = lib or load()
+    c = np.asarray(codes, dtype=np.uint8).ravel()
+    return np.array([lib.orc_e4m3_decode(int(x)) for x in c], dtype=np.float64).reshape(
+        np.shape(codes))
+
+
+def e4m3_encode(values, lib=None) -> np.ndarray:
+    """float32 values -> nearest E4M3 codes (ties to even, saturating at +-448)."""
+    lib = lib or load()
+    v = np.asarray(values, dtype=np.float32).ravel()
+    return np.array([lib.orc_e4m3_encode(float(x)) for x in v], dtype=np.uint8).reshape(
+        np.shape(values))
+
+
+def quantize_rows(x_bits: np.ndarray, lib=None):
+    """FP8 storage of cached rows: bf16 bits [..., cols] -> (e4m3 codes uint8 [..., cols],
+    fp32 scales [...]); one scale per row, amax / 448, all in fp32 (see the C header)."""
+    lib = lib or load()
+    x = _u16(x_bits)
+    cols = x.shape[-1]
+    rows = x.size // cols if cols else 0
+    codes = np.empty(x.shape, dtype=np.uint8)
+    scales = np.empty(x.shape[:-1], dtype=np.float32)
+    lib.orc_quantize_rows(_ptr(x), rows, cols, _ptr(codes), _ptr(scales))
+    return codes, scales
+
+
+def dequant_rows(codes: np.ndarray, scales: np.ndarray, lib=None) -> np.ndarray:
+    """e4m3 codes [..., cols] and fp32 scales [...] -> float64 values."""
+    lib = lib or load()
+    c = np.ascontiguousarray(codes, dtype=np.uint8)
+    sc = np.ascontiguousarray(scales, dtype=np.float32)
+    cols = c.shape[-1]
+    rows = c.size // cols if cols else 0
+    if sc.size != rows:
+        raise ValueError("one scale per row")
+    out = np.empty(c.shape, dtype=np.float64)
+    lib.orc_dequant_rows(_ptr(c), _ptr(sc), rows, cols, _ptr(out))
+    return out
 
 
 def sparse_attention(q_bits, t, K_bits, V_bits, G_bits, idx, B: int, scale: float, lib=None):

@@ -250,11 +250,12 @@ static double logistic(double x)
  *   z_s  = scale * sum_i q[h][i] * K[s][g][i]
  *   a    = sum_s softmax(z)_s * V[s][g][:]
  *   out  = a * sigmoid(gate[h]);   lse = log sum_s exp(z_s)
- *   q : [Hq][d]; krows, vrows : [n][Hkv][d]; gate : [Hq]; out : [Hq][d]
+ *   q : [Hq][d] bf16; krows, vrows : [n][Hkv][d] double; gate : [Hq] bf16;
+ *   out : [Hq][d]
  */
-void orc_attend(const uint16_t *q, const uint16_t *krows, const uint16_t *vrows, int64_t n,
-                const uint16_t *gate, int32_t Hq, int32_t Hkv, int32_t d, double scale,
-                double *out, double *lse)
+void orc_attend_f64(const uint16_t *q, const double *krows, const double *vrows, int64_t n,
+                    const uint16_t *gate, int32_t Hq, int32_t Hkv, int32_t d, double scale,
+                    double *out, double *lse)
 {
     const int32_t heads_per_group = Hq / Hkv;
     double *z = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
@@ -264,7 +265,7 @@ void orc_attend(const uint16_t *q, const uint16_t *krows, const uint16_t *vrows,
         for (int64_t s = 0; s < n; ++s) {
             double dot = 0.0;
             for (int32_t i = 0; i < d; ++i)
-                dot += widen_bf16(q[h * d + i]) * widen_bf16(krows[(s * Hkv + g) * d + i]);
+                dot += widen_bf16(q[h * d + i]) * krows[(s * Hkv + g) * d + i];
             z[s] = scale * dot;
             if (z[s] > m)
                 m = z[s];
@@ -278,13 +279,30 @@ void orc_attend(const uint16_t *q, const uint16_t *krows, const uint16_t *vrows,
         for (int32_t i = 0; i < d; ++i) {
             double acc = 0.0;
             for (int64_t s = 0; s < n; ++s)
-                acc += z[s] * widen_bf16(vrows[(s * Hkv + g) * d + i]);
+                acc += z[s] * vrows[(s * Hkv + g) * d + i];
             out[h * d + i] = (acc / Z) * gate_factor;
         }
         if (lse)
             lse[h] = m + log(Z);
     }
     free(z);
+}
+
+/* The same over bf16 rows: widened exactly, then orc_attend_f64. */
+void orc_attend(const uint16_t *q, const uint16_t *krows, const uint16_t *vrows, int64_t n,
+                const uint16_t *gate, int32_t Hq, int32_t Hkv, int32_t d, double scale,
+                double *out, double *lse)
+{
+    const size_t cnt = (size_t)(n > 0 ? n : 1) * (size_t)Hkv * (size_t)d;
+    double *kd = (double *)malloc(cnt * sizeof(double));
+    double *vd = (double *)malloc(cnt * sizeof(double));
+    for (size_t e = 0; e < (size_t)n * (size_t)Hkv * (size_t)d; ++e) {
+        kd[e] = widen_bf16(krows[e]);
+        vd[e] = widen_bf16(vrows[e]);
+    }
+    orc_attend_f64(q, kd, vd, n, gate, Hq, Hkv, d, scale, out, lse);
+    free(kd);
+    free(vd);
 }
 
 /*
@@ -375,4 +393,86 @@ int orc_window_attention(const uint16_t *q, const int64_t *t, int64_t nrows, con
         free(tok);
     }
     return bad ? -1 : 0;
+}
+
+/*
+ * FP8 storage of cached rows (decode path).  The pages give FP8 only for the
+ * released checkpoint: e4m3 with scaling blocks of 128 (phantomic12 entry,
+ * "quant_method fp8, e4m3, block size 128"; ai4snews "Open Weights" para. on
+ * FP8 vs BF16).  Reading: a cached row (one token's K or V row of one KV head,
+ * d values, or one index row, P values) is stored as e4m3 codes with one fp32
+ * scale per row.
+ *
+ * OCP 8-bit E4M3: sign bit, 4 exponent bits (bias 7), 3 fraction bits;
+ * exponent field 0 holds subnormals m * 2^-9; S.1111.111 is NaN; no
+ * infinities; the largest finite magnitude is 448.
+ */
+double orc_e4m3_decode(uint8_t c)
+{
+    const int sgn = c >> 7, e = (c >> 3) & 15, m = c & 7;
+    if (e == 15 && m == 7)
+        return NAN;
+    const double v = e == 0 ? ldexp((double)m, -9) : ldexp(1.0 + m / 8.0, e - 7);
+    return sgn ? -v : v;
+}
+
+/* Nearest e4m3 value of y, ties to the even code, magnitudes >= 448 saturate. */
+uint8_t orc_e4m3_encode(float y)
+{
+    const uint8_t sgn = signbit(y) ? 0x80 : 0x00;
+    const double a = fabs((double)y);
+    if (a >= 448.0)
+        return (uint8_t)(sgn | 0x7E);
+    int ex;
+    frexp(a, &ex);          /* a = f * 2^ex, f in [0.5, 1): floor(log2 a) = ex - 1 */
+    int E = ex - 1;
+    if (a == 0.0 || E < -6)
+        E = -6;             /* subnormal range: spacing 2^-9 */
+    const double r = nearbyint(ldexp(a, 3 - E));  /* value / spacing, ties to even */
+    if (r == 0.0)
+        return sgn;
+    if (E == -6 && r < 8.0)
+        return (uint8_t)(sgn | (uint8_t)r);       /* subnormal code m */
+    int Ev = E, mant = (int)r - 8;
+    if (r == 16.0) {        /* rounded up into the next binade */
+        Ev = E + 1;
+        mant = 0;
+    }
+    return (uint8_t)(sgn | (uint8_t)(((Ev + 7) << 3) | mant));
+}
+
+/*
+ * Row quantisation, every step in fp32 so that the integer codes are decided
+ * in the kernel's precision: amax = max |x|, scale = amax / 448 (1 for a zero
+ * row), code = e4m3(x / scale).
+ *   x : [rows][cols] bf16   codes : [rows][cols]   scales : [rows] float
+ */
+void orc_quantize_rows(const uint16_t *x, int64_t rows, int32_t cols, uint8_t *codes,
+                       float *scales)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r) {
+        float amax = 0.0f;
+        for (int32_t i = 0; i < cols; ++i) {
+            const float v = fabsf((float)widen_bf16(x[r * cols + i]));
+            if (v > amax)
+                amax = v;
+        }
+        float scale = amax / 448.0f;
+        if (!(scale > 0.0f))
+            scale = 1.0f;
+        scales[r] = scale;
+        for (int32_t i = 0; i < cols; ++i)
+            codes[r * cols + i] = orc_e4m3_encode((float)widen_bf16(x[r * cols + i]) / scale);
+    }
+}
+
+/* Dequantised rows: e4m3 value times the row's scale, in double. */
+void orc_dequant_rows(const uint8_t *codes, const float *scales, int64_t rows, int32_t cols,
+                      double *out)
+{
+#pragma omp parallel for schedule(static)
+    for (int64_t r = 0; r < rows; ++r)
+        for (int32_t i = 0; i < cols; ++i)
+            out[r * cols + i] = orc_e4m3_decode(codes[r * cols + i]) * (double)scales[r];
 }

@@ -392,7 +392,91 @@ def pin_window_token_count(lib):
         assert toks[n - 1] == t_ and toks[0] == t_ - n + 1
 
 
+# --------------------------------------------------------------------------- FP8 storage
+def _torch_e4m3_bits(values) -> np.ndarray:
+    """Library cast: torch float32 -> float8_e4m3fn (round to nearest even), as codes."""
+    t = torch.as_tensor(np.asarray(values, dtype=np.float32))
+    return t.to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+
+
+def pin_e4m3_decode_library(lib):
+    """All 256 E4M3 codes decode to torch's float8_e4m3fn values (NaN codes to NaN)."""
+    codes = np.arange(256, dtype=np.uint8)
+    ours = oracle.e4m3_decode(codes, lib=lib)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.array_equal(np.isnan(ours), np.isnan(ref))
+    ok = ~np.isnan(ref)
+    assert np.array_equal(ours[ok], ref[ok])
+
+
+def pin_e4m3_encode_library(lib):
+    """Encoding equals torch's round-to-nearest-even cast on every representable value, every
+    midpoint, one float32 ulp either side of each midpoint, and random values in range;
+    magnitudes from 448 up saturate to the largest finite code."""
+    codes = np.arange(256, dtype=np.uint8)
+    vals = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    vals = np.unique(vals[~np.isnan(vals)])
+    mids = (vals[1:] + vals[:-1]) / 2
+    mids = mids.astype(np.float32)
+    probe = np.concatenate([vals.astype(np.float32), mids, np.nextafter(mids, np.float32(np.inf)),
+                            np.nextafter(mids, np.float32(-np.inf)),
+                            np.random.default_rng(31).uniform(-448, 448, 4000).astype(np.float32),
+                            np.random.default_rng(32).uniform(-0.02, 0.02, 4000).astype(np.float32)])
+    probe = probe[np.abs(probe) <= 448]
+    assert np.array_equal(oracle.e4m3_encode(probe, lib=lib), _torch_e4m3_bits(probe))
+    sat = np.array([448.0, 460.0, 500.0, 1e6, -448.0, -1e6], dtype=np.float32)
+    assert oracle.e4m3_encode(sat, lib=lib).tolist() == [0x7E] * 4 + [0xFE] * 2
+
+
+def pin_quantize_rows_error_bound(lib):
+    """Row quantisation: the dequantised value is within half an E4M3 spacing (times the row
+    scale) of the input, the row's largest magnitude lands on a code of magnitude >= 416 (the
+    top two E4M3 values), and a zero row gives zero codes."""
+    rng = np.random.default_rng(33)
+    x = rng.standard_normal((50, 192)) * np.exp(rng.uniform(-6, 6, (50, 1)))
+    x[7] = 0.0
+    bits = bf16_bits(x)
+    codes, scales = oracle.quantize_rows(bits, lib=lib)
+    deq = oracle.dequant_rows(codes, scales, lib=lib)
+    xv = widen(bits)
+    y = np.abs(xv) / scales[:, None].astype(np.float64)
+    spacing = np.where(y < 2.0 ** -6, 2.0 ** -9, 2.0 ** (np.floor(np.log2(np.maximum(y, 1e-300))) - 3))
+    assert np.all(np.abs(deq - xv) <= 0.5 * spacing * scales[:, None] * (1 + 1e-6))
+    top = np.abs(oracle.e4m3_decode(codes, lib=lib)).max(axis=1)
+    assert np.all(top[np.arange(50) != 7] >= 416) and np.all(top <= 448)
+    assert np.all(codes[7] == 0)
+
+
+def pin_attend_f64_sdpa(lib):
+    """The attention core on float64 rows (dequantised FP8) equals torch SDPA in fp64, and on
+    widened bf16 rows it equals the bf16 entry bit for bit."""
+    rng = np.random.default_rng(34)
+    n, Hq, Hkv, d = 37, 8, 2, 64
+    q = bf16_bits(rng.standard_normal((Hq, d)))
+    g = bf16_bits(rng.standard_normal(Hq))
+    K = rng.standard_normal((n, Hkv, d)) * 0.7
+    V = rng.standard_normal((n, Hkv, d))
+    scale = 1 / math.sqrt(d)
+    out, lse = oracle.attend_f64(q, K, V, g, scale, lib=lib)
+    Qt = torch.from_numpy(widen(q))[:, None, :]                       # [Hq, 1, d]
+    Kt = torch.from_numpy(K).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+    Vt = torch.from_numpy(V).permute(1, 0, 2).repeat_interleave(Hq // Hkv, dim=0)
+    o = torch.nn.functional.scaled_dot_product_attention(Qt, Kt, Vt, scale=scale)[:, 0, :]
+    o = o * torch.sigmoid(torch.from_numpy(widen(g)))[:, None]
+    assert np.allclose(out, o.numpy(), rtol=1e-12, atol=1e-12)
+    z = (torch.from_numpy(widen(q))[:, None, :] * Kt).sum(-1) * scale
+    assert np.allclose(lse, torch.logsumexp(z, dim=-1).numpy(), rtol=1e-12, atol=1e-12)
+    kb, vb = bf16_bits(K), bf16_bits(V)
+    o1, l1 = oracle.attend(q, kb, vb, g, scale, lib=lib)
+    o2, l2 = oracle.attend_f64(q, widen(kb), widen(vb), g, scale, lib=lib)
+    assert np.array_equal(o1, o2) and np.array_equal(l1, l2)
+
+
 ALL_PINS = [
+    pin_e4m3_decode_library,
+    pin_e4m3_encode_library,
+    pin_quantize_rows_error_bound,
+    pin_attend_f64_sdpa,
     pin_index_b1_identity,
     pin_index_closed_form,
     pin_index_from_keys_project_then_average,

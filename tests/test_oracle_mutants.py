@@ -36,7 +36,12 @@ MUTANTS = [
     ("scale-dropped", "z[s] = scale * dot;", "z[s] = dot;"),
     ("group-map-interleaved", "const int32_t g = h / heads_per_group;",
      "const int32_t g = h % Hkv;"),
-    ("key-is-value", "widen_bf16(krows[(s * Hkv + g) * d + i])", "widen_bf16(vrows[(s * Hkv + g) * d + i])"),
+    ("key-is-value", "widen_bf16(q[h * d + i]) * krows[(s * Hkv + g) * d + i]",
+     "widen_bf16(q[h * d + i]) * vrows[(s * Hkv + g) * d + i]"),
+    ("e4m3-bias-off-by-one", "ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
+    ("e4m3-truncates", "const double r = nearbyint(ldexp(a, 3 - E));", "const double r = floor(ldexp(a, 3 - E));"),
+    ("e4m3-subnormal-edge", "if (a == 0.0 || E < -6)\n        E = -6;", "if (a == 0.0 || E < -7)\n        E = -7;"),
+    ("fp8-scale-wrong-max", "float scale = amax / 448.0f;", "float scale = amax / 240.0f;"),
     ("gate-sign", "return 1.0 / (1.0 + exp(-x));", "return 1.0 / (1.0 + exp(x));"),
     ("no-normalisation", "out[h * d + i] = (acc / Z) * gate_factor;", "out[h * d + i] = acc * gate_factor;"),
     ("lse-drops-max", "lse[h] = m + log(Z);", "lse[h] = log(Z);"),
