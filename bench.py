@@ -220,9 +220,62 @@ def bench_decode(steps: int, warmup: int):
         + (2 * s.num_q_heads * s.head_dim * 2 + s.proxy_dim * 2 + s.num_q_heads * 2
            + s.topk_blocks * 4)
     bytes_total = per_seq * n
-    return dict(us_median=med, us_topk=sorted(t_topk)[len(t_topk) // 2],
-                us_attn=sorted(t_attn)[len(t_attn) // 2], bytes=bytes_total,
-                gbs=bytes_total / (med * 1e-6) / 1e9)
+    res = dict(us_median=med, us_topk=sorted(t_topk)[len(t_topk) // 2],
+               us_attn=sorted(t_attn)[len(t_attn) // 2], bytes=bytes_total,
+               gbs=bytes_total / (med * 1e-6) / 1e9)
+
+    # the same step on FP8 storage (E4M3 rows with one fp32 scale each) of index and caches
+    log("decode: quantising index and caches to FP8")
+    kbq = torch.empty(kb.shape, dtype=torch.uint8, device=dev)
+    kbs = torch.empty(kb.shape[:2], dtype=torch.float32, device=dev)
+    sgqa.quantize_fp8(kb, kbq, kbs)
+    del kb
+    cq = {}
+    for name in ("K", "V"):
+        cq[name] = (torch.empty(d[name].shape, dtype=torch.uint8, device=dev),
+                    torch.empty(d[name].shape[:3], dtype=torch.float32, device=dev))
+        sgqa.quantize_fp8(d[name], *cq[name])
+        del d[name]
+    torch.cuda.empty_cache()
+    idx8 = idx.view(n, -1)
+
+    def step8():
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        m = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        sgqa.indexer_topk_fp8(s, d["qp"], kbq, kbs, [wl.L - 1] * n, idx8, workspace=ws_topk,
+                              stream=stream)
+        m.record(stream)
+        sgqa.sparse_attn_decode_fp8(s, d["Q"], cq["K"][0], cq["V"][0], cq["K"][1], cq["V"][1],
+                                    d["G"], idx8, [wl.L] * n, scale, out, workspace=ws_attn,
+                                    stream=stream)
+        b.record(stream)
+        return a, m, b
+
+    for _ in range(warmup):
+        flush.sum()
+        step8()
+    torch.cuda.synchronize()
+    times, t_topk, t_attn = [], [], []
+    for _ in range(steps):
+        flush.sum()
+        a, m, b = step8()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b) * 1e3)
+        t_topk.append(a.elapsed_time(m) * 1e3)
+        t_attn.append(m.elapsed_time(b) * 1e3)
+    times.sort()
+    med8 = times[len(times) // 2]
+    c = (wl.L - 1) // s.block_size
+    per_seq8 = c * (s.proxy_dim + 4) \
+        + s.topk_blocks * s.block_size * s.num_kv_heads * (s.head_dim + 4) * 2 \
+        + (2 * s.num_q_heads * s.head_dim * 2 + s.proxy_dim * 2 + s.num_q_heads * 2
+           + s.topk_blocks * 4)
+    res["fp8"] = dict(us_median=med8, us_topk=sorted(t_topk)[len(t_topk) // 2],
+                      us_attn=sorted(t_attn)[len(t_attn) // 2], bytes=per_seq8 * n,
+                      gbs=per_seq8 * n / (med8 * 1e-6) / 1e9)
+    return res
 
 
 def bench_coverage():
@@ -359,7 +412,9 @@ def main():
     if args.no_prefill:
         dec = bench_decode(max(args.steps, 5), args.warmup)
         log(f"decode: {dec['us_median']:.1f} us/step (topk {dec['us_topk']:.1f}, attn "
-            f"{dec['us_attn']:.1f}), {dec['gbs']:.0f} GB/s")
+            f"{dec['us_attn']:.1f}), {dec['gbs']:.0f} GB/s; FP8 storage "
+            f"{dec['fp8']['us_median']:.1f} us/step (topk {dec['fp8']['us_topk']:.1f}, attn "
+            f"{dec['fp8']['us_attn']:.1f}), {dec['fp8']['gbs']:.0f} GB/s")
         return
 
     pre = bench_prefill(args.steps, args.warmup)
@@ -390,7 +445,9 @@ def main():
     if not args.no_decode:
         dec = bench_decode(max(args.steps, 5), args.warmup)
         log(f"decode: {dec['us_median']:.1f} us/step (topk {dec['us_topk']:.1f}, attn "
-            f"{dec['us_attn']:.1f}), {dec['gbs']:.0f} GB/s")
+            f"{dec['us_attn']:.1f}), {dec['gbs']:.0f} GB/s; FP8 storage "
+            f"{dec['fp8']['us_median']:.1f} us/step (topk {dec['fp8']['us_topk']:.1f}, attn "
+            f"{dec['fp8']['us_attn']:.1f}), {dec['fp8']['gbs']:.0f} GB/s")
 
     line = {
         "metric": METRIC,
@@ -427,6 +484,14 @@ def main():
                           "us_indexer_topk": dec["us_topk"], "us_attention": dec["us_attn"],
                           "GBps": dec["gbs"], "hbm_frac": dec["gbs"] / PEAK_HBM_GBS,
                           "algorithmic_bytes": dec["bytes"]}
+        f8 = dec["fp8"]
+        line["decode_fp8_storage"] = {"workload": "decode-1m-x16", "storage": "e4m3 rows + fp32 "
+                                      "scale per row (index, K, V)",
+                                      "us_per_layer": f8["us_median"],
+                                      "us_indexer_topk": f8["us_topk"],
+                                      "us_attention": f8["us_attn"], "GBps": f8["gbs"],
+                                      "hbm_frac": f8["gbs"] / PEAK_HBM_GBS,
+                                      "algorithmic_bytes": f8["bytes"]}
     print(json.dumps(line), flush=True)
 
 

@@ -213,6 +213,61 @@ sgqa_status sgqa_swa_prefill(const sgqa_dims *dims, const sgqa_bf16 *q, const sg
                              sgqa_bf16 *out, float *lse, void *stream);
 
 /*
+ * FP8 storage for the decode path.  The pages give FP8 (e4m3) only for the
+ * released checkpoint (phantomic12 entry: quant_method fp8, e4m3, scaling
+ * blocks of 128; ai4snews "Open Weights": FP8 for deployment).  Here a cached
+ * row - one token's K or V row of one KV head (d values) or one index row (P
+ * values) - is stored as OCP E4M3 codes (sign, 4 exponent bits with bias 7, 3
+ * fraction bits; largest finite 448) with one fp32 scale per row, halving the
+ * bytes the decode step reads.
+ *
+ * Row quantisation, every step in fp32: scale[r] = max_i |x[r][i]| / 448 (1 for
+ * an all-zero row), codes[r][i] = nearest e4m3 of x[r][i] / scale[r] (ties to
+ * even, saturating at +-448).  Dequantised value = e4m3 value * scale[r].
+ *   x      [dev] [rows][cols] bf16     codes [dev] [rows][cols] uint8
+ *   scales [dev] [rows] fp32;  1 <= cols <= 4096
+ * For a [nseq][L][Hkv][d] cache the rows are its nseq*L*Hkv head rows (cols = d).
+ */
+sgqa_status sgqa_quantize_fp8(const sgqa_bf16 *x, int64_t rows, int32_t cols, uint8_t *codes,
+                              float *scales, void *stream);
+
+/*
+ * sgqa_indexer_topk for one query per sequence (decode) on an FP8 index: the
+ * score of block j is (qp . codes[j]) * scale[j] with the codes read as exact
+ * bf16 (fp32 accumulation); selection as sgqa_indexer_topk.  Needs proxy_dim in
+ * {64, 128, 256, 512}, k >= 2 and at most 131072 candidate blocks.
+ *   qp        [dev]  [nseq][P] bf16, sequence stride qp_seq_stride elements
+ *   kb_codes  [dev]  [nseq][kb_seq_stride][P] uint8; kb_scales [dev] [nseq][kb_seq_stride] fp32
+ *   q_pos     [host] [nseq] position of each sequence's query
+ *   idx       [dev]  [nseq][k]; sel_scores [dev] [nseq][k] or NULL
+ *   workspace [dev]  >= sgqa_workspace_bytes(SGQA_OP_INDEXER_TOPK, dims, nseq, 1, Lmax)
+ */
+sgqa_status sgqa_indexer_topk_fp8(const sgqa_dims *dims, const sgqa_bf16 *qp,
+                                  int64_t qp_seq_stride, const uint8_t *kb_codes,
+                                  const float *kb_scales, int64_t kb_seq_stride,
+                                  const int64_t *q_pos, int32_t nseq, int32_t *idx,
+                                  float *sel_scores, void *workspace, size_t workspace_bytes,
+                                  void *stream);
+
+/*
+ * sgqa_sparse_attn_decode on FP8 caches: logits use (q . codes) * k_scale of the
+ * row, and each softmax weight is multiplied by its row's v_scale before the
+ * product with the V codes (read as exact bf16); normalisation, merge and gate
+ * as sgqa_sparse_attn_decode.
+ *   k_codes, v_codes   [dev] [nseq][cache_seq_stride][Hkv][d] uint8
+ *   k_scales, v_scales [dev] [nseq][cache_seq_stride][Hkv] fp32
+ *   cache_seq_stride: tokens per sequence slot; other arguments as the bf16 call
+ */
+sgqa_status sgqa_sparse_attn_decode_fp8(const sgqa_dims *dims, const sgqa_bf16 *q,
+                                        const uint8_t *k_codes, const uint8_t *v_codes,
+                                        const float *k_scales, const float *v_scales,
+                                        int64_t cache_seq_stride, const sgqa_bf16 *gate,
+                                        const int32_t *idx, const int64_t *cache_lens,
+                                        int32_t nseq, float softmax_scale, sgqa_bf16 *out,
+                                        float *lse, void *workspace, size_t workspace_bytes,
+                                        void *stream);
+
+/*
  * Workspace size in bytes for `op` (SGQA_OP_INDEXER_TOPK, SGQA_OP_ATTN_DECODE or
  * SGQA_OP_ATTN_PREFILL) given nseq sequences of T queries and caches of at
  * most Lmax tokens.  For the indexer this is the size that lets one pass cover

@@ -81,14 +81,29 @@ struct WindowTokens {
     }
 };
 
-// Attend one wave's (token, group) over the tokens of `src`.
-// Kg/Vg point at element (token 0, group g, dim 0) of the cache; rows are
-// Hkv*D elements apart.  `vs` is this wave's LDS buffer [kSlots][D + 4].
-template <int D, typename Src>
-__device__ __forceinline__ void attend_range(const uint16_t *__restrict__ Kg,
-                                             const uint16_t *__restrict__ Vg, int Hkv,
-                                             const Src &src, const bf16x8 (&qf)[D / 32],
-                                             float scale_log2, uint16_t *vs, WaveState<D> &st)
+// Where the K/V rows of one KV group g come from.  Bf16Rows: Kg/Vg point at element
+// (token 0, group g, dim 0) of a bf16 cache; rows are Hkv*D elements apart.
+struct Bf16Rows {
+    static constexpr bool kFp8 = false;
+    const uint16_t *Kg, *Vg;
+};
+// Fp8Rows: e4m3 codes laid out the same way (one byte per element), and one fp32 scale per
+// (token, group) at Ks[token * Hkv] / Vs[token * Hkv]: the row's values are code * scale.
+struct Fp8Rows {
+    static constexpr bool kFp8 = true;
+    const uint8_t *Kg, *Vg;
+    const float *Ks, *Vs;
+};
+
+// Attend one wave's (token, group) over the tokens of `src`, reading rows from `rows`.
+// `vs` is this wave's LDS buffer [kSlots][D + 4].  With FP8 rows the query fragments must be
+// in the permuted dim order of load_q_perm: K codes are read 16 at a time (dims
+// [64 k2 + 16 q4, +16)) and feed two MFMA steps; each row's K scale multiplies its logits and
+// its V scale its softmax weight, so the products run on exact bf16 copies of the codes.
+template <int D, typename Src, typename Rows>
+__device__ __forceinline__ void attend_range(const Rows &rows, int Hkv, const Src &src,
+                                             const bf16x8 (&qf)[D / 32], float scale_log2,
+                                             uint16_t *vs, WaveState<D> &st)
 {
     constexpr int kLd = D + 4;         // LDS row stride in elements (bytes = 8 mod 32)
     constexpr int kPieces = D / 8;     // 16-byte pieces per row
@@ -107,27 +122,48 @@ __device__ __forceinline__ void attend_range(const uint16_t *__restrict__ Kg,
         const uint64_t vmask = __ballot(valid);
         const int s_lo = (int)(s_ld & 0xffffffff), s_hi = (int)(s_ld >> 32);
 
-        // K rows for the two 16-slot A tiles.
-        u32x4 kv[2][D / 32];
+        // K rows for the two 16-slot A tiles (bf16: D/32 loads of 8 values; FP8: D/64 loads
+        // of 16 codes).
+        constexpr int kKLoads = Rows::kFp8 ? D / 64 : D / 32;
+        u32x4 kv[2][kKLoads];
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             const int src = h * 16 + col;
             const int64_t sk = ((int64_t)(uint32_t)__shfl(s_lo, src)) |
                                ((int64_t)__shfl(s_hi, src) << 32);
-            const uint16_t *kr = Kg + sk * row_elems + q4 * 8;
+            if constexpr (Rows::kFp8) {
+                const uint8_t *kr = rows.Kg + sk * row_elems + q4 * 16;
 #pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk)
-                kv[h][kk] = load16(kr + kk * 32);
+                for (int k2 = 0; k2 < kKLoads; ++k2)
+                    kv[h][k2] = load16(kr + k2 * 64);
+            } else {
+                const uint16_t *kr = rows.Kg + sk * row_elems + q4 * 8;
+#pragma unroll
+                for (int kk = 0; kk < kKLoads; ++kk)
+                    kv[h][kk] = load16(kr + kk * 32);
+            }
         }
-        // V pieces: flat piece f = lane + 64*ci covers slot f / kPieces, piece f % kPieces.
-        u32x4 vv[kVChunks];
+        // V pieces: flat piece f = lane + 64*ci covers slot f / pieces, piece f % pieces
+        // (pieces of 8 bf16 values, or of 16 FP8 codes).
+        constexpr int kVPieces = Rows::kFp8 ? D / 16 : kPieces;
+        constexpr int kVLoads = Rows::kFp8 ? D / 32 : kVChunks;
+        u32x4 vv[kVLoads];
 #pragma unroll
-        for (int ci = 0; ci < kVChunks; ++ci) {
+        for (int ci = 0; ci < kVLoads; ++ci) {
             const int f = lane + 64 * ci;
-            const int slot = f / kPieces, piece = f - slot * kPieces;
+            const int slot = f / kVPieces, piece = f - slot * kVPieces;
             const int64_t sv = ((int64_t)(uint32_t)__shfl(s_lo, slot)) |
                                ((int64_t)__shfl(s_hi, slot) << 32);
-            vv[ci] = load16(Vg + sv * row_elems + piece * 8);
+            if constexpr (Rows::kFp8)
+                vv[ci] = load16(rows.Vg + sv * row_elems + piece * 16);
+            else
+                vv[ci] = load16(rows.Vg + sv * row_elems + piece * 8);
+        }
+        // FP8: the scales of this lane's slot (lane & 31); others read them by shuffle
+        float k_scale = 1.0f, v_scale = 1.0f;
+        if constexpr (Rows::kFp8) {
+            k_scale = rows.Ks[s_ld * Hkv];
+            v_scale = rows.Vs[s_ld * Hkv];
         }
 
         // S^T = K Q^T for slots 0-15 and 16-31.
@@ -135,9 +171,22 @@ __device__ __forceinline__ void attend_range(const uint16_t *__restrict__ Kg,
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
             sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if constexpr (Rows::kFp8) {
 #pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk)
-                sc[h] = mfma_16x16x32(as_bf16x8(kv[h][kk]), qf[kk], sc[h]);
+                for (int k2 = 0; k2 < kKLoads; ++k2) {
+                    bf16x8 lo, hi;
+                    e4m3x16_to_bf16x8x2(kv[h][k2], lo, hi);
+                    sc[h] = mfma_16x16x32(lo, qf[2 * k2], sc[h]);
+                    sc[h] = mfma_16x16x32(hi, qf[2 * k2 + 1], sc[h]);
+                }
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    sc[h][r] *= __shfl(k_scale, h * 16 + q4 * 4 + r);
+            } else {
+#pragma unroll
+                for (int kk = 0; kk < kKLoads; ++kk)
+                    sc[h] = mfma_16x16x32(as_bf16x8(kv[h][kk]), qf[kk], sc[h]);
+            }
         }
 
         // Online softmax (base 2).  Lane holds slots 16h + 4*q4 + r of head col.
@@ -166,6 +215,8 @@ __device__ __forceinline__ void attend_range(const uint16_t *__restrict__ Kg,
                 p[h][r] = bf16_bits_to_f32(f32_to_bf16_bits(pe));
                 psum += p[h][r];
                 psum32 += pe;
+                if constexpr (Rows::kFp8)  // the V row's scale rides on its weight
+                    p[h][r] = pe * __shfl(v_scale, h * 16 + q4 * 4 + r);
             }
         st.l = st.l * alpha + psum;
         st.l32 = st.l32 * alpha + psum32;
@@ -185,12 +236,23 @@ __device__ __forceinline__ void attend_range(const uint16_t *__restrict__ Kg,
         // Stage V rows in LDS (row stride kLd elements, 8-byte aligned).
         wave_lds_handoff();
 #pragma unroll
-        for (int ci = 0; ci < kVChunks; ++ci) {
+        for (int ci = 0; ci < kVLoads; ++ci) {
             const int f = lane + 64 * ci;
-            const int slot = f / kPieces, piece = f - slot * kPieces;
-            uint2 *dst = reinterpret_cast<uint2 *>(vs + slot * kLd + piece * 8);
-            dst[0] = uint2{vv[ci][0], vv[ci][1]};
-            dst[1] = uint2{vv[ci][2], vv[ci][3]};
+            const int slot = f / kVPieces, piece = f - slot * kVPieces;
+            if constexpr (Rows::kFp8) {
+                uint32_t w[8];
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    e4m3x4_to_bf16(vv[ci][e], w[2 * e], w[2 * e + 1]);
+                uint2 *dst = reinterpret_cast<uint2 *>(vs + slot * kLd + piece * 16);
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    dst[e] = uint2{w[2 * e], w[2 * e + 1]};
+            } else {
+                uint2 *dst = reinterpret_cast<uint2 *>(vs + slot * kLd + piece * 8);
+                dst[0] = uint2{vv[ci][0], vv[ci][1]};
+                dst[1] = uint2{vv[ci][2], vv[ci][3]};
+            }
         }
         wave_lds_handoff();
 
@@ -222,6 +284,26 @@ __device__ __forceinline__ void load_q(const uint16_t *__restrict__ qh, int hpg,
         if (col < hpg)
             v = load16(qh + (int64_t)col * D + kk * 32 + q4 * 8);
         qf[kk] = as_bf16x8(v);
+    }
+}
+
+// Query fragments in the dim order the FP8 rows use: qf[2 k2 + h] holds dims
+// [64 k2 + 16 q4 + 8 h, +8) of head col (D a multiple of 64).
+template <int D>
+__device__ __forceinline__ void load_q_perm(const uint16_t *__restrict__ qh, int hpg,
+                                            bf16x8 (&qf)[D / 32])
+{
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int k2 = 0; k2 < D / 64; ++k2) {
+        u32x4 v0 = {0u, 0u, 0u, 0u}, v1 = {0u, 0u, 0u, 0u};
+        if (col < hpg) {
+            v0 = load16(qh + (int64_t)col * D + k2 * 64 + q4 * 16);
+            v1 = load16(qh + (int64_t)col * D + k2 * 64 + q4 * 16 + 8);
+        }
+        qf[2 * k2] = as_bf16x8(v0);
+        qf[2 * k2 + 1] = as_bf16x8(v1);
     }
 }
 
@@ -372,8 +454,8 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
     else
         load_state<D>(st, a.state + state_offset(a, r, g));
     const SparseTokens src{a.idx + r * a.k, e_lo, e_hi, t, c, a.B};
-    attend_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D, a.Hkv, src, qf, a.scale_log2,
-                    lds + wave * kSlots * (D + 4), st);
+    attend_range<D>(Bf16Rows{a.kc + (int64_t)g * D, a.vc + (int64_t)g * D}, a.Hkv, src, qf,
+                    a.scale_log2, lds + wave * kSlots * (D + 4), st);
 
     if (a.slice + 1 >= a.nslices)
         store_row<D>(st, a, r, g, hpg);
@@ -401,12 +483,12 @@ __global__ __launch_bounds__(512) void k_swa(AttnArgs a)
     WaveState<D> st;
     init_state<D>(st);
     const WindowTokens src{s0, t};
-    attend_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D, a.Hkv, src, qf, a.scale_log2,
-                    lds + wave * kSlots * (D + 4), st);
+    attend_range<D>(Bf16Rows{a.kc + (int64_t)g * D, a.vc + (int64_t)g * D}, a.Hkv, src, qf,
+                    a.scale_log2, lds + wave * kSlots * (D + 4), st);
     store_row<D>(st, a, r, g, hpg);
 }
 
-template <int D>
+template <int D, bool kFp8>
 __global__ __launch_bounds__(512) void k_attn_decode_part(AttnArgs a)
 {
     extern __shared__ __align__(16) uint16_t lds[];
@@ -423,14 +505,24 @@ __global__ __launch_bounds__(512) void k_attn_decode_part(AttnArgs a)
     const int hpg = a.Hq / a.Hkv;
 
     bf16x8 qf[D / 32];
-    load_q<D>(a.q + ((int64_t)s * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
+    if constexpr (kFp8)
+        load_q_perm<D>(a.q + ((int64_t)s * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
+    else
+        load_q<D>(a.q + ((int64_t)s * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
     WaveState<D> st;
     init_state<D>(st);
     const int64_t base = (int64_t)s * a.cache_seq_stride + (int64_t)g * D;
     if (e0 < e1) {
         const SparseTokens src{a.idx + (int64_t)s * a.k, e0, e1, t, c, a.B};
-        attend_range<D>(a.kc + base, a.vc + base, a.Hkv, src, qf, a.scale_log2,
-                        lds + wave * kSlots * (D + 4), st);
+        uint16_t *vs = lds + wave * kSlots * (D + 4);
+        if constexpr (kFp8) {
+            const int64_t sb = (int64_t)s * a.scale_seq_stride * a.Hkv + g;
+            attend_range<D>(Fp8Rows{a.kq + base, a.vq + base, a.ksc + sb, a.vsc + sb}, a.Hkv,
+                            src, qf, a.scale_log2, vs, st);
+        } else {
+            attend_range<D>(Bf16Rows{a.kc + base, a.vc + base}, a.Hkv, src, qf, a.scale_log2,
+                            vs, st);
+        }
     }
 
     const float l = sum_across_rows(st.l);
@@ -565,8 +657,12 @@ template <int D>
 static hipError_t launch_decode_d(const AttnArgs &a, hipStream_t stream)
 {
     const size_t lds = (size_t)a.Hkv * kSlots * (D + 4) * sizeof(uint16_t);
-    hipLaunchKernelGGL(k_attn_decode_part<D>, dim3((unsigned)a.nsplit, (unsigned)a.rows),
-                       dim3(64 * a.Hkv), lds, stream, a);
+    if (a.kq)
+        hipLaunchKernelGGL((k_attn_decode_part<D, true>), dim3((unsigned)a.nsplit, (unsigned)a.rows),
+                           dim3(64 * a.Hkv), lds, stream, a);
+    else
+        hipLaunchKernelGGL((k_attn_decode_part<D, false>), dim3((unsigned)a.nsplit, (unsigned)a.rows),
+                           dim3(64 * a.Hkv), lds, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

@@ -273,4 +273,50 @@ hipError_t launch_index_from_keys(const IndexKeysArgs &a, int64_t max_blocks, hi
     return hipGetLastError();
 }
 
+// --------------------------------------------------------------------------------------------
+// FP8 storage of cached rows for the decode path (the released checkpoint is e4m3 with
+// scaling blocks; here one fp32 scale per cached row).  One wave per row: the row's largest
+// magnitude by a wave reduction, scale = amax / 448 (1 for a zero row), then each element's
+// e4m3 code of x / scale; every step in fp32, rounding to nearest even.
+__global__ __launch_bounds__(256) void k_quantize_rows(const uint16_t *__restrict__ x, int64_t rows,
+                                                       int cols, uint8_t *__restrict__ codes,
+                                                       float *__restrict__ scales)
+{
+    const int64_t r = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= rows)
+        return;
+    const int lane = threadIdx.x & 63;
+    const uint16_t *xr = x + r * cols;
+    float amax = 0.0f;
+    for (int e = lane; e < cols; e += 64)
+        amax = fmaxf(amax, fabsf(bf16_bits_to_f32(xr[e])));
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        amax = fmaxf(amax, __shfl_xor(amax, o));
+    float scale = amax / 448.0f;
+    if (!(scale > 0.0f))
+        scale = 1.0f;
+    uint8_t *cr = codes + r * cols;
+    for (int e = lane; e < cols; e += 64)
+        cr[e] = (uint8_t)e4m3_encode(bf16_bits_to_f32(xr[e]) / scale);
+    if (lane == 0)
+        scales[r] = scale;
+}
+
+hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int cols, uint8_t *codes,
+                                float *scales, hipStream_t stream)
+{
+    // a dispatch counts its work-items in 32 bits: launch at most 2^24 rows (2^30 items) at once
+    constexpr int64_t kChunk = (int64_t)1 << 24;
+    for (int64_t r0 = 0; r0 < rows; r0 += kChunk) {
+        const int64_t n = rows - r0 < kChunk ? rows - r0 : kChunk;
+        hipLaunchKernelGGL(k_quantize_rows, dim3((unsigned)((n + 3) / 4)), dim3(256), 0, stream,
+                           x + r0 * cols, n, cols, codes + r0 * cols, scales + r0);
+        const hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
+}
+
 } // namespace sgqa

@@ -357,6 +357,78 @@ __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
     }
 }
 
+// FP8 index variant of k_decode_keys: rows of P e4m3 codes with one fp32 scale each.  A lane
+// loads 16 codes (dims [64 k2 + 16 q4, +16)) per 64-dim step and converts them exactly to two
+// bf16 fragments for two MFMA steps; the query proxy is loaded in the same permuted order, so
+// the contraction is unchanged.  The row's scale multiplies the product afterwards.
+template <int P>
+__global__ __launch_bounds__(256) void k_decode_keys_fp8(DecodeTopkArgs a)
+{
+    constexpr int U = 8;  // 16-block groups in flight per wave (16 B per row and step)
+    const int s = blockIdx.y;
+    const int64_t t = a.pos.v[s];
+    const int64_t c = t / a.B;
+    const int64_t j0 = (int64_t)blockIdx.x * kKeysPerWG;
+    if (j0 >= c)
+        return;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    const uint8_t *kq = a.kbq + (int64_t)s * a.kbs_seq_stride * P;
+    const float *ksc = a.kbs + (int64_t)s * a.kbs_seq_stride;
+    const uint16_t *qp = a.qp + (int64_t)s * a.qp_seq_stride;
+    uint32_t *keys = a.keys + (int64_t)s * a.keys_ld;
+
+    bf16x8 af[P / 32];  // af[2 k2 + h] = qp[64 k2 + 16 q4 + 8 h, +8)
+#pragma unroll
+    for (int k2 = 0; k2 < P / 64; ++k2) {
+        af[2 * k2] = as_bf16x8(load16(qp + k2 * 64 + q4 * 16));
+        af[2 * k2 + 1] = as_bf16x8(load16(qp + k2 * 64 + q4 * 16 + 8));
+    }
+
+    uint32_t *umax = a.umax + (int64_t)s * a.units_ld + (int64_t)blockIdx.x * kUnitsPerWG;
+    constexpr int NG = kKeysPerWG / kUnitBlocks;
+#pragma unroll 1
+    for (int g0 = wave; g0 < NG; g0 += 4 * U) {
+        u32x4 bv[U][P / 64];
+        float sc[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            int64_t jb = j0 + (int64_t)(g0 + 4 * u) * kUnitBlocks + col;
+            if (jb >= c)
+                jb = j0;  // a valid row; its score is discarded
+#pragma unroll
+            for (int k2 = 0; k2 < P / 64; ++k2)
+                bv[u][k2] = load16(kq + jb * P + k2 * 64 + q4 * 16);
+            sc[u] = ksc[jb];
+        }
+#pragma unroll
+        for (int u = 0; u < U; ++u) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int k2 = 0; k2 < P / 64; ++k2) {
+                bf16x8 lo, hi;
+                e4m3x16_to_bf16x8x2(bv[u][k2], lo, hi);
+                acc = mfma_16x16x32(af[2 * k2], lo, acc);
+                acc = mfma_16x16x32(af[2 * k2 + 1], hi, acc);
+            }
+            const int64_t j = j0 + (int64_t)(g0 + 4 * u) * kUnitBlocks + col;
+            const uint32_t key = j < c ? score_key(acc[0] * sc[u]) : 0u;
+            uint32_t m = key;
+#pragma unroll
+            for (int o = 8; o > 0; o >>= 1) {
+                const uint32_t v = (uint32_t)__shfl_xor((int)m, o);
+                m = v > m ? v : m;
+            }
+            if (q4 == 0) {
+                if (j < c)
+                    keys[j] = key;
+                if (col == 0)
+                    umax[g0 + 4 * u] = m;
+            }
+        }
+    }
+}
+
 // Bitwise OR and AND over the workgroup (every thread calls; `red` holds 2 * NT/64 words).
 template <int NT>
 __device__ __forceinline__ void block_or_and(uint32_t &vor, uint32_t &vand, uint32_t *red)
@@ -720,14 +792,31 @@ static void launch_decode_keys_p(const DecodeTopkArgs &a, hipStream_t stream)
     hipLaunchKernelGGL(k_decode_keys<P>, dim3(nwg, (unsigned)a.nseq), dim3(256), 0, stream, a);
 }
 
+template <int P>
+static void launch_decode_keys_fp8_p(const DecodeTopkArgs &a, hipStream_t stream)
+{
+    const unsigned nwg = (unsigned)(a.keys_ld / kKeysPerWG);
+    hipLaunchKernelGGL(k_decode_keys_fp8<P>, dim3(nwg, (unsigned)a.nseq), dim3(256), 0, stream, a);
+}
+
 hipError_t launch_decode_topk(const DecodeTopkArgs &a, hipStream_t stream)
 {
-    switch (a.P) {
-    case 32: launch_decode_keys_p<32>(a, stream); break;
-    case 64: launch_decode_keys_p<64>(a, stream); break;
-    case 128: launch_decode_keys_p<128>(a, stream); break;
-    case 256: launch_decode_keys_p<256>(a, stream); break;
-    default: return hipErrorInvalidValue;
+    if (a.kbq) {
+        switch (a.P) {
+        case 64: launch_decode_keys_fp8_p<64>(a, stream); break;
+        case 128: launch_decode_keys_fp8_p<128>(a, stream); break;
+        case 256: launch_decode_keys_fp8_p<256>(a, stream); break;
+        case 512: launch_decode_keys_fp8_p<512>(a, stream); break;
+        default: return hipErrorInvalidValue;
+        }
+    } else {
+        switch (a.P) {
+        case 32: launch_decode_keys_p<32>(a, stream); break;
+        case 64: launch_decode_keys_p<64>(a, stream); break;
+        case 128: launch_decode_keys_p<128>(a, stream); break;
+        case 256: launch_decode_keys_p<256>(a, stream); break;
+        default: return hipErrorInvalidValue;
+        }
     }
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)

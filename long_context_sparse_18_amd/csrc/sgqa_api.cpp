@@ -580,3 +580,163 @@ sgqa_status sgqa_sparse_attn_decode(const sgqa_dims *dims, const sgqa_bf16 *q,
 }
 
 } // extern "C"
+
+// ---------------------------------------------------------------------------------- FP8 decode
+sgqa_status sgqa_quantize_fp8(const sgqa_bf16 *x, int64_t rows, int32_t cols, uint8_t *codes,
+                              float *scales, void *stream)
+{
+    if (rows < 0 || cols <= 0 || cols > 4096)
+        return fail(rows < 0 || cols <= 0 ? SGQA_ERR_SHAPE : SGQA_ERR_UNSUPPORTED,
+                    "rows %lld must be >= 0 and cols %d in [1, 4096]", (long long)rows, cols);
+    if (rows == 0)
+        return ok();
+    if (!x || !codes || !scales)
+        return fail(SGQA_ERR_NULL, "x, codes and scales must be non-NULL");
+    if (!aligned(x, 2) || !aligned(scales, 4))
+        return fail(SGQA_ERR_SHAPE, "x must be 2-byte and scales 4-byte aligned");
+    return hip_status(sgqa::launch_quantize_rows(x, rows, cols, codes, scales,
+                                                 reinterpret_cast<hipStream_t>(stream)),
+                      "quantize_fp8 launch");
+}
+
+sgqa_status sgqa_indexer_topk_fp8(const sgqa_dims *dims, const sgqa_bf16 *qp,
+                                  int64_t qp_seq_stride, const uint8_t *kb_codes,
+                                  const float *kb_scales, int64_t kb_seq_stride,
+                                  const int64_t *q_pos, int32_t nseq, int32_t *idx,
+                                  float *sel_scores, void *workspace, size_t workspace_bytes,
+                                  void *stream)
+{
+    sgqa_status st = check_dims(dims, false, true);
+    if (st != SGQA_OK)
+        return st;
+    const int P = dims->proxy_dim;
+    if (P != 64 && P != 128 && P != 256 && P != 512)
+        return fail(SGQA_ERR_UNSUPPORTED, "FP8 index needs proxy_dim in {64,128,256,512}, got %d", P);
+    if (nseq < 0)
+        return fail(SGQA_ERR_SHAPE, "nseq %d is negative", nseq);
+    if (nseq > sgqa::kMaxSeq)
+        return fail(SGQA_ERR_UNSUPPORTED, "nseq %d exceeds %d", nseq, sgqa::kMaxSeq);
+    if (nseq == 0)
+        return ok();
+    if (!qp || !kb_codes || !kb_scales || !q_pos || !idx)
+        return fail(SGQA_ERR_NULL, "qp, kb_codes, kb_scales, q_pos and idx must be non-NULL");
+    if (!aligned(qp, 16) || !aligned(kb_codes, 16) || !aligned(kb_scales, 4) ||
+        !aligned(idx, 4) || !aligned(sel_scores, 4))
+        return fail(SGQA_ERR_SHAPE, "qp and kb_codes must be 16-byte aligned");
+    int64_t max_pos = 0;
+    for (int s = 0; s < nseq; ++s) {
+        if (q_pos[s] < 0)
+            return fail(SGQA_ERR_SHAPE, "q_pos[%d] = %lld is negative", s, (long long)q_pos[s]);
+        max_pos = q_pos[s] > max_pos ? q_pos[s] : max_pos;
+    }
+    const int64_t max_cand = max_pos / dims->block_size;
+    if (nseq > 1 && (qp_seq_stride < P || qp_seq_stride % 8 != 0))
+        return fail(SGQA_ERR_SHAPE, "qp_seq_stride %lld must be >= P and a multiple of 8",
+                    (long long)qp_seq_stride);
+    if (nseq > 1 && kb_seq_stride < max_cand)
+        return fail(SGQA_ERR_SHAPE, "kb_seq_stride %lld must cover %lld blocks",
+                    (long long)kb_seq_stride, (long long)max_cand);
+    if (max_cand > 0 && !sgqa::decode_topk_supported(max_cand, dims->topk_blocks))
+        return fail(SGQA_ERR_UNSUPPORTED, "FP8 decode top-k needs 2 <= k and <= %lld candidate blocks",
+                    (long long)sgqa::kDecodeMaxCand);
+    const size_t need = max_cand > 0 ? sgqa::decode_topk_workspace(nseq, max_cand) : 0;
+    if (need > 0 && (!workspace || workspace_bytes < need))
+        return fail(SGQA_ERR_WORKSPACE, "FP8 decode top-k needs %zu bytes of workspace, got %zu",
+                    need, workspace ? workspace_bytes : (size_t)0);
+    if (workspace && !aligned(workspace, 16))
+        return fail(SGQA_ERR_SHAPE, "workspace must be 16-byte aligned");
+    sgqa::DecodeTopkArgs da{};
+    da.qp = qp;
+    da.qp_seq_stride = qp_seq_stride;
+    da.kbq = kb_codes;
+    da.kbs = kb_scales;
+    da.kbs_seq_stride = kb_seq_stride;
+    for (int s = 0; s < nseq; ++s)
+        da.pos.v[s] = q_pos[s];
+    da.nseq = nseq;
+    da.P = P;
+    da.B = dims->block_size;
+    da.k = dims->topk_blocks;
+    const int64_t mc = max_cand > 0 ? max_cand : 1;
+    da.keys = static_cast<uint32_t *>(workspace);
+    da.keys_ld = sgqa::decode_keys_ld(mc);
+    da.umax = da.keys ? da.keys + (size_t)nseq * da.keys_ld : nullptr;
+    da.units_ld = sgqa::decode_units_ld(mc);
+    da.idx = idx;
+    da.sel_scores = sel_scores;
+    return hip_status(sgqa::launch_decode_topk(da, reinterpret_cast<hipStream_t>(stream)),
+                      "FP8 decode top-k launch");
+}
+
+sgqa_status sgqa_sparse_attn_decode_fp8(const sgqa_dims *dims, const sgqa_bf16 *q,
+                                        const uint8_t *k_codes, const uint8_t *v_codes,
+                                        const float *k_scales, const float *v_scales,
+                                        int64_t cache_seq_stride, const sgqa_bf16 *gate,
+                                        const int32_t *idx, const int64_t *cache_lens,
+                                        int32_t nseq, float softmax_scale, sgqa_bf16 *out,
+                                        float *lse, void *workspace, size_t workspace_bytes,
+                                        void *stream)
+{
+    sgqa_status st = check_dims(dims, true, false);
+    if (st != SGQA_OK)
+        return st;
+    if (nseq < 0)
+        return fail(SGQA_ERR_SHAPE, "nseq %d is negative", nseq);
+    if (nseq > sgqa::kMaxSeq)
+        return fail(SGQA_ERR_UNSUPPORTED, "nseq %d exceeds %d", nseq, sgqa::kMaxSeq);
+    if (!std::isfinite(softmax_scale))
+        return fail(SGQA_ERR_SHAPE, "softmax_scale must be finite");
+    if (nseq == 0)
+        return ok();
+    if (!q || !k_codes || !v_codes || !k_scales || !v_scales || !gate || !idx || !out ||
+        !cache_lens)
+        return fail(SGQA_ERR_NULL, "q, codes, scales, gate, idx, cache_lens and out must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k_codes, 16) || !aligned(v_codes, 16) ||
+        !aligned(k_scales, 4) || !aligned(v_scales, 4) || !aligned(out, 2) || !aligned(idx, 4) ||
+        !aligned(lse, 4) || !aligned(gate, 2))
+        return fail(SGQA_ERR_SHAPE, "q and code arrays must be 16-byte aligned");
+    int64_t max_len = 0;
+    for (int s = 0; s < nseq; ++s) {
+        if (cache_lens[s] < 1)
+            return fail(SGQA_ERR_SHAPE, "cache_lens[%d] = %lld must be >= 1", s,
+                        (long long)cache_lens[s]);
+        max_len = cache_lens[s] > max_len ? cache_lens[s] : max_len;
+    }
+    if (nseq > 1 && cache_seq_stride < max_len)
+        return fail(SGQA_ERR_SHAPE, "cache_seq_stride %lld (tokens) must be >= %lld",
+                    (long long)cache_seq_stride, (long long)max_len);
+    const size_t need = sgqa_workspace_bytes(SGQA_OP_ATTN_DECODE, dims, nseq, 1, max_len);
+    if (!workspace || workspace_bytes < need)
+        return fail(SGQA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 16))
+        return fail(SGQA_ERR_SHAPE, "workspace must be 16-byte aligned");
+    const int64_t row = (int64_t)dims->num_kv_heads * dims->head_dim;
+    sgqa::AttnArgs a{};
+    a.q = q;
+    a.kq = k_codes;
+    a.vq = v_codes;
+    a.ksc = k_scales;
+    a.vsc = v_scales;
+    a.scale_seq_stride = cache_seq_stride;
+    a.cache_seq_stride = cache_seq_stride * row;  // elements (= bytes) of codes
+    a.gate = gate;
+    a.idx = idx;
+    for (int s = 0; s < nseq; ++s)
+        a.qpos.v[s] = cache_lens[s] - 1;
+    a.rows = nseq;
+    a.Hq = dims->num_q_heads;
+    a.Hkv = dims->num_kv_heads;
+    a.d = dims->head_dim;
+    a.B = dims->block_size;
+    a.k = dims->topk_blocks;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.out = out;
+    a.lse = lse;
+    sgqa::decode_split_plan(a.k, a.B, a.nsplit, a.entries_per_split);
+    const size_t slots = (size_t)nseq * a.nsplit * a.Hq;
+    a.part_o = static_cast<float *>(workspace);
+    a.part_ml = a.part_o + slots * a.d;
+    return hip_status(sgqa::launch_attn_decode(a, reinterpret_cast<hipStream_t>(stream)),
+                      "FP8 sparse_attn_decode launch");
+}

@@ -137,4 +137,52 @@ __device__ __forceinline__ int block_exclusive_scan(int v, int *scratch, int &to
     return before + inc - v;
 }
 
+// ---- OCP E4M3 (8-bit float: sign, 4 exponent bits with bias 7, 3 fraction bits) ----
+// Four e4m3 codes (bytes of c, low byte first) -> four bf16 (two per word, low half first).
+// Every e4m3 value is a bf16 value, so taking the top half of the fp32 conversion is exact.
+__device__ __forceinline__ void e4m3x4_to_bf16(uint32_t c, uint32_t &w0, uint32_t &w1)
+{
+    const auto a = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, false);  // bytes 0, 1
+    const auto b = __builtin_amdgcn_cvt_pk_f32_fp8((int)c, true);   // bytes 2, 3
+    w0 = (__float_as_uint(a[0]) >> 16) | (__float_as_uint(a[1]) & 0xffff0000u);
+    w1 = (__float_as_uint(b[0]) >> 16) | (__float_as_uint(b[1]) & 0xffff0000u);
+}
+
+// Sixteen e4m3 codes -> two MFMA fragments of eight bf16 (codes 0-7, then 8-15).
+__device__ __forceinline__ void e4m3x16_to_bf16x8x2(const u32x4 &c, bf16x8 &lo, bf16x8 &hi)
+{
+    uint32_t w[8];
+    e4m3x4_to_bf16(c[0], w[0], w[1]);
+    e4m3x4_to_bf16(c[1], w[2], w[3]);
+    e4m3x4_to_bf16(c[2], w[4], w[5]);
+    e4m3x4_to_bf16(c[3], w[6], w[7]);
+    lo = as_bf16x8(u32x4{w[0], w[1], w[2], w[3]});
+    hi = as_bf16x8(u32x4{w[4], w[5], w[6], w[7]});
+}
+
+// Nearest e4m3 code of y, ties to the even code, magnitudes >= 448 saturating to 448.
+// In units of the spacing 2^(E-3) of y's binade (2^-9 below 2^-6) the value rounds to an
+// integer r in [0, 16]; r = 16 is the next binade's first value.
+__device__ __forceinline__ uint32_t e4m3_encode(float y)
+{
+    const uint32_t sgn = (__float_as_uint(y) >> 24) & 0x80u;
+    const float a = fabsf(y);
+    if (a >= 448.0f)
+        return sgn | 0x7Eu;
+    int E = (int)((__float_as_uint(a) >> 23) & 0xffu) - 127;
+    if (E < -6)
+        E = -6;
+    const float r = rintf(ldexpf(a, 3 - E));
+    if (r == 0.0f)
+        return sgn;
+    if (E == -6 && r < 8.0f)
+        return sgn | (uint32_t)r;
+    int Ev = E, mant = (int)r - 8;
+    if (r == 16.0f) {
+        Ev = E + 1;
+        mant = 0;
+    }
+    return sgn | (uint32_t)(((Ev + 7) << 3) | mant);
+}
+
 } // namespace sgqa

@@ -31,6 +31,11 @@ struct IndexKeysArgs {
 };
 hipError_t launch_index_from_keys(const IndexKeysArgs &a, int64_t max_blocks, hipStream_t stream);
 
+// FP8 storage of rows: codes[r][i] = e4m3(x[r][i] / scale[r]), scale[r] = max_i |x[r][i]| / 448
+// (1 for a zero row), all in fp32.
+hipError_t launch_quantize_rows(const uint16_t *x, int64_t rows, int cols, uint8_t *codes,
+                                float *scales, hipStream_t stream);
+
 // Indexer scores for queries [t0, t0+nq) of every sequence into ws rows
 // (row = s*nq + i, row stride ld floats); only blocks j < (q_start[s]+i)/B are written.
 struct ScoreArgs {
@@ -87,6 +92,10 @@ struct DecodeTopkArgs {
     int64_t units_ld;
     int32_t *idx;        // [nseq][k]
     float *sel_scores;   // [nseq][k] or null
+    // FP8 index (instead of kb): e4m3 codes [nseq][kbs_seq_stride][P], one fp32 scale per row
+    const uint8_t *kbq;
+    const float *kbs;
+    int64_t kbs_seq_stride;  // rows (blocks) per sequence
 };
 // False when the shape is outside the decode path (then the general path is used).
 bool decode_topk_supported(int64_t max_cand, int k);
@@ -122,6 +131,13 @@ struct AttnArgs {
     float *state;
     int64_t state_bytes;
     int32_t state_stride;
+    // FP8 caches (decode): e4m3 codes [nseq][scale_seq_stride][Hkv][d] and one fp32 scale per
+    // (token, KV head) [nseq][scale_seq_stride][Hkv]; used instead of kc / vc when kq is set
+    const uint8_t *kq;
+    const uint8_t *vq;
+    const float *ksc;
+    const float *vsc;
+    int64_t scale_seq_stride;  // tokens per sequence
 };
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream);

@@ -23,7 +23,8 @@ OP_ATTN_DECODE = 2
 OP_ATTN_PREFILL = 3
 
 EXPORTS = ("sgqa_index_build", "sgqa_index_build_from_keys", "sgqa_indexer_topk", "sgqa_sparse_attn_prefill",
-           "sgqa_sparse_attn_decode", "sgqa_swa_prefill", "sgqa_workspace_bytes",
+           "sgqa_sparse_attn_decode", "sgqa_swa_prefill", "sgqa_quantize_fp8",
+           "sgqa_indexer_topk_fp8", "sgqa_sparse_attn_decode_fp8", "sgqa_workspace_bytes",
            "sgqa_status_string", "sgqa_last_error")
 
 
@@ -73,6 +74,13 @@ def load():
                                             p, sz, p]
     lib.sgqa_swa_prefill.restype = st
     lib.sgqa_swa_prefill.argtypes = [dp, p, p, p, p, i64, i32, i64, i64, ctypes.c_float, p, p, p]
+    lib.sgqa_quantize_fp8.restype = st
+    lib.sgqa_quantize_fp8.argtypes = [p, i64, i32, p, p, p]
+    lib.sgqa_indexer_topk_fp8.restype = st
+    lib.sgqa_indexer_topk_fp8.argtypes = [dp, p, i64, p, p, i64, p, i32, p, p, p, sz, p]
+    lib.sgqa_sparse_attn_decode_fp8.restype = st
+    lib.sgqa_sparse_attn_decode_fp8.argtypes = [dp, p, p, p, p, p, i64, p, p, p, i32,
+                                                ctypes.c_float, p, p, p, sz, p]
     lib.sgqa_workspace_bytes.restype = sz
     lib.sgqa_workspace_bytes.argtypes = [ctypes.c_int, dp, i32, i32, i64]
     lib.sgqa_status_string.restype = ctypes.c_char_p
@@ -205,3 +213,67 @@ def swa_prefill(shape: LayerShape, q, k_cache, v_cache, gate, q_start: int, L: i
     check(load().sgqa_swa_prefill(ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                   _ptr(gate), q_start, q.shape[0], L, window, softmax_scale,
                                   _ptr(out), _ptr(lse), _stream(stream, q)))
+
+
+def quantize_fp8(x: torch.Tensor, codes: torch.Tensor, scales: torch.Tensor, stream=None):
+    """FP8 (E4M3) storage of rows: x [..., cols] bf16 -> codes [..., cols] uint8 and one fp32
+    scale per row, scales [...]."""
+    _need_cuda(x, codes, scales)
+    cols = x.shape[-1]
+    rows = x.numel() // cols if cols else 0
+    if codes.shape != x.shape or scales.numel() != rows:
+        raise ValueError("codes must match x and scales hold one value per row")
+    check(load().sgqa_quantize_fp8(_ptr(x), rows, cols, _ptr(codes), _ptr(scales),
+                                   _stream(stream, x)))
+
+
+def indexer_topk_fp8(shape: LayerShape, qp: torch.Tensor, kb_codes: torch.Tensor,
+                     kb_scales: torch.Tensor, q_pos, idx: torch.Tensor,
+                     sel_scores: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                     stream=None):
+    """One query per sequence on an FP8 index: qp [nseq, P], kb_codes [nseq, nblk, P] uint8,
+    kb_scales [nseq, nblk] fp32 -> idx [nseq, k]."""
+    _need_cuda(qp, kb_codes, kb_scales, idx, sel_scores, workspace)
+    q_pos = list(q_pos)
+    nseq = len(q_pos)
+    qp2 = qp.reshape(nseq, -1)
+    if (kb_codes.dim() != 3 or kb_scales.shape != kb_codes.shape[:2] or
+            not kb_codes.is_contiguous() or not kb_scales.is_contiguous()):
+        raise ValueError("FP8 index must be contiguous codes [nseq, nblk, P] with scales "
+                         "[nseq, nblk]")
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(OP_INDEXER_TOPK, shape, nseq, 1, max(q_pos) + 1),
+                                dtype=torch.uint8, device=qp.device)
+    d = Dims.of(shape)
+    check(load().sgqa_indexer_topk_fp8(ctypes.byref(d), _ptr(qp2), qp2.stride(0), _ptr(kb_codes),
+                                       _ptr(kb_scales), kb_scales.stride(0), _i64_array(q_pos),
+                                       nseq, _ptr(idx), _ptr(sel_scores), _ptr(workspace),
+                                       workspace.numel(), _stream(stream, qp)))
+
+
+def sparse_attn_decode_fp8(shape: LayerShape, q, k_codes, v_codes, k_scales, v_scales, gate, idx,
+                           cache_lens, softmax_scale: float, out, lse=None, workspace=None,
+                           stream=None):
+    """q [nseq, Hq, d]; k/v codes [nseq, Lmax, Hkv, d] uint8; k/v scales [nseq, Lmax, Hkv] fp32."""
+    _need_cuda(q, k_codes, v_codes, k_scales, v_scales, gate, idx, out, lse, workspace)
+    cache_lens = list(cache_lens)
+    nseq = len(cache_lens)
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(OP_ATTN_DECODE, shape, nseq, 1, max(cache_lens)),
+                                dtype=torch.uint8, device=q.device)
+    # tokens per sequence slot, the same for codes [nseq, Lmax, Hkv, d] and scales
+    # [nseq, Lmax, Hkv] (the ABI takes this count, not an element stride)
+    hkv, hd = shape.num_kv_heads, shape.head_dim
+    slot = k_codes.shape[1]
+    for c_, s_ in ((k_codes, k_scales), (v_codes, v_scales)):
+        if (c_.dim() != 4 or c_.shape[1:] != (slot, hkv, hd) or not c_.is_contiguous()
+                or s_.shape != c_.shape[:3] or not s_.is_contiguous()):
+            raise ValueError("FP8 caches must be contiguous codes [nseq, Lmax, Hkv, d] with "
+                             "scales [nseq, Lmax, Hkv]")
+    d = Dims.of(shape)
+    check(load().sgqa_sparse_attn_decode_fp8(ctypes.byref(d), _ptr(q), _ptr(k_codes),
+                                             _ptr(v_codes), _ptr(k_scales), _ptr(v_scales),
+                                             slot, _ptr(gate), _ptr(idx),
+                                             _i64_array(cache_lens), nseq, softmax_scale,
+                                             _ptr(out), _ptr(lse), _ptr(workspace),
+                                             workspace.numel(), _stream(stream, q)))

@@ -18,7 +18,7 @@ FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(sgqa_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(sgqa_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_library_exports_every_declared_symbol():
@@ -152,6 +152,41 @@ def test_index_build_from_keys_validation():
     assert call(d=dims(head_dim=96)) == sgqa.ERR_UNSUPPORTED
     assert call(nseq=65) == sgqa.ERR_UNSUPPORTED
     assert call(nseq=0) == sgqa.OK
+
+
+def test_fp8_validation():
+    lib = sgqa.load()
+    u8 = FAKE
+    assert lib.sgqa_quantize_fp8(FAKE, 10, 0, u8, FAKE, None) == sgqa.ERR_SHAPE
+    assert lib.sgqa_quantize_fp8(FAKE, -1, 8, u8, FAKE, None) == sgqa.ERR_SHAPE
+    assert lib.sgqa_quantize_fp8(FAKE, 10, 5000, u8, FAKE, None) == sgqa.ERR_UNSUPPORTED
+    assert lib.sgqa_quantize_fp8(None, 10, 8, u8, FAKE, None) == sgqa.ERR_NULL
+    assert lib.sgqa_quantize_fp8(FAKE, 0, 8, u8, FAKE, None) == sgqa.OK
+    d = dims()
+    pos = (ctypes.c_int64 * 2)((1 << 20) - 1, (1 << 20) - 1)
+    need = lib.sgqa_workspace_bytes(sgqa.OP_INDEXER_TOPK, ctypes.byref(d), 2, 1, 1 << 20)
+
+    def topk(d=d, qp=FAKE, ws=FAKE, wsb=need, kbs_stride=1 << 17):
+        return lib.sgqa_indexer_topk_fp8(ctypes.byref(d), qp, 256, FAKE, FAKE, kbs_stride, pos, 2,
+                                         FAKE, None, ws, wsb, None)
+
+    assert topk(qp=None) == sgqa.ERR_NULL
+    assert topk(d=dims(proxy_dim=32)) == sgqa.ERR_UNSUPPORTED
+    assert topk(d=dims(topk_blocks=1)) == sgqa.ERR_UNSUPPORTED
+    assert topk(wsb=need - 1) == sgqa.ERR_WORKSPACE
+    assert topk(kbs_stride=100) == sgqa.ERR_SHAPE
+    lens = (ctypes.c_int64 * 2)(1 << 20, 1 << 20)
+    dneed = lib.sgqa_workspace_bytes(sgqa.OP_ATTN_DECODE, ctypes.byref(d), 2, 1, 1 << 20)
+
+    def attn(q=FAKE, stride=1 << 20, wsb=dneed, ks=FAKE):
+        return lib.sgqa_sparse_attn_decode_fp8(ctypes.byref(d), q, FAKE, FAKE, ks, FAKE, stride,
+                                               FAKE, FAKE, lens, 2, 0.07, FAKE, None, FAKE, wsb,
+                                               None)
+
+    assert attn(q=None) == sgqa.ERR_NULL
+    assert attn(ks=None) == sgqa.ERR_NULL
+    assert attn(stride=100) == sgqa.ERR_SHAPE
+    assert attn(wsb=dneed - 1) == sgqa.ERR_WORKSPACE
 
 
 def test_decode_validation():

@@ -1,6 +1,7 @@
 """GPU parity on the tiny layer (8 query heads, 2 KV heads, d 64, proxy 32): every row,
 every stage, plus the edge cases (k = all, k = 1, B = 1, mid-block chunks, several
 sequences, decode with mixed cache lengths, small workspaces, empty calls)."""
+import dataclasses
 import math
 
 import numpy as np
@@ -351,3 +352,80 @@ def test_tiny_index_from_keys(tiny, B):
         mask = torch.ones(nblk, dtype=torch.bool, device=DEV)
         mask[last[b]] = False
         assert torch.equal(kb[b][mask], before[b][mask])
+
+
+def test_quantize_fp8_bit_exact():
+    """Row quantisation to E4M3 codes and fp32 scales equals the oracle bit for bit, on rows of
+    32, 64, 192 and 256 values spanning 2^-60 .. 2^60 in magnitude, with an all-zero row and
+    rows that reach the subnormal codes."""
+    g = torch.Generator().manual_seed(41)
+    for cols in (32, 64, 192, 256):
+        x = torch.randn((300, cols), generator=g) * torch.exp2(torch.randint(-60, 60, (300, 1),
+                                                                               generator=g).float())
+        x[3] = 0.0
+        x[5, :] = x[5, :] * 1e-3  # small values next to one large one: subnormal codes
+        x[5, 0] = 1.0
+        xb = x.to(torch.bfloat16).to(DEV)
+        codes = torch.empty(xb.shape, dtype=torch.uint8, device=DEV)
+        scales = torch.empty(xb.shape[0], dtype=torch.float32, device=DEV)
+        sgqa.quantize_fp8(xb, codes, scales)
+        torch.cuda.synchronize()
+        rc, rs = oracle.quantize_rows(bits(xb))
+        assert np.array_equal(codes.cpu().numpy(), rc), cols
+        assert np.array_equal(scales.cpu().numpy().view(np.uint32), rs.view(np.uint32)), cols
+
+
+def test_decode_fp8_mixed_lengths():
+    """FP8 decode (index and K/V caches stored as E4M3 rows with fp32 scales) for 5 sequences
+    of 1 .. 1024 tokens: codes bit-exact, selection and attention against the oracle on the
+    dequantised values."""
+    shape = dataclasses.replace(WL.shape, proxy_dim=64)
+    wl = dataclasses.replace(WL, shape=shape)
+    d = inputs.make_prefill(wl, 5, DEV)
+    lens = [1, 9, 130, 1000, 1024]
+    n, Lmax, B, k = len(lens), wl.L, shape.block_size, shape.topk_blocks
+    K = d["K"].unsqueeze(0).expand(n, -1, -1, -1).contiguous()
+    V = d["V"].unsqueeze(0).expand(n, -1, -1, -1).contiguous()
+    kp = d["kp"].unsqueeze(0).expand(n, -1, -1).contiguous()
+    Q = torch.stack([d["Q"][L_ - 1] for L_ in lens])
+    G = torch.stack([d["G"][L_ - 1] for L_ in lens])
+    qp = torch.stack([d["qp"][L_ - 1] for L_ in lens])
+    kb = torch.empty((n, wl.nblk, shape.proxy_dim), dtype=torch.bfloat16, device=DEV)
+    sgqa.index_build(shape, kp, kb, lens)
+    kbq = torch.empty(kb.shape, dtype=torch.uint8, device=DEV)
+    kbs = torch.empty(kb.shape[:2], dtype=torch.float32, device=DEV)
+    Kq = torch.empty(K.shape, dtype=torch.uint8, device=DEV)
+    Vq = torch.empty(V.shape, dtype=torch.uint8, device=DEV)
+    Ks = torch.empty(K.shape[:3], dtype=torch.float32, device=DEV)
+    Vs = torch.empty(V.shape[:3], dtype=torch.float32, device=DEV)
+    sgqa.quantize_fp8(kb, kbq, kbs)
+    sgqa.quantize_fp8(K, Kq, Ks)
+    sgqa.quantize_fp8(V, Vq, Vs)
+    idx = torch.empty((n, k), dtype=torch.int32, device=DEV)
+    sel = torch.empty((n, k), dtype=torch.float32, device=DEV)
+    sgqa.indexer_topk_fp8(shape, qp, kbq, kbs, [L_ - 1 for L_ in lens], idx, sel)
+    out = torch.empty_like(Q)
+    lse = torch.empty((n, shape.num_q_heads), dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(shape.head_dim)
+    sgqa.sparse_attn_decode_fp8(shape, Q, Kq, Vq, Ks, Vs, G, idx, lens, scale, out, lse)
+    torch.cuda.synchronize()
+    rc, rs = oracle.quantize_rows(bits(K[0]))
+    assert np.array_equal(Kq[0].cpu().numpy(), rc) and np.array_equal(Ks[0].cpu().numpy(), rs)
+    for b, L_ in enumerate(lens):
+        t = np.array([L_ - 1])
+        c = int(t[0] // B)
+        nb = -(-L_ // B)
+        kb_deq = oracle.dequant_rows(kbq[b, :nb].cpu().numpy(), kbs[b, :nb].cpu().numpy())
+        sc = oracle.scores(bits(qp[b:b + 1]), t, B, kb_deq, width=max(1, nb))
+        ref = oracle.topk(sc, t, B, k)
+        got = idx[b].cpu().numpy()
+        parity.check_selection(got, sc[0], c, k, ref[0])
+        parity.check_sel_scores(sel[b].cpu().numpy(), got, sc[0], c, k)
+        toks = torch.from_numpy(oracle.token_set(got, B, L_ - 1)).to(DEV)
+        kd = oracle.dequant_rows(Kq[b].index_select(0, toks).cpu().numpy(),
+                                 Ks[b].index_select(0, toks).cpu().numpy())
+        vd = oracle.dequant_rows(Vq[b].index_select(0, toks).cpu().numpy(),
+                                 Vs[b].index_select(0, toks).cpu().numpy())
+        o_ref, l_ref = oracle.attend_f64(bits(Q[b]), kd, vd, bits(G[b]), scale)
+        parity.check_attention(bits(out[b:b + 1]), o_ref[None], lse[b:b + 1].cpu().numpy(),
+                               l_ref[None])

@@ -119,6 +119,62 @@ def test_decode_1m_batch16():
     assert exact >= n - 1
 
 
+def test_decode_fp8_1m_batch16():
+    """FP8 decode at the full size: the 16 x 1M-token index and K/V caches stored as E4M3 rows
+    with fp32 scales; every sequence's selection and attention against the oracle on the
+    dequantised values."""
+    wl = WORKLOADS[3]
+    shape = wl.shape
+    n, L, B, k = wl.nseq, wl.L, shape.block_size, shape.topk_blocks
+    say("fp8 decode: generating 16 x 1M-token caches")
+    d = inputs.make_decode(wl, 3, DEV)
+    kb = torch.empty((n, wl.nblk, shape.proxy_dim), dtype=torch.bfloat16, device=DEV)
+    sgqa.index_build(shape, d["kp"], kb, [L] * n)
+    del d["kp"]
+    say("fp8 decode: quantising")
+    kbq = torch.empty(kb.shape, dtype=torch.uint8, device=DEV)
+    kbs = torch.empty(kb.shape[:2], dtype=torch.float32, device=DEV)
+    sgqa.quantize_fp8(kb, kbq, kbs)
+    Kq = torch.empty(d["K"].shape, dtype=torch.uint8, device=DEV)
+    Ks = torch.empty(d["K"].shape[:3], dtype=torch.float32, device=DEV)
+    sgqa.quantize_fp8(d["K"], Kq, Ks)
+    Vq = torch.empty(d["V"].shape, dtype=torch.uint8, device=DEV)
+    Vs = torch.empty(d["V"].shape[:3], dtype=torch.float32, device=DEV)
+    sgqa.quantize_fp8(d["V"], Vq, Vs)
+    idx = torch.empty((n, k), dtype=torch.int32, device=DEV)
+    sel = torch.empty((n, k), dtype=torch.float32, device=DEV)
+    say("fp8 decode: indexer + attention")
+    sgqa.indexer_topk_fp8(shape, d["qp"], kbq, kbs, [L - 1] * n, idx, sel)
+    out = torch.empty_like(d["Q"])
+    lse = torch.empty((n, shape.num_q_heads), dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(shape.head_dim)
+    sgqa.sparse_attn_decode_fp8(shape, d["Q"], Kq, Vq, Ks, Vs, d["G"], idx, [L] * n, scale, out,
+                                lse)
+    torch.cuda.synchronize()
+    t = np.array([L - 1])
+    c = (L - 1) // B
+    exact = 0
+    for b in range(n):
+        kb_deq = oracle.dequant_rows(kbq[b].cpu().numpy(), kbs[b].cpu().numpy())
+        sc = oracle.scores(bits(d["qp"][b:b + 1]), t, B, kb_deq, width=c)
+        ref = oracle.topk(sc, t, B, k)
+        got = idx[b].cpu().numpy()
+        exact += parity.check_selection(got, sc[0], c, k, ref[0])
+        parity.check_sel_scores(sel[b].cpu().numpy(), got, sc[0], c, k)
+        toks = torch.from_numpy(oracle.token_set(got, B, L - 1)).to(DEV)
+        kd = oracle.dequant_rows(Kq[b].index_select(0, toks).cpu().numpy(),
+                                 Ks[b].index_select(0, toks).cpu().numpy())
+        vd = oracle.dequant_rows(Vq[b].index_select(0, toks).cpu().numpy(),
+                                 Vs[b].index_select(0, toks).cpu().numpy())
+        o_ref, l_ref = oracle.attend_f64(bits(d["Q"][b]), kd, vd, bits(d["G"][b]), scale)
+        st = parity.check_attention(bits(out[b:b + 1]), o_ref[None], lse[b:b + 1].cpu().numpy(),
+                                    l_ref[None])
+        if b == 0:
+            say(f"fp8 decode: sequence 0 {st}")
+    assert exact >= n - 1
+    say("fp8 decode: all 16 sequences ok")
+
+
 def test_index_from_keys_128k():
     """Fused index maintenance at the real shape (width 4 x 192, proxy 256) over the whole
     128K prefill: every block against the oracle."""
