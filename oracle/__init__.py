@@ -57,6 +57,11 @@ def _bind(lib):
     lib.orc_attend.argtypes = [p, p, p, i64, p, i32, i32, i32, dbl, p, p]
     lib.orc_attend_f64.restype = None
     lib.orc_attend_f64.argtypes = [p, p, p, i64, p, i32, i32, i32, dbl, p, p]
+    lib.orc_attend_backward.restype = None
+    lib.orc_attend_backward.argtypes = [p, p, p, i64, p, p, i32, i32, i32, dbl, p, p, p, p]
+    lib.orc_sparse_attention_backward.restype = ctypes.c_int
+    lib.orc_sparse_attention_backward.argtypes = [p, p, i64, p, p, i64, p, p, i32, i32, i32, i32,
+                                                  i32, dbl, p, p, p, p, p]
     lib.orc_e4m3_decode.restype = dbl
     lib.orc_e4m3_decode.argtypes = [ctypes.c_uint8]
     lib.orc_e4m3_encode.restype = ctypes.c_uint8
@@ -291,6 +296,37 @@ def sparse_attention(q_bits, t, K_bits, V_bits, G_bits, idx, B: int, scale: floa
     if rc != 0:
         raise ValueError("a selected token lies outside the cache")
     return out, lse
+
+
+def sparse_attention_backward(q_bits, t, K_bits, V_bits, G_bits, idx, B: int, scale: float,
+                              gout_bits, lib=None):
+    """Backward of sparse_attention with the selection fixed, for the loss whose gradient
+    with respect to out is ``gout_bits`` [n, Hq, d] (bf16 bits).  Returns (dq [n, Hq, d],
+    dK [L, Hkv, d], dV [L, Hkv, d], dgate [n, Hq]), all float64; dK / dV sum over the rows."""
+    lib = lib or load()
+    q = _u16(q_bits)
+    K = _u16(K_bits)
+    V = _u16(V_bits)
+    G = _u16(G_bits)
+    go = _u16(gout_bits)
+    idx = np.ascontiguousarray(idx, dtype=np.int32)
+    t = np.ascontiguousarray(t, dtype=np.int64)
+    n, Hq, d = q.shape
+    L, Hkv, d2 = K.shape
+    if (d2 != d or V.shape != K.shape or G.shape != (n, Hq) or idx.shape[0] != n
+            or t.shape != (n,) or go.shape != q.shape):
+        raise ValueError("shape mismatch in sparse_attention_backward")
+    k = idx.shape[1]
+    dq = np.empty((n, Hq, d), dtype=np.float64)
+    dK = np.empty((L, Hkv, d), dtype=np.float64)
+    dV = np.empty((L, Hkv, d), dtype=np.float64)
+    dg = np.empty((n, Hq), dtype=np.float64)
+    rc = lib.orc_sparse_attention_backward(_ptr(q), _ptr(t), n, _ptr(K), _ptr(V), L, _ptr(G),
+                                           _ptr(idx), k, B, Hq, Hkv, d, float(scale), _ptr(go),
+                                           _ptr(dq), _ptr(dK), _ptr(dV), _ptr(dg))
+    if rc != 0:
+        raise ValueError("a selected token lies outside the cache")
+    return dq, dK, dV, dg
 
 
 def window_attention(q_bits, t, K_bits, V_bits, G_bits, window: int, scale: float, lib=None):

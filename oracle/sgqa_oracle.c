@@ -396,6 +396,149 @@ int orc_window_attention(const uint16_t *q, const int64_t *t, int64_t nrows, con
 }
 
 /*
+ * Backward of the gated sparse attention with the selection held fixed.  The
+ * pages say full attention is the bottleneck in training as well as in
+ * inference (ai.info "Sparse GQA targets million-token context"); they state no
+ * training recipe for the indexer, so the selection is an input here.  For one
+ * query, given g_out[h][:] = dL/dout[h][:] and the forward of orc_attend_f64
+ * (z_s = scale * q_h . k_s, P_s = softmax(z)_s, a_h = sum_s P_s v_s,
+ * out_h = sigmoid(G_h) a_h), the chain rule gives, for head h of group g:
+ *   dG_h   = (g_out_h . a_h) * sigmoid(G_h) * (1 - sigmoid(G_h))
+ *   da_h   = sigmoid(G_h) g_out_h
+ *   dP_s   = da_h . v_s,   dz_s = P_s (dP_s - sum_r P_r dP_r)
+ *   dq_h   = scale * sum_s dz_s k_s
+ *   dk_s  += scale * dz_s q_h,   dv_s += P_s da_h       (summed over the heads of g)
+ * The forward is recomputed here; dkrows / dvrows [n][Hkv][d] are accumulated
+ * into (the caller zeroes them), dq [Hq][d] and dgate [Hq] are written.
+ */
+void orc_attend_backward(const uint16_t *q, const uint16_t *krows, const uint16_t *vrows,
+                         int64_t n, const uint16_t *gate, const uint16_t *gout, int32_t Hq,
+                         int32_t Hkv, int32_t d, double scale, double *dq, double *dkrows,
+                         double *dvrows, double *dgate)
+{
+    const int32_t heads_per_group = Hq / Hkv;
+    double *P = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    double *dP = (double *)malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+    double *a = (double *)malloc((size_t)d * sizeof(double));
+    for (int32_t h = 0; h < Hq; ++h) {
+        const int32_t g = h / heads_per_group;
+        double m = -INFINITY;
+        for (int64_t s = 0; s < n; ++s) {
+            double dot = 0.0;
+            for (int32_t i = 0; i < d; ++i)
+                dot += widen_bf16(q[h * d + i]) * widen_bf16(krows[(s * Hkv + g) * d + i]);
+            P[s] = scale * dot;
+            if (P[s] > m)
+                m = P[s];
+        }
+        double Z = 0.0;
+        for (int64_t s = 0; s < n; ++s) {
+            P[s] = exp(P[s] - m);
+            Z += P[s];
+        }
+        for (int64_t s = 0; s < n; ++s)
+            P[s] /= Z;
+        for (int32_t i = 0; i < d; ++i) {
+            double acc = 0.0;
+            for (int64_t s = 0; s < n; ++s)
+                acc += P[s] * widen_bf16(vrows[(s * Hkv + g) * d + i]);
+            a[i] = acc;
+        }
+        const double sg = logistic(widen_bf16(gate[h]));
+        double go_a = 0.0;
+        for (int32_t i = 0; i < d; ++i)
+            go_a += widen_bf16(gout[h * d + i]) * a[i];
+        dgate[h] = go_a * sg * (1.0 - sg);
+        double Dsum = 0.0;
+        for (int64_t s = 0; s < n; ++s) {
+            double acc = 0.0;
+            for (int32_t i = 0; i < d; ++i)
+                acc += sg * widen_bf16(gout[h * d + i]) * widen_bf16(vrows[(s * Hkv + g) * d + i]);
+            dP[s] = acc;
+            Dsum += P[s] * acc;
+        }
+        for (int32_t i = 0; i < d; ++i)
+            dq[h * d + i] = 0.0;
+        for (int64_t s = 0; s < n; ++s) {
+            const double dz = P[s] * (dP[s] - Dsum);
+            for (int32_t i = 0; i < d; ++i) {
+                dq[h * d + i] += scale * dz * widen_bf16(krows[(s * Hkv + g) * d + i]);
+                dkrows[(s * Hkv + g) * d + i] += scale * dz * widen_bf16(q[h * d + i]);
+                dvrows[(s * Hkv + g) * d + i] += P[s] * sg * widen_bf16(gout[h * d + i]);
+            }
+        }
+    }
+    free(P);
+    free(dP);
+    free(a);
+}
+
+/*
+ * The backward for query rows at positions t over selections idx (as
+ * orc_sparse_attention): dq [nrows][Hq][d] and dgate [nrows][Hq] per row, and
+ * dK / dV [L][Hkv][d] summed over every row that attends to a token (zeroed
+ * here).  Rows run in parallel with private dK / dV sums added at the end.
+ */
+int orc_sparse_attention_backward(const uint16_t *q, const int64_t *t, int64_t nrows,
+                                  const uint16_t *K, const uint16_t *V, int64_t L,
+                                  const uint16_t *G, const int32_t *idx, int32_t k, int32_t B,
+                                  int32_t Hq, int32_t Hkv, int32_t d, double scale,
+                                  const uint16_t *gout, double *dq, double *dK, double *dV,
+                                  double *dgate)
+{
+    int bad = 0;
+    const int64_t row = (int64_t)Hkv * d;
+    memset(dK, 0, (size_t)L * row * sizeof(double));
+    memset(dV, 0, (size_t)L * row * sizeof(double));
+#pragma omp parallel reduction(| : bad)
+    {
+        double *pk = (double *)calloc((size_t)L * row, sizeof(double));
+        double *pv = (double *)calloc((size_t)L * row, sizeof(double));
+#pragma omp for schedule(dynamic, 1)
+        for (int64_t r = 0; r < nrows; ++r) {
+            int64_t *tok = (int64_t *)malloc((size_t)k * B * sizeof(int64_t));
+            const int64_t n = orc_token_set(idx + r * (int64_t)k, k, B, t[r], tok);
+            const size_t cnt = (size_t)(n > 0 ? n : 1) * row;
+            uint16_t *kr = (uint16_t *)malloc(cnt * sizeof(uint16_t));
+            uint16_t *vr = (uint16_t *)malloc(cnt * sizeof(uint16_t));
+            double *dkr = (double *)calloc(cnt, sizeof(double));
+            double *dvr = (double *)calloc(cnt, sizeof(double));
+            for (int64_t i = 0; i < n; ++i) {
+                if (tok[i] < 0 || tok[i] >= L) {
+                    bad = 1;
+                    tok[i] = 0;
+                }
+                memcpy(kr + i * row, K + tok[i] * row, (size_t)row * sizeof(uint16_t));
+                memcpy(vr + i * row, V + tok[i] * row, (size_t)row * sizeof(uint16_t));
+            }
+            orc_attend_backward(q + r * (int64_t)Hq * d, kr, vr, n, G + r * (int64_t)Hq,
+                                gout + r * (int64_t)Hq * d, Hq, Hkv, d, scale,
+                                dq + r * (int64_t)Hq * d, dkr, dvr, dgate + r * (int64_t)Hq);
+            for (int64_t i = 0; i < n; ++i)
+                for (int64_t e = 0; e < row; ++e) {
+                    pk[tok[i] * row + e] += dkr[i * row + e];
+                    pv[tok[i] * row + e] += dvr[i * row + e];
+                }
+            free(kr);
+            free(vr);
+            free(dkr);
+            free(dvr);
+            free(tok);
+        }
+#pragma omp critical
+        {
+            for (int64_t e = 0; e < L * row; ++e) {
+                dK[e] += pk[e];
+                dV[e] += pv[e];
+            }
+        }
+        free(pk);
+        free(pv);
+    }
+    return bad ? -1 : 0;
+}
+
+/*
  * FP8 storage of cached rows (decode path).  The pages give FP8 only for the
  * released checkpoint: e4m3 with scaling blocks of 128 (phantomic12 entry,
  * "quant_method fp8, e4m3, block size 128"; ai4snews "Open Weights" para. on

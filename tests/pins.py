@@ -392,6 +392,55 @@ def pin_window_token_count(lib):
         assert toks[n - 1] == t_ and toks[0] == t_ - n + 1
 
 
+# --------------------------------------------------------------------------- backward
+def _autograd_reference(p, mask: np.ndarray, scale: float, gout: np.ndarray):
+    """Library gradients: torch autograd through fp64 SDPA (KV heads repeated, block mask)
+    times sigmoid(gate), for the loss sum(out * gout)."""
+    Q = torch.from_numpy(widen(p["Q"])).requires_grad_(True)
+    K = torch.from_numpy(widen(p["K"])).requires_grad_(True)
+    V = torch.from_numpy(widen(p["V"])).requires_grad_(True)
+    G = torch.from_numpy(widen(p["G"])).requires_grad_(True)
+    rep = Q.shape[1] // K.shape[1]
+    q = Q.permute(1, 0, 2)
+    k = K.permute(1, 0, 2).repeat_interleave(rep, dim=0)
+    v = V.permute(1, 0, 2).repeat_interleave(rep, dim=0)
+    o = torch.nn.functional.scaled_dot_product_attention(q, k, v, attn_mask=torch.from_numpy(mask),
+                                                         scale=scale)
+    out = o.permute(1, 0, 2) * torch.sigmoid(G)[:, :, None]
+    (out * torch.from_numpy(gout)).sum().backward()
+    return Q.grad.numpy(), K.grad.numpy(), V.grad.numpy(), G.grad.numpy()
+
+
+def pin_backward_autograd(lib):
+    """The fixed-selection backward equals torch autograd through SDPA (fp64) under the mask
+    built from the selected blocks, for a sparse (k = 4) and a dense selection; and the sums
+    over key rows obey sum_s dV[s][g] = sum_t sum_{h in g} sigmoid(G) gout and
+    sum_s dK[s][g] = 0 (the dz of each (t, h) sum to zero)."""
+    p = small_problem(seed=12)
+    L, Hkv, d = p["K"].shape
+    Hq = p["Q"].shape[1]
+    rng = np.random.default_rng(13)
+    gout = bf16_bits(rng.standard_normal((L, Hq, d)))
+    scale = 1 / math.sqrt(d)
+    t = np.arange(L, dtype=np.int64)
+    for B, k in ((8, 4), (8, 64)):
+        kb = oracle.index_build(p["kp"], B, lib=lib)
+        sc = oracle.scores(p["qp"], t, B, kb, width=max(1, (L - 1) // B), lib=lib)
+        idx = oracle.topk(sc, t, B, k, lib=lib)
+        mask = np.zeros((L, L), dtype=bool)
+        for r in range(L):
+            mask[r, oracle.token_set(idx[r], B, r, lib=lib)] = True
+        dq, dK, dV, dg = oracle.sparse_attention_backward(p["Q"], t, p["K"], p["V"], p["G"], idx,
+                                                          B, scale, gout, lib=lib)
+        rq, rK, rV, rg = _autograd_reference(p, mask, scale, widen(gout))
+        for ours, ref in ((dq, rq), (dK, rK), (dV, rV), (dg, rg)):
+            assert np.allclose(ours, ref, rtol=1e-9, atol=1e-11), np.abs(ours - ref).max()
+        sg = 1 / (1 + np.exp(-widen(p["G"])))
+        want_v = (sg[:, :, None] * widen(gout)).reshape(L, Hkv, Hq // Hkv, d).sum(axis=(0, 2))
+        assert np.allclose(dV.sum(axis=0), want_v, rtol=1e-10, atol=1e-10)
+        assert np.allclose(dK.sum(axis=0), 0.0, atol=1e-10)
+
+
 # --------------------------------------------------------------------------- FP8 storage
 def _torch_e4m3_bits(values) -> np.ndarray:
     """Library cast: torch float32 -> float8_e4m3fn (round to nearest even), as codes."""
@@ -473,6 +522,7 @@ def pin_attend_f64_sdpa(lib):
 
 
 ALL_PINS = [
+    pin_backward_autograd,
     pin_e4m3_decode_library,
     pin_e4m3_encode_library,
     pin_quantize_rows_error_bound,

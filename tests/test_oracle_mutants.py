@@ -34,10 +34,20 @@ MUTANTS = [
     ("small-case-drops-own", "for (int64_t j = 0; j <= c; ++j)", "for (int64_t j = 0; j < c; ++j)"),
     ("causal-excludes-self", "if (s <= t)", "if (s < t)"),
     ("scale-dropped", "z[s] = scale * dot;", "z[s] = dot;"),
-    ("group-map-interleaved", "const int32_t g = h / heads_per_group;",
-     "const int32_t g = h % Hkv;"),
+    ("group-map-interleaved",
+     "const int32_t g = h / heads_per_group;\n        double m = -INFINITY;\n        for (int64_t s = 0; s < n; ++s) {\n            double dot = 0.0;\n            for (int32_t i = 0; i < d; ++i)\n                dot += widen_bf16(q[h * d + i]) * krows[",
+     "const int32_t g = h % Hkv;\n        double m = -INFINITY;\n        for (int64_t s = 0; s < n; ++s) {\n            double dot = 0.0;\n            for (int32_t i = 0; i < d; ++i)\n                dot += widen_bf16(q[h * d + i]) * krows["),
+    ("backward-group-map-interleaved",
+     "const int32_t g = h / heads_per_group;\n        double m = -INFINITY;\n        for (int64_t s = 0; s < n; ++s) {\n            double dot = 0.0;\n            for (int32_t i = 0; i < d; ++i)\n                dot += widen_bf16(q[h * d + i]) * widen_bf16(krows[",
+     "const int32_t g = h % Hkv;\n        double m = -INFINITY;\n        for (int64_t s = 0; s < n; ++s) {\n            double dot = 0.0;\n            for (int32_t i = 0; i < d; ++i)\n                dot += widen_bf16(q[h * d + i]) * widen_bf16(krows["),
     ("key-is-value", "widen_bf16(q[h * d + i]) * krows[(s * Hkv + g) * d + i]",
      "widen_bf16(q[h * d + i]) * vrows[(s * Hkv + g) * d + i]"),
+    ("backward-drops-D", "const double dz = P[s] * (dP[s] - Dsum);", "const double dz = P[s] * dP[s];"),
+    ("backward-gate-derivative", "dgate[h] = go_a * sg * (1.0 - sg);", "dgate[h] = go_a * sg;"),
+    ("backward-dv-ungated", "dvrows[(s * Hkv + g) * d + i] += P[s] * sg * widen_bf16(gout[h * d + i]);",
+     "dvrows[(s * Hkv + g) * d + i] += P[s] * widen_bf16(gout[h * d + i]);"),
+    ("backward-dq-unscaled", "dq[h * d + i] += scale * dz * widen_bf16(krows[(s * Hkv + g) * d + i]);",
+     "dq[h * d + i] += dz * widen_bf16(krows[(s * Hkv + g) * d + i]);"),
     ("e4m3-bias-off-by-one", "ldexp(1.0 + m / 8.0, e - 7)", "ldexp(1.0 + m / 8.0, e - 8)"),
     ("e4m3-truncates", "const double r = nearbyint(ldexp(a, 3 - E));", "const double r = floor(ldexp(a, 3 - E));"),
     ("e4m3-subnormal-edge", "if (a == 0.0 || E < -6)\n        E = -6;", "if (a == 0.0 || E < -7)\n        E = -7;"),
