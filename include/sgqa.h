@@ -71,7 +71,8 @@ typedef struct {
 } sgqa_dims;
 
 /* Operation ids for sgqa_workspace_bytes. */
-enum { SGQA_OP_INDEXER_TOPK = 1, SGQA_OP_ATTN_DECODE = 2, SGQA_OP_ATTN_PREFILL = 3 };
+enum { SGQA_OP_INDEXER_TOPK = 1, SGQA_OP_ATTN_DECODE = 2, SGQA_OP_ATTN_PREFILL = 3,
+       SGQA_OP_ATTN_BACKWARD = 4 };
 
 /*
  * Block compression (ai4snews Interpretation para. 2; ai.info "Sparse GQA
@@ -211,6 +212,35 @@ sgqa_status sgqa_swa_prefill(const sgqa_dims *dims, const sgqa_bf16 *q, const sg
                              const sgqa_bf16 *v_cache, const sgqa_bf16 *gate, int64_t q_start,
                              int32_t T, int64_t L, int64_t window, float softmax_scale,
                              sgqa_bf16 *out, float *lse, void *stream);
+
+/*
+ * Backward of sgqa_sparse_attn_prefill with the selection held fixed (the pages
+ * count training at long context among the costs of full attention, ai.info
+ * "Sparse GQA targets million-token context"; how the indexer itself is trained
+ * is not stated, so idx is an input).  For the loss whose gradient with respect
+ * to out is dout, with P_s = exp(z_s - lse) the forward's weights and
+ * a = out / sigmoid(gate):
+ *   D      = dout . out                    per (row, head)
+ *   dgate  = D * (1 - sigmoid(gate))
+ *   dz_s   = P_s * (sigmoid(gate) dout . v_s - D)
+ *   dq     = softmax_scale * sum_s dz_s k_s
+ *   dk_s   = softmax_scale * sum over (row, head of the group) of dz_s q
+ *   dv_s   = sum over (row, head of the group) of P_s sigmoid(gate) dout
+ * The forward's out and lse are inputs.  dk and dv are written for every token
+ * of [0, L) (zero where no row attends); every sum runs in a fixed order, so the
+ * results are deterministic.  Layouts as sgqa_sparse_attn_prefill; dq
+ * [T][Hq][d], dk / dv [L][Hkv][d] and dgate [T][Hq] are fp32.  nseq is 1.
+ *   workspace [dev] >= sgqa_workspace_bytes(SGQA_OP_ATTN_BACKWARD, dims, 1, T, L),
+ *                   256-byte aligned
+ */
+sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
+                                      const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
+                                      const sgqa_bf16 *gate, const int32_t *idx, int64_t q_start,
+                                      int32_t T, int64_t L, float softmax_scale,
+                                      const sgqa_bf16 *out, const float *lse,
+                                      const sgqa_bf16 *dout, float *dq, float *dk, float *dv,
+                                      float *dgate, void *workspace, size_t workspace_bytes,
+                                      void *stream);
 
 /*
  * FP8 storage for the decode path.  The pages give FP8 (e4m3) only for the

@@ -386,8 +386,8 @@ __device__ __forceinline__ void load_state(WaveState<D> &st, const float *p)
 
 // Row and group of this wave under the two workgroup mappings (see k_attn_prefill).
 // Returns false for waves past the last row.
-template <bool kGroupPerXcd>
-__device__ __forceinline__ bool wave_row_group(const AttnArgs &a, int64_t &r, int &g)
+template <bool kGroupPerXcd, typename Args>
+__device__ __forceinline__ bool wave_row_group(const Args &a, int64_t &r, int &g)
 {
     const int wave = threadIdx.x >> 6;
     if constexpr (kGroupPerXcd) {
@@ -717,6 +717,397 @@ hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream)
     case 64: return launch_decode_d<64>(a, stream);
     case 128: return launch_decode_d<128>(a, stream);
     case 192: return launch_decode_d<192>(a, stream);
+    default: return hipErrorInvalidValue;
+    }
+}
+
+// ============================================================================ backward
+// Backward of the gated sparse attention with the selection fixed (the pages name training
+// at long context among the costs of full attention; ai.info "Sparse GQA targets
+// million-token context").  With P_s = exp(z_s - lse) the forward's probabilities,
+// a = sum_s P_s v_s, out = sigmoid(G) a and g_out = dL/dout:
+//   D = g_out . out (= da . a),  dG = D (1 - sigmoid(G)),  da = sigmoid(G) g_out,
+//   dP_s = da . v_s,  dz_s = P_s (dP_s - D),
+//   dq = scale sum_s dz_s k_s,  dk_s = scale sum_(t,h) dz_s q,  dv_s = sum_(t,h) P_s da.
+// Four launches: k_bwd_prep (D, dG, da), a zero fill and k_bwd_bitmap (for every key block
+// the set of query rows that selected it, one bit per row, by atomicOr, whose result does not
+// depend on order), k_bwd_dq (query-major, the forward's wave with a second product
+// dP^T = V da^T and K staged for dq^T += K^T dz^T), and k_bwd_dkdv (key-major: a workgroup per
+// 16-token tile of a block, a wave per KV group, walking the tile's query rows in ascending
+// order, so dK and dV are sums in a fixed order and written once).
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+__device__ __forceinline__ f32x4 mfma_16x16x16(s16x4 a, s16x4 b, f32x4 c)
+{
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ s16x4 pack4_bf16(float x0, float x1, float x2, float x3)
+{
+    const uint64_t w = (uint64_t)pack_bf16x2(x0, x1) | ((uint64_t)pack_bf16x2(x2, x3) << 32);
+    return __builtin_bit_cast(s16x4, w);
+}
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+// One wave per (row, head): D, dG and da = sigmoid(G) g_out (bf16).
+__global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a)
+{
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (int64_t)a.rows * a.Hq)
+        return;
+    const int lane = threadIdx.x & 63;
+    const int d = a.d;
+    const uint16_t *go = a.dout + row * d;
+    const uint16_t *o = a.out + row * d;
+    const float sg = sigmoid_f32(bf16_bits_to_f32(a.gate[row]));
+    float dot = 0.f;
+    for (int e = lane; e < d; e += 64) {
+        const float g = bf16_bits_to_f32(go[e]);
+        dot += g * bf16_bits_to_f32(o[e]);
+        a.da[row * d + e] = (uint16_t)f32_to_bf16_bits(sg * g);
+    }
+#pragma unroll
+    for (int off = 32; off > 0; off >>= 1)
+        dot += __shfl_xor(dot, off);
+    if (lane == 0) {
+        a.dsum[row] = dot;
+        a.dgate[row] = dot * (1.0f - sg);
+    }
+}
+
+__global__ __launch_bounds__(256) void k_bwd_zero(uint32_t *p, int64_t n)
+{
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256)
+        p[i] = 0u;
+}
+
+// One thread per selection entry: set bit r of block j's row.
+__global__ __launch_bounds__(256) void k_bwd_bitmap(BwdArgs a)
+{
+    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    if (gid >= (int64_t)a.rows * a.k)
+        return;
+    const int64_t r = gid / a.k;
+    const int32_t j = a.idx[gid];
+    const int64_t c = (a.q_start + r) / a.B;
+    if (j < 0 || (int64_t)j > c || (int64_t)j >= a.nblk)
+        return;
+    atomicOr(&a.bits[(int64_t)j * a.bits_ld + (r >> 5)], 1u << (r & 31));
+}
+
+// dq of one wave's (row, group) over its selected tokens; acc = dq^T (unscaled).
+template <int D>
+__device__ __forceinline__ void dq_range(const uint16_t *__restrict__ Kg,
+                                         const uint16_t *__restrict__ Vg, int Hkv,
+                                         const SparseTokens &src, const bf16x8 (&qf)[D / 32],
+                                         const bf16x8 (&daf)[D / 32], float scale_log2,
+                                         float lse2, float dsum, uint16_t *ks,
+                                         f32x4 (&acc)[D / 16])
+{
+    constexpr int kLd = D + 4;
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    const int64_t row_elems = (int64_t)Hkv * D;
+    const int nsteps = src.steps();
+    for (int step = 0; step < nsteps; ++step) {
+        int64_t s_ld;
+        bool valid;
+        src.slot(step, lane & 31, s_ld, valid);
+        const uint64_t vmask = __ballot(valid);
+        const int s_lo = (int)(s_ld & 0xffffffff), s_hi = (int)(s_ld >> 32);
+        u32x4 kv[2][D / 32], vv[2][D / 32];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int sl = h * 16 + col;
+            const int64_t sk = ((int64_t)(uint32_t)__shfl(s_lo, sl)) |
+                               ((int64_t)__shfl(s_hi, sl) << 32);
+            const uint16_t *kr = Kg + sk * row_elems + q4 * 8;
+            const uint16_t *vr = Vg + sk * row_elems + q4 * 8;
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                kv[h][kk] = load16(kr + kk * 32);
+                vv[h][kk] = load16(vr + kk * 32);
+            }
+        }
+        // S^T = K Q^T and dP^T = V dA^T; lane holds slots 16h + 4 q4 + r of head col
+        f32x4 sc[2], dp[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+            dp[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                sc[h] = mfma_16x16x32(as_bf16x8(kv[h][kk]), qf[kk], sc[h]);
+                dp[h] = mfma_16x16x32(as_bf16x8(vv[h][kk]), daf[kk], dp[h]);
+            }
+        }
+        float dz[2][4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int slot = h * 16 + q4 * 4 + r;
+                const bool ok = (vmask >> slot) & 1ull;
+                const float p = ok ? fast_exp2(sc[h][r] * scale_log2 - lse2) : 0.f;
+                dz[h][r] = p * (dp[h][r] - dsum);
+            }
+        u32x4 zw;
+        zw[0] = pack_bf16x2(dz[0][0], dz[0][1]);
+        zw[1] = pack_bf16x2(dz[0][2], dz[0][3]);
+        zw[2] = pack_bf16x2(dz[1][0], dz[1][1]);
+        zw[3] = pack_bf16x2(dz[1][2], dz[1][3]);
+        const bf16x8 zf = as_bf16x8(zw);
+
+        // stage the K rows in LDS [slot][d] and read them transposed
+        wave_lds_handoff();
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                uint2 *dst = reinterpret_cast<uint2 *>(ks + (h * 16 + col) * kLd + kk * 32 + q4 * 8);
+                dst[0] = uint2{kv[h][kk][0], kv[h][kk][1]};
+                dst[1] = uint2{kv[h][kk][2], kv[h][kk][3]};
+            }
+        wave_lds_handoff();
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) {
+            const uint16_t *kc = ks + mt * 16 + col;
+            u32x4 aw;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const int j0 = 2 * jj, j1 = 2 * jj + 1;
+                const int sl0 = j0 < 4 ? q4 * 4 + j0 : 16 + q4 * 4 + (j0 - 4);
+                const int sl1 = j1 < 4 ? q4 * 4 + j1 : 16 + q4 * 4 + (j1 - 4);
+                aw[jj] = (uint32_t)kc[sl0 * kLd] | ((uint32_t)kc[sl1 * kLd] << 16);
+            }
+            acc[mt] = mfma_16x16x32(as_bf16x8(aw), zf, acc[mt]);
+        }
+    }
+}
+
+template <int D, bool kGroupPerXcd>
+__global__ __launch_bounds__(512) void k_bwd_dq(BwdArgs a)
+{
+    extern __shared__ __align__(16) uint16_t lds[];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    const int hpg = a.Hq / a.Hkv;
+    int64_t r;
+    int g;
+    if (!wave_row_group<kGroupPerXcd>(a, r, g))
+        return;
+    const int64_t t = a.q_start + r;
+    const int64_t c = t / a.B;
+    const int nvalid = (int)((c + 1 < a.k) ? c + 1 : a.k);
+    const int64_t head0 = r * a.Hq + (int64_t)g * hpg;
+    bf16x8 qf[D / 32], daf[D / 32];
+    load_q<D>(a.q + head0 * D, hpg, qf);
+    load_q<D>(a.da + head0 * D, hpg, daf);
+    const float lse2 = col < hpg ? a.lse[head0 + col] * kLog2e : 0.f;
+    const float dsum = col < hpg ? a.dsum[head0 + col] : 0.f;
+    f32x4 acc[D / 16];
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt)
+        acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const SparseTokens src{a.idx + r * a.k, 0, nvalid, t, c, a.B};
+    dq_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D, a.Hkv, src, qf, daf, a.scale_log2,
+                lse2, dsum, lds + wave * kSlots * (D + 4), acc);
+    if (col < hpg) {
+        float *dst = a.dq + (head0 + col) * D + q4 * 4;
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt)
+            *reinterpret_cast<f32x4 *>(dst + mt * 16) = acc[mt] * a.scale;
+    }
+}
+
+// dK and dV of one 16-token tile of key block j for KV group g (one wave), over the query
+// rows whose selection holds j, in ascending order.  Per row: S = q K^T and dP = dA V^T with
+// M = heads, so each lane holds heads 4 q4 + i of token col - exactly the A operand of the
+// 16x16x16 products dV += P^T dA and dK += dz^T q (M = tokens, K = heads); q and dA are
+// staged in LDS for the B operands.
+template <int D>
+__global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
+{
+    extern __shared__ __align__(16) uint16_t lds[];
+    constexpr int kLd = D + 8;
+    const int ntile = (a.B + 15) / 16;
+    const int64_t j = blockIdx.x / ntile;
+    const int tile = blockIdx.x - (int)(j * ntile);
+    const int g = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    const int hpg = a.Hq / a.Hkv;
+    const int64_t s0 = j * a.B + (int64_t)tile * 16;  // first token of the tile
+    int64_t ntok = a.B - tile * 16;
+    ntok = ntok < 16 ? ntok : 16;
+    ntok = a.L - s0 < ntok ? a.L - s0 : ntok;
+    if (ntok <= 0)
+        return;  // a tile past the end of a short last block
+    uint16_t *qs = lds + g * 2 * 16 * kLd;
+    uint16_t *ds = qs + 16 * kLd;
+    const int64_t row_elems = (int64_t)a.Hkv * D;
+
+    // K and V of the tile's tokens as B operands (token col; padding lanes repeat token s0)
+    const int64_t sc_tok = col < ntok ? s0 + col : s0;
+    bf16x8 kB[D / 32], vB[D / 32];
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        kB[kk] = as_bf16x8(load16(a.kc + sc_tok * row_elems + (int64_t)g * D + kk * 32 + q4 * 8));
+        vB[kk] = as_bf16x8(load16(a.vc + sc_tok * row_elems + (int64_t)g * D + kk * 32 + q4 * 8));
+    }
+    f32x4 dk[D / 16], dv[D / 16];
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) {
+        dk[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        dv[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    const uint32_t *brow = a.bits + j * a.bits_ld;
+    const int64_t nw = ((int64_t)a.rows + 31) >> 5;
+    const int64_t first_row = j * a.B - a.q_start;  // no row before it can select block j
+    const int64_t w0 = first_row > 0 ? first_row >> 5 : 0;
+#pragma unroll 1
+    for (int64_t w = w0; w < nw; ++w) {
+        uint32_t word = brow[w];
+#pragma unroll 1
+        while (word) {
+            const int64_t r = (w << 5) + __builtin_ctz(word);
+            word &= word - 1;
+            const int64_t t = a.q_start + r;
+            const int64_t head0 = r * a.Hq + (int64_t)g * hpg;
+            // q and dA of the group's heads (head col, dims 8 q4 + 32 kk ..) as A operands
+            u32x4 qa[D / 32], da[D / 32];
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                qa[kk] = u32x4{0u, 0u, 0u, 0u};
+                da[kk] = u32x4{0u, 0u, 0u, 0u};
+                if (col < hpg) {
+                    qa[kk] = load16(a.q + (head0 + col) * D + kk * 32 + q4 * 8);
+                    da[kk] = load16(a.da + (head0 + col) * D + kk * 32 + q4 * 8);
+                }
+            }
+            float lse2[4], dsum[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int h = q4 * 4 + i;
+                lse2[i] = h < hpg ? a.lse[head0 + h] * kLog2e : 0.f;
+                dsum[i] = h < hpg ? a.dsum[head0 + h] : 0.f;
+            }
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                sc = mfma_16x16x32(as_bf16x8(qa[kk]), kB[kk], sc);
+                dp = mfma_16x16x32(as_bf16x8(da[kk]), vB[kk], dp);
+            }
+            // lane holds heads 4 q4 + i of token col
+            float p[4], dz[4];
+            const bool tok_ok = col < ntok && s0 + col <= t;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = tok_ok && q4 * 4 + i < hpg;
+                p[i] = ok ? fast_exp2(sc[i] * a.scale_log2 - lse2[i]) : 0.f;
+                dz[i] = p[i] * (dp[i] - dsum[i]) * a.scale;
+            }
+            const s16x4 pa = pack4_bf16(p[0], p[1], p[2], p[3]);
+            const s16x4 za = pack4_bf16(dz[0], dz[1], dz[2], dz[3]);
+
+            wave_lds_handoff();
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                uint2 *dq_ = reinterpret_cast<uint2 *>(qs + col * kLd + kk * 32 + q4 * 8);
+                uint2 *dd_ = reinterpret_cast<uint2 *>(ds + col * kLd + kk * 32 + q4 * 8);
+                dq_[0] = uint2{qa[kk][0], qa[kk][1]};
+                dq_[1] = uint2{qa[kk][2], qa[kk][3]};
+                dd_[0] = uint2{da[kk][0], da[kk][1]};
+                dd_[1] = uint2{da[kk][2], da[kk][3]};
+            }
+            wave_lds_handoff();
+#pragma unroll
+            for (int nt = 0; nt < D / 16; ++nt) {
+                const int dcol = nt * 16 + col;
+                const uint16_t *qc = qs + (q4 * 4) * kLd + dcol;
+                const uint16_t *dc = ds + (q4 * 4) * kLd + dcol;
+                const uint64_t qw = (uint64_t)qc[0] | ((uint64_t)qc[kLd] << 16) |
+                                    ((uint64_t)qc[2 * kLd] << 32) | ((uint64_t)qc[3 * kLd] << 48);
+                const uint64_t dw = (uint64_t)dc[0] | ((uint64_t)dc[kLd] << 16) |
+                                    ((uint64_t)dc[2 * kLd] << 32) | ((uint64_t)dc[3 * kLd] << 48);
+                dv[nt] = mfma_16x16x16(pa, __builtin_bit_cast(s16x4, dw), dv[nt]);
+                dk[nt] = mfma_16x16x16(za, __builtin_bit_cast(s16x4, qw), dk[nt]);
+            }
+        }
+    }
+    // lane holds dK / dV of token 4 q4 + i, dim 16 nt + col
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = q4 * 4 + i;
+        if (tok < ntok) {
+            const int64_t base = ((s0 + tok) * a.Hkv + g) * D;
+#pragma unroll
+            for (int nt = 0; nt < D / 16; ++nt) {
+                a.dk[base + nt * 16 + col] = dk[nt][i];
+                a.dv[base + nt * 16 + col] = dv[nt][i];
+            }
+        }
+    }
+}
+
+size_t attn_backward_workspace(int64_t T, int Hq, int d, int64_t nblk)
+{
+    const int64_t bits_ld = (((T + 31) / 32) + 3) / 4 * 4;
+    const size_t da = ((size_t)T * Hq * d * 2 + 255) / 256 * 256;
+    const size_t ds = ((size_t)T * Hq * 4 + 255) / 256 * 256;
+    return da + ds + (size_t)nblk * bits_ld * 4;
+}
+
+template <int D>
+static hipError_t launch_backward_d(const BwdArgs &a, hipStream_t stream)
+{
+    // dq: the forward's launch shape
+    if (8 % a.Hkv == 0) {
+        const int R = 8 / a.Hkv;
+        const int64_t ntiles = ((int64_t)a.rows + 3) / 4;
+        const int64_t nwg = (ntiles + R - 1) / R * 8;
+        const size_t lds = (size_t)4 * kSlots * (D + 4) * sizeof(uint16_t);
+        hipLaunchKernelGGL((k_bwd_dq<D, true>), dim3((unsigned)nwg), dim3(256), lds, stream, a);
+    } else {
+        const size_t lds = (size_t)a.Hkv * kSlots * (D + 4) * sizeof(uint16_t);
+        hipLaunchKernelGGL((k_bwd_dq<D, false>), dim3((unsigned)a.rows), dim3(64 * a.Hkv), lds,
+                           stream, a);
+    }
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int ntile = (a.B + 15) / 16;
+    const size_t lds = (size_t)a.Hkv * 2 * 16 * (D + 8) * sizeof(uint16_t);
+    hipLaunchKernelGGL(k_bwd_dkdv<D>, dim3((unsigned)(a.nblk * ntile)), dim3(64 * a.Hkv), lds,
+                       stream, a);
+    return hipGetLastError();
+}
+
+hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t stream)
+{
+    if (a.rows <= 0)
+        return hipSuccess;
+    const int64_t nrow = (int64_t)a.rows * a.Hq;
+    hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)((nrow + 3) / 4)), dim3(256), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t words = a.nblk * a.bits_ld;
+    hipLaunchKernelGGL(k_bwd_zero, dim3((unsigned)(words < 65536 * 256 ? (words + 255) / 256 : 65536)),
+                       dim3(256), 0, stream, a.bits, words);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t ent = (int64_t)a.rows * a.k;
+    hipLaunchKernelGGL(k_bwd_bitmap, dim3((unsigned)((ent + 255) / 256)), dim3(256), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    switch (a.d) {
+    case 64: return launch_backward_d<64>(a, stream);
+    case 128: return launch_backward_d<128>(a, stream);
+    case 192: return launch_backward_d<192>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }

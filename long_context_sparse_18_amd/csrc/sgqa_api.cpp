@@ -183,6 +183,12 @@ size_t sgqa_workspace_bytes(int op, const sgqa_dims *dims, int32_t nseq, int32_t
         return (size_t)rows * dims->num_kv_heads * 64 * sgqa::prefill_state_stride(dims->head_dim) *
                sizeof(float);
     }
+    if (op == SGQA_OP_ATTN_BACKWARD) {
+        if (check_dims(dims, true, false) != SGQA_OK || nseq != 1)
+            return 0;
+        return sgqa::attn_backward_workspace(T, dims->num_q_heads, dims->head_dim,
+                                             ceil_div(Lmax, dims->block_size));
+    }
     if (op == SGQA_OP_ATTN_DECODE) {
         if (check_dims(dims, true, false) != SGQA_OK)
             return 0;
@@ -739,4 +745,75 @@ sgqa_status sgqa_sparse_attn_decode_fp8(const sgqa_dims *dims, const sgqa_bf16 *
     a.part_ml = a.part_o + slots * a.d;
     return hip_status(sgqa::launch_attn_decode(a, reinterpret_cast<hipStream_t>(stream)),
                       "FP8 sparse_attn_decode launch");
+}
+
+// ------------------------------------------------------------------------------ backward
+sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
+                                      const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
+                                      const sgqa_bf16 *gate, const int32_t *idx, int64_t q_start,
+                                      int32_t T, int64_t L, float softmax_scale,
+                                      const sgqa_bf16 *out, const float *lse,
+                                      const sgqa_bf16 *dout, float *dq, float *dk, float *dv,
+                                      float *dgate, void *workspace, size_t workspace_bytes,
+                                      void *stream)
+{
+    sgqa_status st = check_dims(dims, true, false);
+    if (st != SGQA_OK)
+        return st;
+    if (T < 0 || q_start < 0 || L < 0)
+        return fail(SGQA_ERR_SHAPE, "T %d, q_start %lld and L %lld must be non-negative", T,
+                    (long long)q_start, (long long)L);
+    if (q_start + T > L)
+        return fail(SGQA_ERR_SHAPE, "queries [q_start, q_start+T) must lie inside the cache of %lld",
+                    (long long)L);
+    if (!std::isfinite(softmax_scale))
+        return fail(SGQA_ERR_SHAPE, "softmax_scale must be finite");
+    if (T == 0 || L == 0)
+        return ok();
+    if (!q || !k_cache || !v_cache || !gate || !idx || !out || !lse || !dout || !dq || !dk ||
+        !dv || !dgate)
+        return fail(SGQA_ERR_NULL, "every tensor argument must be non-NULL");
+    if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(dq, 16) ||
+        !aligned(out, 2) || !aligned(dout, 2) || !aligned(gate, 2) || !aligned(idx, 4) ||
+        !aligned(lse, 4) || !aligned(dk, 4) || !aligned(dv, 4) || !aligned(dgate, 4))
+        return fail(SGQA_ERR_SHAPE, "q, caches and dq must be 16-byte aligned");
+    const size_t need = sgqa_workspace_bytes(SGQA_OP_ATTN_BACKWARD, dims, 1, T, L);
+    if (!workspace || workspace_bytes < need)
+        return fail(SGQA_ERR_WORKSPACE, "backward workspace needs %zu bytes, got %zu", need,
+                    workspace ? workspace_bytes : (size_t)0);
+    if (!aligned(workspace, 256))
+        return fail(SGQA_ERR_SHAPE, "workspace must be 256-byte aligned");
+    sgqa::BwdArgs a{};
+    a.q = q;
+    a.kc = k_cache;
+    a.vc = v_cache;
+    a.gate = gate;
+    a.out = out;
+    a.dout = dout;
+    a.lse = lse;
+    a.idx = idx;
+    a.q_start = q_start;
+    a.rows = T;
+    a.L = L;
+    a.Hq = dims->num_q_heads;
+    a.Hkv = dims->num_kv_heads;
+    a.d = dims->head_dim;
+    a.B = dims->block_size;
+    a.k = dims->topk_blocks;
+    a.scale = softmax_scale;
+    a.scale_log2 = softmax_scale * 1.4426950408889634f;
+    a.dq = dq;
+    a.dk = dk;
+    a.dv = dv;
+    a.dgate = dgate;
+    a.nblk = ceil_div(L, dims->block_size);
+    a.bits_ld = ((((int64_t)T + 31) / 32) + 3) / 4 * 4;
+    char *w = static_cast<char *>(workspace);
+    const size_t da_bytes = ((size_t)T * a.Hq * a.d * 2 + 255) / 256 * 256;
+    const size_t ds_bytes = ((size_t)T * a.Hq * 4 + 255) / 256 * 256;
+    a.da = reinterpret_cast<uint16_t *>(w);
+    a.dsum = reinterpret_cast<float *>(w + da_bytes);
+    a.bits = reinterpret_cast<uint32_t *>(w + da_bytes + ds_bytes);
+    return hip_status(sgqa::launch_attn_backward(a, reinterpret_cast<hipStream_t>(stream)),
+                      "sparse_attn_backward launch");
 }

@@ -142,6 +142,27 @@ struct AttnArgs {
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream);
 hipError_t launch_swa(const AttnArgs &a, hipStream_t stream);
+
+// Backward of the sparse attention with the selection fixed (prefill layout: T query rows at
+// q_start .. q_start+T-1 over an L-token cache).
+struct BwdArgs {
+    const uint16_t *q, *kc, *vc, *gate, *out, *dout;  // forward inputs, output, dL/dout
+    const float *lse;                                 // forward log-sum-exp [T][Hq]
+    const int32_t *idx;                               // [T][k]
+    int64_t q_start;
+    int32_t rows;                                     // T
+    int64_t L;
+    int32_t Hq, Hkv, d, B, k;
+    float scale, scale_log2;
+    float *dq, *dk, *dv, *dgate;                      // [T][Hq][d], [L][Hkv][d] x2, [T][Hq]
+    uint16_t *da;                                     // workspace: sigmoid(gate) dL/dout, bf16
+    float *dsum;                                      // workspace: dL/dout . out per (row, head)
+    uint32_t *bits;                                   // workspace: [nblk][bits_ld] row bitmap
+    int64_t bits_ld;
+    int64_t nblk;
+};
+hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t stream);
+size_t attn_backward_workspace(int64_t T, int Hq, int d, int64_t nblk);
 int prefill_state_stride(int d);
 
 // Decode split-K geometry for k selected entries of B tokens.

@@ -21,10 +21,12 @@ OK, ERR_NULL, ERR_SHAPE, ERR_UNSUPPORTED, ERR_WORKSPACE, ERR_HIP = range(6)
 OP_INDEXER_TOPK = 1
 OP_ATTN_DECODE = 2
 OP_ATTN_PREFILL = 3
+OP_ATTN_BACKWARD = 4
 
 EXPORTS = ("sgqa_index_build", "sgqa_index_build_from_keys", "sgqa_indexer_topk", "sgqa_sparse_attn_prefill",
            "sgqa_sparse_attn_decode", "sgqa_swa_prefill", "sgqa_quantize_fp8",
-           "sgqa_indexer_topk_fp8", "sgqa_sparse_attn_decode_fp8", "sgqa_workspace_bytes",
+           "sgqa_indexer_topk_fp8", "sgqa_sparse_attn_decode_fp8", "sgqa_sparse_attn_backward",
+           "sgqa_workspace_bytes",
            "sgqa_status_string", "sgqa_last_error")
 
 
@@ -81,6 +83,9 @@ def load():
     lib.sgqa_sparse_attn_decode_fp8.restype = st
     lib.sgqa_sparse_attn_decode_fp8.argtypes = [dp, p, p, p, p, p, i64, p, p, p, i32,
                                                 ctypes.c_float, p, p, p, sz, p]
+    lib.sgqa_sparse_attn_backward.restype = st
+    lib.sgqa_sparse_attn_backward.argtypes = [dp, p, p, p, p, p, i64, i32, i64, ctypes.c_float, p,
+                                              p, p, p, p, p, p, p, sz, p]
     lib.sgqa_workspace_bytes.restype = sz
     lib.sgqa_workspace_bytes.argtypes = [ctypes.c_int, dp, i32, i32, i64]
     lib.sgqa_status_string.restype = ctypes.c_char_p
@@ -277,3 +282,21 @@ def sparse_attn_decode_fp8(shape: LayerShape, q, k_codes, v_codes, k_scales, v_s
                                              _i64_array(cache_lens), nseq, softmax_scale,
                                              _ptr(out), _ptr(lse), _ptr(workspace),
                                              workspace.numel(), _stream(stream, q)))
+
+
+def sparse_attn_backward(shape: LayerShape, q, k_cache, v_cache, gate, idx, q_start: int, L: int,
+                         softmax_scale: float, out, lse, dout, dq, dk, dv, dgate, workspace=None,
+                         stream=None):
+    """Backward of sparse_attn_prefill with idx fixed: fp32 dq [T, Hq, d], dk / dv [L, Hkv, d]
+    and dgate [T, Hq] from dout [T, Hq, d] and the forward's out and lse."""
+    _need_cuda(q, k_cache, v_cache, gate, idx, out, lse, dout, dq, dk, dv, dgate, workspace)
+    T = q.shape[0]
+    if workspace is None:
+        workspace = torch.empty(workspace_bytes(OP_ATTN_BACKWARD, shape, 1, T, L),
+                                dtype=torch.uint8, device=q.device)
+    d = Dims.of(shape)
+    check(load().sgqa_sparse_attn_backward(ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache),
+                                           _ptr(gate), _ptr(idx), q_start, T, L, softmax_scale,
+                                           _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                           _ptr(dv), _ptr(dgate), _ptr(workspace),
+                                           workspace.numel(), _stream(stream, q)))

@@ -141,6 +141,25 @@ def check_attention(out_gpu_bits: np.ndarray, out_ref: np.ndarray, lse_gpu=None,
     return res
 
 
+# Gradients of the fixed-selection backward: the matrix-core products take bf16 operands
+# (2^-9 relative each: the softmax weights, dz, q, dA), D = dout . out uses the bf16 forward
+# output, and dz = P (dP - D) cancels where dP ~ D.  Bound: relative L2 within 5x the bf16
+# step, and no element further than 3 % of the tensor's largest magnitude from the oracle.
+GRAD_REL_L2 = 1e-2
+GRAD_MAX_REL = 3e-2
+
+
+def check_grad(name: str, gpu: np.ndarray, ref: np.ndarray) -> dict:
+    g = np.asarray(gpu, dtype=np.float64).reshape(ref.shape)
+    err = np.abs(g - ref)
+    scale = max(float(np.abs(ref).max()), 1e-300)
+    rel = float(np.linalg.norm(g - ref) / max(np.linalg.norm(ref), 1e-300))
+    worst = float(err.max() / scale)
+    assert rel <= GRAD_REL_L2, f"{name}: relative L2 error {rel:.4g} > {GRAD_REL_L2}"
+    assert worst <= GRAD_MAX_REL, f"{name}: max error {worst:.4g} of max|ref| > {GRAD_MAX_REL}"
+    return {f"{name}_rel_l2": rel, f"{name}_max_rel": worst}
+
+
 def stratified_rows(q_start: int, T: int, B: int, k: int, n_random: int, seed: int,
                     extra=()) -> np.ndarray:
     """Query rows to check at full size: block edges, the k*B regime edge, chunk edges,

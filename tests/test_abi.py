@@ -189,6 +189,27 @@ def test_fp8_validation():
     assert attn(wsb=dneed - 1) == sgqa.ERR_WORKSPACE
 
 
+def test_backward_validation():
+    lib = sgqa.load()
+    d = dims()
+    need = lib.sgqa_workspace_bytes(sgqa.OP_ATTN_BACKWARD, ctypes.byref(d), 1, 64, 1024)
+    assert need > 0
+
+    def call(q=FAKE, lse=FAKE, T=64, L=1024, q_start=0, ws=FAKE, wsb=need):
+        return lib.sgqa_sparse_attn_backward(ctypes.byref(d), q, FAKE, FAKE, FAKE, FAKE, q_start, T,
+                                             L, 0.07, FAKE, lse, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
+                                             wsb, None)
+
+    assert call(q=None) == sgqa.ERR_NULL
+    assert call(lse=None) == sgqa.ERR_NULL
+    assert call(q_start=1000) == sgqa.ERR_SHAPE   # rows past the cache
+    assert call(T=-1) == sgqa.ERR_SHAPE
+    assert call(wsb=need - 1) == sgqa.ERR_WORKSPACE
+    assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == sgqa.ERR_SHAPE
+    assert call(T=0) == sgqa.OK
+    assert lib.sgqa_workspace_bytes(sgqa.OP_ATTN_BACKWARD, ctypes.byref(d), 2, 64, 1024) == 0
+
+
 def test_decode_validation():
     lib = sgqa.load()
     d = dims()

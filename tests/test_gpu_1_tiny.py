@@ -429,3 +429,53 @@ def test_decode_fp8_mixed_lengths():
         o_ref, l_ref = oracle.attend_f64(bits(Q[b]), kd, vd, bits(G[b]), scale)
         parity.check_attention(bits(out[b:b + 1]), o_ref[None], lse[b:b + 1].cpu().numpy(),
                                l_ref[None])
+
+
+def _backward_case(d, shape, q0: int, L: int, seed: int):
+    """Forward on the GPU (index, top-k, attention with lse), then the backward for a seeded
+    dout; returns the GPU gradients and the oracle's on the same selection."""
+    B, k = shape.block_size, shape.topk_blocks
+    Q, G = d["Q"][q0:], d["G"][q0:]
+    T = Q.shape[0]
+    kb = torch.empty((-(-L // B), shape.proxy_dim), dtype=torch.bfloat16, device=DEV)
+    sgqa.index_build(shape, d["kp"][:L], kb, [L])
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    sgqa.indexer_topk(shape, d["qp"][q0:], kb, [q0], idx)
+    scale = 1.0 / math.sqrt(shape.head_dim)
+    out = torch.empty_like(Q)
+    lse = torch.empty((T, shape.num_q_heads), dtype=torch.float32, device=DEV)
+    K, V = d["K"][:L], d["V"][:L]
+    sgqa.sparse_attn_prefill(shape, Q, K, V, G, idx, q0, L, scale, out, lse)
+    g = torch.Generator(device=DEV).manual_seed(seed)
+    dout = torch.randn(Q.shape, generator=g, device=DEV).to(torch.bfloat16)
+    grads = dict(dq=torch.empty(Q.shape, dtype=torch.float32, device=DEV),
+                 dk=torch.empty(K.shape, dtype=torch.float32, device=DEV),
+                 dv=torch.empty(V.shape, dtype=torch.float32, device=DEV),
+                 dg=torch.empty(G.shape, dtype=torch.float32, device=DEV))
+    sgqa.sparse_attn_backward(shape, Q, K, V, G, idx, q0, L, scale, out, lse, dout,
+                              grads["dq"], grads["dk"], grads["dv"], grads["dg"])
+    torch.cuda.synchronize()
+    t = np.arange(q0, q0 + T, dtype=np.int64)
+    ref = oracle.sparse_attention_backward(bits(Q), t, bits(K), bits(V), bits(G),
+                                           idx.cpu().numpy(), B, scale, bits(dout))
+    return grads, dict(zip(("dq", "dk", "dv", "dg"), ref)), (Q, K, V, G, idx, out, lse, dout)
+
+
+@pytest.mark.parametrize("B,k,q0", [(8, 16, 0), (8, 4, 0), (1, 64, 0), (8, 16, 517), (16, 8, 100)])
+def test_tiny_backward(tiny, B, k, q0):
+    """Fixed-selection backward on the tiny layer against the oracle: every dq, dK, dV and
+    dgate element, sparse and dense rows, B in {1, 8, 16}, a chunk starting mid-block; two
+    calls give identical bits."""
+    shape = with_selection(WL.shape, B, k)
+    grads, ref, args = _backward_case(tiny, shape, q0, WL.L, 7 + q0)
+    st = {}
+    for name in ("dq", "dk", "dv", "dg"):
+        st.update(parity.check_grad(name, grads[name].cpu().numpy(), ref[name]))
+    say(f"backward B={B} k={k} q0={q0}: {st}")
+    Q, K, V, G, idx, out, lse, dout = args
+    again = {n: torch.empty_like(v) for n, v in grads.items()}
+    sgqa.sparse_attn_backward(shape, Q, K, V, G, idx, q0, WL.L, 1.0 / math.sqrt(shape.head_dim),
+                              out, lse, dout, again["dq"], again["dk"], again["dv"], again["dg"])
+    torch.cuda.synchronize()
+    for n in grads:
+        assert torch.equal(grads[n], again[n]), n
