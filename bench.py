@@ -154,8 +154,33 @@ def bench_prefill(steps: int, warmup: int):
                    "algorithmic_bytes": fk_bytes,
                    "mfma_tflops": 2 * 2 * wl.nblk * width * s.proxy_dim / (fk_ms / 1e3) / 1e12}
     del kb_f
+    # backward of the attention with this step's selection fixed (training), same inputs
+    g = torch.Generator(device=dev).manual_seed(9)
+    dout = torch.randn(d["Q"].shape, generator=g, device=dev).to(torch.bfloat16)
+    dq = torch.empty(d["Q"].shape, dtype=torch.float32, device=dev)
+    dk = torch.empty(d["K"].shape, dtype=torch.float32, device=dev)
+    dv = torch.empty(d["V"].shape, dtype=torch.float32, device=dev)
+    dg = torch.empty(d["G"].shape, dtype=torch.float32, device=dev)
+    ws_b = torch.empty(sgqa.workspace_bytes(sgqa.OP_ATTN_BACKWARD, s, 1, wl.T, wl.L),
+                       dtype=torch.uint8, device=dev)
+
+    def bwd():
+        sgqa.sparse_attn_backward(s, d["Q"], d["K"], d["V"], d["G"], idx, wl.q_start, wl.L, scale,
+                                  lse, dout, dq, dk, dv, dg, workspace=ws_b, stream=stream)
+
+    bwd()
+    a.record(stream)
+    for _ in range(steps):
+        bwd()
+    b.record(stream)
+    torch.cuda.synchronize()
+    bwd_ms = a.elapsed_time(b) / steps
+    backward = {"ms": bwd_ms, "tokens_per_s": wl.T / (bwd_ms / 1e3),
+                "tflops_minimal": 10 * s.head_dim * s.num_q_heads * pairs / (bwd_ms / 1e3) / 1e12,
+                "ratio_to_forward_attention": bwd_ms / attn_ms}
+    del dout, dq, dk, dv, dg, ws_b
     res = dict(wl=wl, total_ms=total_ms, ms_per_step=total_ms / steps, build_ms=build_ms, swa=swa,
-               fused_index=fused_index,
+               fused_index=fused_index, backward=backward,
                topk_ms=topk_ms, attn_ms=attn_ms, pairs=pairs, attn_flops=flops,
                gather_bytes=gather_bytes, attn_bytes=gather_bytes + io_bytes, data=d, kb=kb,
                idx=idx)
@@ -427,7 +452,9 @@ def main():
         f"{pre['topk_ms']:.3f}, attn {pre['attn_ms']:.3f}) -> {tokens_per_s:,.0f} tokens/s, "
         f"attention {attn_tflops:.1f} TFLOP/s")
     log(f"sliding window: {pre['swa']['ms']:.3f} ms; index from keys: "
-        f"{pre['fused_index']['ms']:.3f} ms ({pre['fused_index']['GBps']:.0f} GB/s)")
+        f"{pre['fused_index']['ms']:.3f} ms ({pre['fused_index']['GBps']:.0f} GB/s); backward "
+        f"{pre['backward']['ms']:.1f} ms ({pre['backward']['ratio_to_forward_attention']:.2f}x "
+        f"the forward attention)")
     cpu = None
     if not args.no_cpu:
         log(f"cpu baseline: oracle on {args.cpu_rows} rows")
@@ -477,6 +504,7 @@ def main():
     }
     line["sliding_window_attention"] = pre["swa"]
     line["index_build_from_keys"] = pre["fused_index"]
+    line["attention_backward"] = pre["backward"]
     if cov is not None:
         line["coverage"] = cov
     if dec is not None:

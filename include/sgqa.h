@@ -218,15 +218,16 @@ sgqa_status sgqa_swa_prefill(const sgqa_dims *dims, const sgqa_bf16 *q, const sg
  * count training at long context among the costs of full attention, ai.info
  * "Sparse GQA targets million-token context"; how the indexer itself is trained
  * is not stated, so idx is an input).  For the loss whose gradient with respect
- * to out is dout, with P_s = exp(z_s - lse) the forward's weights and
- * a = out / sigmoid(gate):
- *   D      = dout . out                    per (row, head)
+ * to out is dout, with P_s = exp(z_s - lse) the forward's weights (lse from the
+ * forward call) and dP_s = sigmoid(gate) dout . v_s:
+ *   D      = sum_s P_s dP_s                per (row, head; = dout . out exactly)
  *   dgate  = D * (1 - sigmoid(gate))
- *   dz_s   = P_s * (sigmoid(gate) dout . v_s - D)
+ *   dz_s   = P_s * (dP_s - D)
  *   dq     = softmax_scale * sum_s dz_s k_s
  *   dk_s   = softmax_scale * sum over (row, head of the group) of dz_s q
  *   dv_s   = sum over (row, head of the group) of P_s sigmoid(gate) dout
- * The forward's out and lse are inputs.  dk and dv are written for every token
+ * D is formed from the same P and dP the gradients use (not from the rounded
+ * forward output), so the dz of a row sum to zero.  dk and dv are written for every token
  * of [0, L) (zero where no row attends); every sum runs in a fixed order, so the
  * results are deterministic.  Layouts as sgqa_sparse_attn_prefill; dq
  * [T][Hq][d], dk / dv [L][Hkv][d] and dgate [T][Hq] are fp32.  nseq is 1.
@@ -236,8 +237,7 @@ sgqa_status sgqa_swa_prefill(const sgqa_dims *dims, const sgqa_bf16 *q, const sg
 sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
                                       const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
                                       const sgqa_bf16 *gate, const int32_t *idx, int64_t q_start,
-                                      int32_t T, int64_t L, float softmax_scale,
-                                      const sgqa_bf16 *out, const float *lse,
+                                      int32_t T, int64_t L, float softmax_scale, const float *lse,
                                       const sgqa_bf16 *dout, float *dq, float *dk, float *dv,
                                       float *dgate, void *workspace, size_t workspace_bytes,
                                       void *stream);

@@ -676,6 +676,8 @@ hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream)
 {
     if (a.rows <= 0)
         return hipSuccess;
+    if (!a.q || !a.out || (!a.idx && !a.window))
+        return hipErrorInvalidValue;  // never launch without the tensors the kernels touch
     if (a.nslices > 1) {
         switch (a.d) {
         case 64: return launch_prefill_sliced<64>(a, stream);
@@ -701,6 +703,8 @@ hipError_t launch_swa(const AttnArgs &a, hipStream_t stream)
 {
     if (a.rows <= 0)
         return hipSuccess;
+    if (!a.q || !a.out || (!a.idx && !a.window))
+        return hipErrorInvalidValue;  // never launch without the tensors the kernels touch
     switch (a.d) {
     case 64: return launch_prefill_d<64, true>(a, stream);
     case 128: return launch_prefill_d<128, true>(a, stream);
@@ -713,6 +717,8 @@ hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream)
 {
     if (a.rows <= 0)
         return hipSuccess;
+    if (!a.q || !a.out || (!a.idx && !a.window))
+        return hipErrorInvalidValue;  // never launch without the tensors the kernels touch
     switch (a.d) {
     case 64: return launch_decode_d<64>(a, stream);
     case 128: return launch_decode_d<128>(a, stream);
@@ -729,9 +735,12 @@ hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream)
 //   D = g_out . out (= da . a),  dG = D (1 - sigmoid(G)),  da = sigmoid(G) g_out,
 //   dP_s = da . v_s,  dz_s = P_s (dP_s - D),
 //   dq = scale sum_s dz_s k_s,  dk_s = scale sum_(t,h) dz_s q,  dv_s = sum_(t,h) P_s da.
-// Four launches: k_bwd_prep (D, dG, da), a zero fill and k_bwd_bitmap (for every key block
-// the set of query rows that selected it, one bit per row, by atomicOr, whose result does not
-// depend on order), k_bwd_dq (query-major, the forward's wave with a second product
+// D is formed as sum_s P_s dP_s from the kernel's own fp32 P and dP (a first sweep over the
+// row), not from the bf16 forward output: then the dz of a row sum to zero and each dz carries
+// only its own bf16 rounding, instead of an error of D shared by every attended key.
+// Launches: k_bwd_prep (da), a zero fill and k_bwd_bitmap (for every key block the set of
+// query rows that selected it, one bit per row, by atomicOr, whose result does not depend on
+// order), k_bwd_dq (query-major, the forward's wave: a sweep for D and dG, then a second with
 // dP^T = V da^T and K staged for dq^T += K^T dz^T), and k_bwd_dkdv (key-major: a workgroup per
 // 16-token tile of a block, a wave per KV group, walking the tile's query rows in ascending
 // order, so dK and dV are sums in a fixed order and written once).
@@ -750,7 +759,7 @@ __device__ __forceinline__ s16x4 pack4_bf16(float x0, float x1, float x2, float 
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// One wave per (row, head): D, dG and da = sigmoid(G) g_out (bf16).
+// One wave per (row, head): da = sigmoid(G) g_out, rounded to bf16 for the matrix cores.
 __global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a)
 {
     const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -759,21 +768,9 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a)
     const int lane = threadIdx.x & 63;
     const int d = a.d;
     const uint16_t *go = a.dout + row * d;
-    const uint16_t *o = a.out + row * d;
     const float sg = sigmoid_f32(bf16_bits_to_f32(a.gate[row]));
-    float dot = 0.f;
-    for (int e = lane; e < d; e += 64) {
-        const float g = bf16_bits_to_f32(go[e]);
-        dot += g * bf16_bits_to_f32(o[e]);
-        a.da[row * d + e] = (uint16_t)f32_to_bf16_bits(sg * g);
-    }
-#pragma unroll
-    for (int off = 32; off > 0; off >>= 1)
-        dot += __shfl_xor(dot, off);
-    if (lane == 0) {
-        a.dsum[row] = dot;
-        a.dgate[row] = dot * (1.0f - sg);
-    }
+    for (int e = lane; e < d; e += 64)
+        a.da[row * d + e] = (uint16_t)f32_to_bf16_bits(sg * bf16_bits_to_f32(go[e]));
 }
 
 __global__ __launch_bounds__(256) void k_bwd_zero(uint32_t *p, int64_t n)
@@ -794,6 +791,59 @@ __global__ __launch_bounds__(256) void k_bwd_bitmap(BwdArgs a)
     if (j < 0 || (int64_t)j > c || (int64_t)j >= a.nblk)
         return;
     atomicOr(&a.bits[(int64_t)j * a.bits_ld + (r >> 5)], 1u << (r & 31));
+}
+
+// First sweep of a wave's (row, group): D = sum_s P_s dP_s per head (this lane's share),
+// from the same fp32 P and dP the second sweep uses, so the dz of a row sum to zero.
+template <int D>
+__device__ __forceinline__ float dsum_range(const uint16_t *__restrict__ Kg,
+                                            const uint16_t *__restrict__ Vg, int Hkv,
+                                            const SparseTokens &src, const bf16x8 (&qf)[D / 32],
+                                            const bf16x8 (&daf)[D / 32], float scale_log2,
+                                            float lse2)
+{
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    const int64_t row_elems = (int64_t)Hkv * D;
+    const int nsteps = src.steps();
+    float part = 0.f;
+    for (int step = 0; step < nsteps; ++step) {
+        int64_t s_ld;
+        bool valid;
+        src.slot(step, lane & 31, s_ld, valid);
+        const uint64_t vmask = __ballot(valid);
+        const int s_lo = (int)(s_ld & 0xffffffff), s_hi = (int)(s_ld >> 32);
+        u32x4 kv[2][D / 32], vv[2][D / 32];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const int sl = h * 16 + col;
+            const int64_t sk = ((int64_t)(uint32_t)__shfl(s_lo, sl)) |
+                               ((int64_t)__shfl(s_hi, sl) << 32);
+            const uint16_t *kr = Kg + sk * row_elems + q4 * 8;
+            const uint16_t *vr = Vg + sk * row_elems + q4 * 8;
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                kv[h][kk] = load16(kr + kk * 32);
+                vv[h][kk] = load16(vr + kk * 32);
+            }
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                sc = mfma_16x16x32(as_bf16x8(kv[h][kk]), qf[kk], sc);
+                dp = mfma_16x16x32(as_bf16x8(vv[h][kk]), daf[kk], dp);
+            }
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int slot = h * 16 + q4 * 4 + r;
+                if ((vmask >> slot) & 1ull)
+                    part += fast_exp2(sc[r] * scale_log2 - lse2) * dp[r];
+            }
+        }
+    }
+    return part;
 }
 
 // dq of one wave's (row, group) over its selected tokens; acc = dq^T (unscaled).
@@ -905,12 +955,19 @@ __global__ __launch_bounds__(512) void k_bwd_dq(BwdArgs a)
     load_q<D>(a.q + head0 * D, hpg, qf);
     load_q<D>(a.da + head0 * D, hpg, daf);
     const float lse2 = col < hpg ? a.lse[head0 + col] * kLog2e : 0.f;
-    const float dsum = col < hpg ? a.dsum[head0 + col] : 0.f;
+    const SparseTokens src{a.idx + r * a.k, 0, nvalid, t, c, a.B};
+    // D = sum_s P_s dP_s (so that dG = D (1 - sigmoid(G)) and the dz of the row sum to zero)
+    const float dsum = sum_across_rows(dsum_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D,
+                                                     a.Hkv, src, qf, daf, a.scale_log2, lse2));
+    if (col < hpg && q4 == 0) {
+        a.dsum[head0 + col] = dsum;
+        a.dgate[head0 + col] =
+            dsum * (1.0f - sigmoid_f32(bf16_bits_to_f32(a.gate[head0 + col])));
+    }
     f32x4 acc[D / 16];
 #pragma unroll
     for (int mt = 0; mt < D / 16; ++mt)
         acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    const SparseTokens src{a.idx + r * a.k, 0, nvalid, t, c, a.B};
     dq_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D, a.Hkv, src, qf, daf, a.scale_log2,
                 lse2, dsum, lds + wave * kSlots * (D + 4), acc);
     if (col < hpg) {
@@ -1088,6 +1145,8 @@ hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t stream)
 {
     if (a.rows <= 0)
         return hipSuccess;
+    if (!a.q || !a.dout || !a.dq || !a.dk || !a.dv || !a.dgate || !a.da || !a.dsum || !a.bits)
+        return hipErrorInvalidValue;  // never launch without the tensors the kernels touch
     const int64_t nrow = (int64_t)a.rows * a.Hq;
     hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)((nrow + 3) / 4)), dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();

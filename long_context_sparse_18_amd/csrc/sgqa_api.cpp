@@ -751,8 +751,7 @@ sgqa_status sgqa_sparse_attn_decode_fp8(const sgqa_dims *dims, const sgqa_bf16 *
 sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
                                       const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
                                       const sgqa_bf16 *gate, const int32_t *idx, int64_t q_start,
-                                      int32_t T, int64_t L, float softmax_scale,
-                                      const sgqa_bf16 *out, const float *lse,
+                                      int32_t T, int64_t L, float softmax_scale, const float *lse,
                                       const sgqa_bf16 *dout, float *dq, float *dk, float *dv,
                                       float *dgate, void *workspace, size_t workspace_bytes,
                                       void *stream)
@@ -770,11 +769,11 @@ sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
         return fail(SGQA_ERR_SHAPE, "softmax_scale must be finite");
     if (T == 0 || L == 0)
         return ok();
-    if (!q || !k_cache || !v_cache || !gate || !idx || !out || !lse || !dout || !dq || !dk ||
-        !dv || !dgate)
+    if (!q || !k_cache || !v_cache || !gate || !idx || !lse || !dout || !dq || !dk || !dv ||
+        !dgate)
         return fail(SGQA_ERR_NULL, "every tensor argument must be non-NULL");
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(dq, 16) ||
-        !aligned(out, 2) || !aligned(dout, 2) || !aligned(gate, 2) || !aligned(idx, 4) ||
+        !aligned(dout, 2) || !aligned(gate, 2) || !aligned(idx, 4) ||
         !aligned(lse, 4) || !aligned(dk, 4) || !aligned(dv, 4) || !aligned(dgate, 4))
         return fail(SGQA_ERR_SHAPE, "q, caches and dq must be 16-byte aligned");
     const size_t need = sgqa_workspace_bytes(SGQA_OP_ATTN_BACKWARD, dims, 1, T, L);
@@ -788,7 +787,6 @@ sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
     a.kc = k_cache;
     a.vc = v_cache;
     a.gate = gate;
-    a.out = out;
     a.dout = dout;
     a.lse = lse;
     a.idx = idx;

@@ -146,7 +146,7 @@ hipError_t launch_swa(const AttnArgs &a, hipStream_t stream);
 // Backward of the sparse attention with the selection fixed (prefill layout: T query rows at
 // q_start .. q_start+T-1 over an L-token cache).
 struct BwdArgs {
-    const uint16_t *q, *kc, *vc, *gate, *out, *dout;  // forward inputs, output, dL/dout
+    const uint16_t *q, *kc, *vc, *gate, *dout;        // forward inputs and dL/dout
     const float *lse;                                 // forward log-sum-exp [T][Hq]
     const int32_t *idx;                               // [T][k]
     int64_t q_start;
@@ -156,7 +156,7 @@ struct BwdArgs {
     float scale, scale_log2;
     float *dq, *dk, *dv, *dgate;                      // [T][Hq][d], [L][Hkv][d] x2, [T][Hq]
     uint16_t *da;                                     // workspace: sigmoid(gate) dL/dout, bf16
-    float *dsum;                                      // workspace: dL/dout . out per (row, head)
+    float *dsum;                                      // workspace: sum_s P_s dP_s per (row, head)
     uint32_t *bits;                                   // workspace: [nblk][bits_ld] row bitmap
     int64_t bits_ld;
     int64_t nblk;

@@ -85,7 +85,7 @@ def load():
                                                 ctypes.c_float, p, p, p, sz, p]
     lib.sgqa_sparse_attn_backward.restype = st
     lib.sgqa_sparse_attn_backward.argtypes = [dp, p, p, p, p, p, i64, i32, i64, ctypes.c_float, p,
-                                              p, p, p, p, p, p, p, sz, p]
+                                              p, p, p, p, p, p, sz, p]
     lib.sgqa_workspace_bytes.restype = sz
     lib.sgqa_workspace_bytes.argtypes = [ctypes.c_int, dp, i32, i32, i64]
     lib.sgqa_status_string.restype = ctypes.c_char_p
@@ -285,11 +285,11 @@ def sparse_attn_decode_fp8(shape: LayerShape, q, k_codes, v_codes, k_scales, v_s
 
 
 def sparse_attn_backward(shape: LayerShape, q, k_cache, v_cache, gate, idx, q_start: int, L: int,
-                         softmax_scale: float, out, lse, dout, dq, dk, dv, dgate, workspace=None,
+                         softmax_scale: float, lse, dout, dq, dk, dv, dgate, workspace=None,
                          stream=None):
     """Backward of sparse_attn_prefill with idx fixed: fp32 dq [T, Hq, d], dk / dv [L, Hkv, d]
-    and dgate [T, Hq] from dout [T, Hq, d] and the forward's out and lse."""
-    _need_cuda(q, k_cache, v_cache, gate, idx, out, lse, dout, dq, dk, dv, dgate, workspace)
+    and dgate [T, Hq] from dout [T, Hq, d] and the forward's lse."""
+    _need_cuda(q, k_cache, v_cache, gate, idx, lse, dout, dq, dk, dv, dgate, workspace)
     T = q.shape[0]
     if workspace is None:
         workspace = torch.empty(workspace_bytes(OP_ATTN_BACKWARD, shape, 1, T, L),
@@ -297,6 +297,6 @@ def sparse_attn_backward(shape: LayerShape, q, k_cache, v_cache, gate, idx, q_st
     d = Dims.of(shape)
     check(load().sgqa_sparse_attn_backward(ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                            _ptr(gate), _ptr(idx), q_start, T, L, softmax_scale,
-                                           _ptr(out), _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                           _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                                            _ptr(dv), _ptr(dgate), _ptr(workspace),
                                            workspace.numel(), _stream(stream, q)))

@@ -197,8 +197,8 @@ def test_backward_validation():
 
     def call(q=FAKE, lse=FAKE, T=64, L=1024, q_start=0, ws=FAKE, wsb=need):
         return lib.sgqa_sparse_attn_backward(ctypes.byref(d), q, FAKE, FAKE, FAKE, FAKE, q_start, T,
-                                             L, 0.07, FAKE, lse, FAKE, FAKE, FAKE, FAKE, FAKE, ws,
-                                             wsb, None)
+                                             L, 0.07, lse, FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb,
+                                             None)
 
     assert call(q=None) == sgqa.ERR_NULL
     assert call(lse=None) == sgqa.ERR_NULL

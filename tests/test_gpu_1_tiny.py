@@ -452,7 +452,7 @@ def _backward_case(d, shape, q0: int, L: int, seed: int):
                  dk=torch.empty(K.shape, dtype=torch.float32, device=DEV),
                  dv=torch.empty(V.shape, dtype=torch.float32, device=DEV),
                  dg=torch.empty(G.shape, dtype=torch.float32, device=DEV))
-    sgqa.sparse_attn_backward(shape, Q, K, V, G, idx, q0, L, scale, out, lse, dout,
+    sgqa.sparse_attn_backward(shape, Q, K, V, G, idx, q0, L, scale, lse, dout,
                               grads["dq"], grads["dk"], grads["dv"], grads["dg"])
     torch.cuda.synchronize()
     t = np.arange(q0, q0 + T, dtype=np.int64)
@@ -475,7 +475,7 @@ def test_tiny_backward(tiny, B, k, q0):
     Q, K, V, G, idx, out, lse, dout = args
     again = {n: torch.empty_like(v) for n, v in grads.items()}
     sgqa.sparse_attn_backward(shape, Q, K, V, G, idx, q0, WL.L, 1.0 / math.sqrt(shape.head_dim),
-                              out, lse, dout, again["dq"], again["dk"], again["dv"], again["dg"])
+                              lse, dout, again["dq"], again["dk"], again["dv"], again["dg"])
     torch.cuda.synchronize()
     for n in grads:
         assert torch.equal(grads[n], again[n]), n
