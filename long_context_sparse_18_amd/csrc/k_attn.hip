@@ -741,9 +741,9 @@ hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream)
 // Launches: k_bwd_prep (da), a zero fill and k_bwd_bitmap (for every key block the set of
 // query rows that selected it, one bit per row, by atomicOr, whose result does not depend on
 // order), k_bwd_dq (query-major, the forward's wave: a sweep for D and dG, then a second with
-// dP^T = V da^T and K staged for dq^T += K^T dz^T), and k_bwd_dkdv (key-major: a workgroup per
-// 16-token tile of a block, a wave per KV group, walking the tile's query rows in ascending
-// order, so dK and dV are sums in a fixed order and written once).
+// dP^T = V da^T and K staged for dq^T += K^T dz^T), and k_bwd_dkdv (key-major: a wave per
+// 16-token tile of a block and KV group, walking the tile's query rows in a fixed order, so dK
+// and dV are sums in a fixed order and written once).
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 
 __device__ __forceinline__ f32x4 mfma_16x16x16(s16x4 a, s16x4 b, f32x4 c)
@@ -978,20 +978,28 @@ __global__ __launch_bounds__(512) void k_bwd_dq(BwdArgs a)
     }
 }
 
-// dK and dV of one 16-token tile of key block j for KV group g (one wave), over the query
-// rows whose selection holds j, in ascending order.  Per row: S = q K^T and dP = dA V^T with
-// M = heads, so each lane holds heads 4 q4 + i of token col - exactly the A operand of the
-// 16x16x16 products dV += P^T dA and dK += dz^T q (M = tokens, K = heads); q and dA are
-// staged in LDS for the B operands.
+// dK and dV of one 16-token tile of a key block for one KV group (one wave), over the query
+// rows whose selection holds the block.  Per row: S = q K^T and dP = dA V^T with M = heads, so
+// each lane holds heads 4 q4 + i of token col - exactly the A operand of the 16x16x16
+// products dV += P^T dA and dK += dz^T q (M = tokens, K = heads); q and dA sit in LDS, where
+// the B operands are read.  A workgroup takes 4 tiles of one group (group = blockIdx % Hkv, so
+// with Hkv dividing 8 each XCD's L2 serves one group's rows), and every wave walks its rows
+// from the last one down: rows select about the same number of blocks whatever the block, so
+// concurrent waves stay in the same window of rows and share those rows' q and dA in L2.  The
+// next row's q and dA are loaded while the current one is computed.
 template <int D>
 __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
 {
     extern __shared__ __align__(16) uint16_t lds[];
     constexpr int kLd = D + 8;
     const int ntile = (a.B + 15) / 16;
-    const int64_t j = blockIdx.x / ntile;
-    const int tile = blockIdx.x - (int)(j * ntile);
-    const int g = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int g = (int)(blockIdx.x % (unsigned)a.Hkv);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t tid = (int64_t)(blockIdx.x / (unsigned)a.Hkv) * 4 + wave;  // tile index
+    if (tid >= a.nblk * ntile)
+        return;
+    const int64_t j = tid / ntile;
+    const int tile = (int)(tid - j * ntile);
     const int col = lane & 15, q4 = lane >> 4;
     const int hpg = a.Hq / a.Hkv;
     const int64_t s0 = j * a.B + (int64_t)tile * 16;  // first token of the tile
@@ -1000,7 +1008,7 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
     ntok = a.L - s0 < ntok ? a.L - s0 : ntok;
     if (ntok <= 0)
         return;  // a tile past the end of a short last block
-    uint16_t *qs = lds + g * 2 * 16 * kLd;
+    uint16_t *qs = lds + wave * 2 * 16 * kLd;
     uint16_t *ds = qs + 16 * kLd;
     const int64_t row_elems = (int64_t)a.Hkv * D;
 
@@ -1019,79 +1027,118 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
         dv[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+    // the block's rows, last first (uniform across the wave)
     const uint32_t *brow = a.bits + j * a.bits_ld;
-    const int64_t nw = ((int64_t)a.rows + 31) >> 5;
     const int64_t first_row = j * a.B - a.q_start;  // no row before it can select block j
     const int64_t w0 = first_row > 0 ? first_row >> 5 : 0;
-#pragma unroll 1
-    for (int64_t w = w0; w < nw; ++w) {
-        uint32_t word = brow[w];
-#pragma unroll 1
-        while (word) {
-            const int64_t r = (w << 5) + __builtin_ctz(word);
-            word &= word - 1;
-            const int64_t t = a.q_start + r;
-            const int64_t head0 = r * a.Hq + (int64_t)g * hpg;
-            // q and dA of the group's heads (head col, dims 8 q4 + 32 kk ..) as A operands
-            u32x4 qa[D / 32], da[D / 32];
+    int64_t w = (((int64_t)a.rows + 31) >> 5) - 1;
+    uint32_t word = w >= w0 ? brow[w] : 0u;
+    auto next_row = [&](int64_t &r) -> bool {
+        while (word == 0u) {
+            if (--w < w0)
+                return false;
+            word = brow[w];
+        }
+        const int b = 31 - __builtin_clz(word);
+        word &= ~(1u << b);
+        r = (w << 5) + b;
+        return true;
+    };
+    // q and dA of the group's heads of row r (head col, dims 8 q4 + 32 kk), lse / D of heads
+    // 4 q4 + i
+    auto fetch = [&](int64_t r, u32x4 (&qa)[D / 32], u32x4 (&da)[D / 32], float (&l2)[4],
+                     float (&dsm)[4]) {
+        const int64_t head0 = r * a.Hq + (int64_t)g * hpg;
 #pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                qa[kk] = u32x4{0u, 0u, 0u, 0u};
-                da[kk] = u32x4{0u, 0u, 0u, 0u};
-                if (col < hpg) {
-                    qa[kk] = load16(a.q + (head0 + col) * D + kk * 32 + q4 * 8);
-                    da[kk] = load16(a.da + (head0 + col) * D + kk * 32 + q4 * 8);
-                }
-            }
-            float lse2[4], dsum[4];
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int h = q4 * 4 + i;
-                lse2[i] = h < hpg ? a.lse[head0 + h] * kLog2e : 0.f;
-                dsum[i] = h < hpg ? a.dsum[head0 + h] : 0.f;
-            }
-            f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                sc = mfma_16x16x32(as_bf16x8(qa[kk]), kB[kk], sc);
-                dp = mfma_16x16x32(as_bf16x8(da[kk]), vB[kk], dp);
-            }
-            // lane holds heads 4 q4 + i of token col
-            float p[4], dz[4];
-            const bool tok_ok = col < ntok && s0 + col <= t;
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const bool ok = tok_ok && q4 * 4 + i < hpg;
-                p[i] = ok ? fast_exp2(sc[i] * a.scale_log2 - lse2[i]) : 0.f;
-                dz[i] = p[i] * (dp[i] - dsum[i]) * a.scale;
-            }
-            const s16x4 pa = pack4_bf16(p[0], p[1], p[2], p[3]);
-            const s16x4 za = pack4_bf16(dz[0], dz[1], dz[2], dz[3]);
-
-            wave_lds_handoff();
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                uint2 *dq_ = reinterpret_cast<uint2 *>(qs + col * kLd + kk * 32 + q4 * 8);
-                uint2 *dd_ = reinterpret_cast<uint2 *>(ds + col * kLd + kk * 32 + q4 * 8);
-                dq_[0] = uint2{qa[kk][0], qa[kk][1]};
-                dq_[1] = uint2{qa[kk][2], qa[kk][3]};
-                dd_[0] = uint2{da[kk][0], da[kk][1]};
-                dd_[1] = uint2{da[kk][2], da[kk][3]};
-            }
-            wave_lds_handoff();
-#pragma unroll
-            for (int nt = 0; nt < D / 16; ++nt) {
-                const int dcol = nt * 16 + col;
-                const uint16_t *qc = qs + (q4 * 4) * kLd + dcol;
-                const uint16_t *dc = ds + (q4 * 4) * kLd + dcol;
-                const uint64_t qw = (uint64_t)qc[0] | ((uint64_t)qc[kLd] << 16) |
-                                    ((uint64_t)qc[2 * kLd] << 32) | ((uint64_t)qc[3 * kLd] << 48);
-                const uint64_t dw = (uint64_t)dc[0] | ((uint64_t)dc[kLd] << 16) |
-                                    ((uint64_t)dc[2 * kLd] << 32) | ((uint64_t)dc[3 * kLd] << 48);
-                dv[nt] = mfma_16x16x16(pa, __builtin_bit_cast(s16x4, dw), dv[nt]);
-                dk[nt] = mfma_16x16x16(za, __builtin_bit_cast(s16x4, qw), dk[nt]);
+        for (int kk = 0; kk < D / 32; ++kk) {
+            qa[kk] = u32x4{0u, 0u, 0u, 0u};
+            da[kk] = u32x4{0u, 0u, 0u, 0u};
+            if (col < hpg) {
+                qa[kk] = load16(a.q + (head0 + col) * D + kk * 32 + q4 * 8);
+                da[kk] = load16(a.da + (head0 + col) * D + kk * 32 + q4 * 8);
             }
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int h = q4 * 4 + i;
+            l2[i] = h < hpg ? a.lse[head0 + h] * kLog2e : 0.f;
+            dsm[i] = h < hpg ? a.dsum[head0 + h] : 0.f;
+        }
+    };
+    auto stage = [&](const u32x4 (&qa)[D / 32], const u32x4 (&da)[D / 32]) {
+        wave_lds_handoff();
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            uint2 *dq_ = reinterpret_cast<uint2 *>(qs + col * kLd + kk * 32 + q4 * 8);
+            uint2 *dd_ = reinterpret_cast<uint2 *>(ds + col * kLd + kk * 32 + q4 * 8);
+            dq_[0] = uint2{qa[kk][0], qa[kk][1]};
+            dq_[1] = uint2{qa[kk][2], qa[kk][3]};
+            dd_[0] = uint2{da[kk][0], da[kk][1]};
+            dd_[1] = uint2{da[kk][2], da[kk][3]};
+        }
+        wave_lds_handoff();
+    };
+
+    int64_t r;
+    bool have = next_row(r);
+    float lse2[4], dsum[4];
+    if (have) {
+        u32x4 qa[D / 32], da[D / 32];
+        fetch(r, qa, da, lse2, dsum);
+        stage(qa, da);
+    }
+#pragma unroll 1
+    while (have) {
+        int64_t rn = 0;
+        const bool have_next = next_row(rn);
+        u32x4 nq[D / 32], nd[D / 32];
+        float nl[4], ns[4];
+        if (have_next)
+            fetch(rn, nq, nd, nl, ns);
+        const int64_t t = a.q_start + r;
+
+        // S = q K^T and dP = dA V^T from the staged rows
+        f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const u32x4 qa = *reinterpret_cast<const u32x4 *>(qs + col * kLd + kk * 32 + q4 * 8);
+            const u32x4 da = *reinterpret_cast<const u32x4 *>(ds + col * kLd + kk * 32 + q4 * 8);
+            sc = mfma_16x16x32(as_bf16x8(qa), kB[kk], sc);
+            dp = mfma_16x16x32(as_bf16x8(da), vB[kk], dp);
+        }
+        // lane holds heads 4 q4 + i of token col
+        float p[4], dz[4];
+        const bool tok_ok = col < ntok && s0 + col <= t;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = tok_ok && q4 * 4 + i < hpg;
+            p[i] = ok ? fast_exp2(sc[i] * a.scale_log2 - lse2[i]) : 0.f;
+            dz[i] = p[i] * (dp[i] - dsum[i]) * a.scale;
+        }
+        const s16x4 pa = pack4_bf16(p[0], p[1], p[2], p[3]);
+        const s16x4 za = pack4_bf16(dz[0], dz[1], dz[2], dz[3]);
+#pragma unroll
+        for (int nt = 0; nt < D / 16; ++nt) {
+            const int dcol = nt * 16 + col;
+            const uint16_t *qc = qs + (q4 * 4) * kLd + dcol;
+            const uint16_t *dc = ds + (q4 * 4) * kLd + dcol;
+            const uint64_t qw = (uint64_t)qc[0] | ((uint64_t)qc[kLd] << 16) |
+                                ((uint64_t)qc[2 * kLd] << 32) | ((uint64_t)qc[3 * kLd] << 48);
+            const uint64_t dw = (uint64_t)dc[0] | ((uint64_t)dc[kLd] << 16) |
+                                ((uint64_t)dc[2 * kLd] << 32) | ((uint64_t)dc[3 * kLd] << 48);
+            dv[nt] = mfma_16x16x16(pa, __builtin_bit_cast(s16x4, dw), dv[nt]);
+            dk[nt] = mfma_16x16x16(za, __builtin_bit_cast(s16x4, qw), dk[nt]);
+        }
+        if (have_next) {
+            stage(nq, nd);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lse2[i] = nl[i];
+                dsum[i] = ns[i];
+            }
+        }
+        r = rn;
+        have = have_next;
     }
     // lane holds dK / dV of token 4 q4 + i, dim 16 nt + col
 #pragma unroll
@@ -1134,10 +1181,10 @@ static hipError_t launch_backward_d(const BwdArgs &a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
-    const int ntile = (a.B + 15) / 16;
-    const size_t lds = (size_t)a.Hkv * 2 * 16 * (D + 8) * sizeof(uint16_t);
-    hipLaunchKernelGGL(k_bwd_dkdv<D>, dim3((unsigned)(a.nblk * ntile)), dim3(64 * a.Hkv), lds,
-                       stream, a);
+    const int64_t ntiles = a.nblk * ((a.B + 15) / 16);
+    const int64_t nwg = (ntiles + 3) / 4 * a.Hkv;  // 4 tiles of one group per workgroup
+    const size_t lds = (size_t)4 * 2 * 16 * (D + 8) * sizeof(uint16_t);
+    hipLaunchKernelGGL(k_bwd_dkdv<D>, dim3((unsigned)nwg), dim3(256), lds, stream, a);
     return hipGetLastError();
 }
 
