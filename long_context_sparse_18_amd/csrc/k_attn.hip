@@ -38,6 +38,29 @@ __device__ __forceinline__ void wave_lds_handoff()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
+// The MFMA A operand V^T[d0 + col][slots] of a [slot][d] bf16 tile in LDS (row stride ld
+// elements, a multiple of 4): 4 bf16 per transposing read (ds_read_b64_tr_b16, gfx950).  Within
+// each 16-lane group, lane i receives element i % 4 of the 8-byte chunks read by lanes
+// i / 4 + {0, 4, 8, 12}; so lane L reads row slot(L / 4), columns d0 + 4 (L % 4) .. +3, and
+// lane col receives the column d0 + col of those four rows.  The two reads cover the slots
+// {4 q4 .. 4 q4 + 3} and {16 + 4 q4 .. 16 + 4 q4 + 3}: the contraction order P^T uses.
+typedef __attribute__((ext_vector_type(4))) short s16x4;
+
+__device__ __forceinline__ bf16x8 vt_fragment(const uint16_t *tile, int ld, int d0)
+{
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    const uint16_t *p0 = tile + (q4 * 4 + (col >> 2)) * ld + d0 + 4 * (col & 3);
+    const uint16_t *p1 = p0 + 16 * ld;
+    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (s16x4 __attribute__((address_space(3))) *)p0);
+    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (s16x4 __attribute__((address_space(3))) *)p1);
+    typedef __attribute__((ext_vector_type(8))) short s16x8;
+    const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    return __builtin_bit_cast(bf16x8, v);
+}
+
 template <int D>
 struct WaveState {
     f32x4 acc[D / 16];  // acc[mt][i] = O^T[d = 16*mt + 4*q + i][head = lane % 16]
@@ -65,18 +88,6 @@ struct SparseTokens {
         const int32_t blk = (e < e_end) ? sel[e] : -1;
         const int64_t s = (int64_t)blk * B + (sl % B);
         valid = blk >= 0 && (int64_t)blk <= c && s <= t;
-        s_ld = valid ? s : t;
-    }
-};
-
-// WindowTokens: the contiguous positions [s0, t].
-struct WindowTokens {
-    int64_t s0, t;
-    __device__ int steps() const { return (int)((t - s0 + kSlots) / kSlots); }
-    __device__ void slot(int step, int sl, int64_t &s_ld, bool &valid) const
-    {
-        const int64_t s = s0 + (int64_t)step * kSlots + sl;
-        valid = s <= t;
         s_ld = valid ? s : t;
     }
 };
@@ -463,29 +474,205 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
         save_state<D>(st, a.state + state_offset(a, r, g));
 }
 
-// Gated sliding-window attention: the same per-(token, group) wave over the contiguous
-// positions [max(0, t - window + 1), t].
-template <int D, bool kGroupPerXcd>
-__global__ __launch_bounds__(512) void k_swa(AttnArgs a)
+typedef __attribute__((ext_vector_type(2))) float f2v;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+
+// Gated sliding-window attention, query-tiled: neighbouring queries share all but one of
+// their window positions, so a workgroup takes 16 consecutive queries of one KV group and each
+// 32-position step of the group's K and V rows is staged once in LDS for all of them.  One wave
+// per head of the group; the wave's arithmetic is the sparse kernel's with the MFMA N
+// dimension taken as the 16 queries of one head instead of the 16 heads of one query:
+//   S^T[pos][query] = K_tile . Q_h^T (K rows from LDS as the A operand),
+//   online softmax per query (= lane % 16), O^T[d][query] += V_tile^T . P^T.
+// Positions outside [t - window + 1, t] of a query are masked.  Group = blockIdx % Hkv, so
+// with Hkv dividing 8 each XCD's L2 holds one group's rows.  The tile is double-buffered and
+// filled by direct global-to-LDS loads (global_load_lds_dwordx4: lane l of an instruction
+// writes 16 bytes at base + 16 l), so the next step's rows stream in while the current step is
+// computed, without holding registers.  A step's tile is 2 x 32 rows of kLd/8 16-byte pieces
+// (a whole number of 64-piece instructions); the pad piece of a row reloads the row's first
+// piece and is never read.
+template <int D>
+__global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
 {
     extern __shared__ __align__(16) uint16_t lds[];
-    const int wave = threadIdx.x >> 6;
+    constexpr int kLd = D + 8;  // row stride (elements): 16-byte aligned rows
+    constexpr int kTile = 2 * kSlots * kLd;  // K then V rows of one step
     const int hpg = a.Hq / a.Hkv;
-    int64_t r;
-    int g;
-    if (!wave_row_group<kGroupPerXcd>(a, r, g))
-        return;
-    const int64_t t = a.q_start + r;
-    const int64_t s0 = t - a.window + 1 > 0 ? t - a.window + 1 : 0;
+    const int g = (int)(blockIdx.x % (unsigned)a.Hkv);
+    const int64_t r0 = (int64_t)(blockIdx.x / (unsigned)a.Hkv) * 16;  // first query row
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nwaves = (int)(blockDim.x >> 6);
+    const int col = lane & 15, q4 = lane >> 4;
+    const int nq = a.rows - r0 < 16 ? (int)(a.rows - r0) : 16;
+    const bool has_head = wave < hpg;
+    const int h = g * hpg + (has_head ? wave : 0);
+    const int64_t t0 = a.q_start + r0;
+    const int64_t t_last = t0 + nq - 1;
+    const int64_t ks0 = t0 - a.window + 1 > 0 ? t0 - a.window + 1 : 0;
+    const int nsteps = (int)((t_last - ks0 + kSlots) / kSlots);
+    const int64_t row_elems = (int64_t)a.Hkv * D;
+    const float neg_inf = -__builtin_inff();
 
+    // Q of head h for the tile's queries (B operand: query col, dims 8 q4 + 32 kk)
     bf16x8 qf[D / 32];
-    load_q<D>(a.q + (r * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (col < nq)
+            v = load16(a.q + ((r0 + col) * a.Hq + h) * D + kk * 32 + q4 * 8);
+        qf[kk] = as_bf16x8(v);
+    }
     WaveState<D> st;
     init_state<D>(st);
-    const WindowTokens src{s0, t};
-    attend_range<D>(Bf16Rows{a.kc + (int64_t)g * D, a.vc + (int64_t)g * D}, a.Hkv, src, qf,
-                    a.scale_log2, lds + wave * kSlots * (D + 4), st);
-    store_row<D>(st, a, r, g, hpg);
+    const int64_t tq = t0 + col;  // this lane's query position
+
+    constexpr int kPpr = kLd / 8;                       // 16-byte pieces per LDS row
+    constexpr int kTilePieces = 2 * kSlots * kPpr;
+    static_assert(kTilePieces % 64 == 0, "whole instructions");
+    // this lane's piece of the wave's first two DMA instructions (the same every step): the
+    // row within the step, K or V, and the element offset within the group's row
+    constexpr int kPre = 2;
+    int dslot[kPre], doff[kPre];
+    bool dv_[kPre];
+#pragma unroll
+    for (int u = 0; u < kPre; ++u) {
+        const int i = wave + u * nwaves;
+        const int pc = (i < kTilePieces / 64 ? i : 0) * 64 + lane;
+        const int which = pc / (kSlots * kPpr);
+        const int rem = pc - which * kSlots * kPpr;
+        const int slot = rem / kPpr, piece = rem - slot * kPpr;
+        dslot[u] = slot;
+        dv_[u] = which != 0;
+        doff[u] = g * D + (piece < D / 8 ? piece : 0) * 8;
+    }
+    auto dma = [&](int step, uint16_t *buf) {
+        const int64_t k0 = ks0 + (int64_t)step * kSlots;
+#pragma unroll
+        for (int u = 0; u < kPre; ++u) {
+            const int i = wave + u * nwaves;
+            if (i < kTilePieces / 64) {
+                int64_t sp = k0 + dslot[u];
+                if (sp > t_last)
+                    sp = t_last;  // a valid row; masked below
+                const uint16_t *src = (dv_[u] ? a.vc : a.kc) + sp * row_elems + doff[u];
+                __builtin_amdgcn_global_load_lds(
+                    (const void __attribute__((address_space(1))) *)src,
+                    (void __attribute__((address_space(3))) *)(buf + i * 64 * 8), 16, 0, 0);
+            }
+        }
+        // small workgroups issue the remaining instructions here
+        for (int i = wave + kPre * nwaves; i < kTilePieces / 64; i += nwaves) {
+            const int pc = i * 64 + lane;
+            const int which = pc / (kSlots * kPpr);
+            const int rem = pc - which * kSlots * kPpr;
+            const int slot = rem / kPpr, piece = rem - slot * kPpr;
+            int64_t sp = k0 + slot;
+            if (sp > t_last)
+                sp = t_last;
+            const uint16_t *src = (which ? a.vc : a.kc) + sp * row_elems + (int64_t)g * D +
+                                  (piece < D / 8 ? piece : 0) * 8;
+            __builtin_amdgcn_global_load_lds(
+                (const void __attribute__((address_space(1))) *)src,
+                (void __attribute__((address_space(3))) *)(buf + i * 64 * 8), 16, 0, 0);
+        }
+    };
+    dma(0, lds);
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
+    __syncthreads();
+
+    for (int step = 0; step < nsteps; ++step) {
+        const int64_t k0 = ks0 + (int64_t)step * kSlots;
+        const bool more = step + 1 < nsteps;
+        if (more)
+            dma(step + 1, lds + ((step + 1) & 1) * kTile);
+        const uint16_t *ks = lds + (step & 1) * kTile;
+        const uint16_t *vs = ks + kSlots * kLd;
+
+        // S^T for positions 0-15 and 16-31 of the tile
+        f32x4 sc[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            sc[hh] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const u32x4 kv =
+                    *reinterpret_cast<const u32x4 *>(ks + (hh * 16 + col) * kLd + kk * 32 + q4 * 8);
+                sc[hh] = mfma_16x16x32(as_bf16x8(kv), qf[kk], sc[hh]);
+            }
+        }
+        // online softmax (base 2) per query; lane holds positions 16 hh + 4 q4 + r of query col;
+        // rel = position - query, in [1 - window, 0] inside the window
+        const int rel0 = (int)(k0 - tq) + q4 * 4;
+        float x[2][4];
+        float mloc = neg_inf;
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) {
+                const int rel = rel0 + hh * 16 + r;
+                const bool ok = col < nq && rel <= 0 && rel > -a.window;
+                x[hh][r] = ok ? sc[hh][r] * a.scale_log2 : neg_inf;
+                mloc = fmaxf(mloc, x[hh][r]);
+            }
+        const float m_new = fmaxf(st.m, max_across_rows(mloc));
+        const bool any = m_new != neg_inf;
+        const float alpha = any ? fast_exp2(st.m - m_new) : 1.0f;
+        float pe[2][4];
+        f2v pv[4];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                pe[hh][r] = any ? fast_exp2(x[hh][r] - m_new) : 0.f;
+        // the weights PV uses are the bf16 ones; normalise by their sum too
+#pragma unroll
+        for (int c = 0; c < 4; ++c)
+            pv[c] = f2v{pe[c >> 1][2 * (c & 1)], pe[c >> 1][2 * (c & 1) + 1]};
+        float psum = 0.f, psum32 = 0.f;
+        u32x4 pw;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+            const bf16x2v b = __builtin_convertvector(pv[c], bf16x2v);
+            pw[c] = __builtin_bit_cast(uint32_t, b);
+            psum += bf16_bits_to_f32(pw[c] & 0xffffu) + bf16_bits_to_f32(pw[c] >> 16);
+            psum32 += pv[c][0] + pv[c][1];
+        }
+        st.l = st.l * alpha + psum;
+        st.l32 = st.l32 * alpha + psum32;
+        st.m = m_new;
+        if (__ballot(alpha != 1.0f)) {  // no lane's maximum moved: nothing to rescale
+#pragma unroll
+            for (int mt = 0; mt < D / 16; ++mt)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    st.acc[mt][r] *= alpha;
+        }
+        const bf16x8 pf = as_bf16x8(pw);
+        // O^T += V^T P^T: A[m = d][k = position perm(8 q4 + j)] from the staged V rows
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt)
+            st.acc[mt] = mfma_16x16x32(vt_fragment(vs, kLd, mt * 16), pf, st.acc[mt]);
+        __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next tile has landed
+        __syncthreads();                 // the next tile is complete; this one is no longer read
+    }
+
+    // lane holds O^T[d = 16 mt + 4 q4 + i][query col] of head h
+    const float l = sum_across_rows(st.l);
+    const float l32 = sum_across_rows(st.l32);
+    if (has_head && col < nq) {
+        const int64_t row = (r0 + col) * a.Hq + h;
+        const float f = sigmoid_f32(bf16_bits_to_f32(a.gate[row])) / l;
+        uint16_t *o = a.out + row * D + q4 * 4;
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt) {
+            uint2 w;
+            w.x = pack_bf16x2(st.acc[mt][0] * f, st.acc[mt][1] * f);
+            w.y = pack_bf16x2(st.acc[mt][2] * f, st.acc[mt][3] * f);
+            *reinterpret_cast<uint2 *>(o + mt * 16) = w;
+        }
+        if (a.lse && q4 == 0)
+            a.lse[row] = (st.m + fast_log2(l32)) * 0.6931471805599453f;
+    }
 }
 
 template <int D, bool kFp8>
@@ -598,7 +785,7 @@ void decode_split_plan(int k, int B, int &nsplit, int &entries_per_split)
     nsplit = (k + per - 1) / per;
 }
 
-template <int D, bool kWindow>
+template <int D>
 static hipError_t launch_prefill_d(const AttnArgs &a, hipStream_t stream)
 {
     // Group-per-XCD mapping whenever the groups divide the 8 XCDs (measured 17 % faster
@@ -608,20 +795,23 @@ static hipError_t launch_prefill_d(const AttnArgs &a, hipStream_t stream)
         const int64_t ntiles = ((int64_t)a.rows + 3) / 4;
         const int64_t nwg = (ntiles + R - 1) / R * 8;
         const size_t lds = (size_t)4 * kSlots * (D + 4) * sizeof(uint16_t);
-        if (kWindow)
-            hipLaunchKernelGGL((k_swa<D, true>), dim3((unsigned)nwg), dim3(256), lds, stream, a);
-        else
-            hipLaunchKernelGGL((k_attn_prefill<D, true>), dim3((unsigned)nwg), dim3(256), lds,
-                               stream, a);
+        hipLaunchKernelGGL((k_attn_prefill<D, true>), dim3((unsigned)nwg), dim3(256), lds, stream,
+                           a);
     } else {
         const size_t lds = (size_t)a.Hkv * kSlots * (D + 4) * sizeof(uint16_t);
-        if (kWindow)
-            hipLaunchKernelGGL((k_swa<D, false>), dim3((unsigned)a.rows), dim3(64 * a.Hkv), lds,
-                               stream, a);
-        else
-            hipLaunchKernelGGL((k_attn_prefill<D, false>), dim3((unsigned)a.rows),
-                               dim3(64 * a.Hkv), lds, stream, a);
+        hipLaunchKernelGGL((k_attn_prefill<D, false>), dim3((unsigned)a.rows), dim3(64 * a.Hkv),
+                           lds, stream, a);
     }
+    return hipGetLastError();
+}
+
+template <int D>
+static hipError_t launch_swa_d(const AttnArgs &a, hipStream_t stream)
+{
+    const int64_t nwg = ((int64_t)a.rows + 15) / 16 * a.Hkv;
+    const size_t lds = (size_t)2 * 2 * kSlots * (D + 8) * sizeof(uint16_t);
+    const int hpg = a.Hq / a.Hkv;
+    hipLaunchKernelGGL(k_swa_tiled<D>, dim3((unsigned)nwg), dim3(64 * hpg), lds, stream, a);
     return hipGetLastError();
 }
 
@@ -645,7 +835,7 @@ static hipError_t launch_prefill_sliced(const AttnArgs &a0, hipStream_t stream)
         a.lse = a0.lse ? a0.lse + r0 * a0.Hq : nullptr;
         for (int sl = 0; sl < a0.nslices; ++sl) {
             a.slice = sl;
-            hipError_t e = launch_prefill_d<D, false>(a, stream);
+            hipError_t e = launch_prefill_d<D>(a, stream);
             if (e != hipSuccess)
                 return e;
         }
@@ -687,9 +877,9 @@ hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream)
         }
     }
     switch (a.d) {
-    case 64: return launch_prefill_d<64, false>(a, stream);
-    case 128: return launch_prefill_d<128, false>(a, stream);
-    case 192: return launch_prefill_d<192, false>(a, stream);
+    case 64: return launch_prefill_d<64>(a, stream);
+    case 128: return launch_prefill_d<128>(a, stream);
+    case 192: return launch_prefill_d<192>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -706,9 +896,9 @@ hipError_t launch_swa(const AttnArgs &a, hipStream_t stream)
     if (!a.q || !a.out || (!a.idx && !a.window))
         return hipErrorInvalidValue;  // never launch without the tensors the kernels touch
     switch (a.d) {
-    case 64: return launch_prefill_d<64, true>(a, stream);
-    case 128: return launch_prefill_d<128, true>(a, stream);
-    case 192: return launch_prefill_d<192, true>(a, stream);
+    case 64: return launch_swa_d<64>(a, stream);
+    case 128: return launch_swa_d<128>(a, stream);
+    case 192: return launch_swa_d<192>(a, stream);
     default: return hipErrorInvalidValue;
     }
 }
@@ -744,8 +934,6 @@ hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream)
 // dP^T = V da^T and K staged for dq^T += K^T dz^T), and k_bwd_dkdv (key-major: a wave per
 // 16-token tile of a block and KV group, walking the tile's query rows in a fixed order, so dK
 // and dV are sums in a fixed order and written once).
-typedef __attribute__((ext_vector_type(4))) short s16x4;
-
 __device__ __forceinline__ f32x4 mfma_16x16x16(s16x4 a, s16x4 b, f32x4 c)
 {
     return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
