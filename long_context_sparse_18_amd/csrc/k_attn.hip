@@ -38,26 +38,28 @@ __device__ __forceinline__ void wave_lds_handoff()
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// The MFMA A operand V^T[d0 + col][slots] of a [slot][d] bf16 tile in LDS (row stride ld
-// elements, a multiple of 4): 4 bf16 per transposing read (ds_read_b64_tr_b16, gfx950).  Within
-// each 16-lane group, lane i receives element i % 4 of the 8-byte chunks read by lanes
-// i / 4 + {0, 4, 8, 12}; so lane L reads row slot(L / 4), columns d0 + 4 (L % 4) .. +3, and
-// lane col receives the column d0 + col of those four rows.  The two reads cover the slots
-// {4 q4 .. 4 q4 + 3} and {16 + 4 q4 .. 16 + 4 q4 + 3}: the contraction order P^T uses.
+// Column reads of a [row][d] bf16 tile in LDS (row stride ld elements, a multiple of 4) by the
+// transposing read ds_read_b64_tr_b16 (gfx950).  Within each 16-lane group, lane i receives
+// element i % 4 of the 8-byte chunks read by lanes i / 4 + {0, 4, 8, 12}; so when lane L reads
+// row 4 q4 + L / 4, columns d0 + 4 (L % 4) .. +3, lane (col, q4) receives
+// tile[4 q4 + j][d0 + col] for j = 0..3: one 16x16x16 MFMA operand quad.
 typedef __attribute__((ext_vector_type(4))) short s16x4;
 
-__device__ __forceinline__ bf16x8 vt_fragment(const uint16_t *tile, int ld, int d0)
+__device__ __forceinline__ s16x4 tr_quad(const uint16_t *tile, int ld, int d0)
 {
     const int lane = threadIdx.x & 63;
     const int col = lane & 15, q4 = lane >> 4;
-    const uint16_t *p0 = tile + (q4 * 4 + (col >> 2)) * ld + d0 + 4 * (col & 3);
-    const uint16_t *p1 = p0 + 16 * ld;
-    const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (s16x4 __attribute__((address_space(3))) *)p0);
-    const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (s16x4 __attribute__((address_space(3))) *)p1);
+    const uint16_t *p = tile + (q4 * 4 + (col >> 2)) * ld + d0 + 4 * (col & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((s16x4 __attribute__((address_space(3))) *)p);
+}
+
+// The MFMA A operand V^T[d0 + col][slots] of a [slot][d] tile: the slots {4 q4 .. 4 q4 + 3}
+// then {16 + 4 q4 .. 16 + 4 q4 + 3}, the contraction order P^T uses.
+__device__ __forceinline__ bf16x8 vt_fragment(const uint16_t *tile, int ld, int d0)
+{
     typedef __attribute__((ext_vector_type(8))) short s16x8;
-    const s16x8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+    const s16x8 v = __builtin_shufflevector(tr_quad(tile, ld, d0), tr_quad(tile + 16 * ld, ld, d0),
+                                            0, 1, 2, 3, 4, 5, 6, 7);
     return __builtin_bit_cast(bf16x8, v);
 }
 
@@ -269,18 +271,8 @@ __device__ __forceinline__ void attend_range(const Rows &rows, int Hkv, const Sr
 
         // O^T += V^T P^T: A[m = d][k = slot perm(8*q4 + j)], slots 4q4+j (j<4), 16+4q4+j-4.
 #pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt) {
-            const uint16_t *vc = vs + mt * 16 + col;
-            u32x4 aw;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int j0 = 2 * jj, j1 = 2 * jj + 1;
-                const int sl0 = j0 < 4 ? q4 * 4 + j0 : 16 + q4 * 4 + (j0 - 4);
-                const int sl1 = j1 < 4 ? q4 * 4 + j1 : 16 + q4 * 4 + (j1 - 4);
-                aw[jj] = (uint32_t)vc[sl0 * kLd] | ((uint32_t)vc[sl1 * kLd] << 16);
-            }
-            st.acc[mt] = mfma_16x16x32(as_bf16x8(aw), pf, st.acc[mt]);
-        }
+        for (int mt = 0; mt < D / 16; ++mt)
+            st.acc[mt] = mfma_16x16x32(vt_fragment(vs, kLd, mt * 16), pf, st.acc[mt]);
     }
 }
 
@@ -1109,18 +1101,8 @@ __device__ __forceinline__ void dq_range(const uint16_t *__restrict__ Kg,
             }
         wave_lds_handoff();
 #pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt) {
-            const uint16_t *kc = ks + mt * 16 + col;
-            u32x4 aw;
-#pragma unroll
-            for (int jj = 0; jj < 4; ++jj) {
-                const int j0 = 2 * jj, j1 = 2 * jj + 1;
-                const int sl0 = j0 < 4 ? q4 * 4 + j0 : 16 + q4 * 4 + (j0 - 4);
-                const int sl1 = j1 < 4 ? q4 * 4 + j1 : 16 + q4 * 4 + (j1 - 4);
-                aw[jj] = (uint32_t)kc[sl0 * kLd] | ((uint32_t)kc[sl1 * kLd] << 16);
-            }
-            acc[mt] = mfma_16x16x32(as_bf16x8(aw), zf, acc[mt]);
-        }
+        for (int mt = 0; mt < D / 16; ++mt)
+            acc[mt] = mfma_16x16x32(vt_fragment(ks, kLd, mt * 16), zf, acc[mt]);
     }
 }
 
@@ -1305,17 +1287,11 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
         }
         const s16x4 pa = pack4_bf16(p[0], p[1], p[2], p[3]);
         const s16x4 za = pack4_bf16(dz[0], dz[1], dz[2], dz[3]);
+        // B[k = head 4 q4 + i][n = dim 16 nt + col] of dA and q, read transposed
 #pragma unroll
         for (int nt = 0; nt < D / 16; ++nt) {
-            const int dcol = nt * 16 + col;
-            const uint16_t *qc = qs + (q4 * 4) * kLd + dcol;
-            const uint16_t *dc = ds + (q4 * 4) * kLd + dcol;
-            const uint64_t qw = (uint64_t)qc[0] | ((uint64_t)qc[kLd] << 16) |
-                                ((uint64_t)qc[2 * kLd] << 32) | ((uint64_t)qc[3 * kLd] << 48);
-            const uint64_t dw = (uint64_t)dc[0] | ((uint64_t)dc[kLd] << 16) |
-                                ((uint64_t)dc[2 * kLd] << 32) | ((uint64_t)dc[3 * kLd] << 48);
-            dv[nt] = mfma_16x16x16(pa, __builtin_bit_cast(s16x4, dw), dv[nt]);
-            dk[nt] = mfma_16x16x16(za, __builtin_bit_cast(s16x4, qw), dk[nt]);
+            dv[nt] = mfma_16x16x16(pa, tr_quad(ds, kLd, nt * 16), dv[nt]);
+            dk[nt] = mfma_16x16x16(za, tr_quad(qs, kLd, nt * 16), dk[nt]);
         }
         if (have_next) {
             stage(nq, nd);
