@@ -233,6 +233,10 @@ sgqa_status sgqa_swa_prefill(const sgqa_dims *dims, const sgqa_bf16 *q, const sg
  * [T][Hq][d], dk / dv [L][Hkv][d] and dgate [T][Hq] are fp32.  nseq is 1.
  *   workspace [dev] >= sgqa_workspace_bytes(SGQA_OP_ATTN_BACKWARD, dims, 1, T, L),
  *                   256-byte aligned
+ *   dkdv_row_slice  query rows per dk / dv pass: 0 picks it from the sizes (rows whose q
+ *                   and dout take about 192 MiB), else a positive multiple of 32 (anything
+ *                   else is SGQA_ERR_SHAPE).  The passes run from the last rows down and
+ *                   every sum keeps one order, so the results do not depend on it.
  */
 sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
                                       const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
@@ -240,7 +244,7 @@ sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
                                       int32_t T, int64_t L, float softmax_scale, const float *lse,
                                       const sgqa_bf16 *dout, float *dq, float *dk, float *dv,
                                       float *dgate, void *workspace, size_t workspace_bytes,
-                                      void *stream);
+                                      int64_t dkdv_row_slice, void *stream);
 
 /*
  * FP8 storage for the decode path.  The pages give FP8 (e4m3) only for the

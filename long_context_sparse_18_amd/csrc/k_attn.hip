@@ -1154,9 +1154,11 @@ __global__ __launch_bounds__(512) void k_bwd_dq(BwdArgs a)
 // products dV += P^T dA and dK += dz^T q (M = tokens, K = heads); q and dA sit in LDS, where
 // the B operands are read.  A workgroup takes 4 tiles of one group (group = blockIdx % Hkv, so
 // with Hkv dividing 8 each XCD's L2 serves one group's rows), and every wave walks its rows
-// from the last one down: rows select about the same number of blocks whatever the block, so
-// concurrent waves stay in the same window of rows and share those rows' q and dA in L2.  The
-// next row's q and dA are loaded while the current one is computed.
+// from the last one down.  One launch covers the rows [row_lo, row_hi) only: the launcher runs
+// the slices from the last one down, so that the q and dA rows in use at any time fit in the
+// memory-side cache, and each wave carries its sums over from the previous slice through the
+// fp32 dK / dV outputs (same summation order as a single sweep).  The next row's q and dA are
+// loaded while the current one is computed.
 template <int D>
 __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
 {
@@ -1191,23 +1193,35 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
         vB[kk] = as_bf16x8(load16(a.vc + sc_tok * row_elems + (int64_t)g * D + kk * 32 + q4 * 8));
     }
     f32x4 dk[D / 16], dv[D / 16];
-#pragma unroll
-    for (int nt = 0; nt < D / 16; ++nt) {
-        dk[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        dv[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
 
     // the block's rows, last first (uniform across the wave)
     const uint32_t *brow = a.bits + j * a.bits_ld;
-    const int64_t first_row = j * a.B - a.q_start;  // no row before it can select block j
-    const int64_t w0 = first_row > 0 ? first_row >> 5 : 0;
-    int64_t w = (((int64_t)a.rows + 31) >> 5) - 1;
-    uint32_t word = w >= w0 ? brow[w] : 0u;
+    // this launch's rows [row_lo, row_hi) (row_lo a multiple of 32); none before first_row
+    // can select block j
+    const int64_t first_row = j * a.B - a.q_start;
+    const int64_t w_lo = a.row_lo >> 5;
+    const int64_t w0 = first_row > 0 && (first_row >> 5) > w_lo ? first_row >> 5 : w_lo;
+    // The bitmap words are read 64 at a time (lane l: word top - l), and the wave finds the
+    // non-zero ones by ballot, so finding the next row costs no dependent load.
+    int64_t top = ((a.row_hi + 31) >> 5) - 1;  // highest word of the current window
+    uint32_t lw = top - lane >= w0 ? brow[top - lane] : 0u;
+    uint64_t nz = __ballot(lw != 0u);
+    uint32_t word = 0u;
+    int64_t w = top;
     auto next_row = [&](int64_t &r) -> bool {
         while (word == 0u) {
-            if (--w < w0)
-                return false;
-            word = brow[w];
+            if (nz == 0ull) {
+                top -= 64;
+                if (top < w0)
+                    return false;
+                lw = top - lane >= w0 ? brow[top - lane] : 0u;
+                nz = __ballot(lw != 0u);
+                continue;
+            }
+            const int l = __builtin_ctzll(nz);  // the highest non-zero word left
+            nz &= nz - 1ull;
+            word = (uint32_t)__builtin_amdgcn_readlane((int)lw, l);
+            w = top - l;
         }
         const int b = 31 - __builtin_clz(word);
         word &= ~(1u << b);
@@ -1215,25 +1229,21 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
         return true;
     };
     // q and dA of the group's heads of row r (head col, dims 8 q4 + 32 kk), lse / D of heads
-    // 4 q4 + i
-    auto fetch = [&](int64_t r, u32x4 (&qa)[D / 32], u32x4 (&da)[D / 32], float (&l2)[4],
-                     float (&dsm)[4]) {
-        const int64_t head0 = r * a.Hq + (int64_t)g * hpg;
+    // 4 q4 + i.  The loads are unconditional, so none of them makes the wave wait before the
+    // values are used: lanes past the group's heads re-read its last head, whose P and dz are
+    // masked to zero (so those staged rows meet only zero weights).
+    // lse and D come one per lane (head col) and reach the lanes holding heads 4 q4 + i by
+    // shuffles where they are used.
+    auto fetch = [&](int64_t r, u32x4 (&qa)[D / 32], u32x4 (&da)[D / 32], float &l1,
+                     float &ds1) {
+        const int64_t hr = r * a.Hq + (int64_t)g * hpg + (col < hpg ? col : hpg - 1);
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
-            qa[kk] = u32x4{0u, 0u, 0u, 0u};
-            da[kk] = u32x4{0u, 0u, 0u, 0u};
-            if (col < hpg) {
-                qa[kk] = load16(a.q + (head0 + col) * D + kk * 32 + q4 * 8);
-                da[kk] = load16(a.da + (head0 + col) * D + kk * 32 + q4 * 8);
-            }
+            qa[kk] = load16(a.q + hr * D + kk * 32 + q4 * 8);
+            da[kk] = load16(a.da + hr * D + kk * 32 + q4 * 8);
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int h = q4 * 4 + i;
-            l2[i] = h < hpg ? a.lse[head0 + h] * kLog2e : 0.f;
-            dsm[i] = h < hpg ? a.dsum[head0 + h] : 0.f;
-        }
+        l1 = a.lse[hr];  // natural log; scaled to base 2 where it is used
+        ds1 = a.dsum[hr];
     };
     auto stage = [&](const u32x4 (&qa)[D / 32], const u32x4 (&da)[D / 32]) {
         wave_lds_handoff();
@@ -1251,18 +1261,34 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
 
     int64_t r;
     bool have = next_row(r);
-    float lse2[4], dsum[4];
-    if (have) {
+    if (!have)
+        return;  // no row of this slice selects the block: its sums stay as they are
+    float lse1, ds1;  // the staged row's lse and D of head col
+    {
         u32x4 qa[D / 32], da[D / 32];
-        fetch(r, qa, da, lse2, dsum);
+        fetch(r, qa, da, lse1, ds1);
         stage(qa, da);
     }
+    // continue the sums of the slices already done (the launcher zeroes dK and dV first)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = q4 * 4 + i;
+        const int64_t base = ((s0 + (tok < ntok ? tok : 0)) * a.Hkv + g) * D;
+#pragma unroll
+        for (int nt = 0; nt < D / 16; ++nt) {
+            dk[nt][i] = tok < ntok ? a.dk[base + nt * 16 + col] : 0.f;
+            dv[nt][i] = tok < ntok ? a.dv[base + nt * 16 + col] : 0.f;
+        }
+    }
+    // Let these loads land here: the wait the compiler would otherwise put before the first
+    // product in the loop (it cannot tell they finished) would also drain each row's prefetch.
+    __builtin_amdgcn_s_waitcnt(0);
 #pragma unroll 1
     while (have) {
         int64_t rn = 0;
         const bool have_next = next_row(rn);
         u32x4 nq[D / 32], nd[D / 32];
-        float nl[4], ns[4];
+        float nl = 0.f, ns = 0.f;
         if (have_next)
             fetch(rn, nq, nd, nl, ns);
         const int64_t t = a.q_start + r;
@@ -1282,8 +1308,9 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const bool ok = tok_ok && q4 * 4 + i < hpg;
-            p[i] = ok ? fast_exp2(sc[i] * a.scale_log2 - lse2[i]) : 0.f;
-            dz[i] = p[i] * (dp[i] - dsum[i]) * a.scale;
+            const float lse_i = __shfl(lse1, q4 * 4 + i), ds_i = __shfl(ds1, q4 * 4 + i);
+            p[i] = ok ? fast_exp2(sc[i] * a.scale_log2 - lse_i * kLog2e) : 0.f;
+            dz[i] = p[i] * (dp[i] - ds_i) * a.scale;
         }
         const s16x4 pa = pack4_bf16(p[0], p[1], p[2], p[3]);
         const s16x4 za = pack4_bf16(dz[0], dz[1], dz[2], dz[3]);
@@ -1295,11 +1322,8 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
         }
         if (have_next) {
             stage(nq, nd);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                lse2[i] = nl[i];
-                dsum[i] = ns[i];
-            }
+            lse1 = nl;
+            ds1 = ns;
         }
         r = rn;
         have = have_next;
@@ -1327,6 +1351,16 @@ size_t attn_backward_workspace(int64_t T, int Hq, int d, int64_t nblk)
     return da + ds + (size_t)nblk * bits_ld * 4;
 }
 
+// Query rows per dK / dV launch: a multiple of 32 (one bitmap word) whose q and dA take about
+// 192 MiB, inside the 256 MiB memory-side cache (at 64 heads of 192: 4096 rows; 512 to 8192
+// rows measured within 5 % of it at 128K, one pass over all rows 9 % slower).
+static int64_t bwd_row_slice(int Hq, int d)
+{
+    const int64_t per_row = (int64_t)Hq * d * 2 * 2;
+    const int64_t rows = ((int64_t)192 << 20) / per_row / 32 * 32;
+    return rows > 32 ? rows : 32;
+}
+
 template <int D>
 static hipError_t launch_backward_d(const BwdArgs &a, hipStream_t stream)
 {
@@ -1345,11 +1379,28 @@ static hipError_t launch_backward_d(const BwdArgs &a, hipStream_t stream)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
+    // dK / dV: zeroed, then one launch per slice of rows, last slice first
+    const int64_t nkv = a.L * a.Hkv * D;
+    const unsigned zg = (unsigned)(nkv < 65536 * 256 ? (nkv + 255) / 256 : 65536);
+    hipLaunchKernelGGL(k_bwd_zero, dim3(zg), dim3(256), 0, stream, (uint32_t *)a.dk, nkv);
+    hipLaunchKernelGGL(k_bwd_zero, dim3(zg), dim3(256), 0, stream, (uint32_t *)a.dv, nkv);
+    e = hipGetLastError();
+    if (e != hipSuccess)
+        return e;
+    const int64_t slice = a.row_slice > 0 ? a.row_slice : bwd_row_slice(a.Hq, D);
     const int64_t ntiles = a.nblk * ((a.B + 15) / 16);
     const int64_t nwg = (ntiles + 3) / 4 * a.Hkv;  // 4 tiles of one group per workgroup
     const size_t lds = (size_t)4 * 2 * 16 * (D + 8) * sizeof(uint16_t);
-    hipLaunchKernelGGL(k_bwd_dkdv<D>, dim3((unsigned)nwg), dim3(256), lds, stream, a);
-    return hipGetLastError();
+    for (int64_t lo = ((int64_t)a.rows - 1) / slice * slice; lo >= 0; lo -= slice) {
+        BwdArgs s = a;
+        s.row_lo = lo;
+        s.row_hi = lo + slice < a.rows ? lo + slice : a.rows;
+        hipLaunchKernelGGL(k_bwd_dkdv<D>, dim3((unsigned)nwg), dim3(256), lds, stream, s);
+        e = hipGetLastError();
+        if (e != hipSuccess)
+            return e;
+    }
+    return hipSuccess;
 }
 
 hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t stream)

@@ -754,7 +754,7 @@ sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
                                       int32_t T, int64_t L, float softmax_scale, const float *lse,
                                       const sgqa_bf16 *dout, float *dq, float *dk, float *dv,
                                       float *dgate, void *workspace, size_t workspace_bytes,
-                                      void *stream)
+                                      int64_t dkdv_row_slice, void *stream)
 {
     sgqa_status st = check_dims(dims, true, false);
     if (st != SGQA_OK)
@@ -767,6 +767,9 @@ sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
                     (long long)L);
     if (!std::isfinite(softmax_scale))
         return fail(SGQA_ERR_SHAPE, "softmax_scale must be finite");
+    if (dkdv_row_slice < 0 || dkdv_row_slice % 32 != 0)
+        return fail(SGQA_ERR_SHAPE, "dkdv_row_slice %lld must be 0 or a positive multiple of 32",
+                    (long long)dkdv_row_slice);
     if (T == 0 || L == 0)
         return ok();
     if (!q || !k_cache || !v_cache || !gate || !idx || !lse || !dout || !dq || !dk || !dv ||
@@ -804,6 +807,7 @@ sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
     a.dk = dk;
     a.dv = dv;
     a.dgate = dgate;
+    a.row_slice = dkdv_row_slice;
     a.nblk = ceil_div(L, dims->block_size);
     a.bits_ld = ((((int64_t)T + 31) / 32) + 3) / 4 * 4;
     char *w = static_cast<char *>(workspace);

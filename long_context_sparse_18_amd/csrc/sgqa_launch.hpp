@@ -160,6 +160,8 @@ struct BwdArgs {
     uint32_t *bits;                                   // workspace: [nblk][bits_ld] row bitmap
     int64_t bits_ld;
     int64_t nblk;
+    int64_t row_slice;                                // rows per dK / dV launch (0: automatic)
+    int64_t row_lo, row_hi;                           // dK / dV launch: rows of this slice
 };
 hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t stream);
 size_t attn_backward_workspace(int64_t T, int Hq, int d, int64_t nblk);

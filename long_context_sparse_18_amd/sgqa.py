@@ -85,7 +85,7 @@ def load():
                                                 ctypes.c_float, p, p, p, sz, p]
     lib.sgqa_sparse_attn_backward.restype = st
     lib.sgqa_sparse_attn_backward.argtypes = [dp, p, p, p, p, p, i64, i32, i64, ctypes.c_float, p,
-                                              p, p, p, p, p, p, sz, p]
+                                              p, p, p, p, p, p, sz, i64, p]
     lib.sgqa_workspace_bytes.restype = sz
     lib.sgqa_workspace_bytes.argtypes = [ctypes.c_int, dp, i32, i32, i64]
     lib.sgqa_status_string.restype = ctypes.c_char_p
@@ -286,9 +286,10 @@ def sparse_attn_decode_fp8(shape: LayerShape, q, k_codes, v_codes, k_scales, v_s
 
 def sparse_attn_backward(shape: LayerShape, q, k_cache, v_cache, gate, idx, q_start: int, L: int,
                          softmax_scale: float, lse, dout, dq, dk, dv, dgate, workspace=None,
-                         stream=None):
+                         stream=None, dkdv_row_slice: int = 0):
     """Backward of sparse_attn_prefill with idx fixed: fp32 dq [T, Hq, d], dk / dv [L, Hkv, d]
-    and dgate [T, Hq] from dout [T, Hq, d] and the forward's lse."""
+    and dgate [T, Hq] from dout [T, Hq, d] and the forward's lse.  ``dkdv_row_slice``: query
+    rows per dk / dv pass (0 = chosen from the sizes; else a multiple of 32)."""
     _need_cuda(q, k_cache, v_cache, gate, idx, lse, dout, dq, dk, dv, dgate, workspace)
     T = q.shape[0]
     if workspace is None:
@@ -299,4 +300,5 @@ def sparse_attn_backward(shape: LayerShape, q, k_cache, v_cache, gate, idx, q_st
                                            _ptr(gate), _ptr(idx), q_start, T, L, softmax_scale,
                                            _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
                                            _ptr(dv), _ptr(dgate), _ptr(workspace),
-                                           workspace.numel(), _stream(stream, q)))
+                                           workspace.numel(), dkdv_row_slice,
+                                           _stream(stream, q)))

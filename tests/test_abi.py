@@ -195,10 +195,10 @@ def test_backward_validation():
     need = lib.sgqa_workspace_bytes(sgqa.OP_ATTN_BACKWARD, ctypes.byref(d), 1, 64, 1024)
     assert need > 0
 
-    def call(q=FAKE, lse=FAKE, T=64, L=1024, q_start=0, ws=FAKE, wsb=need):
+    def call(q=FAKE, lse=FAKE, T=64, L=1024, q_start=0, ws=FAKE, wsb=need, slice_=0):
         return lib.sgqa_sparse_attn_backward(ctypes.byref(d), q, FAKE, FAKE, FAKE, FAKE, q_start, T,
                                              L, 0.07, lse, FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb,
-                                             None)
+                                             slice_, None)
 
     assert call(q=None) == sgqa.ERR_NULL
     assert call(lse=None) == sgqa.ERR_NULL
@@ -206,7 +206,10 @@ def test_backward_validation():
     assert call(T=-1) == sgqa.ERR_SHAPE
     assert call(wsb=need - 1) == sgqa.ERR_WORKSPACE
     assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == sgqa.ERR_SHAPE
+    assert call(slice_=16) == sgqa.ERR_SHAPE      # dk / dv row slices are whole bitmap words
+    assert call(slice_=-32) == sgqa.ERR_SHAPE
     assert call(T=0) == sgqa.OK
+    assert call(T=0, slice_=64) == sgqa.OK
     assert lib.sgqa_workspace_bytes(sgqa.OP_ATTN_BACKWARD, ctypes.byref(d), 2, 64, 1024) == 0
 
 
