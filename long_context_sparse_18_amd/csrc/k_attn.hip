@@ -74,25 +74,76 @@ struct WaveState {
 // Where the tokens of one query come from, 32 slots per step.
 // SparseTokens: the selected blocks idx[e_begin, e_end) of a query at t (own block c);
 // slots beyond t, -1 entries and ids outside [0, c] are invalid.
+// Selection entries a wave keeps in its LDS window.
+constexpr int kWin = 256;
+
+// The tokens a wave attends: the selected blocks sel[e_begin, e_end) of query position t (own
+// block c), kSlots tokens per step.  Each step's entries come from the wave's LDS window `win`,
+// refilled by one coalesced read of the next kWin entries only when a step runs past it, so the
+// gathers of a step never wait on a global load of its entries.
 struct SparseTokens {
     const int32_t *sel;
     int e_begin, e_end;
     int64_t t, c;
     int B;
+    int32_t *win;
     __device__ int steps() const
     {
         const int eps = kSlots / B;
         return (e_end - e_begin + eps - 1) / eps;
     }
-    __device__ void slot(int step, int sl, int64_t &s_ld, bool &valid) const
+    // Block of slot sl at step `step` (-1 past e_end); wbase = first entry in the window
+    // (start it below any entry, e.g. INT_MIN / 2).  Uniform across the wave except for sl.
+    __device__ int32_t block(int step, int sl, int &wbase) const
     {
-        const int e = e_begin + step * (kSlots / B) + sl / B;
-        const int32_t blk = (e < e_end) ? sel[e] : -1;
+        const int e0 = e_begin + step * (kSlots / B);
+        if (e0 + kSlots / B > wbase + kWin) {
+            const int lane = threadIdx.x & 63;
+            int32_t v[kWin / 64];
+#pragma unroll
+            for (int j = 0; j < kWin / 64; ++j) {  // in-range reads, issued together
+                const int e = e0 + lane + 64 * j;
+                v[j] = sel[e < e_end ? e : e_end - 1];
+                v[j] = e < e_end ? v[j] : -1;
+            }
+            wave_lds_handoff();
+#pragma unroll
+            for (int j = 0; j < kWin / 64; ++j)
+                win[lane + 64 * j] = v[j];
+            wave_lds_handoff();
+            wbase = e0;
+        }
+        return win[e0 - wbase + sl / B];
+    }
+    // Token of slot sl: clamped load position + validity.
+    __device__ void slot(int step, int sl, int &wbase, int64_t &s_ld, bool &valid) const
+    {
+        const int32_t blk = block(step, sl, wbase);
         const int64_t s = (int64_t)blk * B + (sl % B);
         valid = blk >= 0 && (int64_t)blk <= c && s <= t;
         s_ld = valid ? s : t;
     }
 };
+
+// A wave's V (or K) staging buffer of the sparse kernels: kSlots rows of D + 8 bf16 (elements).
+constexpr int attn_vbuf_elems(int D)
+{
+    return kSlots * (D + 8);
+}
+
+// LDS bytes per wave of the sparse kernels: V buffer plus the entry window.
+constexpr size_t attn_wave_lds(int D)
+{
+    return (size_t)attn_vbuf_elems(D) * sizeof(uint16_t) + kWin * sizeof(int32_t);
+}
+
+// This wave's entry window: after the workgroup's V buffers.
+template <int D>
+__device__ __forceinline__ int32_t *entry_window(uint16_t *lds)
+{
+    const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
+    return reinterpret_cast<int32_t *>(lds + nw * attn_vbuf_elems(D)) + wave * kWin;
+}
 
 // Where the K/V rows of one KV group g come from.  Bf16Rows: Kg/Vg point at element
 // (token 0, group g, dim 0) of a bf16 cache; rows are Hkv*D elements apart.
@@ -109,29 +160,30 @@ struct Fp8Rows {
 };
 
 // Attend one wave's (token, group) over the tokens of `src`, reading rows from `rows`.
-// `vs` is this wave's LDS buffer [kSlots][D + 4].  With FP8 rows the query fragments must be
-// in the permuted dim order of load_q_perm: K codes are read 16 at a time (dims
-// [64 k2 + 16 q4, +16)) and feed two MFMA steps; each row's K scale multiplies its logits and
-// its V scale its softmax weight, so the products run on exact bf16 copies of the codes.
+// `vs` is this wave's LDS buffer [kSlots][D + 8].  Per 32-slot step the K rows go straight into
+// MFMA A operands and the V rows are staged in `vs` and read transposed.  With FP8 rows the
+// query fragments must be in the permuted dim order of load_q_perm: K codes are read 16 at a
+// time (dims [64 k2 + 16 q4, +16)) and feed two MFMA steps; V codes are converted to bf16
+// while staged; each row's K scale multiplies its logits and its V scale its softmax weight,
+// so the products run on exact bf16 copies of the codes.
 template <int D, typename Src, typename Rows>
 __device__ __forceinline__ void attend_range(const Rows &rows, int Hkv, const Src &src,
                                              const bf16x8 (&qf)[D / 32], float scale_log2,
                                              uint16_t *vs, WaveState<D> &st)
 {
-    constexpr int kLd = D + 4;         // LDS row stride in elements (bytes = 8 mod 32)
-    constexpr int kPieces = D / 8;     // 16-byte pieces per row
-    constexpr int kVChunks = D / 16;   // V pieces per lane per step (32 * kPieces / 64)
+    constexpr int kLd = D + 8;  // LDS row stride in elements (conflict-free transposing reads)
     const int lane = threadIdx.x & 63;
     const int col = lane & 15, q4 = lane >> 4;
     const int64_t row_elems = (int64_t)Hkv * D;
     const float neg_inf = -__builtin_inff();
     const int nsteps = src.steps();
+    int wbase = -(1 << 30);  // empty window
 
     for (int step = 0; step < nsteps; ++step) {
         // Token of slot (lane & 31): clamped load position + validity.
         int64_t s_ld;
         bool valid;
-        src.slot(step, lane & 31, s_ld, valid);
+        src.slot(step, lane & 31, wbase, s_ld, valid);
         const uint64_t vmask = __ballot(valid);
         const int s_lo = (int)(s_ld & 0xffffffff), s_hi = (int)(s_ld >> 32);
 
@@ -156,10 +208,10 @@ __device__ __forceinline__ void attend_range(const Rows &rows, int Hkv, const Sr
                     kv[h][kk] = load16(kr + kk * 32);
             }
         }
-        // V pieces: flat piece f = lane + 64*ci covers slot f / pieces, piece f % pieces
+        // V pieces: flat piece f = lane + 64 ci covers slot f / pieces, piece f % pieces
         // (pieces of 8 bf16 values, or of 16 FP8 codes).
-        constexpr int kVPieces = Rows::kFp8 ? D / 16 : kPieces;
-        constexpr int kVLoads = Rows::kFp8 ? D / 32 : kVChunks;
+        constexpr int kVPieces = Rows::kFp8 ? D / 16 : D / 8;
+        constexpr int kVLoads = Rows::kFp8 ? D / 32 : D / 16;
         u32x4 vv[kVLoads];
 #pragma unroll
         for (int ci = 0; ci < kVLoads; ++ci) {
@@ -246,7 +298,7 @@ __device__ __forceinline__ void attend_range(const Rows &rows, int Hkv, const Sr
         pw[3] = pack_bf16x2(p[1][2], p[1][3]);
         const bf16x8 pf = as_bf16x8(pw);
 
-        // Stage V rows in LDS (row stride kLd elements, 8-byte aligned).
+        // Stage V rows in LDS (row stride kLd elements, 16-byte aligned rows).
         wave_lds_handoff();
 #pragma unroll
         for (int ci = 0; ci < kVLoads; ++ci) {
@@ -456,9 +508,9 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
         init_state<D>(st);
     else
         load_state<D>(st, a.state + state_offset(a, r, g));
-    const SparseTokens src{a.idx + r * a.k, e_lo, e_hi, t, c, a.B};
+    const SparseTokens src{a.idx + r * a.k, e_lo, e_hi, t, c, a.B, entry_window<D>(lds)};
     attend_range<D>(Bf16Rows{a.kc + (int64_t)g * D, a.vc + (int64_t)g * D}, a.Hkv, src, qf,
-                    a.scale_log2, lds + wave * kSlots * (D + 4), st);
+                    a.scale_log2, lds + wave * attn_vbuf_elems(D), st);
 
     if (a.slice + 1 >= a.nslices)
         store_row<D>(st, a, r, g, hpg);
@@ -692,8 +744,8 @@ __global__ __launch_bounds__(512) void k_attn_decode_part(AttnArgs a)
     init_state<D>(st);
     const int64_t base = (int64_t)s * a.cache_seq_stride + (int64_t)g * D;
     if (e0 < e1) {
-        const SparseTokens src{a.idx + (int64_t)s * a.k, e0, e1, t, c, a.B};
-        uint16_t *vs = lds + wave * kSlots * (D + 4);
+        const SparseTokens src{a.idx + (int64_t)s * a.k, e0, e1, t, c, a.B, entry_window<D>(lds)};
+        uint16_t *vs = lds + wave * attn_vbuf_elems(D);
         if constexpr (kFp8) {
             const int64_t sb = (int64_t)s * a.scale_seq_stride * a.Hkv + g;
             attend_range<D>(Fp8Rows{a.kq + base, a.vq + base, a.ksc + sb, a.vsc + sb}, a.Hkv,
@@ -786,11 +838,11 @@ static hipError_t launch_prefill_d(const AttnArgs &a, hipStream_t stream)
         const int R = 8 / a.Hkv;
         const int64_t ntiles = ((int64_t)a.rows + 3) / 4;
         const int64_t nwg = (ntiles + R - 1) / R * 8;
-        const size_t lds = (size_t)4 * kSlots * (D + 4) * sizeof(uint16_t);
+        const size_t lds = (size_t)4 * attn_wave_lds(D);
         hipLaunchKernelGGL((k_attn_prefill<D, true>), dim3((unsigned)nwg), dim3(256), lds, stream,
                            a);
     } else {
-        const size_t lds = (size_t)a.Hkv * kSlots * (D + 4) * sizeof(uint16_t);
+        const size_t lds = (size_t)a.Hkv * attn_wave_lds(D);
         hipLaunchKernelGGL((k_attn_prefill<D, false>), dim3((unsigned)a.rows), dim3(64 * a.Hkv),
                            lds, stream, a);
     }
@@ -838,7 +890,7 @@ static hipError_t launch_prefill_sliced(const AttnArgs &a0, hipStream_t stream)
 template <int D>
 static hipError_t launch_decode_d(const AttnArgs &a, hipStream_t stream)
 {
-    const size_t lds = (size_t)a.Hkv * kSlots * (D + 4) * sizeof(uint16_t);
+    const size_t lds = (size_t)a.Hkv * attn_wave_lds(D);
     if (a.kq)
         hipLaunchKernelGGL((k_attn_decode_part<D, true>), dim3((unsigned)a.nsplit, (unsigned)a.rows),
                            dim3(64 * a.Hkv), lds, stream, a);
@@ -986,11 +1038,12 @@ __device__ __forceinline__ float dsum_range(const uint16_t *__restrict__ Kg,
     const int col = lane & 15, q4 = lane >> 4;
     const int64_t row_elems = (int64_t)Hkv * D;
     const int nsteps = src.steps();
+    int wbase = -(1 << 30);  // empty window
     float part = 0.f;
     for (int step = 0; step < nsteps; ++step) {
         int64_t s_ld;
         bool valid;
-        src.slot(step, lane & 31, s_ld, valid);
+        src.slot(step, lane & 31, wbase, s_ld, valid);
         const uint64_t vmask = __ballot(valid);
         const int s_lo = (int)(s_ld & 0xffffffff), s_hi = (int)(s_ld >> 32);
         u32x4 kv[2][D / 32], vv[2][D / 32];
@@ -1035,15 +1088,16 @@ __device__ __forceinline__ void dq_range(const uint16_t *__restrict__ Kg,
                                          float lse2, float dsum, uint16_t *ks,
                                          f32x4 (&acc)[D / 16])
 {
-    constexpr int kLd = D + 4;
+    constexpr int kLd = D + 8;
     const int lane = threadIdx.x & 63;
     const int col = lane & 15, q4 = lane >> 4;
     const int64_t row_elems = (int64_t)Hkv * D;
     const int nsteps = src.steps();
+    int wbase = -(1 << 30);  // empty window
     for (int step = 0; step < nsteps; ++step) {
         int64_t s_ld;
         bool valid;
-        src.slot(step, lane & 31, s_ld, valid);
+        src.slot(step, lane & 31, wbase, s_ld, valid);
         const uint64_t vmask = __ballot(valid);
         const int s_lo = (int)(s_ld & 0xffffffff), s_hi = (int)(s_ld >> 32);
         u32x4 kv[2][D / 32], vv[2][D / 32];
@@ -1125,7 +1179,7 @@ __global__ __launch_bounds__(512) void k_bwd_dq(BwdArgs a)
     load_q<D>(a.q + head0 * D, hpg, qf);
     load_q<D>(a.da + head0 * D, hpg, daf);
     const float lse2 = col < hpg ? a.lse[head0 + col] * kLog2e : 0.f;
-    const SparseTokens src{a.idx + r * a.k, 0, nvalid, t, c, a.B};
+    const SparseTokens src{a.idx + r * a.k, 0, nvalid, t, c, a.B, entry_window<D>(lds)};
     // D = sum_s P_s dP_s (so that dG = D (1 - sigmoid(G)) and the dz of the row sum to zero)
     const float dsum = sum_across_rows(dsum_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D,
                                                      a.Hkv, src, qf, daf, a.scale_log2, lse2));
@@ -1139,7 +1193,7 @@ __global__ __launch_bounds__(512) void k_bwd_dq(BwdArgs a)
     for (int mt = 0; mt < D / 16; ++mt)
         acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     dq_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D, a.Hkv, src, qf, daf, a.scale_log2,
-                lse2, dsum, lds + wave * kSlots * (D + 4), acc);
+                lse2, dsum, lds + wave * attn_vbuf_elems(D), acc);
     if (col < hpg) {
         float *dst = a.dq + (head0 + col) * D + q4 * 4;
 #pragma unroll
@@ -1369,10 +1423,10 @@ static hipError_t launch_backward_d(const BwdArgs &a, hipStream_t stream)
         const int R = 8 / a.Hkv;
         const int64_t ntiles = ((int64_t)a.rows + 3) / 4;
         const int64_t nwg = (ntiles + R - 1) / R * 8;
-        const size_t lds = (size_t)4 * kSlots * (D + 4) * sizeof(uint16_t);
+        const size_t lds = (size_t)4 * attn_wave_lds(D);
         hipLaunchKernelGGL((k_bwd_dq<D, true>), dim3((unsigned)nwg), dim3(256), lds, stream, a);
     } else {
-        const size_t lds = (size_t)a.Hkv * kSlots * (D + 4) * sizeof(uint16_t);
+        const size_t lds = (size_t)a.Hkv * attn_wave_lds(D);
         hipLaunchKernelGGL((k_bwd_dq<D, false>), dim3((unsigned)a.rows), dim3(64 * a.Hkv), lds,
                            stream, a);
     }
