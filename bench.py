@@ -397,6 +397,48 @@ def cpu_baseline(pre, rows: int, seed: int = 0):
                        f"{t3 - t2:.2f} s), extrapolated to all rows")}
 
 
+def measure_peaks():
+    """Measured machine peaks for the rooflines: dense bf16 MFMA (a loop of independent
+    32x32x16 products in every SIMD) and streaming HBM reads (a 4 GiB buffer read once per
+    pass), each checked against its closed-form result."""
+    import torch
+    from long_context_sparse_18_amd import sgqa
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    waves, iters = cus * 4 * 8, 4096
+    sink = torch.empty(waves, dtype=torch.float32, device="cuda")
+    sgqa.probe_mfma_bf16(sink, iters)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    mfma_tflops = 0.0
+    for _ in range(3):
+        e0.record()
+        sgqa.probe_mfma_bf16(sink, iters)
+        e1.record()
+        torch.cuda.synchronize()
+        mfma_tflops = max(mfma_tflops,
+                          waves * iters * 8 * 32768 / (e0.elapsed_time(e1) / 1e3) / 1e12)
+    if not bool(torch.all(sink == 2048.0 * iters)):
+        raise RuntimeError("MFMA probe returned a wrong result")
+    nbytes = 4 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    best = 0.0
+    for blocks in (cus * 8, cus * 16, cus * 32):
+        part = torch.empty(blocks, dtype=torch.int32, device="cuda")
+        sgqa.probe_read(buf, part)
+        e0.record()
+        for _ in range(5):
+            sgqa.probe_read(buf, part)
+        e1.record()
+        torch.cuda.synchronize()
+        if int(part.to(torch.int64).sum().item()) & 0xFFFFFFFF != (nbytes // 4) & 0xFFFFFFFF:
+            raise RuntimeError("read probe returned a wrong sum")
+        best = max(best, 5 * nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9)
+    del buf
+    torch.cuda.empty_cache()
+    return {"mfma_bf16_tflops": mfma_tflops, "hbm_read_GBps": best,
+            "method": f"{waves} waves x {iters} x 8 bf16 32x32x16 MFMA (best of 3); 4 GiB "
+                      "streamed read, best of 8/16/32 workgroups per CU"}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -408,6 +450,8 @@ def main():
     ap.add_argument("--no-coverage", action="store_true")
     ap.add_argument("--no-prefill", action="store_true",
                     help="time only the decode workload (for profiling runs)")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the measured MFMA / HBM-read peak probes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 1 GiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -442,6 +486,11 @@ def main():
             f"{dec['fp8']['us_attn']:.1f}), {dec['fp8']['gbs']:.0f} GB/s")
         return
 
+    peaks = None
+    if not args.no_peaks:
+        peaks = measure_peaks()
+        log(f"measured peaks: {peaks['mfma_bf16_tflops']:.0f} TFLOP/s bf16 MFMA, "
+            f"{peaks['hbm_read_GBps']:.0f} GB/s streamed HBM read")
     pre = bench_prefill(args.steps, args.warmup)
     wl = pre["wl"]
     s = wl.shape
@@ -497,11 +546,15 @@ def main():
                      "traffic": measured_traffic("attn_prefill_128k"),
                      "kernel": "k_attn_prefill<192>", "algorithmic_bytes": pre["attn_bytes"],
                      "mfma_tflops": attn_tflops, "mfma_frac": attn_tflops / PEAK_BF16_TFLOPS},
+        "measured_peaks": peaks,
         "cpu_baseline": cpu,
         "stages_ms": {"index_build": pre["build_ms"], "indexer_topk": pre["topk_ms"],
                       "sparse_attn_prefill": pre["attn_ms"]},
         "indexer_share": (pre["build_ms"] + pre["topk_ms"]) / pre["ms_per_step"],
     }
+    if peaks is not None:
+        line["roofline"]["frac_of_measured_read"] = attn_gbs / peaks["hbm_read_GBps"]
+        line["roofline"]["mfma_frac_of_measured"] = attn_tflops / peaks["mfma_bf16_tflops"]
     line["sliding_window_attention"] = pre["swa"]
     line["index_build_from_keys"] = pre["fused_index"]
     line["attention_backward"] = pre["backward"]
@@ -512,6 +565,8 @@ def main():
                           "us_indexer_topk": dec["us_topk"], "us_attention": dec["us_attn"],
                           "GBps": dec["gbs"], "hbm_frac": dec["gbs"] / PEAK_HBM_GBS,
                           "algorithmic_bytes": dec["bytes"]}
+        if peaks is not None:
+            line["decode"]["hbm_frac_of_measured_read"] = dec["gbs"] / peaks["hbm_read_GBps"]
         f8 = dec["fp8"]
         line["decode_fp8_storage"] = {"workload": "decode-1m-x16", "storage": "e4m3 rows + fp32 "
                                       "scale per row (index, K, V)",

@@ -311,6 +311,24 @@ sgqa_status sgqa_sparse_attn_decode_fp8(const sgqa_dims *dims, const sgqa_bf16 *
  */
 size_t sgqa_workspace_bytes(int op, const sgqa_dims *dims, int32_t nseq, int32_t T, int64_t Lmax);
 
+/*
+ * Machine-peak probes, so that rooflines can be quoted against measured peaks as well as the
+ * vendor ones (dense bf16 MFMA and streaming HBM reads of this device).
+ *
+ * sgqa_probe_mfma_bf16: `waves` waves (1 <= waves <= 1 << 20) each run iters (1..8192)
+ * rounds of 8 independent 32x32x16 bf16 matrix products (32 768 flop each) on operands equal
+ * to 1.0, and wave w writes 2048 * iters (exact) to sink[w] (device, fp32, [waves]).
+ * Total work: waves * iters * 8 * 32768 flop.
+ *
+ * sgqa_probe_read: reads `bytes` (a positive multiple of 16) of device memory at buf
+ * (16-byte aligned) once, `blocks` workgroups (1..65536) striding over it, and writes to
+ * sink[b] (device, uint32, [blocks]) the sum modulo 2^32 of the 32-bit words workgroup b
+ * read; the partial sums add up (mod 2^32) to the sum of all the buffer's words.
+ */
+sgqa_status sgqa_probe_mfma_bf16(int32_t waves, int32_t iters, float *sink, void *stream);
+sgqa_status sgqa_probe_read(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks,
+                            void *stream);
+
 /* Static description of a status code. */
 const char *sgqa_status_string(sgqa_status status);
 

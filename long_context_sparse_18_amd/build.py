@@ -18,7 +18,7 @@ INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libsgqa.so")
 
-SOURCES = ["k_index.hip", "k_indexer.hip", "k_attn.hip", "sgqa_api.cpp"]
+SOURCES = ["k_index.hip", "k_indexer.hip", "k_attn.hip", "k_probe.hip", "sgqa_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
 COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]

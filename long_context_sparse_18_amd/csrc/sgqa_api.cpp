@@ -136,6 +136,34 @@ constexpr size_t kIndexerWorkspaceCap = size_t(2) << 30;
 
 extern "C" {
 
+sgqa_status sgqa_probe_mfma_bf16(int32_t waves, int32_t iters, float *sink, void *stream)
+{
+    if (waves < 1 || waves > (1 << 20) || iters < 1 || iters > 8192)
+        return fail(SGQA_ERR_SHAPE, "probe needs 1 <= waves <= 2^20 and 1 <= iters <= 8192");
+    if (!sink)
+        return fail(SGQA_ERR_NULL, "sink is NULL");
+    if (!aligned(sink, 4))
+        return fail(SGQA_ERR_SHAPE, "sink must be 4-byte aligned");
+    return hip_status(sgqa::launch_probe_mfma(waves, iters, sink,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                      "probe_mfma launch");
+}
+
+sgqa_status sgqa_probe_read(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks,
+                            void *stream)
+{
+    if (bytes == 0 || bytes % 16 != 0 || blocks < 1 || blocks > 65536)
+        return fail(SGQA_ERR_SHAPE, "probe needs bytes a positive multiple of 16 and 1..65536 "
+                                    "workgroups");
+    if (!buf || !sink)
+        return fail(SGQA_ERR_NULL, "buf and sink must be non-NULL");
+    if (!aligned(buf, 16) || !aligned(sink, 4))
+        return fail(SGQA_ERR_SHAPE, "buf must be 16-byte and sink 4-byte aligned");
+    return hip_status(sgqa::launch_probe_read(buf, (int64_t)bytes, sink, blocks,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                      "probe_read launch");
+}
+
 const char *sgqa_status_string(sgqa_status st)
 {
     switch (st) {

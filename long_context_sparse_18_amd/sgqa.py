@@ -26,7 +26,7 @@ OP_ATTN_BACKWARD = 4
 EXPORTS = ("sgqa_index_build", "sgqa_index_build_from_keys", "sgqa_indexer_topk", "sgqa_sparse_attn_prefill",
            "sgqa_sparse_attn_decode", "sgqa_swa_prefill", "sgqa_quantize_fp8",
            "sgqa_indexer_topk_fp8", "sgqa_sparse_attn_decode_fp8", "sgqa_sparse_attn_backward",
-           "sgqa_workspace_bytes",
+           "sgqa_probe_mfma_bf16", "sgqa_probe_read", "sgqa_workspace_bytes",
            "sgqa_status_string", "sgqa_last_error")
 
 
@@ -86,6 +86,10 @@ def load():
     lib.sgqa_sparse_attn_backward.restype = st
     lib.sgqa_sparse_attn_backward.argtypes = [dp, p, p, p, p, p, i64, i32, i64, ctypes.c_float, p,
                                               p, p, p, p, p, p, sz, i64, p]
+    lib.sgqa_probe_mfma_bf16.restype = st
+    lib.sgqa_probe_mfma_bf16.argtypes = [i32, i32, p, p]
+    lib.sgqa_probe_read.restype = st
+    lib.sgqa_probe_read.argtypes = [p, sz, p, i32, p]
     lib.sgqa_workspace_bytes.restype = sz
     lib.sgqa_workspace_bytes.argtypes = [ctypes.c_int, dp, i32, i32, i64]
     lib.sgqa_status_string.restype = ctypes.c_char_p
@@ -302,3 +306,23 @@ def sparse_attn_backward(shape: LayerShape, q, k_cache, v_cache, gate, idx, q_st
                                            _ptr(dv), _ptr(dgate), _ptr(workspace),
                                            workspace.numel(), dkdv_row_slice,
                                            _stream(stream, q)))
+
+
+def probe_mfma_bf16(sink, iters: int, stream=None):
+    """Dense bf16 MFMA probe: sink.numel() waves, each iters x 8 32x32x16 products
+    (32768 flop each); every sink entry becomes 2048 * iters."""
+    _need_cuda(sink)
+    if sink.dtype != torch.float32 or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous float32 tensor (one entry per wave)")
+    check(load().sgqa_probe_mfma_bf16(sink.numel(), iters, _ptr(sink), _stream(stream, sink)))
+
+
+def probe_read(buf, sink, stream=None):
+    """Streaming-read probe over the bytes of buf: sink (uint32 as int32, one entry per
+    workgroup) receives partial word sums that add up mod 2^32 to the buffer's word sum."""
+    _need_cuda(buf, sink)
+    if not buf.is_contiguous() or sink.dtype != torch.int32 or not sink.is_contiguous():
+        raise ValueError("buf must be contiguous and sink a contiguous int32 tensor")
+    nbytes = buf.numel() * buf.element_size()
+    check(load().sgqa_probe_read(_ptr(buf), nbytes, _ptr(sink), sink.numel(),
+                                 _stream(stream, buf)))

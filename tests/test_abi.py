@@ -213,6 +213,22 @@ def test_backward_validation():
     assert lib.sgqa_workspace_bytes(sgqa.OP_ATTN_BACKWARD, ctypes.byref(d), 2, 64, 1024) == 0
 
 
+def test_probe_validation():
+    lib = sgqa.load()
+    sink = FAKE
+    assert lib.sgqa_probe_mfma_bf16(0, 10, sink, None) == sgqa.ERR_SHAPE
+    assert lib.sgqa_probe_mfma_bf16(64, 0, sink, None) == sgqa.ERR_SHAPE
+    assert lib.sgqa_probe_mfma_bf16(64, 8193, sink, None) == sgqa.ERR_SHAPE
+    assert lib.sgqa_probe_mfma_bf16(64, 10, None, None) == sgqa.ERR_NULL
+    assert lib.sgqa_probe_read(FAKE, 0, sink, 8, None) == sgqa.ERR_SHAPE
+    assert lib.sgqa_probe_read(FAKE, 24, sink, 8, None) == sgqa.ERR_SHAPE
+    assert lib.sgqa_probe_read(FAKE, 1024, sink, 0, None) == sgqa.ERR_SHAPE
+    assert lib.sgqa_probe_read(FAKE, 1024, sink, 65537, None) == sgqa.ERR_SHAPE
+    assert lib.sgqa_probe_read(None, 1024, sink, 8, None) == sgqa.ERR_NULL
+    assert lib.sgqa_probe_read(ctypes.c_void_p((1 << 20) + 8), 1024, sink, 8, None) == \
+        sgqa.ERR_SHAPE
+
+
 def test_decode_validation():
     lib = sgqa.load()
     d = dims()

@@ -482,3 +482,25 @@ def test_tiny_backward(tiny, B, k, q0):
         torch.cuda.synchronize()
         for n in grads:
             assert torch.equal(grads[n], again[n]), (n, row_slice)
+
+
+@pytest.mark.gpu
+def test_peak_probes():
+    """The machine-peak probes compute what they state: every MFMA-probe wave reports
+    2048 * iters (37 waves: a partial last workgroup), and the read probe's partial sums add
+    up to the buffer's 32-bit word sum mod 2^32, for a buffer that leaves a ragged tail over
+    the grid stride and for a single 16-byte word."""
+    sink = torch.full((37,), -1.0, dtype=torch.float32, device=DEV)
+    sgqa.probe_mfma_bf16(sink, 100)
+    torch.cuda.synchronize()
+    assert torch.all(sink == 204800.0), sink
+    g = torch.Generator(device=DEV).manual_seed(3)
+    for words in (1 << 20, 4):
+        buf = torch.randint(-2 ** 31, 2 ** 31 - 1, (words,), dtype=torch.int32, device=DEV,
+                            generator=g)
+        part = torch.empty(96, dtype=torch.int32, device=DEV)
+        sgqa.probe_read(buf, part)
+        torch.cuda.synchronize()
+        want = int(buf.to(torch.int64).sum().item()) & 0xFFFFFFFF
+        got = int(part.to(torch.int64).sum().item()) & 0xFFFFFFFF
+        assert got == want, (words, got, want)
