@@ -364,7 +364,9 @@ __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
 template <int P>
 __global__ __launch_bounds__(256) void k_decode_keys_fp8(DecodeTopkArgs a)
 {
-    constexpr int U = 8;  // 16-block groups in flight per wave (16 B per row and step)
+    // 16-block groups in flight per wave (16 B per row and step): 4 keeps the wave under 128
+    // registers (4 waves per SIMD); measured 124 us per 16 x 1M batch vs 131 us with 8
+    constexpr int U = 4;
     const int s = blockIdx.y;
     const int64_t t = a.pos.v[s];
     const int64_t c = t / a.B;
