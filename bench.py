@@ -433,10 +433,32 @@ def measure_peaks():
             raise RuntimeError("read probe returned a wrong sum")
         best = max(best, 5 * nbytes / (e0.elapsed_time(e1) / 1e3) / 1e9)
     del buf
+    # random gathers of 384-byte rows over 403 MB, the K/V footprint of the 128K layer
+    rows, row_words, n = 1 << 20, 96, 1 << 26
+    table = torch.ones((rows, row_words), dtype=torch.int32, device="cuda")
+    g = torch.Generator(device="cuda").manual_seed(0)
+    idx = torch.randint(0, rows, (n,), dtype=torch.int32, device="cuda", generator=g)
+    part = torch.empty(cus * 16, dtype=torch.int32, device="cuda")
+    sgqa.probe_gather(table, idx, part)
+    gather = 0.0
+    for _ in range(3):
+        e0.record()
+        sgqa.probe_gather(table, idx, part)
+        e1.record()
+        torch.cuda.synchronize()
+        gather = max(gather, n * row_words * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9)
+    if int(part.to(torch.int64).sum().item()) & 0xFFFFFFFF != (n * row_words) & 0xFFFFFFFF:
+        raise RuntimeError("gather probe returned a wrong sum")
+    del table, idx
     torch.cuda.empty_cache()
     return {"mfma_bf16_tflops": mfma_tflops, "hbm_read_GBps": best,
+            "random_row_gather_GBps": gather,
+            "gather_roofline_tflops": 16 * gather / 1e3,
             "method": f"{waves} waves x {iters} x 8 bf16 32x32x16 MFMA (best of 3); 4 GiB "
-                      "streamed read, best of 8/16/32 workgroups per CU"}
+                      "streamed read, best of 8/16/32 workgroups per CU; 2^26 uniform random "
+                      "384-byte rows of a 403 MB table (best of 3); the gather roofline is "
+                      "16 flop per gathered byte (one K or V row feeds the 16 heads of its "
+                      "group) times that gather rate"}
 
 
 def main():
@@ -490,7 +512,8 @@ def main():
     if not args.no_peaks:
         peaks = measure_peaks()
         log(f"measured peaks: {peaks['mfma_bf16_tflops']:.0f} TFLOP/s bf16 MFMA, "
-            f"{peaks['hbm_read_GBps']:.0f} GB/s streamed HBM read")
+            f"{peaks['hbm_read_GBps']:.0f} GB/s streamed HBM read, "
+            f"{peaks['random_row_gather_GBps']:.0f} GB/s random 384-byte row gathers")
     pre = bench_prefill(args.steps, args.warmup)
     wl = pre["wl"]
     s = wl.shape
@@ -555,6 +578,7 @@ def main():
     if peaks is not None:
         line["roofline"]["frac_of_measured_read"] = attn_gbs / peaks["hbm_read_GBps"]
         line["roofline"]["mfma_frac_of_measured"] = attn_tflops / peaks["mfma_bf16_tflops"]
+        line["roofline"]["frac_of_gather_roofline"] = attn_tflops / peaks["gather_roofline_tflops"]
     line["sliding_window_attention"] = pre["swa"]
     line["index_build_from_keys"] = pre["fused_index"]
     line["attention_backward"] = pre["backward"]

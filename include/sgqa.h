@@ -324,10 +324,21 @@ size_t sgqa_workspace_bytes(int op, const sgqa_dims *dims, int32_t nseq, int32_t
  * (16-byte aligned) once, `blocks` workgroups (1..65536) striding over it, and writes to
  * sink[b] (device, uint32, [blocks]) the sum modulo 2^32 of the 32-bit words workgroup b
  * read; the partial sums add up (mod 2^32) to the sum of all the buffer's words.
+ *
+ * sgqa_probe_gather: the access pattern of the sparse attention's K/V gathers without its
+ * arithmetic.  table (device, 16-byte aligned) holds rows of row_bytes (a positive multiple
+ * of 16, at most 65536); for i < n it reads row idx[i] (device int32, each in
+ * [0, table_rows), unchecked on the device: the caller guarantees it), `blocks` workgroups
+ * (1..65536) striding over the n * row_bytes / 16 words; sink[b] (device, uint32, [blocks])
+ * gets the sum modulo 2^32 of the 32-bit words workgroup b read, so the partial sums add up
+ * to the sum over i of the words of row idx[i].
  */
 sgqa_status sgqa_probe_mfma_bf16(int32_t waves, int32_t iters, float *sink, void *stream);
 sgqa_status sgqa_probe_read(const void *buf, size_t bytes, uint32_t *sink, int32_t blocks,
                             void *stream);
+sgqa_status sgqa_probe_gather(const void *table, int64_t table_rows, int32_t row_bytes,
+                              const int32_t *idx, int64_t n, uint32_t *sink, int32_t blocks,
+                              void *stream);
 
 /* Static description of a status code. */
 const char *sgqa_status_string(sgqa_status status);

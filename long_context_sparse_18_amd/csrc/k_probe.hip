@@ -69,6 +69,78 @@ __global__ __launch_bounds__(256) void k_probe_read(const u32x4 *__restrict__ p,
         sink[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
 }
 
+// Random-row gather: for i < n, the row16 16-byte words of row idx[i] of the table, the
+// workgroups striding over the n * row16 words one word per lane; sink[b] is the sum
+// (mod 2^32) of the uint32 words workgroup b read.  The access pattern of the sparse
+// attention's K/V gathers without the arithmetic.
+__global__ __launch_bounds__(256) void k_probe_gather(const u32x4 *__restrict__ table,
+                                                      int row16, const int32_t *__restrict__ idx,
+                                                      int64_t n, uint32_t *sink)
+{
+    __shared__ uint32_t part[4];
+    // word w = i * row16 + k; the stride is split once into rows and words, so the walk
+    // needs no division
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    const int64_t sq = stride / row16;
+    const int sr = (int)(stride - sq * row16);
+    const int64_t w0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    int64_t i = w0 / row16;
+    int k = (int)(w0 - i * row16);
+    auto step = [&](int64_t &ii, int &kk) {
+        ii += sq;
+        kk += sr;
+        if (kk >= row16) {
+            kk -= row16;
+            ++ii;
+        }
+    };
+    uint32_t x = 0;
+    while (true) {  // four rows' words in flight per thread
+        int64_t iu[4];
+        int ku[4];
+        iu[0] = i;
+        ku[0] = k;
+#pragma unroll
+        for (int u = 1; u < 4; ++u) {
+            iu[u] = iu[u - 1];
+            ku[u] = ku[u - 1];
+            step(iu[u], ku[u]);
+        }
+        if (iu[3] >= n)
+            break;
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v[u] = table[(int64_t)idx[iu[u]] * row16 + ku[u]];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            x += v[u][0] + v[u][1] + v[u][2] + v[u][3];
+        i = iu[3];
+        k = ku[3];
+        step(i, k);
+    }
+    for (; i < n; step(i, k)) {
+        const u32x4 v = table[(int64_t)idx[i] * row16 + k];
+        x += v[0] + v[1] + v[2] + v[3];
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        x += (uint32_t)__shfl_xor((int)x, o);
+    if ((threadIdx.x & 63) == 0)
+        part[threadIdx.x >> 6] = x;
+    __syncthreads();
+    if (threadIdx.x == 0)
+        sink[blockIdx.x] = part[0] + part[1] + part[2] + part[3];
+}
+
+hipError_t launch_probe_gather(const void *table, int row16, const int32_t *idx, int64_t n,
+                               uint32_t *sink, int blocks, hipStream_t stream)
+{
+    hipLaunchKernelGGL(k_probe_gather, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const u32x4 *>(table), row16, idx, n, sink);
+    return hipGetLastError();
+}
+
 hipError_t launch_probe_mfma(int waves, int iters, float *sink, hipStream_t stream)
 {
     const int blocks = (waves + 3) / 4;

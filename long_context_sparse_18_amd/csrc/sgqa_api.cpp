@@ -164,6 +164,23 @@ sgqa_status sgqa_probe_read(const void *buf, size_t bytes, uint32_t *sink, int32
                       "probe_read launch");
 }
 
+sgqa_status sgqa_probe_gather(const void *table, int64_t table_rows, int32_t row_bytes,
+                              const int32_t *idx, int64_t n, uint32_t *sink, int32_t blocks,
+                              void *stream)
+{
+    if (table_rows < 1 || row_bytes < 16 || row_bytes > 65536 || row_bytes % 16 != 0 || n < 1 ||
+        blocks < 1 || blocks > 65536)
+        return fail(SGQA_ERR_SHAPE, "probe needs table_rows >= 1, row_bytes a multiple of 16 in "
+                                    "[16, 65536], n >= 1 and 1..65536 workgroups");
+    if (!table || !idx || !sink)
+        return fail(SGQA_ERR_NULL, "table, idx and sink must be non-NULL");
+    if (!aligned(table, 16) || !aligned(idx, 4) || !aligned(sink, 4))
+        return fail(SGQA_ERR_SHAPE, "table must be 16-byte, idx and sink 4-byte aligned");
+    return hip_status(sgqa::launch_probe_gather(table, row_bytes / 16, idx, n, sink, blocks,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                      "probe_gather launch");
+}
+
 const char *sgqa_status_string(sgqa_status st)
 {
     switch (st) {

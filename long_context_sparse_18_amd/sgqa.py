@@ -26,7 +26,8 @@ OP_ATTN_BACKWARD = 4
 EXPORTS = ("sgqa_index_build", "sgqa_index_build_from_keys", "sgqa_indexer_topk", "sgqa_sparse_attn_prefill",
            "sgqa_sparse_attn_decode", "sgqa_swa_prefill", "sgqa_quantize_fp8",
            "sgqa_indexer_topk_fp8", "sgqa_sparse_attn_decode_fp8", "sgqa_sparse_attn_backward",
-           "sgqa_probe_mfma_bf16", "sgqa_probe_read", "sgqa_workspace_bytes",
+           "sgqa_probe_mfma_bf16", "sgqa_probe_read", "sgqa_probe_gather",
+           "sgqa_workspace_bytes",
            "sgqa_status_string", "sgqa_last_error")
 
 
@@ -90,6 +91,8 @@ def load():
     lib.sgqa_probe_mfma_bf16.argtypes = [i32, i32, p, p]
     lib.sgqa_probe_read.restype = st
     lib.sgqa_probe_read.argtypes = [p, sz, p, i32, p]
+    lib.sgqa_probe_gather.restype = st
+    lib.sgqa_probe_gather.argtypes = [p, i64, i32, p, i64, p, i32, p]
     lib.sgqa_workspace_bytes.restype = sz
     lib.sgqa_workspace_bytes.argtypes = [ctypes.c_int, dp, i32, i32, i64]
     lib.sgqa_status_string.restype = ctypes.c_char_p
@@ -326,3 +329,18 @@ def probe_read(buf, sink, stream=None):
     nbytes = buf.numel() * buf.element_size()
     check(load().sgqa_probe_read(_ptr(buf), nbytes, _ptr(sink), sink.numel(),
                                  _stream(stream, buf)))
+
+
+def probe_gather(table, idx, sink, stream=None):
+    """Random-row gather probe: table [rows, row_bytes] (contiguous, any dtype), idx int32 [n]
+    with entries in [0, rows); sink (int32, one entry per workgroup) receives partial word sums
+    that add up mod 2^32 to the word sum of the gathered rows."""
+    _need_cuda(table, idx, sink)
+    if not table.is_contiguous() or idx.dtype != torch.int32 or sink.dtype != torch.int32:
+        raise ValueError("table must be contiguous, idx and sink int32")
+    rows = table.shape[0]
+    row_bytes = table[0].numel() * table.element_size()
+    if idx.numel() and (int(idx.min()) < 0 or int(idx.max()) >= rows):
+        raise ValueError("idx entries must lie in [0, table rows)")
+    check(load().sgqa_probe_gather(_ptr(table), rows, row_bytes, _ptr(idx), idx.numel(),
+                                   _ptr(sink), sink.numel(), _stream(stream, table)))

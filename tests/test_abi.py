@@ -227,6 +227,14 @@ def test_probe_validation():
     assert lib.sgqa_probe_read(None, 1024, sink, 8, None) == sgqa.ERR_NULL
     assert lib.sgqa_probe_read(ctypes.c_void_p((1 << 20) + 8), 1024, sink, 8, None) == \
         sgqa.ERR_SHAPE
+    g = lib.sgqa_probe_gather
+    assert g(FAKE, 0, 384, FAKE, 10, sink, 8, None) == sgqa.ERR_SHAPE
+    assert g(FAKE, 100, 392, FAKE, 10, sink, 8, None) == sgqa.ERR_SHAPE
+    assert g(FAKE, 100, 65552, FAKE, 10, sink, 8, None) == sgqa.ERR_SHAPE
+    assert g(FAKE, 100, 384, FAKE, 0, sink, 8, None) == sgqa.ERR_SHAPE
+    assert g(FAKE, 100, 384, FAKE, 10, sink, 0, None) == sgqa.ERR_SHAPE
+    assert g(FAKE, 100, 384, None, 10, sink, 8, None) == sgqa.ERR_NULL
+    assert g(ctypes.c_void_p((1 << 20) + 8), 100, 384, FAKE, 10, sink, 8, None) == sgqa.ERR_SHAPE
 
 
 def test_decode_validation():

@@ -504,3 +504,14 @@ def test_peak_probes():
         want = int(buf.to(torch.int64).sum().item()) & 0xFFFFFFFF
         got = int(part.to(torch.int64).sum().item()) & 0xFFFFFFFF
         assert got == want, (words, got, want)
+    # gathers of 384-byte rows (and of 16-byte rows) in a random order, with repeats
+    for row_words, n in ((96, 5000), (4, 777)):
+        table = torch.randint(-2 ** 31, 2 ** 31 - 1, (1000, row_words), dtype=torch.int32,
+                              device=DEV, generator=g)
+        idx = torch.randint(0, 1000, (n,), dtype=torch.int32, device=DEV, generator=g)
+        part = torch.empty(96, dtype=torch.int32, device=DEV)
+        sgqa.probe_gather(table, idx, part)
+        torch.cuda.synchronize()
+        want = int(table.index_select(0, idx.long()).to(torch.int64).sum().item()) & 0xFFFFFFFF
+        got = int(part.to(torch.int64).sum().item()) & 0xFFFFFFFF
+        assert got == want, (row_words, n, got, want)
