@@ -53,7 +53,7 @@ typedef enum {
     SGQA_OK = 0,
     SGQA_ERR_NULL = 1,        /* a required pointer is NULL */
     SGQA_ERR_SHAPE = 2,       /* sizes, strides or positions are inconsistent */
-    SGQA_ERR_UNSUPPORTED = 3, /* a valid shape this build does not implement */
+    SGQA_ERR_UNSUPPORTED = 3, /* a valid shape the library does not implement */
     SGQA_ERR_WORKSPACE = 4,   /* workspace missing or smaller than required */
     SGQA_ERR_HIP = 5          /* a HIP launch failed */
 } sgqa_status;

@@ -22,7 +22,7 @@
  *     head_dim 192; sparse_config topk 512, proxy_dim 256 on the
  *     full-attention layers.
  *
- * Readings taken where the pages are silent (each is listed in the design doc):
+ * Readings taken where the pages are silent:
  *   block representation = mean of the block's proxy keys over the tokens
  *   present; score = plain dot product of the query's proxy with a block
  *   representation; candidates = complete past blocks j < floor(t/B); k counts
