@@ -524,7 +524,8 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
 // Gated sliding-window attention, query-tiled: neighbouring queries share all but one of
 // their window positions, so a workgroup takes 16 consecutive queries of one KV group and each
 // 32-position step of the group's K and V rows is staged once in LDS for all of them.  One wave
-// per head of the group; the wave's arithmetic is the sparse kernel's with the MFMA N
+// per head; the group's heads are split over a few workgroups (blockIdx / Hkv % parts), each
+// staging the same tiles.  The wave's arithmetic is the sparse kernel's with the MFMA N
 // dimension taken as the 16 queries of one head instead of the 16 heads of one query:
 //   S^T[pos][query] = K_tile . Q_h^T (K rows from LDS as the A operand),
 //   online softmax per query (= lane % 16), O^T[d][query] += V_tile^T . P^T.
@@ -542,14 +543,17 @@ __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
     constexpr int kLd = D + 8;  // row stride (elements): 16-byte aligned rows
     constexpr int kTile = 2 * kSlots * kLd;  // K then V rows of one step
     const int hpg = a.Hq / a.Hkv;
-    const int g = (int)(blockIdx.x % (unsigned)a.Hkv);
-    const int64_t r0 = (int64_t)(blockIdx.x / (unsigned)a.Hkv) * 16;  // first query row
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int nwaves = (int)(blockDim.x >> 6);
+    const int nwaves = (int)(blockDim.x >> 6);      // heads per workgroup
+    const int hs = (hpg + nwaves - 1) / nwaves;     // workgroups per (query tile, group)
+    const int g = (int)(blockIdx.x % (unsigned)a.Hkv);
+    const int part = (int)((blockIdx.x / (unsigned)a.Hkv) % (unsigned)hs);
+    const int64_t r0 = (int64_t)(blockIdx.x / (unsigned)(a.Hkv * hs)) * 16;  // first query row
     const int col = lane & 15, q4 = lane >> 4;
     const int nq = a.rows - r0 < 16 ? (int)(a.rows - r0) : 16;
-    const bool has_head = wave < hpg;
-    const int h = g * hpg + (has_head ? wave : 0);
+    const int hw = part * nwaves + wave;            // this wave's head within the group
+    const bool has_head = hw < hpg;
+    const int h = g * hpg + (has_head ? hw : 0);
     const int64_t t0 = a.q_start + r0;
     const int64_t t_last = t0 + nq - 1;
     const int64_t ks0 = t0 - a.window + 1 > 0 ? t0 - a.window + 1 : 0;
@@ -575,7 +579,7 @@ __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
     static_assert(kTilePieces % 64 == 0, "whole instructions");
     // this lane's piece of the wave's first two DMA instructions (the same every step): the
     // row within the step, K or V, and the element offset within the group's row
-    constexpr int kPre = 2;
+    constexpr int kPre = 4;
     int dslot[kPre], doff[kPre];
     bool dv_[kPre];
 #pragma unroll
@@ -852,10 +856,15 @@ static hipError_t launch_prefill_d(const AttnArgs &a, hipStream_t stream)
 template <int D>
 static hipError_t launch_swa_d(const AttnArgs &a, hipStream_t stream)
 {
-    const int64_t nwg = ((int64_t)a.rows + 15) / 16 * a.Hkv;
-    const size_t lds = (size_t)2 * 2 * kSlots * (D + 8) * sizeof(uint16_t);
+    // The group's heads are split over two workgroups (8 waves each at 16 heads), so that two
+    // of them share a CU and one computes while the other waits at its step barrier
+    // (6.37 -> 6.04 ms at 128K; four workgroups of 4 waves: 7.25 ms)
     const int hpg = a.Hq / a.Hkv;
-    hipLaunchKernelGGL(k_swa_tiled<D>, dim3((unsigned)nwg), dim3(64 * hpg), lds, stream, a);
+    const int hs = hpg >= 2 ? 2 : 1;
+    const int nw = (hpg + hs - 1) / hs;
+    const int64_t nwg = ((int64_t)a.rows + 15) / 16 * a.Hkv * hs;
+    const size_t lds = (size_t)2 * 2 * kSlots * (D + 8) * sizeof(uint16_t);
+    hipLaunchKernelGGL(k_swa_tiled<D>, dim3((unsigned)nwg), dim3(64 * nw), lds, stream, a);
     return hipGetLastError();
 }
 
