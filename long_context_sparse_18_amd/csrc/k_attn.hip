@@ -534,13 +534,15 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
 // filled by direct global-to-LDS loads (global_load_lds_dwordx4: lane l of an instruction
 // writes 16 bytes at base + 16 l), so the next step's rows stream in while the current step is
 // computed, without holding registers.  A step's tile is 2 x 32 rows of kLd/8 16-byte pieces
-// (a whole number of 64-piece instructions); the pad piece of a row reloads the row's first
-// piece and is never read.
+// (a whole number of 64-piece instructions); the pad pieces of a row reload the row's first
+// piece and are never read.
 template <int D>
 __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
 {
     extern __shared__ __align__(16) uint16_t lds[];
-    constexpr int kLd = D + 8;  // row stride (elements): 16-byte aligned rows
+    // row stride (elements): 16-byte aligned rows, padded by 16 so the transposing V reads are
+    // free of bank conflicts (5.87 ms vs 6.05 ms with a pad of 8 at 128K)
+    constexpr int kLd = D + 16;
     constexpr int kTile = 2 * kSlots * kLd;  // K then V rows of one step
     const int hpg = a.Hq / a.Hkv;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -863,7 +865,7 @@ static hipError_t launch_swa_d(const AttnArgs &a, hipStream_t stream)
     const int hs = hpg >= 2 ? 2 : 1;
     const int nw = (hpg + hs - 1) / hs;
     const int64_t nwg = ((int64_t)a.rows + 15) / 16 * a.Hkv * hs;
-    const size_t lds = (size_t)2 * 2 * kSlots * (D + 8) * sizeof(uint16_t);
+    const size_t lds = (size_t)2 * 2 * kSlots * (D + 16) * sizeof(uint16_t);
     hipLaunchKernelGGL(k_swa_tiled<D>, dim3((unsigned)nwg), dim3(64 * nw), lds, stream, a);
     return hipGetLastError();
 }
