@@ -35,7 +35,9 @@
  * Supported shapes: heads_per_group = Hq / Hkv in 1..16, Hkv in 1..8,
  * head_dim in {64, 128, 192}, proxy_dim a multiple of 32 up to 512,
  * block_size in {1, 2, 4, 8, 16, 32}, 1 <= topk_blocks <= 4096 with
- * topk_blocks * block_size <= 32768, nseq <= 64.
+ * topk_blocks * block_size <= 32768, nseq <= 64.  Prefill, sliding-window and backward calls
+ * take at most 2^24 query rows (and the backward at most 2^24 cache blocks) per call; larger
+ * ones return SGQA_ERR_UNSUPPORTED and are split by the caller into chunks of rows.
  */
 #ifndef SGQA_H
 #define SGQA_H

@@ -1002,18 +1002,21 @@ __device__ __forceinline__ s16x4 pack4_bf16(float x0, float x1, float x2, float 
 
 constexpr float kLog2e = 1.4426950408889634f;
 
-// One wave per (row, head): da = sigmoid(G) g_out, rounded to bf16 for the matrix cores.
+// One wave per (row, head), the waves striding over all of them (the grid is capped, so the
+// launch stays inside 32-bit work-item counts at any T): da = sigmoid(G) g_out, rounded to
+// bf16 for the matrix cores.
 __global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a)
 {
-    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-    if (row >= (int64_t)a.rows * a.Hq)
-        return;
+    const int64_t nrow = (int64_t)a.rows * a.Hq;
     const int lane = threadIdx.x & 63;
     const int d = a.d;
-    const uint16_t *go = a.dout + row * d;
-    const float sg = sigmoid_f32(bf16_bits_to_f32(a.gate[row]));
-    for (int e = lane; e < d; e += 64)
-        a.da[row * d + e] = (uint16_t)f32_to_bf16_bits(sg * bf16_bits_to_f32(go[e]));
+    for (int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6); row < nrow;
+         row += (int64_t)gridDim.x * 4) {
+        const uint16_t *go = a.dout + row * d;
+        const float sg = sigmoid_f32(bf16_bits_to_f32(a.gate[row]));
+        for (int e = lane; e < d; e += 64)
+            a.da[row * d + e] = (uint16_t)f32_to_bf16_bits(sg * bf16_bits_to_f32(go[e]));
+    }
 }
 
 __global__ __launch_bounds__(256) void k_bwd_zero(uint32_t *p, int64_t n)
@@ -1022,18 +1025,19 @@ __global__ __launch_bounds__(256) void k_bwd_zero(uint32_t *p, int64_t n)
         p[i] = 0u;
 }
 
-// One thread per selection entry: set bit r of block j's row.
+// One thread per selection entry (grid-stride, capped grid): set bit r of block j's row.
 __global__ __launch_bounds__(256) void k_bwd_bitmap(BwdArgs a)
 {
-    const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-    if (gid >= (int64_t)a.rows * a.k)
-        return;
-    const int64_t r = gid / a.k;
-    const int32_t j = a.idx[gid];
-    const int64_t c = (a.q_start + r) / a.B;
-    if (j < 0 || (int64_t)j > c || (int64_t)j >= a.nblk)
-        return;
-    atomicOr(&a.bits[(int64_t)j * a.bits_ld + (r >> 5)], 1u << (r & 31));
+    const int64_t n = (int64_t)a.rows * a.k;
+    for (int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x; gid < n;
+         gid += (int64_t)gridDim.x * 256) {
+        const int64_t r = gid / a.k;
+        const int32_t j = a.idx[gid];
+        const int64_t c = (a.q_start + r) / a.B;
+        if (j < 0 || (int64_t)j > c || (int64_t)j >= a.nblk)
+            continue;
+        atomicOr(&a.bits[(int64_t)j * a.bits_ld + (r >> 5)], 1u << (r & 31));
+    }
 }
 
 // First sweep of a wave's (row, group): D = sum_s P_s dP_s per head (this lane's share),
@@ -1475,7 +1479,9 @@ hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t stream)
     if (!a.q || !a.dout || !a.dq || !a.dk || !a.dv || !a.dgate || !a.da || !a.dsum || !a.bits)
         return hipErrorInvalidValue;  // never launch without the tensors the kernels touch
     const int64_t nrow = (int64_t)a.rows * a.Hq;
-    hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)((nrow + 3) / 4)), dim3(256), 0, stream, a);
+    const int64_t prep_wg = (nrow + 3) / 4;
+    hipLaunchKernelGGL(k_bwd_prep, dim3((unsigned)(prep_wg < (1 << 20) ? prep_wg : (1 << 20))),
+                       dim3(256), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
@@ -1486,7 +1492,9 @@ hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t stream)
     if (e != hipSuccess)
         return e;
     const int64_t ent = (int64_t)a.rows * a.k;
-    hipLaunchKernelGGL(k_bwd_bitmap, dim3((unsigned)((ent + 255) / 256)), dim3(256), 0, stream, a);
+    const int64_t bm_wg = (ent + 255) / 256;
+    hipLaunchKernelGGL(k_bwd_bitmap, dim3((unsigned)(bm_wg < (1 << 20) ? bm_wg : (1 << 20))),
+                       dim3(256), 0, stream, a);
     e = hipGetLastError();
     if (e != hipSuccess)
         return e;

@@ -49,6 +49,18 @@ int64_t round_up(int64_t a, int64_t b)
     return ceil_div(a, b) * b;
 }
 
+// Launches sized by query rows (or by cache blocks in the backward) keep their work-item
+// counts inside 32 bits up to this many rows per call.
+constexpr int64_t kMaxRowsPerCall = (int64_t)1 << 24;
+
+sgqa_status check_rows(int64_t rows, const char *what)
+{
+    if (rows > kMaxRowsPerCall)
+        return fail(SGQA_ERR_UNSUPPORTED, "%s: %lld exceeds %lld per call (split the call)", what,
+                    (long long)rows, (long long)kMaxRowsPerCall);
+    return SGQA_OK;
+}
+
 sgqa_status check_dims(const sgqa_dims *d, bool need_attn, bool need_proxy)
 {
     if (!d)
@@ -477,6 +489,8 @@ sgqa_status sgqa_sparse_attn_prefill(const sgqa_dims *dims, const sgqa_bf16 *q,
                     (long long)L);
     if (!std::isfinite(softmax_scale))
         return fail(SGQA_ERR_SHAPE, "softmax_scale must be finite");
+    if ((st = check_rows(T, "query rows")) != SGQA_OK)
+        return st;
     if (T == 0)
         return ok();
     if (!q || !k_cache || !v_cache || !gate || !idx || !out)
@@ -539,6 +553,8 @@ sgqa_status sgqa_swa_prefill(const sgqa_dims *dims, const sgqa_bf16 *q, const sg
         return fail(SGQA_ERR_SHAPE, "window %lld must be >= 1", (long long)window);
     if (!std::isfinite(softmax_scale))
         return fail(SGQA_ERR_SHAPE, "softmax_scale must be finite");
+    if ((st = check_rows(T, "query rows")) != SGQA_OK)
+        return st;
     if (T == 0)
         return ok();
     if (!q || !k_cache || !v_cache || !gate || !out)
@@ -815,6 +831,9 @@ sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
     if (dkdv_row_slice < 0 || dkdv_row_slice % 32 != 0)
         return fail(SGQA_ERR_SHAPE, "dkdv_row_slice %lld must be 0 or a positive multiple of 32",
                     (long long)dkdv_row_slice);
+    if ((st = check_rows(T, "query rows")) != SGQA_OK ||
+        (st = check_rows(ceil_div(L, dims->block_size), "cache blocks")) != SGQA_OK)
+        return st;
     if (T == 0 || L == 0)
         return ok();
     if (!q || !k_cache || !v_cache || !gate || !idx || !lse || !dout || !dq || !dk || !dv ||

@@ -82,6 +82,11 @@ def test_prefill_rejects_bad_sizes_and_pointers():
     assert sgqa.load().sgqa_last_error() == b""
     assert call_prefill(d, q_start=10, T=16, L=20) == sgqa.ERR_SHAPE
     assert b"exceeds L" in sgqa.load().sgqa_last_error()
+    # more query rows than one call takes (the launches would pass 32-bit work-item counts)
+    big = (1 << 24) + 1
+    assert call_prefill(d, T=big, L=big) == sgqa.ERR_UNSUPPORTED
+    assert b"per call" in sgqa.load().sgqa_last_error()
+    assert call_prefill(d, T=1 << 24, L=1 << 24, q=None) == sgqa.ERR_NULL  # the limit itself is fine
 
 
 def test_null_dims():
@@ -206,6 +211,8 @@ def test_backward_validation():
     assert call(T=-1) == sgqa.ERR_SHAPE
     assert call(wsb=need - 1) == sgqa.ERR_WORKSPACE
     assert call(ws=ctypes.c_void_p((1 << 20) + 16)) == sgqa.ERR_SHAPE
+    assert call(T=(1 << 24) + 1, L=(1 << 24) + 1) == sgqa.ERR_UNSUPPORTED
+    assert call(T=64, L=((1 << 24) + 1) * 8) == sgqa.ERR_UNSUPPORTED  # cache blocks
     assert call(slice_=16) == sgqa.ERR_SHAPE      # dk / dv row slices are whole bitmap words
     assert call(slice_=-32) == sgqa.ERR_SHAPE
     assert call(T=0) == sgqa.OK
@@ -270,3 +277,21 @@ def test_workspace_sizes():
     assert ws == 16 * 32 * 64 * (192 + 3) * 4
     assert sgqa.workspace_bytes(sgqa.OP_ATTN_DECODE, with_selection(TINY, 8, 16), 1, 1, 1024) > 0
     assert sgqa.workspace_bytes(7, REAL, 1, 1, 1) == 0
+
+
+def test_swa_validation():
+    lib = sgqa.load()
+    d = dims()
+
+    def call(q=FAKE, T=64, L=1024, q_start=0, window=512, scale=0.07, out=FAKE):
+        return lib.sgqa_swa_prefill(ctypes.byref(d), q, FAKE, FAKE, FAKE, q_start, T, L, window,
+                                    scale, out, None, None)
+
+    assert call(q=None) == sgqa.ERR_NULL
+    assert call(out=None) == sgqa.ERR_NULL
+    assert call(window=0) == sgqa.ERR_SHAPE
+    assert call(q_start=1000) == sgqa.ERR_SHAPE
+    assert call(scale=float("nan")) == sgqa.ERR_SHAPE
+    assert call(q=ctypes.c_void_p((1 << 20) + 2)) == sgqa.ERR_SHAPE
+    assert call(T=(1 << 24) + 1, L=(1 << 24) + 1) == sgqa.ERR_UNSUPPORTED
+    assert call(T=0) == sgqa.OK
