@@ -764,6 +764,237 @@ __global__ __launch_bounds__(NT) void k_decode_select(DecodeTopkArgs a)
     emit_selected<NT>(key_at, cn, th, keep, sh, emit);
 }
 
+// ---- prefill rows of at most kSel2MaxCand candidates, without a histogram of the whole row ----
+// Normally distributed scores put nearly all keys into a few dozen bins of a 12-bit histogram,
+// so a full-row histogram serialises on LDS atomics.  Instead: (1) a sample of at most
+// kSel2Samp keys (every stride-th block) gives T0, its q-th largest key, with q about twice
+// the sample's expected share of the kept blocks; (2) one read of the row lists every block
+// whose key is >= T0 (about twice `keep` of them); (3) the `keep` largest of the listed keys are
+// found exactly (radix passes over the list in LDS, exact ties of the full key to the lowest
+// block) and marked in an LDS bitmap, which (4) gives every selected block its output
+// position in block order.  The result does not depend on the sample: when fewer than `keep`
+// or more than kSel2Cap blocks reach T0, the four-read selection over the whole row runs.
+constexpr int kSel2MaxCand = 16384;
+constexpr int kSel2Words = kSel2MaxCand / 32;
+constexpr int kSel2Cap = 2048;
+constexpr int kSel2Samp = 1024;
+
+// find_bin for any NT dividing 4096: thread t owns bins [t * 4096/NT, (t+1) * 4096/NT).
+template <int NT>
+__device__ __forceinline__ BinFind find_bin_n(const uint32_t *hist, int need, int *scan,
+                                              BinFind &res)
+{
+    constexpr int kPer = 4096 / NT;
+    const int tid = threadIdx.x;
+    int local = 0;
+#pragma unroll
+    for (int b = 0; b < kPer; ++b)
+        local += (int)hist[tid * kPer + b];
+    int total;
+    const int below = block_exclusive_scan<NT>(local, scan, total);
+    const int above = total - below - local;
+    if (above < need && need <= above + local) {
+        int acc = above;
+#pragma unroll
+        for (int b = kPer - 1; b >= 0; --b) {
+            const int hb = (int)hist[tid * kPer + b];
+            if (acc < need && need <= acc + hb) {
+                res.digit = (uint32_t)(tid * kPer + b);
+                res.need = need - acc;
+                res.cnt = hb;
+                res.ge = acc + hb;
+            }
+            acc += hb;
+        }
+    }
+    __syncthreads();
+    return res;
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void k_select2(SelectArgs a)
+{
+    static_assert(kSel2Words % NT == 0, "");
+    __shared__ __align__(16) SelectShared sh;
+    __shared__ uint32_t bitmap[kSel2Words];
+    __shared__ uint32_t samp[kSel2Samp];
+    __shared__ uint32_t cand_key[kSel2Cap];
+    __shared__ int32_t cand_idx[kSel2Cap];
+    __shared__ int n_cand;
+    __shared__ BinFind bf;
+    const int tid = threadIdx.x;
+    const int row = blockIdx.x;
+    const int s = row / a.nq;
+    const int i = row - s * a.nq;
+    const int64_t t = a.q_start.v[s] + a.t0 + i;
+    const int64_t c = t / a.B;
+    const int k = a.k, keep = k - 1;
+    const float *srow = a.ws + (int64_t)row * a.ld;
+    int32_t *out = a.idx + ((int64_t)s * a.T + a.t0 + i) * k;
+    float *osc = a.sel_scores ? a.sel_scores + ((int64_t)s * a.T + a.t0 + i) * k : nullptr;
+
+    if (c <= (int64_t)keep) {
+        for (int e = tid; e < k; e += NT) {
+            out[e] = e <= c ? e : -1;
+            if (osc)
+                osc[e] = (e < c) ? srow[e] : (e == c ? __builtin_inff() : -__builtin_inff());
+        }
+        return;
+    }
+    if (tid == 0) {
+        out[keep] = (int32_t)c;
+        if (osc)
+            osc[keep] = __builtin_inff();
+    }
+    if (keep == 0)
+        return;
+    const int n = (int)c;
+    uint32_t *hist = sh.hist;
+    auto emit = [&](int pos, int j, uint32_t key) {
+        out[pos] = j;
+        if (osc)
+            osc[pos] = key_score(key);
+    };
+
+    // (1) T0 from the sample
+    const int stride = (n + kSel2Samp - 1) / kSel2Samp;
+    const int ns = (n + stride - 1) / stride;
+    {
+        constexpr int kSp = kSel2Samp / NT;  // samples per thread, loaded together
+        float v[kSp];
+#pragma unroll
+        for (int u = 0; u < kSp; ++u) {
+            const int e = u * NT + tid;
+            v[u] = srow[(int64_t)(e < ns ? e : 0) * stride];
+        }
+#pragma unroll
+        for (int u = 0; u < kSp; ++u)
+            if (u * NT + tid < ns)
+                samp[u * NT + tid] = score_key(v[u]);
+    }
+    const int64_t share = ((int64_t)keep * ns + n - 1) / n;  // expected kept samples, rounded up
+    const int q = (int)(2 * share + 16 < ns ? 2 * share + 16 : ns);
+    __syncthreads();
+    const KthKey tq = radix_select<NT>([&](int e) { return samp[e]; }, ns, q, sh);
+    const uint32_t t0key = tq.key;
+
+    // (2) the blocks whose key reaches T0
+    if (tid == 0)
+        n_cand = 0;
+    __syncthreads();
+    // 16 keys per thread and iteration, four 16-byte loads in flight (rows start 256-byte
+    // aligned and hold at least round_up(n, 64) floats, so the last group reads inside it)
+    const u32x4 *row4 = reinterpret_cast<const u32x4 *>(srow);
+    for (int g0 = 0; g0 * 16 < n; g0 += NT) {
+        const int g = g0 + tid;
+        u32x4 v[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v[u] = g * 16 < n ? row4[g * 4 + u] : u32x4{0u, 0u, 0u, 0u};
+        uint32_t kk[16];
+        int cnt = 0;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int j = g * 16 + e;
+            kk[e] = score_key(__uint_as_float(v[e >> 2][e & 3]));
+            cnt += (j < n && kk[e] >= t0key) ? 1 : 0;
+        }
+        int slot = wave_append(cnt, &n_cand);
+#pragma unroll
+        for (int e = 0; e < 16; ++e) {
+            const int j = g * 16 + e;
+            if (j < n && kk[e] >= t0key) {
+                if (slot < kSel2Cap) {
+                    cand_key[slot] = kk[e];
+                    cand_idx[slot] = j;
+                }
+                ++slot;
+            }
+        }
+    }
+    __syncthreads();
+    const int m = n_cand;
+    if (m < keep || m > kSel2Cap) {
+        auto key_at = [&](int j) { return score_key(srow[j]); };
+        const KthKey th = radix_select<NT>(key_at, n, keep, sh);
+        emit_selected<NT>(key_at, n, th, keep, sh, emit);
+        return;
+    }
+
+    // (3) exact selection of `keep` of the m listed keys
+    int need = keep, cnt = m;
+    uint32_t P = 0u, pmask = 0u;
+    const int shifts[3] = {20, 8, 0};
+    const uint32_t dmasks[3] = {0xfffu, 0xfffu, 0xffu};
+#pragma unroll 1
+    for (int pass = 0; pass < 3 && need != cnt; ++pass) {
+        const int shift = shifts[pass];
+        const uint32_t dmask = dmasks[pass];
+        for (int b = tid; b < 4096; b += NT)
+            hist[b] = 0u;
+        __syncthreads();
+        for (int e = tid; e < m; e += NT)
+            if ((cand_key[e] & pmask) == P)
+                atomicAdd(&hist[(cand_key[e] >> shift) & dmask], 1u);
+        __syncthreads();
+        const BinFind rb = find_bin_n<NT>(hist, need, sh.scan, bf);
+        P |= rb.digit << shift;
+        pmask |= dmask << shift;
+        need = rb.need;
+        cnt = rb.cnt;
+    }
+    const int nwords = (n + 31) / 32;
+    for (int w = tid; w < nwords; w += NT)
+        bitmap[w] = 0u;
+    __syncthreads();
+    // take: keys above the prefix P; at P all of them when the count matches, else (exact
+    // ties of the full key) the `need` lowest blocks
+    for (int e = tid; e < m; e += NT) {
+        const uint32_t key = cand_key[e];
+        const int j = cand_idx[e];
+        const uint32_t km = key & pmask;
+        bool take = km > P;
+        if (km == P) {
+            if (need == cnt) {
+                take = true;
+            } else {
+                int rank = 0;
+                for (int f = 0; f < m; ++f)
+                    rank += (cand_key[f] == key && cand_idx[f] < j) ? 1 : 0;
+                take = rank < need;
+            }
+        }
+        if (take)
+            atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+    }
+    __syncthreads();
+
+    // (4) output positions: exclusive prefix of the bitmap popcounts
+    constexpr int kWpt = kSel2Words / NT;  // bitmap words per thread
+    uint32_t wv[kWpt];
+    int cntw = 0;
+#pragma unroll
+    for (int qq = 0; qq < kWpt; ++qq) {
+        const int w = tid * kWpt + qq;
+        wv[qq] = w < nwords ? bitmap[w] : 0u;
+        cntw += __popc(wv[qq]);
+    }
+    int total;
+    int pos = block_exclusive_scan<NT>(cntw, sh.scan, total);
+#pragma unroll
+    for (int qq = 0; qq < kWpt; ++qq) {
+        uint32_t bits = wv[qq];
+        while (bits) {
+            const int b = __builtin_ctz(bits);
+            bits &= bits - 1u;
+            const int j = (tid * kWpt + qq) * 32 + b;
+            if (pos < keep)  // exactly `keep` bits are set
+                emit(pos, j, score_key(srow[j]));
+            ++pos;
+        }
+    }
+}
+
 bool decode_topk_supported(int64_t max_cand, int k)
 {
     // the unit maxima of one sequence and the bitmap of its blocks fit in the select's LDS
@@ -832,6 +1063,10 @@ hipError_t launch_select(const SelectArgs &a, hipStream_t stream)
     const unsigned rows = (unsigned)(a.nseq * a.nq);
     if (rows == 0)
         return hipSuccess;
+    if (a.max_cand <= kSel2MaxCand) {
+        hipLaunchKernelGGL(k_select2<256>, dim3(rows), dim3(256), 0, stream, a);
+        return hipGetLastError();
+    }
     if (a.max_cand > 32768 && rows <= 256)
         hipLaunchKernelGGL(k_select<1024>, dim3(rows), dim3(1024), 0, stream, a);
     else
