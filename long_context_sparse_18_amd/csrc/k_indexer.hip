@@ -26,6 +26,7 @@ namespace sgqa {
 constexpr int kTileQ = 64;
 constexpr int kTileB = 64;
 
+template <int P>
 __global__ __launch_bounds__(256) void k_scores(ScoreArgs a)
 {
     extern __shared__ __align__(16) uint16_t kb_tile[];  // [kTileB][P + 8]
@@ -38,19 +39,34 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a)
     if (j0 >= c_last)
         return;
 
-    const int P = a.P;
-    const int ldt = P + 8;
+    constexpr int ldt = P + 8;
     const int tid = threadIdx.x;
     const uint16_t *kb = a.kb + (int64_t)s * a.kb_seq_stride;
 
-    // Stage kb rows j0 .. j0+63 (rows at or past c_last are zero).
-    const int chunks = P >> 3;
-    for (int e = tid; e < kTileB * chunks; e += 256) {
+    // Stage kb rows j0 .. j0+63 (rows at or past c_last are zero); every load of the tile is
+    // issued before the first store
+    constexpr int chunks = P / 8;
+    constexpr int kPer = (kTileB * chunks + 255) / 256;
+    u32x4 tv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {  // unconditional loads (row j0 is always valid)
+        const int e = u * 256 + tid;
         const int r = e / chunks, cc = e - r * chunks;
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (j0 + r < c_last)
-            v = load16(kb + (j0 + r) * P + cc * 8);
-        *reinterpret_cast<u32x4 *>(kb_tile + r * ldt + cc * 8) = v;
+        const int64_t row = j0 + r < c_last && e < kTileB * chunks ? j0 + r : j0;
+        tv[u] = load16(kb + row * P + cc * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int e = u * 256 + tid;
+        if (j0 + e / chunks >= c_last)
+            tv[u] = u32x4{0u, 0u, 0u, 0u};
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int e = u * 256 + tid;
+        const int r = e / chunks, cc = e - r * chunks;
+        if (e < kTileB * chunks)
+            *reinterpret_cast<u32x4 *>(kb_tile + r * ldt + cc * 8) = tv[u];
     }
     __syncthreads();
 
@@ -61,19 +77,24 @@ __global__ __launch_bounds__(256) void k_scores(ScoreArgs a)
         return;
     const uint16_t *qp = a.qp + (int64_t)s * a.qp_seq_stride + (int64_t)(a.t0 + qrow) * P;
 
+    // the query proxies of this lane's row, every slice loaded together
+    // (rows past nq read row i0 + 16 wave, which exists, and are never stored)
+    const uint16_t *qpr = qrow < a.nq ? qp : qp - (int64_t)col * P;
+    u32x4 av[P / 32];
+#pragma unroll
+    for (int kk = 0; kk < P / 32; ++kk)
+        av[kk] = load16(qpr + kk * 32 + q4 * 8);
     f32x4 acc[4];
 #pragma unroll
     for (int n = 0; n < 4; ++n)
         acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-    for (int kk = 0; kk < P; kk += 32) {
-        u32x4 av = {0u, 0u, 0u, 0u};
-        if (qrow < a.nq)
-            av = load16(qp + kk + q4 * 8);
-        const bf16x8 af = as_bf16x8(av);
+#pragma unroll
+    for (int kk = 0; kk < P / 32; ++kk) {
+        const bf16x8 af = as_bf16x8(av[kk]);
 #pragma unroll
         for (int n = 0; n < 4; ++n) {
-            const u32x4 bv =
-                *reinterpret_cast<const u32x4 *>(kb_tile + (n * 16 + col) * ldt + kk + q4 * 8);
+            const u32x4 bv = *reinterpret_cast<const u32x4 *>(kb_tile + (n * 16 + col) * ldt +
+                                                              kk * 32 + q4 * 8);
             acc[n] = mfma_16x16x32(af, as_bf16x8(bv), acc[n]);
         }
     }
@@ -102,7 +123,25 @@ hipError_t launch_scores(const ScoreArgs &a, hipStream_t stream)
     const dim3 grid((unsigned)((a.max_cand + kTileB - 1) / kTileB),
                     (unsigned)((a.nq + kTileQ - 1) / kTileQ), (unsigned)a.nseq);
     const size_t lds = (size_t)kTileB * (a.P + 8) * sizeof(uint16_t);
-    hipLaunchKernelGGL(k_scores, grid, dim3(256), lds, stream, a);
+    switch (a.P) {
+    case 32: hipLaunchKernelGGL(k_scores<32>, grid, dim3(256), lds, stream, a); break;
+    case 64: hipLaunchKernelGGL(k_scores<64>, grid, dim3(256), lds, stream, a); break;
+    case 96: hipLaunchKernelGGL(k_scores<96>, grid, dim3(256), lds, stream, a); break;
+    case 128: hipLaunchKernelGGL(k_scores<128>, grid, dim3(256), lds, stream, a); break;
+    case 160: hipLaunchKernelGGL(k_scores<160>, grid, dim3(256), lds, stream, a); break;
+    case 192: hipLaunchKernelGGL(k_scores<192>, grid, dim3(256), lds, stream, a); break;
+    case 224: hipLaunchKernelGGL(k_scores<224>, grid, dim3(256), lds, stream, a); break;
+    case 256: hipLaunchKernelGGL(k_scores<256>, grid, dim3(256), lds, stream, a); break;
+    case 288: hipLaunchKernelGGL(k_scores<288>, grid, dim3(256), lds, stream, a); break;
+    case 320: hipLaunchKernelGGL(k_scores<320>, grid, dim3(256), lds, stream, a); break;
+    case 352: hipLaunchKernelGGL(k_scores<352>, grid, dim3(256), lds, stream, a); break;
+    case 384: hipLaunchKernelGGL(k_scores<384>, grid, dim3(256), lds, stream, a); break;
+    case 416: hipLaunchKernelGGL(k_scores<416>, grid, dim3(256), lds, stream, a); break;
+    case 448: hipLaunchKernelGGL(k_scores<448>, grid, dim3(256), lds, stream, a); break;
+    case 480: hipLaunchKernelGGL(k_scores<480>, grid, dim3(256), lds, stream, a); break;
+    case 512: hipLaunchKernelGGL(k_scores<512>, grid, dim3(256), lds, stream, a); break;
+    default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 
