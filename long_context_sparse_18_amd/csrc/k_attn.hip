@@ -491,10 +491,19 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
         const int32_t *row = a.idx + r * a.k;
         const int lane = threadIdx.x & 63;
         int below_lo = 0, below_hi = 0;
-        for (int e = lane; e < nvalid; e += 64) {
-            const int32_t b = row[e];
-            below_lo += (b >= 0 && b < lo) ? 1 : 0;
-            below_hi += (b >= 0 && b < hi) ? 1 : 0;
+        for (int e0 = 0; e0 < nvalid; e0 += 256) {  // four loads in flight per lane
+            int32_t b[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const int e = e0 + u * 64 + lane;
+                b[u] = row[e < nvalid ? e : 0];
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const bool in = e0 + u * 64 + lane < nvalid && b[u] >= 0;
+                below_lo += (in && b[u] < lo) ? 1 : 0;
+                below_hi += (in && b[u] < hi) ? 1 : 0;
+            }
         }
 #pragma unroll
         for (int o = 32; o > 0; o >>= 1) {
