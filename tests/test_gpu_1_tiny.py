@@ -294,9 +294,13 @@ def test_decode_topk_exact_ties(k):
         assert np.array_equal(sel[b, 0].cpu().numpy().astype(np.float64), want)
 
 
-def test_prefill_topk_exact_ties():
-    """Prefill top-k (one workgroup per query row) on integer-valued scores: exact."""
-    k, T, q0 = 512, 96, 30000
+@pytest.mark.parametrize("q0", [30000, 8000])
+def test_prefill_topk_exact_ties(q0):
+    """Prefill top-k (one workgroup per query row) on integer-valued scores: exact.  Row 7 has
+    all scores equal: with ~3 750 candidate blocks (q0 = 30000) more keys tie than the
+    selection lists, so it takes the full-row path; with ~1 000 (q0 = 8000) the ties of the
+    full key are broken inside the listed keys (lowest blocks first)."""
+    k, T = 512, 96
     shape = with_selection(WL.shape, 8, k)
     nblk = -(-(q0 + T) // 8)
     kb = _integer_index(shape, 1, nblk, 3)[0].to(DEV)
