@@ -317,6 +317,31 @@ def test_prefill_topk_exact_ties(q0):
     assert np.array_equal(idx.cpu().numpy(), ref)
 
 
+@pytest.mark.gpu
+def test_prefill_topk_sample_bound_too_high():
+    """Prefill top-k when the sampled lower bound of the threshold overshoots: only every 16th
+    block scores above -1 (exactly the blocks a 1024-key sample of a ~16 000-block row reads,
+    with integer values that tie), so fewer than k-1 blocks reach the sample's bound and the
+    full-row selection must give the oracle's exact result, ties to the lowest block."""
+    k, T, q0 = 512, 8, 128000
+    shape = with_selection(WL.shape, 8, k)
+    nblk = -(-(q0 + T) // 8)
+    j = torch.arange(nblk)
+    kb = torch.zeros((nblk, shape.proxy_dim))
+    kb[:, 0] = torch.where(j % 16 == 0, (j // 16) % 256, torch.full_like(j, -1)).float()
+    kb = kb.to(torch.bfloat16).to(DEV)
+    qp = torch.zeros((T, shape.proxy_dim))
+    qp[:, 0] = 1.0
+    qp = qp.to(torch.bfloat16).to(DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    sgqa.indexer_topk(shape, qp, kb, [q0], idx)
+    torch.cuda.synchronize()
+    t = np.arange(q0, q0 + T)
+    sc = oracle.scores(bits(qp), t, 8, parity.widen(bits(kb)), width=int(t.max()) // 8)
+    ref = oracle.topk(sc, t, 8, k)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+
+
 def _w_kt(wl, seed):
     """The key projection of the synthetic recipe as bf16 W^T [P, Hkv*d]."""
     return inputs.proxy_weights(wl, seed, DEV)[1].t().contiguous().to(torch.bfloat16)
