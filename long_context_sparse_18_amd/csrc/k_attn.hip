@@ -734,20 +734,25 @@ __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
     }
 }
 
+// Decode, split over the selection: a workgroup takes one (sequence, KV group) and nw
+// consecutive splits of its selection entries, one split per wave.  The waves' partial
+// softmax states are combined in LDS (in wave order, so the sums do not depend on timing)
+// and the workgroup writes one partial state; k_attn_decode_merge combines the workgroups'.
 template <int D, bool kFp8>
 __global__ __launch_bounds__(512) void k_attn_decode_part(AttnArgs a)
 {
     extern __shared__ __align__(16) uint16_t lds[];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int nw = blockDim.x >> 6;
     const int col = lane & 15, q4 = lane >> 4;
-    const int s = blockIdx.y;
-    const int split = blockIdx.x;
+    const int s = blockIdx.y / a.Hkv;
+    const int g = blockIdx.y - s * a.Hkv;
+    const int split = blockIdx.x * nw + wave;
     const int64_t t = a.qpos.v[s];
     const int64_t c = t / a.B;
     const int nvalid = (int)((c + 1 < a.k) ? c + 1 : a.k);
     const int e0 = split * a.entries_per_split;
     const int e1 = min(e0 + a.entries_per_split, nvalid);
-    const int g = wave;
     const int hpg = a.Hq / a.Hkv;
 
     bf16x8 qf[D / 32];
@@ -771,26 +776,66 @@ __global__ __launch_bounds__(512) void k_attn_decode_part(AttnArgs a)
         }
     }
 
+    // combine the waves: (max, sums) per (wave, head), then every wave's accumulators scaled
+    // to the workgroup's maximum, summed over the waves in order by the whole workgroup.
+    // The LDS of the attention (V buffers, windows) is reused: 64 D + 192 bytes per wave.
     const float l = sum_across_rows(st.l);
     const float l32 = sum_across_rows(st.l32);
-    if (col < hpg) {
-        const int h = g * hpg + col;
-        const int64_t slot = ((int64_t)s * a.nsplit + split) * a.Hq + h;
-        float *po = a.part_o + slot * D + q4 * 4;
+    float *accb = reinterpret_cast<float *>(lds);  // [nw][64 lanes][D / 4]
+    float *mlb = accb + nw * 64 * (D / 4);          // [nw][16 heads][3]
+    __syncthreads();  // every wave is done with its V buffer and window
+    if (q4 == 0) {
+        mlb[(wave * 16 + col) * 3 + 0] = st.m;
+        mlb[(wave * 16 + col) * 3 + 1] = l;
+        mlb[(wave * 16 + col) * 3 + 2] = l32;
+    }
+    __syncthreads();
+    const float neg_inf = -__builtin_inff();
+    float M = neg_inf;
+    for (int w = 0; w < nw; ++w)
+        M = fmaxf(M, mlb[(w * 16 + col) * 3]);
+    const float f = st.m == neg_inf ? 0.f : fast_exp2(st.m - M);
+    float *mine = accb + (wave * 64 + lane) * (D / 4);
 #pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt)
-            *reinterpret_cast<f32x4 *>(po + mt * 16) = st.acc[mt];
-        if (q4 == 0) {
-            a.part_ml[slot * 3 + 0] = st.m;
-            a.part_ml[slot * 3 + 1] = l;
-            a.part_ml[slot * 3 + 2] = l32;
+    for (int mt = 0; mt < D / 16; ++mt)
+        *reinterpret_cast<f32x4 *>(mine + mt * 4) = st.acc[mt] * f;
+    __syncthreads();
+    const int64_t slot0 = ((int64_t)s * a.npart + blockIdx.x) * a.Hq + (int64_t)g * hpg;
+    // value v = (head v / D, dim v % D): consecutive threads write consecutive dims
+    for (int v = threadIdx.x; v < hpg * D; v += nw * 64) {
+        const int head = v / D, dim = v - head * D;
+        const int src = (((dim & 15) >> 2) * 16 + head) * (D / 4) + (dim >> 4) * 4 + (dim & 3);
+        float o = 0.f;
+        for (int w = 0; w < nw; ++w)
+            o += accb[w * 64 * (D / 4) + src];
+        a.part_o[(slot0 + head) * D + dim] = o;
+    }
+    if (threadIdx.x < hpg) {
+        const int head = threadIdx.x;
+        float m = neg_inf, ls = 0.f, l32s = 0.f;
+        for (int w = 0; w < nw; ++w)
+            m = fmaxf(m, mlb[(w * 16 + head) * 3]);
+        for (int w = 0; w < nw; ++w) {
+            const float mw = mlb[(w * 16 + head) * 3];
+            const float fw = mw == neg_inf ? 0.f : fast_exp2(mw - m);
+            ls += mlb[(w * 16 + head) * 3 + 1] * fw;
+            l32s += mlb[(w * 16 + head) * 3 + 2] * fw;
         }
+        a.part_ml[(slot0 + head) * 3 + 0] = m;
+        a.part_ml[(slot0 + head) * 3 + 1] = ls;
+        a.part_ml[(slot0 + head) * 3 + 2] = l32s;
     }
 }
 
-// Exact merge of the split partial states of one (sequence, head), then the gate.
-// One thread per output dimension; the per-split (max, sums) go through LDS once.
-constexpr int kMaxSplits = 64;
+// Exact merge of the workgroups' partial states of one (sequence, head), then the gate.
+// One thread per output dimension.  Every thread first issues the loads of its dimension's
+// partial outputs of all parts (clamped addresses, no branch, so they are in flight
+// together), then the (max, sums) go through LDS once; the merge waits for memory once.
+constexpr int kMaxSplits = 32;  // decode_split_plan never makes more
+#ifndef SGQA_DECODE_WAVES
+#define SGQA_DECODE_WAVES 8
+#endif
+constexpr int kDecodeWaves = SGQA_DECODE_WAVES;  // splits (waves) per decode workgroup
 
 __global__ __launch_bounds__(256) void k_attn_decode_merge(AttnArgs a)
 {
@@ -798,9 +843,15 @@ __global__ __launch_bounds__(256) void k_attn_decode_merge(AttnArgs a)
     __shared__ float l_sh[kMaxSplits];
     __shared__ float l32_sh[kMaxSplits];
     const int s = blockIdx.y, h = blockIdx.x;
-    const int D = a.d, ns = a.nsplit, tid = threadIdx.x;
+    const int D = a.d, ns = a.npart, tid = threadIdx.x;
     const float neg_inf = -__builtin_inff();
-    const int64_t base = (int64_t)s * ns * a.Hq + h;  // slot of split 0
+    const int64_t base = (int64_t)s * ns * a.Hq + h;  // slot of part 0
+    const int64_t step = (int64_t)a.Hq * D;
+    const float *po = a.part_o + base * D + (tid < D ? tid : D - 1);
+    float ov[kMaxSplits];
+#pragma unroll
+    for (int i = 0; i < kMaxSplits; ++i)
+        ov[i] = po[(i < ns ? i : ns - 1) * step];
     if (tid < ns) {
         const float *ml = a.part_ml + (base + (int64_t)tid * a.Hq) * 3;
         w_sh[tid] = ml[0];
@@ -811,23 +862,17 @@ __global__ __launch_bounds__(256) void k_attn_decode_merge(AttnArgs a)
     float M = neg_inf;
     for (int i = 0; i < ns; ++i)
         M = fmaxf(M, w_sh[i]);
-    float Lsum = 0.f, L32 = 0.f;
-    for (int i = 0; i < ns; ++i) {
-        const float w = w_sh[i] == neg_inf ? 0.f : fast_exp2(w_sh[i] - M);
-        Lsum += l_sh[i] * w;
-        L32 += l32_sh[i] * w;
+    float Lsum = 0.f, L32 = 0.f, o = 0.f;
+#pragma unroll
+    for (int i = 0; i < kMaxSplits; ++i) {
+        if (i < ns) {
+            const float w = w_sh[i] == neg_inf ? 0.f : fast_exp2(w_sh[i] - M);
+            Lsum += l_sh[i] * w;
+            L32 += l32_sh[i] * w;
+            o += ov[i] * w;
+        }
     }
-    __syncthreads();
-    if (tid < ns)
-        w_sh[tid] = w_sh[tid] == neg_inf ? 0.f : fast_exp2(w_sh[tid] - M);
-    __syncthreads();
     if (tid < D) {
-        const float *po = a.part_o + base * D + tid;
-        const int64_t step = (int64_t)a.Hq * D;
-        float o = 0.f;
-#pragma unroll 8
-        for (int i = 0; i < ns; ++i)
-            o += po[i * step] * w_sh[i];
         const float gsig = sigmoid_f32(bf16_bits_to_f32(a.gate[(int64_t)s * a.Hq + h]));
         a.out[((int64_t)s * a.Hq + h) * D + tid] = (uint16_t)f32_to_bf16_bits(o * (gsig / Lsum));
     }
@@ -908,15 +953,21 @@ static hipError_t launch_prefill_sliced(const AttnArgs &a0, hipStream_t stream)
 }
 
 template <int D>
-static hipError_t launch_decode_d(const AttnArgs &a, hipStream_t stream)
+static hipError_t launch_decode_d(const AttnArgs &a0, hipStream_t stream)
 {
-    const size_t lds = (size_t)a.Hkv * attn_wave_lds(D);
+    if (a0.nsplit < 1 || a0.nsplit > kMaxSplits)
+        return hipErrorInvalidValue;  // the merge holds at most kMaxSplits partial states
+    AttnArgs a = a0;
+    const int nw = a.nsplit < kDecodeWaves ? a.nsplit : kDecodeWaves;
+    a.npart = (a.nsplit + nw - 1) / nw;
+    // the V buffers and windows of the waves hold their combine buffers (64 D + 192 B each)
+    static_assert(attn_wave_lds(D) >= (size_t)64 * D + 192, "decode combine buffer");
+    const size_t lds = (size_t)nw * attn_wave_lds(D);
+    const dim3 grid((unsigned)a.npart, (unsigned)(a.rows * a.Hkv));
     if (a.kq)
-        hipLaunchKernelGGL((k_attn_decode_part<D, true>), dim3((unsigned)a.nsplit, (unsigned)a.rows),
-                           dim3(64 * a.Hkv), lds, stream, a);
+        hipLaunchKernelGGL((k_attn_decode_part<D, true>), grid, dim3(64 * nw), lds, stream, a);
     else
-        hipLaunchKernelGGL((k_attn_decode_part<D, false>), dim3((unsigned)a.nsplit, (unsigned)a.rows),
-                           dim3(64 * a.Hkv), lds, stream, a);
+        hipLaunchKernelGGL((k_attn_decode_part<D, false>), grid, dim3(64 * nw), lds, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;

@@ -119,10 +119,11 @@ struct AttnArgs {
     uint16_t *out;
     float *lse;
     // decode split-K partials
-    float *part_o;           // [nseq][nsplit][Hq][d]
-    float *part_ml;          // [nseq][nsplit][Hq][3]: max, bf16-weight sum, fp32-weight sum
-    int32_t nsplit;
+    float *part_o;           // [nseq][npart][Hq][d]
+    float *part_ml;          // [nseq][npart][Hq][3]: max, bf16-weight sum, fp32-weight sum
+    int32_t nsplit;          // splits of the selection entries (one wave each)
     int32_t entries_per_split;
+    int32_t npart;           // partial states per (sequence, head): one per workgroup
     int64_t window;          // sliding-window attention: tokens per window
     // sliced prefill: launch `slice` of `nslices` over each query's blocks, parking the
     // per-lane softmax state (state_stride floats per lane) in `state`

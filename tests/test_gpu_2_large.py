@@ -296,24 +296,27 @@ def test_index_from_keys_decode_1m():
     say("fused index 1M x 16: ok")
 
 
-def test_sliding_window_32k_real_shape():
-    """Gated sliding-window attention (window 512) at the real layer shape on the 32K
-    prefill, sampled rows against the oracle."""
-    wl = WORKLOADS[1]
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_sliding_window_real_shape(cfg):
+    """Gated sliding-window attention (window 512) at the real layer shape on the 32K and the
+    128K prefill (the latter the benchmark's launch), sampled rows against the oracle."""
+    wl = WORKLOADS[cfg]
     shape = wl.shape
-    say("swa: generating prefill-32k")
+    say(f"swa: generating {wl.name}")
     d = inputs.make_prefill(wl, 11, DEV)
     out = torch.empty_like(d["Q"])
     lse = torch.empty((wl.T, shape.num_q_heads), dtype=torch.float32, device=DEV)
     scale = 1.0 / math.sqrt(shape.head_dim)
     sgqa.swa_prefill(shape, d["Q"], d["K"], d["V"], d["G"], 0, wl.L, 512, scale, out, lse)
     torch.cuda.synchronize()
-    rows = np.array(sorted({0, 1, 510, 511, 512, 513, 4095, wl.T - 1} |
-                           set(np.random.default_rng(5).integers(0, wl.T, 48).tolist())))
+    rows = np.array(sorted({0, 1, 15, 16, 510, 511, 512, 513, 4095, wl.T - 17, wl.T - 1} |
+                           set(np.random.default_rng(5 + cfg).integers(0, wl.T, 48).tolist())))
     rt = torch.from_numpy(rows).to(DEV)
     o_ref, l_ref = oracle.window_attention(bits(d["Q"].index_select(0, rt)), rows, bits(d["K"]),
                                            bits(d["V"]), bits(d["G"].index_select(0, rt)), 512,
                                            scale)
     st = parity.check_attention(bits(out.index_select(0, rt)), o_ref,
                                 lse.index_select(0, rt).cpu().numpy(), l_ref)
-    say(f"swa 32k: {st}")
+    say(f"swa {wl.name}: {st}")
+    del d, out, lse
+    torch.cuda.empty_cache()
