@@ -383,6 +383,36 @@ def test_tiny_index_from_keys(tiny, B):
         assert torch.equal(kb[b][mask], before[b][mask])
 
 
+@pytest.mark.parametrize("B", [8, 16])
+def test_index_from_keys_odd_width(B):
+    """Fused index maintenance where the key width (1 KV head x 192) is not a multiple of the
+    kernel's 128-column step (a 64-column last step), proxy 64, for B = 8 and 16 (two row
+    groups per step); then a rebuild of blocks [70, 200), which starts inside a workgroup's
+    range of a full build, must give the same bits as the full build."""
+    from long_context_sparse_18_amd.configs import LayerShape
+    shape = LayerShape(num_q_heads=8, num_kv_heads=1, head_dim=192, proxy_dim=64,
+                       block_size=B, topk_blocks=16)
+    lens = [3001, 1024, 37]
+    n, Lmax = len(lens), max(lens)
+    g = torch.Generator(device=DEV).manual_seed(21)
+    K = torch.randn((n, Lmax, 1, 192), generator=g, device=DEV).to(torch.bfloat16)
+    wkt = (torch.randn((64, 192), generator=g, device=DEV) / 14).to(torch.bfloat16)
+    nblk = -(-Lmax // B)
+    kb = torch.full((n, nblk, 64), 7.0, dtype=torch.bfloat16, device=DEV)
+    sgqa.index_build_from_keys(shape, K, wkt, kb, lens)
+    torch.cuda.synchronize()
+    for b, L_ in enumerate(lens):
+        ref = oracle.index_build_from_keys(bits(K[b, :L_]), bits(wkt), B)
+        st = parity.check_kb_projected(bits(kb[b, : ref.shape[0]]), ref)
+        assert st["kb_bit_equal_to_rne"] >= 0.99, st
+        assert torch.all(kb[b, ref.shape[0]:] == 7.0)
+    full = kb.clone()
+    kb[0, 70:200] = 0
+    sgqa.index_build_from_keys(shape, K[0], wkt, kb[0], [lens[0]], 70, 200)
+    torch.cuda.synchronize()
+    assert torch.equal(kb, full)
+
+
 def test_quantize_fp8_bit_exact():
     """Row quantisation to E4M3 codes and fp32 scales equals the oracle bit for bit, on rows of
     32, 64, 192 and 256 values spanning 2^-60 .. 2^60 in magnitude, with an all-zero row and
