@@ -900,16 +900,30 @@ __global__ __launch_bounds__(NT) void k_select2(SelectArgs a)
     const int ns = (n + stride - 1) / stride;
     {
         constexpr int kSp = kSel2Samp / NT;  // samples per thread, loaded together
-        float v[kSp];
+        float sv[kSp];
 #pragma unroll
         for (int u = 0; u < kSp; ++u) {
             const int e = u * NT + tid;
-            v[u] = srow[(int64_t)(e < ns ? e : 0) * stride];
+            sv[u] = srow[(int64_t)(e < ns ? e : 0) * stride];
         }
 #pragma unroll
         for (int u = 0; u < kSp; ++u)
             if (u * NT + tid < ns)
-                samp[u * NT + tid] = score_key(v[u]);
+                samp[u * NT + tid] = score_key(sv[u]);
+    }
+    // The whole row, 16 keys per thread and group (at most kIt groups per thread), is requested
+    // now: its loads are in flight while T0 is selected from the sample.  Rows start 256-byte
+    // aligned and hold at least round_up(n, 64) floats, so a group that starts inside the row
+    // reads inside it; groups past the row re-read group 0 and are skipped.
+    constexpr int kIt = kSel2MaxCand / (16 * NT);
+    const u32x4 *row4 = reinterpret_cast<const u32x4 *>(srow);
+    u32x4 v[kIt][4];
+#pragma unroll
+    for (int it = 0; it < kIt; ++it) {
+        const int g = it * NT + tid;
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            v[it][u] = row4[(g * 16 < n ? g : 0) * 4 + u];
     }
     const int64_t share = ((int64_t)keep * ns + n - 1) / n;  // expected kept samples, rounded up
     const int q = (int)(2 * share + 16 < ns ? 2 * share + 16 : ns);
@@ -921,21 +935,18 @@ __global__ __launch_bounds__(NT) void k_select2(SelectArgs a)
     if (tid == 0)
         n_cand = 0;
     __syncthreads();
-    // 16 keys per thread and iteration, four 16-byte loads in flight (rows start 256-byte
-    // aligned and hold at least round_up(n, 64) floats, so the last group reads inside it)
-    const u32x4 *row4 = reinterpret_cast<const u32x4 *>(srow);
-    for (int g0 = 0; g0 * 16 < n; g0 += NT) {
-        const int g = g0 + tid;
-        u32x4 v[4];
+    // 16 keys per thread and group (the whole row, requested above)
 #pragma unroll
-        for (int u = 0; u < 4; ++u)
-            v[u] = g * 16 < n ? row4[g * 4 + u] : u32x4{0u, 0u, 0u, 0u};
+    for (int it = 0; it < kIt; ++it) {
+        if (it * NT * 16 >= n)
+            break;  // uniform: every thread leaves together
+        const int g = it * NT + tid;
         uint32_t kk[16];
         int cnt = 0;
 #pragma unroll
         for (int e = 0; e < 16; ++e) {
             const int j = g * 16 + e;
-            kk[e] = score_key(__uint_as_float(v[e >> 2][e & 3]));
+            kk[e] = score_key(__uint_as_float(v[it][e >> 2][e & 3]));
             cnt += (j < n && kk[e] >= t0key) ? 1 : 0;
         }
         int slot = wave_append(cnt, &n_cand);
