@@ -2,8 +2,8 @@
 a 1024-token sequence: head_dim 128; 1, 2, 4 and 8 query heads per KV group; 3 KV groups
 (which do not divide the 8 XCDs, so the kernels take their other workgroup mapping) and 8;
 proxy widths 32 to 512; B from 2 to 16.  Stages: index, top-k and attention of the prefill,
-decode for three sequences of different lengths, sliding-window attention, the index from the
-keys, and the fixed-selection backward."""
+decode for three sequences of different lengths (also with FP8 storage), sliding-window
+attention, the index from the keys, and the fixed-selection backward."""
 import math
 
 import numpy as np
@@ -140,3 +140,55 @@ def test_shape_backward(case):
     for name, r in zip(("dq", "dk", "dv", "dg"), ref):
         st.update(parity.check_grad(name, grads[name].cpu().numpy(), r))
     say(f"shapes {_id(shape)} backward: {st}")
+
+
+def test_shape_decode_fp8(case):
+    """The FP8-storage decode path (E4M3 rows with one fp32 scale each for the index and the
+    K/V caches) against the oracle on the dequantised values."""
+    wl, d, host = case
+    shape = wl.shape
+    if shape.proxy_dim not in (64, 128, 256, 512):
+        pytest.skip("the FP8 index takes proxy widths 64 to 512 (the API reports 32 unsupported)")
+    B, k = shape.block_size, shape.topk_blocks
+    lens = [1024, 333]
+    n = len(lens)
+    K = d["K"].unsqueeze(0).expand(n, -1, -1, -1).contiguous()
+    V = d["V"].unsqueeze(0).expand(n, -1, -1, -1).contiguous()
+    kp = d["kp"].unsqueeze(0).expand(n, -1, -1).contiguous()
+    Q = torch.stack([d["Q"][L_ - 1] for L_ in lens])
+    G = torch.stack([d["G"][L_ - 1] for L_ in lens])
+    qp = torch.stack([d["qp"][L_ - 1] for L_ in lens])
+    kb = torch.empty((n, wl.nblk, shape.proxy_dim), dtype=torch.bfloat16, device=DEV)
+    sgqa.index_build(shape, kp, kb, lens)
+    kbq = torch.empty(kb.shape, dtype=torch.uint8, device=DEV)
+    kbs = torch.empty(kb.shape[:2], dtype=torch.float32, device=DEV)
+    Kq = torch.empty(K.shape, dtype=torch.uint8, device=DEV)
+    Vq = torch.empty(V.shape, dtype=torch.uint8, device=DEV)
+    Ks = torch.empty(K.shape[:3], dtype=torch.float32, device=DEV)
+    Vs = torch.empty(V.shape[:3], dtype=torch.float32, device=DEV)
+    sgqa.quantize_fp8(kb, kbq, kbs)
+    sgqa.quantize_fp8(K, Kq, Ks)
+    sgqa.quantize_fp8(V, Vq, Vs)
+    idx = torch.empty((n, k), dtype=torch.int32, device=DEV)
+    sgqa.indexer_topk_fp8(shape, qp, kbq, kbs, [L_ - 1 for L_ in lens], idx)
+    out = torch.empty_like(Q)
+    lse = torch.empty((n, shape.num_q_heads), dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(shape.head_dim)
+    sgqa.sparse_attn_decode_fp8(shape, Q, Kq, Vq, Ks, Vs, G, idx, lens, scale, out, lse)
+    torch.cuda.synchronize()
+    for b, L_ in enumerate(lens):
+        t = np.array([L_ - 1])
+        nb = -(-L_ // B)
+        kb_deq = oracle.dequant_rows(kbq[b, :nb].cpu().numpy(), kbs[b, :nb].cpu().numpy())
+        sc = oracle.scores(bits(qp[b:b + 1]), t, B, kb_deq, width=max(1, nb))
+        ref = oracle.topk(sc, t, B, k)
+        got = idx[b].cpu().numpy()
+        parity.check_selection(got, sc[0], int(t[0] // B), k, ref[0])
+        toks = torch.from_numpy(oracle.token_set(got, B, L_ - 1)).to(DEV)
+        kd = oracle.dequant_rows(Kq[b].index_select(0, toks).cpu().numpy(),
+                                 Ks[b].index_select(0, toks).cpu().numpy())
+        vd = oracle.dequant_rows(Vq[b].index_select(0, toks).cpu().numpy(),
+                                 Vs[b].index_select(0, toks).cpu().numpy())
+        o_ref, l_ref = oracle.attend_f64(bits(Q[b]), kd, vd, bits(G[b]), scale)
+        parity.check_attention(bits(out[b:b + 1]), o_ref[None], lse[b:b + 1].cpu().numpy(),
+                               l_ref[None])
