@@ -192,3 +192,61 @@ def test_shape_decode_fp8(case):
         o_ref, l_ref = oracle.attend_f64(bits(Q[b]), kd, vd, bits(G[b]), scale)
         parity.check_attention(bits(out[b:b + 1]), o_ref[None], lse[b:b + 1].cpu().numpy(),
                                l_ref[None])
+
+
+def test_decode_largest_batch():
+    """Decode for the largest batch the API takes (64 sequences), caches of 1 to 1024 tokens
+    on the tiny layer: every sequence's selection and output against the oracle."""
+    from long_context_sparse_18_amd import WORKLOADS
+    wl = WORKLOADS[0]
+    shape = wl.shape
+    B, k = shape.block_size, shape.topk_blocks
+    d = inputs.make_prefill(wl, 9, DEV)
+    lens = [1 + (37 * i) % 1024 for i in range(64)]
+    lens[0], lens[1] = 1024, 1
+    n = len(lens)
+    K = d["K"].unsqueeze(0).expand(n, -1, -1, -1).contiguous()
+    V = d["V"].unsqueeze(0).expand(n, -1, -1, -1).contiguous()
+    kp = d["kp"].unsqueeze(0).expand(n, -1, -1).contiguous()
+    Q = torch.stack([d["Q"][L_ - 1] for L_ in lens])
+    G = torch.stack([d["G"][L_ - 1] for L_ in lens])
+    qp = torch.stack([d["qp"][L_ - 1] for L_ in lens]).unsqueeze(1)
+    kb = torch.empty((n, wl.nblk, shape.proxy_dim), dtype=torch.bfloat16, device=DEV)
+    sgqa.index_build(shape, kp, kb, lens)
+    idx = torch.empty((n, 1, k), dtype=torch.int32, device=DEV)
+    sgqa.indexer_topk(shape, qp, kb, [L_ - 1 for L_ in lens], idx)
+    out = torch.empty_like(Q)
+    lse = torch.empty((n, shape.num_q_heads), dtype=torch.float32, device=DEV)
+    scale = 1.0 / math.sqrt(shape.head_dim)
+    sgqa.sparse_attn_decode(shape, Q, K, V, G, idx.view(n, -1), lens, scale, out, lse)
+    torch.cuda.synchronize()
+    Kb, Vb = bits(d["K"]), bits(d["V"])
+    for b, L_ in enumerate(lens):
+        t = np.array([L_ - 1])
+        nb = -(-L_ // B)
+        sc = oracle.scores(bits(qp[b]), t, B, parity.widen(bits(kb[b, :nb])), width=max(1, nb))
+        ref = oracle.topk(sc, t, B, k)
+        got = idx[b, 0].cpu().numpy()
+        parity.check_selection(got, sc[0], int(t[0] // B), k, ref[0])
+        o_ref, l_ref = oracle.sparse_attention(bits(Q[b:b + 1]), t, Kb[:L_], Vb[:L_],
+                                               bits(G[b:b + 1]), got[None, :], B, scale)
+        parity.check_attention(bits(out[b:b + 1]), o_ref, lse[b:b + 1].cpu().numpy(), l_ref)
+
+
+def test_prefill_largest_selection_32k():
+    """The largest selection the API takes at B = 8 (k = 4 096 blocks = 32 768 tokens) on the
+    32K prefill at the real layer shape, where every query attends its whole causal history:
+    sampled rows (block edges, the k*B edge, random rows) against the oracle."""
+    from long_context_sparse_18_amd import WORKLOADS
+    from long_context_sparse_18_amd.configs import with_selection
+    wl = WORKLOADS[1]
+    shape = with_selection(wl.shape, 8, 4096)
+    say("shapes: 32K prefill at k = 4096")
+    d = inputs.make_prefill(wl, 13, DEV)
+    res = run_prefill(shape, d, 0, wl.L)
+    rows = parity.stratified_rows(0, wl.T, 8, 4096, 16, 3)
+    st = check_prefill_rows(shape, d, res, 0, rows)
+    say(f"shapes: 32K k=4096: {st}")
+    assert st["exact_iso"] == st["rows"]
+    del d, res
+    torch.cuda.empty_cache()
