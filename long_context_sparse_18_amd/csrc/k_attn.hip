@@ -31,6 +31,13 @@ constexpr int kSlots = 32;  // token slots per step
 // Each wave stages V in its own LDS region, so only the wave's own LDS operations need
 // ordering: they execute in issue order, and these fences keep the compiler from moving
 // LDS accesses across the hand-off.  Waves of one workgroup never wait for each other.
+// This thread's wave within the workgroup, as a wave-uniform (scalar) value: values derived
+// from it (rows, groups, pointers) then live in scalar registers.
+__device__ __forceinline__ int wave_index()
+{
+    return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
+}
+
 __device__ __forceinline__ void wave_lds_handoff()
 {
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -141,7 +148,7 @@ constexpr size_t attn_wave_lds(int D)
 template <int D>
 __device__ __forceinline__ int32_t *entry_window(uint16_t *lds)
 {
-    const int nw = blockDim.x >> 6, wave = threadIdx.x >> 6;
+    const int nw = blockDim.x >> 6, wave = wave_index();
     return reinterpret_cast<int32_t *>(lds + nw * attn_vbuf_elems(D)) + wave * kWin;
 }
 
@@ -187,31 +194,30 @@ __device__ __forceinline__ void attend_range(const Rows &rows, int Hkv, const Sr
         const uint64_t vmask = __ballot(valid);
         const int s_lo = (int)(s_ld & 0xffffffff), s_hi = (int)(s_ld >> 32);
 
-        // K rows for the two 16-slot A tiles (bf16: D/32 loads of 8 values; FP8: D/64 loads
-        // of 16 codes).
-        constexpr int kKLoads = Rows::kFp8 ? D / 64 : D / 32;
+        // Row pieces: flat piece f = lane + 64 ci covers slot f / pieces, piece f % pieces
+        // (pieces of 8 bf16 values, or of 16 FP8 codes), so each load instruction reads whole
+        // rows.  bf16 K rows are read this way too and staged in LDS for the A operands: read
+        // straight in the operand layout (16 rows x 64 bytes per instruction) the same gathers
+        // took 135 instead of 113 ms in a loads-only copy of the 128K prefill.
+        constexpr int kVPieces = Rows::kFp8 ? D / 16 : D / 8;
+        constexpr int kVLoads = Rows::kFp8 ? D / 32 : D / 16;
+        // FP8 K rows for the two 16-slot A tiles, straight in the operand layout (D/64 loads
+        // of 16 codes)
+        constexpr int kKLoads = Rows::kFp8 ? D / 64 : 1;
         u32x4 kv[2][kKLoads];
+        u32x4 kp[Rows::kFp8 ? 1 : kVLoads];
+        if constexpr (Rows::kFp8) {
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int src = h * 16 + col;
-            const int64_t sk = ((int64_t)(uint32_t)__shfl(s_lo, src)) |
-                               ((int64_t)__shfl(s_hi, src) << 32);
-            if constexpr (Rows::kFp8) {
+            for (int h = 0; h < 2; ++h) {
+                const int src = h * 16 + col;
+                const int64_t sk = ((int64_t)(uint32_t)__shfl(s_lo, src)) |
+                                   ((int64_t)__shfl(s_hi, src) << 32);
                 const uint8_t *kr = rows.Kg + sk * row_elems + q4 * 16;
 #pragma unroll
                 for (int k2 = 0; k2 < kKLoads; ++k2)
                     kv[h][k2] = load16(kr + k2 * 64);
-            } else {
-                const uint16_t *kr = rows.Kg + sk * row_elems + q4 * 8;
-#pragma unroll
-                for (int kk = 0; kk < kKLoads; ++kk)
-                    kv[h][kk] = load16(kr + kk * 32);
             }
         }
-        // V pieces: flat piece f = lane + 64 ci covers slot f / pieces, piece f % pieces
-        // (pieces of 8 bf16 values, or of 16 FP8 codes).
-        constexpr int kVPieces = Rows::kFp8 ? D / 16 : D / 8;
-        constexpr int kVLoads = Rows::kFp8 ? D / 32 : D / 16;
         u32x4 vv[kVLoads];
 #pragma unroll
         for (int ci = 0; ci < kVLoads; ++ci) {
@@ -219,10 +225,13 @@ __device__ __forceinline__ void attend_range(const Rows &rows, int Hkv, const Sr
             const int slot = f / kVPieces, piece = f - slot * kVPieces;
             const int64_t sv = ((int64_t)(uint32_t)__shfl(s_lo, slot)) |
                                ((int64_t)__shfl(s_hi, slot) << 32);
-            if constexpr (Rows::kFp8)
+            if constexpr (Rows::kFp8) {
                 vv[ci] = load16(rows.Vg + sv * row_elems + piece * 16);
-            else
-                vv[ci] = load16(rows.Vg + sv * row_elems + piece * 8);
+            } else {  // the K and V pieces of a row share their offset
+                const int64_t off = sv * row_elems + piece * 8;
+                kp[ci] = load16(rows.Kg + off);
+                vv[ci] = load16(rows.Vg + off);
+            }
         }
         // FP8: the scales of this lane's slot (lane & 31); others read them by shuffle
         float k_scale = 1.0f, v_scale = 1.0f;
@@ -231,6 +240,20 @@ __device__ __forceinline__ void attend_range(const Rows &rows, int Hkv, const Sr
             v_scale = rows.Vs[s_ld * Hkv];
         }
 
+        // bf16: stage the K rows in the wave's buffer (the previous step's transposed V reads
+        // are done at the handoff), then read the A operands from it
+        if constexpr (!Rows::kFp8) {
+            wave_lds_handoff();
+#pragma unroll
+            for (int ci = 0; ci < kVLoads; ++ci) {
+                const int f = lane + 64 * ci;
+                const int slot = f / kVPieces, piece = f - slot * kVPieces;
+                uint2 *dst = reinterpret_cast<uint2 *>(vs + slot * kLd + piece * 8);
+                dst[0] = uint2{kp[ci][0], kp[ci][1]};
+                dst[1] = uint2{kp[ci][2], kp[ci][3]};
+            }
+            wave_lds_handoff();
+        }
         // S^T = K Q^T for slots 0-15 and 16-31.
         f32x4 sc[2];
 #pragma unroll
@@ -249,8 +272,11 @@ __device__ __forceinline__ void attend_range(const Rows &rows, int Hkv, const Sr
                     sc[h][r] *= __shfl(k_scale, h * 16 + q4 * 4 + r);
             } else {
 #pragma unroll
-                for (int kk = 0; kk < kKLoads; ++kk)
-                    sc[h] = mfma_16x16x32(as_bf16x8(kv[h][kk]), qf[kk], sc[h]);
+                for (int kk = 0; kk < D / 32; ++kk) {
+                    const u32x4 ka = *reinterpret_cast<const u32x4 *>(
+                        vs + (h * 16 + col) * kLd + kk * 32 + q4 * 8);
+                    sc[h] = mfma_16x16x32(as_bf16x8(ka), qf[kk], sc[h]);
+                }
             }
         }
 
@@ -444,7 +470,7 @@ __device__ __forceinline__ void load_state(WaveState<D> &st, const float *p)
 template <bool kGroupPerXcd, typename Args>
 __device__ __forceinline__ bool wave_row_group(const Args &a, int64_t &r, int &g)
 {
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_index();
     if constexpr (kGroupPerXcd) {
         const int R = 8 / a.Hkv;
         const int x = blockIdx.x & 7;
@@ -469,7 +495,7 @@ template <int D, bool kGroupPerXcd>
 __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
 {
     extern __shared__ __align__(16) uint16_t lds[];
-    const int wave = threadIdx.x >> 6;
+    const int wave = wave_index();
     const int hpg = a.Hq / a.Hkv;
     int64_t r;
     int g;
@@ -554,7 +580,7 @@ __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
     constexpr int kLd = D + 16;
     constexpr int kTile = 2 * kSlots * kLd;  // K then V rows of one step
     const int hpg = a.Hq / a.Hkv;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_index(), lane = threadIdx.x & 63;
     const int nwaves = (int)(blockDim.x >> 6);      // heads per workgroup
     const int hs = (hpg + nwaves - 1) / nwaves;     // workgroups per (query tile, group)
     const int g = (int)(blockIdx.x % (unsigned)a.Hkv);
@@ -742,7 +768,7 @@ template <int D, bool kFp8>
 __global__ __launch_bounds__(512) void k_attn_decode_part(AttnArgs a)
 {
     extern __shared__ __align__(16) uint16_t lds[];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_index(), lane = threadIdx.x & 63;
     const int nw = blockDim.x >> 6;
     const int col = lane & 15, q4 = lane >> 4;
     const int s = blockIdx.y / a.Hkv;
@@ -1240,7 +1266,7 @@ template <int D, bool kGroupPerXcd>
 __global__ __launch_bounds__(512) void k_bwd_dq(BwdArgs a)
 {
     extern __shared__ __align__(16) uint16_t lds[];
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_index(), lane = threadIdx.x & 63;
     const int col = lane & 15, q4 = lane >> 4;
     const int hpg = a.Hq / a.Hkv;
     int64_t r;
@@ -1296,7 +1322,7 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
     constexpr int kLd = D + 8;
     const int ntile = (a.B + 15) / 16;
     const int g = (int)(blockIdx.x % (unsigned)a.Hkv);
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = wave_index(), lane = threadIdx.x & 63;
     const int64_t tid = (int64_t)(blockIdx.x / (unsigned)a.Hkv) * 4 + wave;  // tile index
     if (tid >= a.nblk * ntile)
         return;
