@@ -1384,20 +1384,34 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
         r = (w << 5) + b;
         return true;
     };
-    // q and dA of the group's heads of row r (head col, dims 8 q4 + 32 kk), lse / D of heads
-    // 4 q4 + i.  The loads are unconditional, so none of them makes the wave wait before the
-    // values are used: lanes past the group's heads re-read its last head, whose P and dz are
-    // masked to zero (so those staged rows meet only zero weights).
+    // q and dA of the group's heads of row r, lse / D of heads 4 q4 + i.  The loads are
+    // unconditional, so none of them makes the wave wait before the values are used: staged
+    // rows past the group's heads repeat its last head, whose P and dz are masked to zero (so
+    // those rows meet only zero weights).
     // lse and D come one per lane (head col) and reach the lanes holding heads 4 q4 + i by
     // shuffles where they are used.
+    // whole rows: 16-byte piece f = lane + 64 kk of the 16 staged rows is piece f % (D/8) of
+    // row f / (D/8); the group's heads are contiguous, so each load instruction reads whole
+    // rows (rows past the group's heads repeat its last head).  The byte offsets within the
+    // group's rows are the same for every query row.
+    uint32_t poff[D / 32];
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        const int f = lane + 64 * kk;
+        const int hd = f / (D / 8), pc = f - hd * (D / 8);
+        poff[kk] = (uint32_t)(((hd < hpg ? hd : hpg - 1) * D + pc * 8) * 2);
+    }
     auto fetch = [&](int64_t r, u32x4 (&qa)[D / 32], u32x4 (&da)[D / 32], float &l1,
                      float &ds1) {
-        const int64_t hr = r * a.Hq + (int64_t)g * hpg + (col < hpg ? col : hpg - 1);
+        const int64_t h0 = r * a.Hq + (int64_t)g * hpg;  // the group's first head of row r
+        const char *qb = reinterpret_cast<const char *>(a.q + h0 * D);
+        const char *db = reinterpret_cast<const char *>(a.da + h0 * D);
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
-            qa[kk] = load16(a.q + hr * D + kk * 32 + q4 * 8);
-            da[kk] = load16(a.da + hr * D + kk * 32 + q4 * 8);
+            qa[kk] = load16(qb + poff[kk]);
+            da[kk] = load16(db + poff[kk]);
         }
+        const int64_t hr = h0 + (col < hpg ? col : hpg - 1);
         l1 = a.lse[hr];  // natural log; scaled to base 2 where it is used
         ds1 = a.dsum[hr];
     };
@@ -1405,8 +1419,10 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
         wave_lds_handoff();
 #pragma unroll
         for (int kk = 0; kk < D / 32; ++kk) {
-            uint2 *dq_ = reinterpret_cast<uint2 *>(qs + col * kLd + kk * 32 + q4 * 8);
-            uint2 *dd_ = reinterpret_cast<uint2 *>(ds + col * kLd + kk * 32 + q4 * 8);
+            const int f = lane + 64 * kk;
+            const int hd = f / (D / 8), pc = f - hd * (D / 8);
+            uint2 *dq_ = reinterpret_cast<uint2 *>(qs + hd * kLd + pc * 8);
+            uint2 *dd_ = reinterpret_cast<uint2 *>(ds + hd * kLd + pc * 8);
             dq_[0] = uint2{qa[kk][0], qa[kk][1]};
             dq_[1] = uint2{qa[kk][2], qa[kk][3]};
             dd_[0] = uint2{da[kk][0], da[kk][1]};
