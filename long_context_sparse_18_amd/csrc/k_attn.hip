@@ -504,12 +504,18 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
     const int64_t t = a.q_start + r;
     const int64_t c = t / a.B;
     const int nvalid = (int)((c + 1 < a.k) ? c + 1 : a.k);
+    // Rows with a short history (c < 2k, the launcher's own threshold for slicing at all) are
+    // attended in one pass, in the last slice: then a row's result depends only on the row,
+    // not on which other rows share its launch.
+    const bool sliced = a.nslices > 1 && c >= 2 * (int64_t)a.k;
+    if (a.nslices > 1 && !sliced && a.slice + 1 < a.nslices)
+        return;
 
     bf16x8 qf[D / 32];
     load_q<D>(a.q + (r * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
     WaveState<D> st;
     int e_lo = 0, e_hi = nvalid;
-    if (a.nslices > 1) {
+    if (sliced) {
         // this launch covers the blocks in [c*s/S, c*(s+1)/S) (the last slice also holds the
         // own block c); the idx row is ascending, so that is a contiguous run of entries
         const int64_t lo = c * a.slice / a.nslices;
@@ -539,7 +545,7 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
         e_lo = below_lo;
         e_hi = a.slice + 1 == a.nslices ? nvalid : below_hi;
     }
-    if (a.slice == 0)
+    if (a.slice == 0 || !sliced)
         init_state<D>(st);
     else
         load_state<D>(st, a.state + state_offset(a, r, g));

@@ -525,7 +525,8 @@ sgqa_status sgqa_sparse_attn_prefill(const sgqa_dims *dims, const sgqa_bf16 *q,
         // Six history slices measured best on the 128K prefill (145.8 ms vs 159.8 ms in one
         // pass; 4: 147.6, 8: 148.3, 12: 162.3): each XCD's L2 then holds a sixth of its
         // group's history, while every slice boundary parks ~13 KB of state per row and group.
-        // Short histories gain nothing and stay in one pass.
+        // Short histories gain nothing and stay in one pass (row by row: the kernel attends
+        // rows with c < 2k in one pass even in a sliced launch).
         const int64_t max_cand = (q_start + T - 1) / dims->block_size;
         a.nslices = max_cand >= 2 * (int64_t)dims->topk_blocks ? 6 : 1;
         a.state = static_cast<float *>(workspace);

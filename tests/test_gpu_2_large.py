@@ -52,6 +52,36 @@ def test_prefill_128k():
     torch.cuda.empty_cache()
 
 
+def test_prefill_128k_layer_schedule():
+    """The schedule the benchmark times (8 row chunks, each chunk's top-k on a side stream under
+    the previous chunk's attention) gives the same bits as the stages run one after the other
+    (which test_prefill_128k checks against the oracle)."""
+    from long_context_sparse_18_amd import layer
+    wl = WORKLOADS[2]
+    s = wl.shape
+    say("layer schedule 128K: generating")
+    d = inputs.make_prefill(wl, 2, DEV)
+    ws_t = torch.empty(sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, s, 1, wl.T, wl.L),
+                       dtype=torch.uint8, device=DEV)
+    ws_a = torch.empty(sgqa.workspace_bytes(sgqa.OP_ATTN_PREFILL, s, 1, wl.T, wl.L),
+                       dtype=torch.uint8, device=DEV)
+    ref = run_prefill(s, d, wl.q_start, wl.L, workspace=ws_t, attn_workspace=ws_a)
+    kb = torch.empty_like(ref["kb"])
+    idx = torch.full_like(ref["idx"], -7)
+    out = torch.empty_like(ref["out"])
+    lse = torch.empty_like(ref["lse"])
+    side = torch.cuda.Stream(DEV)
+    layer.prefill_layer(s, d, wl.q_start, wl.L, 1.0 / math.sqrt(s.head_dim), kb, idx, out, lse,
+                        ws_t, ws_a, chunks=8, side_stream=side)
+    torch.cuda.synchronize()
+    for name, a, b in (("kb", kb, ref["kb"]), ("idx", idx, ref["idx"]), ("out", out, ref["out"]),
+                       ("lse", lse, ref["lse"])):
+        assert torch.equal(a, b), name
+    say("layer schedule 128K: identical")
+    del d, ref
+    torch.cuda.empty_cache()
+
+
 def test_chunked_prefill_1m():
     """8192 queries at positions [1040388, 1048580); the chunk starts at offset 4 of block
     130048 and the trailing block holds 4 tokens.  The history index is built first, then
