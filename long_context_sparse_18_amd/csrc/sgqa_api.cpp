@@ -522,13 +522,13 @@ sgqa_status sgqa_sparse_attn_prefill(const sgqa_dims *dims, const sgqa_bf16 *q,
         if (workspace_bytes < row_state)
             return fail(SGQA_ERR_WORKSPACE, "prefill workspace needs >= %zu bytes, got %zu",
                         row_state, workspace_bytes);
-        // Six history slices measured best on the 128K prefill (145.8 ms vs 159.8 ms in one
-        // pass; 4: 147.6, 8: 148.3, 12: 162.3): each XCD's L2 then holds a sixth of its
-        // group's history, while every slice boundary parks ~13 KB of state per row and group.
-        // Short histories gain nothing and stay in one pass (row by row: the kernel attends
-        // rows with c < 2k in one pass even in a sliced launch).
+        // Eight history slices measured best on the 128K prefill (126.9 ms; 4/5/6/10/12/16:
+        // 141.4/134.3/130.9/127.3/130.8/142.6; one pass ~160): each XCD's L2 then holds an
+        // eighth of its group's history, while every slice boundary parks ~13 KB of state per
+        // row and group.  Short histories gain nothing and stay in one pass (row by row: the
+        // kernel attends rows with c < 2k in one pass even in a sliced launch).
         const int64_t max_cand = (q_start + T - 1) / dims->block_size;
-        a.nslices = max_cand >= 2 * (int64_t)dims->topk_blocks ? 6 : 1;
+        a.nslices = max_cand >= 2 * (int64_t)dims->topk_blocks ? 8 : 1;
         a.state = static_cast<float *>(workspace);
         a.state_bytes = (int64_t)workspace_bytes;
         a.state_stride = sgqa::prefill_state_stride(a.d);
