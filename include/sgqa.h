@@ -157,11 +157,13 @@ sgqa_status sgqa_indexer_topk(const sgqa_dims *dims, const sgqa_bf16 *qp, int64_
  * online; probabilities are rounded to bf16 for PV; out is rounded to bf16.
  * Only the first min(k, c+1) entries of each idx row are read; entries that
  * are -1 or outside [0, c] are skipped.
- * With a workspace (optional) the selected blocks of each query are visited in
- * several launches, each over one slice of the history, so that each XCD's L2
- * holds a smaller working set; the softmax state is carried exactly between
- * launches, so the result does not depend on the workspace size beyond the
- * order of fp32 additions.  Rows are processed in chunks that fit it.
+ * With a workspace (optional) the selected blocks of each query whose own block
+ * c is at least 2k are visited in several launches, each over one slice of its
+ * history, so that each XCD's L2 holds a smaller working set; the softmax state
+ * is carried exactly between launches.  Whether a row is sliced depends only on
+ * its own c, so every workspace size, and every split of the rows over calls,
+ * gives the same bits; a call without a workspace differs from them only in the
+ * order of fp32 additions.  Rows are processed in chunks that fit the workspace.
  *   q     [dev] [T][Hq][d] bf16        k_cache, v_cache [dev] [L][Hkv][d] bf16
  *   gate  [dev] [T][Hq] bf16 logits    idx [dev] [T][k] int32 (as produced above)
  *   out   [dev] [T][Hq][d] bf16        lse [dev] [T][Hq] fp32, may be NULL
