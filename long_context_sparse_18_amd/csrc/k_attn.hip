@@ -1133,6 +1133,85 @@ __global__ __launch_bounds__(256) void k_bwd_bitmap(BwdArgs a)
     }
 }
 
+// The dq sweeps gather a step's K rows whole (16-byte piece f = lane + 64 ci is piece
+// f % (D/8) of slot f / (D/8), so each load instruction reads whole rows), place them in the
+// wave's buffer [slot][D + 8] and only then request the step's V rows in the A-operand layout:
+// with both in flight at once the kernel had no registers left for whole-row K (it spilled),
+// and whole-row K reads made the backward 733 -> 685 ms at 128K.
+template <int D>
+__device__ __forceinline__ void stage_k_whole(const uint16_t *__restrict__ Kg, int64_t row_elems,
+                                              int s_lo, int s_hi, uint16_t *buf)
+{
+    const int lane = threadIdx.x & 63;
+    u32x4 kp[D / 16];
+#pragma unroll
+    for (int ci = 0; ci < D / 16; ++ci) {
+        const int f = lane + 64 * ci;
+        const int slot = f / (D / 8), piece = f - slot * (D / 8);
+        const int64_t sk = ((int64_t)(uint32_t)__shfl(s_lo, slot)) |
+                           ((int64_t)__shfl(s_hi, slot) << 32);
+        kp[ci] = load16(Kg + sk * row_elems + piece * 8);
+    }
+    wave_lds_handoff();
+#pragma unroll
+    for (int ci = 0; ci < D / 16; ++ci) {
+        const int f = lane + 64 * ci;
+        const int slot = f / (D / 8), piece = f - slot * (D / 8);
+        uint2 *dst = reinterpret_cast<uint2 *>(buf + slot * (D + 8) + piece * 8);
+        dst[0] = uint2{kp[ci][0], kp[ci][1]};
+        dst[1] = uint2{kp[ci][2], kp[ci][3]};
+    }
+    wave_lds_handoff();
+}
+
+// V rows of the step's slots 16 h + col in the MFMA A-operand layout (dims 32 kk + 8 q4).
+template <int D>
+__device__ __forceinline__ void v_operand_loads(const uint16_t *__restrict__ Vg, int64_t row_elems,
+                                                int s_lo, int s_hi, u32x4 (&vv)[2][D / 32])
+{
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int sl = h * 16 + col;
+        const int64_t sv = ((int64_t)(uint32_t)__shfl(s_lo, sl)) |
+                           ((int64_t)__shfl(s_hi, sl) << 32);
+        const uint16_t *vr = Vg + sv * row_elems + q4 * 8;
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+            vv[h][kk] = load16(vr + kk * 32);
+    }
+}
+
+// S^T = K Q^T from the staged K rows and dP^T = V dA^T from the V rows in registers; lane
+// holds slots 16 h + 4 q4 + r of head col.
+template <int D>
+__device__ __forceinline__ void sdp_products(const uint16_t *buf, const u32x4 (&vv)[2][D / 32],
+                                             const bf16x8 (&qf)[D / 32],
+                                             const bf16x8 (&daf)[D / 32], f32x4 (&sc)[2],
+                                             f32x4 (&dp)[2])
+{
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk) {
+            const u32x4 ka =
+                *reinterpret_cast<const u32x4 *>(buf + (h * 16 + col) * (D + 8) + kk * 32 + q4 * 8);
+            sc[h] = mfma_16x16x32(as_bf16x8(ka), qf[kk], sc[h]);
+        }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        dp[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < D / 32; ++kk)
+            dp[h] = mfma_16x16x32(as_bf16x8(vv[h][kk]), daf[kk], dp[h]);
+    }
+}
+
 // First sweep of a wave's (row, group): D = sum_s P_s dP_s per head (this lane's share),
 // from the same fp32 P and dP the second sweep uses, so the dz of a row sum to zero.
 template <int D>
@@ -1140,13 +1219,13 @@ __device__ __forceinline__ float dsum_range(const uint16_t *__restrict__ Kg,
                                             const uint16_t *__restrict__ Vg, int Hkv,
                                             const SparseTokens &src, const bf16x8 (&qf)[D / 32],
                                             const bf16x8 (&daf)[D / 32], float scale_log2,
-                                            float lse2)
+                                            float lse2, uint16_t *vs)
 {
     const int lane = threadIdx.x & 63;
-    const int col = lane & 15, q4 = lane >> 4;
+    const int q4 = lane >> 4;
     const int64_t row_elems = (int64_t)Hkv * D;
     const int nsteps = src.steps();
-    int wbase = -(1 << 30);  // empty window
+    int wbase = -(1 << 30);
     float part = 0.f;
     for (int step = 0; step < nsteps; ++step) {
         int64_t s_ld;
@@ -1154,40 +1233,25 @@ __device__ __forceinline__ float dsum_range(const uint16_t *__restrict__ Kg,
         src.slot(step, lane & 31, wbase, s_ld, valid);
         const uint64_t vmask = __ballot(valid);
         const int s_lo = (int)(s_ld & 0xffffffff), s_hi = (int)(s_ld >> 32);
-        u32x4 kv[2][D / 32], vv[2][D / 32];
+        stage_k_whole<D>(Kg, row_elems, s_lo, s_hi, vs);
+        u32x4 vv[2][D / 32];
+        v_operand_loads<D>(Vg, row_elems, s_lo, s_hi, vv);
+        f32x4 sc[2], dp[2];
+        sdp_products<D>(vs, vv, qf, daf, sc, dp);
 #pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int sl = h * 16 + col;
-            const int64_t sk = ((int64_t)(uint32_t)__shfl(s_lo, sl)) |
-                               ((int64_t)__shfl(s_hi, sl) << 32);
-            const uint16_t *kr = Kg + sk * row_elems + q4 * 8;
-            const uint16_t *vr = Vg + sk * row_elems + q4 * 8;
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                kv[h][kk] = load16(kr + kk * 32);
-                vv[h][kk] = load16(vr + kk * 32);
-            }
-        }
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                sc = mfma_16x16x32(as_bf16x8(kv[h][kk]), qf[kk], sc);
-                dp = mfma_16x16x32(as_bf16x8(vv[h][kk]), daf[kk], dp);
-            }
+        for (int h = 0; h < 2; ++h)
 #pragma unroll
             for (int r = 0; r < 4; ++r) {
                 const int slot = h * 16 + q4 * 4 + r;
                 if ((vmask >> slot) & 1ull)
-                    part += fast_exp2(sc[r] * scale_log2 - lse2) * dp[r];
+                    part += fast_exp2(sc[h][r] * scale_log2 - lse2) * dp[h][r];
             }
-        }
     }
     return part;
 }
 
-// dq of one wave's (row, group) over its selected tokens; acc = dq^T (unscaled).
+// dq of one wave's (row, group) over its selected tokens; acc = dq^T (unscaled).  The staged
+// K rows serve S^T and then dq^T += K^T dz^T, read transposed.
 template <int D>
 __device__ __forceinline__ void dq_range(const uint16_t *__restrict__ Kg,
                                          const uint16_t *__restrict__ Vg, int Hkv,
@@ -1198,42 +1262,21 @@ __device__ __forceinline__ void dq_range(const uint16_t *__restrict__ Kg,
 {
     constexpr int kLd = D + 8;
     const int lane = threadIdx.x & 63;
-    const int col = lane & 15, q4 = lane >> 4;
+    const int q4 = lane >> 4;
     const int64_t row_elems = (int64_t)Hkv * D;
     const int nsteps = src.steps();
-    int wbase = -(1 << 30);  // empty window
+    int wbase = -(1 << 30);
     for (int step = 0; step < nsteps; ++step) {
         int64_t s_ld;
         bool valid;
         src.slot(step, lane & 31, wbase, s_ld, valid);
         const uint64_t vmask = __ballot(valid);
         const int s_lo = (int)(s_ld & 0xffffffff), s_hi = (int)(s_ld >> 32);
-        u32x4 kv[2][D / 32], vv[2][D / 32];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const int sl = h * 16 + col;
-            const int64_t sk = ((int64_t)(uint32_t)__shfl(s_lo, sl)) |
-                               ((int64_t)__shfl(s_hi, sl) << 32);
-            const uint16_t *kr = Kg + sk * row_elems + q4 * 8;
-            const uint16_t *vr = Vg + sk * row_elems + q4 * 8;
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                kv[h][kk] = load16(kr + kk * 32);
-                vv[h][kk] = load16(vr + kk * 32);
-            }
-        }
-        // S^T = K Q^T and dP^T = V dA^T; lane holds slots 16h + 4 q4 + r of head col
+        stage_k_whole<D>(Kg, row_elems, s_lo, s_hi, ks);
+        u32x4 vv[2][D / 32];
+        v_operand_loads<D>(Vg, row_elems, s_lo, s_hi, vv);
         f32x4 sc[2], dp[2];
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-            dp[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                sc[h] = mfma_16x16x32(as_bf16x8(kv[h][kk]), qf[kk], sc[h]);
-                dp[h] = mfma_16x16x32(as_bf16x8(vv[h][kk]), daf[kk], dp[h]);
-            }
-        }
+        sdp_products<D>(ks, vv, qf, daf, sc, dp);
         float dz[2][4];
 #pragma unroll
         for (int h = 0; h < 2; ++h)
@@ -1250,18 +1293,6 @@ __device__ __forceinline__ void dq_range(const uint16_t *__restrict__ Kg,
         zw[2] = pack_bf16x2(dz[1][0], dz[1][1]);
         zw[3] = pack_bf16x2(dz[1][2], dz[1][3]);
         const bf16x8 zf = as_bf16x8(zw);
-
-        // stage the K rows in LDS [slot][d] and read them transposed
-        wave_lds_handoff();
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int kk = 0; kk < D / 32; ++kk) {
-                uint2 *dst = reinterpret_cast<uint2 *>(ks + (h * 16 + col) * kLd + kk * 32 + q4 * 8);
-                dst[0] = uint2{kv[h][kk][0], kv[h][kk][1]};
-                dst[1] = uint2{kv[h][kk][2], kv[h][kk][3]};
-            }
-        wave_lds_handoff();
 #pragma unroll
         for (int mt = 0; mt < D / 16; ++mt)
             acc[mt] = mfma_16x16x32(vt_fragment(ks, kLd, mt * 16), zf, acc[mt]);
@@ -1289,8 +1320,9 @@ __global__ __launch_bounds__(512) void k_bwd_dq(BwdArgs a)
     const float lse2 = col < hpg ? a.lse[head0 + col] * kLog2e : 0.f;
     const SparseTokens src{a.idx + r * a.k, 0, nvalid, t, c, a.B, entry_window<D>(lds)};
     // D = sum_s P_s dP_s (so that dG = D (1 - sigmoid(G)) and the dz of the row sum to zero)
+    uint16_t *vs = lds + wave * attn_vbuf_elems(D);
     const float dsum = sum_across_rows(dsum_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D,
-                                                     a.Hkv, src, qf, daf, a.scale_log2, lse2));
+                                                     a.Hkv, src, qf, daf, a.scale_log2, lse2, vs));
     if (col < hpg && q4 == 0) {
         a.dsum[head0 + col] = dsum;
         a.dgate[head0 + col] =
@@ -1301,7 +1333,7 @@ __global__ __launch_bounds__(512) void k_bwd_dq(BwdArgs a)
     for (int mt = 0; mt < D / 16; ++mt)
         acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
     dq_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D, a.Hkv, src, qf, daf, a.scale_log2,
-                lse2, dsum, lds + wave * attn_vbuf_elems(D), acc);
+                lse2, dsum, vs, acc);
     if (col < hpg) {
         float *dst = a.dq + (head0 + col) * D + q4 * 4;
 #pragma unroll
