@@ -139,12 +139,13 @@ def bench_prefill(steps: int, warmup: int):
                        + s.topk_blocks * 4)
     # the sibling layer type on the same inputs: gated sliding-window attention, window 512
     W = 512
-    sgqa.swa_prefill(s, d["Q"], d["K"], d["V"], d["G"], wl.q_start, wl.L, W, scale, out,
+    swa_out = torch.empty_like(out)  # out keeps the sparse forward's output for the backward
+    sgqa.swa_prefill(s, d["Q"], d["K"], d["V"], d["G"], wl.q_start, wl.L, W, scale, swa_out,
                      stream=stream)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record(stream)
     for _ in range(steps):
-        sgqa.swa_prefill(s, d["Q"], d["K"], d["V"], d["G"], wl.q_start, wl.L, W, scale, out,
+        sgqa.swa_prefill(s, d["Q"], d["K"], d["V"], d["G"], wl.q_start, wl.L, W, scale, swa_out,
                          stream=stream)
     b.record(stream)
     torch.cuda.synchronize()
@@ -180,21 +181,29 @@ def bench_prefill(steps: int, warmup: int):
     ws_b = torch.empty(sgqa.workspace_bytes(sgqa.OP_ATTN_BACKWARD, s, 1, wl.T, wl.L),
                        dtype=torch.uint8, device=dev)
 
-    def bwd():
+    def bwd(fwd_out=None):
         sgqa.sparse_attn_backward(s, d["Q"], d["K"], d["V"], d["G"], idx, wl.q_start, wl.L, scale,
-                                  lse, dout, dq, dk, dv, dg, workspace=ws_b, stream=stream)
+                                  lse, dout, dq, dk, dv, dg, workspace=ws_b, stream=stream,
+                                  out=fwd_out)
 
-    bwd()
-    a.record(stream)
-    for _ in range(steps):
-        bwd()
-    b.record(stream)
-    torch.cuda.synchronize()
-    bwd_ms = a.elapsed_time(b) / steps
+    def time_bwd(fwd_out):
+        bwd(fwd_out)
+        a.record(stream)
+        for _ in range(steps):
+            bwd(fwd_out)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / steps
+
+    bwd_ms = time_bwd(None)
+    bwd_out_ms = time_bwd(out)
     backward = {"ms": bwd_ms, "tokens_per_s": wl.T / (bwd_ms / 1e3),
                 "tflops_minimal": 10 * s.head_dim * s.num_q_heads * pairs / (bwd_ms / 1e3) / 1e12,
-                "ratio_to_forward_attention": bwd_ms / attn_ms}
-    del dout, dq, dk, dv, dg, ws_b
+                "ratio_to_forward_attention": bwd_ms / attn_ms,
+                "d_from_forward_output": {"ms": bwd_out_ms,
+                                          "tokens_per_s": wl.T / (bwd_out_ms / 1e3),
+                                          "ratio_to_forward_attention": bwd_out_ms / attn_ms}}
+    del dout, dq, dk, dv, dg, ws_b, swa_out
     res = dict(wl=wl, total_ms=total_ms, ms_per_step=total_ms / steps, build_ms=build_ms, swa=swa,
                sequential_ms=sum(sum(p) for p in per) / steps,
                fused_index=fused_index, backward=backward,
@@ -555,7 +564,8 @@ def main():
     log(f"sliding window: {pre['swa']['ms']:.3f} ms; index from keys: "
         f"{pre['fused_index']['ms']:.3f} ms ({pre['fused_index']['GBps']:.0f} GB/s); backward "
         f"{pre['backward']['ms']:.1f} ms ({pre['backward']['ratio_to_forward_attention']:.2f}x "
-        f"the forward attention)")
+        f"the forward attention), {pre['backward']['d_from_forward_output']['ms']:.1f} ms with "
+        f"D from the forward output")
     cpu = None
     if not args.no_cpu:
         log(f"cpu baseline: oracle on up to {args.cpu_rows} rows (~15 s of oracle time)")

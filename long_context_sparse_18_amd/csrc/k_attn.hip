@@ -1073,9 +1073,11 @@ hipError_t launch_attn_decode(const AttnArgs &a, hipStream_t stream)
 //   D = g_out . out (= da . a),  dG = D (1 - sigmoid(G)),  da = sigmoid(G) g_out,
 //   dP_s = da . v_s,  dz_s = P_s (dP_s - D),
 //   dq = scale sum_s dz_s k_s,  dk_s = scale sum_(t,h) dz_s q,  dv_s = sum_(t,h) P_s da.
-// D is formed as sum_s P_s dP_s from the kernel's own fp32 P and dP (a first sweep over the
-// row), not from the bf16 forward output: then the dz of a row sum to zero and each dz carries
-// only its own bf16 rounding, instead of an error of D shared by every attended key.
+// Without the forward output, D is formed as sum_s P_s dP_s from the kernel's own fp32 P and
+// dP (a first sweep over the row): then the dz of a row sum to zero and each dz carries only
+// its own bf16 rounding, instead of an error of D shared by every attended key.  Given the
+// bf16 forward output, D = g_out . out is one elementwise pass and k_bwd_dq makes one sweep:
+// half the dq gathers, at the price of that shared error (one bf16 rounding of out per term).
 // Launches: k_bwd_prep (da), a zero fill and k_bwd_bitmap (for every key block the set of
 // query rows that selected it, one bit per row, by atomicOr, whose result does not depend on
 // order), k_bwd_dq (query-major, the forward's wave: a sweep for D and dG, then a second with
@@ -1097,7 +1099,8 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 // One wave per (row, head), the waves striding over all of them (the grid is capped, so the
 // launch stays inside 32-bit work-item counts at any T): da = sigmoid(G) g_out, rounded to
-// bf16 for the matrix cores.
+// bf16 for the matrix cores.  Given the forward output, also D = g_out . out (fp32 products,
+// lane partial sums added by a fixed butterfly) and dG = D (1 - sigmoid(G)).
 __global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a)
 {
     const int64_t nrow = (int64_t)a.rows * a.Hq;
@@ -1107,8 +1110,22 @@ __global__ __launch_bounds__(256) void k_bwd_prep(BwdArgs a)
          row += (int64_t)gridDim.x * 4) {
         const uint16_t *go = a.dout + row * d;
         const float sg = sigmoid_f32(bf16_bits_to_f32(a.gate[row]));
-        for (int e = lane; e < d; e += 64)
-            a.da[row * d + e] = (uint16_t)f32_to_bf16_bits(sg * bf16_bits_to_f32(go[e]));
+        float part = 0.f;
+        for (int e = lane; e < d; e += 64) {
+            const float g = bf16_bits_to_f32(go[e]);
+            a.da[row * d + e] = (uint16_t)f32_to_bf16_bits(sg * g);
+            if (a.out)
+                part = fmaf(g, bf16_bits_to_f32(a.out[row * d + e]), part);
+        }
+        if (a.out) {
+#pragma unroll
+            for (int o = 32; o > 0; o >>= 1)
+                part += __shfl_xor(part, o);
+            if (lane == 0) {
+                a.dsum[row] = part;
+                a.dgate[row] = part * (1.0f - sg);
+            }
+        }
     }
 }
 
@@ -1319,14 +1336,20 @@ __global__ __launch_bounds__(512) void k_bwd_dq(BwdArgs a)
     load_q<D>(a.da + head0 * D, hpg, daf);
     const float lse2 = col < hpg ? a.lse[head0 + col] * kLog2e : 0.f;
     const SparseTokens src{a.idx + r * a.k, 0, nvalid, t, c, a.B, entry_window<D>(lds)};
-    // D = sum_s P_s dP_s (so that dG = D (1 - sigmoid(G)) and the dz of the row sum to zero)
     uint16_t *vs = lds + wave * attn_vbuf_elems(D);
-    const float dsum = sum_across_rows(dsum_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D,
-                                                     a.Hkv, src, qf, daf, a.scale_log2, lse2, vs));
-    if (col < hpg && q4 == 0) {
-        a.dsum[head0 + col] = dsum;
-        a.dgate[head0 + col] =
-            dsum * (1.0f - sigmoid_f32(bf16_bits_to_f32(a.gate[head0 + col])));
+    float dsum;
+    if (a.out) {
+        // D = g_out . out, formed by k_bwd_prep
+        dsum = col < hpg ? a.dsum[head0 + col] : 0.f;
+    } else {
+        // D = sum_s P_s dP_s (so that dG = D (1 - sigmoid(G)) and the dz of the row sum to 0)
+        dsum = sum_across_rows(dsum_range<D>(a.kc + (int64_t)g * D, a.vc + (int64_t)g * D,
+                                             a.Hkv, src, qf, daf, a.scale_log2, lse2, vs));
+        if (col < hpg && q4 == 0) {
+            a.dsum[head0 + col] = dsum;
+            a.dgate[head0 + col] =
+                dsum * (1.0f - sigmoid_f32(bf16_bits_to_f32(a.gate[head0 + col])));
+        }
     }
     f32x4 acc[D / 16];
 #pragma unroll

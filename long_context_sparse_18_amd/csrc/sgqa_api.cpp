@@ -814,9 +814,10 @@ sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
                                       const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
                                       const sgqa_bf16 *gate, const int32_t *idx, int64_t q_start,
                                       int32_t T, int64_t L, float softmax_scale, const float *lse,
-                                      const sgqa_bf16 *dout, float *dq, float *dk, float *dv,
-                                      float *dgate, void *workspace, size_t workspace_bytes,
-                                      int64_t dkdv_row_slice, void *stream)
+                                      const sgqa_bf16 *dout, const sgqa_bf16 *out, float *dq,
+                                      float *dk, float *dv, float *dgate, void *workspace,
+                                      size_t workspace_bytes, int64_t dkdv_row_slice,
+                                      void *stream)
 {
     sgqa_status st = check_dims(dims, true, false);
     if (st != SGQA_OK)
@@ -841,7 +842,7 @@ sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
         !dgate)
         return fail(SGQA_ERR_NULL, "every tensor argument must be non-NULL");
     if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(dq, 16) ||
-        !aligned(dout, 2) || !aligned(gate, 2) || !aligned(idx, 4) ||
+        !aligned(dout, 2) || !aligned(out, 2) || !aligned(gate, 2) || !aligned(idx, 4) ||
         !aligned(lse, 4) || !aligned(dk, 4) || !aligned(dv, 4) || !aligned(dgate, 4))
         return fail(SGQA_ERR_SHAPE, "q, caches and dq must be 16-byte aligned");
     const size_t need = sgqa_workspace_bytes(SGQA_OP_ATTN_BACKWARD, dims, 1, T, L);
@@ -856,6 +857,7 @@ sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
     a.vc = v_cache;
     a.gate = gate;
     a.dout = dout;
+    a.out = out;
     a.lse = lse;
     a.idx = idx;
     a.q_start = q_start;

@@ -148,6 +148,7 @@ hipError_t launch_swa(const AttnArgs &a, hipStream_t stream);
 // q_start .. q_start+T-1 over an L-token cache).
 struct BwdArgs {
     const uint16_t *q, *kc, *vc, *gate, *dout;        // forward inputs and dL/dout
+    const uint16_t *out;                              // forward output or null (D from P dP)
     const float *lse;                                 // forward log-sum-exp [T][Hq]
     const int32_t *idx;                               // [T][k]
     int64_t q_start;

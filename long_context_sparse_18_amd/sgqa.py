@@ -86,7 +86,7 @@ def load():
                                                 ctypes.c_float, p, p, p, sz, p]
     lib.sgqa_sparse_attn_backward.restype = st
     lib.sgqa_sparse_attn_backward.argtypes = [dp, p, p, p, p, p, i64, i32, i64, ctypes.c_float, p,
-                                              p, p, p, p, p, p, sz, i64, p]
+                                              p, p, p, p, p, p, p, sz, i64, p]
     lib.sgqa_probe_mfma_bf16.restype = st
     lib.sgqa_probe_mfma_bf16.argtypes = [i32, i32, p, p]
     lib.sgqa_probe_read.restype = st
@@ -293,11 +293,12 @@ def sparse_attn_decode_fp8(shape: LayerShape, q, k_codes, v_codes, k_scales, v_s
 
 def sparse_attn_backward(shape: LayerShape, q, k_cache, v_cache, gate, idx, q_start: int, L: int,
                          softmax_scale: float, lse, dout, dq, dk, dv, dgate, workspace=None,
-                         stream=None, dkdv_row_slice: int = 0):
+                         stream=None, dkdv_row_slice: int = 0, out=None):
     """Backward of sparse_attn_prefill with idx fixed: fp32 dq [T, Hq, d], dk / dv [L, Hkv, d]
     and dgate [T, Hq] from dout [T, Hq, d] and the forward's lse.  ``dkdv_row_slice``: query
-    rows per dk / dv pass (0 = chosen from the sizes; else a multiple of 32)."""
-    _need_cuda(q, k_cache, v_cache, gate, idx, lse, dout, dq, dk, dv, dgate, workspace)
+    rows per dk / dv pass (0 = chosen from the sizes; else a multiple of 32).  ``out``: the
+    forward's output [T, Hq, d]; given, D = dout . out and dq sweeps the selection once."""
+    _need_cuda(q, k_cache, v_cache, gate, idx, lse, dout, dq, dk, dv, dgate, workspace, out)
     T = q.shape[0]
     if workspace is None:
         workspace = torch.empty(workspace_bytes(OP_ATTN_BACKWARD, shape, 1, T, L),
@@ -305,7 +306,7 @@ def sparse_attn_backward(shape: LayerShape, q, k_cache, v_cache, gate, idx, q_st
     d = Dims.of(shape)
     check(load().sgqa_sparse_attn_backward(ctypes.byref(d), _ptr(q), _ptr(k_cache), _ptr(v_cache),
                                            _ptr(gate), _ptr(idx), q_start, T, L, softmax_scale,
-                                           _ptr(lse), _ptr(dout), _ptr(dq), _ptr(dk),
+                                           _ptr(lse), _ptr(dout), _ptr(out), _ptr(dq), _ptr(dk),
                                            _ptr(dv), _ptr(dgate), _ptr(workspace),
                                            workspace.numel(), dkdv_row_slice,
                                            _stream(stream, q)))

@@ -202,7 +202,8 @@ def test_backward_validation():
 
     def call(q=FAKE, lse=FAKE, T=64, L=1024, q_start=0, ws=FAKE, wsb=need, slice_=0):
         return lib.sgqa_sparse_attn_backward(ctypes.byref(d), q, FAKE, FAKE, FAKE, FAKE, q_start, T,
-                                             L, 0.07, lse, FAKE, FAKE, FAKE, FAKE, FAKE, ws, wsb,
+                                             L, 0.07, lse, FAKE, None, FAKE, FAKE, FAKE, FAKE, ws,
+                                             wsb,
                                              slice_, None)
 
     assert call(q=None) == sgqa.ERR_NULL

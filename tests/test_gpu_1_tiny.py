@@ -547,7 +547,8 @@ def test_tiny_backward(tiny, B, k, q0):
     """Fixed-selection backward on the tiny layer against the oracle: every dq, dK, dV and
     dgate element, sparse and dense rows, B in {1, 8, 16}, a chunk starting mid-block.  A
     second call that runs dK / dV 32 (then 96) query rows per pass gives identical bits: the
-    passes carry their sums over in one fixed order."""
+    passes carry their sums over in one fixed order.  With the forward output given (D from
+    dout . out) dq, dK and dgate meet the same bar and dV keeps its bits."""
     shape = with_selection(WL.shape, B, k)
     grads, ref, args = _backward_case(tiny, shape, q0, WL.L, 7 + q0)
     st = {}
@@ -563,6 +564,16 @@ def test_tiny_backward(tiny, B, k, q0):
         torch.cuda.synchronize()
         for n in grads:
             assert torch.equal(grads[n], again[n]), (n, row_slice)
+    # D from the forward's bf16 output: one dq sweep; dV does not involve D, so its bits stay
+    fo = {n: torch.full_like(v, float("nan")) for n, v in grads.items()}
+    sgqa.sparse_attn_backward(shape, Q, K, V, G, idx, q0, WL.L, 1.0 / math.sqrt(shape.head_dim),
+                              lse, dout, fo["dq"], fo["dk"], fo["dv"], fo["dg"], out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(fo["dv"], grads["dv"])
+    st = {}
+    for name in ("dq", "dk", "dg"):
+        st.update(parity.check_grad(name, fo[name].cpu().numpy(), ref[name]))
+    say(f"backward with out B={B} k={k} q0={q0}: {st}")
 
 
 @pytest.mark.gpu

@@ -205,8 +205,9 @@ def test_decode_fp8_1m_batch16():
     say("fp8 decode: all 16 sequences ok")
 
 
-def _forward_backward(shape, d, q_start: int, L: int, seed: int, ws_attn=None):
-    """GPU forward (index, top-k, attention with lse) and backward for a seeded dout."""
+def _forward_backward(shape, d, q_start: int, L: int, seed: int, ws_attn=None, with_out=False):
+    """GPU forward (index, top-k, attention with lse) and backward for a seeded dout (with
+    with_out, D from dout . out)."""
     B, k = shape.block_size, shape.topk_blocks
     Q, G = d["Q"], d["G"]
     T = Q.shape[0]
@@ -219,21 +220,24 @@ def _forward_backward(shape, d, q_start: int, L: int, seed: int, ws_attn=None):
                  dg=torch.empty(G.shape, dtype=torch.float32, device=DEV))
     sgqa.sparse_attn_backward(shape, Q, d["K"], d["V"], G, res["idx"], q_start, L,
                               1.0 / math.sqrt(shape.head_dim), res["lse"], dout,
-                              grads["dq"], grads["dk"], grads["dv"], grads["dg"])
+                              grads["dq"], grads["dk"], grads["dv"], grads["dg"],
+                              out=res["out"] if with_out else None)
     torch.cuda.synchronize()
     return res, dout, grads
 
 
-def test_backward_real_shape_chunk():
+@pytest.mark.parametrize("with_out", [False, True])
+def test_backward_real_shape_chunk(with_out):
     """Fixed-selection backward at the real shape (64/4 heads, d 192, B 8, k 512) on a chunk of
     128 query rows at positions 8320 .. 8447 (sparse selections over ~1040 blocks): every dq,
-    dK, dV and dgate element against the oracle."""
+    dK, dV and dgate element against the oracle, with D formed in the kernel's sweep and from
+    the forward output."""
     from long_context_sparse_18_amd.configs import Workload
     wl = Workload("bwd-chunk", WORKLOADS[1].shape, nseq=1, T=128, L=8448, q_start=8320)
     shape = wl.shape
     say("backward chunk: generating")
     d = inputs.make_prefill(wl, 21, DEV)
-    res, dout, grads = _forward_backward(shape, d, wl.q_start, wl.L, 22)
+    res, dout, grads = _forward_backward(shape, d, wl.q_start, wl.L, 22, with_out=with_out)
     say("backward chunk: oracle")
     t = np.arange(wl.q_start, wl.q_start + wl.T, dtype=np.int64)
     ref = oracle.sparse_attention_backward(bits(d["Q"]), t, bits(d["K"]), bits(d["V"]),
@@ -243,7 +247,7 @@ def test_backward_real_shape_chunk():
     st = {}
     for name, r in zip(("dq", "dk", "dv", "dg"), ref):
         st.update(parity.check_grad(name, grads[name].cpu().numpy(), r))
-    say(f"backward chunk: {st}")
+    say(f"backward chunk (D from out: {with_out}): {st}")
 
 
 def test_backward_128k_sampled():
