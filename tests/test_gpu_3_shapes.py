@@ -140,6 +140,18 @@ def test_shape_backward(case):
     for name, r in zip(("dq", "dk", "dv", "dg"), ref):
         st.update(parity.check_grad(name, grads[name].cpu().numpy(), r))
     say(f"shapes {_id(shape)} backward: {st}")
+    # D from the forward output: dq, dK and dgate meet the same bar, dV keeps its bits
+    fo = {n: torch.full_like(v, float("nan")) for n, v in grads.items()}
+    sgqa.sparse_attn_backward(shape, d["Q"], d["K"], d["V"], d["G"], res["idx"], 0, wl.L, scale,
+                              res["lse"], dout, fo["dq"], fo["dk"], fo["dv"], fo["dg"],
+                              out=res["out"])
+    torch.cuda.synchronize()
+    assert torch.equal(fo["dv"], grads["dv"])
+    st = {}
+    for name, r in zip(("dq", "dk", "dv", "dg"), ref):
+        if name != "dv":
+            st.update(parity.check_grad(name, fo[name].cpu().numpy(), r))
+    say(f"shapes {_id(shape)} backward with out: {st}")
 
 
 def test_shape_decode_fp8(case):
