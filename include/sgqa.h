@@ -200,6 +200,28 @@ sgqa_status sgqa_sparse_attn_decode(const sgqa_dims *dims, const sgqa_bf16 *q,
                                     void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * sgqa_sparse_attn_decode for callers that cannot allocate device memory (code
+ * under stream capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments without the workspace, the same kernels, the same output
+ * bits.  The partial softmax states live in a fixed 16 MiB device array that
+ * the library holds on every GPU it runs on until the process ends, looked up
+ * once per device on the first call there; nothing is allocated or freed.
+ * Limit: nseq * parts * Hq * (d + 3) * 4 bytes <= 16 MiB, where parts (the
+ * decode workgroups per sequence and KV head) is at most 4; at the real shape
+ * (64 heads, d 192, 512 blocks of 8) that is 200 KB per sequence, so every
+ * nseq <= 64 fits.  Larger calls return SGQA_ERR_UNSUPPORTED.  Every call on one GPU shares that GPU's array, so calls
+ * that overlap on one GPU (other streams, other host threads) race; calls on
+ * one stream are ordered.  Nothing in the array needs to start at zero: every
+ * call writes each partial state before it reads it.
+ */
+sgqa_status sgqa_sparse_attn_decode_noalloc(const sgqa_dims *dims, const sgqa_bf16 *q,
+                                            const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
+                                            int64_t cache_seq_stride, const sgqa_bf16 *gate,
+                                            const int32_t *idx, const int64_t *cache_lens,
+                                            int32_t nseq, float softmax_scale, sgqa_bf16 *out,
+                                            float *lse, void *stream);
+
+/*
  * Gated sliding-window attention, the sibling layer type (ai.info "Why StepFun
  * chose 92 transformer blocks": the efficient layers use Gated Sliding Window
  * Attention; phantomic12 config.json: sliding_window 512).  For query row i at

@@ -985,6 +985,12 @@ static hipError_t launch_prefill_sliced(const AttnArgs &a0, hipStream_t stream)
     return hipSuccess;
 }
 
+int decode_parts(int nsplit)
+{
+    const int nw = nsplit < kDecodeWaves ? nsplit : kDecodeWaves;
+    return (nsplit + nw - 1) / nw;
+}
+
 template <int D>
 static hipError_t launch_decode_d(const AttnArgs &a0, hipStream_t stream)
 {
@@ -992,7 +998,7 @@ static hipError_t launch_decode_d(const AttnArgs &a0, hipStream_t stream)
         return hipErrorInvalidValue;  // the merge holds at most kMaxSplits partial states
     AttnArgs a = a0;
     const int nw = a.nsplit < kDecodeWaves ? a.nsplit : kDecodeWaves;
-    a.npart = (a.nsplit + nw - 1) / nw;
+    a.npart = decode_parts(a.nsplit);
     // the V buffers and windows of the waves hold their combine buffers (64 D + 192 B each)
     static_assert(attn_wave_lds(D) >= (size_t)64 * D + 192, "decode combine buffer");
     const size_t lds = (size_t)nw * attn_wave_lds(D);

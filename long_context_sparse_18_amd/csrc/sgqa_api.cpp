@@ -581,12 +581,16 @@ sgqa_status sgqa_swa_prefill(const sgqa_dims *dims, const sgqa_bf16 *q, const sg
                       "swa_prefill launch");
 }
 
-sgqa_status sgqa_sparse_attn_decode(const sgqa_dims *dims, const sgqa_bf16 *q,
+// Validation and launch shared by sgqa_sparse_attn_decode (caller's workspace, partial
+// states laid out by split) and sgqa_sparse_attn_decode_noalloc (the library's fixed scratch,
+// partial states laid out by workgroup part, which is all the kernels write).
+static sgqa_status attn_decode_impl(const sgqa_dims *dims, const sgqa_bf16 *q,
                                     const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
                                     int64_t cache_seq_stride, const sgqa_bf16 *gate,
                                     const int32_t *idx, const int64_t *cache_lens, int32_t nseq,
                                     float softmax_scale, sgqa_bf16 *out, float *lse,
-                                    void *workspace, size_t workspace_bytes, void *stream)
+                                    void *workspace, size_t workspace_bytes, bool fixed_scratch,
+                                    void *stream)
 {
     sgqa_status st = check_dims(dims, true, false);
     if (st != SGQA_OK)
@@ -615,13 +619,30 @@ sgqa_status sgqa_sparse_attn_decode(const sgqa_dims *dims, const sgqa_bf16 *q,
     if (nseq > 1 && (cache_seq_stride < max_len * row || cache_seq_stride % 8 != 0))
         return fail(SGQA_ERR_SHAPE, "cache_seq_stride %lld must be >= %lld and a multiple of 8",
                     (long long)cache_seq_stride, (long long)(max_len * row));
-    const size_t need = sgqa_workspace_bytes(SGQA_OP_ATTN_DECODE, dims, nseq, 1, max_len);
-    if (!workspace || workspace_bytes < need)
-        return fail(SGQA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
-                    workspace ? workspace_bytes : (size_t)0);
-    if (!aligned(workspace, 16))
-        return fail(SGQA_ERR_SHAPE, "workspace must be 16-byte aligned");
     sgqa::AttnArgs a{};
+    sgqa::decode_split_plan(dims->topk_blocks, dims->block_size, a.nsplit, a.entries_per_split);
+    size_t slots = 0;
+    if (fixed_scratch) {
+        slots = (size_t)nseq * sgqa::decode_parts(a.nsplit) * dims->num_q_heads;
+        const size_t need = slots * ((size_t)dims->head_dim + 3) * sizeof(float);
+        if (need > sgqa::kScratchBytes)
+            return fail(SGQA_ERR_UNSUPPORTED,
+                        "decode without allocation needs %zu bytes of partial states, more than "
+                        "the library's fixed %zu-byte scratch (fewer sequences per call)",
+                        need, sgqa::kScratchBytes);
+        size_t have = 0;
+        hipError_t e = sgqa::scratch_region(&workspace, &have);
+        if (e != hipSuccess)
+            return hip_status(e, "scratch address lookup");
+    } else {
+        slots = (size_t)nseq * a.nsplit * dims->num_q_heads;
+        const size_t need = sgqa_workspace_bytes(SGQA_OP_ATTN_DECODE, dims, nseq, 1, max_len);
+        if (!workspace || workspace_bytes < need)
+            return fail(SGQA_ERR_WORKSPACE, "decode workspace needs %zu bytes, got %zu", need,
+                        workspace ? workspace_bytes : (size_t)0);
+        if (!aligned(workspace, 16))
+            return fail(SGQA_ERR_SHAPE, "workspace must be 16-byte aligned");
+    }
     a.q = q;
     a.kc = k_cache;
     a.vc = v_cache;
@@ -639,12 +660,33 @@ sgqa_status sgqa_sparse_attn_decode(const sgqa_dims *dims, const sgqa_bf16 *q,
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.out = out;
     a.lse = lse;
-    sgqa::decode_split_plan(a.k, a.B, a.nsplit, a.entries_per_split);
-    const size_t slots = (size_t)nseq * a.nsplit * a.Hq;
     a.part_o = static_cast<float *>(workspace);
     a.part_ml = a.part_o + slots * a.d;
     return hip_status(sgqa::launch_attn_decode(a, reinterpret_cast<hipStream_t>(stream)),
                       "sparse_attn_decode launch");
+}
+
+sgqa_status sgqa_sparse_attn_decode(const sgqa_dims *dims, const sgqa_bf16 *q,
+                                    const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
+                                    int64_t cache_seq_stride, const sgqa_bf16 *gate,
+                                    const int32_t *idx, const int64_t *cache_lens, int32_t nseq,
+                                    float softmax_scale, sgqa_bf16 *out, float *lse,
+                                    void *workspace, size_t workspace_bytes, void *stream)
+{
+    return attn_decode_impl(dims, q, k_cache, v_cache, cache_seq_stride, gate, idx, cache_lens,
+                            nseq, softmax_scale, out, lse, workspace, workspace_bytes, false,
+                            stream);
+}
+
+sgqa_status sgqa_sparse_attn_decode_noalloc(const sgqa_dims *dims, const sgqa_bf16 *q,
+                                            const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,
+                                            int64_t cache_seq_stride, const sgqa_bf16 *gate,
+                                            const int32_t *idx, const int64_t *cache_lens,
+                                            int32_t nseq, float softmax_scale, sgqa_bf16 *out,
+                                            float *lse, void *stream)
+{
+    return attn_decode_impl(dims, q, k_cache, v_cache, cache_seq_stride, gate, idx, cache_lens,
+                            nseq, softmax_scale, out, lse, nullptr, 0, true, stream);
 }
 
 } // extern "C"

@@ -178,5 +178,13 @@ hipError_t launch_probe_gather(const void *table, int row16, const int32_t *idx,
 
 // Decode split-K geometry for k selected entries of B tokens.
 void decode_split_plan(int k, int B, int &nsplit, int &entries_per_split);
+// Partial states per (sequence, head) the decode attention writes for nsplit splits (one per
+// decode workgroup).
+int decode_parts(int nsplit);
+
+// Fixed device scratch of kScratchBytes for the entry points that allocate nothing
+// (sgqa_scratch.hip): the current device's copy, looked up once per device.
+constexpr size_t kScratchBytes = size_t(16) << 20;
+hipError_t scratch_region(void **ptr, size_t *bytes);
 
 } // namespace sgqa

@@ -24,7 +24,7 @@ OP_ATTN_PREFILL = 3
 OP_ATTN_BACKWARD = 4
 
 EXPORTS = ("sgqa_index_build", "sgqa_index_build_from_keys", "sgqa_indexer_topk", "sgqa_sparse_attn_prefill",
-           "sgqa_sparse_attn_decode", "sgqa_swa_prefill", "sgqa_quantize_fp8",
+           "sgqa_sparse_attn_decode", "sgqa_sparse_attn_decode_noalloc", "sgqa_swa_prefill", "sgqa_quantize_fp8",
            "sgqa_indexer_topk_fp8", "sgqa_sparse_attn_decode_fp8", "sgqa_sparse_attn_backward",
            "sgqa_probe_mfma_bf16", "sgqa_probe_read", "sgqa_probe_gather",
            "sgqa_workspace_bytes",
@@ -75,6 +75,9 @@ def load():
     lib.sgqa_sparse_attn_decode.restype = st
     lib.sgqa_sparse_attn_decode.argtypes = [dp, p, p, p, i64, p, p, p, i32, ctypes.c_float, p, p,
                                             p, sz, p]
+    lib.sgqa_sparse_attn_decode_noalloc.restype = st
+    lib.sgqa_sparse_attn_decode_noalloc.argtypes = [dp, p, p, p, i64, p, p, p, i32,
+                                                    ctypes.c_float, p, p, p]
     lib.sgqa_swa_prefill.restype = st
     lib.sgqa_swa_prefill.argtypes = [dp, p, p, p, p, i64, i32, i64, i64, ctypes.c_float, p, p, p]
     lib.sgqa_quantize_fp8.restype = st
@@ -215,6 +218,20 @@ def sparse_attn_decode(shape: LayerShape, q, k_cache, v_cache, gate, idx, cache_
                                          _i64_array(cache_lens), nseq, softmax_scale, _ptr(out),
                                          _ptr(lse), _ptr(workspace), workspace.numel(),
                                          _stream(stream, q)))
+
+
+def sparse_attn_decode_noalloc(shape: LayerShape, q, k_cache, v_cache, gate, idx, cache_lens,
+                               softmax_scale: float, out, lse=None, stream=None):
+    """sparse_attn_decode without a workspace: the library's fixed per-device scratch holds
+    the partial states (calls that overlap on one GPU race)."""
+    _need_cuda(q, k_cache, v_cache, gate, idx, out, lse)
+    cache_lens = list(cache_lens)
+    d = Dims.of(shape)
+    check(load().sgqa_sparse_attn_decode_noalloc(ctypes.byref(d), _ptr(q), _ptr(k_cache),
+                                                 _ptr(v_cache), k_cache.stride(0), _ptr(gate),
+                                                 _ptr(idx), _i64_array(cache_lens),
+                                                 len(cache_lens), softmax_scale, _ptr(out),
+                                                 _ptr(lse), _stream(stream, q)))
 
 
 def swa_prefill(shape: LayerShape, q, k_cache, v_cache, gate, q_start: int, L: int, window: int,

@@ -267,6 +267,28 @@ def test_decode_validation():
     assert call(nseq=0) == sgqa.OK
 
 
+def test_decode_noalloc_validation():
+    """The decode entry point without a workspace: the same checks, and calls whose partial
+    states exceed the library's 16 MiB scratch are refused before any HIP call."""
+    lib = sgqa.load()
+    lens = (ctypes.c_int64 * 64)(*([1 << 16] * 64))
+
+    def call(d, nseq=2, q=FAKE, lens=lens, stride=(1 << 16) * 4 * 192):
+        return lib.sgqa_sparse_attn_decode_noalloc(ctypes.byref(d), q, FAKE, FAKE, stride, FAKE,
+                                                   FAKE, lens, nseq, 0.07, FAKE, None, None)
+
+    d = dims()
+    assert call(d, q=None) == sgqa.ERR_NULL
+    assert call(d, lens=None) == sgqa.ERR_NULL
+    assert call(d, stride=100) == sgqa.ERR_SHAPE
+    assert call(d, nseq=65) == sgqa.ERR_UNSUPPORTED
+    assert call(d, nseq=0) == sgqa.OK
+    # 128 heads of d 192 over 64 sequences: 64 x 4 parts x 128 x 195 x 4 B = 25.6 MB > 16 MiB
+    big = dims(num_q_heads=128, num_kv_heads=8)
+    assert call(big, nseq=64, stride=(1 << 16) * 8 * 192) == sgqa.ERR_UNSUPPORTED
+    assert b"scratch" in lib.sgqa_last_error()
+
+
 def test_workspace_sizes():
     # full pass for a 32K prefill: 32768 rows x 4096 candidates (ld 4096) x 4 B = 512 MiB
     assert sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, REAL, 1, 32768, 32768) == 32768 * 4096 * 4
