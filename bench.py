@@ -114,11 +114,15 @@ def bench_prefill(steps: int, warmup: int):
     torch.cuda.synchronize()
     log(f"prefill: timing {steps} steps")
     t0 = ev()
+    step_marks = [t0]
     for _ in range(steps):
         layer_step()
-    t1 = ev()
+        step_marks.append(ev())
+    t1 = step_marks[-1]
     torch.cuda.synchronize()
     total_ms = t0.elapsed_time(t1)
+    step_ms = sorted(step_marks[i].elapsed_time(step_marks[i + 1]) for i in range(steps))
+    median_ms = step_ms[len(step_ms) // 2]
     # the stage times: the same stages one after the other on one stream
     step([])
     marks = []
@@ -130,6 +134,21 @@ def bench_prefill(steps: int, warmup: int):
     build_ms = sum(p[0] for p in per) / steps
     topk_ms = sum(p[1] for p in per) / steps
     attn_ms = sum(p[2] for p in per) / steps
+    attn_ms_median = sorted(p[2] for p in per)[steps // 2]
+    # the index build alone, back to back (one stage mark is too coarse for ~20 us)
+    a0, a1 = ev(), None
+    for _ in range(steps * 10):
+        sgqa.index_build(s, d["kp"], kb, [wl.L], stream=stream)
+    a1 = ev()
+    torch.cuda.synchronize()
+    build_loop_ms = a0.elapsed_time(a1) / (steps * 10)
+    build_bytes = wl.L * s.proxy_dim * 2 + wl.nblk * s.proxy_dim * 2
+    index_build = {"ms": build_loop_ms, "algorithmic_bytes": build_bytes,
+                   "GBps": build_bytes / (build_loop_ms / 1e3) / 1e9,
+                   "hbm_frac": build_bytes / (build_loop_ms / 1e3) / 1e9 / PEAK_HBM_GBS,
+                   "traffic": measured_traffic("index_build_128k"),
+                   "kernel": "k_index_build<8>",
+                   "timing": f"{steps * 10} calls back to back, HIP events on the stream"}
     pairs = attended_pairs(wl.q_start, wl.T, s.block_size, s.topk_blocks)
     flops = 4 * s.head_dim * s.num_q_heads * pairs
     # algorithmic bytes of the attention launch: every attended (query, token) pair reads that
@@ -196,15 +215,14 @@ def bench_prefill(steps: int, warmup: int):
         return a.elapsed_time(b) / steps
 
     bwd_ms = time_bwd(None)
-    bwd_out_ms = time_bwd(out)
+    # (the variant that takes D from the forward output is experimental: its dq error on the
+    # 128K rows sits at the gradient bound, so it is not timed here)
     backward = {"ms": bwd_ms, "tokens_per_s": wl.T / (bwd_ms / 1e3),
                 "tflops_minimal": 10 * s.head_dim * s.num_q_heads * pairs / (bwd_ms / 1e3) / 1e12,
-                "ratio_to_forward_attention": bwd_ms / attn_ms,
-                "d_from_forward_output": {"ms": bwd_out_ms,
-                                          "tokens_per_s": wl.T / (bwd_out_ms / 1e3),
-                                          "ratio_to_forward_attention": bwd_out_ms / attn_ms}}
+                "ratio_to_forward_attention": bwd_ms / attn_ms}
     del dout, dq, dk, dv, dg, ws_b, swa_out
     res = dict(wl=wl, total_ms=total_ms, ms_per_step=total_ms / steps, build_ms=build_ms, swa=swa,
+               median_ms=median_ms, attn_ms_median=attn_ms_median, index_build=index_build,
                sequential_ms=sum(sum(p) for p in per) / steps,
                fused_index=fused_index, backward=backward,
                topk_ms=topk_ms, attn_ms=attn_ms, pairs=pairs, attn_flops=flops,
@@ -213,7 +231,81 @@ def bench_prefill(steps: int, warmup: int):
     return res
 
 
-def bench_decode(steps: int, warmup: int):
+def bench_chunked(steps: int, warmup: int, cpu: bool):
+    """Chunked prefill: 8192 new query tokens at positions 1 040 388 .. 1 048 579 of a
+    1 048 580-token cache (131 072 candidate blocks for the last rows).  A step is the index
+    rebuild of the blocks the chunk touched ([130048, 131073)), the indexer top-k of the 8192
+    rows and their sparse attention, one after the other on one stream."""
+    import torch
+    from long_context_sparse_18_amd import WORKLOADS, inputs, sgqa
+
+    wl = WORKLOADS[4]
+    s = wl.shape
+    dev = torch.device("cuda:0")
+    log(f"chunked prefill: generating {wl.name}")
+    d = inputs.make_prefill(wl, 4, dev)
+    kb = torch.empty((wl.nblk, s.proxy_dim), dtype=torch.bfloat16, device=dev)
+    sgqa.index_build(s, d["kp"], kb, [wl.L])  # the history's index, built before the chunk
+    blk0 = wl.q_start // s.block_size
+    idx = torch.empty((wl.T, s.topk_blocks), dtype=torch.int32, device=dev)
+    out = torch.empty_like(d["Q"])
+    lse = torch.empty((wl.T, s.num_q_heads), dtype=torch.float32, device=dev)
+    ws = torch.empty(sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, s, 1, wl.T, wl.L),
+                     dtype=torch.uint8, device=dev)
+    ws_attn = torch.empty(sgqa.workspace_bytes(sgqa.OP_ATTN_PREFILL, s, 1, wl.T, wl.L),
+                          dtype=torch.uint8, device=dev)
+    scale = 1.0 / math.sqrt(s.head_dim)
+    stream = torch.cuda.current_stream(dev)
+
+    def ev():
+        e = torch.cuda.Event(enable_timing=True)
+        e.record(stream)
+        return e
+
+    def step():
+        m = [ev()]
+        sgqa.index_build(s, d["kp"], kb, [wl.L], blk_begin=blk0, stream=stream)
+        m.append(ev())
+        sgqa.indexer_topk(s, d["qp"], kb, [wl.q_start], idx, workspace=ws, stream=stream)
+        m.append(ev())
+        sgqa.sparse_attn_prefill(s, d["Q"], d["K"], d["V"], d["G"], idx, wl.q_start, wl.L, scale,
+                                 out, lse, workspace=ws_attn, stream=stream)
+        m.append(ev())
+        return m
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    marks = [step() for _ in range(steps)]
+    torch.cuda.synchronize()
+    per = [[m[j].elapsed_time(m[j + 1]) for j in range(3)] for m in marks]
+    med = lambda xs: sorted(xs)[len(xs) // 2]  # noqa: E731
+    build_ms, topk_ms, attn_ms = (med([p[j] for p in per]) for j in range(3))
+    layer_ms = med([sum(p) for p in per])
+    pairs = attended_pairs(wl.q_start, wl.T, s.block_size, s.topk_blocks)
+    sc_pairs = scored_pairs(wl.q_start, wl.T, s.block_size)
+    attn_flops = 4 * s.head_dim * s.num_q_heads * pairs
+    res = {"workload": wl.name, "T": wl.T, "L": wl.L, "q_start": wl.q_start,
+           "ms_per_step": layer_ms, "tokens_per_s": wl.T / (layer_ms / 1e3),
+           "stages_ms": {"index_build_range": build_ms, "indexer_topk": topk_ms,
+                         "sparse_attn_prefill": attn_ms},
+           "indexer_share": (build_ms + topk_ms) / layer_ms,
+           "attention_tflops": attn_flops / (attn_ms / 1e3) / 1e12,
+           "indexer_tflops": 2 * s.proxy_dim * sc_pairs / (topk_ms / 1e3) / 1e12,
+           "indexer_to_attention_flops": (2 * s.proxy_dim * sc_pairs) / attn_flops,
+           "timing": f"median of {steps} steps, stages one after the other on one stream"}
+    log(f"chunked prefill: {layer_ms:.2f} ms/step (build {build_ms:.3f}, topk {topk_ms:.3f}, "
+        f"attn {attn_ms:.3f}) -> {res['tokens_per_s']:,.0f} tokens/s, indexer share "
+        f"{res['indexer_share']:.3f}")
+    if cpu:
+        res["cpu_baseline"] = cpu_baseline_chunked(wl, d, rows=512)
+        log(f"chunked prefill cpu baseline: {res['cpu_baseline']['sample']}")
+    del d, kb, idx, out, lse, ws, ws_attn
+    torch.cuda.empty_cache()
+    return res
+
+
+def bench_decode(steps: int, warmup: int, cpu: bool = False):
     import torch
     from long_context_sparse_18_amd import WORKLOADS, inputs, sgqa
 
@@ -225,7 +317,6 @@ def bench_decode(steps: int, warmup: int):
     d = inputs.make_decode(wl, 3, dev)
     kb = torch.empty((n, wl.nblk, s.proxy_dim), dtype=torch.bfloat16, device=dev)
     sgqa.index_build(s, d["kp"], kb, [wl.L] * n)
-    del d["kp"]
     idx = torch.empty((n, 1, s.topk_blocks), dtype=torch.int32, device=dev)
     out = torch.empty_like(d["Q"])
     ws_topk = torch.empty(sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, s, n, 1, wl.L),
@@ -274,6 +365,12 @@ def bench_decode(steps: int, warmup: int):
     res = dict(us_median=med, us_topk=sorted(t_topk)[len(t_topk) // 2],
                us_attn=sorted(t_attn)[len(t_attn) // 2], bytes=bytes_total,
                gbs=bytes_total / (med * 1e-6) / 1e9)
+    if cpu:
+        log("decode: oracle on all 16 sequences")
+        res["cpu_baseline"] = cpu_baseline_decode(wl, d, d["qp"], idx.shape)
+        log(f"decode cpu baseline: {res['cpu_baseline']['sample']}")
+    del d["kp"]
+    torch.cuda.empty_cache()
 
     # the same step on FP8 storage (E4M3 rows with one fp32 scale each) of index and caches
     log("decode: quantising index and caches to FP8")
@@ -427,11 +524,127 @@ def cpu_baseline(pre, rows: int, seed: int = 0, budget_s: float = 15.0):
         done += len(sel_rows)
     per_row = (t_sel + t_att) / done
     full_s = (t1 - t0) + per_row * wl.T
-    cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
-    return {"value": wl.T / full_s, "unit": "tokens/s/layer", "cores": cores, "kind": "oracle",
+    host = host_description(lib)
+    return {"value": wl.T / full_s, "unit": "tokens/s/layer", "cores": host["oracle_threads"],
+            "kind": "oracle", "host": host, "extrapolated": True,
+            "stages_s": {"index_build": t1 - t0, "scores_topk_per_row": t_sel / done,
+                         "attention_per_row": t_att / done},
             "sample": (f"full index build ({t1 - t0:.2f} s) + {done} random query rows of the "
                        f"131072-token prefill (scores+sort {t_sel:.2f} s, attention "
                        f"{t_att:.2f} s), extrapolated to all rows")}
+
+
+def host_description(lib=None) -> dict:
+    """The host the oracle ran on: CPU model, logical CPUs, CPUs this process may use, the
+    OpenMP setting and the threads the oracle's parallel loops actually ran on."""
+    import oracle
+    model = "unknown"
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"cpu_model": model, "nproc": os.cpu_count(),
+            "affinity_cpus": len(os.sched_getaffinity(0)),
+            "OMP_NUM_THREADS": os.environ.get("OMP_NUM_THREADS"),
+            "oracle_threads": oracle.num_threads(lib)}
+
+
+def cpu_baseline_chunked(wl, d, rows: int, seed: int = 0, budget_s: float = 20.0):
+    """The fp64 oracle on the chunked prefill: the index rebuild of the blocks the chunk touched
+    (timed in full), then scores + sort top-k and attention on random query rows in chunks of
+    64 until about ``budget_s`` seconds or ``rows`` rows, extrapolated to all 8192 rows."""
+    import numpy as np
+    import oracle
+    import torch
+    from long_context_sparse_18_amd.inputs import bits
+
+    s = wl.shape
+    B = s.block_size
+    lib = oracle.load()
+    kp = bits(d["kp"])
+    blk0 = wl.q_start // B
+    kb = oracle.index_build(kp[: blk0 * B], B, lib=lib)  # the history, built before the chunk
+    t0 = time.perf_counter()
+    kb_new = oracle.index_build(kp[blk0 * B:], B, lib=lib)
+    t1 = time.perf_counter()
+    kb = np.concatenate([kb, kb_new])
+    del kp
+    K, V = bits(d["K"]), bits(d["V"])
+    rng = np.random.default_rng(seed)
+    order = rng.choice(wl.T, size=rows, replace=False).astype(np.int64)
+    done, t_sel, t_att = 0, 0.0, 0.0
+    while done < rows and t_sel + t_att < budget_s:
+        sel_rows = np.sort(order[done:done + 64])
+        rt = torch.from_numpy(sel_rows).to(d["Q"].device)
+        t = sel_rows + wl.q_start
+        qp = bits(d["qp"].index_select(0, rt))
+        q, g = bits(d["Q"].index_select(0, rt)), bits(d["G"].index_select(0, rt))
+        ta = time.perf_counter()
+        sc = oracle.scores(qp, t, B, kb, width=int(t.max()) // B, lib=lib)
+        idx = oracle.topk(sc, t, B, s.topk_blocks, lib=lib)
+        tb = time.perf_counter()
+        oracle.sparse_attention(q, t, K, V, g, idx, B, 1.0 / math.sqrt(s.head_dim), lib=lib)
+        tc = time.perf_counter()
+        t_sel += tb - ta
+        t_att += tc - tb
+        done += len(sel_rows)
+    full_s = (t1 - t0) + (t_sel + t_att) / done * wl.T
+    host = host_description(lib)
+    return {"value": wl.T / full_s, "unit": "tokens/s/layer", "cores": host["oracle_threads"],
+            "kind": "oracle", "host": host, "extrapolated": True,
+            "stages_s": {"index_build_range": t1 - t0, "scores_topk_per_row": t_sel / done,
+                         "attention_per_row": t_att / done},
+            "sample": (f"index rebuild of blocks [{blk0}, {wl.nblk}) in full ({t1 - t0:.2f} s) "
+                       f"+ {done} random query rows of the chunk (scores+sort {t_sel:.2f} s, "
+                       f"attention {t_att:.2f} s), extrapolated to all {wl.T} rows")}
+
+
+def cpu_baseline_decode(wl, d, qp, idx_shape) -> dict:
+    """The fp64 oracle on the whole decode batch (16 sequences, one query each at t = L - 1):
+    per sequence the scores over all 131 071 past blocks, the sort top-k and the attention,
+    timed; the oracle's own index build of each sequence (untimed on the GPU path, where the
+    index is precomputed) is timed separately."""
+    import numpy as np
+    import oracle
+    from long_context_sparse_18_amd.inputs import bits
+
+    s = wl.shape
+    B = s.block_size
+    lib = oracle.load()
+    t = np.array([wl.L - 1], dtype=np.int64)
+    c = (wl.L - 1) // B
+    t_build = t_sel = t_att = 0.0
+    for b in range(wl.nseq):
+        kp = bits(d["kp"][b])
+        ta = time.perf_counter()
+        kb = oracle.index_build(kp, B, lib=lib)
+        tb = time.perf_counter()
+        del kp
+        sc = oracle.scores(bits(qp[b:b + 1]), t, B, kb, width=c, lib=lib)
+        sel = oracle.topk(sc, t, B, s.topk_blocks, lib=lib)
+        tc = time.perf_counter()
+        K, V = bits(d["K"][b]), bits(d["V"][b])
+        td = time.perf_counter()
+        oracle.sparse_attention(bits(d["Q"][b:b + 1]), t, K, V, bits(d["G"][b:b + 1]), sel, B,
+                                1.0 / math.sqrt(s.head_dim), lib=lib)
+        te = time.perf_counter()
+        del K, V
+        t_build += tb - ta
+        t_sel += tc - tb
+        t_att += te - td
+    host = host_description(lib)
+    us = (t_sel + t_att) * 1e6
+    return {"value": us, "unit": "us/layer/batch", "cores": host["oracle_threads"],
+            "kind": "oracle", "host": host, "extrapolated": False,
+            "stages_s": {"scores_topk": t_sel, "attention": t_att,
+                         "index_build_untimed_on_gpu": t_build},
+            "sample": (f"all {wl.nseq} sequences of the 1 048 576-token decode in full: scores "
+                       f"over 131 071 blocks + sort top-k {t_sel:.2f} s, attention {t_att:.2f} s "
+                       f"(the oracle's index builds, {t_build:.2f} s, are outside the figure as "
+                       f"the GPU's are)")}
 
 
 def measure_peaks():
@@ -507,6 +720,8 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=3072)
     ap.add_argument("--no-coverage", action="store_true")
+    ap.add_argument("--no-chunked", action="store_true",
+                    help="skip the chunked prefill (8192 rows against 1M tokens)")
     ap.add_argument("--no-prefill", action="store_true",
                     help="time only the decode workload (for profiling runs)")
     ap.add_argument("--no-peaks", action="store_true",
@@ -556,7 +771,6 @@ def main():
     s = wl.shape
     tokens_per_s = wl.T / (pre["ms_per_step"] / 1e3)
     attn_tflops = pre["attn_flops"] / (pre["attn_ms"] / 1e3) / 1e12
-    attn_gbs = pre["attn_bytes"] / (pre["attn_ms"] / 1e3) / 1e9
     log(f"prefill: {pre['ms_per_step']:.2f} ms/step (stages one after the other "
         f"{pre['sequential_ms']:.2f}: build {pre['build_ms']:.3f}, topk {pre['topk_ms']:.3f}, "
         f"attn {pre['attn_ms']:.3f}) -> {tokens_per_s:,.0f} tokens/s, "
@@ -564,8 +778,7 @@ def main():
     log(f"sliding window: {pre['swa']['ms']:.3f} ms; index from keys: "
         f"{pre['fused_index']['ms']:.3f} ms ({pre['fused_index']['GBps']:.0f} GB/s); backward "
         f"{pre['backward']['ms']:.1f} ms ({pre['backward']['ratio_to_forward_attention']:.2f}x "
-        f"the forward attention), {pre['backward']['d_from_forward_output']['ms']:.1f} ms with "
-        f"D from the forward output")
+        f"the forward attention)")
     cpu = None
     if not args.no_cpu:
         log(f"cpu baseline: oracle on up to {args.cpu_rows} rows (~15 s of oracle time)")
@@ -580,14 +793,30 @@ def main():
         cov = bench_coverage()
         log(f"coverage: {cov}")
         torch.cuda.empty_cache()
+    chunked = None
+    if not args.no_chunked:
+        chunked = bench_chunked(max(args.steps // 2, 5), args.warmup, cpu=not args.no_cpu)
     dec = None
     if not args.no_decode:
-        dec = bench_decode(max(args.steps, 5), args.warmup)
+        dec = bench_decode(max(args.steps, 5), args.warmup, cpu=not args.no_cpu)
         log(f"decode: {dec['us_median']:.1f} us/step (topk {dec['us_topk']:.1f}, attn "
             f"{dec['us_attn']:.1f}), {dec['gbs']:.0f} GB/s; FP8 storage "
             f"{dec['fp8']['us_median']:.1f} us/step (topk {dec['fp8']['us_topk']:.1f}, attn "
             f"{dec['fp8']['us_attn']:.1f}), {dec['fp8']['gbs']:.0f} GB/s")
 
+    traffic = measured_traffic("attn_prefill_128k")
+    attn_s = pre["attn_ms"] / 1e3
+    # the memory side of the same kernel: the K/V rows every attended pair gathers (no reuse)
+    # against the bytes that reached past L2 (FETCH_SIZE + WRITE_SIZE, copy-calibrated; these
+    # include hits in the memory-side cache, so they bound the HBM bytes from above)
+    memory_side = {"gathered_bytes_no_reuse": pre["gather_bytes"],
+                   "io_bytes": pre["attn_bytes"] - pre["gather_bytes"],
+                   "gathered_GBps": pre["gather_bytes"] / attn_s / 1e9,
+                   "past_L2_bytes": traffic,
+                   "past_L2_GBps": None if traffic is None else traffic / attn_s / 1e9,
+                   "past_L2_frac_of_hbm_peak": (None if traffic is None else
+                                                traffic / attn_s / 1e9 / PEAK_HBM_GBS),
+                   "l2_reuse": None if traffic is None else pre["attn_bytes"] / traffic}
     line = {
         "metric": METRIC,
         "value": tokens_per_s,
@@ -604,11 +833,16 @@ def main():
         "config": {"workload": wl.name, "T": wl.T, "L": wl.L, "q_heads": s.num_q_heads,
                    "kv_heads": s.num_kv_heads, "head_dim": s.head_dim, "proxy_dim": s.proxy_dim,
                    "block_size": s.block_size, "topk_blocks": s.topk_blocks},
-        "roofline": {"bound": "hbm", "achieved": attn_gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s",
-                     "frac": attn_gbs / PEAK_HBM_GBS,
-                     "traffic": measured_traffic("attn_prefill_128k"),
-                     "kernel": "k_attn_prefill<192>", "algorithmic_bytes": pre["attn_bytes"],
-                     "mfma_tflops": attn_tflops, "mfma_frac": attn_tflops / PEAK_BF16_TFLOPS},
+        "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
+                     "traffic": traffic,
+                     "kernel": "k_attn_prefill<192>",
+                     "launch": ("one sgqa_sparse_attn_prefill call over all 131072 rows: 4 row "
+                                "chunks x 8 history slices = 32 dispatches"),
+                     "algorithmic_flops": pre["attn_flops"],
+                     "flops_per_attended_pair": 4 * s.head_dim * s.num_q_heads,
+                     "attended_pairs": pre["pairs"],
+                     "memory_side": memory_side},
         "measured_peaks": peaks,
         "cpu_baseline": cpu,
         "stages_ms": {"index_build": pre["build_ms"], "indexer_topk": pre["topk_ms"],
@@ -619,9 +853,13 @@ def main():
                      f"stages run one after the other ({pre['sequential_ms']:.2f} ms per step)"),
     }
     if peaks is not None:
-        line["roofline"]["frac_of_measured_read"] = attn_gbs / peaks["hbm_read_GBps"]
-        line["roofline"]["mfma_frac_of_measured"] = attn_tflops / peaks["mfma_bf16_tflops"]
+        line["roofline"]["frac_of_measured_mfma"] = attn_tflops / peaks["mfma_bf16_tflops"]
         line["roofline"]["frac_of_gather_roofline"] = attn_tflops / peaks["gather_roofline_tflops"]
+    line["ms_per_step_median"] = pre["median_ms"]
+    line["attention_ms_median"] = pre["attn_ms_median"]
+    line["index_build"] = pre["index_build"]
+    if chunked is not None:
+        line["chunked_prefill"] = chunked
     line["sliding_window_attention"] = pre["swa"]
     line["index_build_from_keys"] = pre["fused_index"]
     line["attention_backward"] = pre["backward"]
@@ -631,7 +869,10 @@ def main():
         line["decode"] = {"workload": "decode-1m-x16", "us_per_layer": dec["us_median"],
                           "us_indexer_topk": dec["us_topk"], "us_attention": dec["us_attn"],
                           "GBps": dec["gbs"], "hbm_frac": dec["gbs"] / PEAK_HBM_GBS,
-                          "algorithmic_bytes": dec["bytes"]}
+                          "algorithmic_bytes": dec["bytes"],
+                          "timing": "median of the steps, 512 MiB read between steps"}
+        if "cpu_baseline" in dec:
+            line["decode"]["cpu_baseline"] = dec["cpu_baseline"]
         if peaks is not None:
             line["decode"]["hbm_frac_of_measured_read"] = dec["gbs"] / peaks["hbm_read_GBps"]
         f8 = dec["fp8"]

@@ -253,13 +253,14 @@ sgqa_status sgqa_swa_prefill(const sgqa_dims *dims, const sgqa_bf16 *q, const sg
  *   dk_s   = softmax_scale * sum over (row, head of the group) of dz_s q
  *   dv_s   = sum over (row, head of the group) of P_s sigmoid(gate) dout
  * With out NULL, D is formed from the same P and dP the gradients use (a first
- * sweep over the selection), so the dz of a row sum to zero.  With out the
- * forward's bf16 output [T][Hq][d] (2-byte aligned), D = dout . out in fp32: one
- * elementwise pass, and dq sweeps the selection once instead of twice; every dz
- * of a row then shares the error of D (from the rounding of out), which grows
- * with the attended keys: on a 128K prefill (4096 keys per row) dq is 0.99 %
- * rel-L2 from the exact gradient with out and 0.32 % without; dv does not
- * involve D and is the same bits either way.  dk and dv are written for every token
+ * sweep over the selection), so the dz of a row sum to zero.  EXPERIMENTAL:
+ * with out the forward's bf16 output [T][Hq][d] (2-byte aligned), D = dout . out
+ * in fp32: one elementwise pass, and dq sweeps the selection once instead of
+ * twice; every dz of a row then shares the error of D (from the rounding of
+ * out), which grows with the attended keys: on a 128K prefill (4096 keys per
+ * row) dq is 0.99 % rel-L2 from the exact gradient with out, at the 1 % bound
+ * the default meets with 0.32 %, so rows that attend thousands of keys should
+ * pass NULL; dv does not involve D and is the same bits either way.  dk and dv are written for every token
  * of [0, L) (zero where no row attends); every sum runs in a fixed order, so the
  * results are deterministic.  Layouts as sgqa_sparse_attn_prefill; dq
  * [T][Hq][d], dk / dv [L][Hkv][d] and dgate [T][Hq] are fp32.  nseq is 1.

@@ -39,6 +39,8 @@ def build(force: bool = False, src: str = _SRC, out: str = _LIB, extra_flags=())
 def _bind(lib):
     i64, i32, dbl = ctypes.c_int64, ctypes.c_int32, ctypes.c_double
     p = ctypes.c_void_p
+    lib.orc_num_threads.restype = i32
+    lib.orc_num_threads.argtypes = []
     lib.orc_num_blocks.restype = i64
     lib.orc_num_blocks.argtypes = [i64, i32]
     lib.orc_num_candidates.restype = i64
@@ -99,6 +101,11 @@ def _u16(a) -> np.ndarray:
 
 def _ptr(a: np.ndarray):
     return a.ctypes.data_as(ctypes.c_void_p)
+
+
+def num_threads(lib=None) -> int:
+    """Threads the oracle's parallel loops run on."""
+    return int((lib or load()).orc_num_threads())
 
 
 def num_blocks(L: int, B: int, lib=None) -> int:

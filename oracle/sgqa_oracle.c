@@ -36,6 +36,7 @@
  * Nothing here is blocked, fused or reordered beyond the definitions above.
  */
 #include <math.h>
+#include <omp.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -47,6 +48,18 @@ static double widen_bf16(uint16_t h)
     float f;
     memcpy(&f, &bits, sizeof f);
     return (double)f;
+}
+
+/* Threads an OpenMP region of this library uses (reported beside the oracle's timings). */
+int32_t orc_num_threads(void)
+{
+    int32_t n = 1;
+#pragma omp parallel
+    {
+#pragma omp single
+        n = (int32_t)omp_get_num_threads();
+    }
+    return n;
 }
 
 /* Number of index blocks for a sequence of L tokens: ceil(L / B). */

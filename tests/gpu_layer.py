@@ -66,7 +66,8 @@ def check_prefill_rows(shape, d, res, q_start: int, rows: np.ndarray, kb_ref=Non
     for r in range(len(rows)):
         c = int(t[r] // B)
         exact_iso += parity.check_selection(idx_rows[r], s_iso[r], c, k, ref_iso[r])
-        exact_e2e += parity.check_selection(idx_rows[r], s_e2e[r], c, k, ref_e2e[r])
+        exact_e2e += parity.check_selection(idx_rows[r], s_e2e[r], c, k, ref_e2e[r],
+                                            end_to_end=True)
         worst_score = max(worst_score, parity.check_sel_scores(sel_rows[r], idx_rows[r], s_iso[r], c, k))
     # attention given the GPU's selection
     if host_cache is None:

@@ -139,7 +139,8 @@ def test_decode_1m_batch16():
         exact += parity.check_selection(got, s_iso[0], c, k, ref_iso[0])
         parity.check_sel_scores(sel[b, 0].cpu().numpy(), got, s_iso[0], c, k)
         s_e2e = oracle.scores(bits(d["qp"][b:b + 1]), t, B, kb_ref, width=c)
-        parity.check_selection(got, s_e2e[0], c, k, oracle.topk(s_e2e, t, B, k)[0])
+        parity.check_selection(got, s_e2e[0], c, k, oracle.topk(s_e2e, t, B, k)[0],
+                               end_to_end=True)
         toks = oracle.token_set(got, B, L - 1)
         tt = torch.from_numpy(toks).to(DEV)
         o_ref, l_ref = oracle.attend(bits(d["Q"][b]), bits(d["K"][b].index_select(0, tt)),
@@ -284,6 +285,42 @@ def test_backward_128k_sampled():
     say(f"backward 128K: {st} dV-sum rel {rel_v:.3g} dK-sum rel {rel_k:.3g}")
     assert rel_v <= 4e-3, rel_v
     assert rel_k <= 1e-2, rel_k
+
+    # dK and dV element by element on sampled key blocks.  Only the rows whose selection holds
+    # block j attend to its tokens (a row's own block is in its selection too), so the oracle's
+    # backward over exactly those rows gives the whole gradient of the block's 8 tokens.  The
+    # blocks: the last one (the own block of the last 8 rows only), two more near the end,
+    # seeded late blocks that a hundred or two rows selected, and one block at ~70 % of the
+    # cache that ~1 500 rows selected, spread over ~10 of the 32 dK/dV row slices; up to ~2 000
+    # rows in all (the oracle's backward runs ~20 rows/s on 16 threads).
+    B = shape.block_size
+    idx = res["idx"]
+    nblk = wl.nblk
+    rng = np.random.default_rng(25)
+    cands = ([nblk - 1, nblk - 2, nblk - 40, int(nblk * 0.7)] +
+             rng.integers(nblk - 1000, nblk - 100, 12).tolist())
+    blocks, total = [], 0
+    for j in cands:
+        n_j = int((idx == j).any(dim=1).sum().item())
+        if j not in blocks and total + n_j <= 2000 and len(blocks) < 6:
+            blocks.append(j)
+            total += n_j
+    say(f"backward 128K: dK/dV of blocks {blocks} ({total} rows)")
+    Kb, Vb = bits(d["K"]), bits(d["V"])
+    scale = 1.0 / math.sqrt(shape.head_dim)
+    for j in blocks:
+        sel = torch.nonzero((idx == j).any(dim=1)).flatten()
+        rows_np = sel.cpu().numpy()
+        _, dk_ref, dv_ref, _ = oracle.sparse_attention_backward(
+            bits(d["Q"].index_select(0, sel)), rows_np + wl.q_start, Kb, Vb,
+            bits(d["G"].index_select(0, sel)), idx.index_select(0, sel).cpu().numpy(), B, scale,
+            bits(dout.index_select(0, sel)))
+        tok = slice(j * B, min((j + 1) * B, wl.L))
+        st_k = parity.check_grad("dk", grads["dk"][tok].cpu().numpy(), dk_ref[tok])
+        st_v = parity.check_grad("dv", grads["dv"][tok].cpu().numpy(), dv_ref[tok])
+        say(f"backward 128K: block {j} ({rows_np.size} rows, rows {rows_np.min()}.."
+            f"{rows_np.max()}) {st_k} {st_v}")
+    assert len(blocks) >= 5 and int(nblk * 0.7) in blocks
 
 
 def test_index_from_keys_128k():
