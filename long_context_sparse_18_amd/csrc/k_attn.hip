@@ -504,25 +504,31 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
     const int64_t t = a.q_start + r;
     const int64_t c = t / a.B;
     const int nvalid = (int)((c + 1 < a.k) ? c + 1 : a.k);
-    // Rows with a short history (c < 2k, the launcher's own threshold for slicing at all) are
-    // attended in one pass, in the last slice: then a row's result depends only on the row,
-    // not on which other rows share its launch.
-    const bool sliced = a.nslices > 1 && c >= 2 * (int64_t)a.k;
-    if (a.nslices > 1 && !sliced && a.slice + 1 < a.nslices)
+    // History-sliced launches: launch `slice` covers the blocks [slice*W, (slice+1)*W) of every
+    // row's history, so each launch's rows gather from one W-block range of the cache.  A row
+    // takes part in launches 0 .. c/W (the last one also holds its own block c).  Rows with a
+    // short history (c < 2k) are attended in one pass, in launch c/W.  Every choice depends only
+    // on the row's own c and selection, so a row's bits do not depend on its launch's other rows.
+    const int64_t W = a.slice_blocks;
+    const int64_t last = W > 0 ? c / W : 0;
+    if (W > 0 && a.slice > last)
+        return;
+    const bool sliced = W > 0 && c >= 2 * (int64_t)a.k;
+    if (W > 0 && !sliced && a.slice != last)
         return;
 
-    bf16x8 qf[D / 32];
-    load_q<D>(a.q + (r * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
-    WaveState<D> st;
     int e_lo = 0, e_hi = nvalid;
+    bool first = true;
     if (sliced) {
-        // this launch covers the blocks in [c*s/S, c*(s+1)/S) (the last slice also holds the
-        // own block c); the idx row is ascending, so that is a contiguous run of entries
-        const int64_t lo = c * a.slice / a.nslices;
-        const int64_t hi = a.slice + 1 == a.nslices ? c + 1 : c * (a.slice + 1) / a.nslices;
+        // entries of this launch: the idx row is ascending, so the blocks in [lo, hi) are a
+        // contiguous run of entries; the row's first launch with entries is the one holding its
+        // first entry's block
+        const int64_t lo = (int64_t)a.slice * W;
+        const int64_t hi = a.slice == last ? c + 1 : lo + W;
         const int32_t *row = a.idx + r * a.k;
         const int lane = threadIdx.x & 63;
         int below_lo = 0, below_hi = 0;
+        int32_t head = 0;
         for (int e0 = 0; e0 < nvalid; e0 += 256) {  // four loads in flight per lane
             int32_t b[4];
 #pragma unroll
@@ -530,6 +536,8 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
                 const int e = e0 + u * 64 + lane;
                 b[u] = row[e < nvalid ? e : 0];
             }
+            if (e0 == 0)
+                head = b[0];
 #pragma unroll
             for (int u = 0; u < 4; ++u) {
                 const bool in = e0 + u * 64 + lane < nvalid && b[u] >= 0;
@@ -542,10 +550,20 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
             below_lo += __shfl_xor(below_lo, o);
             below_hi += __shfl_xor(below_hi, o);
         }
+        const int64_t first_slice = (int64_t)__shfl(head, 0) / W;  // lane 0 read entry 0
+        if (a.slice < first_slice)
+            return;  // no entries yet: the state starts in a later launch
         e_lo = below_lo;
-        e_hi = a.slice + 1 == a.nslices ? nvalid : below_hi;
+        e_hi = a.slice == last ? nvalid : below_hi;
+        first = a.slice == first_slice;
+        if (!first && a.slice < last && e_lo == e_hi)
+            return;  // nothing in this range: the parked state stays as it is
     }
-    if (a.slice == 0 || !sliced)
+
+    bf16x8 qf[D / 32];
+    load_q<D>(a.q + (r * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
+    WaveState<D> st;
+    if (first)
         init_state<D>(st);
     else
         load_state<D>(st, a.state + state_offset(a, r, g));
@@ -553,7 +571,7 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
     attend_range<D>(Bf16Rows{a.kc + (int64_t)g * D, a.vc + (int64_t)g * D}, a.Hkv, src, qf,
                     a.scale_log2, lds + wave * attn_vbuf_elems(D), st);
 
-    if (a.slice + 1 >= a.nslices)
+    if (!sliced || a.slice == last)
         store_row<D>(st, a, r, g, hpg);
     else
         save_state<D>(st, a.state + state_offset(a, r, g));
@@ -957,7 +975,8 @@ static hipError_t launch_swa_d(const AttnArgs &a, hipStream_t stream)
     return hipGetLastError();
 }
 
-// Sliced prefill: rows in chunks that fit the workspace, each chunk in `nslices` launches.
+// Sliced prefill: rows in chunks that fit the workspace; each chunk in one launch per
+// slice_blocks-block range of history, up to the range holding the chunk's last own block.
 template <int D>
 static hipError_t launch_prefill_sliced(const AttnArgs &a0, hipStream_t stream)
 {
@@ -975,8 +994,10 @@ static hipError_t launch_prefill_sliced(const AttnArgs &a0, hipStream_t stream)
         a.idx = a0.idx + r0 * a0.k;
         a.out = a0.out + r0 * a0.Hq * D;
         a.lse = a0.lse ? a0.lse + r0 * a0.Hq : nullptr;
-        for (int sl = 0; sl < a0.nslices; ++sl) {
-            a.slice = sl;
+        const int64_t c_last = (a.q_start + n - 1) / a0.B;
+        const int64_t nsl = c_last / a0.slice_blocks + 1;
+        for (int64_t sl = 0; sl < nsl; ++sl) {
+            a.slice = (int32_t)sl;
             hipError_t e = launch_prefill_d<D>(a, stream);
             if (e != hipSuccess)
                 return e;
@@ -1022,7 +1043,7 @@ hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream)
         return hipSuccess;
     if (!a.q || !a.out || (!a.idx && !a.window))
         return hipErrorInvalidValue;  // never launch without the tensors the kernels touch
-    if (a.nslices > 1) {
+    if (a.slice_blocks > 0) {
         switch (a.d) {
         case 64: return launch_prefill_sliced<64>(a, stream);
         case 128: return launch_prefill_sliced<128>(a, stream);

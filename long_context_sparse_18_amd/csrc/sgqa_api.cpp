@@ -144,6 +144,13 @@ TopkPlan topk_plan(const sgqa_dims *d, const int64_t *q_start, int32_t nseq, int
 
 constexpr size_t kIndexerWorkspaceCap = size_t(2) << 30;
 
+#ifndef SGQA_SLICE_HALF_K
+#define SGQA_SLICE_HALF_K 4
+#endif
+// Blocks per history slice of the sliced prefill attention, in units of k/2 (2k: 1024 blocks
+// at the real shape).
+constexpr int64_t kPrefillSliceHalfK = SGQA_SLICE_HALF_K;
+
 } // namespace
 
 extern "C" {
@@ -514,7 +521,7 @@ sgqa_status sgqa_sparse_attn_prefill(const sgqa_dims *dims, const sgqa_bf16 *q,
     a.scale_log2 = softmax_scale * 1.4426950408889634f;
     a.out = out;
     a.lse = lse;
-    a.nslices = 1;
+    a.slice_blocks = 0;
     const size_t row_state = sgqa_workspace_bytes(SGQA_OP_ATTN_PREFILL, dims, 1, 1, L);
     if (workspace) {
         if (!aligned(workspace, 16))
@@ -522,13 +529,14 @@ sgqa_status sgqa_sparse_attn_prefill(const sgqa_dims *dims, const sgqa_bf16 *q,
         if (workspace_bytes < row_state)
             return fail(SGQA_ERR_WORKSPACE, "prefill workspace needs >= %zu bytes, got %zu",
                         row_state, workspace_bytes);
-        // Eight history slices measured best on the 128K prefill (126.9 ms; 4/5/6/10/12/16:
-        // 141.4/134.3/130.9/127.3/130.8/142.6; one pass ~160): each XCD's L2 then holds an
-        // eighth of its group's history, while every slice boundary parks ~13 KB of state per
-        // row and group.  Short histories gain nothing and stay in one pass (row by row: the
-        // kernel attends rows with c < 2k in one pass even in a sliced launch).
+        // History slices of W = kPrefillSliceHalfK * k / 2 blocks: each launch's rows gather from
+        // one such range of the cache, which each XCD's L2 holds for its KV group, while every
+        // slice boundary a row crosses parks ~13 KB of state per group.  Short histories gain
+        // nothing and stay in one pass (row by row: the kernel attends rows with c < 2k in one
+        // pass even in a sliced launch).
         const int64_t max_cand = (q_start + T - 1) / dims->block_size;
-        a.nslices = max_cand >= 2 * (int64_t)dims->topk_blocks ? 8 : 1;
+        const int64_t W = (kPrefillSliceHalfK * dims->topk_blocks + 1) / 2;
+        a.slice_blocks = max_cand >= 2 * (int64_t)dims->topk_blocks ? W : 0;
         a.state = static_cast<float *>(workspace);
         a.state_bytes = (int64_t)workspace_bytes;
         a.state_stride = sgqa::prefill_state_stride(a.d);

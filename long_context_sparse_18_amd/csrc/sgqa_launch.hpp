@@ -125,9 +125,10 @@ struct AttnArgs {
     int32_t entries_per_split;
     int32_t npart;           // partial states per (sequence, head): one per workgroup
     int64_t window;          // sliding-window attention: tokens per window
-    // sliced prefill: launch `slice` of `nslices` over each query's blocks, parking the
-    // per-lane softmax state (state_stride floats per lane) in `state`
-    int32_t nslices;
+    // sliced prefill: launch `slice` covers the history blocks [slice, slice + 1) *
+    // slice_blocks of every row (0: one pass), parking the per-lane softmax state
+    // (state_stride floats per lane) in `state` between launches
+    int64_t slice_blocks;
     int32_t slice;
     float *state;
     int64_t state_bytes;
