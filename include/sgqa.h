@@ -139,6 +139,16 @@ sgqa_status sgqa_index_build_from_keys(const sgqa_dims *dims, const sgqa_bf16 *k
  *   workspace  [dev]  scratch of workspace_bytes bytes (at least
  *                      sgqa_workspace_bytes(SGQA_OP_INDEXER_TOPK, ...) with
  *                      T = 1 rounded up; more lets one launch cover more rows)
+ * Rows of at most 131072 candidate blocks with k <= 1024 and proxy_dim in
+ * {32, 64, 128, 256, 512} are selected without storing their scores: a sampled
+ * lower bound of each row's threshold filters the scores as the matrix cores
+ * produce them, and only the blocks above it are listed (about 2.5 (k-1) per
+ * row) and selected exactly; a row whose bound misses is re-scored in full by
+ * one of 64 fallback workgroups.  The result is the same bits either way.  This
+ * path needs 256 B + 64 * ceil64(c_max) * 4 B plus, per query row of a pass,
+ * 4 ns + 12 + 8 cap bytes (ns, cap = 1024, 2048 up to 32768 candidates, else
+ * 4096, 4096); smaller workspaces, longer rows and other shapes store every
+ * score row ([rows][ceil64(c_max)] fp32 per pass) and select over it.
  */
 sgqa_status sgqa_indexer_topk(const sgqa_dims *dims, const sgqa_bf16 *qp, int64_t qp_seq_stride,
                               const sgqa_bf16 *kb, int64_t kb_seq_stride, const int64_t *q_start,

@@ -38,12 +38,6 @@ __device__ __forceinline__ int wave_index()
     return __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
 }
 
-__device__ __forceinline__ void wave_lds_handoff()
-{
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-}
 
 // Column reads of a [row][d] bf16 tile in LDS (row stride ld elements, a multiple of 4) by the
 // transposing read ds_read_b64_tr_b16 (gfx950).  Within each 16-lane group, lane i receives
@@ -465,6 +459,9 @@ __device__ __forceinline__ void load_state(WaveState<D> &st, const float *p)
     st.l32 = v[2];
 }
 
+// Histories of more than this many slice_blocks ranges are cut into long_slices ranges.
+constexpr int64_t kMaxBaseSlices = 16;
+
 // Row and group of this wave under the two workgroup mappings (see k_attn_prefill).
 // Returns false for waves past the last row.
 template <bool kGroupPerXcd, typename Args>
@@ -504,12 +501,17 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
     const int64_t t = a.q_start + r;
     const int64_t c = t / a.B;
     const int nvalid = (int)((c + 1 < a.k) ? c + 1 : a.k);
-    // History-sliced launches: launch `slice` covers the blocks [slice*W, (slice+1)*W) of every
-    // row's history, so each launch's rows gather from one W-block range of the cache.  A row
-    // takes part in launches 0 .. c/W (the last one also holds its own block c).  Rows with a
-    // short history (c < 2k) are attended in one pass, in launch c/W.  Every choice depends only
-    // on the row's own c and selection, so a row's bits do not depend on its launch's other rows.
-    const int64_t W = a.slice_blocks;
+    // History-sliced launches: launch `slice` covers the blocks [slice*W, (slice+1)*W) of a
+    // row's history, so the launch's rows gather from one W-block range of the cache.  W is
+    // slice_blocks for histories of up to 16 such ranges; a longer history is cut into
+    // long_slices ranges of its own length instead (a row would otherwise park its state at
+    // more boundaries than it has entries to gather between them).  A row takes part in
+    // launches 0 .. c/W (the last one also holds its own block c).  Rows with a short history
+    // (c < 2k) are attended in one pass, in launch c/W.  Every choice depends only on the row's
+    // own c and selection, so a row's bits do not depend on its launch's other rows.
+    int64_t W = a.slice_blocks;
+    if (W > 0 && c + 1 > kMaxBaseSlices * W)
+        W = (c + a.long_slices) / a.long_slices;  // ceil((c + 1) / long_slices)
     const int64_t last = W > 0 ? c / W : 0;
     if (W > 0 && a.slice > last)
         return;
@@ -994,8 +996,15 @@ static hipError_t launch_prefill_sliced(const AttnArgs &a0, hipStream_t stream)
         a.idx = a0.idx + r0 * a0.k;
         a.out = a0.out + r0 * a0.Hq * D;
         a.lse = a0.lse ? a0.lse + r0 * a0.Hq : nullptr;
-        const int64_t c_last = (a.q_start + n - 1) / a0.B;
-        const int64_t nsl = c_last / a0.slice_blocks + 1;
+        // rows of up to kMaxBaseSlices ranges end in launch c / slice_blocks; longer ones in
+        // launch long_slices - 1 or earlier
+        const int64_t c_first = a.q_start / a0.B, c_last = (a.q_start + n - 1) / a0.B;
+        const int64_t c_short_max = kMaxBaseSlices * a0.slice_blocks - 1;
+        int64_t nsl = 0;
+        if (c_first <= c_short_max)  // rows of the base ranges
+            nsl = (c_last < c_short_max ? c_last : c_short_max) / a0.slice_blocks + 1;
+        if (c_last > c_short_max && a0.long_slices > nsl)  // rows cut into long_slices ranges
+            nsl = a0.long_slices;
         for (int64_t sl = 0; sl < nsl; ++sl) {
             a.slice = (int32_t)sl;
             hipError_t e = launch_prefill_d<D>(a, stream);

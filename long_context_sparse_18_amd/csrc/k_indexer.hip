@@ -11,11 +11,14 @@
 // four waves; each wave owns 16 queries.  Tiles entirely past the causal limit
 // exit at once, and only complete past blocks (j < t/B) are written.
 //
-// Selection: one workgroup per query row runs an exact radix select on
-// order-preserving u32 keys (digits of 12, 12 and 8 bits, histograms in LDS),
-// then emits the chosen block ids in ascending order with a workgroup scan.
-// Ties at the threshold go to the lowest block indices, so the result is the
-// unique set "k-1 best by (score desc, index asc)" plus the own block.
+// Prefill selection without a score matrix (k_fused_*, the default for rows of up to
+// 131072 candidates): a sampled lower bound of each row's threshold filters the scores
+// as the matrix cores produce them; the listed blocks are selected exactly, one wave per
+// row, with ballot counts.  Otherwise the scores are stored and one workgroup per query
+// row runs an exact radix select on order-preserving u32 keys (digits of 12, 12 and
+// 8 bits, histograms in LDS), then emits the chosen block ids in ascending order with a
+// workgroup scan.  Ties at the threshold go to the lowest block indices, so the result
+// is the unique set "k-1 best by (score desc, index asc)" plus the own block.
 #include <hip/hip_runtime.h>
 
 #include "sgqa_device.hpp"
@@ -1043,6 +1046,780 @@ __global__ __launch_bounds__(NT) void k_select2(SelectArgs a)
             ++pos;
         }
     }
+}
+
+// ---- prefill top-k without the score matrix -------------------------------------------------
+// For rows of at most kFusedMaxCand candidate blocks (and k <= kFusedMaxK) no score row is
+// stored.  One pass over a block of query rows runs:
+//  1. k_fused_sample<P>: the scores of a strided sample of each row's blocks (ns per row; the
+//     stride is set per 64-row tile from the tile's first row), as order-preserving keys;
+//  2. k_fused_threshold: one wave per row takes T0 = the q-th largest sample key, found bit by
+//     bit from the top with the wave counting the keys at or above each candidate value
+//     (q is about twice the sample's expected share of the kept blocks, plus 16);
+//  3. k_fused_filter<P>: the scores of every candidate block, 64 queries x 64 blocks per
+//     workgroup on the matrix cores as in k_scores; each key >= T0 of a row is appended as
+//     (key, block) to that row's list (the 16 lanes holding a row's keys of a tile reserve their
+//     slots with one atomic add; the count keeps counting past the list's capacity);
+//  4. k_fused_select<NT>: one workgroup per row selects the k-1 largest listed keys exactly
+//     (radix passes over the list in LDS; exact ties of the full key go to the lowest block)
+//     and writes them in block order from per-word prefix counts of an LDS bitmap.  A row
+//     whose list holds fewer than k-1 keys (T0 above the row's threshold) or overflowed is
+//     queued instead;
+//  5. k_fused_fallback<NT>: a few persistent workgroups take the queued rows one at a time,
+//     score every candidate block of the row into their own scratch row with the same
+//     matrix-core arithmetic (so the same fp32 scores), and select exactly over it.
+// The listed keys are a superset of the selection whenever step 4 accepts a row, so the result
+// never depends on the sample, and it equals what the score-matrix path selects.
+constexpr int64_t kFusedMaxCand = 131072;       // bitmap words of the select's LDS, times 32
+constexpr int kFusedMaxK = 1024;
+constexpr int kFusedBitmapWords = (int)(kFusedMaxCand / 32);
+constexpr int kFusedFallbackWGs = 64;
+
+// sample size, list capacity and stride rule shared by the host and the kernels
+__host__ __device__ __forceinline__ int fused_ns(int64_t max_cand)
+{
+    return max_cand <= 32768 ? 1024 : 4096;
+}
+__host__ __device__ __forceinline__ int fused_cap(int64_t max_cand)
+{
+    return max_cand <= 32768 ? 2048 : 4096;
+}
+__device__ __forceinline__ int64_t fused_stride(int64_t c_first, int ns)
+{
+    const int64_t s = (c_first + ns - 1) / ns;
+    return s > 1 ? s : 1;
+}
+
+// Row r = s * nq + i of a pass; its position and own block.
+__device__ __forceinline__ int64_t fused_c(const FusedTopkArgs &a, int s, int i)
+{
+    return (a.q_start.v[s] + a.t0 + i) / a.B;
+}
+
+template <int P>
+__global__ __launch_bounds__(256) void k_fused_sample(FusedTopkArgs a)
+{
+    extern __shared__ __align__(16) uint16_t kb_tile[];  // [kTileB][P + 8]
+    const int s = blockIdx.z;
+    const int i0 = blockIdx.y * kTileQ;
+    const int m0 = blockIdx.x * kTileB;  // first sample of this tile
+    const int64_t stride = fused_stride(fused_c(a, s, i0), a.ns);
+    const int i_last = min(i0 + kTileQ, a.nq) - 1;
+    const int64_t c_last = fused_c(a, s, i_last);
+    constexpr int ldt = P + 8;
+    const int tid = threadIdx.x;
+    const uint16_t *kb = a.kb + (int64_t)s * a.kb_seq_stride;
+    constexpr int chunks = P / 8;
+    constexpr int kPer = (kTileB * chunks + 255) / 256;
+    u32x4 tv[kPer];
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {  // rows past the tile's last candidate load block 0
+        const int e = u * 256 + tid;
+        const int r = e / chunks, cc = e - r * chunks;
+        const int64_t j = (int64_t)(m0 + r) * stride;
+        const int64_t row = j < c_last && e < kTileB * chunks ? j : 0;
+        tv[u] = load16(kb + row * P + cc * 8);
+    }
+#pragma unroll
+    for (int u = 0; u < kPer; ++u) {
+        const int e = u * 256 + tid;
+        const int r = e / chunks, cc = e - r * chunks;
+        if (e < kTileB * chunks)
+            *reinterpret_cast<u32x4 *>(kb_tile + r * ldt + cc * 8) = tv[u];
+    }
+    __syncthreads();
+    const int wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    if (i0 + wave * 16 >= a.nq)
+        return;
+    const int qrow = i0 + wave * 16 + col;
+    const uint16_t *qp = a.qp + (int64_t)s * a.qp_seq_stride + (int64_t)(a.t0 + qrow) * P;
+    const uint16_t *qpr = qrow < a.nq ? qp : qp - (int64_t)col * P;
+    u32x4 av[P / 32];
+#pragma unroll
+    for (int kk = 0; kk < P / 32; ++kk)
+        av[kk] = load16(qpr + kk * 32 + q4 * 8);
+    f32x4 acc[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+        acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < P / 32; ++kk) {
+        const bf16x8 af = as_bf16x8(av[kk]);
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const u32x4 bv = *reinterpret_cast<const u32x4 *>(kb_tile + (n * 16 + col) * ldt +
+                                                              kk * 32 + q4 * 8);
+            acc[n] = mfma_16x16x32(af, as_bf16x8(bv), acc[n]);
+        }
+    }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = i0 + wave * 16 + q4 * 4 + r;
+        if (i >= a.nq)
+            continue;
+        const int64_t c = fused_c(a, s, i);
+        uint32_t *dst = a.samp + ((int64_t)s * a.nq + i) * a.ns;
+#pragma unroll
+        for (int n = 0; n < 4; ++n) {
+            const int m = m0 + n * 16 + col;
+            const int64_t j = (int64_t)m * stride;
+            if (m < a.ns)
+                dst[m] = j < c ? score_key(acc[n][r]) : 0u;  // 0: below every real key
+        }
+    }
+}
+
+// Number of sample keys of a row and the rank q whose key becomes T0.
+__device__ __forceinline__ void fused_rank(const FusedTopkArgs &a, int64_t c, int64_t stride,
+                                           int &ns_row, int &q)
+{
+    const int64_t n = (c + stride - 1) / stride;
+    ns_row = (int)(n < a.ns ? n : a.ns);
+    const int keep = a.k - 1;
+    if (stride == 1 && ns_row == c) {  // the sample is the whole row: T0 is the exact threshold
+        q = keep;
+        return;
+    }
+    const int64_t share = ((int64_t)keep * ns_row + c - 1) / c;  // expected kept samples, up
+    const int64_t qq = 2 * share + 16;
+    q = (int)(qq < ns_row ? qq : ns_row);
+}
+
+template <int KPL>  // sample keys per lane: ns / 64
+__global__ __launch_bounds__(256) void k_fused_threshold(FusedTopkArgs a)
+{
+    const int lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (row >= (int64_t)a.nseq * a.nq)
+        return;
+    const int s = (int)(row / a.nq), i = (int)(row - (int64_t)s * a.nq);
+    const int64_t c = fused_c(a, s, i);
+    if (c <= a.k - 1) {  // every past block is kept: list them all
+        if (lane == 0)
+            a.thr[row] = 0u;
+        return;
+    }
+    const int64_t stride = fused_stride(fused_c(a, s, i & ~(kTileQ - 1)), a.ns);
+    int ns_row, q;
+    fused_rank(a, c, stride, ns_row, q);
+    const uint32_t *src = a.samp + row * a.ns;
+    uint32_t key[KPL];
+#pragma unroll
+    for (int e = 0; e < KPL; ++e)
+        key[e] = src[e * 64 + lane];  // invalid samples hold 0 and never count
+    // the largest T with #{keys >= T} >= q, decided from the top bit down (the wave counts
+    // with one ballot per key slot)
+    uint32_t t = 0u;
+#pragma unroll 1
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = t | (1u << b);
+        int n = 0;
+#pragma unroll
+        for (int e = 0; e < KPL; ++e)
+            n += __popcll(__ballot(key[e] >= cand));
+        if (n >= q)
+            t = cand;
+    }
+    if (lane == 0)
+        a.thr[row] = t;
+}
+
+// A filter workgroup takes kFilterWaves * 16 queries x kFilterTiles tiles of 64 blocks.  The
+// keys a row keeps are staged in LDS, and each row then reserves its slots in the global list
+// with one atomic add per workgroup; a tile's keys that no longer fit a row's stage (rows that
+// keep most of their blocks) reserve and write their slots in the global list at once.  A
+// row's stage and its count are only touched by the 16 lanes that hold the row's keys.
+#ifndef SGQA_FILTER_WAVES
+#define SGQA_FILTER_WAVES 4
+#endif
+#ifndef SGQA_FILTER_TILES
+#define SGQA_FILTER_TILES 8
+#endif
+#ifndef SGQA_FILTER_STAGE
+#define SGQA_FILTER_STAGE 64
+#endif
+constexpr int kFilterWaves = SGQA_FILTER_WAVES;
+constexpr int kFilterTiles = SGQA_FILTER_TILES;
+constexpr int kStage = SGQA_FILTER_STAGE;
+constexpr int kFilterQ = 16 * kFilterWaves;  // query rows per workgroup
+constexpr int kFilterNT = 64 * kFilterWaves;
+
+template <int P>
+__global__ __launch_bounds__(kFilterNT) void k_fused_filter(FusedTopkArgs a)
+{
+    extern __shared__ __align__(16) uint16_t kb_tile[];  // [kTileB][P + 8], then the stage
+    constexpr int ldt = P + 8;
+    uint2 *stage = reinterpret_cast<uint2 *>(kb_tile + kTileB * ldt);  // [kFilterQ][kStage]
+    uint32_t *lcnt = reinterpret_cast<uint32_t *>(stage + kFilterQ * kStage);  // [kFilterQ]
+    uint32_t *gbase = lcnt + kFilterQ;                                         // [kFilterQ]
+    const int s = blockIdx.z;
+    const int i0 = blockIdx.x * kFilterQ;  // query tiles vary fastest: neighbouring workgroups
+                                           // share their kb tiles in L2, their counters differ
+    const int i_last = min(i0 + kFilterQ, a.nq) - 1;
+    const int64_t c_last = fused_c(a, s, i_last);
+    const int64_t jt0 = (int64_t)blockIdx.y * kFilterTiles * kTileB;
+    if (jt0 >= c_last)
+        return;
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    const uint16_t *kb = a.kb + (int64_t)s * a.kb_seq_stride;
+    if (tid < kFilterQ)
+        lcnt[tid] = 0u;
+    const bool wave_live = i0 + wave * 16 < a.nq;
+    const int qrow = i0 + wave * 16 + col;
+    const uint16_t *qp = a.qp + (int64_t)s * a.qp_seq_stride + (int64_t)(a.t0 + qrow) * P;
+    const uint16_t *qpr = qrow < a.nq ? qp : qp - (int64_t)(qrow - i0) * P;  // row i0 exists
+    u32x4 av[P / 32];
+#pragma unroll
+    for (int kk = 0; kk < P / 32; ++kk)
+        av[kk] = load16(qpr + kk * 32 + q4 * 8);
+    uint32_t thr[4];
+    int64_t cr[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        const int i = i0 + wave * 16 + q4 * 4 + r;
+        thr[r] = a.thr[(int64_t)s * a.nq + (i < a.nq ? i : i0)];
+        cr[r] = i < a.nq ? fused_c(a, s, i) : 0;
+    }
+    constexpr int chunks = P / 8;
+    constexpr int kPer = (kTileB * chunks + kFilterNT - 1) / kFilterNT;
+    // a tile's kb rows are requested while the previous tile is computed
+    u32x4 tv[kPer];
+    auto load_tile = [&](int64_t j0) {
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {  // unconditional loads (row j0 is always valid)
+            const int e = u * kFilterNT + tid;
+            const int r = e / chunks, cc = e - r * chunks;
+            const int64_t row = j0 + r < c_last && e < kTileB * chunks ? j0 + r : j0;
+            tv[u] = load16(kb + row * P + cc * 8);
+        }
+    };
+    load_tile(jt0);
+#pragma unroll 1
+    for (int tl = 0; tl < kFilterTiles; ++tl) {
+        const int64_t j0 = jt0 + (int64_t)tl * kTileB;
+        if (j0 >= c_last)
+            break;  // uniform over the workgroup
+        __syncthreads();  // the previous tile's operand reads are done
+#pragma unroll
+        for (int u = 0; u < kPer; ++u) {
+            const int e = u * kFilterNT + tid;
+            const int r = e / chunks, cc = e - r * chunks;
+            if (e < kTileB * chunks)
+                *reinterpret_cast<u32x4 *>(kb_tile + r * ldt + cc * 8) = tv[u];
+        }
+        __syncthreads();
+        if (tl + 1 < kFilterTiles && j0 + kTileB < c_last)
+            load_tile(j0 + kTileB);
+        if (!wave_live)
+            continue;
+        f32x4 acc[4];
+#pragma unroll
+        for (int n = 0; n < 4; ++n)
+            acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < P / 32; ++kk) {
+            const bf16x8 af = as_bf16x8(av[kk]);
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const u32x4 bv = *reinterpret_cast<const u32x4 *>(
+                    kb_tile + (n * 16 + col) * ldt + kk * 32 + q4 * 8);
+                acc[n] = mfma_16x16x32(af, as_bf16x8(bv), acc[n]);
+            }
+        }
+        // Lane (col, q4) holds the keys of rows 4 q4 + r at blocks j0 + 16 n + col: a row's
+        // keys of this tile sit in the 16 lanes of one q4, which count theirs, scan the counts,
+        // and reserve stage slots with one LDS atomic add (lane col 0).
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            const int rl = wave * 16 + q4 * 4 + r;  // row within the workgroup
+            uint32_t key[4];
+            int cnt = 0;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int64_t j = j0 + n * 16 + col;
+                key[n] = score_key(acc[n][r]);
+                cnt += (j < cr[r] && key[n] >= thr[r]) ? 1 : 0;
+            }
+            int inc = cnt;
+#pragma unroll
+            for (int o = 1; o < 16; o <<= 1) {
+                const int v = __shfl_up(inc, o, 16);
+                if (col >= o)
+                    inc += v;
+            }
+            const int tot = __shfl(inc, 15, 16);
+            if (tot == 0)
+                continue;  // uniform over the row's 16 lanes
+            const int local = (int)lcnt[rl];
+            const bool spill = local + tot > kStage;
+            int base = 0;
+            if (spill && col == 0)
+                base = (int)atomicAdd(&a.cnt[(int64_t)s * a.nq + i0 + rl], (uint32_t)tot);
+            base = spill ? __shfl(base, 0, 16) : local;
+            int slot = base + inc - cnt;
+            uint2 *list = a.cand + ((int64_t)s * a.nq + i0 + rl) * a.cap;
+#pragma unroll
+            for (int n = 0; n < 4; ++n) {
+                const int64_t j = j0 + n * 16 + col;
+                if (j < cr[r] && key[n] >= thr[r]) {
+                    if (!spill)
+                        stage[rl * kStage + slot] = uint2{key[n], (uint32_t)j};
+                    else if (slot < a.cap)
+                        list[slot] = uint2{key[n], (uint32_t)j};
+                    ++slot;
+                }
+            }
+            if (!spill && col == 0)
+                lcnt[rl] = (uint32_t)(local + tot);
+        }
+    }
+    __syncthreads();
+    // one reservation per row for its staged keys
+    if (tid < kFilterQ) {
+        const uint32_t n = lcnt[tid];
+        uint32_t b = 0u;
+        if (n > 0u && i0 + tid < a.nq)
+            b = atomicAdd(&a.cnt[(int64_t)s * a.nq + i0 + tid], n);
+        gbase[tid] = b;
+    }
+    __syncthreads();
+    for (int e = tid; e < kFilterQ * kStage; e += kFilterNT) {
+        const int rl = e / kStage, f = e - rl * kStage;
+        const uint32_t n = lcnt[rl];
+        if ((uint32_t)f < n && i0 + rl < a.nq) {
+            const uint32_t slot = gbase[rl] + (uint32_t)f;
+            if (slot < (uint32_t)a.cap)
+                a.cand[((int64_t)s * a.nq + i0 + rl) * a.cap + slot] = stage[e];
+        }
+    }
+}
+
+// Clear the pass's counters (a fill kernel, so a captured pass records no memset).
+__global__ __launch_bounds__(256) void k_fused_clear(FusedTopkArgs a)
+{
+    const int64_t n = (int64_t)a.nseq * a.nq;
+    for (int64_t e = (int64_t)blockIdx.x * 256 + threadIdx.x; e < n; e += (int64_t)gridDim.x * 256)
+        a.cnt[e] = 0u;
+    if (blockIdx.x == 0 && threadIdx.x < 2)
+        a.queue_ctr[threadIdx.x] = 0u;
+}
+
+template <int NT>
+__global__ __launch_bounds__(NT) void k_fused_select(FusedTopkArgs a)
+{
+    __shared__ __align__(16) SelectShared sh;
+    __shared__ __align__(16) uint32_t bitmap[kFusedBitmapWords];
+    __shared__ uint32_t cand_key[4096];
+    __shared__ int32_t cand_idx[4096];
+    __shared__ BinFind bf;
+    const int tid = threadIdx.x;
+    const int64_t row = blockIdx.x;
+    const int s = (int)(row / a.nq), i = (int)(row - (int64_t)s * a.nq);
+    const int64_t c = fused_c(a, s, i);
+    const int k = a.k, keep = k - 1;
+    int32_t *out = a.idx + ((int64_t)s * a.T + a.t0 + i) * k;
+    float *osc = a.sel_scores ? a.sel_scores + ((int64_t)s * a.T + a.t0 + i) * k : nullptr;
+    const int m = (int)a.cnt[row];
+    const uint2 *list = a.cand + row * a.cap;
+
+    if (c <= (int64_t)keep) {
+        // every past block and the own block are kept; the list holds all c past blocks
+        for (int e = tid; e < k; e += NT) {
+            out[e] = e <= c ? e : -1;
+            if (osc && e >= c)
+                osc[e] = e == c ? __builtin_inff() : -__builtin_inff();
+        }
+        if (osc)
+            for (int e = tid; e < m && e < a.cap; e += NT) {
+                const uint2 v = list[e];
+                osc[v.y] = key_score(v.x);
+            }
+        return;
+    }
+    if (m < keep || m > a.cap) {  // T0 missed: the fallback selects over every block
+        if (tid == 0)
+            a.queue[atomicAdd(&a.queue_ctr[0], 1u)] = (uint32_t)row;
+        return;
+    }
+    if (tid == 0) {
+        out[keep] = (int32_t)c;
+        if (osc)
+            osc[keep] = __builtin_inff();
+    }
+    for (int e = tid; e < m; e += NT) {
+        const uint2 v = list[e];
+        cand_key[e] = v.x;
+        cand_idx[e] = (int32_t)v.y;
+    }
+    const int nwords = (int)((c + 31) / 32);
+    for (int w = tid; w < nwords; w += NT)
+        bitmap[w] = 0u;
+    __syncthreads();
+    // exact selection of `keep` of the m listed keys: radix passes below the bits all taken
+    int need = keep, cnt = m;
+    uint32_t Pf = 0u, pmask = 0u;
+    uint32_t *hist = sh.hist;
+    const int shifts[3] = {20, 8, 0};
+    const uint32_t dmasks[3] = {0xfffu, 0xfffu, 0xffu};
+#pragma unroll 1
+    for (int pass = 0; pass < 3 && need != cnt; ++pass) {
+        const int shift = shifts[pass];
+        const uint32_t dmask = dmasks[pass];
+        for (int b = tid; b < 4096; b += NT)
+            hist[b] = 0u;
+        __syncthreads();
+        for (int e = tid; e < m; e += NT)
+            if ((cand_key[e] & pmask) == Pf)
+                atomicAdd(&hist[(cand_key[e] >> shift) & dmask], 1u);
+        __syncthreads();
+        const BinFind rb = find_bin_n<NT>(hist, need, sh.scan, bf);
+        Pf |= rb.digit << shift;
+        pmask |= dmask << shift;
+        need = rb.need;
+        cnt = rb.cnt;
+    }
+    // take: keys above the prefix; at the prefix all of them when the count matches, else
+    // (exact ties of the full key) the `need` lowest blocks.  The flags are kept in registers
+    // until every thread has ranked its ties against the unmodified list.
+    constexpr int kPerThread = 4096 / NT;
+    bool taken[kPerThread];
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        const int e = tid + u * NT;
+        taken[u] = false;
+        if (e >= m)
+            continue;
+        const uint32_t key = cand_key[e];
+        const int j = cand_idx[e];
+        const uint32_t km = key & pmask;
+        bool take = km > Pf;
+        if (km == Pf) {
+            if (need == cnt) {
+                take = true;
+            } else {
+                int rank = 0;
+                for (int f = 0; f < m; ++f)
+                    rank += (cand_key[f] == key && cand_idx[f] < j) ? 1 : 0;
+                take = rank < need;
+            }
+        }
+        if (take)
+            atomicOr(&bitmap[j >> 5], 1u << (j & 31));
+        taken[u] = take;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int u = 0; u < kPerThread; ++u) {
+        const int e = tid + u * NT;
+        if (e < m && !taken[u])
+            cand_idx[e] = -1;
+    }
+    // output positions: exclusive prefix of the bitmap popcounts per word, then each taken
+    // candidate writes itself at its rank among the set bits
+    uint32_t *wpre = hist;  // kFusedBitmapWords == 4096 words
+    constexpr int kWpt = kFusedBitmapWords / NT;
+    int cntw = 0;
+#pragma unroll
+    for (int qq = 0; qq < kWpt; ++qq) {
+        const int w = tid * kWpt + qq;
+        cntw += w < nwords ? __popc(bitmap[w]) : 0;
+    }
+    int total;
+    int before = block_exclusive_scan<NT>(cntw, sh.scan, total);
+#pragma unroll
+    for (int qq = 0; qq < kWpt; ++qq) {
+        const int w = tid * kWpt + qq;
+        wpre[w] = (uint32_t)before;
+        before += w < nwords ? __popc(bitmap[w]) : 0;
+    }
+    __syncthreads();
+    for (int e = tid; e < m; e += NT) {
+        const int j = cand_idx[e];
+        if (j >= 0) {
+            const int w = j >> 5;
+            const int p = (int)wpre[w] + __popc(bitmap[w] & ((1u << (j & 31)) - 1u));
+            if (p < keep) {  // exactly `keep` bits are set
+                out[p] = j;
+                if (osc)
+                    osc[p] = key_score(cand_key[e]);
+            }
+        }
+    }
+}
+
+// k_fused_select for passes of at most 32768 candidates per row (list capacity 2048): one wave
+// per row and no workgroup barriers.  The (k-1)-th largest listed key K is found bit by bit
+// from the top, counting the keys at or above each candidate value with ballots; if fewer keys
+// equal K are taken than are listed, the taken ones are those up to the right block, found the
+// same way over the blocks of the tied keys.  The taken blocks are marked in the wave's LDS
+// bitmap, whose per-word prefix counts (a wave scan) give every taken block its position.
+constexpr int kWselCap = 2048;
+constexpr int kWselWords = 1024;  // bitmap words per wave: 32768 candidates
+
+__global__ __launch_bounds__(256) void k_fused_select_wave(FusedTopkArgs a)
+{
+    __shared__ uint32_t bitmap_all[4][kWselWords];
+    __shared__ uint32_t wpre_all[4][kWselWords];
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+    if (row >= (int64_t)a.nseq * a.nq)
+        return;  // waves never synchronise with each other
+    const int s = (int)(row / a.nq), i = (int)(row - (int64_t)s * a.nq);
+    const int64_t c = fused_c(a, s, i);
+    const int k = a.k, keep = k - 1;
+    int32_t *out = a.idx + ((int64_t)s * a.T + a.t0 + i) * k;
+    float *osc = a.sel_scores ? a.sel_scores + ((int64_t)s * a.T + a.t0 + i) * k : nullptr;
+    const int m = (int)a.cnt[row];
+    const uint2 *list = a.cand + row * a.cap;
+
+    if (c <= (int64_t)keep) {
+        // every past block and the own block are kept; the list holds all c past blocks
+        for (int e = lane; e < k; e += 64) {
+            out[e] = e <= c ? e : -1;
+            if (osc && e >= c)
+                osc[e] = e == c ? __builtin_inff() : -__builtin_inff();
+        }
+        if (osc)
+            for (int e = lane; e < m && e < a.cap; e += 64) {
+                const uint2 v = list[e];
+                osc[v.y] = key_score(v.x);
+            }
+        return;
+    }
+    if (m < keep || m > a.cap) {  // T0 missed: the fallback selects over every block
+        if (lane == 0)
+            a.queue[atomicAdd(&a.queue_ctr[0], 1u)] = (uint32_t)row;
+        return;
+    }
+    constexpr int U = kWselCap / 64;
+    uint32_t kr[U];
+    int32_t jr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const int e = lane + 64 * u;
+        const uint2 v = list[e < m ? e : 0];
+        kr[u] = e < m ? v.x : 0u;  // 0 lies below every listed key
+        jr[u] = e < m ? (int32_t)v.y : -1;
+    }
+    // K: the largest value with at least `keep` listed keys at or above it
+    uint32_t K = 0u;
+#pragma unroll 1
+    for (int b = 31; b >= 0; --b) {
+        const uint32_t cand = K | (1u << b);
+        int n = 0;
+#pragma unroll
+        for (int u = 0; u < U; ++u)
+            n += __popcll(__ballot(kr[u] >= cand));
+        if (n >= keep)
+            K = cand;
+    }
+    int n_gt = 0, n_eq = 0;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        n_gt += __popcll(__ballot(kr[u] > K));
+        n_eq += __popcll(__ballot(kr[u] == K));
+    }
+    const int take_eq = keep - n_gt;  // 1 .. n_eq
+    int32_t jmax = 0x7fffffff;         // tied keys are taken up to this block
+    if (take_eq < n_eq) {
+        // the largest J with fewer than take_eq tied keys at blocks below J is the block of
+        // the take_eq-th tied key in block order
+        int32_t J = 0;
+#pragma unroll 1
+        for (int b = 17; b >= 0; --b) {
+            const int32_t cand = J | (1 << b);
+            int n = 0;
+#pragma unroll
+            for (int u = 0; u < U; ++u)
+                n += __popcll(__ballot(kr[u] == K && jr[u] < cand));
+            if (n < take_eq)
+                J = cand;
+        }
+        jmax = J;
+    }
+    uint32_t *bitmap = bitmap_all[wave];
+    uint32_t *wpre = wpre_all[wave];
+    const int nwords = (int)((c + 31) / 32);
+    for (int w = lane; w < nwords; w += 64)
+        bitmap[w] = 0u;
+    wave_lds_handoff();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const bool take = kr[u] > K || (kr[u] == K && jr[u] <= jmax);
+        if (take)
+            atomicOr(&bitmap[jr[u] >> 5], 1u << (jr[u] & 31));
+    }
+    wave_lds_handoff();
+    constexpr int kWpl = kWselWords / 64;  // bitmap words per lane
+    uint32_t wv[kWpl];
+    int cntw = 0;
+#pragma unroll
+    for (int q = 0; q < kWpl; ++q) {
+        const int w = lane * kWpl + q;
+        wv[q] = w < nwords ? bitmap[w] : 0u;
+        cntw += __popc(wv[q]);
+    }
+    int before = wave_inclusive_scan(cntw) - cntw;
+#pragma unroll
+    for (int q = 0; q < kWpl; ++q) {
+        wpre[lane * kWpl + q] = (uint32_t)before;
+        before += __popc(wv[q]);
+    }
+    wave_lds_handoff();
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+        const bool take = kr[u] > K || (kr[u] == K && jr[u] <= jmax);
+        if (take) {
+            const int j = jr[u], w = j >> 5;
+            const int p = (int)wpre[w] + __popc(bitmap[w] & ((1u << (j & 31)) - 1u));
+            if (p < keep) {  // exactly `keep` bits are set
+                out[p] = j;
+                if (osc)
+                    osc[p] = key_score(kr[u]);
+            }
+        }
+    }
+    if (lane == 0) {
+        out[keep] = (int32_t)c;
+        if (osc)
+            osc[keep] = __builtin_inff();
+    }
+}
+
+// The queued rows: each workgroup scores one row's blocks into its scratch row with the
+// filter's matrix-core arithmetic (the query proxy broadcast to all 16 A rows, so one
+// product gives 16 blocks), then selects exactly over the row.  Workgroups loop until the
+// queue, complete before this launch, is empty.
+template <int P, int NT>
+__global__ __launch_bounds__(NT) void k_fused_fallback(FusedTopkArgs a)
+{
+    __shared__ SelectShared sh;
+    __shared__ int cur;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    float *sc = a.fb_scores + (int64_t)blockIdx.x * a.fb_ld;
+    const int nq_total = (int)a.queue_ctr[0];
+#pragma unroll 1
+    for (;;) {
+        if (tid == 0)
+            cur = (int)atomicAdd(&a.queue_ctr[1], 1u);
+        __syncthreads();
+        const int qi = cur;
+        __syncthreads();
+        if (qi >= nq_total)
+            break;
+        const int64_t row = a.queue[qi];
+        const int s = (int)(row / a.nq), i = (int)(row - (int64_t)s * a.nq);
+        const int64_t c = fused_c(a, s, i);
+        const int k = a.k, keep = k - 1;
+        const uint16_t *qp = a.qp + (int64_t)s * a.qp_seq_stride + (int64_t)(a.t0 + i) * P;
+        const uint16_t *kb = a.kb + (int64_t)s * a.kb_seq_stride;
+        bf16x8 af[P / 32];
+#pragma unroll
+        for (int kk = 0; kk < P / 32; ++kk)
+            af[kk] = as_bf16x8(load16(qp + kk * 32 + q4 * 8));
+        for (int64_t jb = (int64_t)wave * 16; jb < c; jb += (NT / 64) * 16) {
+            const int64_t j = jb + col < c ? jb + col : jb;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < P / 32; ++kk)
+                acc = mfma_16x16x32(af[kk], as_bf16x8(load16(kb + j * P + kk * 32 + q4 * 8)),
+                                    acc);
+            if (q4 == 0 && jb + col < c)
+                sc[jb + col] = acc[0];
+        }
+        __syncthreads();
+        int32_t *out = a.idx + ((int64_t)s * a.T + a.t0 + i) * k;
+        float *osc = a.sel_scores ? a.sel_scores + ((int64_t)s * a.T + a.t0 + i) * k : nullptr;
+        auto key_at = [&](int j) { return score_key(sc[j]); };
+        const KthKey th = radix_select<NT>(key_at, (int)c, keep, sh);
+        emit_selected<NT>(key_at, (int)c, th, keep, sh, [&](int pos, int j, uint32_t key) {
+            out[pos] = j;
+            if (osc)
+                osc[pos] = key_score(key);
+        });
+        if (tid == 0) {
+            out[keep] = (int32_t)c;
+            if (osc)
+                osc[keep] = __builtin_inff();
+        }
+        __syncthreads();
+    }
+}
+
+bool fused_topk_supported(int64_t max_cand, int k, int P)
+{
+    return max_cand <= kFusedMaxCand && k >= 2 && k <= kFusedMaxK &&
+           (P == 32 || P == 64 || P == 128 || P == 256 || P == 512);
+}
+
+void fused_topk_geometry(int64_t max_cand, int &ns, int &cap)
+{
+    ns = fused_ns(max_cand);
+    cap = fused_cap(max_cand);
+}
+
+size_t fused_topk_row_bytes(int64_t max_cand)
+{
+    // sample keys, threshold, count, queue slot, candidate list
+    return (size_t)fused_ns(max_cand) * 4 + 12 + (size_t)fused_cap(max_cand) * 8;
+}
+
+size_t fused_topk_fixed_bytes(int64_t max_cand)
+{
+    const int64_t ld = (max_cand + 63) / 64 * 64;
+    return 256 + (size_t)kFusedFallbackWGs * ld * 4;
+}
+
+template <int P>
+static void launch_fused_p(const FusedTopkArgs &a, hipStream_t stream)
+{
+    const unsigned qt = (unsigned)((a.nq + kTileQ - 1) / kTileQ);
+    const size_t lds = (size_t)kTileB * (P + 8) * sizeof(uint16_t);
+    const int64_t rows = (int64_t)a.nseq * a.nq;
+    hipLaunchKernelGGL(k_fused_clear, dim3((unsigned)((rows + 255) / 256 < 1024 ? (rows + 255) / 256 : 1024)),
+                       dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_fused_sample<P>, dim3((unsigned)(a.ns / kTileB), qt, (unsigned)a.nseq),
+                       dim3(256), lds, stream, a);
+    if (a.ns == 1024)
+        hipLaunchKernelGGL(k_fused_threshold<16>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL(k_fused_threshold<64>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                           stream, a);
+    const int64_t span = (int64_t)kFilterTiles * kTileB;
+    const size_t lds_f = lds + (size_t)kFilterQ * kStage * 8 + 2 * kFilterQ * 4;
+    hipLaunchKernelGGL(k_fused_filter<P>,
+                       dim3((unsigned)((a.nq + kFilterQ - 1) / kFilterQ),
+                            (unsigned)((a.max_cand + span - 1) / span), (unsigned)a.nseq),
+                       dim3(kFilterNT), lds_f, stream, a);
+    if (a.cap == kWselCap && a.max_cand <= 32 * (int64_t)kWselWords)
+        hipLaunchKernelGGL(k_fused_select_wave, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
+                           stream, a);
+    else
+        hipLaunchKernelGGL(k_fused_select<512>, dim3((unsigned)rows), dim3(512), 0, stream, a);
+    const unsigned nfb = (unsigned)(rows < kFusedFallbackWGs ? rows : kFusedFallbackWGs);
+    hipLaunchKernelGGL((k_fused_fallback<P, 512>), dim3(nfb), dim3(512), 0, stream, a);
+}
+
+hipError_t launch_fused_topk(const FusedTopkArgs &a, hipStream_t stream)
+{
+    if ((int64_t)a.nseq * a.nq == 0)
+        return hipSuccess;
+    if (a.max_cand > kFusedMaxCand || a.fb_ld < a.max_cand)
+        return hipErrorInvalidValue;  // the select's bitmap and the scratch rows hold max_cand
+    switch (a.P) {
+    case 32: launch_fused_p<32>(a, stream); break;
+    case 64: launch_fused_p<64>(a, stream); break;
+    case 128: launch_fused_p<128>(a, stream); break;
+    case 256: launch_fused_p<256>(a, stream); break;
+    case 512: launch_fused_p<512>(a, stream); break;
+    default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
 }
 
 bool decode_topk_supported(int64_t max_cand, int k)

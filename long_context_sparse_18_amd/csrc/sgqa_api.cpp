@@ -147,6 +147,11 @@ constexpr size_t kIndexerWorkspaceCap = size_t(2) << 30;
 #ifndef SGQA_SLICE_HALF_K
 #define SGQA_SLICE_HALF_K 4
 #endif
+#ifndef SGQA_LONG_SLICES
+#define SGQA_LONG_SLICES 1
+#endif
+// History ranges of a row whose history is longer than 16 slices of the above.
+constexpr int kPrefillLongSlices = SGQA_LONG_SLICES;
 // Blocks per history slice of the sliced prefill attention, in units of k/2 (2k: 1024 blocks
 // at the real shape).
 constexpr int64_t kPrefillSliceHalfK = SGQA_SLICE_HALF_K;
@@ -236,7 +241,19 @@ size_t sgqa_workspace_bytes(int op, const sgqa_dims *dims, int32_t nseq, int32_t
             bytes = per_q * min_rows;
         if (T == 1 && sgqa::decode_topk_supported(max_cand, dims->topk_blocks)) {
             const int64_t dec = (int64_t)sgqa::decode_topk_workspace(nseq, max_cand);
-            bytes = dec > bytes ? dec : bytes;
+            return (size_t)(dec > bytes ? dec : bytes);
+        }
+        if (max_cand >= 1 &&
+            sgqa::fused_topk_supported(max_cand, dims->topk_blocks, dims->proxy_dim)) {
+            const int64_t row = (int64_t)sgqa::fused_topk_row_bytes(max_cand) * nseq;
+            const int64_t fixed = (int64_t)sgqa::fused_topk_fixed_bytes(max_cand);
+            int64_t rows = T > 0 ? T : 1;
+            if (fixed + rows * row > (int64_t)kIndexerWorkspaceCap)
+                rows = ((int64_t)kIndexerWorkspaceCap - fixed) / row / 64 * 64;
+            if (rows < min_rows)
+                rows = min_rows;
+            const int64_t fused = fixed + rows * row;
+            bytes = fused > bytes ? fused : bytes;
         }
         return (size_t)bytes;
     }
@@ -406,11 +423,8 @@ sgqa_status sgqa_indexer_topk(const sgqa_dims *dims, const sgqa_bf16 *qp, int64_
     if (nseq > 1 && kb_seq_stride % 8 != 0)
         return fail(SGQA_ERR_SHAPE, "kb_seq_stride must be a multiple of 8");
     const TopkPlan plan = topk_plan(dims, q_start, nseq, T, workspace ? workspace_bytes : 0);
-    if (!workspace || plan.nq <= 0)
-        return fail(SGQA_ERR_WORKSPACE,
-                    "workspace of %zu bytes cannot hold one pass (need >= %lld bytes)",
-                    workspace ? workspace_bytes : (size_t)0,
-                    (long long)(plan.ld * 4 * nseq * (T < 64 ? T : 64)));
+    if (!workspace)
+        return fail(SGQA_ERR_WORKSPACE, "workspace is NULL");
     if (!aligned(workspace, 16))
         return fail(SGQA_ERR_SHAPE, "workspace must be 16-byte aligned");
 
@@ -440,6 +454,66 @@ sgqa_status sgqa_indexer_topk(const sgqa_dims *dims, const sgqa_bf16 *qp, int64_
         return hip_status(sgqa::launch_decode_topk(da, hs), "decode top-k launch");
     }
 
+    // Rows of at most 131072 candidates: scores are filtered against a sampled threshold as
+    // they are computed, so no score matrix is stored (k_fused_*).
+    const int k = dims->topk_blocks;
+    if (plan.max_cand >= 1 && sgqa::fused_topk_supported(plan.max_cand, k, P)) {
+        const size_t fixed = sgqa::fused_topk_fixed_bytes(plan.max_cand);
+        const size_t row = sgqa::fused_topk_row_bytes(plan.max_cand) * (size_t)nseq;
+        int64_t nq = workspace_bytes > fixed ? (int64_t)((workspace_bytes - fixed) / row) : 0;
+        if (nq >= T)
+            nq = T;
+        else
+            nq = nq / 64 * 64;
+        if (nq > 0) {
+            sgqa::FusedTopkArgs fa{};
+            fa.qp = qp;
+            fa.qp_seq_stride = qp_seq_stride;
+            fa.kb = kb;
+            fa.kb_seq_stride = kb_seq_stride;
+            for (int s = 0; s < nseq; ++s)
+                fa.q_start.v[s] = q_start[s];
+            fa.nseq = nseq;
+            fa.T = T;
+            fa.P = P;
+            fa.B = dims->block_size;
+            fa.k = k;
+            sgqa::fused_topk_geometry(plan.max_cand, fa.ns, fa.cap);
+            fa.fb_ld = round_up(plan.max_cand, 64);
+            char *w = static_cast<char *>(workspace);
+            fa.queue_ctr = reinterpret_cast<uint32_t *>(w);
+            fa.fb_scores = reinterpret_cast<float *>(w + 256);
+            char *rows0 = w + fixed;
+            const int64_t nrows = nq * nseq;
+            fa.cand = reinterpret_cast<uint2 *>(rows0);
+            fa.samp = reinterpret_cast<uint32_t *>(rows0 + (size_t)nrows * fa.cap * 8);
+            fa.thr = fa.samp + (size_t)nrows * fa.ns;
+            fa.cnt = fa.thr + nrows;
+            fa.queue = fa.cnt + nrows;
+            fa.idx = idx;
+            fa.sel_scores = sel_scores;
+            for (int32_t t0 = 0; t0 < T; t0 += (int32_t)nq) {
+                const int32_t n = (T - t0) < nq ? (T - t0) : (int32_t)nq;
+                int64_t max_pos = 0;
+                for (int s = 0; s < nseq; ++s)
+                    max_pos = q_start[s] + t0 + n - 1 > max_pos ? q_start[s] + t0 + n - 1 : max_pos;
+                fa.t0 = t0;
+                fa.nq = n;
+                fa.max_cand = max_pos / dims->block_size;
+                if (fa.max_cand < 1)
+                    fa.max_cand = 1;
+                hipError_t e = sgqa::launch_fused_topk(fa, hs);
+                if (e != hipSuccess)
+                    return hip_status(e, "fused top-k launch");
+            }
+            return ok();
+        }
+    }
+
+    if (plan.nq <= 0)
+        return fail(SGQA_ERR_WORKSPACE,
+                    "workspace of %zu bytes cannot hold one pass (need >= %lld bytes)",
+                    workspace_bytes, (long long)(plan.ld * 4 * nseq * (T < 64 ? T : 64)));
     sgqa::ScoreArgs sa{};
     sa.qp = qp;
     sa.qp_seq_stride = qp_seq_stride;
@@ -533,10 +607,13 @@ sgqa_status sgqa_sparse_attn_prefill(const sgqa_dims *dims, const sgqa_bf16 *q,
         // one such range of the cache, which each XCD's L2 holds for its KV group, while every
         // slice boundary a row crosses parks ~13 KB of state per group.  Short histories gain
         // nothing and stay in one pass (row by row: the kernel attends rows with c < 2k in one
-        // pass even in a sliced launch).
+        // pass even in a sliced launch), and so do histories longer than 16 ranges (chunked
+        // prefill at 1M tokens: ~4 entries per range, 13.9 ms unsliced against 14.0/14.5/15.2 ms
+        // with 4/8/16 ranges of the row's own length).
         const int64_t max_cand = (q_start + T - 1) / dims->block_size;
         const int64_t W = (kPrefillSliceHalfK * dims->topk_blocks + 1) / 2;
         a.slice_blocks = max_cand >= 2 * (int64_t)dims->topk_blocks ? W : 0;
+        a.long_slices = kPrefillLongSlices;
         a.state = static_cast<float *>(workspace);
         a.state_bytes = (int64_t)workspace_bytes;
         a.state_stride = sgqa::prefill_state_stride(a.d);

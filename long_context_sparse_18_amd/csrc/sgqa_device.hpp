@@ -101,6 +101,15 @@ __device__ __forceinline__ float sum_across_rows(float v)
     return v;
 }
 
+// Orders the LDS accesses of one wave around a hand-off between its lanes (LDS operations of a
+// wave execute in issue order; the fences keep the compiler from moving accesses across).
+__device__ __forceinline__ void wave_lds_handoff()
+{
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
 // Inclusive prefix sum of an int across a 64-lane wave.
 __device__ __forceinline__ int wave_inclusive_scan(int v)
 {

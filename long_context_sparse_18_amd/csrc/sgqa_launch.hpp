@@ -2,6 +2,7 @@
 #pragma once
 
 #include <hip/hip_runtime_api.h>
+#include <hip/hip_vector_types.h>
 #include <stdint.h>
 
 namespace sgqa {
@@ -72,6 +73,32 @@ struct SelectArgs {
 };
 hipError_t launch_select(const SelectArgs &a, hipStream_t stream);
 
+// Prefill top-k without a score matrix (k_fused_* in k_indexer.hip), for the queries
+// [t0, t0+nq) of every sequence; row r = s*nq + i.  Workspace arrays per pass:
+// samp [rows][ns] u32, thr / cnt / queue [rows] u32, cand [rows][cap] (key, block),
+// queue_ctr [2] u32 (queued rows, rows taken), fb_scores [kFusedFallbackWGs][fb_ld] fp32.
+struct FusedTopkArgs {
+    const uint16_t *qp;
+    int64_t qp_seq_stride;
+    const uint16_t *kb;
+    int64_t kb_seq_stride;
+    SeqPositions q_start;
+    int32_t nseq, t0, nq, T, P, B, k;
+    int64_t max_cand;  // largest candidate count over the rows of this pass
+    int32_t ns, cap;
+    uint32_t *samp, *thr, *cnt, *queue, *queue_ctr;
+    uint2 *cand;
+    float *fb_scores;
+    int64_t fb_ld;
+    int32_t *idx;
+    float *sel_scores;
+};
+bool fused_topk_supported(int64_t max_cand, int k, int P);
+void fused_topk_geometry(int64_t max_cand, int &ns, int &cap);
+size_t fused_topk_row_bytes(int64_t max_cand);    // per query row of a pass
+size_t fused_topk_fixed_bytes(int64_t max_cand);  // counters and fallback scratch rows
+hipError_t launch_fused_topk(const FusedTopkArgs &a, hipStream_t stream);
+
 // Decode-shaped top-k (one query per sequence): score keys for every block, then one
 // selection workgroup per sequence.  The workspace holds keys [nseq][keys_ld] and unit
 // maxima [nseq][units_ld] (u32).
@@ -129,6 +156,7 @@ struct AttnArgs {
     // slice_blocks of every row (0: one pass), parking the per-lane softmax state
     // (state_stride floats per lane) in `state` between launches
     int64_t slice_blocks;
+    int32_t long_slices;     // ranges of a history longer than 16 slice_blocks ranges
     int32_t slice;
     float *state;
     int64_t state_bytes;

@@ -46,6 +46,15 @@ def test_prefill_32k():
     assert st["exact_iso"] >= st["rows"] - 2
 
 
+def test_prefill_32k_topk_paths_agree():
+    """32K prefill: the top-k without a score matrix against the score-matrix path, every row."""
+    wl = WORKLOADS[1]
+    s = wl.shape
+    d = inputs.make_prefill(wl, 1, DEV)
+    res = run_prefill(s, d, wl.q_start, wl.L)
+    _same_as_score_matrix_path(s, d["qp"], res["kb"], wl.q_start, res)
+
+
 def test_prefill_128k():
     st = _prefill_case(2, 64, 2, sliced=True)
     assert st["exact_iso"] >= st["rows"] - 2
@@ -106,6 +115,25 @@ def test_chunked_prefill_1m():
     st = check_prefill_rows(shape, d, res, wl.q_start, rows, kb_ref=kb_ref)
     say(f"config 4: {st} {st_kb}")
     assert st["exact_iso"] >= st["rows"] - 2
+    _same_as_score_matrix_path(shape, d["qp"], kb, wl.q_start, res)
+
+
+def _same_as_score_matrix_path(shape, qp, kb, q_start, res):
+    """The selection without a score matrix (sampled threshold, listed candidates) equals the
+    one from the stored score rows bit for bit, scores included: a workspace too small for the
+    former's 64-row pass makes the call take the latter."""
+    T = qp.shape[0]
+    max_cand = (q_start + T - 1) // shape.block_size
+    ld = -(-max_cand // 64) * 64
+    # 64 score rows and no room for the other path's fallback rows and counters
+    ws = torch.empty(ld * 4 * 64 + 128, dtype=torch.uint8, device=DEV)
+    idx = torch.full_like(res["idx"], -7)
+    sel = torch.empty_like(res["sel"])
+    sgqa.indexer_topk(shape, qp, kb, [q_start], idx, sel, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, res["idx"]), "selections differ between the two paths"
+    assert torch.equal(sel.view(torch.int32), res["sel"].view(torch.int32)), "scores differ"
+    say(f"score-matrix path: same {T} selections and scores")
 
 
 def test_decode_1m_batch16():
