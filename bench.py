@@ -728,6 +728,8 @@ def main():
                     help="skip the measured MFMA / HBM-read peak probes")
     ap.add_argument("--copy-probe", action="store_true",
                     help="run only a plain 1 GiB device copy (calibrates HBM byte counters)")
+    ap.add_argument("--mfma-probe", action="store_true",
+                    help="run only the dense bf16 MFMA loop (calibrates the MFMA counters)")
     args = ap.parse_args()
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) > 1:
         print("bench.py measures one GPU: this layer is not sharded across GPUs here "
@@ -751,6 +753,15 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("copy probe: 3 copies of 1 GiB")
+        return
+    if args.mfma_probe:
+        cus = torch.cuda.get_device_properties(0).multi_processor_count
+        waves, iters = cus * 4 * 8, 4096
+        sink = torch.empty(waves, dtype=torch.float32, device="cuda")
+        for _ in range(3):
+            sgqa.probe_mfma_bf16(sink, iters)
+        torch.cuda.synchronize()
+        log(f"mfma probe: 3 x {waves} waves x {iters} x 8 bf16 32x32x16 products")
         return
     if args.no_prefill:
         dec = bench_decode(max(args.steps, 5), args.warmup)
