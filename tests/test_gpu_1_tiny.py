@@ -340,6 +340,48 @@ def test_prefill_topk_exact_ties(q0):
 
 
 @pytest.mark.gpu
+def test_prefill_topk_every_row_falls_back():
+    """Every row's list overflows (all scores tie: zero query proxies), so all 300 rows are
+    queued and the 64 persistent fallback workgroups each take several of them: the result is
+    the lowest k-1 blocks plus the own block, with their scores, as the oracle has it."""
+    k, T, q0 = 512, 300, 30000
+    shape = with_selection(WL.shape, 8, k)
+    nblk = -(-(q0 + T) // 8)
+    kb = _integer_index(shape, 1, nblk, 5)[0].to(DEV)
+    qp = torch.zeros((T, shape.proxy_dim), dtype=torch.bfloat16, device=DEV)
+    idx = torch.empty((T, k), dtype=torch.int32, device=DEV)
+    sel = torch.empty((T, k), dtype=torch.float32, device=DEV)
+    sgqa.indexer_topk(shape, qp, kb, [q0], idx, sel)
+    torch.cuda.synchronize()
+    t = np.arange(q0, q0 + T)
+    sc = oracle.scores(bits(qp), t, 8, parity.widen(bits(kb)), width=int(t.max()) // 8)
+    ref = oracle.topk(sc, t, 8, k)
+    assert np.array_equal(idx.cpu().numpy(), ref)
+    got = sel.cpu().numpy()
+    assert np.all(got[:, : k - 1] == 0.0) and np.all(np.isinf(got[:, k - 1]))
+
+
+def test_prefill_topk_several_passes_same_bits(tiny):
+    """A workspace that holds exactly one 64-row pass of the selection without a score matrix
+    (the layer's 1024 rows in 16 passes) gives the bits of the one-pass call, scores included."""
+    shape = with_selection(WL.shape, 8, 16)
+    kb = torch.empty((WL.nblk, shape.proxy_dim), dtype=torch.bfloat16, device=DEV)
+    sgqa.index_build(shape, tiny["kp"], kb, [WL.L])
+    full_idx = torch.empty((WL.T, 16), dtype=torch.int32, device=DEV)
+    full_sel = torch.empty((WL.T, 16), dtype=torch.float32, device=DEV)
+    sgqa.indexer_topk(shape, tiny["qp"], kb, [0], full_idx, full_sel)
+    # fixed part: 256 B of counters + 64 fallback rows of ld = 128 floats; per row: 1024
+    # sample keys, threshold, count, queue slot, 2048 listed (key, block) pairs
+    ws = torch.empty(256 + 64 * 128 * 4 + 64 * (1024 * 4 + 12 + 2048 * 8), dtype=torch.uint8,
+                     device=DEV)
+    idx = torch.full_like(full_idx, -7)
+    sel = torch.empty_like(full_sel)
+    sgqa.indexer_topk(shape, tiny["qp"], kb, [0], idx, sel, workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, full_idx)
+    assert torch.equal(sel.view(torch.int32), full_sel.view(torch.int32))
+
+
 def test_prefill_topk_sample_bound_too_high():
     """Prefill top-k when the sampled lower bound of the threshold overshoots: only every 16th
     block scores above -1 (exactly the blocks a 1024-key sample of a ~16 000-block row reads,
