@@ -1060,11 +1060,12 @@ __global__ __launch_bounds__(NT) void k_select2(SelectArgs a)
 //     workgroup on the matrix cores as in k_scores; each key >= T0 of a row is appended as
 //     (key, block) to that row's list (the 16 lanes holding a row's keys of a tile reserve their
 //     slots with one atomic add; the count keeps counting past the list's capacity);
-//  4. k_fused_select<NT>: one workgroup per row selects the k-1 largest listed keys exactly
-//     (radix passes over the list in LDS; exact ties of the full key go to the lowest block)
-//     and writes them in block order from per-word prefix counts of an LDS bitmap.  A row
-//     whose list holds fewer than k-1 keys (T0 above the row's threshold) or overflowed is
-//     queued instead;
+//  4. k_fused_select_wave (rows of up to 32768 candidates; one wave per row, bit by bit with
+//     ballot counts) or k_fused_select<NT> (longer rows; one workgroup per row, radix passes
+//     over the list in LDS) selects the k-1 largest listed keys exactly (exact ties of the
+//     full key go to the lowest block) and writes them in block order from per-word prefix
+//     counts of an LDS bitmap.  A row whose list holds fewer than k-1 keys (T0 above the
+//     row's threshold) or overflowed is queued instead;
 //  5. k_fused_fallback<NT>: a few persistent workgroups take the queued rows one at a time,
 //     score every candidate block of the row into their own scratch row with the same
 //     matrix-core arithmetic (so the same fp32 scores), and select exactly over it.
@@ -1550,21 +1551,20 @@ __global__ __launch_bounds__(NT) void k_fused_select(FusedTopkArgs a)
     }
 }
 
-// k_fused_select for passes of at most 32768 candidates per row (list capacity 2048): one wave
-// per row and no workgroup barriers.  The (k-1)-th largest listed key K is found bit by bit
-// from the top, counting the keys at or above each candidate value with ballots; if fewer keys
-// equal K are taken than are listed, the taken ones are those up to the right block, found the
-// same way over the blocks of the tied keys.  The taken blocks are marked in the wave's LDS
-// bitmap, whose per-word prefix counts (a wave scan) give every taken block its position.
-constexpr int kWselCap = 2048;
-constexpr int kWselWords = 1024;  // bitmap words per wave: 32768 candidates
-
-__global__ __launch_bounds__(256) void k_fused_select_wave(FusedTopkArgs a)
+// The selection of a pass, one wave per row and no workgroup barriers: CAP listed keys per row
+// at most (CAP / 64 per lane in registers), candidates below WORDS * 32, NW rows (waves) per
+// workgroup.  The (k-1)-th largest listed key K is found bit by bit from the top, counting the
+// keys at or above each candidate value with ballots; if fewer keys equal K are taken than are
+// listed, the taken ones are those up to the right block, found the same way over the blocks of
+// the tied keys.  The taken blocks are marked in the wave's LDS bitmap, whose per-word prefix
+// counts (a wave scan) give every taken block its output position.
+template <int CAP, int WORDS, int NW>
+__global__ __launch_bounds__(64 * NW) void k_fused_select_wave(FusedTopkArgs a)
 {
-    __shared__ uint32_t bitmap_all[4][kWselWords];
-    __shared__ uint32_t wpre_all[4][kWselWords];
+    __shared__ uint32_t bitmap_all[NW][WORDS];
+    __shared__ uint32_t wpre_all[NW][WORDS];
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-    const int64_t row = (int64_t)blockIdx.x * 4 + wave;
+    const int64_t row = (int64_t)blockIdx.x * NW + wave;
     if (row >= (int64_t)a.nseq * a.nq)
         return;  // waves never synchronise with each other
     const int s = (int)(row / a.nq), i = (int)(row - (int64_t)s * a.nq);
@@ -1594,7 +1594,7 @@ __global__ __launch_bounds__(256) void k_fused_select_wave(FusedTopkArgs a)
             a.queue[atomicAdd(&a.queue_ctr[0], 1u)] = (uint32_t)row;
         return;
     }
-    constexpr int U = kWselCap / 64;
+    constexpr int U = CAP / 64;
     uint32_t kr[U];
     int32_t jr[U];
 #pragma unroll
@@ -1653,20 +1653,17 @@ __global__ __launch_bounds__(256) void k_fused_select_wave(FusedTopkArgs a)
             atomicOr(&bitmap[jr[u] >> 5], 1u << (jr[u] & 31));
     }
     wave_lds_handoff();
-    constexpr int kWpl = kWselWords / 64;  // bitmap words per lane
-    uint32_t wv[kWpl];
+    constexpr int kWpl = WORDS / 64;  // bitmap words per lane
     int cntw = 0;
-#pragma unroll
     for (int q = 0; q < kWpl; ++q) {
         const int w = lane * kWpl + q;
-        wv[q] = w < nwords ? bitmap[w] : 0u;
-        cntw += __popc(wv[q]);
+        cntw += w < nwords ? __popc(bitmap[w]) : 0;
     }
     int before = wave_inclusive_scan(cntw) - cntw;
-#pragma unroll
     for (int q = 0; q < kWpl; ++q) {
-        wpre[lane * kWpl + q] = (uint32_t)before;
-        before += __popc(wv[q]);
+        const int w = lane * kWpl + q;
+        wpre[w] = (uint32_t)before;
+        before += w < nwords ? __popc(bitmap[w]) : 0;
     }
     wave_lds_handoff();
 #pragma unroll
@@ -1796,9 +1793,12 @@ static void launch_fused_p(const FusedTopkArgs &a, hipStream_t stream)
                        dim3((unsigned)((a.nq + kFilterQ - 1) / kFilterQ),
                             (unsigned)((a.max_cand + span - 1) / span), (unsigned)a.nseq),
                        dim3(kFilterNT), lds_f, stream, a);
-    if (a.cap == kWselCap && a.max_cand <= 32 * (int64_t)kWselWords)
-        hipLaunchKernelGGL(k_fused_select_wave, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
-                           stream, a);
+    // one wave per row for lists of 2048 keys with bitmaps for 32768 candidates, four rows per
+    // workgroup; longer rows take a 512-thread workgroup each (one wave per row with 4096-key
+    // lists holds 256 registers and 32 KB of LDS: 2.75 against 2.45 ms for the chunked prefill)
+    if (a.cap <= 2048 && a.max_cand <= 32768)
+        hipLaunchKernelGGL((k_fused_select_wave<2048, 1024, 4>),
+                           dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, a);
     else
         hipLaunchKernelGGL(k_fused_select<512>, dim3((unsigned)rows), dim3(512), 0, stream, a);
     const unsigned nfb = (unsigned)(rows < kFusedFallbackWGs ? rows : kFusedFallbackWGs);
