@@ -252,8 +252,8 @@ size_t sgqa_workspace_bytes(int op, const sgqa_dims *dims, int32_t nseq, int32_t
                 rows = ((int64_t)kIndexerWorkspaceCap - fixed) / row / 64 * 64;
             if (rows < min_rows)
                 rows = min_rows;
-            const int64_t fused = fixed + rows * row;
-            bytes = fused > bytes ? fused : bytes;
+            // the path without a score matrix runs whenever its workspace holds one pass
+            return (size_t)(fixed + rows * row);
         }
         return (size_t)bytes;
     }

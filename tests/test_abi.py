@@ -290,16 +290,21 @@ def test_decode_noalloc_validation():
 
 
 def test_workspace_sizes():
-    # a 32K prefill in one pass: the larger of the score-matrix path (32768 rows x ld 4096 x
-    # 4 B = 512 MiB) and the path without a score matrix (per row: 1024 sample keys, threshold,
-    # count, queue slot and a 2048-entry candidate list; 64 fallback score rows of ld floats
-    # and 256 bytes of counters)
+    # a 32K prefill in one pass of the path without a score matrix: per row 1024 sample keys,
+    # threshold, count, queue slot and a 2048-entry candidate list; 64 fallback score rows of
+    # ld = 4096 floats and 256 bytes of counters
     fused = 256 + 64 * 4096 * 4 + 32768 * (1024 * 4 + 12 + 2048 * 8)
-    assert sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, REAL, 1, 32768, 32768) == max(
-        32768 * 4096 * 4, fused)
+    assert sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, REAL, 1, 32768, 32768) == fused
     # capped at 2 GiB for the 128K prefill
     big = sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, REAL, 1, 131072, 131072)
     assert big <= 2 << 30
+    # the chunked prefill (131072 candidates: 4096 sample keys, 4096-entry lists) in one pass
+    ch = sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, REAL, 1, 8192, 1048580)
+    assert ch == 256 + 64 * 131072 * 4 + 8192 * (4096 * 4 + 12 + 4096 * 8)
+    # k beyond the selection without a score matrix: whole score rows, 2 GiB at most
+    wide = sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, with_selection(REAL, 1, 2048), 1, 32768,
+                                32768)
+    assert wide == 2 << 30  # 32768 rows x ld 32768 x 4 B = 4 GiB, capped in 64-row passes
     # decode: 32 splits of 16 blocks; partial o + (max, two sums) per (seq, split, head)
     ws = sgqa.workspace_bytes(sgqa.OP_ATTN_DECODE, REAL, 16, 1, 1 << 20)
     assert ws == 16 * 32 * 64 * (192 + 3) * 4
