@@ -1242,11 +1242,15 @@ __global__ __launch_bounds__(256) void k_fused_threshold(FusedTopkArgs a)
 #endif
 constexpr int kFilterWaves = SGQA_FILTER_WAVES;
 constexpr int kFilterTiles = SGQA_FILTER_TILES;
+#ifndef SGQA_FILTER_TILES_LONG
+#define SGQA_FILTER_TILES_LONG 32
+#endif
+constexpr int kFilterTilesLong = SGQA_FILTER_TILES_LONG;  // passes of > 32768 candidates
 constexpr int kStage = SGQA_FILTER_STAGE;
 constexpr int kFilterQ = 16 * kFilterWaves;  // query rows per workgroup
 constexpr int kFilterNT = 64 * kFilterWaves;
 
-template <int P>
+template <int P, int FT>
 __global__ __launch_bounds__(kFilterNT) void k_fused_filter(FusedTopkArgs a)
 {
     extern __shared__ __align__(16) uint16_t kb_tile[];  // [kTileB][P + 8], then the stage
@@ -1259,7 +1263,7 @@ __global__ __launch_bounds__(kFilterNT) void k_fused_filter(FusedTopkArgs a)
                                            // share their kb tiles in L2, their counters differ
     const int i_last = min(i0 + kFilterQ, a.nq) - 1;
     const int64_t c_last = fused_c(a, s, i_last);
-    const int64_t jt0 = (int64_t)blockIdx.y * kFilterTiles * kTileB;
+    const int64_t jt0 = (int64_t)blockIdx.y * FT * kTileB;
     if (jt0 >= c_last)
         return;
     const int tid = threadIdx.x;
@@ -1299,7 +1303,7 @@ __global__ __launch_bounds__(kFilterNT) void k_fused_filter(FusedTopkArgs a)
     };
     load_tile(jt0);
 #pragma unroll 1
-    for (int tl = 0; tl < kFilterTiles; ++tl) {
+    for (int tl = 0; tl < FT; ++tl) {
         const int64_t j0 = jt0 + (int64_t)tl * kTileB;
         if (j0 >= c_last)
             break;  // uniform over the workgroup
@@ -1312,7 +1316,7 @@ __global__ __launch_bounds__(kFilterNT) void k_fused_filter(FusedTopkArgs a)
                 *reinterpret_cast<u32x4 *>(kb_tile + r * ldt + cc * 8) = tv[u];
         }
         __syncthreads();
-        if (tl + 1 < kFilterTiles && j0 + kTileB < c_last)
+        if (tl + 1 < FT && j0 + kTileB < c_last)
             load_tile(j0 + kTileB);
         if (!wave_live)
             continue;
@@ -1787,12 +1791,19 @@ static void launch_fused_p(const FusedTopkArgs &a, hipStream_t stream)
     else
         hipLaunchKernelGGL(k_fused_threshold<64>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
                            stream, a);
-    const int64_t span = (int64_t)kFilterTiles * kTileB;
     const size_t lds_f = lds + (size_t)kFilterQ * kStage * 8 + 2 * kFilterQ * 4;
-    hipLaunchKernelGGL(k_fused_filter<P>,
-                       dim3((unsigned)((a.nq + kFilterQ - 1) / kFilterQ),
-                            (unsigned)((a.max_cand + span - 1) / span), (unsigned)a.nseq),
-                       dim3(kFilterNT), lds_f, stream, a);
+    const unsigned fq = (unsigned)((a.nq + kFilterQ - 1) / kFilterQ);
+    if (a.cap > 2048) {  // long rows keep few keys per block: longer spans per workgroup
+        const int64_t span = (int64_t)kFilterTilesLong * kTileB;
+        hipLaunchKernelGGL((k_fused_filter<P, kFilterTilesLong>),
+                           dim3(fq, (unsigned)((a.max_cand + span - 1) / span), (unsigned)a.nseq),
+                           dim3(kFilterNT), lds_f, stream, a);
+    } else {
+        const int64_t span = (int64_t)kFilterTiles * kTileB;
+        hipLaunchKernelGGL((k_fused_filter<P, kFilterTiles>),
+                           dim3(fq, (unsigned)((a.max_cand + span - 1) / span), (unsigned)a.nseq),
+                           dim3(kFilterNT), lds_f, stream, a);
+    }
     // one wave per row for lists of 2048 keys with bitmaps for 32768 candidates, four rows per
     // workgroup; longer rows take a 512-thread workgroup each (one wave per row with 4096-key
     // lists holds 256 registers and 32 KB of LDS: 2.75 against 2.45 ms for the chunked prefill)
