@@ -66,6 +66,21 @@ def scored_pairs(q_start: int, T: int, B: int) -> int:
 PREFILL_CHUNKS = 8
 
 
+def prefill_launches(wl) -> str:
+    """How one sgqa_sparse_attn_prefill call over all rows of the workload is dispatched: row
+    chunks of the workspace's 32768 rows, each in one launch per 2k-block range of history up
+    to its last own block (at most 16 ranges)."""
+    s = wl.shape
+    W, chunk = 2 * s.topk_blocks, min(32768, wl.T)
+    per = []
+    for r0 in range(0, wl.T, chunk):
+        c_last = (wl.q_start + min(wl.T, r0 + chunk) - 1) // s.block_size
+        per.append(min(c_last // W + 1, 16))
+    return (f"one sgqa_sparse_attn_prefill call over all {wl.T} rows: {len(per)} row chunks, "
+            f"each in one launch per {W}-block history range "
+            f"({' + '.join(map(str, per))} = {sum(per)} dispatches)")
+
+
 def bench_prefill(steps: int, warmup: int):
     import torch
     from long_context_sparse_18_amd import WORKLOADS, inputs, layer, sgqa
@@ -848,8 +863,7 @@ def main():
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
                      "kernel": "k_attn_prefill<192>",
-                     "launch": ("one sgqa_sparse_attn_prefill call over all 131072 rows: 4 row "
-                                "chunks x 8 history slices = 32 dispatches"),
+                     "launch": prefill_launches(wl),
                      "algorithmic_flops": pre["attn_flops"],
                      "flops_per_attended_pair": 4 * s.head_dim * s.num_q_heads,
                      "attended_pairs": pre["pairs"],
