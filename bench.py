@@ -320,6 +320,48 @@ def bench_chunked(steps: int, warmup: int, cpu: bool):
     return res
 
 
+def time_decode_step(topk, attn, flush, stream, steps: int, warmup: int):
+    """Median microseconds of one decode step (top-k then attention, back to back on the
+    stream) and of its two calls.  Every step starts after a 512 MiB read, so no step starts
+    with the caches warm.  The whole-step figure comes from steps with events only at their
+    ends: an event recorded between the two calls leaves the GPU idle for ~6 us while the
+    marker is processed, so the split comes from separate steps with that middle event."""
+    import torch
+
+    def run(mid: bool):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        m = torch.cuda.Event(enable_timing=True) if mid else None
+        a.record(stream)
+        topk()
+        if mid:
+            m.record(stream)
+        attn()
+        b.record(stream)
+        return a, m, b
+
+    for _ in range(warmup):
+        flush.sum()
+        run(True)
+    torch.cuda.synchronize()
+    whole, t_topk, t_attn = [], [], []
+    for _ in range(steps):
+        for mid in (False, True):
+            flush.sum()
+            a, m, b = run(mid)
+            torch.cuda.synchronize()
+            if mid:
+                t_topk.append(a.elapsed_time(m) * 1e3)
+                t_attn.append(m.elapsed_time(b) * 1e3)
+            else:
+                whole.append(a.elapsed_time(b) * 1e3)
+
+    def median(v):
+        return sorted(v)[len(v) // 2]
+
+    return median(whole), median(t_topk), median(t_attn)
+
+
 def bench_decode(steps: int, warmup: int, cpu: bool = False):
     import torch
     from long_context_sparse_18_amd import WORKLOADS, inputs, sgqa
@@ -345,40 +387,21 @@ def bench_decode(steps: int, warmup: int, cpu: bool = False):
     stream = torch.cuda.current_stream(dev)
     qp = d["qp"].unsqueeze(1)
 
-    def step():
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        m = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
+    def topk():
         sgqa.indexer_topk(s, qp, kb, [wl.L - 1] * n, idx, workspace=ws_topk, stream=stream)
-        m.record(stream)
+
+    def attn():
         sgqa.sparse_attn_decode(s, d["Q"], d["K"], d["V"], d["G"], idx.view(n, -1), [wl.L] * n,
                                 scale, out, workspace=ws_attn, stream=stream)
-        b.record(stream)
-        return a, m, b
 
-    for _ in range(warmup):
-        flush.sum()
-        step()
-    torch.cuda.synchronize()
-    times, t_topk, t_attn = [], [], []
-    for _ in range(steps):
-        flush.sum()   # no step starts with the caches warm
-        a, m, b = step()
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b) * 1e3)
-        t_topk.append(a.elapsed_time(m) * 1e3)
-        t_attn.append(m.elapsed_time(b) * 1e3)
-    times.sort()
-    med = times[len(times) // 2]
+    med, us_topk, us_attn = time_decode_step(topk, attn, flush, stream, steps, warmup)
     # algorithmic bytes: the whole index scan, the gathered K/V rows, and the small tensors
     per_seq = ((wl.L - 1) // s.block_size) * s.proxy_dim * 2 \
         + s.topk_blocks * s.block_size * s.num_kv_heads * s.head_dim * 2 * 2 \
         + (2 * s.num_q_heads * s.head_dim * 2 + s.proxy_dim * 2 + s.num_q_heads * 2
            + s.topk_blocks * 4)
     bytes_total = per_seq * n
-    res = dict(us_median=med, us_topk=sorted(t_topk)[len(t_topk) // 2],
-               us_attn=sorted(t_attn)[len(t_attn) // 2], bytes=bytes_total,
+    res = dict(us_median=med, us_topk=us_topk, us_attn=us_attn, bytes=bytes_total,
                gbs=bytes_total / (med * 1e-6) / 1e9)
     if cpu:
         log("decode: oracle on all 16 sequences")
@@ -402,41 +425,22 @@ def bench_decode(steps: int, warmup: int, cpu: bool = False):
     torch.cuda.empty_cache()
     idx8 = idx.view(n, -1)
 
-    def step8():
-        a = torch.cuda.Event(enable_timing=True)
-        b = torch.cuda.Event(enable_timing=True)
-        m = torch.cuda.Event(enable_timing=True)
-        a.record(stream)
+    def topk8():
         sgqa.indexer_topk_fp8(s, d["qp"], kbq, kbs, [wl.L - 1] * n, idx8, workspace=ws_topk,
                               stream=stream)
-        m.record(stream)
+
+    def attn8():
         sgqa.sparse_attn_decode_fp8(s, d["Q"], cq["K"][0], cq["V"][0], cq["K"][1], cq["V"][1],
                                     d["G"], idx8, [wl.L] * n, scale, out, workspace=ws_attn,
                                     stream=stream)
-        b.record(stream)
-        return a, m, b
 
-    for _ in range(warmup):
-        flush.sum()
-        step8()
-    torch.cuda.synchronize()
-    times, t_topk, t_attn = [], [], []
-    for _ in range(steps):
-        flush.sum()
-        a, m, b = step8()
-        torch.cuda.synchronize()
-        times.append(a.elapsed_time(b) * 1e3)
-        t_topk.append(a.elapsed_time(m) * 1e3)
-        t_attn.append(m.elapsed_time(b) * 1e3)
-    times.sort()
-    med8 = times[len(times) // 2]
+    med8, us_topk8, us_attn8 = time_decode_step(topk8, attn8, flush, stream, steps, warmup)
     c = (wl.L - 1) // s.block_size
     per_seq8 = c * (s.proxy_dim + 4) \
         + s.topk_blocks * s.block_size * s.num_kv_heads * (s.head_dim + 4) * 2 \
         + (2 * s.num_q_heads * s.head_dim * 2 + s.proxy_dim * 2 + s.num_q_heads * 2
            + s.topk_blocks * 4)
-    res["fp8"] = dict(us_median=med8, us_topk=sorted(t_topk)[len(t_topk) // 2],
-                      us_attn=sorted(t_attn)[len(t_attn) // 2], bytes=per_seq8 * n,
+    res["fp8"] = dict(us_median=med8, us_topk=us_topk8, us_attn=us_attn8, bytes=per_seq8 * n,
                       gbs=per_seq8 * n / (med8 * 1e-6) / 1e9)
     return res
 
@@ -895,7 +899,9 @@ def main():
                           "us_indexer_topk": dec["us_topk"], "us_attention": dec["us_attn"],
                           "GBps": dec["gbs"], "hbm_frac": dec["gbs"] / PEAK_HBM_GBS,
                           "algorithmic_bytes": dec["bytes"],
-                          "timing": "median of the steps, 512 MiB read between steps"}
+                          "timing": ("median of the steps, 512 MiB read between steps; "
+                                     "us_per_layer from steps timed at their ends only, the "
+                                     "split from steps with an event between the two calls")}
         if "cpu_baseline" in dec:
             line["decode"]["cpu_baseline"] = dec["cpu_baseline"]
         if peaks is not None:

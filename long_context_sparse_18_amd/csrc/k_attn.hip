@@ -160,191 +160,318 @@ struct Fp8Rows {
     const float *Ks, *Vs;
 };
 
-// Attend one wave's (token, group) over the tokens of `src`, reading rows from `rows`.
-// `vs` is this wave's LDS buffer [kSlots][D + 8].  Per 32-slot step the K rows go straight into
-// MFMA A operands and the V rows are staged in `vs` and read transposed.  With FP8 rows the
-// query fragments must be in the permuted dim order of load_q_perm: K codes are read 16 at a
-// time (dims [64 k2 + 16 q4, +16)) and feed two MFMA steps; V codes are converted to bf16
-// while staged; each row's K scale multiplies its logits and its V scale its softmax weight,
-// so the products run on exact bf16 copies of the codes.
-template <int D, typename Src, typename Rows>
-__device__ __forceinline__ void attend_range(const Rows &rows, int Hkv, const Src &src,
-                                             const bf16x8 (&qf)[D / 32], float scale_log2,
-                                             uint16_t *vs, WaveState<D> &st)
+// The query operand of Sᵀ = K·Qᵀ: fragment kk holds dims [32 kk + 8 q4, +8) of head col
+// (lane = 16 q4 + col), in registers (load_q / load_q_perm).
+template <int D>
+struct QRegs {
+    const bf16x8 (&f)[D / 32];
+    __device__ __forceinline__ bf16x8 operator()(int kk) const { return f[kk]; }
+};
+
+// One 32-slot step's rows of a wave, as loaded into registers: for bf16 rows, the K and V
+// pieces of whole rows (flat piece f = lane + 64 ci covers slot f / pieces, piece f % pieces:
+// pieces of 8 values, or of 16 FP8 codes, so each load instruction reads whole rows); for FP8
+// rows, the K codes straight in the A-operand layout and the row scales of this lane's slot
+// (lane & 31).
+template <int D, bool kFp8>
+struct StepRows {
+    static constexpr int kVPieces = kFp8 ? D / 16 : D / 8;
+    static constexpr int kVLoads = kFp8 ? D / 32 : D / 16;
+    static constexpr int kKLoads = kFp8 ? D / 64 : 1;
+    u32x4 kv[2][kKLoads];
+    u32x4 kp[kFp8 ? 1 : kVLoads];
+    u32x4 vv[kVLoads];
+    float k_scale, v_scale;
+};
+
+// The tokens of one step: slot validity (bit per slot) and this lane's slot (lane & 31)
+// clamped load position, split in 32-bit halves for the shuffles.
+struct StepSlots {
+    uint64_t vmask;
+    int64_t s_ld;
+    int s_lo, s_hi;
+};
+
+// Reads the wave's entry window, which it refills from the selection row when the step runs
+// past it.
+template <typename Src>
+__device__ __forceinline__ StepSlots step_slots(const Src &src, int step, int &wbase)
 {
-    constexpr int kLd = D + 8;  // LDS row stride in elements (conflict-free transposing reads)
+    StepSlots p;
+    bool valid;
+    src.slot(step, (int)(threadIdx.x & 31), wbase, p.s_ld, valid);
+    p.vmask = __ballot(valid);
+    p.s_lo = (int)(p.s_ld & 0xffffffff);
+    p.s_hi = (int)(p.s_ld >> 32);
+    return p;
+}
+
+// Address of element `elem` of the row of slot `slot` (the token p.s_ld of lane `slot`).
+template <typename T>
+__device__ __forceinline__ const T *row_piece(const T *base, const StepSlots &p, int slot,
+                                              int64_t row_elems, int elem)
+{
+    const int64_t sv = ((int64_t)(uint32_t)__shfl(p.s_lo, slot)) |
+                       ((int64_t)__shfl(p.s_hi, slot) << 32);
+    return base + sv * row_elems + elem;
+}
+
+// Issue the K loads of a step.  bf16 K rows are read whole and staged in LDS for the A
+// operands: read straight in the operand layout (16 rows x 64 bytes per instruction) the same
+// gathers took 135 instead of 113 ms in a loads-only copy of the 128K prefill.
+template <int D, typename Rows>
+__device__ __forceinline__ void issue_k(const Rows &rows, int Hkv, const StepSlots &p,
+                                        StepRows<D, Rows::kFp8> &r)
+{
+    using SR = StepRows<D, Rows::kFp8>;
     const int lane = threadIdx.x & 63;
     const int col = lane & 15, q4 = lane >> 4;
     const int64_t row_elems = (int64_t)Hkv * D;
-    const float neg_inf = -__builtin_inff();
-    const int nsteps = src.steps();
-    int wbase = -(1 << 30);  // empty window
-
-    for (int step = 0; step < nsteps; ++step) {
-        // Token of slot (lane & 31): clamped load position + validity.
-        int64_t s_ld;
-        bool valid;
-        src.slot(step, lane & 31, wbase, s_ld, valid);
-        const uint64_t vmask = __ballot(valid);
-        const int s_lo = (int)(s_ld & 0xffffffff), s_hi = (int)(s_ld >> 32);
-
-        // Row pieces: flat piece f = lane + 64 ci covers slot f / pieces, piece f % pieces
-        // (pieces of 8 bf16 values, or of 16 FP8 codes), so each load instruction reads whole
-        // rows.  bf16 K rows are read this way too and staged in LDS for the A operands: read
-        // straight in the operand layout (16 rows x 64 bytes per instruction) the same gathers
-        // took 135 instead of 113 ms in a loads-only copy of the 128K prefill.
-        constexpr int kVPieces = Rows::kFp8 ? D / 16 : D / 8;
-        constexpr int kVLoads = Rows::kFp8 ? D / 32 : D / 16;
-        // FP8 K rows for the two 16-slot A tiles, straight in the operand layout (D/64 loads
-        // of 16 codes)
-        constexpr int kKLoads = Rows::kFp8 ? D / 64 : 1;
-        u32x4 kv[2][kKLoads];
-        u32x4 kp[Rows::kFp8 ? 1 : kVLoads];
-        if constexpr (Rows::kFp8) {
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-                const int src = h * 16 + col;
-                const int64_t sk = ((int64_t)(uint32_t)__shfl(s_lo, src)) |
-                                   ((int64_t)__shfl(s_hi, src) << 32);
-                const uint8_t *kr = rows.Kg + sk * row_elems + q4 * 16;
-#pragma unroll
-                for (int k2 = 0; k2 < kKLoads; ++k2)
-                    kv[h][k2] = load16(kr + k2 * 64);
-            }
-        }
-        u32x4 vv[kVLoads];
-#pragma unroll
-        for (int ci = 0; ci < kVLoads; ++ci) {
-            const int f = lane + 64 * ci;
-            const int slot = f / kVPieces, piece = f - slot * kVPieces;
-            const int64_t sv = ((int64_t)(uint32_t)__shfl(s_lo, slot)) |
-                               ((int64_t)__shfl(s_hi, slot) << 32);
-            if constexpr (Rows::kFp8) {
-                vv[ci] = load16(rows.Vg + sv * row_elems + piece * 16);
-            } else {  // the K and V pieces of a row share their offset
-                const int64_t off = sv * row_elems + piece * 8;
-                kp[ci] = load16(rows.Kg + off);
-                vv[ci] = load16(rows.Vg + off);
-            }
-        }
-        // FP8: the scales of this lane's slot (lane & 31); others read them by shuffle
-        float k_scale = 1.0f, v_scale = 1.0f;
-        if constexpr (Rows::kFp8) {
-            k_scale = rows.Ks[s_ld * Hkv];
-            v_scale = rows.Vs[s_ld * Hkv];
-        }
-
-        // bf16: stage the K rows in the wave's buffer (the previous step's transposed V reads
-        // are done at the handoff), then read the A operands from it
-        if constexpr (!Rows::kFp8) {
-            wave_lds_handoff();
-#pragma unroll
-            for (int ci = 0; ci < kVLoads; ++ci) {
-                const int f = lane + 64 * ci;
-                const int slot = f / kVPieces, piece = f - slot * kVPieces;
-                uint2 *dst = reinterpret_cast<uint2 *>(vs + slot * kLd + piece * 8);
-                dst[0] = uint2{kp[ci][0], kp[ci][1]};
-                dst[1] = uint2{kp[ci][2], kp[ci][3]};
-            }
-            wave_lds_handoff();
-        }
-        // S^T = K Q^T for slots 0-15 and 16-31.
-        f32x4 sc[2];
+    if constexpr (Rows::kFp8) {
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
-            sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if constexpr (Rows::kFp8) {
+            const int src_lane = h * 16 + col;
+            const int64_t sk = ((int64_t)(uint32_t)__shfl(p.s_lo, src_lane)) |
+                               ((int64_t)__shfl(p.s_hi, src_lane) << 32);
+            const uint8_t *kr = rows.Kg + sk * row_elems + q4 * 16;
 #pragma unroll
-                for (int k2 = 0; k2 < kKLoads; ++k2) {
-                    bf16x8 lo, hi;
-                    e4m3x16_to_bf16x8x2(kv[h][k2], lo, hi);
-                    sc[h] = mfma_16x16x32(lo, qf[2 * k2], sc[h]);
-                    sc[h] = mfma_16x16x32(hi, qf[2 * k2 + 1], sc[h]);
-                }
-#pragma unroll
-                for (int r = 0; r < 4; ++r)
-                    sc[h][r] *= __shfl(k_scale, h * 16 + q4 * 4 + r);
-            } else {
-#pragma unroll
-                for (int kk = 0; kk < D / 32; ++kk) {
-                    const u32x4 ka = *reinterpret_cast<const u32x4 *>(
-                        vs + (h * 16 + col) * kLd + kk * 32 + q4 * 8);
-                    sc[h] = mfma_16x16x32(as_bf16x8(ka), qf[kk], sc[h]);
-                }
-            }
+            for (int k2 = 0; k2 < SR::kKLoads; ++k2)
+                r.kv[h][k2] = load16(kr + k2 * 64);
         }
-
-        // Online softmax (base 2).  Lane holds slots 16h + 4*q4 + r of head col.
-        float x[2][4];
-        float mloc = neg_inf;
+    } else {
 #pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int slot = h * 16 + q4 * 4 + r;
-                const bool ok = (vmask >> slot) & 1ull;
-                x[h][r] = ok ? sc[h][r] * scale_log2 : neg_inf;
-                mloc = fmaxf(mloc, x[h][r]);
-            }
-        const float m_new = fmaxf(st.m, max_across_rows(mloc));
-        const bool any = m_new != neg_inf;
-        const float alpha = any ? fast_exp2(st.m - m_new) : 1.0f;
-        float p[2][4];
-        float psum = 0.f, psum32 = 0.f;
-#pragma unroll
-        for (int h = 0; h < 2; ++h)
-#pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const float pe = any ? fast_exp2(x[h][r] - m_new) : 0.f;
-                // normalise by the bf16 weights PV uses, so the output is a convex combination
-                p[h][r] = bf16_bits_to_f32(f32_to_bf16_bits(pe));
-                psum += p[h][r];
-                psum32 += pe;
-                if constexpr (Rows::kFp8)  // the V row's scale rides on its weight
-                    p[h][r] = pe * __shfl(v_scale, h * 16 + q4 * 4 + r);
-            }
-        st.l = st.l * alpha + psum;
-        st.l32 = st.l32 * alpha + psum32;
-        st.m = m_new;
-#pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt)
-#pragma unroll
-            for (int r = 0; r < 4; ++r)
-                st.acc[mt][r] *= alpha;
-        u32x4 pw;
-        pw[0] = pack_bf16x2(p[0][0], p[0][1]);
-        pw[1] = pack_bf16x2(p[0][2], p[0][3]);
-        pw[2] = pack_bf16x2(p[1][0], p[1][1]);
-        pw[3] = pack_bf16x2(p[1][2], p[1][3]);
-        const bf16x8 pf = as_bf16x8(pw);
-
-        // Stage V rows in LDS (row stride kLd elements, 16-byte aligned rows).
-        wave_lds_handoff();
-#pragma unroll
-        for (int ci = 0; ci < kVLoads; ++ci) {
+        for (int ci = 0; ci < SR::kVLoads; ++ci) {
             const int f = lane + 64 * ci;
-            const int slot = f / kVPieces, piece = f - slot * kVPieces;
-            if constexpr (Rows::kFp8) {
-                uint32_t w[8];
+            const int slot = f / SR::kVPieces, piece = f - slot * SR::kVPieces;
+            r.kp[ci] = load16(row_piece(rows.Kg, p, slot, row_elems, piece * 8));
+        }
+    }
+}
+
+// Issue the V loads of a step (and, for FP8 rows, the row scales of this lane's slot).
+template <int D, typename Rows>
+__device__ __forceinline__ void issue_v(const Rows &rows, int Hkv, const StepSlots &p,
+                                        StepRows<D, Rows::kFp8> &r)
+{
+    using SR = StepRows<D, Rows::kFp8>;
+    const int lane = threadIdx.x & 63;
+    const int64_t row_elems = (int64_t)Hkv * D;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    e4m3x4_to_bf16(vv[ci][e], w[2 * e], w[2 * e + 1]);
-                uint2 *dst = reinterpret_cast<uint2 *>(vs + slot * kLd + piece * 16);
+    for (int ci = 0; ci < SR::kVLoads; ++ci) {
+        const int f = lane + 64 * ci;
+        const int slot = f / SR::kVPieces, piece = f - slot * SR::kVPieces;
+        if constexpr (Rows::kFp8)
+            r.vv[ci] = load16(row_piece(rows.Vg, p, slot, row_elems, piece * 16));
+        else
+            r.vv[ci] = load16(row_piece(rows.Vg, p, slot, row_elems, piece * 8));
+    }
+    r.k_scale = 1.0f;
+    r.v_scale = 1.0f;
+    if constexpr (Rows::kFp8) {
+        r.k_scale = rows.Ks[p.s_ld * Hkv];
+        r.v_scale = rows.Vs[p.s_ld * Hkv];
+    }
+}
+
+// Issue all loads of a step; bf16 K and V pieces of a row share one offset computation.
+template <int D, typename Rows>
+__device__ __forceinline__ void issue_kv(const Rows &rows, int Hkv, const StepSlots &p,
+                                         StepRows<D, Rows::kFp8> &r)
+{
+    if constexpr (Rows::kFp8) {
+        issue_k<D>(rows, Hkv, p, r);
+        issue_v<D>(rows, Hkv, p, r);
+    } else {
+        using SR = StepRows<D, false>;
+        const int lane = threadIdx.x & 63;
+        const int64_t row_elems = (int64_t)Hkv * D;
 #pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    dst[e] = uint2{w[2 * e], w[2 * e + 1]};
-            } else {
-                uint2 *dst = reinterpret_cast<uint2 *>(vs + slot * kLd + piece * 8);
-                dst[0] = uint2{vv[ci][0], vv[ci][1]};
-                dst[1] = uint2{vv[ci][2], vv[ci][3]};
-            }
+        for (int ci = 0; ci < SR::kVLoads; ++ci) {
+            const int f = lane + 64 * ci;
+            const int slot = f / SR::kVPieces, piece = f - slot * SR::kVPieces;
+            const int64_t sv = ((int64_t)(uint32_t)__shfl(p.s_lo, slot)) |
+                               ((int64_t)__shfl(p.s_hi, slot) << 32);
+            const int64_t off = sv * row_elems + piece * 8;
+            r.kp[ci] = load16(rows.Kg + off);
+            r.vv[ci] = load16(rows.Vg + off);
+        }
+        r.k_scale = 1.0f;
+        r.v_scale = 1.0f;
+    }
+}
+
+// Sᵀ = K·Qᵀ for slots 0-15 (sc[0]) and 16-31 (sc[1]).  bf16: the K rows are first staged in
+// the wave's buffer `vs` [kSlots][D + 8] (the previous step's transposed V reads are done at
+// the handoff) and the A operands read from it.  FP8: the query fragments must be in the
+// permuted dim order of load_q_perm; each 16 codes feed two MFMA steps after an exact
+// conversion to bf16, and the row's K scale multiplies its logits.
+template <int D, bool kFp8, typename Q>
+__device__ __forceinline__ void step_scores(const StepRows<D, kFp8> &r, const Q &qf, uint16_t *vs,
+                                            f32x4 (&sc)[2])
+{
+    using SR = StepRows<D, kFp8>;
+    constexpr int kLd = D + 8;  // LDS row stride in elements (conflict-free transposing reads)
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    if constexpr (!kFp8) {
+        wave_lds_handoff();
+#pragma unroll
+        for (int ci = 0; ci < SR::kVLoads; ++ci) {
+            const int f = lane + 64 * ci;
+            const int slot = f / SR::kVPieces, piece = f - slot * SR::kVPieces;
+            uint2 *dst = reinterpret_cast<uint2 *>(vs + slot * kLd + piece * 8);
+            dst[0] = uint2{r.kp[ci][0], r.kp[ci][1]};
+            dst[1] = uint2{r.kp[ci][2], r.kp[ci][3]};
         }
         wave_lds_handoff();
-
-        // O^T += V^T P^T: A[m = d][k = slot perm(8*q4 + j)], slots 4q4+j (j<4), 16+4q4+j-4.
+    }
 #pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt)
-            st.acc[mt] = mfma_16x16x32(vt_fragment(vs, kLd, mt * 16), pf, st.acc[mt]);
+    for (int h = 0; h < 2; ++h) {
+        sc[h] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if constexpr (kFp8) {
+#pragma unroll
+            for (int k2 = 0; k2 < SR::kKLoads; ++k2) {
+                bf16x8 lo, hi;
+                e4m3x16_to_bf16x8x2(r.kv[h][k2], lo, hi);
+                sc[h] = mfma_16x16x32(lo, qf(2 * k2), sc[h]);
+                sc[h] = mfma_16x16x32(hi, qf(2 * k2 + 1), sc[h]);
+            }
+        } else {
+#pragma unroll
+            for (int kk = 0; kk < D / 32; ++kk) {
+                const u32x4 ka = *reinterpret_cast<const u32x4 *>(
+                    vs + (h * 16 + col) * kLd + kk * 32 + q4 * 8);
+                sc[h] = mfma_16x16x32(as_bf16x8(ka), qf(kk), sc[h]);
+            }
+        }
+    }
+}
+
+// Online softmax (base 2) of one step's scores; returns the Pᵀ operand of the PV product.
+// Lane holds slots 16h + 4*q4 + i of head col.  The weights are normalised by their bf16
+// values, the ones PV uses, so the output is a convex combination; with FP8 rows each V
+// row's scale rides on its weight.
+template <int D, bool kFp8>
+__device__ __forceinline__ bf16x8 step_softmax(const f32x4 (&sc_in)[2], uint64_t vmask,
+                                               float k_scale, float v_scale, float scale_log2,
+                                               WaveState<D> &st)
+{
+    const int lane = threadIdx.x & 63;
+    const int q4 = lane >> 4;
+    const float neg_inf = -__builtin_inff();
+    f32x4 sc[2] = {sc_in[0], sc_in[1]};
+    if constexpr (kFp8) {
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                sc[h][i] *= __shfl(k_scale, h * 16 + q4 * 4 + i);
+    }
+    float x[2][4];
+    float mloc = neg_inf;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int slot = h * 16 + q4 * 4 + i;
+            const bool ok = (vmask >> slot) & 1ull;
+            x[h][i] = ok ? sc[h][i] * scale_log2 : neg_inf;
+            mloc = fmaxf(mloc, x[h][i]);
+        }
+    const float m_new = fmaxf(st.m, max_across_rows(mloc));
+    const bool any = m_new != neg_inf;
+    const float alpha = any ? fast_exp2(st.m - m_new) : 1.0f;
+    float p[2][4];
+    float psum = 0.f, psum32 = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float pe = any ? fast_exp2(x[h][i] - m_new) : 0.f;
+            p[h][i] = bf16_bits_to_f32(f32_to_bf16_bits(pe));
+            psum += p[h][i];
+            psum32 += pe;
+            if constexpr (kFp8)
+                p[h][i] = pe * __shfl(v_scale, h * 16 + q4 * 4 + i);
+        }
+    st.l = st.l * alpha + psum;
+    st.l32 = st.l32 * alpha + psum32;
+    st.m = m_new;
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            st.acc[mt][i] *= alpha;
+    u32x4 pw;
+    pw[0] = pack_bf16x2(p[0][0], p[0][1]);
+    pw[1] = pack_bf16x2(p[0][2], p[0][3]);
+    pw[2] = pack_bf16x2(p[1][0], p[1][1]);
+    pw[3] = pack_bf16x2(p[1][2], p[1][3]);
+    return as_bf16x8(pw);
+}
+
+// Stage a step's V rows in the wave's buffer (FP8 codes converted to bf16 on the way).
+template <int D, bool kFp8>
+__device__ __forceinline__ void stage_v(const StepRows<D, kFp8> &r, uint16_t *vs)
+{
+    using SR = StepRows<D, kFp8>;
+    constexpr int kLd = D + 8;
+    const int lane = threadIdx.x & 63;
+    wave_lds_handoff();
+#pragma unroll
+    for (int ci = 0; ci < SR::kVLoads; ++ci) {
+        const int f = lane + 64 * ci;
+        const int slot = f / SR::kVPieces, piece = f - slot * SR::kVPieces;
+        if constexpr (kFp8) {
+            uint32_t w[8];
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                e4m3x4_to_bf16(r.vv[ci][e], w[2 * e], w[2 * e + 1]);
+            uint2 *dst = reinterpret_cast<uint2 *>(vs + slot * kLd + piece * 16);
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+                dst[e] = uint2{w[2 * e], w[2 * e + 1]};
+        } else {
+            uint2 *dst = reinterpret_cast<uint2 *>(vs + slot * kLd + piece * 8);
+            dst[0] = uint2{r.vv[ci][0], r.vv[ci][1]};
+            dst[1] = uint2{r.vv[ci][2], r.vv[ci][3]};
+        }
+    }
+    wave_lds_handoff();
+}
+
+// Oᵀ += Vᵀ·Pᵀ from the staged V rows: A[m = d][k = slot perm(8*q4 + j)], slots 4q4+j (j<4),
+// 16+4q4+j-4.
+template <int D>
+__device__ __forceinline__ void step_pv(const uint16_t *vs, bf16x8 pf, WaveState<D> &st)
+{
+#pragma unroll
+    for (int mt = 0; mt < D / 16; ++mt)
+        st.acc[mt] = mfma_16x16x32(vt_fragment(vs, D + 8, mt * 16), pf, st.acc[mt]);
+}
+
+// Attend one wave's (token, group) over the tokens of `src`, reading rows from `rows`, one
+// 32-slot step at a time (`vs`: the wave's LDS buffer [kSlots][D + 8]).  Per step the K rows
+// feed Sᵀ = K·Qᵀ, an online softmax gives Pᵀ, and the V rows, staged in `vs` and read
+// transposed, feed Oᵀ += Vᵀ·Pᵀ.
+template <int D, typename Src, typename Rows, typename Q>
+__device__ __forceinline__ void attend_range(const Rows &rows, int Hkv, const Src &src,
+                                             const Q &qf, float scale_log2, uint16_t *vs,
+                                             WaveState<D> &st)
+{
+    constexpr bool kFp8 = Rows::kFp8;
+    const int nsteps = src.steps();
+    int wbase = -(1 << 30);  // empty window
+    for (int step = 0; step < nsteps; ++step) {
+        const StepSlots p = step_slots(src, step, wbase);
+        StepRows<D, kFp8> r;
+        issue_kv<D>(rows, Hkv, p, r);
+        f32x4 sc[2];
+        step_scores<D, kFp8>(r, qf, vs, sc);
+        const bf16x8 pf = step_softmax<D, kFp8>(sc, p.vmask, r.k_scale, r.v_scale, scale_log2,
+                                                st);
+        stage_v<D, kFp8>(r, vs);
+        step_pv<D>(vs, pf, st);
     }
 }
 
@@ -570,8 +697,8 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
     else
         load_state<D>(st, a.state + state_offset(a, r, g));
     const SparseTokens src{a.idx + r * a.k, e_lo, e_hi, t, c, a.B, entry_window<D>(lds)};
-    attend_range<D>(Bf16Rows{a.kc + (int64_t)g * D, a.vc + (int64_t)g * D}, a.Hkv, src, qf,
-                    a.scale_log2, lds + wave * attn_vbuf_elems(D), st);
+    attend_range<D>(Bf16Rows{a.kc + (int64_t)g * D, a.vc + (int64_t)g * D}, a.Hkv, src,
+                    QRegs<D>{qf}, a.scale_log2, lds + wave * attn_vbuf_elems(D), st);
 
     if (!sliced || a.slice == last)
         store_row<D>(st, a, r, g, hpg);
@@ -807,24 +934,25 @@ __global__ __launch_bounds__(512) void k_attn_decode_part(AttnArgs a)
     const int e1 = min(e0 + a.entries_per_split, nvalid);
     const int hpg = a.Hq / a.Hkv;
 
-    bf16x8 qf[D / 32];
-    if constexpr (kFp8)
-        load_q_perm<D>(a.q + ((int64_t)s * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
-    else
-        load_q<D>(a.q + ((int64_t)s * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
     WaveState<D> st;
     init_state<D>(st);
     const int64_t base = (int64_t)s * a.cache_seq_stride + (int64_t)g * D;
+    const uint16_t *qg = a.q + ((int64_t)s * a.Hq + (int64_t)g * hpg) * D;
+    bf16x8 qf[D / 32];
+    if constexpr (kFp8)
+        load_q_perm<D>(qg, hpg, qf);
+    else
+        load_q<D>(qg, hpg, qf);
     if (e0 < e1) {
         const SparseTokens src{a.idx + (int64_t)s * a.k, e0, e1, t, c, a.B, entry_window<D>(lds)};
         uint16_t *vs = lds + wave * attn_vbuf_elems(D);
         if constexpr (kFp8) {
             const int64_t sb = (int64_t)s * a.scale_seq_stride * a.Hkv + g;
-            attend_range<D>(Fp8Rows{a.kq + base, a.vq + base, a.ksc + sb, a.vsc + sb}, a.Hkv,
-                            src, qf, a.scale_log2, vs, st);
+            const Fp8Rows rows{a.kq + base, a.vq + base, a.ksc + sb, a.vsc + sb};
+            attend_range<D>(rows, a.Hkv, src, QRegs<D>{qf}, a.scale_log2, vs, st);
         } else {
-            attend_range<D>(Bf16Rows{a.kc + base, a.vc + base}, a.Hkv, src, qf, a.scale_log2,
-                            vs, st);
+            const Bf16Rows rows{a.kc + base, a.vc + base};
+            attend_range<D>(rows, a.Hkv, src, QRegs<D>{qf}, a.scale_log2, vs, st);
         }
     }
 
