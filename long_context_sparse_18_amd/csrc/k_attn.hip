@@ -160,6 +160,16 @@ struct Fp8Rows {
     const float *Ks, *Vs;
 };
 
+// Online softmax with a lazy running maximum: a step moves a query's (or head's) maximum only
+// when it raises it by more than kLazyMax in log2 units, so most steps keep the maximum and
+// skip the rescale of the accumulators; the weights exp2(x - m) then stay below 2^kLazyMax,
+// well inside the range of fp32 sums and bf16 weights, and the output and lse use the same m
+// as the sums.
+#ifndef SGQA_LAZY_MAX
+#define SGQA_LAZY_MAX 8.0f
+#endif
+constexpr float kLazyMax = SGQA_LAZY_MAX;
+
 // The query operand of Sᵀ = K·Qᵀ: fragment kk holds dims [32 kk + 8 q4, +8) of head col
 // (lane = 16 q4 + col), in registers (load_q / load_q_perm).
 template <int D>
@@ -378,7 +388,11 @@ __device__ __forceinline__ bf16x8 step_softmax(const f32x4 (&sc_in)[2], uint64_t
             x[h][i] = ok ? sc[h][i] * scale_log2 : neg_inf;
             mloc = fmaxf(mloc, x[h][i]);
         }
-    const float m_new = fmaxf(st.m, max_across_rows(mloc));
+    // the running maximum moves only when a step raises it by more than kLazyMax (log2
+    // units), so most steps skip the accumulators' rescale (wave vote); the weights stay
+    // below 2^kLazyMax
+    const float m_row = fmaxf(st.m, max_across_rows(mloc));
+    const float m_new = m_row > st.m + kLazyMax ? m_row : st.m;
     const bool any = m_new != neg_inf;
     const float alpha = any ? fast_exp2(st.m - m_new) : 1.0f;
     float p[2][4];
@@ -397,11 +411,13 @@ __device__ __forceinline__ bf16x8 step_softmax(const f32x4 (&sc_in)[2], uint64_t
     st.l = st.l * alpha + psum;
     st.l32 = st.l32 * alpha + psum32;
     st.m = m_new;
+    if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-    for (int mt = 0; mt < D / 16; ++mt)
+        for (int mt = 0; mt < D / 16; ++mt)
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            st.acc[mt][i] *= alpha;
+            for (int i = 0; i < 4; ++i)
+                st.acc[mt][i] *= alpha;
+    }
     u32x4 pw;
     pw[0] = pack_bf16x2(p[0][0], p[0][1]);
     pw[1] = pack_bf16x2(p[0][2], p[0][3]);
@@ -763,38 +779,47 @@ __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
     WaveState<D> st;
     init_state<D>(st);
     const int64_t tq = t0 + col;  // this lane's query position
+    // the window, at most every position up to the tile's last query (positions < 2^31)
+    const int wnd = (int)(a.window < t_last + 1 ? a.window : t_last + 1);
+    const uint32_t win = col < nq ? (uint32_t)wnd : 0u;
+    // |scale| (at least the smallest normal float, so that a zero scale still gives -inf for
+    // masked scores and equal weights for the others)
+    const float scale_abs = fmaxf(__builtin_fabsf(a.scale_log2), 1.17549435e-38f);
 
     constexpr int kPpr = kLd / 8;                       // 16-byte pieces per LDS row
     constexpr int kTilePieces = 2 * kSlots * kPpr;
-    static_assert(kTilePieces % 64 == 0, "whole instructions");
-    // this lane's piece of the wave's first two DMA instructions (the same every step): the
-    // row within the step, K or V, and the element offset within the group's row
+    // K pieces fill whole instructions, so each instruction reads only K or only V rows
+    static_assert((kSlots * kPpr) % 64 == 0, "whole instructions");
+    // this lane's piece of the wave's first kPre DMA instructions (the same every step): the
+    // row within the step (low 8 bits) and the byte offset of the piece within the row's group
+    // part (the bits above); the step's first row and K or V come from a wave-uniform base
     constexpr int kPre = 4;
-    int dslot[kPre], doff[kPre];
-    bool dv_[kPre];
+    const uint32_t row_bytes = (uint32_t)(row_elems * sizeof(uint16_t));
+    uint32_t dpiece[kPre];
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
         const int i = wave + u * nwaves;
         const int pc = (i < kTilePieces / 64 ? i : 0) * 64 + lane;
-        const int which = pc / (kSlots * kPpr);
-        const int rem = pc - which * kSlots * kPpr;
+        const int rem = pc % (kSlots * kPpr);
         const int slot = rem / kPpr, piece = rem - slot * kPpr;
-        dslot[u] = slot;
-        dv_[u] = which != 0;
-        doff[u] = g * D + (piece < D / 8 ? piece : 0) * 8;
+        dpiece[u] = (uint32_t)slot | ((uint32_t)(piece < D / 8 ? piece : 0) * 16u << 8);
     }
     auto dma = [&](int step, uint16_t *buf) {
         const int64_t k0 = ks0 + (int64_t)step * kSlots;
+        // rows past t_last (only in the last step) reload row t_last; they are masked below
+        const uint32_t last_rel = (uint32_t)(t_last - k0);
 #pragma unroll
         for (int u = 0; u < kPre; ++u) {
             const int i = wave + u * nwaves;
             if (i < kTilePieces / 64) {
-                int64_t sp = k0 + dslot[u];
-                if (sp > t_last)
-                    sp = t_last;  // a valid row; masked below
-                const uint16_t *src = (dv_[u] ? a.vc : a.kc) + sp * row_elems + doff[u];
+                const bool is_v = i * 64 >= kSlots * kPpr;
+                const char *base = reinterpret_cast<const char *>((is_v ? a.vc : a.kc) +
+                                                                  k0 * row_elems + g * D);
+                const uint32_t slot = dpiece[u] & 0xffu;
+                const uint32_t off = (slot < last_rel ? slot : last_rel) * row_bytes +
+                                     (dpiece[u] >> 8);
                 __builtin_amdgcn_global_load_lds(
-                    (const void __attribute__((address_space(1))) *)src,
+                    (const void __attribute__((address_space(1))) *)(base + off),
                     (void __attribute__((address_space(3))) *)(buf + i * 64 * 8), 16, 0, 0);
             }
         }
@@ -838,30 +863,43 @@ __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
                 sc[hh] = mfma_16x16x32(as_bf16x8(kv), qf[kk], sc[hh]);
             }
         }
-        // online softmax (base 2) per query; lane holds positions 16 hh + 4 q4 + r of query col;
-        // rel = position - query, in [1 - window, 0] inside the window
-        const int rel0 = (int)(k0 - tq) + q4 * 4;
-        float x[2][4];
-        float mloc = neg_inf;
+        // online softmax (base 2) per query; lane holds positions 16 hh + 4 q4 + r of query col.
+        // Only a tile's first and last steps hold positions outside some query's window: there
+        // rel = position - query must lie in [1 - window, 0], i.e. rel + window - 1 in
+        // [0, win) as an unsigned compare (win = 0 for the lanes of absent queries), and the
+        // other scores become -inf.  The scale is applied with the exponent's subtraction
+        // (scores negated first for a negative scale, so the maximum commutes with it).
+        if (a.scale_log2 < 0.f) {
 #pragma unroll
-        for (int hh = 0; hh < 2; ++hh)
+            for (int hh = 0; hh < 2; ++hh)
+                sc[hh] = -sc[hh];
+        }
+        if (!(nq == 16 && k0 + kSlots - 1 <= t0 && k0 > t_last - wnd)) {
+            const int rel0 = (int)(k0 - tq) + q4 * 4 + wnd - 1;
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int rel = rel0 + hh * 16 + r;
-                const bool ok = col < nq && rel <= 0 && rel > -a.window;
-                x[hh][r] = ok ? sc[hh][r] * a.scale_log2 : neg_inf;
-                mloc = fmaxf(mloc, x[hh][r]);
-            }
-        const float m_new = fmaxf(st.m, max_across_rows(mloc));
+            for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+                for (int r = 0; r < 4; ++r)
+                    if (!((uint32_t)(rel0 + hh * 16 + r) < win))
+                        sc[hh][r] = neg_inf;
+        }
+        const float mloc = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
+                                 fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        // the running maximum moves only when a step raises it by more than kLazyMax (log2
+        // units), so most steps skip the rescale; the weights exp2(x - m) stay below
+        // 2^kLazyMax, and the output and lse use the same m as the sums
+        const float m_row = fmaxf(st.m, max_across_rows(mloc) * scale_abs);
+        const float m_new = m_row > st.m + kLazyMax ? m_row : st.m;
         const bool any = m_new != neg_inf;
         const float alpha = any ? fast_exp2(st.m - m_new) : 1.0f;
+        const float m_sub = any ? -m_new : 0.f;  // masked scores stay -inf, their weights 0
         float pe[2][4];
         f2v pv[4];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
-                pe[hh][r] = any ? fast_exp2(x[hh][r] - m_new) : 0.f;
+                pe[hh][r] = fast_exp2(__builtin_fmaf(sc[hh][r], scale_abs, m_sub));
         // the weights PV uses are the bf16 ones; normalise by their sum too
 #pragma unroll
         for (int c = 0; c < 4; ++c)

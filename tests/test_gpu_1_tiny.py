@@ -262,6 +262,24 @@ def test_tiny_sliding_window_every_row(tiny, tiny_host, window):
     parity.check_attention(bits(out), o_ref, lse.cpu().numpy(), l_ref)
 
 
+@pytest.mark.parametrize("scale", [-0.3, 0.0, 0.4])
+def test_tiny_sliding_window_scales(tiny, tiny_host, scale):
+    """The sliding-window kernel applies the scale inside the exponent, after the maximum:
+    a negative scale (scores negated first), a zero scale (equal weights over the window)
+    and a large one, on every row against the oracle, at window 17 and 300."""
+    shape = WL.shape
+    t = np.arange(WL.T)
+    for window in (17, 300):
+        out = torch.empty_like(tiny["Q"])
+        lse = torch.empty((WL.T, shape.num_q_heads), dtype=torch.float32, device=DEV)
+        sgqa.swa_prefill(shape, tiny["Q"], tiny["K"], tiny["V"], tiny["G"], 0, WL.L, window,
+                         scale, out, lse)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.window_attention(bits(tiny["Q"]), t, tiny_host[0], tiny_host[1],
+                                               bits(tiny["G"]), window, scale)
+        parity.check_attention(bits(out), o_ref, lse.cpu().numpy(), l_ref)
+
+
 def test_tiny_sliding_window_chunk_mid_sequence(tiny, tiny_host):
     """Queries [300, 700) of a 700-token cache with a window of 64."""
     shape = WL.shape
