@@ -1256,8 +1256,10 @@ __global__ __launch_bounds__(kFilterNT) void k_fused_filter(FusedTopkArgs a)
     extern __shared__ __align__(16) uint16_t kb_tile[];  // [kTileB][P + 8], then the stage
     constexpr int ldt = P + 8;
     uint2 *stage = reinterpret_cast<uint2 *>(kb_tile + kTileB * ldt);  // [kFilterQ][kStage]
-    uint32_t *lcnt = reinterpret_cast<uint32_t *>(stage + kFilterQ * kStage);  // [kFilterQ]
-    uint32_t *gbase = lcnt + kFilterQ;                                         // [kFilterQ]
+    // [kFilterQ * kStage] row stages, then one trash entry per thread
+    const int trash = kFilterQ * kStage + (int)threadIdx.x;
+    uint32_t *lcnt = reinterpret_cast<uint32_t *>(stage + kFilterQ * kStage + kFilterNT);
+    uint32_t *gbase = lcnt + kFilterQ;  // [kFilterQ]
     const int s = blockIdx.z;
     const int i0 = blockIdx.x * kFilterQ;  // query tiles vary fastest: neighbouring workgroups
                                            // share their kb tiles in L2, their counters differ
@@ -1280,14 +1282,10 @@ __global__ __launch_bounds__(kFilterNT) void k_fused_filter(FusedTopkArgs a)
 #pragma unroll
     for (int kk = 0; kk < P / 32; ++kk)
         av[kk] = load16(qpr + kk * 32 + q4 * 8);
-    uint32_t thr[4];
-    int64_t cr[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) {
-        const int i = i0 + wave * 16 + q4 * 4 + r;
-        thr[r] = a.thr[(int64_t)s * a.nq + (i < a.nq ? i : i0)];
-        cr[r] = i < a.nq ? fused_c(a, s, i) : 0;
-    }
+    // this lane's query (col of the wave's 16): its threshold, candidate count and row
+    const int rl = wave * 16 + col;  // row within the workgroup
+    const uint32_t thr_row = a.thr[(int64_t)s * a.nq + (qrow < a.nq ? qrow : i0)];
+    const int64_t c_row = qrow < a.nq ? fused_c(a, s, qrow) : 0;
     constexpr int chunks = P / 8;
     constexpr int kPer = (kTileB * chunks + kFilterNT - 1) / kFilterNT;
     // a tile's kb rows are requested while the previous tile is computed
@@ -1320,65 +1318,77 @@ __global__ __launch_bounds__(kFilterNT) void k_fused_filter(FusedTopkArgs a)
             load_tile(j0 + kTileB);
         if (!wave_live)
             continue;
+        // Sᵀ: the tile's blocks as the MFMA rows, the wave's 16 queries as its columns, so lane
+        // (col, q4) holds the keys of query col at blocks j0 + 16 n + 4 q4 + r (each output is
+        // the same sum of the same 32-element products as in the score kernel)
         f32x4 acc[4];
 #pragma unroll
         for (int n = 0; n < 4; ++n)
             acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int kk = 0; kk < P / 32; ++kk) {
-            const bf16x8 af = as_bf16x8(av[kk]);
+            const bf16x8 qf = as_bf16x8(av[kk]);
 #pragma unroll
             for (int n = 0; n < 4; ++n) {
                 const u32x4 bv = *reinterpret_cast<const u32x4 *>(
                     kb_tile + (n * 16 + col) * ldt + kk * 32 + q4 * 8);
-                acc[n] = mfma_16x16x32(af, as_bf16x8(bv), acc[n]);
+                acc[n] = mfma_16x16x32(as_bf16x8(bv), qf, acc[n]);
             }
         }
-        // Lane (col, q4) holds the keys of rows 4 q4 + r at blocks j0 + 16 n + col: a row's
-        // keys of this tile sit in the 16 lanes of one q4, which count theirs, scan the counts,
-        // and reserve stage slots with one LDS atomic add (lane col 0).
+        // the query's keys >= its threshold among its candidate blocks (block < c): j0 + 16 n +
+        // 4 q4 + r < c, i.e. 16 n + r < lim
+        const int lim = (int)(c_row - j0) - 4 * q4;
+        uint32_t key[4][4];
+        int cnt = 0;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            const int rl = wave * 16 + q4 * 4 + r;  // row within the workgroup
-            uint32_t key[4];
-            int cnt = 0;
+        for (int n = 0; n < 4; ++n)
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const int64_t j = j0 + n * 16 + col;
-                key[n] = score_key(acc[n][r]);
-                cnt += (j < cr[r] && key[n] >= thr[r]) ? 1 : 0;
+            for (int r = 0; r < 4; ++r) {
+                key[n][r] = score_key(acc[n][r]);
+                cnt += (16 * n + r < lim && key[n][r] >= thr_row) ? 1 : 0;
             }
-            int inc = cnt;
-#pragma unroll
-            for (int o = 1; o < 16; o <<= 1) {
-                const int v = __shfl_up(inc, o, 16);
-                if (col >= o)
-                    inc += v;
-            }
-            const int tot = __shfl(inc, 15, 16);
-            if (tot == 0)
-                continue;  // uniform over the row's 16 lanes
+        // the query's 4 lanes (q4 = 0..3): exclusive prefix of their counts and the total
+        const int c1 = __shfl_xor(cnt, 16);
+        const int pair = cnt + c1;
+        const int c2 = __shfl_xor(pair, 32);
+        const int tot = pair + c2;
+        if (tot != 0) {  // (the same for the query's 4 lanes)
+            const int excl = ((q4 & 1) ? c1 : 0) + ((q4 & 2) ? c2 : 0);
             const int local = (int)lcnt[rl];
             const bool spill = local + tot > kStage;
             int base = 0;
-            if (spill && col == 0)
+            if (spill && q4 == 0)
                 base = (int)atomicAdd(&a.cnt[(int64_t)s * a.nq + i0 + rl], (uint32_t)tot);
-            base = spill ? __shfl(base, 0, 16) : local;
-            int slot = base + inc - cnt;
-            uint2 *list = a.cand + ((int64_t)s * a.nq + i0 + rl) * a.cap;
+            base = spill ? __shfl(base, col) : local;
+            int slot = base + excl;
+            if (!spill) {
+                // every key is written, the ones not kept to this lane's own trash entry, so
+                // the writes need no branches
 #pragma unroll
-            for (int n = 0; n < 4; ++n) {
-                const int64_t j = j0 + n * 16 + col;
-                if (j < cr[r] && key[n] >= thr[r]) {
-                    if (!spill)
-                        stage[rl * kStage + slot] = uint2{key[n], (uint32_t)j};
-                    else if (slot < a.cap)
-                        list[slot] = uint2{key[n], (uint32_t)j};
-                    ++slot;
-                }
+                for (int n = 0; n < 4; ++n)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        const bool keep = 16 * n + r < lim && key[n][r] >= thr_row;
+                        const uint32_t j = (uint32_t)j0 + (uint32_t)(16 * n + 4 * q4 + r);
+                        stage[keep ? rl * kStage + slot : trash] = uint2{key[n][r], j};
+                        slot += keep ? 1 : 0;
+                    }
+                if (q4 == 3)
+                    lcnt[rl] = (uint32_t)(local + tot);
+            } else {
+                uint2 *list = a.cand + ((int64_t)s * a.nq + i0 + rl) * a.cap;
+#pragma unroll
+                for (int n = 0; n < 4; ++n)
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) {
+                        if (16 * n + r < lim && key[n][r] >= thr_row) {
+                            const uint32_t j = (uint32_t)j0 + (uint32_t)(16 * n + 4 * q4 + r);
+                            if (slot < a.cap)
+                                list[slot] = uint2{key[n][r], j};
+                            ++slot;
+                        }
+                    }
             }
-            if (!spill && col == 0)
-                lcnt[rl] = (uint32_t)(local + tot);
         }
     }
     __syncthreads();
@@ -1791,7 +1801,7 @@ static void launch_fused_p(const FusedTopkArgs &a, hipStream_t stream)
     else
         hipLaunchKernelGGL(k_fused_threshold<64>, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0,
                            stream, a);
-    const size_t lds_f = lds + (size_t)kFilterQ * kStage * 8 + 2 * kFilterQ * 4;
+    const size_t lds_f = lds + (size_t)(kFilterQ * kStage + kFilterNT) * 8 + 2 * kFilterQ * 4;
     const unsigned fq = (unsigned)((a.nq + kFilterQ - 1) / kFilterQ);
     if (a.cap > 2048) {  // long rows keep few keys per block: longer spans per workgroup
         const int64_t span = (int64_t)kFilterTilesLong * kTileB;
