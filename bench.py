@@ -671,16 +671,16 @@ def measure_peaks():
     32x32x16 products in every SIMD) and streaming HBM reads (a 4 GiB buffer read once per
     pass), each checked against its closed-form result."""
     import torch
-    from long_context_sparse_18_amd import sgqa
+    from long_context_sparse_18_amd import probe
     cus = torch.cuda.get_device_properties(0).multi_processor_count
     waves, iters = cus * 4 * 8, 4096
     sink = torch.empty(waves, dtype=torch.float32, device="cuda")
-    sgqa.probe_mfma_bf16(sink, iters)
+    probe.probe_mfma_bf16(sink, iters)
     e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     mfma_tflops = 0.0
     for _ in range(3):
         e0.record()
-        sgqa.probe_mfma_bf16(sink, iters)
+        probe.probe_mfma_bf16(sink, iters)
         e1.record()
         torch.cuda.synchronize()
         mfma_tflops = max(mfma_tflops,
@@ -692,10 +692,10 @@ def measure_peaks():
     best = 0.0
     for blocks in (cus * 8, cus * 16, cus * 32):
         part = torch.empty(blocks, dtype=torch.int32, device="cuda")
-        sgqa.probe_read(buf, part)
+        probe.probe_read(buf, part)
         e0.record()
         for _ in range(5):
-            sgqa.probe_read(buf, part)
+            probe.probe_read(buf, part)
         e1.record()
         torch.cuda.synchronize()
         if int(part.to(torch.int64).sum().item()) & 0xFFFFFFFF != (nbytes // 4) & 0xFFFFFFFF:
@@ -708,11 +708,11 @@ def measure_peaks():
     g = torch.Generator(device="cuda").manual_seed(0)
     idx = torch.randint(0, rows, (n,), dtype=torch.int32, device="cuda", generator=g)
     part = torch.empty(cus * 16, dtype=torch.int32, device="cuda")
-    sgqa.probe_gather(table, idx, part)
+    probe.probe_gather(table, idx, part)
     gather = 0.0
     for _ in range(3):
         e0.record()
-        sgqa.probe_gather(table, idx, part)
+        probe.probe_gather(table, idx, part)
         e1.record()
         torch.cuda.synchronize()
         gather = max(gather, n * row_words * 4 / (e0.elapsed_time(e1) / 1e3) / 1e9)
@@ -756,14 +756,15 @@ def main():
         sys.exit(2)
 
     import torch
-    from long_context_sparse_18_amd import sgqa
+    from long_context_sparse_18_amd import probe, sgqa
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
-    if not os.path.exists(sgqa.lib_path()):
+    if not os.path.exists(sgqa.lib_path()) or not os.path.exists(probe.lib_path()):
         from long_context_sparse_18_amd import build as _b
         _b.build()
     sgqa.load()
+    probe.load()
 
     if args.copy_probe:
         src = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")
@@ -778,7 +779,7 @@ def main():
         waves, iters = cus * 4 * 8, 4096
         sink = torch.empty(waves, dtype=torch.float32, device="cuda")
         for _ in range(3):
-            sgqa.probe_mfma_bf16(sink, iters)
+            probe.probe_mfma_bf16(sink, iters)
         torch.cuda.synchronize()
         log(f"mfma probe: 3 x {waves} waves x {iters} x 8 bf16 32x32x16 products")
         return

@@ -1,4 +1,5 @@
-"""Build libsgqa.so for gfx950 with hipcc (in-tree, next to this file).
+"""Build libsgqa.so (the layer) and libsgqa_probe.so (the machine-peak probes the benchmark
+quotes its rooflines against) for gfx950 with hipcc, in-tree next to this file.
 
 Every HIP source is compiled with packed-fp32 instruction selection turned off
 (``-Xclang -target-feature -Xclang -packed-fp32-ops``); the host pass warns that
@@ -17,12 +18,14 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD_DIR = os.path.join(ROOT, "_build")
 LIB_PATH = os.path.join(PKG, "libsgqa.so")
+PROBE_LIB_PATH = os.path.join(PKG, "libsgqa_probe.so")
 
-SOURCES = ["k_index.hip", "k_indexer.hip", "k_attn.hip", "k_probe.hip", "sgqa_scratch.hip",
-           "sgqa_api.cpp"]
+SOURCES = ["k_index.hip", "k_indexer.hip", "k_attn.hip", "sgqa_scratch.hip", "sgqa_api.cpp"]
+PROBE_SOURCES = ["probe/k_probe.hip", "probe/probe_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
-COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", "-Wall", "-Wno-unused-function"]
+COMMON = ["-O3", "-std=c++17", "-fPIC", f"-I{INCLUDE}", f"-I{CSRC}", f"-I{os.path.join(CSRC, 'probe')}",
+          "-Wall", "-Wno-unused-function"]
 DEVICE_FLAGS = [f"--offload-arch={ARCH}", "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops"]
 
 
@@ -43,17 +46,24 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    """Compile every source and link ``libsgqa.so``; returns its path."""
-    os.makedirs(BUILD_DIR, exist_ok=True)
-    with concurrent.futures.ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), SOURCES))
-    tmp = LIB_PATH + ".tmp"
+def _link(objs, path: str) -> None:
+    tmp = path + ".tmp"
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"link failed: {' '.join(cmd)}\n{r.stderr}")
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, path)
+
+
+def build(verbose: bool = False) -> str:
+    """Compile every source and link ``libsgqa.so`` and ``libsgqa_probe.so``; returns the
+    path of ``libsgqa.so``."""
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    srcs = SOURCES + PROBE_SOURCES
+    with concurrent.futures.ThreadPoolExecutor(max_workers=len(srcs)) as ex:
+        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
+    _link(objs[:len(SOURCES)], LIB_PATH)
+    _link(objs[len(SOURCES):], PROBE_LIB_PATH)
     return LIB_PATH
 
 

@@ -2,7 +2,7 @@
 // loop and a streaming read.  Both produce results with a closed form, so a run that was
 // optimised away or read the wrong bytes is caught.
 #include "sgqa_device.hpp"
-#include "sgqa_launch.hpp"
+#include "probe_launch.hpp"
 
 namespace sgqa {
 

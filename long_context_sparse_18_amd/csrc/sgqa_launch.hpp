@@ -198,13 +198,6 @@ hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t stream);
 size_t attn_backward_workspace(int64_t T, int Hq, int d, int64_t nblk);
 int prefill_state_stride(int d);
 
-// Machine-peak probes (k_probe.hip).
-hipError_t launch_probe_mfma(int waves, int iters, float *sink, hipStream_t stream);
-hipError_t launch_probe_read(const void *buf, int64_t bytes, uint32_t *sink, int blocks,
-                             hipStream_t stream);
-hipError_t launch_probe_gather(const void *table, int row16, const int32_t *idx, int64_t n,
-                               uint32_t *sink, int blocks, hipStream_t stream);
-
 // Decode split-K geometry for k selected entries of B tokens.
 void decode_split_plan(int k, int B, int &nsplit, int &entries_per_split);
 // Partial states per (sequence, head) the decode attention writes for nsplit splits (one per

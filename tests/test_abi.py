@@ -6,17 +6,18 @@ import re
 
 import pytest
 
-from long_context_sparse_18_amd import REAL, TINY, sgqa
+from long_context_sparse_18_amd import REAL, TINY, probe, sgqa
 from long_context_sparse_18_amd.configs import with_selection
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "sgqa.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "sgqa_probe.h")
 
 FAKE = ctypes.c_void_p(1 << 20)  # aligned, never dereferenced: validation fails first
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(sgqa_[a-z0-9_]+)\s*\(", text)))
 
@@ -27,6 +28,18 @@ def test_library_exports_every_declared_symbol():
     assert set(names) == set(sgqa.EXPORTS), names
     for n in names:
         assert hasattr(lib, n), n
+
+
+def test_probe_library_exports_every_declared_symbol():
+    """The machine-peak probes live in libsgqa_probe.so, beside the layer's library, which
+    exports none of them."""
+    lib = probe.load()
+    names = declared_functions(PROBE_HEADER)
+    assert set(names) == set(probe.EXPORTS), names
+    for n in names:
+        assert hasattr(lib, n), n
+    for n in names:
+        assert not hasattr(sgqa.load(), n), n
 
 
 def test_status_strings():
@@ -222,7 +235,7 @@ def test_backward_validation():
 
 
 def test_probe_validation():
-    lib = sgqa.load()
+    lib = probe.load()
     sink = FAKE
     assert lib.sgqa_probe_mfma_bf16(0, 10, sink, None) == sgqa.ERR_SHAPE
     assert lib.sgqa_probe_mfma_bf16(64, 0, sink, None) == sgqa.ERR_SHAPE
@@ -243,6 +256,7 @@ def test_probe_validation():
     assert g(FAKE, 100, 384, FAKE, 10, sink, 0, None) == sgqa.ERR_SHAPE
     assert g(FAKE, 100, 384, None, 10, sink, 8, None) == sgqa.ERR_NULL
     assert g(ctypes.c_void_p((1 << 20) + 8), 100, 384, FAKE, 10, sink, 8, None) == sgqa.ERR_SHAPE
+    assert b"aligned" in lib.sgqa_probe_last_error()
 
 
 def test_decode_validation():

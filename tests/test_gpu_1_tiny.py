@@ -11,7 +11,7 @@ import torch
 import oracle
 import parity
 from gpu_layer import check_prefill_rows, run_prefill, say
-from long_context_sparse_18_amd import WORKLOADS, inputs, sgqa
+from long_context_sparse_18_amd import WORKLOADS, inputs, probe, sgqa
 from long_context_sparse_18_amd.configs import Workload, with_selection
 from long_context_sparse_18_amd.inputs import bits
 
@@ -643,7 +643,7 @@ def test_peak_probes():
     up to the buffer's 32-bit word sum mod 2^32, for a buffer that leaves a ragged tail over
     the grid stride and for a single 16-byte word."""
     sink = torch.full((37,), -1.0, dtype=torch.float32, device=DEV)
-    sgqa.probe_mfma_bf16(sink, 100)
+    probe.probe_mfma_bf16(sink, 100)
     torch.cuda.synchronize()
     assert torch.all(sink == 204800.0), sink
     g = torch.Generator(device=DEV).manual_seed(3)
@@ -651,7 +651,7 @@ def test_peak_probes():
         buf = torch.randint(-2 ** 31, 2 ** 31 - 1, (words,), dtype=torch.int32, device=DEV,
                             generator=g)
         part = torch.empty(96, dtype=torch.int32, device=DEV)
-        sgqa.probe_read(buf, part)
+        probe.probe_read(buf, part)
         torch.cuda.synchronize()
         want = int(buf.to(torch.int64).sum().item()) & 0xFFFFFFFF
         got = int(part.to(torch.int64).sum().item()) & 0xFFFFFFFF
@@ -662,7 +662,7 @@ def test_peak_probes():
                               device=DEV, generator=g)
         idx = torch.randint(0, 1000, (n,), dtype=torch.int32, device=DEV, generator=g)
         part = torch.empty(96, dtype=torch.int32, device=DEV)
-        sgqa.probe_gather(table, idx, part)
+        probe.probe_gather(table, idx, part)
         torch.cuda.synchronize()
         want = int(table.index_select(0, idx.long()).to(torch.int64).sum().item()) & 0xFFFFFFFF
         got = int(part.to(torch.int64).sum().item()) & 0xFFFFFFFF
