@@ -722,6 +722,150 @@ __global__ __launch_bounds__(512) void k_attn_prefill(AttnArgs a)
         save_state<D>(st, a.state + state_offset(a, r, g));
 }
 
+// ---- resident prefill: the history ranges of the sliced prefill in one launch ------------
+// The sliced prefill parks every row's softmax state between its range launches (13 KB per row
+// and group each way) and reloads its query.  Here a persistent grid of exactly the resident
+// workgroups keeps each row's state in the wave's registers across the ranges: the waves of one
+// XCD take a batch of nw_x consecutive rows of the XCD's KV group (the R = 8 / Hkv XCDs of a
+// group split the group's batch of R * nw_x rows), attend range 0 of all of them, then range 1,
+// and so on, and move to their next batch.  Between ranges a wave waits, up to a bounded time,
+// until most waves of its XCD have finished the previous range, so the XCD's L2 holds one
+// range of its group's K/V rows at a time; the wait only orders the work for the caches (it
+// guards no data), so a wave that stops waiting at the bound still computes the same result.
+// Each row attends the same entries per range, in the same steps, as in the sliced launches,
+// so its bits equal the sliced prefill's.
+constexpr int kResidentRanges = 16;  // ranges of the longest history the resident prefill takes
+constexpr int kResidentSpin = 4096;  // polls per wait (a few ms) before a wave goes on anyway
+// A wave starts range s once three quarters of its XCD's waves of the batch have finished range
+// s - 1 (waiting for more lets the slowest rows hold everyone up; for fewer, the L2 holds
+// two ranges).  128K prefill, range width x share waited for: 2560 blocks x 3/4 111.3 ms,
+// x 2/3 111.6, x 4/5 112.2, x 1/2 139.8 (3072 blocks); 2048 x 3/4 116.0; 1024 x 3/4 137.4
+// x 15/16 145.7; 4096 x 3/4 123.3; waiting for the range before the previous one, 157.5.
+constexpr int kResidentSlack = 4;     // a wave waits for all but 1/slack of them
+
+// Entries of `row` (nvalid ascending blocks, -1 past the valid ones) below block `lim`.
+__device__ __forceinline__ int entries_below(const int32_t *row, int nvalid, int64_t lim)
+{
+    const int lane = threadIdx.x & 63;
+    int n = 0;
+    for (int e0 = 0; e0 < nvalid; e0 += 256) {  // four loads in flight per lane
+        int32_t b[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const int e = e0 + u * 64 + lane;
+            b[u] = row[e < nvalid ? e : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            const bool in = e0 + u * 64 + lane < nvalid && b[u] >= 0;
+            n += (in && b[u] < lim) ? 1 : 0;
+        }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1)
+        n += __shfl_xor(n, o);
+    return n;
+}
+
+// A wave-uniform value kept in scalar registers.
+__device__ __forceinline__ int uni(int v)
+{
+    return __builtin_amdgcn_readfirstlane(v);
+}
+__device__ __forceinline__ int64_t uni(int64_t v)
+{
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+// Progress words of an XCD's waves: wave i stores, after each range it finishes, the number
+// of ranges it has finished since the launch (each wave its own word, so no two waves write
+// the same address).  A wave waits, up to kResidentSpin polls, until at least `need` of the
+// nw words reach `target`.
+__device__ __forceinline__ void resident_wait(const uint32_t *prog, int nw, uint32_t target,
+                                              int need)
+{
+    const int lane = threadIdx.x & 63;
+    for (int i = 0; i < kResidentSpin; ++i) {
+        int n = 0;
+        for (int w = lane; w < nw; w += 64)
+            n += __hip_atomic_load(prog + w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >= target
+                     ? 1
+                     : 0;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1)
+            n += __shfl_xor(n, o);
+        if (uni(n) >= need)
+            return;
+        __builtin_amdgcn_s_sleep(8);
+    }
+}
+
+// a.state: one progress word per wave (8 XCDs x 4 a.slice, zero at launch); a.slice: the
+// workgroups of one XCD (the grid is 8 times that); a.slice_blocks: the range width W, every
+// row's history within kResidentRanges ranges.
+template <int D>
+__global__ __launch_bounds__(512) void k_attn_prefill_resident(AttnArgs a)
+{
+    extern __shared__ __align__(16) uint16_t lds[];
+    const int wave = wave_index();
+    const int hpg = a.Hq / a.Hkv;
+    const int R = 8 / a.Hkv;                 // XCDs per KV group
+    const int x = blockIdx.x & 7;            // this workgroup's XCD
+    const int g = x / R, h = x % R;
+    const int nw_x = a.slice * 4;            // waves per XCD
+    const int lw = (int)(blockIdx.x >> 3) * 4 + wave;
+    const int64_t W = a.slice_blocks;
+    uint32_t *prog = reinterpret_cast<uint32_t *>(a.state) + (int64_t)x * nw_x;
+    const int64_t per_batch = (int64_t)R * nw_x;
+    uint32_t done = 0;                       // ranges of the earlier batches
+    for (int64_t b = 0; b * per_batch < a.rows; ++b) {
+        // this XCD's rows of the batch, longest history first
+        const int64_t j0 = b * per_batch + (int64_t)h * nw_x;
+        const int64_t left = (int64_t)a.rows - j0;
+        const int nval = (int)(left < 0 ? 0 : (left < nw_x ? left : nw_x));
+        const int64_t c_max = (a.q_start + (int64_t)a.rows - 1 - b * per_batch) / a.B;
+        const int S = (int)(c_max / W) + 1;  // ranges of the batch (its longest row)
+        const bool live = lw < nval;
+        const int64_t r = uni((int64_t)a.rows - 1 - (j0 + lw));
+        const int64_t t = a.q_start + r;
+        const int64_t c = uni(live ? t / a.B : (int64_t)0);
+        const int nvalid = (int)((c + 1 < a.k) ? c + 1 : a.k);
+        const int last = uni((int)(c / W));
+        const bool sliced = c >= 2 * (int64_t)a.k;
+        const int32_t *row = a.idx + (live ? r : 0) * a.k;
+        const int first_slice = uni(live && sliced ? (int)((int64_t)row[0] / W) : last);
+        WaveState<D> st;
+        init_state<D>(st);
+        int e_lo = 0;
+        for (int s = 0; s < S; ++s) {
+            // most of the XCD's waves of this batch are done with range s - 1
+            if (s > 0 && nval > 0)
+                resident_wait(prog, nw_x, done + (uint32_t)s, nval - nval / kResidentSlack);
+            if (live && s >= first_slice && s <= last) {
+                const int e_hi =
+                    uni(s == last ? nvalid : entries_below(row, nvalid, (int64_t)(s + 1) * W));
+                if (e_hi > e_lo) {
+                    bf16x8 qf[D / 32];
+                    load_q<D>(a.q + (r * a.Hq + (int64_t)g * hpg) * D, hpg, qf);
+                    const SparseTokens src{row, e_lo, e_hi, t, c, a.B, entry_window<D>(lds)};
+                    attend_range<D>(Bf16Rows{a.kc + (int64_t)g * D, a.vc + (int64_t)g * D},
+                                    a.Hkv, src, QRegs<D>{qf}, a.scale_log2,
+                                    lds + wave * attn_vbuf_elems(D), st);
+                }
+                e_lo = e_hi;
+            }
+            if (live && (threadIdx.x & 63) == 0)
+                __hip_atomic_store(prog + lw, done + (uint32_t)s + 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (live)
+            store_row<D>(st, a, r, g, hpg);
+        done += (uint32_t)S;
+    }
+}
+
 typedef __attribute__((ext_vector_type(2))) float f2v;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
 
@@ -1212,6 +1356,82 @@ static hipError_t launch_decode_d(const AttnArgs &a0, hipStream_t stream)
     return hipGetLastError();
 }
 
+__global__ __launch_bounds__(256) void k_zero_u32(uint32_t *p, int n)
+{
+    const int i = (int)(blockIdx.x * blockDim.x + threadIdx.x);
+    if (i < n)
+        p[i] = 0u;
+}
+
+// The resident prefill over rows [0, a0.rows), whose histories span at most kResidentRanges
+// ranges of a0.resident_blocks blocks: one launch of as many workgroups as are resident at
+// once (occupancy x CUs), after a fill kernel clears the waves' progress words in the
+// workspace.  Returns hipErrorNotSupported when the workspace cannot hold the progress words.
+template <int D>
+static hipError_t launch_prefill_resident(const AttnArgs &a0, hipStream_t stream)
+{
+    const size_t lds = (size_t)4 * attn_wave_lds(D);
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_attn_prefill_resident<D>, 256,
+                                                         lds);
+    if (e != hipSuccess)
+        return e;
+    const int per_xcd = per_cu * (cus / 8);
+    const int words = 8 * per_xcd * 4;  // one progress word per wave
+    if (per_xcd < 1 || a0.state_bytes < (int64_t)words * (int64_t)sizeof(uint32_t))
+        return hipErrorNotSupported;
+    AttnArgs a = a0;
+    a.slice = per_xcd;
+    a.slice_blocks = a0.resident_blocks;
+    uint32_t *prog = reinterpret_cast<uint32_t *>(a.state);
+    hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                       prog, words);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_attn_prefill_resident<D>, dim3((unsigned)(8 * per_xcd)), dim3(256), lds,
+                       stream, a);
+    return hipGetLastError();
+}
+
+// With a workspace: the rows whose histories span at most kResidentRanges resident ranges
+// (a prefix of the rows) go to the resident prefill when the KV groups divide the 8 XCDs, the
+// others to the sliced launches; which path a row takes depends only on its own history.
+template <int D>
+static hipError_t launch_prefill_ws(const AttnArgs &a0, hipStream_t stream)
+{
+    int64_t n_res = 0;
+    if (a0.resident_blocks > 0 && 8 % a0.Hkv == 0) {
+        // c + 1 <= kResidentRanges * W  <=>  q_start + r < kResidentRanges * W * B
+        const int64_t lim = (int64_t)kResidentRanges * a0.resident_blocks * a0.B - a0.q_start;
+        n_res = lim < 0 ? 0 : (lim < a0.rows ? lim : a0.rows);
+    }
+    if (n_res > 0) {
+        AttnArgs a = a0;
+        a.rows = (int32_t)n_res;
+        hipError_t e = launch_prefill_resident<D>(a, stream);
+        if (e == hipErrorNotSupported)
+            n_res = 0;  // the sliced launches take every row
+        else if (e != hipSuccess)
+            return e;
+    }
+    if (n_res == a0.rows)
+        return hipSuccess;
+    AttnArgs a = a0;
+    const int64_t r0 = n_res;
+    a.rows = (int32_t)(a0.rows - r0);
+    a.q_start = a0.q_start + r0;
+    a.q = a0.q + r0 * a0.Hq * D;
+    a.gate = a0.gate + r0 * a0.Hq;
+    a.idx = a0.idx + r0 * a0.k;
+    a.out = a0.out + r0 * a0.Hq * D;
+    a.lse = a0.lse ? a0.lse + r0 * a0.Hq : nullptr;
+    return launch_prefill_sliced<D>(a, stream);
+}
+
 hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream)
 {
     if (a.rows <= 0)
@@ -1220,9 +1440,9 @@ hipError_t launch_attn_prefill(const AttnArgs &a, hipStream_t stream)
         return hipErrorInvalidValue;  // never launch without the tensors the kernels touch
     if (a.slice_blocks > 0) {
         switch (a.d) {
-        case 64: return launch_prefill_sliced<64>(a, stream);
-        case 128: return launch_prefill_sliced<128>(a, stream);
-        case 192: return launch_prefill_sliced<192>(a, stream);
+        case 64: return launch_prefill_ws<64>(a, stream);
+        case 128: return launch_prefill_ws<128>(a, stream);
+        case 192: return launch_prefill_ws<192>(a, stream);
         default: return hipErrorInvalidValue;
         }
     }

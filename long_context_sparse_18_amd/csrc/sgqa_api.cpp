@@ -155,6 +155,12 @@ constexpr int kPrefillLongSlices = SGQA_LONG_SLICES;
 // Blocks per history slice of the sliced prefill attention, in units of k/2 (2k: 1024 blocks
 // at the real shape).
 constexpr int64_t kPrefillSliceHalfK = SGQA_SLICE_HALF_K;
+#ifndef SGQA_RESIDENT_HALF_K
+#define SGQA_RESIDENT_HALF_K 10
+#endif
+// Blocks per history range of the resident prefill, in units of k/2 (5k: 2560 blocks at the
+// real shape; 0 turns the resident prefill off).
+constexpr int64_t kPrefillResidentHalfK = SGQA_RESIDENT_HALF_K;
 
 } // namespace
 
@@ -558,6 +564,11 @@ sgqa_status sgqa_sparse_attn_prefill(const sgqa_dims *dims, const sgqa_bf16 *q,
         if (workspace_bytes < row_state)
             return fail(SGQA_ERR_WORKSPACE, "prefill workspace needs >= %zu bytes, got %zu",
                         row_state, workspace_bytes);
+        // With a workspace, rows whose histories span at most 16 resident ranges are attended by
+        // the resident prefill (one launch; each XCD's waves take a batch of rows through the
+        // ranges together, so the L2 holds one range at a time, and keep their state in
+        // registers: 111 against 121 ms for the 128K prefill), the other rows by the sliced
+        // launches.
         // History slices of W = kPrefillSliceHalfK * k / 2 blocks: each launch's rows gather from
         // one such range of the cache, which each XCD's L2 holds for its KV group, while every
         // slice boundary a row crosses parks ~13 KB of state per group.  Short histories gain
@@ -569,6 +580,9 @@ sgqa_status sgqa_sparse_attn_prefill(const sgqa_dims *dims, const sgqa_bf16 *q,
         const int64_t W = (kPrefillSliceHalfK * dims->topk_blocks + 1) / 2;
         a.slice_blocks = max_cand >= 2 * (int64_t)dims->topk_blocks ? W : 0;
         a.long_slices = kPrefillLongSlices;
+        // the resident prefill (one launch, the state in registers across the ranges) takes
+        // the rows whose histories span at most 16 of its ranges
+        a.resident_blocks = (kPrefillResidentHalfK * dims->topk_blocks + 1) / 2;
         a.state = static_cast<float *>(workspace);
         a.state_bytes = (int64_t)workspace_bytes;
         a.state_stride = sgqa::prefill_state_stride(a.d);

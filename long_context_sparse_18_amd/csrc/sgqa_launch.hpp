@@ -157,6 +157,9 @@ struct AttnArgs {
     // (state_stride floats per lane) in `state` between launches
     int64_t slice_blocks;
     int32_t long_slices;     // ranges of a history longer than 16 slice_blocks ranges
+    // resident prefill (one launch, the state kept in registers across the ranges): range
+    // width in blocks for rows whose history spans at most 16 such ranges (0: not used)
+    int64_t resident_blocks;
     int32_t slice;
     float *state;
     int64_t state_bytes;

@@ -106,6 +106,35 @@ def test_tiny_layer_schedule_same_bits(tiny, chunks):
     assert torch.equal(lse, ref["lse"]) and torch.equal(kb, ref["kb"])
 
 
+def test_prefill_resident_and_long_rows_in_one_call():
+    """With a workspace, rows whose histories span at most 16 ranges of 5k blocks (here
+    16 x 80 blocks = 10240 tokens) take the resident prefill and the longer ones the sliced
+    launches (one pass each).  A call over 12288 rows uses both; calls over row chunks that cut
+    across that boundary and elsewhere give the same bits, and rows on both sides of it match
+    the oracle."""
+    shape = WL.shape
+    wl = Workload("tiny-12k", shape, nseq=1, T=12288, L=12288, q_start=0)
+    say("resident + long rows: generating")
+    d = inputs.make_prefill(wl, 11, DEV)
+    ws = torch.empty(sgqa.workspace_bytes(sgqa.OP_ATTN_PREFILL, shape, 1, wl.T, wl.L),
+                     dtype=torch.uint8, device=DEV)
+    res = run_prefill(shape, d, 0, wl.L, attn_workspace=ws)
+    out = torch.full_like(res["out"], 7.0)
+    lse = torch.full_like(res["lse"], 7.0)
+    scale = 1.0 / math.sqrt(shape.head_dim)
+    bounds = [0, 3001, 10239, 10241, 12288]
+    for r0, r1 in zip(bounds[:-1], bounds[1:]):
+        sgqa.sparse_attn_prefill(shape, d["Q"][r0:r1], d["K"], d["V"], d["G"][r0:r1],
+                                 res["idx"][r0:r1], r0, wl.L, scale, out[r0:r1], lse[r0:r1],
+                                 workspace=ws)
+    torch.cuda.synchronize()
+    assert torch.equal(out, res["out"]) and torch.equal(lse, res["lse"])
+    rows = np.array([0, 7, 1000, 5000, 10230, 10238, 10239, 10240, 10241, 10250, 12000, 12287])
+    st = check_prefill_rows(shape, d, res, 0, rows)
+    say(f"resident + long rows: {st}")
+    assert st["exact_iso"] >= len(rows) - 1
+
+
 def test_tiny_deterministic(tiny):
     a = run_prefill(WL.shape, tiny, 0, WL.L)
     b = run_prefill(WL.shape, tiny, 0, WL.L)
