@@ -67,18 +67,18 @@ PREFILL_CHUNKS = 8
 
 
 def prefill_launches(wl) -> str:
-    """How one sgqa_sparse_attn_prefill call over all rows of the workload is dispatched: row
-    chunks of the workspace's 32768 rows, each in one launch per 2k-block range of history up
-    to its last own block (at most 16 ranges)."""
+    """How one sgqa_sparse_attn_prefill call over all rows of the workload is dispatched: every
+    row's history spans at most 16 ranges of 5k blocks, so the call is one fill kernel and one
+    persistent launch of the resident workgroups (2 of 4 waves per CU at 256 registers per
+    wave), each XCD's 256 waves taking batches of 256 rows of its KV group through the ranges."""
     s = wl.shape
-    W, chunk = 2 * s.topk_blocks, min(32768, wl.T)
-    per = []
-    for r0 in range(0, wl.T, chunk):
-        c_last = (wl.q_start + min(wl.T, r0 + chunk) - 1) // s.block_size
-        per.append(min(c_last // W + 1, 16))
-    return (f"one sgqa_sparse_attn_prefill call over all {wl.T} rows: {len(per)} row chunks, "
-            f"each in one launch per {W}-block history range "
-            f"({' + '.join(map(str, per))} = {sum(per)} dispatches)")
+    W = 5 * s.topk_blocks
+    per_batch = 8 // s.num_kv_heads * 256
+    batches = -(-wl.T // per_batch)
+    ranges = ((wl.q_start + wl.T - 1) // s.block_size) // W + 1
+    return (f"one sgqa_sparse_attn_prefill call over all {wl.T} rows: a fill kernel, then one "
+            f"persistent launch of 512 workgroups taking {batches} batches of {per_batch} rows "
+            f"per KV group through up to {ranges} history ranges of {W} blocks")
 
 
 def bench_prefill(steps: int, warmup: int):
@@ -867,7 +867,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": attn_tflops, "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": attn_tflops / PEAK_BF16_TFLOPS,
                      "traffic": traffic,
-                     "kernel": "k_attn_prefill<192>",
+                     "kernel": "k_attn_prefill_resident<192>",
                      "launch": prefill_launches(wl),
                      "algorithmic_flops": pre["attn_flops"],
                      "flops_per_attended_pair": 4 * s.head_dim * s.num_q_heads,
