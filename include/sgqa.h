@@ -168,18 +168,25 @@ sgqa_status sgqa_indexer_topk(const sgqa_dims *dims, const sgqa_bf16 *qp, int64_
  * Only the first min(k, c+1) entries of each idx row are read; entries that
  * are -1 or outside [0, c] are skipped.
  * With a workspace (optional) the selected blocks of each query whose own block
- * c is at least 2k are visited in several launches, each over one slice of its
- * history, so that each XCD's L2 holds a smaller working set; the softmax state
- * is carried exactly between launches.  Whether a row is sliced depends only on
- * its own c, so every workspace size, and every split of the rows over calls,
- * gives the same bits; a call without a workspace differs from them only in the
- * order of fp32 additions.  Rows are processed in chunks that fit the workspace.
+ * c is at least 2k are visited one history range at a time, so that each XCD's
+ * L2 holds a smaller working set, with the softmax state carried exactly from
+ * range to range.  When the KV groups divide the 8 XCDs, rows whose history spans
+ * at most 16 ranges of 5k blocks are attended by one persistent launch whose
+ * waves keep their state in registers and step through the ranges together (it
+ * uses the first bytes of the workspace for one progress word per wave); the
+ * other rows are attended in launches of one 2k-block range each, parking the
+ * state in the workspace in row chunks that fit it.  Which ranges a row takes
+ * depends only on its own c (and the shape), so every workspace size, and every
+ * split of the rows over calls, gives the same bits; a call without a workspace
+ * differs from them only in the order of fp32 additions.
  *   q     [dev] [T][Hq][d] bf16        k_cache, v_cache [dev] [L][Hkv][d] bf16
  *   gate  [dev] [T][Hq] bf16 logits    idx [dev] [T][k] int32 (as produced above)
  *   out   [dev] [T][Hq][d] bf16        lse [dev] [T][Hq] fp32, may be NULL
  *   workspace [dev] NULL, or >= sgqa_workspace_bytes(SGQA_OP_ATTN_PREFILL, dims,
- *                   1, 1, L) bytes (one row); sgqa_workspace_bytes with T rows
- *                   gives the size for a single chunk
+ *                   1, 1, L) bytes (one row of parked state, and at least the
+ *                   persistent launch's progress words); sgqa_workspace_bytes
+ *                   with T rows gives the size for a single row chunk
+ *   Calls that overlap on one device must use different workspaces.
  * Requires q_start + T <= L.
  */
 sgqa_status sgqa_sparse_attn_prefill(const sgqa_dims *dims, const sgqa_bf16 *q,
@@ -350,7 +357,8 @@ sgqa_status sgqa_sparse_attn_decode_fp8(const sgqa_dims *dims, const sgqa_bf16 *
  * SGQA_OP_ATTN_PREFILL) given nseq sequences of T queries and caches of at
  * most Lmax tokens.  For the indexer this is the size that lets one pass cover
  * all rows, capped at 2 GiB; smaller buffers (down to one 64-row pass) also
- * work.  For the prefill attention it is the state of min(T, 32768) rows.
+ * work.  For the prefill attention it is the parked state of min(T, 32768) rows,
+ * and at least 32 KiB (the persistent launch's progress words).
  * Returns 0 for invalid arguments.
  */
 size_t sgqa_workspace_bytes(int op, const sgqa_dims *dims, int32_t nseq, int32_t T, int64_t Lmax);

@@ -221,9 +221,13 @@ size_t sgqa_workspace_bytes(int op, const sgqa_dims *dims, int32_t nseq, int32_t
     if (op == SGQA_OP_ATTN_PREFILL) {
         if (check_dims(dims, true, false) != SGQA_OK)
             return 0;
+        // the state of min(T, 32768) rows for the sliced launches, and at least the resident
+        // prefill's progress words (one per resident wave: at most 8 workgroups of 4 waves per
+        // CU on 256 CUs)
         const int64_t rows = T < 1 ? 1 : (T > 32768 ? 32768 : T);
-        return (size_t)rows * dims->num_kv_heads * 64 * sgqa::prefill_state_stride(dims->head_dim) *
-               sizeof(float);
+        const size_t state = (size_t)rows * dims->num_kv_heads * 64 *
+                             sgqa::prefill_state_stride(dims->head_dim) * sizeof(float);
+        return state > sgqa::kResidentProgressBytes ? state : sgqa::kResidentProgressBytes;
     }
     if (op == SGQA_OP_ATTN_BACKWARD) {
         if (check_dims(dims, true, false) != SGQA_OK || nseq != 1)

@@ -201,6 +201,10 @@ hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t stream);
 size_t attn_backward_workspace(int64_t T, int Hq, int d, int64_t nblk);
 int prefill_state_stride(int d);
 
+// Workspace the resident prefill needs for its progress words: one 4-byte word per resident
+// wave, at most 8 workgroups of 4 waves per CU on 256 CUs.
+constexpr size_t kResidentProgressBytes = size_t(256) * 8 * 4 * sizeof(uint32_t);
+
 // Decode split-K geometry for k selected entries of B tokens.
 void decode_split_plan(int k, int B, int &nsplit, int &entries_per_split);
 // Partial states per (sequence, head) the decode attention writes for nsplit splits (one per

@@ -324,6 +324,13 @@ def test_workspace_sizes():
     assert ws == 16 * 32 * 64 * (192 + 3) * 4
     assert sgqa.workspace_bytes(sgqa.OP_ATTN_DECODE, with_selection(TINY, 8, 16), 1, 1, 1024) > 0
     assert sgqa.workspace_bytes(7, REAL, 1, 1, 1) == 0
+    # prefill attention: the parked state of min(T, 32768) rows (4 groups x 64 lanes x 52
+    # floats each at d = 192), and at least the resident prefill's progress words (one 4-byte
+    # word per resident wave: 256 CUs x 8 workgroups x 4 waves)
+    assert sgqa.workspace_bytes(sgqa.OP_ATTN_PREFILL, REAL, 1, 1, 1 << 17) == 4 * 64 * 52 * 4
+    assert sgqa.workspace_bytes(sgqa.OP_ATTN_PREFILL, REAL, 1, 1 << 17, 1 << 17) == \
+        32768 * 4 * 64 * 52 * 4
+    assert sgqa.workspace_bytes(sgqa.OP_ATTN_PREFILL, TINY, 1, 1, 1024) == 256 * 8 * 4 * 4
 
 
 def test_swa_validation():
