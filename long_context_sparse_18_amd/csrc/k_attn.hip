@@ -869,6 +869,42 @@ __global__ __launch_bounds__(512) void k_attn_prefill_resident(AttnArgs a)
 typedef __attribute__((ext_vector_type(2))) float f2v;
 typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
 
+// O^T += V^T P^T for one 32-position step of the sliding-window kernel (V rows [slot][kLd] at
+// `vs`): the transposing reads of two MFMA operands are issued together and waited for inside
+// the asm block.  Written as asm because the compiler has no memory-operand information for
+// the ds_read_b64_tr_b16 builtin and so waits for every global-to-LDS copy in flight, the
+// next tile's included, before the first of them; these reads only touch the current tile.
+template <int D, int kLd>
+__device__ __forceinline__ void swa_pv_step(const uint16_t *vs, bf16x8 pf, f32x4 (&acc)[D / 16])
+{
+    static_assert((D / 16) % 2 == 0 && (D / 16 - 1) * 32 + 64 * kLd < 65536, "ds offsets");
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    // tr_quad's address for d0 = 0; d0 and the second 16 slots are immediate offsets
+    const uint16_t *p = vs + (q4 * 4 + (col >> 2)) * kLd + 4 * (col & 3);
+    const uint32_t addr =
+        (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint16_t *)p;
+    typedef __attribute__((ext_vector_type(8))) short s16x8;
+#pragma unroll
+    for (int mt = 0; mt < D / 16; mt += 2) {
+        s16x4 a0, a1, b0, b1;
+        asm volatile(
+            "ds_read_b64_tr_b16 %0, %4 offset:%5\n\t"
+            "ds_read_b64_tr_b16 %1, %4 offset:%6\n\t"
+            "ds_read_b64_tr_b16 %2, %4 offset:%7\n\t"
+            "ds_read_b64_tr_b16 %3, %4 offset:%8\n\t"
+            "s_waitcnt lgkmcnt(0)"
+            : "=&v"(a0), "=&v"(a1), "=&v"(b0), "=&v"(b1)
+            : "v"(addr), "i"(mt * 32), "i"(mt * 32 + 32 * kLd), "i"(mt * 32 + 32),
+              "i"(mt * 32 + 32 + 32 * kLd)
+            : "memory");
+        const s16x8 va = __builtin_shufflevector(a0, a1, 0, 1, 2, 3, 4, 5, 6, 7);
+        const s16x8 vb = __builtin_shufflevector(b0, b1, 0, 1, 2, 3, 4, 5, 6, 7);
+        acc[mt] = mfma_16x16x32(__builtin_bit_cast(bf16x8, va), pf, acc[mt]);
+        acc[mt + 1] = mfma_16x16x32(__builtin_bit_cast(bf16x8, vb), pf, acc[mt + 1]);
+    }
+}
+
 // Gated sliding-window attention, query-tiled: neighbouring queries share all but one of
 // their window positions, so a workgroup takes 16 consecutive queries of one KV group and each
 // 32-position step of the group's K and V rows is staged once in LDS for all of them.  One wave
@@ -918,6 +954,8 @@ __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
         u32x4 v = {0u, 0u, 0u, 0u};
         if (col < nq)
             v = load16(a.q + ((r0 + col) * a.Hq + h) * D + kk * 32 + q4 * 8);
+        if (a.scale_log2 < 0.f)
+            v ^= 0x80008000u;  // -q, so the scores come out negated (exactly)
         qf[kk] = as_bf16x8(v);
     }
     WaveState<D> st;
@@ -934,34 +972,35 @@ __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
     constexpr int kTilePieces = 2 * kSlots * kPpr;
     // K pieces fill whole instructions, so each instruction reads only K or only V rows
     static_assert((kSlots * kPpr) % 64 == 0, "whole instructions");
-    // this lane's piece of the wave's first kPre DMA instructions (the same every step): the
-    // row within the step (low 8 bits) and the byte offset of the piece within the row's group
-    // part (the bits above); the step's first row and K or V come from a wave-uniform base
+    // The wave's first kPre DMA instructions (i = wave + u * nwaves), described once: this
+    // lane's byte offset from the step's first row, voff = row * row_bytes + piece offset
+    // (the step's first row and K or V come from a wave-uniform base).  Rows past t_last
+    // (only in the last step; they are masked below) must not be read: the offset is capped
+    // at the last piece of the group's part of row t_last, which every larger offset exceeds.
     constexpr int kPre = 4;
+    constexpr int kInstr = kTilePieces / 64;
     const uint32_t row_bytes = (uint32_t)(row_elems * sizeof(uint16_t));
-    uint32_t dpiece[kPre];
+    uint32_t voff[kPre];
 #pragma unroll
     for (int u = 0; u < kPre; ++u) {
         const int i = wave + u * nwaves;
-        const int pc = (i < kTilePieces / 64 ? i : 0) * 64 + lane;
+        const int pc = (i < kInstr ? i : 0) * 64 + lane;
         const int rem = pc % (kSlots * kPpr);
         const int slot = rem / kPpr, piece = rem - slot * kPpr;
-        dpiece[u] = (uint32_t)slot | ((uint32_t)(piece < D / 8 ? piece : 0) * 16u << 8);
+        voff[u] = (uint32_t)slot * row_bytes + (uint32_t)(piece < D / 8 ? piece : 0) * 16u;
     }
     auto dma = [&](int step, uint16_t *buf) {
         const int64_t k0 = ks0 + (int64_t)step * kSlots;
-        // rows past t_last (only in the last step) reload row t_last; they are masked below
-        const uint32_t last_rel = (uint32_t)(t_last - k0);
+        const uint32_t cap = (uint32_t)(t_last - k0) * row_bytes + (uint32_t)(D * 2 - 16);
+        const int64_t roff = k0 * row_elems + g * D;
+        const char *kb = reinterpret_cast<const char *>(a.kc + roff);
+        const char *vb = reinterpret_cast<const char *>(a.vc + roff);
 #pragma unroll
         for (int u = 0; u < kPre; ++u) {
             const int i = wave + u * nwaves;
-            if (i < kTilePieces / 64) {
-                const bool is_v = i * 64 >= kSlots * kPpr;
-                const char *base = reinterpret_cast<const char *>((is_v ? a.vc : a.kc) +
-                                                                  k0 * row_elems + g * D);
-                const uint32_t slot = dpiece[u] & 0xffu;
-                const uint32_t off = (slot < last_rel ? slot : last_rel) * row_bytes +
-                                     (dpiece[u] >> 8);
+            if (i < kInstr) {
+                const char *base = i * 64 >= kSlots * kPpr ? vb : kb;
+                const uint32_t off = voff[u] < cap ? voff[u] : cap;
                 __builtin_amdgcn_global_load_lds(
                     (const void __attribute__((address_space(1))) *)(base + off),
                     (void __attribute__((address_space(3))) *)(buf + i * 64 * 8), 16, 0, 0);
@@ -983,6 +1022,17 @@ __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
                 (void __attribute__((address_space(3))) *)(buf + i * 64 * 8), 16, 0, 0);
         }
     };
+    // steps whose every position lies in every query's window (k0 + 31 <= t0 and
+    // k0 > t_last - wnd, with all 16 queries present) skip the mask
+    int full0 = 0, full1 = -1;
+    if (nq == 16) {
+        const int64_t lo = t_last - wnd + 1 - ks0, hi = t0 - (kSlots - 1) - ks0;
+        full0 = lo <= 0 ? 0 : (int)((lo + kSlots - 1) / kSlots);
+        full1 = hi < 0 ? -1 : (int)(hi / kSlots);
+    }
+    full0 = __builtin_amdgcn_readfirstlane(full0);
+    full1 = __builtin_amdgcn_readfirstlane(full1);
+    const float pinf = opaque_pinf();
     dma(0, lds);
     __builtin_amdgcn_s_waitcnt(0);  // this wave's rows have landed in LDS
     __syncthreads();
@@ -1012,13 +1062,8 @@ __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
         // rel = position - query must lie in [1 - window, 0], i.e. rel + window - 1 in
         // [0, win) as an unsigned compare (win = 0 for the lanes of absent queries), and the
         // other scores become -inf.  The scale is applied with the exponent's subtraction
-        // (scores negated first for a negative scale, so the maximum commutes with it).
-        if (a.scale_log2 < 0.f) {
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh)
-                sc[hh] = -sc[hh];
-        }
-        if (!(nq == 16 && k0 + kSlots - 1 <= t0 && k0 > t_last - wnd)) {
+        // (with a negative scale the query was negated, so the maximum commutes with |scale|).
+        if (step < full0 || step > full1) {
             const int rel0 = (int)(k0 - tq) + q4 * 4 + wnd - 1;
 #pragma unroll
             for (int hh = 0; hh < 2; ++hh)
@@ -1027,12 +1072,14 @@ __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
                     if (!((uint32_t)(rel0 + hh * 16 + r) < win))
                         sc[hh][r] = neg_inf;
         }
-        const float mloc = fmaxf(fmaxf(fmaxf(sc[0][0], sc[0][1]), fmaxf(sc[0][2], sc[0][3])),
-                                 fmaxf(fmaxf(sc[1][0], sc[1][1]), fmaxf(sc[1][2], sc[1][3])));
+        const float mloc =
+            max_med3(max_med3(max_med3(sc[0][0], sc[0][1], pinf), max_med3(sc[0][2], sc[0][3], pinf), pinf),
+                     max_med3(max_med3(sc[1][0], sc[1][1], pinf), max_med3(sc[1][2], sc[1][3], pinf), pinf),
+                     pinf);
         // the running maximum moves only when a step raises it by more than kLazyMax (log2
         // units), so most steps skip the rescale; the weights exp2(x - m) stay below
         // 2^kLazyMax, and the output and lse use the same m as the sums
-        const float m_row = fmaxf(st.m, max_across_rows(mloc) * scale_abs);
+        const float m_row = fmaxf(st.m, max_across_rows_swap(mloc, pinf) * scale_abs);
         const float m_new = m_row > st.m + kLazyMax ? m_row : st.m;
         const bool any = m_new != neg_inf;
         const float alpha = any ? fast_exp2(st.m - m_new) : 1.0f;
@@ -1044,7 +1091,8 @@ __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
 #pragma unroll
             for (int r = 0; r < 4; ++r)
                 pe[hh][r] = fast_exp2(__builtin_fmaf(sc[hh][r], scale_abs, m_sub));
-        // the weights PV uses are the bf16 ones; normalise by their sum too
+        // the weights PV uses are the bf16 ones; normalise by their sum too (a bf16 pair is
+        // summed by one dot product with (1, 1): the products are exact)
 #pragma unroll
         for (int c = 0; c < 4; ++c)
             pv[c] = f2v{pe[c >> 1][2 * (c & 1)], pe[c >> 1][2 * (c & 1) + 1]};
@@ -1054,7 +1102,8 @@ __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
         for (int c = 0; c < 4; ++c) {
             const bf16x2v b = __builtin_convertvector(pv[c], bf16x2v);
             pw[c] = __builtin_bit_cast(uint32_t, b);
-            psum += bf16_bits_to_f32(pw[c] & 0xffffu) + bf16_bits_to_f32(pw[c] >> 16);
+            psum = __builtin_amdgcn_fdot2_f32_bf16(b, bf16x2v{(__bf16)1.0f, (__bf16)1.0f}, psum,
+                                                   false);
             psum32 += pv[c][0] + pv[c][1];
         }
         st.l = st.l * alpha + psum;
@@ -1067,11 +1116,8 @@ __global__ __launch_bounds__(1024) void k_swa_tiled(AttnArgs a)
                 for (int r = 0; r < 4; ++r)
                     st.acc[mt][r] *= alpha;
         }
-        const bf16x8 pf = as_bf16x8(pw);
         // O^T += V^T P^T: A[m = d][k = position perm(8 q4 + j)] from the staged V rows
-#pragma unroll
-        for (int mt = 0; mt < D / 16; ++mt)
-            st.acc[mt] = mfma_16x16x32(vt_fragment(vs, kLd, mt * 16), pf, st.acc[mt]);
+        swa_pv_step<D, kLd>(vs, as_bf16x8(pw), st.acc);
         __builtin_amdgcn_s_waitcnt(0);  // this wave's part of the next tile has landed
         __syncthreads();                 // the next tile is complete; this one is no longer read
     }

@@ -94,6 +94,35 @@ __device__ __forceinline__ float max_across_rows(float v)
     return v;
 }
 
+// The larger of two non-NaN floats in one instruction: the median of (a, b, +inf).  fmaxf
+// must first quiet signalling NaNs, an extra instruction per operand the compiler cannot
+// prove canonical (matrix-core results).  `pinf` must come from opaque_pinf(): with a
+// visible +inf constant the compiler turns the median back into fmaxf.
+__device__ __forceinline__ float max_med3(float a, float b, float pinf)
+{
+    return __builtin_amdgcn_fmed3f(a, b, pinf);
+}
+
+__device__ __forceinline__ float opaque_pinf()
+{
+    float v;
+    asm volatile("v_mov_b32 %0, 0x7f800000" : "=v"(v));
+    return v;
+}
+
+// max_across_rows by the gfx950 lane swaps (v_permlane32_swap, v_permlane16_swap) instead of
+// two LDS permutes: swapping a copy of v with itself puts the value of lane l ^ 32 (then
+// l ^ 16) beside lane l's own, so two medians give every lane the maximum of its four rows.
+__device__ __forceinline__ float max_across_rows_swap(float v, float pinf)
+{
+    const uint32_t u = __float_as_uint(v);
+    const auto p = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const float m = max_med3(__uint_as_float(p[0]), __uint_as_float(p[1]), pinf);
+    const uint32_t w = __float_as_uint(m);
+    const auto q = __builtin_amdgcn_permlane16_swap(w, w, false, false);
+    return max_med3(__uint_as_float(q[0]), __uint_as_float(q[1]), pinf);
+}
+
 __device__ __forceinline__ float sum_across_rows(float v)
 {
     v += __shfl_xor(v, 16);

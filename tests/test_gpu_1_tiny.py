@@ -309,6 +309,29 @@ def test_tiny_sliding_window_scales(tiny, tiny_host, scale):
         parity.check_attention(bits(out), o_ref, lse.cpu().numpy(), l_ref)
 
 
+def test_tiny_sliding_window_peaked(tiny, tiny_host):
+    """A scale of 30: each query's softmax is close to one-hot and its logits span several
+    hundred log2 units, so a running maximum taken over only some of a query's scores (a wrong
+    lane exchange in the cross-row maximum) would overflow the weights to inf.  Output to the
+    usual bounds; lse (up to ~1400) to 2e-2 plus 1e-5 of its size: the fp32 dot products of 64
+    terms carry up to ~2e-4 of rounding, times the scale of 30."""
+    shape = WL.shape
+    t = np.arange(WL.T)
+    for window in (17, 300):
+        out = torch.empty_like(tiny["Q"])
+        lse = torch.empty((WL.T, shape.num_q_heads), dtype=torch.float32, device=DEV)
+        sgqa.swa_prefill(shape, tiny["Q"], tiny["K"], tiny["V"], tiny["G"], 0, WL.L, window,
+                         30.0, out, lse)
+        torch.cuda.synchronize()
+        o_ref, l_ref = oracle.window_attention(bits(tiny["Q"]), t, tiny_host[0], tiny_host[1],
+                                               bits(tiny["G"]), window, 30.0)
+        assert np.abs(l_ref).max() > 100.0  # the logits really are spread wide
+        parity.check_attention(bits(out), o_ref)
+        got = lse.cpu().numpy().astype(np.float64)
+        assert np.all(np.isfinite(got))
+        assert np.all(np.abs(got - l_ref) <= 2e-2 + 1e-5 * np.abs(l_ref))
+
+
 def test_tiny_sliding_window_chunk_mid_sequence(tiny, tiny_host):
     """Queries [300, 700) of a 700-token cache with a window of 64."""
     shape = WL.shape
