@@ -1236,52 +1236,56 @@ __global__ __launch_bounds__(512) void k_attn_decode_part(AttnArgs a)
 }
 
 // Exact merge of the workgroups' partial states of one (sequence, head), then the gate.
-// One thread per output dimension.  Every thread first issues the loads of its dimension's
-// partial outputs of all parts (clamped addresses, no branch, so they are in flight
-// together), then the (max, sums) go through LDS once; the merge waits for memory once.
+// One thread per output dimension.  Every thread issues all its loads at once (its
+// dimension's partial outputs, clamped to the parts present so no branch holds them back,
+// and every part's (max, sums) as vector loads of one address: as scalar loads the compiler
+// waited for each before computing with it), so the merge waits for memory once and needs
+// no barrier.
 constexpr int kMaxSplits = 32;  // decode_split_plan never makes more
 #ifndef SGQA_DECODE_WAVES
 #define SGQA_DECODE_WAVES 8
 #endif
 constexpr int kDecodeWaves = SGQA_DECODE_WAVES;  // splits (waves) per decode workgroup
+constexpr int kMaxParts = (kMaxSplits + kDecodeWaves - 1) / kDecodeWaves;  // workgroups
 
 __global__ __launch_bounds__(256) void k_attn_decode_merge(AttnArgs a)
 {
-    __shared__ float w_sh[kMaxSplits];
-    __shared__ float l_sh[kMaxSplits];
-    __shared__ float l32_sh[kMaxSplits];
     const int s = blockIdx.y, h = blockIdx.x;
     const int D = a.d, ns = a.npart, tid = threadIdx.x;
     const float neg_inf = -__builtin_inff();
     const int64_t base = (int64_t)s * ns * a.Hq + h;  // slot of part 0
     const int64_t step = (int64_t)a.Hq * D;
     const float *po = a.part_o + base * D + (tid < D ? tid : D - 1);
-    float ov[kMaxSplits];
+    int lz;  // a zero the compiler cannot see through, so the (max, sums) loads stay vector
+    asm volatile("v_mov_b32 %0, 0" : "=v"(lz));
+    float ov[kMaxParts], mw[kMaxParts], lw[kMaxParts], l32w[kMaxParts];
 #pragma unroll
-    for (int i = 0; i < kMaxSplits; ++i)
-        ov[i] = po[(i < ns ? i : ns - 1) * step];
-    if (tid < ns) {
-        const float *ml = a.part_ml + (base + (int64_t)tid * a.Hq) * 3;
-        w_sh[tid] = ml[0];
-        l_sh[tid] = ml[1];
-        l32_sh[tid] = ml[2];
+    for (int i = 0; i < kMaxParts; ++i) {
+        const int ic = i < ns ? i : ns - 1;
+        ov[i] = po[ic * step];
+        const float *ml = a.part_ml + (base + (int64_t)ic * a.Hq) * 3 + lz;
+        mw[i] = ml[0];
+        lw[i] = ml[1];
+        l32w[i] = ml[2];
     }
-    __syncthreads();
+    const uint16_t gbits = a.gate[(int64_t)s * a.Hq + h];
     float M = neg_inf;
-    for (int i = 0; i < ns; ++i)
-        M = fmaxf(M, w_sh[i]);
+#pragma unroll
+    for (int i = 0; i < kMaxParts; ++i)
+        if (i < ns)
+            M = fmaxf(M, mw[i]);
     float Lsum = 0.f, L32 = 0.f, o = 0.f;
 #pragma unroll
-    for (int i = 0; i < kMaxSplits; ++i) {
+    for (int i = 0; i < kMaxParts; ++i) {
         if (i < ns) {
-            const float w = w_sh[i] == neg_inf ? 0.f : fast_exp2(w_sh[i] - M);
-            Lsum += l_sh[i] * w;
-            L32 += l32_sh[i] * w;
+            const float w = mw[i] == neg_inf ? 0.f : fast_exp2(mw[i] - M);
+            Lsum += lw[i] * w;
+            L32 += l32w[i] * w;
             o += ov[i] * w;
         }
     }
     if (tid < D) {
-        const float gsig = sigmoid_f32(bf16_bits_to_f32(a.gate[(int64_t)s * a.Hq + h]));
+        const float gsig = sigmoid_f32(bf16_bits_to_f32(gbits));
         a.out[((int64_t)s * a.Hq + h) * D + tid] = (uint16_t)f32_to_bf16_bits(o * (gsig / Lsum));
     }
     if (a.lse && tid == 0)
@@ -1381,10 +1385,12 @@ template <int D>
 static hipError_t launch_decode_d(const AttnArgs &a0, hipStream_t stream)
 {
     if (a0.nsplit < 1 || a0.nsplit > kMaxSplits)
-        return hipErrorInvalidValue;  // the merge holds at most kMaxSplits partial states
+        return hipErrorInvalidValue;  // the merge holds at most kMaxParts partial states
     AttnArgs a = a0;
     const int nw = a.nsplit < kDecodeWaves ? a.nsplit : kDecodeWaves;
     a.npart = decode_parts(a.nsplit);
+    if (a.npart > kMaxParts)
+        return hipErrorInvalidValue;  // the merge holds at most kMaxParts partial states
     // the V buffers and windows of the waves hold their combine buffers (64 D + 192 B each)
     static_assert(attn_wave_lds(D) >= (size_t)64 * D + 192, "decode combine buffer");
     const size_t lds = (size_t)nw * attn_wave_lds(D);

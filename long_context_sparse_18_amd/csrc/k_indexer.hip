@@ -20,6 +20,8 @@
 // workgroup scan.  Ties at the threshold go to the lowest block indices, so the result
 // is the unique set "k-1 best by (score desc, index asc)" plus the own block.
 #include <hip/hip_runtime.h>
+#include <algorithm>
+#include <type_traits>
 
 #include "sgqa_device.hpp"
 #include "sgqa_launch.hpp"
@@ -317,10 +319,9 @@ __global__ __launch_bounds__(NT) void k_select(SelectArgs a)
 
 // --------------------------------------------------------------------------------------------
 // Decode: one query per sequence against the whole index.
-//  1. k_decode_keys streams kb at HBM rate (one workgroup per 1024 blocks): the MFMA A
-//     operand is the query proxy broadcast to all 16 rows, so row 0 of each 16x16 result
-//     holds the scores of 16 consecutive blocks; they are stored as order-preserving keys,
-//     and their largest key (the maximum of that "unit" of 16 blocks) is stored too.
+//  1. k_decode_keys streams kb at HBM rate in 1024-block items: every block's score is
+//     stored as an order-preserving key, and the largest key of each "unit" of 16
+//     consecutive blocks (the unit maximum) is stored too.
 //  2. k_decode_select (one workgroup per sequence): K* = the (k-1)-th largest unit maximum
 //     is a lower bound for the selection (the k-1 best unit maxima are themselves blocks
 //     at or above K*, so the (k-1)-th best block is too), and so is any K' <= K*; every
@@ -338,135 +339,232 @@ constexpr int kBitmapWords = 4096;     // one bit per candidate block
 constexpr int kUnitListCap = 4096;
 constexpr int kCandCap = 2048;
 
+// Sums over the `L` consecutive lanes of each lane group (L = 4 .. 32, a power of two) of N
+// values at once, left in every lane of the group: pair and quad sums by quad permutes, 8 and
+// 16 by rotating each 16-lane row by 4 and then 8 (each lane adds the quads before it, so
+// after both every lane holds its row's total), 32 by the gfx950 row swap.  Each step is
+// applied to all N values before the next, so no permute waits for the add just before it.
+// A fixed order: the same values always round the same way.
+template <int L, int N>
+__device__ __forceinline__ void group_sums(float (&x)[N])
+{
+    static_assert(L >= 4 && L <= 32 && (L & (L - 1)) == 0, "lane groups of 4 to 32");
+    auto dpp = [](float v, auto ctrl) {
+        return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v),
+                                                          decltype(ctrl)::value, 0xf, 0xf, false));
+    };
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+        x[n] += dpp(x[n], std::integral_constant<int, 0xb1>{});  // quad_perm [1,0,3,2]
+#pragma unroll
+    for (int n = 0; n < N; ++n)
+        x[n] += dpp(x[n], std::integral_constant<int, 0x4e>{});  // quad_perm [2,3,0,1]
+    if constexpr (L == 8) {
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            x[n] += __shfl_xor(x[n], 4);
+    }
+    if constexpr (L >= 16) {
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            x[n] += dpp(x[n], std::integral_constant<int, 0x124>{});  // row_ror:4
+#pragma unroll
+        for (int n = 0; n < N; ++n)
+            x[n] += dpp(x[n], std::integral_constant<int, 0x128>{});  // row_ror:8
+    }
+    if constexpr (L == 32) {
+#pragma unroll
+        for (int n = 0; n < N; ++n) {
+            const uint32_t u = __float_as_uint(x[n]);
+            const auto p = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+            x[n] = __uint_as_float(p[0]) + __uint_as_float(p[1]);
+        }
+    }
+}
+
+// Largest uint32 over the wave, in every lane (the rotations of group_sums, then both swaps).
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t x)
+{
+    auto dpp = [](uint32_t v, auto ctrl) {
+        return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, decltype(ctrl)::value, 0xf, 0xf,
+                                                     false);
+    };
+    auto mx = [](uint32_t a, uint32_t b) { return a > b ? a : b; };
+    x = mx(x, dpp(x, std::integral_constant<int, 0xb1>{}));
+    x = mx(x, dpp(x, std::integral_constant<int, 0x4e>{}));
+    x = mx(x, dpp(x, std::integral_constant<int, 0x124>{}));
+    x = mx(x, dpp(x, std::integral_constant<int, 0x128>{}));
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    x = mx((uint32_t)p[0], (uint32_t)p[1]);
+    const auto q = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return mx((uint32_t)q[0], (uint32_t)q[1]);
+}
+
+// The bf16 index scan reads kb as a stream: every wave load covers 1 KB of consecutive rows
+// (lane l takes 16 bytes, 8 dims of one row), which the memory system serves faster than 16
+// rows x 64 bytes per load in the matrix-core operand layout (a 1 GiB read of this pattern
+// measured 7.0 against 6.05 TB/s).  So the dot products are vector code: 8 products per lane
+// in four bf16 dot instructions, then a fixed-order sum over the row's P / 8 lanes.  A grid of
+// two workgroups per CU strides over the (sequence, 1024-block chunk) items (more, smaller
+// workgroups read slower).  Within an item a wave takes the 16-block units w, w + 4, ..., four
+// in flight; lane (row group g, lane-in-group i) keeps the key of the unit's row i * R + g
+// (R = rows per load), so 16 lanes store a unit's 16 keys together and a wave maximum gives
+// the unit maximum.  Only an item that reaches past the sequence's last candidate clamps its
+// rows (to a valid one; those scores are discarded).
+constexpr int kScanWGsPerCU = 2;
+
 template <int P>
 __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
 {
-    constexpr int U = 4;  // 16-block groups in flight per wave
-    const int s = blockIdx.y;
-    const int64_t t = a.pos.v[s];
-    const int64_t c = t / a.B;
-    const int64_t j0 = (int64_t)blockIdx.x * kKeysPerWG;
-    if (j0 >= c)
-        return;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int col = lane & 15, q4 = lane >> 4;
-    const uint16_t *kb = a.kb + (int64_t)s * a.kb_seq_stride;
-    const uint16_t *qp = a.qp + (int64_t)s * a.qp_seq_stride;
-    uint32_t *keys = a.keys + (int64_t)s * a.keys_ld;
-
-    bf16x8 af[P / 32];
-#pragma unroll
-    for (int kk = 0; kk < P / 32; ++kk)
-        af[kk] = as_bf16x8(load16(qp + kk * 32 + q4 * 8));
-
-    // waves interleave over the workgroup's 64 units (adjacent waves read adjacent rows)
-    uint32_t *umax = a.umax + (int64_t)s * a.units_ld + (int64_t)blockIdx.x * kUnitsPerWG;
-    constexpr int NG = kKeysPerWG / kUnitBlocks;
+    constexpr int LPR = P / 8;             // lanes per row
+    constexpr int RPI = 64 / LPR;          // rows per wave load
+    constexpr int NI = kUnitBlocks / RPI;  // loads per unit
+    constexpr int U = 4;                   // units in flight per wave
+    static_assert(LPR >= 4 && LPR <= 32 && NI <= LPR, "P from 32 to 256");
+    static_assert((kUnitsPerWG / 4) % U == 0, "whole iterations over an item's units");
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int grp = lane / LPR, sub = lane % LPR;
+    const int nwg = (int)(a.keys_ld / kKeysPerWG);
+    const int nitems = nwg * a.nseq;
 #pragma unroll 1
-    for (int g0 = wave; g0 < NG; g0 += 4 * U) {
-        u32x4 bv[U][P / 32];
+    for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+        const int s = it / nwg, x = it - s * nwg;
+        const int64_t c = a.pos.v[s] / a.B;
+        const int64_t j0 = (int64_t)x * kKeysPerWG;
+        if (j0 >= c)
+            continue;
+        // rows of this item are j0 + r, r < nrow (uniform); lane offset within a unit
+        const int nrow = c - j0 < kKeysPerWG ? (int)(c - j0) : kKeysPerWG;
+        const char *kbi =
+            reinterpret_cast<const char *>(a.kb + (int64_t)s * a.kb_seq_stride + j0 * P);
+        const u32x4 qv = load16(a.qp + (int64_t)s * a.qp_seq_stride + sub * 8);
+        uint32_t *keys = a.keys + (int64_t)s * a.keys_ld + j0;
+        uint32_t *umax = a.umax + (int64_t)s * a.units_ld + (int64_t)x * kUnitsPerWG;
+#pragma unroll 1
+        for (int g0 = wave; g0 < kUnitsPerWG; g0 += 4 * U) {
+            u32x4 v[U][NI];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int64_t jb = j0 + (int64_t)(g0 + 4 * u) * kUnitBlocks + col;
-            if (jb >= c)
-                jb = j0;  // a valid row; its score is discarded
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int kk = 0; kk < P / 32; ++kk)
-                bv[u][kk] = load16(kb + jb * P + kk * 32 + q4 * 8);
-        }
+                for (int i = 0; i < NI; ++i) {
+                    int r = (g0 + 4 * u) * kUnitBlocks + i * RPI + grp;
+                    r = r < nrow ? r : nrow - 1;
+                    v[u][i] = load16_stream(kbi + ((uint32_t)r * (uint32_t)(P * 2) + sub * 16));
+                }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < U; ++u) {
+                const int ru = (g0 + 4 * u) * kUnitBlocks;
+                float sc[NI];
 #pragma unroll
-            for (int kk = 0; kk < P / 32; ++kk)
-                acc = mfma_16x16x32(af[kk], as_bf16x8(bv[u][kk]), acc);
-            const int64_t j = j0 + (int64_t)(g0 + 4 * u) * kUnitBlocks + col;
-            const uint32_t key = j < c ? score_key(acc[0]) : 0u;
-            // unit maximum over the 16 lanes of this lane's row group (xor stays inside it)
-            uint32_t m = key;
+                for (int i = 0; i < NI; ++i) {
+                    float part = 0.f;
 #pragma unroll
-            for (int o = 8; o > 0; o >>= 1) {
-                const uint32_t v = (uint32_t)__shfl_xor((int)m, o);
-                m = v > m ? v : m;
-            }
-            if (q4 == 0) {
-                if (j < c)
-                    keys[j] = key;
-                if (col == 0)
+                    for (int w = 0; w < 4; ++w) {
+                        // copies first: a bit_cast of an indexed vector element read element 0
+                        const uint32_t kw = v[u][i][w], qw = qv[w];
+                        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, kw),
+                                                               __builtin_bit_cast(bf16x2v, qw),
+                                                               part, false);
+                    }
+                    sc[i] = part;
+                }
+                group_sums<LPR, NI>(sc);
+                float pick = sc[0];
+#pragma unroll
+                for (int i = 1; i < NI; ++i)
+                    pick = sub == i ? sc[i] : pick;
+                const int r = ru + sub * RPI + grp;
+                const uint32_t kreg = r < nrow ? score_key(pick) : 0u;
+                if (sub < NI && r < nrow)
+                    keys[r] = kreg;
+                const uint32_t m = wave_max_u32(kreg);
+                if (lane == 0)
                     umax[g0 + 4 * u] = m;
             }
         }
     }
 }
 
-// FP8 index variant of k_decode_keys: rows of P e4m3 codes with one fp32 scale each.  A lane
-// loads 16 codes (dims [64 k2 + 16 q4, +16)) per 64-dim step and converts them exactly to two
-// bf16 fragments for two MFMA steps; the query proxy is loaded in the same permuted order, so
-// the contraction is unchanged.  The row's scale multiplies the product afterwards.
+// FP8 index variant of k_decode_keys: rows of P e4m3 codes with one fp32 scale each, read
+// the same way (1 KB of consecutive rows per wave load; a lane takes 16 codes of one row,
+// converted exactly to bf16 and dotted with the query proxy's 16 dims in eight bf16 dot
+// instructions); the row's scale multiplies its summed product.
 template <int P>
 __global__ __launch_bounds__(256) void k_decode_keys_fp8(DecodeTopkArgs a)
 {
-    // 16-block groups in flight per wave (16 B per row and step): 4 keeps the wave under 128
-    // registers (4 waves per SIMD); measured 124 us per 16 x 1M batch vs 131 us with 8
-    constexpr int U = 4;
-    const int s = blockIdx.y;
-    const int64_t t = a.pos.v[s];
-    const int64_t c = t / a.B;
-    const int64_t j0 = (int64_t)blockIdx.x * kKeysPerWG;
-    if (j0 >= c)
-        return;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-    const int col = lane & 15, q4 = lane >> 4;
-    const uint8_t *kq = a.kbq + (int64_t)s * a.kbs_seq_stride * P;
-    const float *ksc = a.kbs + (int64_t)s * a.kbs_seq_stride;
-    const uint16_t *qp = a.qp + (int64_t)s * a.qp_seq_stride;
-    uint32_t *keys = a.keys + (int64_t)s * a.keys_ld;
-
-    bf16x8 af[P / 32];  // af[2 k2 + h] = qp[64 k2 + 16 q4 + 8 h, +8)
-#pragma unroll
-    for (int k2 = 0; k2 < P / 64; ++k2) {
-        af[2 * k2] = as_bf16x8(load16(qp + k2 * 64 + q4 * 16));
-        af[2 * k2 + 1] = as_bf16x8(load16(qp + k2 * 64 + q4 * 16 + 8));
-    }
-
-    uint32_t *umax = a.umax + (int64_t)s * a.units_ld + (int64_t)blockIdx.x * kUnitsPerWG;
-    constexpr int NG = kKeysPerWG / kUnitBlocks;
+    constexpr int LPR = P / 16;            // lanes per row
+    constexpr int RPI = 64 / LPR;          // rows per wave load
+    constexpr int NI = kUnitBlocks / RPI;  // loads per unit
+    constexpr int U = 4;                   // units in flight per wave
+    static_assert(LPR >= 4 && LPR <= 32 && NI <= LPR, "P from 64 to 512");
+    static_assert((kUnitsPerWG / 4) % U == 0, "whole iterations over an item's units");
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int grp = lane / LPR, sub = lane % LPR;
+    const int nwg = (int)(a.keys_ld / kKeysPerWG);
+    const int nitems = nwg * a.nseq;
 #pragma unroll 1
-    for (int g0 = wave; g0 < NG; g0 += 4 * U) {
-        u32x4 bv[U][P / 64];
-        float sc[U];
+    for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
+        const int s = it / nwg, x = it - s * nwg;
+        const int64_t c = a.pos.v[s] / a.B;
+        const int64_t j0 = (int64_t)x * kKeysPerWG;
+        if (j0 >= c)
+            continue;
+        const int nrow = c - j0 < kKeysPerWG ? (int)(c - j0) : kKeysPerWG;
+        const char *kqi = reinterpret_cast<const char *>(a.kbq + ((int64_t)s * a.kbs_seq_stride + j0) * P);
+        const float *ksc = a.kbs + (int64_t)s * a.kbs_seq_stride + j0;
+        const uint16_t *qp = a.qp + (int64_t)s * a.qp_seq_stride + sub * 16;
+        const u32x4 q0 = load16(qp), q1 = load16(qp + 8);
+        const uint32_t qw[8] = {q0[0], q0[1], q0[2], q0[3], q1[0], q1[1], q1[2], q1[3]};
+        uint32_t *keys = a.keys + (int64_t)s * a.keys_ld + j0;
+        uint32_t *umax = a.umax + (int64_t)s * a.units_ld + (int64_t)x * kUnitsPerWG;
+#pragma unroll 1
+        for (int g0 = wave; g0 < kUnitsPerWG; g0 += 4 * U) {
+            u32x4 v[U][NI];
+            float rs[U][NI];
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            int64_t jb = j0 + (int64_t)(g0 + 4 * u) * kUnitBlocks + col;
-            if (jb >= c)
-                jb = j0;  // a valid row; its score is discarded
+            for (int u = 0; u < U; ++u)
 #pragma unroll
-            for (int k2 = 0; k2 < P / 64; ++k2)
-                bv[u][k2] = load16(kq + jb * P + k2 * 64 + q4 * 16);
-            sc[u] = ksc[jb];
-        }
+                for (int i = 0; i < NI; ++i) {
+                    int r = (g0 + 4 * u) * kUnitBlocks + i * RPI + grp;
+                    r = r < nrow ? r : nrow - 1;
+                    v[u][i] = load16_stream(kqi + ((uint32_t)r * (uint32_t)P + sub * 16));
+                    rs[u][i] = ksc[r];
+                }
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int u = 0; u < U; ++u) {
+                const int ru = (g0 + 4 * u) * kUnitBlocks;
+                float sc[NI];
 #pragma unroll
-            for (int k2 = 0; k2 < P / 64; ++k2) {
-                bf16x8 lo, hi;
-                e4m3x16_to_bf16x8x2(bv[u][k2], lo, hi);
-                acc = mfma_16x16x32(af[2 * k2], lo, acc);
-                acc = mfma_16x16x32(af[2 * k2 + 1], hi, acc);
-            }
-            const int64_t j = j0 + (int64_t)(g0 + 4 * u) * kUnitBlocks + col;
-            const uint32_t key = j < c ? score_key(acc[0] * sc[u]) : 0u;
-            uint32_t m = key;
+                for (int i = 0; i < NI; ++i) {
+                    uint32_t w[8];
 #pragma unroll
-            for (int o = 8; o > 0; o >>= 1) {
-                const uint32_t v = (uint32_t)__shfl_xor((int)m, o);
-                m = v > m ? v : m;
-            }
-            if (q4 == 0) {
-                if (j < c)
-                    keys[j] = key;
-                if (col == 0)
+                    for (int h = 0; h < 4; ++h) {
+                        const uint32_t code = v[u][i][h];  // a copy: see k_decode_keys
+                        e4m3x4_to_bf16(code, w[2 * h], w[2 * h + 1]);
+                    }
+                    float part = 0.f;
+#pragma unroll
+                    for (int m = 0; m < 8; ++m) {
+                        const uint32_t kw = w[m], q = qw[m];
+                        part = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2v, kw),
+                                                               __builtin_bit_cast(bf16x2v, q),
+                                                               part, false);
+                    }
+                    sc[i] = part;
+                }
+                group_sums<LPR, NI>(sc);
+                float pick = sc[0] * rs[u][0];
+#pragma unroll
+                for (int i = 1; i < NI; ++i)
+                    pick = sub == i ? sc[i] * rs[u][i] : pick;
+                const int r = ru + sub * RPI + grp;
+                const uint32_t kreg = r < nrow ? score_key(pick) : 0u;
+                if (sub < NI && r < nrow)
+                    keys[r] = kreg;
+                const uint32_t m = wave_max_u32(kreg);
+                if (lane == 0)
                     umax[g0 + 4 * u] = m;
             }
         }
@@ -560,7 +658,7 @@ __global__ __launch_bounds__(NT) void k_decode_select(DecodeTopkArgs a)
     __shared__ int32_t cand_idx[kCandCap];
     __shared__ uint16_t units[kUnitListCap];
     __shared__ uint32_t red[4 * (NT / 64)];  // two OR/AND reductions
-    __shared__ int n_units, n_cand;
+    __shared__ int unit_overflow, n_cand;
     __shared__ BinFind bf;
     uint32_t *hist_a = sh.hist;
     const int s = blockIdx.x, tid = threadIdx.x;
@@ -597,7 +695,7 @@ __global__ __launch_bounds__(NT) void k_decode_select(DecodeTopkArgs a)
     for (int w = tid; w < kBitmapWords; w += NT)
         bitmap[w] = 0u;
     if (tid == 0) {
-        n_units = 0;
+        unit_overflow = 0;
         n_cand = 0;
     }
 
@@ -645,56 +743,66 @@ __global__ __launch_bounds__(NT) void k_decode_select(DecodeTopkArgs a)
 
     bool exact_done = false;
     if (nu <= kUnitListCap) {
-        // 2) the qualifying units, in any order
+        // 2) each wave lists its own qualifying units in its share of `units` (only the wave
+        //    reads its list, so no workgroup barrier) and 3) reads their keys, keeping those at
+        //    or above K' (16 bytes = 4 blocks per load).  A wave with more qualifying units
+        //    than its share (heavy ties) flags the exact selection over every key instead.
+        constexpr int kWaveUnits = kUnitListCap / (NT / 64);
+        const int lane = tid & 63;
+        uint16_t *wunits = units + (tid >> 6) * kWaveUnits;
         int q = 0;
 #pragma unroll
         for (int b = 0; b < kPer; ++b)
             q += (b * NT + tid < nunits && mx[b] >= kp) ? 1 : 0;
-        int pos = wave_append(q, &n_units);
+        const int q_inc = wave_inclusive_scan(q);
+        const int wq = __shfl(q_inc, 63);
+        if (wq > kWaveUnits) {
+            if (lane == 0)
+                unit_overflow = 1;  // no exact result from the candidates
+        } else {
+            int pos = q_inc - q;
 #pragma unroll
-        for (int b = 0; b < kPer; ++b)
-            if (b * NT + tid < nunits && mx[b] >= kp)
-                units[pos++] = (uint16_t)(b * NT + tid);
-        __syncthreads();
-        nu = n_units;
-
-        // 3) their keys at or above K' (16 bytes = 4 blocks per load)
-        const int nchunks = nu * (kUnitBlocks / 4);
-        for (int e0 = 0; e0 < nchunks; e0 += 4 * NT) {
-            u32x4 kv[4];
-            int jc[4];
+            for (int b = 0; b < kPer; ++b)
+                if (b * NT + tid < nunits && mx[b] >= kp)
+                    wunits[pos++] = (uint16_t)(b * NT + tid);
+            wave_lds_handoff();
+            const int nchunks = wq * (kUnitBlocks / 4);
+            for (int e0 = 0; e0 < nchunks; e0 += 4 * 64) {
+                u32x4 kv[4];
+                int jc[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) {
-                const int e = e0 + r * NT + tid;
-                jc[r] = e < nchunks ? (int)units[e / (kUnitBlocks / 4)] * kUnitBlocks +
-                                          (e % (kUnitBlocks / 4)) * 4
-                                    : -1;
-            }
+                for (int r = 0; r < 4; ++r) {
+                    const int e = e0 + r * 64 + lane;
+                    jc[r] = e < nchunks ? (int)wunits[e / (kUnitBlocks / 4)] * kUnitBlocks +
+                                              (e % (kUnitBlocks / 4)) * 4
+                                        : -1;
+                }
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
-                kv[r] = jc[r] >= 0 ? *reinterpret_cast<const u32x4 *>(keys + jc[r])
-                                   : u32x4{0u, 0u, 0u, 0u};
-            int cnt = 0;
+                for (int r = 0; r < 4; ++r)
+                    kv[r] = jc[r] >= 0 ? *reinterpret_cast<const u32x4 *>(keys + jc[r])
+                                       : u32x4{0u, 0u, 0u, 0u};
+                int cnt = 0;
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+                for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    cnt += (jc[r] >= 0 && jc[r] + i < cn && kv[r][i] >= kp) ? 1 : 0;
-            int slot = wave_append(cnt, &n_cand);
+                    for (int i = 0; i < 4; ++i)
+                        cnt += (jc[r] >= 0 && jc[r] + i < cn && kv[r][i] >= kp) ? 1 : 0;
+                int slot = wave_append(cnt, &n_cand);
 #pragma unroll
-            for (int r = 0; r < 4; ++r)
+                for (int r = 0; r < 4; ++r)
 #pragma unroll
-                for (int i = 0; i < 4; ++i)
-                    if (jc[r] >= 0 && jc[r] + i < cn && kv[r][i] >= kp) {
-                        if (slot < kCandCap) {
-                            cand_key[slot] = kv[r][i];
-                            cand_idx[slot] = jc[r] + i;
+                    for (int i = 0; i < 4; ++i)
+                        if (jc[r] >= 0 && jc[r] + i < cn && kv[r][i] >= kp) {
+                            if (slot < kCandCap) {
+                                cand_key[slot] = kv[r][i];
+                                cand_idx[slot] = jc[r] + i;
+                            }
+                            ++slot;
                         }
-                        ++slot;
-                    }
+            }
         }
         __syncthreads();
-        const int m = n_cand;
+        const int m = unit_overflow == 0 ? n_cand : kCandCap + 1;
         if (m <= kCandCap) {
             // 4) exact selection of `keep` candidates: radix passes below their common bits,
             //    stopping once the threshold bin is taken whole
@@ -1866,18 +1974,27 @@ size_t decode_topk_workspace(int nseq, int64_t max_cand)
     return (size_t)nseq * (decode_keys_ld(max_cand) + decode_units_ld(max_cand)) * 4;
 }
 
+// Workgroups of a decode scan: kScanWGsPerCU per CU, at most one per item.
+static int64_t scan_grid(const DecodeTopkArgs &a)
+{
+    const int64_t nitems = a.keys_ld / kKeysPerWG * a.nseq;
+    int dev = 0, cus = 256;
+    if (hipGetDevice(&dev) != hipSuccess ||
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+        cus = 256;
+    return std::min<int64_t>(nitems, (int64_t)kScanWGsPerCU * cus);
+}
+
 template <int P>
 static void launch_decode_keys_p(const DecodeTopkArgs &a, hipStream_t stream)
 {
-    const unsigned nwg = (unsigned)(a.keys_ld / kKeysPerWG);
-    hipLaunchKernelGGL(k_decode_keys<P>, dim3(nwg, (unsigned)a.nseq), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_decode_keys<P>, dim3((unsigned)scan_grid(a)), dim3(256), 0, stream, a);
 }
 
 template <int P>
 static void launch_decode_keys_fp8_p(const DecodeTopkArgs &a, hipStream_t stream)
 {
-    const unsigned nwg = (unsigned)(a.keys_ld / kKeysPerWG);
-    hipLaunchKernelGGL(k_decode_keys_fp8<P>, dim3(nwg, (unsigned)a.nseq), dim3(256), 0, stream, a);
+    hipLaunchKernelGGL(k_decode_keys_fp8<P>, dim3((unsigned)scan_grid(a)), dim3(256), 0, stream, a);
 }
 
 hipError_t launch_decode_topk(const DecodeTopkArgs &a, hipStream_t stream)

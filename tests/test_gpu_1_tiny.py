@@ -386,6 +386,42 @@ def test_decode_topk_exact_ties(k):
         assert np.array_equal(sel[b, 0].cpu().numpy().astype(np.float64), want)
 
 
+def test_decode_topk_crowded_units():
+    """Decode top-k where the blocks above the threshold crowd into the 16-block units that one
+    wave of the select holds (units b * 1024 + lane, b < 8): 300 of them carry the top scores,
+    more than the wave's share of the unit list, so the select takes its exact path over every
+    key.  One sequence of 1 048 576 tokens, scores q . kb = kb[:, 0] exactly (one nonzero
+    proxy dim); selection and scores must equal the oracle's exactly."""
+    k, L_ = 512, 1048576
+    shape = with_selection(WL.shape, 8, k)
+    nblk = L_ // 8
+    g = torch.Generator().manual_seed(21)
+    kb = torch.zeros((1, nblk, shape.proxy_dim), dtype=torch.float32)
+    kb[0, :, 0] = torch.randn(nblk, generator=g)
+    units = [b * 1024 + lane for b in range(5) for lane in range(60)]
+    for m, u in enumerate(units):
+        kb[0, 16 * u + 5, 0] = 32.0 + (m % 64) / 4.0
+    kb = kb.to(torch.bfloat16).to(DEV)
+    qp = torch.zeros((1, 1, shape.proxy_dim), dtype=torch.bfloat16)
+    qp[0, 0, 0] = 1.0
+    qp = qp.to(DEV)
+    idx = torch.empty((1, 1, k), dtype=torch.int32, device=DEV)
+    sel = torch.empty((1, 1, k), dtype=torch.float32, device=DEV)
+    say("decode crowded units")
+    sgqa.indexer_topk(shape, qp, kb, [L_ - 1], idx, sel)
+    torch.cuda.synchronize()
+    t = np.array([L_ - 1])
+    c = int(t[0] // 8)
+    kbw = parity.widen(bits(kb[0]))
+    sc = oracle.scores(bits(qp[0]), t, 8, kbw, width=c)
+    ref = oracle.topk(sc, t, 8, k)[0]
+    got = idx[0, 0].cpu().numpy()
+    assert np.array_equal(got, ref), "selection differs"
+    assert set(16 * u + 5 for u in units) <= set(ref.tolist())
+    want = np.where(ref == c, np.inf, sc[0][np.clip(ref, 0, c - 1)])
+    assert np.array_equal(sel[0, 0].cpu().numpy().astype(np.float64), want)
+
+
 @pytest.mark.parametrize("q0", [30000, 8000])
 def test_prefill_topk_exact_ties(q0):
     """Prefill top-k (one workgroup per query row) on integer-valued scores: exact.  Row 7 has
