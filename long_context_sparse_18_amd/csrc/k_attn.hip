@@ -150,15 +150,31 @@ __device__ __forceinline__ int32_t *entry_window(uint16_t *lds)
 // (token 0, group g, dim 0) of a bf16 cache; rows are Hkv*D elements apart.
 struct Bf16Rows {
     static constexpr bool kFp8 = false;
+    static constexpr bool kStream = false;
     const uint16_t *Kg, *Vg;
+};
+// Rows the kernel reads once (the decode's gathers): non-temporal loads, 49.5 -> 45.0 us for
+// the decode attention of 16 x 1M (the FP8 rows measured slower that way)
+struct Bf16StreamRows : Bf16Rows {
+    static constexpr bool kStream = true;
 };
 // Fp8Rows: e4m3 codes laid out the same way (one byte per element), and one fp32 scale per
 // (token, group) at Ks[token * Hkv] / Vs[token * Hkv]: the row's values are code * scale.
 struct Fp8Rows {
     static constexpr bool kFp8 = true;
+    static constexpr bool kStream = false;
     const uint8_t *Kg, *Vg;
     const float *Ks, *Vs;
 };
+
+template <typename Rows>
+__device__ __forceinline__ u32x4 load_row(const void *p)
+{
+    if constexpr (Rows::kStream)
+        return load16_stream(p);
+    else
+        return load16(p);
+}
 
 // Online softmax with a lazy running maximum: a step moves a query's (or head's) maximum only
 // when it raises it by more than kLazyMax in log2 units, so most steps keep the maximum and
@@ -302,8 +318,8 @@ __device__ __forceinline__ void issue_kv(const Rows &rows, int Hkv, const StepSl
             const int64_t sv = ((int64_t)(uint32_t)__shfl(p.s_lo, slot)) |
                                ((int64_t)__shfl(p.s_hi, slot) << 32);
             const int64_t off = sv * row_elems + piece * 8;
-            r.kp[ci] = load16(rows.Kg + off);
-            r.vv[ci] = load16(rows.Vg + off);
+            r.kp[ci] = load_row<Rows>(rows.Kg + off);
+            r.vv[ci] = load_row<Rows>(rows.Vg + off);
         }
         r.k_scale = 1.0f;
         r.v_scale = 1.0f;
@@ -1179,7 +1195,9 @@ __global__ __launch_bounds__(512) void k_attn_decode_part(AttnArgs a)
             const Fp8Rows rows{a.kq + base, a.vq + base, a.ksc + sb, a.vsc + sb};
             attend_range<D>(rows, a.Hkv, src, QRegs<D>{qf}, a.scale_log2, vs, st);
         } else {
-            const Bf16Rows rows{a.kc + base, a.vc + base};
+            Bf16StreamRows rows;
+            rows.Kg = a.kc + base;
+            rows.Vg = a.vc + base;
             attend_range<D>(rows, a.Hkv, src, QRegs<D>{qf}, a.scale_log2, vs, st);
         }
     }
