@@ -405,13 +405,16 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x)
 // rows x 64 bytes per load in the matrix-core operand layout (a 1 GiB read of this pattern
 // measured 7.0 against 6.05 TB/s).  So the dot products are vector code: 8 products per lane
 // in four bf16 dot instructions, then a fixed-order sum over the row's P / 8 lanes.  A grid of
-// two workgroups per CU strides over the (sequence, 1024-block chunk) items (more, smaller
-// workgroups read slower).  Within an item a wave takes the 16-block units w, w + 4, ..., four
+// one workgroup per CU strides over the (sequence, 1024-block chunk) items (more, smaller
+// workgroups read slower: a decode step of 16 x 1M measured 230.5 / 233 / 232 us with 1 / 2 / 3
+// per CU; the FP8 scan, with more conversion work per byte, is fastest with 3: 140.6 against
+// 147.5 and 142 us with 2 and 4).  Within an item a wave takes the 16-block units w, w + 4, ..., four
 // in flight; lane (row group g, lane-in-group i) keeps the key of the unit's row i * R + g
 // (R = rows per load), so 16 lanes store a unit's 16 keys together and a wave maximum gives
 // the unit maximum.  Only an item that reaches past the sequence's last candidate clamps its
 // rows (to a valid one; those scores are discarded).
-constexpr int kScanWGsPerCU = 2;
+constexpr int kScanWGsPerCU = 1;
+constexpr int kScanFp8WGsPerCU = 3;
 
 template <int P>
 __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
@@ -1974,15 +1977,17 @@ size_t decode_topk_workspace(int nseq, int64_t max_cand)
     return (size_t)nseq * (decode_keys_ld(max_cand) + decode_units_ld(max_cand)) * 4;
 }
 
-// Workgroups of a decode scan: kScanWGsPerCU per CU, at most one per item.
+// Workgroups of a decode scan: kScanWGsPerCU (bf16) or kScanFp8WGsPerCU per CU, at most one
+// per item.
 static int64_t scan_grid(const DecodeTopkArgs &a)
 {
+    const int per_cu = a.kbq ? kScanFp8WGsPerCU : kScanWGsPerCU;
     const int64_t nitems = a.keys_ld / kKeysPerWG * a.nseq;
     int dev = 0, cus = 256;
     if (hipGetDevice(&dev) != hipSuccess ||
         hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
         cus = 256;
-    return std::min<int64_t>(nitems, (int64_t)kScanWGsPerCU * cus);
+    return std::min<int64_t>(nitems, (int64_t)per_cu * cus);
 }
 
 template <int P>
