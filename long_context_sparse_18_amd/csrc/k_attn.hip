@@ -1721,21 +1721,21 @@ __device__ __forceinline__ void sdp_products(const uint16_t *buf, const u32x4 (&
     }
 }
 
-// First sweep of a wave's (row, group): D = sum_s P_s dP_s per head (this lane's share),
-// from the same fp32 P and dP the second sweep uses, so the dz of a row sum to zero.
+// First sweep of a wave's (row, group): D = sum_s P_s dP_s per head (this lane's share, added
+// to `part`), from the same fp32 P and dP the second sweep uses, so the dz of a row sum to
+// zero.
 template <int D>
 __device__ __forceinline__ float dsum_range(const uint16_t *__restrict__ Kg,
                                             const uint16_t *__restrict__ Vg, int Hkv,
                                             const SparseTokens &src, const bf16x8 (&qf)[D / 32],
                                             const bf16x8 (&daf)[D / 32], float scale_log2,
-                                            float lse2, uint16_t *vs)
+                                            float lse2, uint16_t *vs, float part = 0.f)
 {
     const int lane = threadIdx.x & 63;
     const int q4 = lane >> 4;
     const int64_t row_elems = (int64_t)Hkv * D;
     const int nsteps = src.steps();
     int wbase = -(1 << 30);
-    float part = 0.f;
     for (int step = 0; step < nsteps; ++step) {
         int64_t s_ld;
         bool valid;
@@ -1854,6 +1854,106 @@ __global__ __launch_bounds__(512) void k_bwd_dq(BwdArgs a)
 #pragma unroll
         for (int mt = 0; mt < D / 16; ++mt)
             *reinterpret_cast<f32x4 *>(dst + mt * 16) = acc[mt] * a.scale;
+    }
+}
+
+// dq on the resident prefill's schedule: the same persistent grid, XCD-to-group mapping,
+// batches of rows (longest history first) and block ranges of width W with the same bounded
+// waits, so an XCD's L2 holds about one range of its group's K/V rows while its waves sweep
+// it.  The first sweep (D, when `out` is NULL) runs over all ranges of the batch, then the
+// second (dz and dq), each range's entries in the same steps as a sliced launch would take
+// them; D is summed per lane across the ranges in entry order.  a.prog: one progress word per
+// wave (8 XCDs x 4 a.res_wgs, zero at launch), counting the ranges the wave has finished.
+template <int D>
+__global__ __launch_bounds__(512) void k_bwd_dq_resident(BwdArgs a)
+{
+    extern __shared__ __align__(16) uint16_t lds[];
+    const int wave = wave_index(), lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    const int hpg = a.Hq / a.Hkv;
+    const int R = 8 / a.Hkv;                 // XCDs per KV group
+    const int x = blockIdx.x & 7;            // this workgroup's XCD
+    const int g = x / R, h = x % R;
+    const int nw_x = a.res_wgs * 4;          // waves per XCD
+    const int lw = (int)(blockIdx.x >> 3) * 4 + wave;
+    const int64_t W = a.res_w;
+    uint32_t *prog = a.prog + (int64_t)x * nw_x;
+    const int64_t per_batch = (int64_t)R * nw_x;
+    const uint16_t *Kg = a.kc + (int64_t)g * D, *Vg = a.vc + (int64_t)g * D;
+    uint16_t *vs = lds + wave * attn_vbuf_elems(D);
+    uint32_t done = 0;                       // ranges finished in the earlier batches and sweeps
+    for (int64_t b = 0; b * per_batch < a.rows; ++b) {
+        const uint32_t done_batch0 = done;   // the batch's first sweep starts without a wait
+        const int64_t j0 = b * per_batch + (int64_t)h * nw_x;
+        const int64_t left = (int64_t)a.rows - j0;
+        const int nval = (int)(left < 0 ? 0 : (left < nw_x ? left : nw_x));
+        const int64_t c_max = (a.q_start + (int64_t)a.rows - 1 - b * per_batch) / a.B;
+        const int S = (int)(c_max / W) + 1;
+        const bool live = lw < nval;
+        const int64_t r = uni((int64_t)a.rows - 1 - (j0 + lw));
+        const int64_t t = a.q_start + r;
+        const int64_t c = uni(live ? t / a.B : (int64_t)0);
+        const int nvalid = (int)((c + 1 < a.k) ? c + 1 : a.k);
+        const int last = uni((int)(c / W));
+        const bool sliced = c >= 2 * (int64_t)a.k;
+        const int32_t *row = a.idx + (live ? r : 0) * a.k;
+        const int first_slice = uni(live && sliced ? (int)((int64_t)row[0] / W) : last);
+        const int64_t head0 = (live ? r : 0) * a.Hq + (int64_t)g * hpg;
+        const float lse2 = live && col < hpg ? a.lse[head0 + col] * kLog2e : 0.f;
+        // one sweep over the batch's ranges: body(src) for this row's entries of each range
+        auto sweep = [&](auto body) {
+            int e_lo = 0;
+            for (int s = 0; s < S; ++s) {
+                // most of the XCD's waves of this batch are done with the previous range
+                if ((s > 0 || done != done_batch0) && nval > 0)
+                    resident_wait(prog, nw_x, done + (uint32_t)s, nval - nval / kResidentSlack);
+                if (live && s >= first_slice && s <= last) {
+                    const int e_hi =
+                        uni(s == last ? nvalid : entries_below(row, nvalid, (int64_t)(s + 1) * W));
+                    if (e_hi > e_lo)
+                        body(SparseTokens{row, e_lo, e_hi, t, c, a.B, entry_window<D>(lds)});
+                    e_lo = e_hi;
+                }
+                if (live && lane == 0)
+                    __hip_atomic_store(prog + lw, done + (uint32_t)s + 1u, __ATOMIC_RELAXED,
+                                       __HIP_MEMORY_SCOPE_AGENT);
+            }
+            done += (uint32_t)S;
+        };
+        float dsum;
+        if (a.out) {
+            dsum = live && col < hpg ? a.dsum[head0 + col] : 0.f;  // k_bwd_prep's D
+        } else {
+            float part = 0.f;
+            sweep([&](const SparseTokens &src) {
+                bf16x8 qf[D / 32], daf[D / 32];
+                load_q<D>(a.q + head0 * D, hpg, qf);
+                load_q<D>(a.da + head0 * D, hpg, daf);
+                part = dsum_range<D>(Kg, Vg, a.Hkv, src, qf, daf, a.scale_log2, lse2, vs, part);
+            });
+            dsum = sum_across_rows(part);
+            if (live && col < hpg && q4 == 0) {
+                a.dsum[head0 + col] = dsum;
+                a.dgate[head0 + col] =
+                    dsum * (1.0f - sigmoid_f32(bf16_bits_to_f32(a.gate[head0 + col])));
+            }
+        }
+        f32x4 acc[D / 16];
+#pragma unroll
+        for (int mt = 0; mt < D / 16; ++mt)
+            acc[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sweep([&](const SparseTokens &src) {
+            bf16x8 qf[D / 32], daf[D / 32];
+            load_q<D>(a.q + head0 * D, hpg, qf);
+            load_q<D>(a.da + head0 * D, hpg, daf);
+            dq_range<D>(Kg, Vg, a.Hkv, src, qf, daf, a.scale_log2, lse2, dsum, vs, acc);
+        });
+        if (live && col < hpg) {
+            float *dst = a.dq + (head0 + col) * D + q4 * 4;
+#pragma unroll
+            for (int mt = 0; mt < D / 16; ++mt)
+                *reinterpret_cast<f32x4 *>(dst + mt * 16) = acc[mt] * a.scale;
+        }
     }
 }
 
@@ -2068,12 +2168,15 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
     }
 }
 
+// Backward workspace: dA (bf16), D (fp32), the row bitmap, then the resident dq's progress
+// words, each part 256-byte aligned.
 size_t attn_backward_workspace(int64_t T, int Hq, int d, int64_t nblk)
 {
     const int64_t bits_ld = (((T + 31) / 32) + 3) / 4 * 4;
     const size_t da = ((size_t)T * Hq * d * 2 + 255) / 256 * 256;
     const size_t ds = ((size_t)T * Hq * 4 + 255) / 256 * 256;
-    return da + ds + (size_t)nblk * bits_ld * 4;
+    const size_t bits = ((size_t)nblk * bits_ld * 4 + 255) / 256 * 256;
+    return da + ds + bits + kResidentProgressBytes;
 }
 
 // Query rows per dK / dV launch: a multiple of 32 (one bitmap word) whose q and dA take about
@@ -2086,22 +2189,58 @@ static int64_t bwd_row_slice(int Hq, int d)
     return rows > 32 ? rows : 32;
 }
 
+// The resident dq when the KV groups divide the 8 XCDs and every row's history lies within
+// kResidentRanges ranges of a.res_w blocks; hipErrorNotSupported otherwise.
+template <int D>
+static hipError_t launch_bwd_dq_resident(const BwdArgs &a0, hipStream_t stream)
+{
+    if (!a0.prog || a0.res_w < 1 || 8 % a0.Hkv != 0 ||
+        (a0.q_start + (int64_t)a0.rows - 1) / a0.B >= (int64_t)kResidentRanges * a0.res_w)
+        return hipErrorNotSupported;
+    const size_t lds = (size_t)4 * attn_wave_lds(D);
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_bwd_dq_resident<D>, 256, lds);
+    if (e != hipSuccess)
+        return e;
+    const int per_xcd = per_cu * (cus / 8);
+    const int words = 8 * per_xcd * 4;  // one progress word per wave
+    if (per_xcd < 1 || (size_t)words * sizeof(uint32_t) > kResidentProgressBytes)
+        return hipErrorNotSupported;
+    BwdArgs a = a0;
+    a.res_wgs = per_xcd;
+    hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                       a.prog, words);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_bwd_dq_resident<D>, dim3((unsigned)(8 * per_xcd)), dim3(256), lds, stream,
+                       a);
+    return hipGetLastError();
+}
+
 template <int D>
 static hipError_t launch_backward_d(const BwdArgs &a, hipStream_t stream)
 {
-    // dq: the forward's launch shape
-    if (8 % a.Hkv == 0) {
-        const int R = 8 / a.Hkv;
-        const int64_t ntiles = ((int64_t)a.rows + 3) / 4;
-        const int64_t nwg = (ntiles + R - 1) / R * 8;
-        const size_t lds = (size_t)4 * attn_wave_lds(D);
-        hipLaunchKernelGGL((k_bwd_dq<D, true>), dim3((unsigned)nwg), dim3(256), lds, stream, a);
-    } else {
-        const size_t lds = (size_t)a.Hkv * attn_wave_lds(D);
-        hipLaunchKernelGGL((k_bwd_dq<D, false>), dim3((unsigned)a.rows), dim3(64 * a.Hkv), lds,
-                           stream, a);
+    // dq: the resident schedule where it applies, else the forward's one-pass launch shape
+    hipError_t e = launch_bwd_dq_resident<D>(a, stream);
+    if (e == hipErrorNotSupported) {
+        if (8 % a.Hkv == 0) {
+            const int R = 8 / a.Hkv;
+            const int64_t ntiles = ((int64_t)a.rows + 3) / 4;
+            const int64_t nwg = (ntiles + R - 1) / R * 8;
+            const size_t lds = (size_t)4 * attn_wave_lds(D);
+            hipLaunchKernelGGL((k_bwd_dq<D, true>), dim3((unsigned)nwg), dim3(256), lds, stream,
+                               a);
+        } else {
+            const size_t lds = (size_t)a.Hkv * attn_wave_lds(D);
+            hipLaunchKernelGGL((k_bwd_dq<D, false>), dim3((unsigned)a.rows), dim3(64 * a.Hkv),
+                               lds, stream, a);
+        }
+        e = hipGetLastError();
     }
-    hipError_t e = hipGetLastError();
     if (e != hipSuccess)
         return e;
     // dK / dV: zeroed, then one launch per slice of rows, last slice first

@@ -161,6 +161,13 @@ constexpr int64_t kPrefillSliceHalfK = SGQA_SLICE_HALF_K;
 // Blocks per history range of the resident prefill, in units of k/2 (5k: 2560 blocks at the
 // real shape; 0 turns the resident prefill off).
 constexpr int64_t kPrefillResidentHalfK = SGQA_RESIDENT_HALF_K;
+// The backward's resident dq ranges are wider: 12k blocks (two ranges at 128K) measured
+// 647 ms for the whole backward, against 649 / 650 / 655 / 663 ms with 8k / 16k / 5k / 32k
+// (one range) and 685 ms with the one-pass dq.
+#ifndef SGQA_BWD_RESIDENT_HALF_K
+#define SGQA_BWD_RESIDENT_HALF_K 24
+#endif
+constexpr int64_t kBwdResidentHalfK = SGQA_BWD_RESIDENT_HALF_K;
 
 } // namespace
 
@@ -980,9 +987,12 @@ sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
     char *w = static_cast<char *>(workspace);
     const size_t da_bytes = ((size_t)T * a.Hq * a.d * 2 + 255) / 256 * 256;
     const size_t ds_bytes = ((size_t)T * a.Hq * 4 + 255) / 256 * 256;
+    const size_t bits_bytes = ((size_t)a.nblk * a.bits_ld * 4 + 255) / 256 * 256;
     a.da = reinterpret_cast<uint16_t *>(w);
     a.dsum = reinterpret_cast<float *>(w + da_bytes);
     a.bits = reinterpret_cast<uint32_t *>(w + da_bytes + ds_bytes);
+    a.prog = reinterpret_cast<uint32_t *>(w + da_bytes + ds_bytes + bits_bytes);
+    a.res_w = (kBwdResidentHalfK * (int64_t)a.k + 1) / 2;
     return hip_status(sgqa::launch_attn_backward(a, reinterpret_cast<hipStream_t>(stream)),
                       "sparse_attn_backward launch");
 }

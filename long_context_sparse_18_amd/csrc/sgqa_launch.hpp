@@ -196,6 +196,9 @@ struct BwdArgs {
     int64_t nblk;
     int64_t row_slice;                                // rows per dK / dV launch (0: automatic)
     int64_t row_lo, row_hi;                           // dK / dV launch: rows of this slice
+    uint32_t *prog;                                   // workspace: resident dq progress words
+    int64_t res_w;                                    // resident dq: range width in blocks
+    int32_t res_wgs;                                  // resident dq: workgroups per XCD
 };
 hipError_t launch_attn_backward(const BwdArgs &a, hipStream_t stream);
 size_t attn_backward_workspace(int64_t T, int Hq, int d, int64_t nblk);

@@ -690,10 +690,13 @@ def _backward_case(d, shape, q0: int, L: int, seed: int):
     return grads, dict(zip(("dq", "dk", "dv", "dg"), ref)), (Q, K, V, G, idx, out, lse, dout)
 
 
-@pytest.mark.parametrize("B,k,q0", [(8, 16, 0), (8, 4, 0), (1, 64, 0), (8, 16, 517), (16, 8, 100)])
+@pytest.mark.parametrize("B,k,q0", [(8, 16, 0), (8, 4, 0), (1, 64, 0), (8, 16, 517), (16, 8, 100),
+                                    (1, 2, 600)])
 def test_tiny_backward(tiny, B, k, q0):
     """Fixed-selection backward on the tiny layer against the oracle: every dq, dK, dV and
-    dgate element, sparse and dense rows, B in {1, 8, 16}, a chunk starting mid-block.  A
+    dgate element, sparse and dense rows, B in {1, 8, 16}, a chunk starting mid-block.  dq
+    runs on the resident schedule except for (B 1, k 2, from row 600), whose histories span
+    more ranges than it takes (the one-pass dq kernel).  A
     second call that runs dK / dV 32 (then 96) query rows per pass gives identical bits: the
     passes carry their sums over in one fixed order.  With the forward output given (D from
     dout . out) dq, dK and dgate meet the same bar and dV keeps its bits."""
