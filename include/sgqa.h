@@ -282,7 +282,9 @@ sgqa_status sgqa_swa_prefill(const sgqa_dims *dims, const sgqa_bf16 *q, const sg
  * results are deterministic.  Layouts as sgqa_sparse_attn_prefill; dq
  * [T][Hq][d], dk / dv [L][Hkv][d] and dgate [T][Hq] are fp32.  nseq is 1.
  *   workspace [dev] >= sgqa_workspace_bytes(SGQA_OP_ATTN_BACKWARD, dims, 1, T, L),
- *                   256-byte aligned
+ *                   256-byte aligned: dA, D, the row bitmap and the progress words of the
+ *                   resident dq schedule (cleared by the call); calls that overlap in time
+ *                   need different workspaces
  *   dkdv_row_slice  query rows per dk / dv pass: 0 picks it from the sizes (rows whose q
  *                   and dout take about 192 MiB), else a positive multiple of 32 (anything
  *                   else is SGQA_ERR_SHAPE).  The passes run from the last rows down and
