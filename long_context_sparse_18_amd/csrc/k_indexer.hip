@@ -408,10 +408,10 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t x)
 // one workgroup per CU strides over the (sequence, 1024-block chunk) items (more, smaller
 // workgroups read slower: a decode step of 16 x 1M measured 230.5 / 233 / 232 us with 1 / 2 / 3
 // per CU; the FP8 scan, with more conversion work per byte, is fastest with 3: 140.6 against
-// 147.5 and 142 us with 2 and 4).  Within an item a wave takes the 16-block units w, w + 4, ..., four
-// in flight; lane (row group g, lane-in-group i) keeps the key of the unit's row i * R + g
-// (R = rows per load), so 16 lanes store a unit's 16 keys together and a wave maximum gives
-// the unit maximum.  Only an item that reaches past the sequence's last candidate clamps its
+// 147.5 and 142 us with 2 and 4).  Within an item a wave takes the 16-block units w, w + 4,
+// ...; lane (row group g, lane-in-group i) keeps the key of the unit's row i * R + g (R = rows
+// per load), so 16 lanes store a unit's 16 keys together and a wave maximum gives the unit
+// maximum.  Only an item that reaches past the sequence's last candidate clamps its
 // rows (to a valid one; those scores are discarded).
 constexpr int kScanWGsPerCU = 1;
 constexpr int kScanFp8WGsPerCU = 3;
@@ -422,11 +422,10 @@ __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
     constexpr int LPR = P / 8;             // lanes per row
     constexpr int RPI = 64 / LPR;          // rows per wave load
     constexpr int NI = kUnitBlocks / RPI;  // loads per unit
-    constexpr int U = 4;                   // units in flight per wave
     static_assert(LPR >= 4 && LPR <= 32 && NI <= LPR, "P from 32 to 256");
-    static_assert((kUnitsPerWG / 4) % U == 0, "whole iterations over an item's units");
+    static_assert(kUnitsPerWG == 64, "a wave takes units w + 4 u, u < 16, in four halves of 2");
     typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2v;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6), lane = threadIdx.x & 63;
     const int grp = lane / LPR, sub = lane % LPR;
     const int nwg = (int)(a.keys_ld / kKeysPerWG);
     const int nitems = nwg * a.nseq;
@@ -444,20 +443,23 @@ __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
         const u32x4 qv = load16(a.qp + (int64_t)s * a.qp_seq_stride + sub * 8);
         uint32_t *keys = a.keys + (int64_t)s * a.keys_ld + j0;
         uint32_t *umax = a.umax + (int64_t)s * a.units_ld + (int64_t)x * kUnitsPerWG;
-#pragma unroll 1
-        for (int g0 = wave; g0 < kUnitsPerWG; g0 += 4 * U) {
-            u32x4 v[U][NI];
+        // two units per half, two halves in flight: a half's rows are requested before the
+        // other half is computed (4.5 us less per 16 x 1M decode step than loading four units,
+        // then computing them)
+        auto load_units = [&](u32x4 (&v)[2][NI], int gb) {
 #pragma unroll
-            for (int u = 0; u < U; ++u)
+            for (int u = 0; u < 2; ++u)
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
-                    int r = (g0 + 4 * u) * kUnitBlocks + i * RPI + grp;
+                    int r = (gb + 4 * u) * kUnitBlocks + i * RPI + grp;
                     r = r < nrow ? r : nrow - 1;
                     v[u][i] = load16_stream(kbi + ((uint32_t)r * (uint32_t)(P * 2) + sub * 16));
                 }
+        };
+        auto compute_units = [&](const u32x4 (&v)[2][NI], int gb) {
 #pragma unroll
-            for (int u = 0; u < U; ++u) {
-                const int ru = (g0 + 4 * u) * kUnitBlocks;
+            for (int u = 0; u < 2; ++u) {
+                const int ru = (gb + 4 * u) * kUnitBlocks;
                 float sc[NI];
 #pragma unroll
                 for (int i = 0; i < NI; ++i) {
@@ -483,9 +485,22 @@ __global__ __launch_bounds__(256) void k_decode_keys(DecodeTopkArgs a)
                     keys[r] = kreg;
                 const uint32_t m = wave_max_u32(kreg);
                 if (lane == 0)
-                    umax[g0 + 4 * u] = m;
+                    umax[gb + 4 * u] = m;
             }
+        };
+        u32x4 va[2][NI], vb[2][NI];
+        load_units(va, wave);
+        load_units(vb, wave + 8);
+        int g0 = wave;
+#pragma unroll 1
+        for (; g0 + 16 < kUnitsPerWG; g0 += 16) {  // the last iteration, peeled, loads nothing
+            compute_units(va, g0);
+            load_units(va, g0 + 16);
+            compute_units(vb, g0 + 8);
+            load_units(vb, g0 + 24);
         }
+        compute_units(va, g0);
+        compute_units(vb, g0 + 8);
     }
 }
 
