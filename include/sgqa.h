@@ -283,12 +283,15 @@ sgqa_status sgqa_swa_prefill(const sgqa_dims *dims, const sgqa_bf16 *q, const sg
  * [T][Hq][d], dk / dv [L][Hkv][d] and dgate [T][Hq] are fp32.  nseq is 1.
  *   workspace [dev] >= sgqa_workspace_bytes(SGQA_OP_ATTN_BACKWARD, dims, 1, T, L),
  *                   256-byte aligned: dA, D, the row bitmap and the progress words of the
- *                   resident dq schedule (cleared by the call); calls that overlap in time
- *                   need different workspaces
- *   dkdv_row_slice  query rows per dk / dv pass: 0 picks it from the sizes (rows whose q
- *                   and dout take about 192 MiB), else a positive multiple of 32 (anything
- *                   else is SGQA_ERR_SHAPE).  The passes run from the last rows down and
- *                   every sum keeps one order, so the results do not depend on it.
+ *                   resident dq and dk / dv schedules (cleared by the call); calls that
+ *                   overlap in time need different workspaces
+ *   dkdv_row_slice  query rows per dk / dv step: 0 picks it, else a positive multiple of 32
+ *                   (anything else is SGQA_ERR_SHAPE).  When the KV heads divide 8, dk / dv
+ *                   run as one persistent launch whose waves sweep the query rows in phases
+ *                   of this many rows (0: 2048); otherwise as one launch per slice of this
+ *                   many rows (0: the rows whose q and dout take about 192 MiB).  Either way
+ *                   the rows are added from the last one down and every sum keeps one order,
+ *                   so the results do not depend on it or on the schedule.
  */
 sgqa_status sgqa_sparse_attn_backward(const sgqa_dims *dims, const sgqa_bf16 *q,
                                       const sgqa_bf16 *k_cache, const sgqa_bf16 *v_cache,

@@ -1961,63 +1961,165 @@ __global__ __launch_bounds__(512) void k_bwd_dq_resident(BwdArgs a)
 // rows whose selection holds the block.  Per row: S = q K^T and dP = dA V^T with M = heads, so
 // each lane holds heads 4 q4 + i of token col - exactly the A operand of the 16x16x16
 // products dV += P^T dA and dK += dz^T q (M = tokens, K = heads); q and dA sit in LDS, where
-// the B operands are read.  A workgroup takes 4 tiles of one group (group = blockIdx % Hkv, so
-// with Hkv dividing 8 each XCD's L2 serves one group's rows), and every wave walks its rows
-// from the last one down.  One launch covers the rows [row_lo, row_hi) only: the launcher runs
-// the slices from the last one down, so that the q and dA rows in use at any time fit in the
-// memory-side cache, and each wave carries its sums over from the previous slice through the
-// fp32 dK / dV outputs (same summation order as a single sweep).  The next row's q and dA are
-// loaded while the current one is computed.
+// the B operands are read.  A wave walks its rows from the last one down (the order of every
+// dK / dV sum), and the next row's q and dA are loaded while the current one is computed.
+// Two schedules share these pieces: k_bwd_dkdv (one launch per slice of rows, the sums carried
+// from slice to slice through the fp32 outputs) and k_bwd_dkdv_resident (a persistent grid
+// whose waves keep their tile's sums in registers while the waves of an XCD sweep the rows
+// together in phases).
+
+// A wave's tile: its tokens, its group's K and V rows of those tokens as B operands (token col;
+// padding lanes repeat token s0), the byte offsets of its staged q / dA pieces, and its LDS.
 template <int D>
-__global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
+struct DkdvTile {
+    int64_t s0;  // first token of the tile
+    int ntok;    // tokens of the tile (<= 0: a tile past the end of a short last block)
+    int g, hpg;
+    bf16x8 kB[D / 32], vB[D / 32];
+    uint32_t poff[D / 32];
+    uint16_t *qs, *ds;  // staged q and dA rows [16][D + 8]
+};
+
+template <int D>
+__device__ __forceinline__ void dkdv_tile(const BwdArgs &a, int64_t j, int tile, int g,
+                                          uint16_t *lds_wave, DkdvTile<D> &c)
 {
-    extern __shared__ __align__(16) uint16_t lds[];
     constexpr int kLd = D + 8;
-    const int ntile = (a.B + 15) / 16;
-    const int g = (int)(blockIdx.x % (unsigned)a.Hkv);
-    const int wave = wave_index(), lane = threadIdx.x & 63;
-    const int64_t tid = (int64_t)(blockIdx.x / (unsigned)a.Hkv) * 4 + wave;  // tile index
-    if (tid >= a.nblk * ntile)
-        return;
-    const int64_t j = tid / ntile;
-    const int tile = (int)(tid - j * ntile);
+    const int lane = threadIdx.x & 63;
     const int col = lane & 15, q4 = lane >> 4;
-    const int hpg = a.Hq / a.Hkv;
-    const int64_t s0 = j * a.B + (int64_t)tile * 16;  // first token of the tile
+    c.g = g;
+    c.hpg = a.Hq / a.Hkv;
+    c.s0 = j * a.B + (int64_t)tile * 16;
     int64_t ntok = a.B - tile * 16;
     ntok = ntok < 16 ? ntok : 16;
-    ntok = a.L - s0 < ntok ? a.L - s0 : ntok;
-    if (ntok <= 0)
-        return;  // a tile past the end of a short last block
-    uint16_t *qs = lds + wave * 2 * 16 * kLd;
-    uint16_t *ds = qs + 16 * kLd;
+    ntok = a.L - c.s0 < ntok ? a.L - c.s0 : ntok;
+    c.ntok = (int)ntok;
+    c.qs = lds_wave;
+    c.ds = lds_wave + 16 * kLd;
     const int64_t row_elems = (int64_t)a.Hkv * D;
-
-    // K and V of the tile's tokens as B operands (token col; padding lanes repeat token s0)
-    const int64_t sc_tok = col < ntok ? s0 + col : s0;
-    bf16x8 kB[D / 32], vB[D / 32];
+    // (a tile past the end of a short last block reads the last token; it is never used)
+    const int64_t sc_tok = col < ntok ? c.s0 + col : (ntok > 0 ? c.s0 : a.L - 1);
 #pragma unroll
     for (int kk = 0; kk < D / 32; ++kk) {
-        kB[kk] = as_bf16x8(load16(a.kc + sc_tok * row_elems + (int64_t)g * D + kk * 32 + q4 * 8));
-        vB[kk] = as_bf16x8(load16(a.vc + sc_tok * row_elems + (int64_t)g * D + kk * 32 + q4 * 8));
+        c.kB[kk] = as_bf16x8(load16(a.kc + sc_tok * row_elems + (int64_t)g * D + kk * 32 + q4 * 8));
+        c.vB[kk] = as_bf16x8(load16(a.vc + sc_tok * row_elems + (int64_t)g * D + kk * 32 + q4 * 8));
     }
-    f32x4 dk[D / 16], dv[D / 16];
+    // whole rows: 16-byte piece f = lane + 64 kk of the 16 staged rows is piece f % (D/8) of
+    // row f / (D/8); the group's heads are contiguous, so each load instruction reads whole
+    // rows (rows past the group's heads repeat its last head, whose P and dz are masked to
+    // zero).  The byte offsets within the group's rows are the same for every query row.
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        const int f = lane + 64 * kk;
+        const int hd = f / (D / 8), pc = f - hd * (D / 8);
+        c.poff[kk] = (uint32_t)(((hd < c.hpg ? hd : c.hpg - 1) * D + pc * 8) * 2);
+    }
+}
 
-    // the block's rows, last first (uniform across the wave)
-    const uint32_t *brow = a.bits + j * a.bits_ld;
-    // this launch's rows [row_lo, row_hi) (row_lo a multiple of 32); none before first_row
-    // can select block j
-    const int64_t first_row = j * a.B - a.q_start;
-    const int64_t w_lo = a.row_lo >> 5;
-    const int64_t w0 = first_row > 0 && (first_row >> 5) > w_lo ? first_row >> 5 : w_lo;
-    // The bitmap words are read 64 at a time (lane l: word top - l), and the wave finds the
-    // non-zero ones by ballot, so finding the next row costs no dependent load.
-    int64_t top = ((a.row_hi + 31) >> 5) - 1;  // highest word of the current window
-    uint32_t lw = top - lane >= w0 ? brow[top - lane] : 0u;
-    uint64_t nz = __ballot(lw != 0u);
-    uint32_t word = 0u;
-    int64_t w = top;
-    auto next_row = [&](int64_t &r) -> bool {
+// q and dA of the group's heads of row r, lse / D of head col (natural log; they reach the
+// lanes holding heads 4 q4 + i by shuffles where they are used).  The loads are unconditional,
+// so none of them makes the wave wait before the values are used.
+template <int D>
+__device__ __forceinline__ void dkdv_fetch(const BwdArgs &a, const DkdvTile<D> &c, int64_t r,
+                                           u32x4 (&qa)[D / 32], u32x4 (&da)[D / 32], float &l1,
+                                           float &ds1)
+{
+    const int col = threadIdx.x & 15;
+    const int64_t h0 = r * a.Hq + (int64_t)c.g * c.hpg;  // the group's first head of row r
+    const char *qb = reinterpret_cast<const char *>(a.q + h0 * D);
+    const char *db = reinterpret_cast<const char *>(a.da + h0 * D);
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        qa[kk] = load16(qb + c.poff[kk]);
+        da[kk] = load16(db + c.poff[kk]);
+    }
+    const int64_t hr = h0 + (col < c.hpg ? col : c.hpg - 1);
+    l1 = a.lse[hr];
+    ds1 = a.dsum[hr];
+}
+
+template <int D>
+__device__ __forceinline__ void dkdv_stage(const DkdvTile<D> &c, const u32x4 (&qa)[D / 32],
+                                           const u32x4 (&da)[D / 32])
+{
+    constexpr int kLd = D + 8;
+    const int lane = threadIdx.x & 63;
+    wave_lds_handoff();
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        const int f = lane + 64 * kk;
+        const int hd = f / (D / 8), pc = f - hd * (D / 8);
+        uint2 *dq_ = reinterpret_cast<uint2 *>(c.qs + hd * kLd + pc * 8);
+        uint2 *dd_ = reinterpret_cast<uint2 *>(c.ds + hd * kLd + pc * 8);
+        dq_[0] = uint2{qa[kk][0], qa[kk][1]};
+        dq_[1] = uint2{qa[kk][2], qa[kk][3]};
+        dd_[0] = uint2{da[kk][0], da[kk][1]};
+        dd_[1] = uint2{da[kk][2], da[kk][3]};
+    }
+    wave_lds_handoff();
+}
+
+// The products of the staged row r (lse1 / ds1: its lse and D of head col) added to dk / dv.
+template <int D>
+__device__ __forceinline__ void dkdv_products(const BwdArgs &a, const DkdvTile<D> &c, int64_t r,
+                                              float lse1, float ds1, f32x4 (&dk)[D / 16],
+                                              f32x4 (&dv)[D / 16])
+{
+    constexpr int kLd = D + 8;
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
+    const int64_t t = a.q_start + r;
+    // S = q K^T and dP = dA V^T from the staged rows
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < D / 32; ++kk) {
+        const u32x4 qa = *reinterpret_cast<const u32x4 *>(c.qs + col * kLd + kk * 32 + q4 * 8);
+        const u32x4 da = *reinterpret_cast<const u32x4 *>(c.ds + col * kLd + kk * 32 + q4 * 8);
+        sc = mfma_16x16x32(as_bf16x8(qa), c.kB[kk], sc);
+        dp = mfma_16x16x32(as_bf16x8(da), c.vB[kk], dp);
+    }
+    // lane holds heads 4 q4 + i of token col
+    float p[4], dz[4];
+    const bool tok_ok = col < c.ntok && c.s0 + col <= t;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool ok = tok_ok && q4 * 4 + i < c.hpg;
+        const float lse_i = __shfl(lse1, q4 * 4 + i), ds_i = __shfl(ds1, q4 * 4 + i);
+        p[i] = ok ? fast_exp2(sc[i] * a.scale_log2 - lse_i * kLog2e) : 0.f;
+        dz[i] = p[i] * (dp[i] - ds_i) * a.scale;
+    }
+    const s16x4 pa = pack4_bf16(p[0], p[1], p[2], p[3]);
+    const s16x4 za = pack4_bf16(dz[0], dz[1], dz[2], dz[3]);
+    // B[k = head 4 q4 + i][n = dim 16 nt + col] of dA and q, read transposed
+#pragma unroll
+    for (int nt = 0; nt < D / 16; ++nt) {
+        dv[nt] = mfma_16x16x16(pa, tr_quad(c.ds, kLd, nt * 16), dv[nt]);
+        dk[nt] = mfma_16x16x16(za, tr_quad(c.qs, kLd, nt * 16), dk[nt]);
+    }
+}
+
+// The rows of one block's bitmap row in words [w0, top], last first.  The words are read 64 at
+// a time (lane l: word top - l) and the wave finds the non-zero ones by ballot, so finding the
+// next row costs no dependent load.  Uniform across the wave.
+struct RowWalk {
+    const uint32_t *brow;
+    int64_t w0, top, w;
+    uint32_t lw, word;
+    uint64_t nz;
+    __device__ __forceinline__ void start(const uint32_t *row_bits, int64_t lo, int64_t hi)
+    {
+        const int lane = threadIdx.x & 63;
+        brow = row_bits;
+        w0 = lo;
+        top = hi;
+        lw = top - lane >= w0 ? brow[top - lane] : 0u;
+        nz = __ballot(lw != 0u);
+        word = 0u;
+        w = top;
+    }
+    __device__ __forceinline__ bool next(int64_t &r)
+    {
+        const int lane = threadIdx.x & 63;
         while (word == 0u) {
             if (nz == 0ull) {
                 top -= 64;
@@ -2036,135 +2138,197 @@ __global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
         word &= ~(1u << b);
         r = (w << 5) + b;
         return true;
-    };
-    // q and dA of the group's heads of row r, lse / D of heads 4 q4 + i.  The loads are
-    // unconditional, so none of them makes the wave wait before the values are used: staged
-    // rows past the group's heads repeat its last head, whose P and dz are masked to zero (so
-    // those rows meet only zero weights).
-    // lse and D come one per lane (head col) and reach the lanes holding heads 4 q4 + i by
-    // shuffles where they are used.
-    // whole rows: 16-byte piece f = lane + 64 kk of the 16 staged rows is piece f % (D/8) of
-    // row f / (D/8); the group's heads are contiguous, so each load instruction reads whole
-    // rows (rows past the group's heads repeat its last head).  The byte offsets within the
-    // group's rows are the same for every query row.
-    uint32_t poff[D / 32];
-#pragma unroll
-    for (int kk = 0; kk < D / 32; ++kk) {
-        const int f = lane + 64 * kk;
-        const int hd = f / (D / 8), pc = f - hd * (D / 8);
-        poff[kk] = (uint32_t)(((hd < hpg ? hd : hpg - 1) * D + pc * 8) * 2);
     }
-    auto fetch = [&](int64_t r, u32x4 (&qa)[D / 32], u32x4 (&da)[D / 32], float &l1,
-                     float &ds1) {
-        const int64_t h0 = r * a.Hq + (int64_t)g * hpg;  // the group's first head of row r
-        const char *qb = reinterpret_cast<const char *>(a.q + h0 * D);
-        const char *db = reinterpret_cast<const char *>(a.da + h0 * D);
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-            qa[kk] = load16(qb + poff[kk]);
-            da[kk] = load16(db + poff[kk]);
-        }
-        const int64_t hr = h0 + (col < hpg ? col : hpg - 1);
-        l1 = a.lse[hr];  // natural log; scaled to base 2 where it is used
-        ds1 = a.dsum[hr];
-    };
-    auto stage = [&](const u32x4 (&qa)[D / 32], const u32x4 (&da)[D / 32]) {
-        wave_lds_handoff();
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-            const int f = lane + 64 * kk;
-            const int hd = f / (D / 8), pc = f - hd * (D / 8);
-            uint2 *dq_ = reinterpret_cast<uint2 *>(qs + hd * kLd + pc * 8);
-            uint2 *dd_ = reinterpret_cast<uint2 *>(ds + hd * kLd + pc * 8);
-            dq_[0] = uint2{qa[kk][0], qa[kk][1]};
-            dq_[1] = uint2{qa[kk][2], qa[kk][3]};
-            dd_[0] = uint2{da[kk][0], da[kk][1]};
-            dd_[1] = uint2{da[kk][2], da[kk][3]};
-        }
-        wave_lds_handoff();
-    };
+};
 
-    int64_t r;
-    bool have = next_row(r);
-    if (!have)
-        return;  // no row of this slice selects the block: its sums stay as they are
-    float lse1, ds1;  // the staged row's lse and D of head col
-    {
-        u32x4 qa[D / 32], da[D / 32];
-        fetch(r, qa, da, lse1, ds1);
-        stage(qa, da);
-    }
-    // continue the sums of the slices already done (the launcher zeroes dK and dV first)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int tok = q4 * 4 + i;
-        const int64_t base = ((s0 + (tok < ntok ? tok : 0)) * a.Hkv + g) * D;
-#pragma unroll
-        for (int nt = 0; nt < D / 16; ++nt) {
-            dk[nt][i] = tok < ntok ? a.dk[base + nt * 16 + col] : 0.f;
-            dv[nt][i] = tok < ntok ? a.dv[base + nt * 16 + col] : 0.f;
-        }
-    }
-    // Let these loads land here: the wait the compiler would otherwise put before the first
-    // product in the loop (it cannot tell they finished) would also drain each row's prefetch.
-    __builtin_amdgcn_s_waitcnt(0);
+// Adds the rows of `it` (the first one, r, already staged with lse1 / ds1) to dk / dv, each
+// row's successor in flight while it is computed.
+template <int D>
+__device__ __forceinline__ void dkdv_walk(const BwdArgs &a, const DkdvTile<D> &c, RowWalk &it,
+                                          int64_t r, float lse1, float ds1, f32x4 (&dk)[D / 16],
+                                          f32x4 (&dv)[D / 16])
+{
+    bool have = true;
 #pragma unroll 1
     while (have) {
         int64_t rn = 0;
-        const bool have_next = next_row(rn);
+        const bool have_next = it.next(rn);
         u32x4 nq[D / 32], nd[D / 32];
         float nl = 0.f, ns = 0.f;
         if (have_next)
-            fetch(rn, nq, nd, nl, ns);
-        const int64_t t = a.q_start + r;
-
-        // S = q K^T and dP = dA V^T from the staged rows
-        f32x4 sc = {0.f, 0.f, 0.f, 0.f}, dp = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < D / 32; ++kk) {
-            const u32x4 qa = *reinterpret_cast<const u32x4 *>(qs + col * kLd + kk * 32 + q4 * 8);
-            const u32x4 da = *reinterpret_cast<const u32x4 *>(ds + col * kLd + kk * 32 + q4 * 8);
-            sc = mfma_16x16x32(as_bf16x8(qa), kB[kk], sc);
-            dp = mfma_16x16x32(as_bf16x8(da), vB[kk], dp);
-        }
-        // lane holds heads 4 q4 + i of token col
-        float p[4], dz[4];
-        const bool tok_ok = col < ntok && s0 + col <= t;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool ok = tok_ok && q4 * 4 + i < hpg;
-            const float lse_i = __shfl(lse1, q4 * 4 + i), ds_i = __shfl(ds1, q4 * 4 + i);
-            p[i] = ok ? fast_exp2(sc[i] * a.scale_log2 - lse_i * kLog2e) : 0.f;
-            dz[i] = p[i] * (dp[i] - ds_i) * a.scale;
-        }
-        const s16x4 pa = pack4_bf16(p[0], p[1], p[2], p[3]);
-        const s16x4 za = pack4_bf16(dz[0], dz[1], dz[2], dz[3]);
-        // B[k = head 4 q4 + i][n = dim 16 nt + col] of dA and q, read transposed
-#pragma unroll
-        for (int nt = 0; nt < D / 16; ++nt) {
-            dv[nt] = mfma_16x16x16(pa, tr_quad(ds, kLd, nt * 16), dv[nt]);
-            dk[nt] = mfma_16x16x16(za, tr_quad(qs, kLd, nt * 16), dk[nt]);
-        }
+            dkdv_fetch<D>(a, c, rn, nq, nd, nl, ns);
+        dkdv_products<D>(a, c, r, lse1, ds1, dk, dv);
         if (have_next) {
-            stage(nq, nd);
+            dkdv_stage<D>(c, nq, nd);
             lse1 = nl;
             ds1 = ns;
         }
         r = rn;
         have = have_next;
     }
-    // lane holds dK / dV of token 4 q4 + i, dim 16 nt + col
+}
+
+// lane holds dK / dV of token 4 q4 + i, dim 16 nt + col
+template <int D>
+__device__ __forceinline__ void dkdv_store(const BwdArgs &a, const DkdvTile<D> &c,
+                                           const f32x4 (&dk)[D / 16], const f32x4 (&dv)[D / 16])
+{
+    const int lane = threadIdx.x & 63;
+    const int col = lane & 15, q4 = lane >> 4;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
         const int tok = q4 * 4 + i;
-        if (tok < ntok) {
-            const int64_t base = ((s0 + tok) * a.Hkv + g) * D;
+        if (tok < c.ntok) {
+            const int64_t base = ((c.s0 + tok) * a.Hkv + c.g) * D;
 #pragma unroll
             for (int nt = 0; nt < D / 16; ++nt) {
                 a.dk[base + nt * 16 + col] = dk[nt][i];
                 a.dv[base + nt * 16 + col] = dv[nt][i];
             }
         }
+    }
+}
+
+// Sliced schedule: a workgroup takes 4 tiles of one group (group = blockIdx % Hkv, so with Hkv
+// dividing 8 each XCD's L2 serves one group's rows).  One launch covers the rows
+// [row_lo, row_hi) only: the launcher runs the slices from the last one down, so that the q
+// and dA rows in use at any time fit in the memory-side cache, and each wave carries its sums
+// over from the previous slice through the fp32 dK / dV outputs (same summation order as a
+// single sweep).
+template <int D>
+__global__ __launch_bounds__(512) void k_bwd_dkdv(BwdArgs a)
+{
+    extern __shared__ __align__(16) uint16_t lds[];
+    constexpr int kLd = D + 8;
+    const int ntile = (a.B + 15) / 16;
+    const int g = (int)(blockIdx.x % (unsigned)a.Hkv);
+    const int wave = wave_index(), lane = threadIdx.x & 63;
+    const int64_t tid = (int64_t)(blockIdx.x / (unsigned)a.Hkv) * 4 + wave;  // tile index
+    if (tid >= a.nblk * ntile)
+        return;
+    const int64_t j = tid / ntile;
+    const int tile = (int)(tid - j * ntile);
+    const int col = lane & 15, q4 = lane >> 4;
+    DkdvTile<D> c;
+    dkdv_tile<D>(a, j, tile, g, lds + wave * 2 * 16 * kLd, c);
+    if (c.ntok <= 0)
+        return;  // a tile past the end of a short last block
+    f32x4 dk[D / 16], dv[D / 16];
+
+    // this launch's rows [row_lo, row_hi) (row_lo a multiple of 32); none before first_row
+    // can select block j
+    const int64_t first_row = j * a.B - a.q_start;
+    const int64_t w_lo = a.row_lo >> 5;
+    const int64_t w0 = first_row > 0 && (first_row >> 5) > w_lo ? first_row >> 5 : w_lo;
+    RowWalk it;
+    it.start(a.bits + j * a.bits_ld, w0, ((a.row_hi + 31) >> 5) - 1);
+    int64_t r;
+    if (!it.next(r))
+        return;  // no row of this slice selects the block: its sums stay as they are
+    float lse1, ds1;  // the staged row's lse and D of head col
+    {
+        u32x4 qa[D / 32], da[D / 32];
+        dkdv_fetch<D>(a, c, r, qa, da, lse1, ds1);
+        dkdv_stage<D>(c, qa, da);
+    }
+    // continue the sums of the slices already done (the launcher zeroes dK and dV first)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int tok = q4 * 4 + i;
+        const int64_t base = ((c.s0 + (tok < c.ntok ? tok : 0)) * a.Hkv + g) * D;
+#pragma unroll
+        for (int nt = 0; nt < D / 16; ++nt) {
+            dk[nt][i] = tok < c.ntok ? a.dk[base + nt * 16 + col] : 0.f;
+            dv[nt][i] = tok < c.ntok ? a.dv[base + nt * 16 + col] : 0.f;
+        }
+    }
+    // Let these loads land here: the wait the compiler would otherwise put before the first
+    // product in the loop (it cannot tell they finished) would also drain each row's prefetch.
+    __builtin_amdgcn_s_waitcnt(0);
+    dkdv_walk<D>(a, c, it, r, lse1, ds1, dk, dv);
+    dkdv_store<D>(a, c, dk, dv);
+}
+
+// Resident schedule: a persistent grid of exactly the resident workgroups.  The waves of one
+// XCD take a batch of nw_x consecutive tiles of the XCD's KV group (the R = 8 / Hkv XCDs of a
+// group split the group's batch of R * nw_x tiles; batches from the last tiles down) and keep
+// their sums in registers while they sweep the query rows from the last one down in phases of
+// a.row_slice rows: a wave starts phase s once most waves of its XCD have finished phase s - 1,
+// so the XCD's L2 holds about one phase's q and dA rows at a time.  The wait only orders the
+// work for the caches (it guards no data; a wave that stops waiting at the bound computes the
+// same result), and each tile's rows are added in the same order as in the sliced schedule,
+// so dK and dV are the same bits.  Every tile's dK / dV is written once, so the outputs need
+// no clearing.  a.prog: one progress word per wave (8 XCDs x 4 a.res_wgs, zero at launch).
+template <int D>
+__global__ __launch_bounds__(512) void k_bwd_dkdv_resident(BwdArgs a)
+{
+    extern __shared__ __align__(16) uint16_t lds[];
+    constexpr int kLd = D + 8;
+    const int wave = wave_index();
+    const int R = 8 / a.Hkv;                 // XCDs per KV group
+    const int x = blockIdx.x & 7;            // this workgroup's XCD
+    const int g = x / R, h = x % R;
+    const int nw_x = a.res_wgs * 4;          // waves per XCD
+    const int lw = (int)(blockIdx.x >> 3) * 4 + wave;
+    uint32_t *prog = a.prog + (int64_t)x * nw_x;
+    const int ntile = (a.B + 15) / 16;
+    const int64_t ntiles = a.nblk * ntile;
+    const int64_t per_batch = (int64_t)R * nw_x;
+    const int64_t pw = a.row_slice >> 5;     // bitmap words per phase
+    const int64_t wtop = ((int64_t)a.rows - 1) >> 5;
+    uint16_t *lds_wave = lds + wave * 2 * 16 * kLd;
+    uint32_t done = 0;                       // phases of the earlier batches
+    for (int64_t b = 0; b * per_batch < ntiles; ++b) {
+        // this XCD's tiles of the batch, from the last one down
+        const int64_t i0 = b * per_batch + (int64_t)h * nw_x;
+        const int64_t left = ntiles - i0;
+        const int nval = (int)(left < 0 ? 0 : (left < nw_x ? left : nw_x));
+        if (nval == 0)
+            break;                           // the other XCDs of the group took the last tiles
+        // phases down to the first row that can select the XCD's lowest block of the batch
+        const int64_t j_lo = (ntiles - 1 - (i0 + nval - 1)) / ntile;
+        const int64_t r_lo = j_lo * a.B - a.q_start;
+        const int64_t w_lo = r_lo > 0 ? r_lo >> 5 : 0;
+        const int S = w_lo > wtop ? 0 : (int)((wtop - w_lo) / pw) + 1;
+        const bool live = lw < nval;
+        const int64_t tid = uni(live ? ntiles - 1 - (i0 + lw) : (int64_t)0);
+        const int64_t j = tid / ntile;
+        const int tile = (int)(tid - j * ntile);
+        DkdvTile<D> c;
+        dkdv_tile<D>(a, j, tile, g, lds_wave, c);
+        const bool work = live && c.ntok > 0;
+        f32x4 dk[D / 16], dv[D / 16];
+#pragma unroll
+        for (int nt = 0; nt < D / 16; ++nt)
+            dk[nt] = dv[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int64_t first_row = j * a.B - a.q_start;  // none before it selects block j
+        const int64_t wf = first_row > 0 ? first_row >> 5 : 0;
+        const uint32_t *brow = a.bits + j * a.bits_ld;
+        for (int s = 0; s < S; ++s) {
+            // most of the XCD's waves of this batch are done with phase s - 1
+            if (s > 0)
+                resident_wait(prog, nw_x, done + (uint32_t)s, nval - nval / kResidentSlack);
+            const int64_t top = wtop - (int64_t)s * pw;
+            if (work && top >= wf) {
+                const int64_t bot = top - pw + 1;
+                RowWalk it;
+                it.start(brow, bot > wf ? bot : wf, top);
+                int64_t r;
+                if (it.next(r)) {
+                    float lse1, ds1;
+                    u32x4 qa[D / 32], da[D / 32];
+                    dkdv_fetch<D>(a, c, r, qa, da, lse1, ds1);
+                    dkdv_stage<D>(c, qa, da);
+                    dkdv_walk<D>(a, c, it, r, lse1, ds1, dk, dv);
+                }
+            }
+            if (live && (threadIdx.x & 63) == 0)
+                __hip_atomic_store(prog + lw, done + (uint32_t)s + 1u, __ATOMIC_RELAXED,
+                                   __HIP_MEMORY_SCOPE_AGENT);
+        }
+        if (work)
+            dkdv_store<D>(a, c, dk, dv);
+        done += (uint32_t)S;
     }
 }
 
@@ -2187,6 +2351,45 @@ static int64_t bwd_row_slice(int Hq, int d)
     const int64_t per_row = (int64_t)Hq * d * 2 * 2;
     const int64_t rows = ((int64_t)192 << 20) / per_row / 32 * 32;
     return rows > 32 ? rows : 32;
+}
+
+// Query rows per phase of the resident dK / dV when the caller leaves it open.  128K prefill,
+// dK / dV pass (sliced: 390 ms, 17.6 % L2 hits): phases of 512 / 1024 / 2048 / 4096 rows
+// 387 / 372 / 368 / 381 ms at 63 / 50 / 36 / 26 % L2 hits - the pass waits on each row's
+// q / dA request about as long whether it hits the L2 or not
+constexpr int64_t kDkdvPhaseRows = 2048;
+
+// The resident dK / dV when the KV groups divide the 8 XCDs and the workspace holds the
+// progress words; hipErrorNotSupported otherwise.  a.row_slice > 0 sets the phase height.
+template <int D>
+static hipError_t launch_bwd_dkdv_resident(const BwdArgs &a0, hipStream_t stream)
+{
+    if (!a0.prog || 8 % a0.Hkv != 0)
+        return hipErrorNotSupported;
+    const size_t lds = (size_t)4 * 2 * 16 * (D + 8) * sizeof(uint16_t);
+    int dev = 0, cus = 0, per_cu = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e == hipSuccess)
+        e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e == hipSuccess)
+        e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, k_bwd_dkdv_resident<D>, 256,
+                                                         lds);
+    if (e != hipSuccess)
+        return e;
+    const int per_xcd = per_cu * (cus / 8);
+    const int words = 8 * per_xcd * 4;  // one progress word per wave
+    if (per_xcd < 1 || (size_t)words * sizeof(uint32_t) > kResidentProgressBytes)
+        return hipErrorNotSupported;
+    BwdArgs a = a0;
+    a.res_wgs = per_xcd;
+    a.row_slice = a0.row_slice > 0 ? a0.row_slice : kDkdvPhaseRows;
+    hipLaunchKernelGGL(k_zero_u32, dim3((unsigned)((words + 255) / 256)), dim3(256), 0, stream,
+                       a.prog, words);
+    if ((e = hipGetLastError()) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(k_bwd_dkdv_resident<D>, dim3((unsigned)(8 * per_xcd)), dim3(256), lds,
+                       stream, a);
+    return hipGetLastError();
 }
 
 // The resident dq when the KV groups divide the 8 XCDs and every row's history lies within
@@ -2243,7 +2446,11 @@ static hipError_t launch_backward_d(const BwdArgs &a, hipStream_t stream)
     }
     if (e != hipSuccess)
         return e;
-    // dK / dV: zeroed, then one launch per slice of rows, last slice first
+    // dK / dV: the resident schedule where it applies; else zeroed, then one launch per slice of
+    // rows, last slice first
+    e = launch_bwd_dkdv_resident<D>(a, stream);
+    if (e != hipErrorNotSupported)
+        return e;
     const int64_t nkv = a.L * a.Hkv * D;
     const unsigned zg = (unsigned)(nkv < 65536 * 256 ? (nkv + 255) / 256 : 65536);
     hipLaunchKernelGGL(k_bwd_zero, dim3(zg), dim3(256), 0, stream, (uint32_t *)a.dk, nkv);

@@ -306,7 +306,8 @@ def sparse_attn_backward(shape: LayerShape, q, k_cache, v_cache, gate, idx, q_st
                          stream=None, dkdv_row_slice: int = 0, out=None):
     """Backward of sparse_attn_prefill with idx fixed: fp32 dq [T, Hq, d], dk / dv [L, Hkv, d]
     and dgate [T, Hq] from dout [T, Hq, d] and the forward's lse.  ``dkdv_row_slice``: query
-    rows per dk / dv pass (0 = chosen from the sizes; else a multiple of 32).  ``out``: the
+    rows per dk / dv phase or slice (0 = chosen by the library; else a multiple of 32); the
+    results do not depend on it.  ``out``: the
     forward's output [T, Hq, d]; given, D = dout . out and dq sweeps the selection once."""
     _need_cuda(q, k_cache, v_cache, gate, idx, lse, dout, dq, dk, dv, dgate, workspace, out)
     T = q.shape[0]

@@ -697,8 +697,8 @@ def test_tiny_backward(tiny, B, k, q0):
     dgate element, sparse and dense rows, B in {1, 8, 16}, a chunk starting mid-block.  dq
     runs on the resident schedule except for (B 1, k 2, from row 600), whose histories span
     more ranges than it takes (the one-pass dq kernel).  A
-    second call that runs dK / dV 32 (then 96) query rows per pass gives identical bits: the
-    passes carry their sums over in one fixed order.  With the forward output given (D from
+    second call that sweeps the query rows for dK / dV in phases of 32 (then 96) rows gives
+    identical bits: every sum keeps one fixed order.  With the forward output given (D from
     dout . out) dq, dK and dgate meet the same bar and dV keeps its bits."""
     shape = with_selection(WL.shape, B, k)
     grads, ref, args = _backward_case(tiny, shape, q0, WL.L, 7 + q0)
