@@ -7,7 +7,9 @@
 //
 // Pure HBM streaming: each thread owns 8 consecutive proxy features (16 B) of
 // one block, issues all B row loads at once, sums exactly in fp64 and writes
-// one 16 B chunk of correctly rounded bf16 means.  A wave covers 64 x 16 B = 1 KiB of contiguous output, and its
+// one 16 B chunk of correctly rounded bf16 means.  The proxy keys are read once,
+// by non-temporal loads (128K: 14.6-14.9 -> 12.7-12.9 us; 16 x 1M tokens:
+// 1.89 -> 1.71 ms); the means stay cacheable for the scoring that follows.  A wave covers 64 x 16 B = 1 KiB of contiguous output, and its
 // loads for row r of the blocks it covers are contiguous 512 B runs.
 #include <hip/hip_runtime.h>
 
@@ -44,7 +46,7 @@ __global__ __launch_bounds__(256) void k_index_build(const uint16_t *__restrict_
         u32x4 v[B];
 #pragma unroll
         for (int r = 0; r < B; ++r)
-            v[r] = load16(src + (int64_t)r * P);
+            v[r] = load16_stream(src + (int64_t)r * P);
 #pragma unroll
         for (int r = 0; r < B; ++r) {
 #pragma unroll
@@ -55,7 +57,7 @@ __global__ __launch_bounds__(256) void k_index_build(const uint16_t *__restrict_
         }
     } else {
         for (int64_t r = 0; r < n; ++r) {
-            u32x4 v = load16(src + r * P);
+            u32x4 v = load16_stream(src + r * P);
 #pragma unroll
             for (int w = 0; w < 4; ++w) {
                 acc[2 * w] += (double)bf16_bits_to_f32(v[w] & 0xffffu);
