@@ -553,6 +553,50 @@ def test_tiny_index_from_keys(tiny, B):
         assert torch.equal(kb[b][mask], before[b][mask])
 
 
+def test_tiny_index_decode_loop_trailing_block(tiny):
+    """A decode loop's index maintenance: three sequences grow by one token per step across
+    block boundaries (8, 517 and 1007 tokens at the start), and each step refreshes only the
+    sequence's trailing block, from the proxy keys (sgqa_index_build) and from the keys
+    (sgqa_index_build_from_keys).  After every step each sequence's index equals the oracle's
+    build of its current length, and no other block changed."""
+    shape = WL.shape
+    B = shape.block_size
+    lens = [8, 517, 1007]
+    steps = 11
+    n, Lmax = len(lens), max(lens) + steps
+    kp = torch.zeros((n, Lmax, shape.proxy_dim), dtype=torch.bfloat16, device=DEV)
+    K = torch.zeros((n, Lmax) + tuple(tiny["K"].shape[1:]), dtype=torch.bfloat16, device=DEV)
+    for b in range(n):
+        kp[b] = tiny["kp"][:Lmax].roll(shifts=131 * b, dims=0)
+        K[b] = tiny["K"][:Lmax].roll(shifts=131 * b, dims=0)
+    wkt = _w_kt(WL, 3)
+    nblk = -(-Lmax // B)
+    kb = torch.full((n, nblk, shape.proxy_dim), 7.0, dtype=torch.bfloat16, device=DEV)
+    kf = torch.full_like(kb, 7.0)
+    sgqa.index_build(shape, kp, kb, lens)
+    sgqa.index_build_from_keys(shape, K, wkt, kf, lens)
+    for step in range(steps):
+        lens = [L_ + 1 for L_ in lens]
+        before, before_f = kb.clone(), kf.clone()
+        last = [-(-L_ // B) - 1 for L_ in lens]
+        for b, L_ in enumerate(lens):
+            sgqa.index_build(shape, kp[b], kb[b], [L_], last[b], last[b] + 1)
+            sgqa.index_build_from_keys(shape, K[b], wkt, kf[b], [L_], last[b], last[b] + 1)
+        torch.cuda.synchronize()
+        for b, L_ in enumerate(lens):
+            nb = last[b] + 1
+            st = parity.check_kb(bits(kb[b, :nb]), oracle.index_build(bits(kp[b, :L_]), B))
+            assert st["kb_bit_equal_to_rne"] >= 0.999, (step, b, st)
+            ref = oracle.index_build_from_keys(bits(K[b, last[b] * B: L_]), bits(wkt), B)
+            parity.check_kb_projected(bits(kf[b, last[b]:nb]), ref)
+            mask = torch.ones(nblk, dtype=torch.bool, device=DEV)
+            mask[last[b]] = False
+            assert torch.equal(kb[b][mask], before[b][mask]), (step, b)
+            assert torch.equal(kf[b][mask], before_f[b][mask]), (step, b)
+            assert torch.all(kb[b, nb:] == 7.0) and torch.all(kf[b, nb:] == 7.0)
+    say(f"index decode loop: {steps} steps, lengths now {lens}")
+
+
 @pytest.mark.parametrize("B", [8, 16])
 def test_index_from_keys_odd_width(B):
     """Fused index maintenance where the key width (1 KV head x 192) is not a multiple of the
