@@ -1364,7 +1364,7 @@ __global__ __launch_bounds__(256) void k_fused_threshold(FusedTopkArgs a)
 #define SGQA_FILTER_TILES 8
 #endif
 #ifndef SGQA_FILTER_STAGE
-#define SGQA_FILTER_STAGE 64
+#define SGQA_FILTER_STAGE 32
 #endif
 constexpr int kFilterWaves = SGQA_FILTER_WAVES;
 constexpr int kFilterTiles = SGQA_FILTER_TILES;
@@ -1376,8 +1376,19 @@ constexpr int kStage = SGQA_FILTER_STAGE;
 constexpr int kFilterQ = 16 * kFilterWaves;  // query rows per workgroup
 constexpr int kFilterNT = 64 * kFilterWaves;
 
+// Occupancy: a workgroup holds its kb tile (~34 KB at P = 256) and the row stages (16 KB), and
+// for P <= 256 the second launch bound keeps the kernel within 168 VGPRs (it took 232 at
+// P = 256), so three workgroups (12 waves) share a CU instead of two: 128K top-k 3.13-3.20 ->
+// 2.88 ms, chunked prefill 1.75 -> 1.46 ms, the same selections (stages of 32 entries with two
+// workgroups per CU: no gain).  At P = 512 the kb tile alone is 66 KB, so the bound stays loose.
+template <int P>
+constexpr int filter_min_waves()
+{
+    return P <= 256 ? 3 : 1;
+}
+
 template <int P, int FT>
-__global__ __launch_bounds__(kFilterNT) void k_fused_filter(FusedTopkArgs a)
+__global__ __launch_bounds__(kFilterNT, filter_min_waves<P>()) void k_fused_filter(FusedTopkArgs a)
 {
     extern __shared__ __align__(16) uint16_t kb_tile[];  // [kTileB][P + 8], then the stage
     constexpr int ldt = P + 8;
