@@ -63,7 +63,7 @@ def scored_pairs(q_start: int, T: int, B: int) -> int:
     return sum(t // B for t in range(q_start, q_start + T))
 
 
-PREFILL_CHUNKS = 8
+PREFILL_CHUNKS = 1  # row ranges of the layer step (one stream; see layer.py)
 
 
 def prefill_launches(wl) -> str:
@@ -116,13 +116,11 @@ def bench_prefill(steps: int, warmup: int):
                                  out, lse, workspace=ws_attn, stream=stream)
         marks.append(ev())
 
-    # the timed step: the layer's own schedule, 8 row chunks whose selections run on a side
-    # stream under the attention of the chunk before (same calls, same result bits)
-    side = torch.cuda.Stream(dev)
-
+    # the timed step: the layer's own schedule on one stream (index build, selections, sparse
+    # attention; same calls, same result bits)
     def layer_step():
         layer.prefill_layer(s, d, wl.q_start, wl.L, scale, kb, idx, out, lse, ws, ws_attn,
-                            chunks=PREFILL_CHUNKS, stream=stream, side_stream=side)
+                            chunks=PREFILL_CHUNKS, stream=stream)
 
     for _ in range(warmup):
         layer_step()
@@ -878,9 +876,9 @@ def main():
         "stages_ms": {"index_build": pre["build_ms"], "indexer_topk": pre["topk_ms"],
                       "sparse_attn_prefill": pre["attn_ms"]},
         "indexer_share": (pre["build_ms"] + pre["topk_ms"]) / pre["sequential_ms"],
-        "schedule": (f"index build, then {PREFILL_CHUNKS} row chunks whose top-k runs on a "
-                     "second stream under the previous chunk's attention; stages_ms are the same "
-                     f"stages run one after the other ({pre['sequential_ms']:.2f} ms per step)"),
+        "schedule": (f"one stream: index build, then top-k and sparse attention over "
+                     f"{PREFILL_CHUNKS} row range(s); stages_ms time the same three calls with "
+                     f"an event between them ({pre['sequential_ms']:.2f} ms per step)"),
     }
     if peaks is not None:
         line["roofline"]["frac_of_measured_mfma"] = attn_tflops / peaks["mfma_bf16_tflops"]

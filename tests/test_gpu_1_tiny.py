@@ -84,10 +84,10 @@ def test_tiny_sliced_prefill_matches(tiny, tiny_host, rows_per_chunk):
     say(f"tiny sliced ({rows_per_chunk} rows/chunk): {st}")
 
 
-@pytest.mark.parametrize("chunks", [3, 8])
+@pytest.mark.parametrize("chunks", [1, 3, 8])
 def test_tiny_layer_schedule_same_bits(tiny, chunks):
-    """Selections of row chunks on a side stream under the attention of the chunk before give
-    the bits of the stages run one after the other (uneven chunks, a sliced workspace)."""
+    """The layer schedule in row chunks (each chunk's selection, then its attention) gives the
+    bits of the stages run one after the other over all rows (uneven chunks)."""
     from long_context_sparse_18_amd import layer
     shape = WL.shape
     ws_a = torch.empty(sgqa.workspace_bytes(sgqa.OP_ATTN_PREFILL, shape, 1, WL.T, WL.L),
@@ -100,7 +100,7 @@ def test_tiny_layer_schedule_same_bits(tiny, chunks):
     ws_t = torch.empty(sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, shape, 1, WL.T, WL.L),
                        dtype=torch.uint8, device=DEV)
     layer.prefill_layer(shape, tiny, 0, WL.L, 1.0 / math.sqrt(shape.head_dim), kb, idx, out,
-                        lse, ws_t, ws_a, chunks=chunks, side_stream=torch.cuda.Stream(DEV))
+                        lse, ws_t, ws_a, chunks=chunks)
     torch.cuda.synchronize()
     assert torch.equal(idx, ref["idx"]) and torch.equal(out, ref["out"])
     assert torch.equal(lse, ref["lse"]) and torch.equal(kb, ref["kb"])
