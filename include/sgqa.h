@@ -187,6 +187,11 @@ sgqa_status sgqa_indexer_topk(const sgqa_dims *dims, const sgqa_bf16 *qp, int64_
  *                   persistent launch's progress words); sgqa_workspace_bytes
  *                   with T rows gives the size for a single row chunk
  *   Calls that overlap on one device must use different workspaces.
+ * With a workspace the persistent launch is sized to the workgroups the whole
+ * GPU holds at once, and its waves wait (for a bounded time) on each other:
+ * kernels running beside it on other streams delay it sharply (a 128K layer
+ * with the selections on a second stream: up to ~2.5x), so run it alone.  The
+ * same holds for the resident schedules of sgqa_sparse_attn_backward.
  * Requires q_start + T <= L.
  */
 sgqa_status sgqa_sparse_attn_prefill(const sgqa_dims *dims, const sgqa_bf16 *q,
