@@ -260,6 +260,47 @@ def _forward_backward(shape, d, q_start: int, L: int, seed: int, ws_attn=None, w
     return res, dout, grads
 
 
+def test_prefill_128k_resident_beside_other_kernels():
+    """The resident attention's waits only order work for the caches: with the next chunks'
+    selections running on a second stream beside each chunk's persistent attention launch (so
+    some of its workgroups start late and the waiting waves run into their bound), every
+    output bit is the same as with the stages run one after the other."""
+    wl = WORKLOADS[2]
+    s = wl.shape
+    say("resident beside other kernels 128K: generating")
+    d = inputs.make_prefill(wl, 2, DEV)
+    ws_t = torch.empty(sgqa.workspace_bytes(sgqa.OP_INDEXER_TOPK, s, 1, wl.T, wl.L),
+                       dtype=torch.uint8, device=DEV)
+    ws_a = torch.empty(sgqa.workspace_bytes(sgqa.OP_ATTN_PREFILL, s, 1, wl.T, wl.L),
+                       dtype=torch.uint8, device=DEV)
+    ref = run_prefill(s, d, wl.q_start, wl.L, workspace=ws_t, attn_workspace=ws_a)
+    kb, idx = ref["kb"], torch.full_like(ref["idx"], -7)
+    out, lse = torch.empty_like(ref["out"]), torch.empty_like(ref["lse"])
+    main, side = torch.cuda.current_stream(DEV), torch.cuda.Stream(DEV)
+    T, chunks = wl.T, 8
+    bounds = [T * c // chunks for c in range(chunks + 1)]
+    ready = []
+    for c in range(chunks):
+        r0, r1 = bounds[c], bounds[c + 1]
+        sgqa.indexer_topk(s, d["qp"][r0:r1], kb, [wl.q_start + r0], idx[r0:r1], workspace=ws_t,
+                          stream=side)
+        ev = torch.cuda.Event()
+        ev.record(side)
+        ready.append(ev)
+    for c in range(chunks):
+        r0, r1 = bounds[c], bounds[c + 1]
+        main.wait_event(ready[c])
+        sgqa.sparse_attn_prefill(s, d["Q"][r0:r1], d["K"], d["V"], d["G"][r0:r1], idx[r0:r1],
+                                 wl.q_start + r0, wl.L, 1.0 / math.sqrt(s.head_dim), out[r0:r1],
+                                 lse[r0:r1], workspace=ws_a, stream=main)
+    torch.cuda.synchronize()
+    for name, a, b in (("idx", idx, ref["idx"]), ("out", out, ref["out"]), ("lse", lse, ref["lse"])):
+        assert torch.equal(a, b), name
+    say("resident beside other kernels 128K: identical")
+    del d, ref
+    torch.cuda.empty_cache()
+
+
 @pytest.mark.parametrize("with_out", [False, True])
 def test_backward_real_shape_chunk(with_out):
     """Fixed-selection backward at the real shape (64/4 heads, d 192, B 8, k 512) on a chunk of
