@@ -772,6 +772,29 @@ def test_tiny_backward(tiny, B, k, q0):
 
 
 @pytest.mark.gpu
+def test_tiny_backward_beside_other_kernels(tiny):
+    """The resident dq and dK / dV schedules wait on each other's progress only to order the work
+    for the caches: with matrix products running on a second stream as the backward starts (so
+    some of its workgroups start late and waiting waves run into their bound), every gradient bit
+    is the same as in a call run alone."""
+    shape = with_selection(WL.shape, 8, 16)
+    grads, _, args = _backward_case(tiny, shape, 0, WL.L, 11)
+    Q, K, V, G, idx, out, lse, dout = args
+    side = torch.cuda.Stream(DEV)
+    x = torch.randn((4096, 4096), dtype=torch.float32, device=DEV)
+    torch.cuda.synchronize()
+    again = {n: torch.full_like(v, float("nan")) for n, v in grads.items()}
+    with torch.cuda.stream(side):
+        for _ in range(4):
+            y = torch.mm(x, x)
+    sgqa.sparse_attn_backward(shape, Q, K, V, G, idx, 0, WL.L, 1.0 / math.sqrt(shape.head_dim),
+                              lse, dout, again["dq"], again["dk"], again["dv"], again["dg"])
+    torch.cuda.synchronize()
+    del y
+    for n in grads:
+        assert torch.equal(grads[n], again[n]), n
+
+
 def test_peak_probes():
     """The machine-peak probes compute what they state: every MFMA-probe wave reports
     2048 * iters (37 waves: a partial last workgroup), and the read probe's partial sums add
